@@ -1,0 +1,422 @@
+"""Plain float64 CPU oracle for layer-wise post-training weight quantization.
+
+TEST INFRASTRUCTURE.  This module is the checker the GPU library is compared
+against.  It is deliberately slow and literal: numpy in float64, one step of the
+method per function, no blocking, fusion or reordering beyond what the method
+itself states.  It shares no code with the HIP library.
+
+Sources (page title, then section):
+
+* [GPT2-RE]  "GPT-2 Quantization Reconstruction Error", sections "What this
+  project does" and "Setup": 4-bit symmetric quantization with one scale per
+  output row (channel), rounded to 15 levels and dequantized; per-layer output MSE.
+* [MQM]      "Model Quantization Mechanics: Precision Reduction and Weight
+  Formatting", section 1 ("Affine Quantization", "Group-wise Quantization") and
+  section 2.1 (GPTQ objective, Cholesky factor of the inverse Hessian).
+* [LESSON17] "17 - GPTQ and AWQ" (Inference and Serving), Part 1, "Your turn" and
+  Example 1.1 "Rounding with the error carried forward".
+* [GPTQ-P]   "GPTQ: Post-Training INT4", sections "OBQ Foundation",
+  "Hessian-Based Weight Update", "The GPTQ Algorithm", "Group Quantization",
+  "Running GPTQ with AutoGPTQ" (config knobs group_size, desc_act, damp_percent, sym).
+* [SWEEP]    "Quantization sweep: perplexity vs compression", "How I ran each
+  one" (damp_percent 0.0 for RTN, 0.01 for GPTQ, group size 128).
+
+Readings taken where the pages are silent, ambiguous or garbled (each is also
+listed in the design notes):
+
+* R1  The factor that drives the column loop is U, the upper-triangular Cholesky
+      factor of H^-1 (H^-1 = U^T U), as [MQM] 2.1 states.  The code listing in
+      [GPTQ-P] indexes the full H^-1 instead; that literal form is exact only for the
+      first column and is not taken.  Only the U form makes each step the OBS
+      update on the still-unquantized set (``direct_obs`` checks this).
+* R2  The OBS update printed in [GPTQ-P] "Hessian-Based Weight Update" uses entries
+      of H where the optimum needs the inverse restricted to the free set; we follow
+      the listing's signs: e = (w - what) / U_jj, then w_k -= e * U_jk for k > j.
+* R3  Damping: lambda = damp * mean(diag H) of the undamped H, added to every
+      diagonal entry ([GPTQ-P] "Running GPTQ with AutoGPTQ", damp_percent; damp may
+      be 0 as in [SWEEP]).
+* R4  H = 2 X^T X with X stored tokens x d_in, summed (not averaged) over tokens
+      ([GPTQ-P] "Hessian-Based Weight Update" and the listing; codes do not depend
+      on a positive factor on H when the damping is relative).
+* R5  A group's scale is taken, when the loop reaches the group's first column,
+      from the current (error-updated) values of the group's columns.  With one
+      scale per row that is the original row.
+* R6  The listing's "q" in (w - q) / h_inv_jj is the dequantized value s * code.
+* R7  Scale: s = fp16( fp32( fp32(absmax) / qmax ) ), qmax = 2^(bits-1) - 1, i.e. one
+      IEEE float32 division rounded to float16 (the stored 16-bit scale of
+      [GPTQ-P] "Group Quantization"); codes are computed against the stored scale.
+* R8  Codes: nearest integer to the exact quotient w / s, ties to even (Python's
+      round, as in [LESSON17]'s listing), clamped to [-qmax, qmax] (15 levels for
+      4 bits, [GPT2-RE]); an all-zero group has s = 0 and all codes 0.
+* R9  Act-order (desc_act): columns processed by descending diag H (stable: lower
+      original index first on ties); groups are consecutive in processing order;
+      codes are returned in original column order with g_idx[c] = position(c) // g.
+* R10 INT4 storage: nibble u = code + 8; byte k of a row holds column 2k in the low
+      nibble and column 2k+1 in the high nibble.
+* R11 Reconstruction MSE: mean over all tokens x outputs of (X (W - What)^T)^2 with the
+      same X for both and the original W ([GPT2-RE] step 5, per layer).
+* R12 A non positive definite H raises NotPositiveDefinite (no automatic re-damping).
+
+Pins (tests/test_oracle_pins.py):
+  rtn / quantize_codes / group_scales : golden tie-to-even rows, code range, error bound,
+                                        level count
+  gptq                                : [LESSON17] worked examples (golden), diagonal-H == rtn,
+                                        direct_obs agreement, block-size invariance,
+                                        scale invariance, brute-force optimum on tiny rows
+  chol_inverse_upper                  : U^T U H = I, triangular, positive diagonal,
+                                        reverse-order Cholesky + triangular inverse route
+  hessian / damp                      : brute force on tiny X, trace identity, symmetry
+  act_order_perm                      : already-sorted diagonal == no act-order; g_idx round trip
+  pack_int4 / dequant                 : golden bytes, storage bits/weight of [GPTQ-P]
+  recon_mse                           : trace identity with the undamped Hessian
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional, Union
+
+import numpy as np
+
+__all__ = [
+    "NotPositiveDefinite", "qmax", "group_scales_from_absmax", "quantize_codes",
+    "hessian", "damp_hessian", "act_order_perm", "chol_inverse_upper",
+    "gptq", "gptq_unblocked", "rtn", "pack_int4", "unpack_int4", "dequant",
+    "recon_mse", "recon_mse_trace", "direct_obs", "quantize_layer", "n_groups",
+    "storage_bytes",
+]
+
+
+class NotPositiveDefinite(ArithmeticError):
+    """H (after damping) is not positive definite; ``pivot`` is the 0-based failing pivot
+    in reverse column order (the order the GPU factorization eliminates in)."""
+
+    def __init__(self, pivot: int):
+        super().__init__(f"Hessian not positive definite (pivot {pivot})")
+        self.pivot = pivot
+
+
+# ------------------------------------------------------------------ quantizer primitives
+
+def qmax(bits: int) -> int:
+    """Largest code magnitude: 7 for 4 bits, i.e. 15 levels -7..7 ([GPT2-RE], R8)."""
+    return (1 << (bits - 1)) - 1
+
+
+def n_groups(d_in: int, group_size: int) -> int:
+    return 1 if group_size == 0 else -(-d_in // group_size)
+
+
+def group_scales_from_absmax(absmax: np.ndarray, bits: int) -> np.ndarray:
+    """Symmetric scale S of [MQM] "Affine Quantization" with Z = 0: absmax / qmax,
+    as one float32 division, stored as float16 (R7).  Returns float16."""
+    a32 = np.asarray(absmax, dtype=np.float64).astype(np.float32)
+    s32 = (a32 / np.float32(qmax(bits))).astype(np.float32)
+    return s32.astype(np.float16)
+
+
+def quantize_codes(w: np.ndarray, s16: np.ndarray, bits: int) -> np.ndarray:
+    """Codes round(w / s) ([MQM] "Affine Quantization", Z = 0), exact quotient rounded to
+    nearest-even in float64, clamped to +-qmax; s = 0 gives code 0 (R8).
+
+    float64 decides these exactly: w has at most 24 significant bits and s 11, so a
+    quotient that is not a tie lies at least 2^-29 (relative) from k + 1/2, far above
+    float64's division error."""
+    w = np.asarray(w, dtype=np.float64)
+    s = np.asarray(s16, dtype=np.float16).astype(np.float64)
+    safe = np.where(s > 0, s, 1.0)
+    q = np.rint(w / safe)
+    q = np.clip(q, -qmax(bits), qmax(bits))
+    q = np.where(s > 0, q, 0.0)
+    return q.astype(np.int8)
+
+
+# ------------------------------------------------------------------ Hessian, damping, order
+
+def hessian(x_tiles: Union[np.ndarray, Iterable[np.ndarray]]) -> np.ndarray:
+    """H = 2 X^T X, summed over all tokens ([GPTQ-P] "Hessian-Based Weight Update", R4).
+
+    ``x_tiles`` is X (tokens x d_in) or an iterable of token tiles; values are taken
+    in float64 exactly as stored."""
+    if isinstance(x_tiles, np.ndarray):
+        x_tiles = [x_tiles]
+    H = None
+    for xt in x_tiles:
+        x = np.asarray(xt, dtype=np.float64)
+        part = x.T @ x
+        H = part if H is None else H + part
+    return 2.0 * H
+
+
+def damp_hessian(H: np.ndarray, damp: float):
+    """H + lambda I with lambda = damp * mean(diag H) (R3).  Returns (H_damped, lambda)."""
+    lam = float(damp) * float(np.mean(np.diag(H)))
+    Hd = H.copy()
+    Hd[np.diag_indices_from(Hd)] += lam
+    return Hd, lam
+
+
+def act_order_perm(H: np.ndarray) -> np.ndarray:
+    """Processing order for desc_act: descending diag H, stable on ties (R9)."""
+    return np.argsort(-np.diag(H), kind="stable").astype(np.int32)
+
+
+def chol_inverse_upper(H: np.ndarray) -> np.ndarray:
+    """U upper triangular with H^-1 = U^T U and U_jj > 0 ([MQM] 2.1, R1).
+
+    Textbook route: invert H, take the lower Cholesky factor L of H^-1, U = L^T.
+    Raises NotPositiveDefinite when H is not positive definite (R12); the pivot is
+    located by LAPACK's Cholesky of H in reversed index order."""
+    from scipy.linalg import lapack
+
+    n = H.shape[0]
+    rev = H[::-1, ::-1]
+    _, info = lapack.dpotrf(np.array(rev, dtype=np.float64, order="F"), lower=1)
+    if info != 0:
+        k = int(info) - 1 if info > 0 else 0
+        raise NotPositiveDefinite(n - 1 - k)
+    Hinv = np.linalg.inv(H)
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    L = np.linalg.cholesky(Hinv)
+    return np.triu(L.T)
+
+
+# ------------------------------------------------------------------ GPTQ column loop
+
+def _group_len(n: int, group_size: int) -> int:
+    return n if group_size == 0 else group_size
+
+
+def _finish(codes_p, scales, perm, group_size, bits):
+    m, n = codes_p.shape
+    if perm is None:
+        codes, g_idx = codes_p, None
+    else:
+        codes = np.empty_like(codes_p)
+        codes[:, perm] = codes_p
+        g = _group_len(n, group_size)
+        g_idx = np.empty(n, dtype=np.int32)
+        g_idx[perm] = (np.arange(n) // g).astype(np.int32)
+    What = dequant(codes, scales, group_size, g_idx=g_idx, out_dtype=np.float64)
+    return {"codes": codes, "scales": scales, "g_idx": g_idx, "What": What, "bits": bits,
+            "group_size": group_size}
+
+
+def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, block_size: int = 128,
+         perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None) -> dict:
+    """GPTQ with lazy block updates ([GPTQ-P] "The GPTQ Algorithm", R1-R9).
+
+    W: d_out x d_in (any float dtype, promoted to float64).  U: the factor of
+    ``chol_inverse_upper`` of the (damped, permuted if ``perm``) Hessian.
+
+    Columns are taken left to right in blocks of ``block_size``.  For each column j of
+    a block: (at a group's first column) the group's scales; codes = round(w_j / s);
+    e_j = (w_j - s * code) / U_jj is stored in the block's error panel; the columns
+    j+1..block end of the panel get w_k -= e_j U_jk at once.  After the block, all
+    columns right of it get W -= Err @ U[block, right] in one product.
+
+    A group that starts inside a block and reaches past its end sees, for its columns
+    right of the block, the updates still pending from the block's earlier columns
+    (the pages' group = block = 128 case never needs this).
+
+    Returns codes (int8, original column order), scales (float16, d_out x groups, in
+    processing order), g_idx (int32 or None) and What (float64)."""
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    Wp = W[:, perm].copy() if perm is not None else W.copy()
+    g = _group_len(n, group_size)
+    ng = n_groups(n, group_size)
+    scales = np.zeros((m, ng), dtype=np.float16) if scales_in is None else np.array(scales_in, dtype=np.float16).reshape(m, ng)
+    codes_p = np.zeros((m, n), dtype=np.int8)
+    B = int(block_size)
+    for b0 in range(0, n, B):
+        b1 = min(b0 + B, n)
+        panel = Wp[:, b0:b1].copy()
+        err = np.zeros((m, b1 - b0))
+        for j in range(b0, b1):
+            jj = j - b0
+            G = j // g
+            if j % g == 0 and scales_in is None:
+                ge = min(j + g, n)
+                vals = panel[:, jj:min(ge, b1) - b0]
+                if ge > b1:
+                    pending = Wp[:, b1:ge] - err[:, :jj] @ U[b0:j, b1:ge]
+                    vals = np.concatenate([vals, pending], axis=1)
+                scales[:, G] = group_scales_from_absmax(np.max(np.abs(vals), axis=1), bits)
+            w = panel[:, jj]
+            q = quantize_codes(w, scales[:, G], bits)
+            codes_p[:, j] = q
+            what = scales[:, G].astype(np.float64) * q
+            e = (w - what) / U[j, j]
+            err[:, jj] = e
+            panel[:, jj + 1:] -= np.outer(e, U[j, j + 1:b1])
+        if b1 < n:
+            Wp[:, b1:] -= err @ U[b0:b1, b1:]
+    return _finish(codes_p, scales, perm, group_size, bits)
+
+
+def gptq_unblocked(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128,
+                   perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None) -> dict:
+    """The column loop without lazy batching: every error goes to all later columns at once."""
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    Wp = W[:, perm].copy() if perm is not None else W.copy()
+    g = _group_len(n, group_size)
+    ng = n_groups(n, group_size)
+    scales = np.zeros((m, ng), dtype=np.float16) if scales_in is None else np.array(scales_in, dtype=np.float16).reshape(m, ng)
+    codes_p = np.zeros((m, n), dtype=np.int8)
+    for j in range(n):
+        G = j // g
+        if j % g == 0 and scales_in is None:
+            scales[:, G] = group_scales_from_absmax(np.max(np.abs(Wp[:, j:j + g]), axis=1), bits)
+        w = Wp[:, j]
+        q = quantize_codes(w, scales[:, G], bits)
+        codes_p[:, j] = q
+        e = (w - scales[:, G].astype(np.float64) * q) / U[j, j]
+        Wp[:, j + 1:] -= np.outer(e, U[j, j + 1:])
+    return _finish(codes_p, scales, perm, group_size, bits)
+
+
+def rtn(W: np.ndarray, bits: int = 4, group_size: int = 128, scales_in: Optional[np.ndarray] = None) -> dict:
+    """Round-to-nearest: scales from the original W per row ([GPT2-RE]) or per group of
+    ``group_size`` consecutive columns ([MQM] "Group-wise Quantization"), then codes."""
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    g = _group_len(n, group_size)
+    ng = n_groups(n, group_size)
+    if scales_in is None:
+        scales = np.zeros((m, ng), dtype=np.float16)
+        for G in range(ng):
+            scales[:, G] = group_scales_from_absmax(np.max(np.abs(W[:, G * g:(G + 1) * g]), axis=1), bits)
+    else:
+        scales = np.array(scales_in, dtype=np.float16).reshape(m, ng)
+    codes = np.zeros((m, n), dtype=np.int8)
+    for G in range(ng):
+        codes[:, G * g:(G + 1) * g] = quantize_codes(W[:, G * g:(G + 1) * g], scales[:, G:G + 1], bits)
+    What = dequant(codes, scales, group_size, out_dtype=np.float64)
+    return {"codes": codes, "scales": scales, "g_idx": None, "What": What, "bits": bits,
+            "group_size": group_size}
+
+
+# ------------------------------------------------------------------ storage
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte, nibble = code + 8, even column in the low nibble (R10)."""
+    c = np.asarray(codes, dtype=np.int16)
+    m, n = c.shape
+    if n % 2:
+        raise ValueError("d_in must be even to pack two codes per byte")
+    u = (c + 8).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray, d_in: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty((p.shape[0], d_in), dtype=np.int8)
+    codes[:, 0::2] = (p & 0x0F).astype(np.int16) - 8
+    codes[:, 1::2] = (p >> 4).astype(np.int16) - 8
+    return codes
+
+
+def storage_bytes(d_out: int, d_in: int, group_size: int) -> int:
+    """Bytes of the packed INT4 codes plus one float16 scale per row and group
+    ([GPTQ-P] "Group Quantization": 4 bits + 16 / group_size bits per weight)."""
+    return d_out * d_in // 2 + 2 * d_out * n_groups(d_in, group_size)
+
+
+def dequant(codes: np.ndarray, scales: np.ndarray, group_size: int, g_idx: Optional[np.ndarray] = None,
+            out_dtype=np.float64) -> np.ndarray:
+    """What[r, c] = s[r, group(c)] * code[r, c] ([MQM] "Affine Quantization" with Z = 0),
+    exact in float64, then rounded once to ``out_dtype``."""
+    codes = np.asarray(codes)
+    m, n = codes.shape
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64).reshape(m, -1)
+    if group_size == 0:
+        gi = np.zeros(n, dtype=np.int64)
+    elif g_idx is not None:
+        gi = np.asarray(g_idx, dtype=np.int64)
+    else:
+        gi = np.arange(n) // group_size
+    What = s[:, gi] * codes.astype(np.float64)
+    return What.astype(out_dtype)
+
+
+# ------------------------------------------------------------------ error measures
+
+def recon_mse(x_tiles: Union[np.ndarray, Iterable[np.ndarray]], W: np.ndarray, What: np.ndarray,
+              row_chunk: int = 2048) -> float:
+    """Mean over tokens x outputs of (X W^T - X What^T)^2 ([GPT2-RE] step 5, R11)."""
+    if isinstance(x_tiles, np.ndarray):
+        x_tiles = [x_tiles]
+    dW = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    total, ntok = 0.0, 0
+    for xt in x_tiles:
+        x = np.asarray(xt, dtype=np.float64)
+        for r0 in range(0, x.shape[0], row_chunk):
+            y = x[r0:r0 + row_chunk] @ dW.T
+            total += float(np.sum(y * y))
+        ntok += x.shape[0]
+    return total / (ntok * dW.shape[0])
+
+
+def recon_mse_trace(H_undamped: np.ndarray, n_tok: int, W: np.ndarray, What: np.ndarray) -> float:
+    """Same quantity as ``recon_mse`` via ||X dW^T||^2 = tr(dW X^T X dW^T), X^T X = H / 2."""
+    dW = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    return float(np.einsum("ij,jk,ik->", dW, 0.5 * H_undamped, dW)) / (n_tok * dW.shape[0])
+
+
+# ------------------------------------------------------------------ OBS reference (tiny sizes)
+
+def direct_obs(W: np.ndarray, H: np.ndarray, bits: int, group_size: int = 0,
+               scales_in: Optional[np.ndarray] = None) -> dict:
+    """Sequential OBS in fixed left-to-right order, with no Cholesky factor at all.
+
+    After column j is fixed at what_j, the still-free columns F = j+1.. move by the
+    minimiser of the quadratic error restricted to F: delta_F = -(H_FF)^-1 H_Fj delta_j,
+    delta_j = what_j - w_j ([GPTQ-P] "OBQ Foundation" and "Hessian-Based Weight Update"
+    with R2).  Linear solves per step: tiny d_in only."""
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    g = _group_len(n, group_size)
+    ng = n_groups(n, group_size)
+    scales = np.zeros((m, ng), dtype=np.float16) if scales_in is None else np.array(scales_in, dtype=np.float16).reshape(m, ng)
+    codes = np.zeros((m, n), dtype=np.int8)
+    Wc = W.copy()
+    for j in range(n):
+        G = j // g
+        if j % g == 0 and scales_in is None:
+            scales[:, G] = group_scales_from_absmax(np.max(np.abs(Wc[:, j:j + g]), axis=1), bits)
+        q = quantize_codes(Wc[:, j], scales[:, G], bits)
+        codes[:, j] = q
+        delta = scales[:, G].astype(np.float64) * q - Wc[:, j]
+        Wc[:, j] += delta
+        if j + 1 < n:
+            F = slice(j + 1, n)
+            step = np.linalg.solve(H[F, F], H[F, j])
+            Wc[:, F] -= np.outer(delta, step)
+    What = dequant(codes, scales, group_size, out_dtype=np.float64)
+    return {"codes": codes, "scales": scales, "What": What}
+
+
+# ------------------------------------------------------------------ whole layer
+
+def quantize_layer(W: np.ndarray, x_tiles, bits: int = 4, group_size: int = 128, block_size: int = 128,
+                   damp: float = 0.01, act_order: bool = False) -> dict:
+    """Hessian -> damping -> [act-order] -> U -> GPTQ, plus RTN and both MSEs on the same X."""
+    if isinstance(x_tiles, np.ndarray):
+        x_tiles = [x_tiles]
+    x_tiles = list(x_tiles)
+    H = hessian(x_tiles)
+    n_tok = sum(int(np.asarray(t).shape[0]) for t in x_tiles)
+    Hd, lam = damp_hessian(H, damp)
+    perm = act_order_perm(Hd) if act_order else None
+    Hp = Hd[np.ix_(perm, perm)] if perm is not None else Hd
+    U = chol_inverse_upper(Hp)
+    res = gptq(W, U, bits, group_size, block_size, perm=perm)
+    r = rtn(W, bits, group_size)
+    res.update({
+        "H": H, "lambda": lam, "perm": perm, "U": U,
+        "rtn": r,
+        "gptq_mse": recon_mse(x_tiles, W, res["What"]),
+        "rtn_mse": recon_mse(x_tiles, W, r["What"]),
+        "n_tok": n_tok,
+    })
+    return res

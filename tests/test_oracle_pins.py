@@ -1,0 +1,420 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with itself: each check is a value the pages print,
+a closed form, an invariant, a special case that reduces to a different computation,
+or brute force on tiny inputs.
+"""
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from conftest import read_golden
+import oracle as O
+
+
+def tril_ones(n):
+    """Token t sees input channels 0..t with value 1.0: the last token's output is the plain
+    sum of the weights, and the Cholesky factor of H^-1 is upper bidiagonal with
+    U[j, j+1] / U[j, j] = -1, so the GPTQ update adds the whole residual of column j to
+    column j+1, which is the error-carry rule of the lesson's Example 1.1."""
+    return np.tril(np.ones((n, n)))
+
+
+def gptq_full(W, X, bits, group_size, block_size, damp, scales_in=None, act_order=False):
+    H = O.hessian(X)
+    Hd, _ = O.damp_hessian(H, damp)
+    perm = O.act_order_perm(Hd) if act_order else None
+    Hp = Hd[np.ix_(perm, perm)] if perm is not None else Hd
+    U = O.chol_inverse_upper(Hp)
+    return O.gptq(W, U, bits, group_size, block_size, perm=perm, scales_in=scales_in), H, Hd, U
+
+
+def ar1_x(rng, n_tok, n, rho=0.9):
+    """Correlated calibration inputs: AR(1) across channels, unit variance."""
+    x = np.empty((n_tok, n))
+    x[:, 0] = rng.standard_normal(n_tok)
+    for c in range(1, n):
+        x[:, c] = rho * x[:, c - 1] + np.sqrt(1 - rho * rho) * rng.standard_normal(n_tok)
+    return x
+
+
+# ---------------------------------------------------------------------------------- p1
+@pytest.mark.parametrize("block_size", [1, 2, 4, 128])
+@pytest.mark.parametrize("damp", [0.0, 0.01])
+def test_lesson17_six_weight_example(block_size, damp):
+    g = read_golden("lesson17_example_1_1.txt")
+    w = np.array([g["weights"]])
+    x_in = np.array(g["inputs"])
+    n = w.shape[1]
+    X = tril_ones(n)
+    assert np.array_equal(X[-1], x_in)       # last token carries the page's all-ones input
+    s = np.array([[g["step"]]], dtype=np.float16)
+    res, *_ = gptq_full(w, X, bits=4, group_size=0, block_size=block_size, damp=damp, scales_in=s)
+    comp = res["What"][0]
+    assert [round(v, 1) for v in comp] == g["compensated"]
+    assert round(abs(comp @ x_in - w[0] @ x_in), 2) == g["compensated_abs_error"]
+    r = O.rtn(w, bits=4, group_size=0, scales_in=s)["What"][0]
+    assert [round(v, 1) for v in r] == g["nearest"]
+    assert round(abs(r @ x_in - w[0] @ x_in), 2) == g["nearest_abs_error"]
+
+
+def test_lesson17_two_weight_exercise():
+    g = read_golden("lesson17_two_weights.txt")
+    w = np.array([g["weights"]])
+    x_in = np.array(g["inputs"])
+    assert abs(w[0] @ x_in - g["true_output"]) < 1e-12
+    for pair, key in (("pair_up_up", "pair_up_up_error"), ("pair_down_down", "pair_down_down_error"),
+                      ("pair_up_down", "pair_up_down_error")):
+        assert round(abs(np.array(g[pair]) @ x_in - g["true_output"]), 2) == g[key]
+    s = np.array([[g["step"]]], dtype=np.float16)
+    res, *_ = gptq_full(w, tril_ones(2), bits=4, group_size=0, block_size=128, damp=0.0, scales_in=s)
+    assert [round(v, 1) for v in res["What"][0]] == g["carried"]
+    assert round(float(res["What"][0] @ x_in), 1) == g["carried_output"]
+    r = O.rtn(w, bits=4, group_size=0, scales_in=s)["What"][0]
+    assert [round(v, 1) for v in r] == g["nearest"]
+
+
+def test_error_carry_rule_equals_gptq_on_random_rows():
+    """For X = lower-triangular ones the U-form loop is exactly the carry rule of Example 1.1
+    (round (v + carry), carry the residual) on any row and grid step."""
+    rng = np.random.default_rng(11)
+    n = 12
+    W = rng.normal(0, 0.3, size=(40, n))
+    s = np.full((40, 1), 0.0625, dtype=np.float16)     # power-of-two grid: all values exact
+    res, *_ = gptq_full(W, tril_ones(n), bits=8, group_size=0, block_size=5, damp=0.0, scales_in=s)
+    step = float(s[0, 0])
+    for r in range(W.shape[0]):
+        carry, comp = 0.0, []
+        for v in W[r]:
+            q = round((v + carry) / step) * step
+            carry = v + carry - q
+            comp.append(q)
+        assert np.allclose(res["What"][r], comp, atol=0, rtol=0)
+
+
+# ---------------------------------------------------------------------------------- p2 / p13 / R7 / R8
+def test_levels_and_code_range():
+    g = read_golden("gpt2_re_levels.txt")
+    assert 2 * O.qmax(int(g["bits"])) + 1 == g["levels"]
+    rng = np.random.default_rng(2)
+    W = rng.normal(0, 0.02, size=(64, 512)).astype(np.float32)
+    for gs in (0, 128):
+        r = O.rtn(W, bits=4, group_size=gs)
+        c = r["codes"]
+        assert c.min() >= -7 and c.max() <= 7
+        assert len(np.unique(c)) <= g["levels"]
+        glen = 512 if gs == 0 else gs
+        for G in range(512 // glen):
+            blk = np.abs(W[:, G * glen:(G + 1) * glen].astype(np.float64))
+            idx = np.argmax(blk, axis=1)
+            assert np.all(np.abs(c[np.arange(64), G * glen + idx]) == 7)   # absmax element -> +-7
+    assert len(np.unique(O.rtn(W, 4, 0)["codes"])) == 15
+
+
+def test_rtn_ties_to_even_closed_form():
+    # absmax 7 -> s = 7/7 = 1 exactly; x.5 quotients are exact ties, decided to even
+    W = np.array([[7.0, -3.5, 0.5, 2.5, -1.5, 0.0, 1.0, -7.0]], dtype=np.float32)
+    assert O.rtn(W, 4, 0)["codes"].tolist() == [[7, -4, 0, 2, -2, 0, 1, -7]]
+    r = O.rtn(W, 4, 4)
+    assert r["scales"].astype(np.float64).tolist() == [[1.0, 1.0]]
+    assert r["codes"].tolist() == [[7, -4, 0, 2, -2, 0, 1, -7]]
+    # absmax 3.5 -> s = 0.5; 1.25 / 0.5 = 2.5 -> 2, 0.75 / 0.5 = 1.5 -> 2
+    W2 = np.array([[3.5, 1.25, 0.75, -0.25]], dtype=np.float32)
+    r2 = O.rtn(W2, 4, 0)
+    assert float(r2["scales"][0, 0]) == 0.5
+    assert r2["codes"].tolist() == [[7, 2, 2, 0]]
+    # all-zero group: s = 0, codes 0
+    W3 = np.zeros((1, 8), dtype=np.float32)
+    r3 = O.rtn(W3, 4, 4)
+    assert r3["scales"].tolist() == [[0.0, 0.0]] and not r3["codes"].any()
+
+
+def _rne_to_precision(x: Fraction, mant_bits: int, emin: int) -> Fraction:
+    """Nearest value with ``mant_bits`` significant bits (ties to even), exponent >= emin."""
+    if x == 0:
+        return Fraction(0)
+    sgn = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, emin)
+    ulp = Fraction(2) ** (e - mant_bits + 1)
+    k = a / ulp
+    f = k.numerator // k.denominator
+    rem = k - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return sgn * f * ulp
+
+
+def test_scale_is_one_fp32_division_then_fp16():
+    rng = np.random.default_rng(3)
+    absmax = np.abs(rng.normal(0, 0.05, size=400)).astype(np.float32)
+    s = O.group_scales_from_absmax(absmax, 4)
+    for a, got in zip(absmax, s):
+        q32 = _rne_to_precision(Fraction(float(a)) / 7, 24, -126)
+        want = _rne_to_precision(q32, 11, -14)
+        assert Fraction(float(got)) == want
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 40), st.integers(1, 40), st.sampled_from([0, 4, 8]), st.integers(0, 2**31 - 1))
+def test_rtn_error_bound_and_pack_round_trip(m, half_n, gs, seed):
+    n = 2 * half_n
+    if gs and n % gs:
+        n = gs * max(1, n // gs)
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_t(3, size=(m, n)) * 0.02).astype(np.float32)
+    r = O.rtn(W, 4, gs)
+    s = r["scales"].astype(np.float64)
+    gi = np.zeros(n, int) if gs == 0 else np.arange(n) // gs
+    err = np.abs(W.astype(np.float64) - r["What"])
+    assert np.all(err <= s[:, gi] / 2)                                 # never clamped for RTN
+    assert np.array_equal(O.unpack_int4(O.pack_int4(r["codes"]), n), r["codes"])
+
+
+# ---------------------------------------------------------------------------------- p3
+@pytest.mark.parametrize("gs", [0, 128])
+def test_diagonal_hessian_gptq_equals_rtn(gs):
+    rng = np.random.default_rng(4)
+    n, m = 256, 48
+    W = rng.normal(0, 0.02, size=(m, n)).astype(np.float32)
+    X = np.diag(rng.uniform(0.5, 3.0, size=n))          # one token per channel: H diagonal
+    res, H, Hd, U = gptq_full(W, X, 4, gs, 128, 0.01)
+    assert np.count_nonzero(U - np.diag(np.diag(U))) == 0
+    r = O.rtn(W, 4, gs)
+    assert np.array_equal(res["codes"], r["codes"])
+    assert np.array_equal(res["scales"].view(np.uint16), r["scales"].view(np.uint16))
+
+
+# ---------------------------------------------------------------------------------- p4 / R11
+def test_recon_mse_trace_identity():
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((300, 64))
+    W = rng.normal(0, 0.02, size=(40, 64))
+    r = O.rtn(W, 4, 16)
+    direct = O.recon_mse([X[:128], X[128:]], W, r["What"])
+    H = O.hessian(X)
+    assert abs(direct - O.recon_mse_trace(H, 300, W, r["What"])) <= 1e-12 * direct
+    # brute force over every token and output on a tiny case
+    Xs, Ws, Wh = X[:5, :6], W[:3, :6], r["What"][:3, :6]
+    tot = 0.0
+    for t in range(5):
+        for o in range(3):
+            y = sum(Xs[t, c] * (Ws[o, c] - Wh[o, c]) for c in range(6))
+            tot += y * y
+    assert abs(O.recon_mse(Xs, Ws, Wh) - tot / 15) <= 1e-14 * max(tot, 1e-300)
+
+
+# ---------------------------------------------------------------------------------- p5
+def test_storage_bits_per_weight():
+    g = read_golden("gptq_page_storage.txt")
+    gs = int(g["group_size"])
+    m, n = 64, 4 * gs
+    bits = O.storage_bytes(m, n, gs) * 8 / (m * n)
+    assert bits == g["bits_per_weight_symmetric"]
+    assert bits + 16 / gs == g["bits_per_weight_with_zero_point"]
+    codes = O.rtn(np.random.default_rng(6).normal(size=(m, n)), 4, gs)["codes"]
+    assert O.pack_int4(codes).nbytes == m * n // 2
+    assert O.storage_bytes(m, n, 0) * 8 / (m * n) == 4 + 16 / n
+
+
+def test_pack_layout_closed_form():
+    # nibble = code + 8, even column in the low nibble
+    codes = np.array([[-7, 7, 0, 1, -8 + 8, 3]], dtype=np.int8)
+    assert O.pack_int4(codes).tolist() == [[0xF1, 0x98, 0xB8]]
+
+
+# ---------------------------------------------------------------------------------- p6 brute force
+def _brute_force_min(w, s, Hq, bits):
+    """min over every code vector in [-qmax, qmax]^n of (s c - w)^T Hq (s c - w)."""
+    qm = O.qmax(bits)
+    n = w.size
+    levels = np.arange(-qm, qm + 1, dtype=np.float64)
+    L = np.linalg.cholesky(Hq + 0 * np.eye(n))
+    head = max(0, n - 6)
+    tail = np.array(list(itertools.product(levels, repeat=n - head)))       # (7^6, n-head)
+    best = np.inf
+    for pre in itertools.product(levels, repeat=head):
+        C = np.concatenate([np.broadcast_to(np.array(pre), (tail.shape[0], head)), tail], axis=1)
+        D = s * C - w
+        e = np.sum((D @ L) ** 2, axis=1)
+        best = min(best, float(e.min()))
+    return best
+
+
+def _row_err(w, what, Hq):
+    d = what - w
+    return float(d @ Hq @ d)
+
+
+@pytest.mark.parametrize("n,rows", [(6, 120), (8, 8)])
+def test_brute_force_optimum_bounds_gptq_and_rtn(n, rows):
+    rng = np.random.default_rng(7 + n)
+    bits = 3
+    X = ar1_x(rng, 64, n)
+    W = rng.normal(0, 0.02, size=(rows, n))
+    res, H, Hd, U = gptq_full(W, X, bits, 0, 128, 0.01)
+    r = O.rtn(W, bits, 0)
+    assert np.array_equal(res["scales"], r["scales"])                 # same per-row scale for all three
+    Hq = 0.5 * H                                                      # X^T X: the layer objective
+    e_g, e_r = [], []
+    for i in range(rows):
+        s = float(r["scales"][i, 0])
+        opt = _brute_force_min(W[i], s, Hq, bits)
+        eg, er = _row_err(W[i], res["What"][i], Hq), _row_err(W[i], r["What"][i], Hq)
+        assert opt <= eg * (1 + 1e-12) and opt <= er * (1 + 1e-12)
+        e_g.append(eg)
+        e_r.append(er)
+    assert np.mean(e_g) < np.mean(e_r)
+
+
+# ---------------------------------------------------------------------------------- p7 (R1)
+def test_u_form_loop_equals_direct_obs():
+    rng = np.random.default_rng(8)
+    n, rows = 8, 400
+    X = ar1_x(rng, 64, n)
+    W = rng.normal(0, 0.02, size=(rows, n))
+    res, H, Hd, U = gptq_full(W, X, 3, 0, 128, 0.01)
+    ref = O.direct_obs(W, Hd, 3, 0)
+    assert np.array_equal(res["codes"], ref["codes"])
+
+
+def test_u_form_loop_equals_direct_obs_groups():
+    rng = np.random.default_rng(9)
+    n, rows = 12, 200
+    X = ar1_x(rng, 80, n, 0.8)
+    W = rng.normal(0, 0.02, size=(rows, n))
+    res, H, Hd, U = gptq_full(W, X, 4, 4, 5, 0.01)
+    ref = O.direct_obs(W, Hd, 4, 4)
+    assert np.array_equal(res["codes"], ref["codes"])
+    assert np.array_equal(res["scales"], ref["scales"])
+
+
+# ---------------------------------------------------------------------------------- p8
+@pytest.mark.parametrize("gs", [0, 8, 16])
+def test_block_size_invariance(gs):
+    rng = np.random.default_rng(10)
+    n, m = 48, 64
+    X = ar1_x(rng, 200, n, 0.7)
+    W = rng.normal(0, 0.02, size=(m, n))
+    H = O.hessian(X)
+    Hd, _ = O.damp_hessian(H, 0.01)
+    U = O.chol_inverse_upper(Hd)
+    ref = O.gptq_unblocked(W, U, 4, gs)
+    for B in (1, 3, 5, 16, 128, n):
+        got = O.gptq(W, U, 4, gs, B)
+        assert np.array_equal(got["codes"], ref["codes"]), B
+        assert np.array_equal(got["scales"], ref["scales"]), B
+
+
+# ---------------------------------------------------------------------------------- p9
+def test_chol_inverse_upper_properties_and_reverse_route():
+    from scipy.linalg import solve_triangular
+    rng = np.random.default_rng(12)
+    n = 40
+    X = ar1_x(rng, 120, n, 0.6)
+    X[:, 3] *= 20
+    Hd, _ = O.damp_hessian(O.hessian(X), 0.01)
+    U = O.chol_inverse_upper(Hd)
+    assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
+    assert np.max(np.abs(U.T @ U @ Hd - np.eye(n))) < 1e-10
+    # reverse-order route: H = Ut Ut^T with Ut upper (Cholesky of the index-reversed matrix),
+    # then U = Ut^-1 by a triangular solve
+    Lr = np.linalg.cholesky(Hd[::-1, ::-1])
+    Ut = Lr[::-1, ::-1]
+    assert np.all(np.tril(Ut, -1) == 0)
+    U2 = solve_triangular(Ut, np.eye(n), lower=False)
+    assert np.max(np.abs(U2 - U)) <= 1e-11 * np.max(np.abs(U))
+
+
+def test_not_positive_definite_pivot():
+    with pytest.raises(O.NotPositiveDefinite) as e:
+        O.chol_inverse_upper(np.zeros((5, 5)))
+    assert e.value.pivot == 4
+    with pytest.raises(O.NotPositiveDefinite) as e:
+        O.chol_inverse_upper(np.diag([1.0, 1.0, -1.0, 1.0]))
+    assert e.value.pivot == 2
+    Hd, lam = O.damp_hessian(np.zeros((4, 4)), 0.01)
+    assert lam == 0.0
+    with pytest.raises(O.NotPositiveDefinite):
+        O.chol_inverse_upper(Hd)
+
+
+# ---------------------------------------------------------------------------------- p10 / R3 / R4
+def test_hessian_brute_force_and_trace():
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((5, 3))
+    H = O.hessian([X[:2], X[2:]])
+    for i in range(3):
+        for j in range(3):
+            assert abs(H[i, j] - 2 * sum(X[t, i] * X[t, j] for t in range(5))) < 1e-13
+    Xb = rng.standard_normal((500, 30))
+    Hb = O.hessian(Xb)
+    assert np.array_equal(Hb, Hb.T)
+    assert abs(np.trace(Hb) - 2 * np.sum(Xb * Xb)) < 1e-10 * np.trace(Hb)
+
+
+def test_damping_closed_form():
+    H = np.diag([1.0, 2.0, 3.0])
+    H[0, 2] = H[2, 0] = 0.5
+    Hd, lam = O.damp_hessian(H, 0.01)
+    assert lam == pytest.approx(0.02, abs=1e-15)
+    assert np.allclose(Hd, H + 0.02 * np.eye(3), atol=1e-15, rtol=0)
+
+
+# ---------------------------------------------------------------------------------- p11
+def test_hessian_scale_invariance_bit_exact():
+    rng = np.random.default_rng(14)
+    n, m = 64, 32
+    X = ar1_x(rng, 256, n, 0.8)
+    W = rng.normal(0, 0.02, size=(m, n))
+    a, *_ = gptq_full(W, X, 4, 16, 16, 0.01)
+    b, *_ = gptq_full(W, 2 * X, 4, 16, 16, 0.01)          # H -> 4 H
+    assert np.array_equal(a["codes"], b["codes"])
+    assert np.array_equal(a["scales"], b["scales"])
+
+
+# ---------------------------------------------------------------------------------- p12 / R9
+def test_act_order_perm_closed_form():
+    H = np.diag([3.0, 5.0, 5.0, 1.0])
+    assert O.act_order_perm(H).tolist() == [1, 2, 0, 3]
+
+
+def test_act_order_identity_when_sorted_and_g_idx_round_trip():
+    rng = np.random.default_rng(15)
+    n, m = 64, 24
+    X = ar1_x(rng, 300, n, 0.5)
+    X = X[:, np.argsort(-np.sum(X * X, axis=0), kind="stable")]    # diag H already descending
+    W = rng.normal(0, 0.02, size=(m, n))
+    a, *_ = gptq_full(W, X, 4, 16, 16, 0.01, act_order=False)
+    b, H, Hd, U = gptq_full(W, X, 4, 16, 16, 0.01, act_order=True)
+    assert O.act_order_perm(Hd).tolist() == list(range(n))
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+    assert b["g_idx"].tolist() == [c // 16 for c in range(n)]
+    # a real permutation: g_idx maps each original column to the group it was processed in
+    X2 = ar1_x(rng, 300, n, 0.5) * rng.uniform(0.5, 3, n)[None, :]
+    c, H2, Hd2, U2 = gptq_full(W, X2, 4, 16, 16, 0.01, act_order=True)
+    perm = O.act_order_perm(Hd2)
+    pos = np.empty(n, int)
+    pos[perm] = np.arange(n)
+    assert np.array_equal(c["g_idx"], pos // 16)
+    Wh = O.dequant(c["codes"], c["scales"], 16, g_idx=c["g_idx"])
+    assert np.array_equal(Wh, c["What"])
+    assert np.array_equal(Wh[:, perm], O.dequant(c["codes"][:, perm], c["scales"], 16))
+
+
+# ---------------------------------------------------------------------------------- dequant rounding
+def test_dequant_rounds_once():
+    s = np.array([[0.0999755859375]], dtype=np.float16)     # fp16(0.1)
+    codes = np.array([[3, -7, 5, 0]], dtype=np.int8)
+    out16 = O.dequant(codes, s, 0, out_dtype=np.float16)
+    exact = [Fraction(float(s[0, 0])) * int(c) for c in codes[0]]
+    for got, ex in zip(out16[0], exact):
+        assert Fraction(float(got)) == _rne_to_precision(ex, 11, -14)
+    out32 = O.dequant(codes, s, 0, out_dtype=np.float32)
+    assert [Fraction(float(v)) for v in out32[0]] == exact
