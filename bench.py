@@ -1,0 +1,232 @@
+"""Throughput of the layer-wise quantization path on one MI355X.
+
+One step = every step of the path for every layer of the workload, on inputs already
+resident in HBM: Hessian from X, damping, [act-order], H^-1 factor, GPTQ (INT4 packed +
+fp16 scales), RTN, dequant of the GPTQ result, and the reconstruction MSE of both.
+The value is weights quantized per second (sum of d_out * d_in over the layers / step).
+
+Prints ONE JSON line.  Per-call durations are taken with HIP events on the stream the
+kernels run on (torch's current stream, which the binding passes to libpwq).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GPTQ INT4-g128 weights quantized/s per layer; XᵀX+update MFMA util"
+PEAK = {"hbm": 8000.0, "mfma_f32": 157.3, "mfma_bf16": 2500.0}   # GB/s, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt2_block")
+    ap.add_argument("--layers", default="", help="comma-separated layer names (default: all)")
+    ap.add_argument("--act-order", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", default="", help="layers the oracle baseline runs (default: all)")
+    return ap.parse_args()
+
+
+class Layer:
+    """Device-resident inputs and preallocated outputs of one layer."""
+
+    def __init__(self, spec, torch, pwq, synth, act_order):
+        import numpy as np
+        self.spec = spec
+        dev = "cuda:0"
+        W = synth.weight(spec)
+        X = synth.x_full(spec, threads=16)
+        self.W = torch.from_numpy(W).to(dev)
+        if spec.x_dtype == synth.BF16:
+            self.X = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            self.X = torch.from_numpy(X).to(dev)
+        n, m = spec.d_in, spec.d_out
+        self.H = torch.empty((n, n), dtype=torch.float32, device=dev)
+        self.U = torch.empty((n, n), dtype=torch.float32, device=dev)
+        self.info = torch.empty(1, dtype=torch.int32, device=dev)
+        self.gq = {}
+        self.rq = {}
+        self.what = torch.empty((m, n), dtype=torch.float16, device=dev)
+        self.mse = torch.empty(2, dtype=torch.float64, device=dev)
+        self.act = act_order
+        del X, W
+
+
+def run_step(L, pwq, timers=None):
+    """One pass of the whole path over one layer.  timers: dict name -> list of (start, end) events."""
+    import torch
+    s = L.spec
+
+    def t(name):
+        if timers is None:
+            return None
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        timers.setdefault(name, []).append([e0, None])
+        return name
+
+    def done(name):
+        if name is None:
+            return
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        timers[name][-1][1] = e1
+
+    k = t("hessian_accumulate"); L.H.zero_(); pwq.hessian_accumulate(L.X, L.H); done(k)
+    k = t("hessian_damp"); pwq.hessian_damp(L.H, s.damp); done(k)
+    perm = None
+    if L.act:
+        k = t("act_order_perm"); perm = pwq.act_order_perm(L.H); done(k)
+    k = t("chol_inverse_upper"); pwq.chol_inverse_upper(L.H, perm, U=L.U, info=L.info); done(k)
+    k = t("gptq_quantize_layer")
+    pwq.gptq_quantize_layer(L.W, L.U, L.info, s.bits, s.group_size, s.block_size, perm=perm, want_codes=False,
+                            want_packed=True, out=L.gq)
+    done(k)
+    k = t("rtn_quantize"); pwq.rtn_quantize(L.W, s.bits, s.group_size, want_codes=False, out=L.rq); done(k)
+    k = t("dequant"); pwq.dequant(L.gq["scales"], s.d_in, s.bits, s.group_size, packed=L.gq["packed"],
+                                  g_idx=L.gq.get("g_idx"), out=L.what); done(k)
+    k = t("recon_mse")
+    pwq.recon_mse(L.X, L.W, L.gq["scales"], s.bits, s.group_size, packed=L.gq["packed"], g_idx=L.gq.get("g_idx"), mse=L.mse[0:1])
+    pwq.recon_mse(L.X, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"], mse=L.mse[1:2])
+    done(k)
+
+
+def work_of(name, spec):
+    """(bound, algorithmic amount per call, unit) of one library call on one layer."""
+    m, n, N = spec.d_out, spec.d_in, spec.n_tok
+    xb = 4 if spec.x_dtype == "f32" else 2
+    wb = 4 if spec.w_dtype == "f32" else 2
+    ng = 1 if spec.group_size == 0 else -(-n // spec.group_size)
+    if name == "hessian_accumulate":
+        return ("mfma_bf16" if xb == 2 else "mfma_f32"), N * n * (n + 1), "flop"
+    if name == "chol_inverse_upper":
+        return "mfma_f32", 2 * n ** 3 / 3, "flop"
+    if name == "gptq_quantize_layer":
+        return "mfma_f32", m * n * (n - spec.block_size) + m * n * (spec.block_size - 1), "flop"
+    if name == "recon_mse":
+        return "mfma_f32", 2 * (2 * N * n * m), "flop"
+    if name == "rtn_quantize":
+        return "hbm", m * n * wb + m * n // 2 + 2 * m * ng, "byte"
+    if name == "dequant":
+        return "hbm", m * n // 2 + 2 * m * ng + 2 * m * n, "byte"
+    return "hbm", 0, "byte"
+
+
+def cpu_baseline(specs, synth, budget_layers):
+    """The oracle, as it stands, on one full step of the selected layers."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    weights = 0
+    for s in specs:
+        if budget_layers and s.name not in budget_layers:
+            continue
+        W = synth.weight(s)
+        X = synth.x_full(s)
+        X64 = synth.as_f64(X, s.x_dtype)
+        r = O.quantize_layer(W, [X64], s.bits, s.group_size, s.block_size, s.damp, False)
+        O.dequant(r["codes"], r["scales"], s.group_size, g_idx=r["g_idx"], out_dtype=np.float16)
+        weights += s.n_weights
+    dt = time.perf_counter() - t0
+    names = [s.name for s in specs if not budget_layers or s.name in budget_layers]
+    return {"value": weights / dt, "unit": "weights/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one full step of layers {','.join(names)} in float64 numpy ({dt:.1f} s)"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py: this build measures one GPU; multi-GPU runs are not supported (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from post_weight_quantization_27_amd import pwq, synth
+    pwq.lib()
+    specs = synth.workload(a.workload)
+    if a.layers:
+        keep = set(a.layers.split(","))
+        specs = [s for s in specs if s.name in keep]
+    layers = [Layer(s, torch, pwq, synth, a.act_order) for s in specs]
+    torch.cuda.synchronize()
+
+    for _ in range(a.warmup):
+        for L in layers:
+            run_step(L, pwq)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, no per-call events (they would add records between launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        for L in layers:
+            run_step(L, pwq)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / a.steps
+
+    # per-call durations: the same steps again with events around every call
+    timers = [dict() for _ in layers]
+    for _ in range(a.steps):
+        for L, T in zip(layers, timers):
+            run_step(L, pwq, T)
+    torch.cuda.synchronize()
+    per = {}
+    for L, T in zip(layers, timers):
+        for name, ev in T.items():
+            d = sum(x[0].elapsed_time(x[1]) for x in ev) / len(ev)
+            per[(L.spec.name, name)] = d
+    breakdown = {}
+    for (lname, name), d in per.items():
+        breakdown[name] = breakdown.get(name, 0.0) + d
+    dom = max(per.items(), key=lambda kv: kv[1])
+    (dl, dn), dms = dom
+    dspec = next(L.spec for L in layers if L.spec.name == dl)
+    bound, amount, unit = work_of(dn, dspec)
+    achieved = amount / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
+    peak = PEAK[bound]
+    roof = {"bound": "hbm" if bound == "hbm" else "mfma", "kernel": f"pwq_{dn}", "layer": dl,
+            "achieved": round(achieved, 3), "peak": peak, "unit": "GB/s" if unit == "byte" else "TFLOP/s",
+            "frac": round(achieved / peak, 5), "traffic": None, "launch_ms": round(dms, 4),
+            "algorithmic": amount}
+    mses = {L.spec.name: [float(x) for x in L.mse.cpu().tolist()] for L in layers}
+
+    weights = sum(s.n_weights for s in specs)
+    value = weights / (ms * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "weights/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if specs[0].x_dtype == "f32" else "bf16-in/f32-acc",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "layers": [f"{s.name}:{s.d_in}->{s.d_out}" for s in specs],
+                   "n_tok": specs[0].n_tok, "bits": specs[0].bits, "group_size": specs[0].group_size,
+                   "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order)},
+        "roofline": roof,
+        "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
+        "mse_gptq_rtn": mses,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not a.no_cpu_baseline:
+        cl = set(a.cpu_layers.split(",")) if a.cpu_layers else set()
+        out["cpu_baseline"] = cpu_baseline(specs, synth, cl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * pwq.h - layer-wise post-training weight quantization (RTN and GPTQ) on gfx950.
+ *
+ * C ABI of libpwq.so.  Every compute call enqueues hand-written HIP kernels on the
+ * caller's stream and returns without synchronising.
+ *
+ * Conventions shared by all calls
+ * -------------------------------
+ *  - Matrices are row-major.  W is d_out x d_in (one row per output channel), X is
+ *    n_tok x d_in (one row per calibration token), H and U are d_in x d_in.
+ *  - Pointers are DEVICE pointers unless the comment says "host".
+ *  - Leading dimensions (ldx, ldw) are in elements and must be >= d_in.
+ *  - Float16 values (scales) travel as their raw 16-bit patterns in uint16_t.
+ *    bfloat16 X travels as raw 16-bit patterns as well (pwq_dtype PWQ_BF16).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *  - The caller owns and allocates every buffer: inputs, outputs and a workspace of
+ *    at least the size the matching *_workspace_size call returns.  The library
+ *    allocates no device memory and keeps no per-call state, so calls on different
+ *    streams with disjoint buffers may run concurrently.
+ *  - Every call checks its arguments on the host first.  On any return other than
+ *    PWQ_OK nothing has been enqueued, except PWQ_EHIP, which reports a launch
+ *    failure after earlier kernels of the same call may already be queued.
+ *  - A numerically failed factorisation (H not positive definite) is not a return
+ *    code: it is written to the device int32 `info` (see pwq_chol_inverse_upper).
+ *  - Empty inputs (n_tok == 0, d_out == 0) are valid and enqueue nothing, except
+ *    that pwq_recon_mse writes 0 to *mse.
+ *
+ * Sources of the method (page title, then section):
+ *  [GPT2-RE]  "GPT-2 Quantization Reconstruction Error" - "What this project does", "Setup".
+ *  [MQM]      "Model Quantization Mechanics: Precision Reduction and Weight Formatting" -
+ *             1 "Affine Quantization", "Group-wise Quantization"; 2.1 "GPTQ".
+ *  [GPTQ-P]   "GPTQ: Post-Training INT4" - "OBQ Foundation", "Hessian-Based Weight Update",
+ *             "The GPTQ Algorithm", "Group Quantization", "Running GPTQ with AutoGPTQ".
+ */
+#ifndef PWQ_H
+#define PWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PWQ_ABI_VERSION 1
+
+typedef enum pwq_status {
+    PWQ_OK = 0,
+    PWQ_EINVAL = 1,      /* bad pointer, size, stride, bits, group or block size      */
+    PWQ_EDTYPE = 2,      /* dtype not supported by this call                          */
+    PWQ_EWORKSPACE = 3,  /* workspace pointer NULL or smaller than *_workspace_size   */
+    PWQ_EHIP = 4         /* a kernel launch failed; see pwq_last_hip_error()          */
+} pwq_status;
+
+typedef enum pwq_dtype {
+    PWQ_F32 = 0,
+    PWQ_F16 = 1,
+    PWQ_BF16 = 2
+} pwq_dtype;
+
+/* Quantizer settings, the knobs of [GPTQ-P] "Running GPTQ with AutoGPTQ" (bits,
+ * group_size, desc_act) plus the lazy-batch width of [GPTQ-P] "The GPTQ Algorithm".
+ * Symmetric only: codes in [-(2^(bits-1)-1), 2^(bits-1)-1], no zero-point.
+ *   bits        2..8
+ *   group_size  0 = one scale per output row ([GPT2-RE]); else an even number >= 2 of
+ *               consecutive input columns sharing one scale ([MQM] "Group-wise
+ *               Quantization").  For GPTQ, group_size must divide block_size or be a
+ *               multiple of it, so a group never starts inside a block and ends
+ *               after it.
+ *   block_size  GPTQ lazy-batch width B: 32, 64 or 128.
+ *   act_order   nonzero: columns were processed in the order `perm` (desc_act). */
+typedef struct pwq_params {
+    int32_t bits;
+    int32_t group_size;
+    int32_t block_size;
+    int32_t act_order;
+} pwq_params;
+
+/* ABI version (PWQ_ABI_VERSION of the build). */
+int pwq_version(void);
+
+/* Static text for a status code. */
+const char* pwq_status_string(int status);
+
+/* hipError_t of the last PWQ_EHIP on the calling thread (0 if none). */
+int pwq_last_hip_error(void);
+
+/* ------------------------------------------------------------------ Hessian -------
+ * H += 2 * X^T X, summed over the n_tok tokens of this call ([GPTQ-P] "Hessian-Based
+ * Weight Update": H = 2 X X^T with X as d_in x tokens; here X is stored tokens x d_in).
+ * Call it once per token tile to stream a large calibration set; the caller zeroes H
+ * before the first tile.  Both triangles of H are written (full symmetric storage).
+ *   X        n_tok x d_in, x_dtype PWQ_F32 or PWQ_BF16, leading dimension ldx.
+ *   H        d_in x d_in float32, accumulated in place.
+ *   ws       workspace of pwq_hessian_workspace_size(n_tok, d_in, x_dtype) bytes
+ *            (may be 0 bytes; then ws may be NULL).
+ * Products are accumulated in float32 with MFMA; partial sums over token chunks are
+ * added in a fixed order, so repeated calls give bit-identical H. */
+size_t pwq_hessian_workspace_size(int64_t n_tok, int64_t d_in, int x_dtype);
+pwq_status pwq_hessian_accumulate(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                                  float* H, void* ws, size_t ws_bytes, void* stream);
+
+/* H_ii += lambda for every i, lambda = damp * mean(diag H) of the undamped H
+ * (damp_percent of [GPTQ-P] "Running GPTQ with AutoGPTQ"; 0 allowed).
+ *   lambda_out  optional device float receiving lambda (NULL to skip). */
+pwq_status pwq_hessian_damp(float* H, int64_t d_in, float damp, float* lambda_out, void* stream);
+
+/* Act-order (desc_act of [GPTQ-P] "Running GPTQ with AutoGPTQ"): perm[p] = the input
+ * column processed at position p, sorting diag H descending, ties by lower index.
+ *   perm  int32[d_in]. */
+pwq_status pwq_act_order_perm(const float* H, int64_t d_in, int32_t* perm, void* stream);
+
+/* ------------------------------------------------------------------ H^-1 factor ---
+ * U upper triangular with H^-1 = U^T U and U_jj > 0: the Cholesky factor of the
+ * inverse Hessian of [MQM] 2.1 "GPTQ", whose rows drive the column loop.  If perm is
+ * not NULL the factor is of P H P^T, i.e. of H[perm][:, perm].
+ * Computed as H = V V^T (V upper: Cholesky eliminating from the last column to the
+ * first) followed by U = V^-1, so H^-1 is never formed.
+ *   H     n x n float32, read only (only the upper triangle is read).
+ *   U     n x n float32 output; the strictly lower triangle is written as 0.
+ *   info  device int32: 0 on success; k > 0 if the pivot of column k-1 (in the order
+ *         of P H P^T) was not positive, i.e. H is not positive definite.  U is then
+ *         undefined, and pwq_gptq_quantize_layer given this info writes nothing.
+ *   ws    pwq_chol_workspace_size(n) bytes. */
+size_t pwq_chol_workspace_size(int64_t n);
+pwq_status pwq_chol_inverse_upper(const float* H, int64_t n, const int32_t* perm, float* U, int32_t* info,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ GPTQ ----------
+ * The column loop of [GPTQ-P] "The GPTQ Algorithm" with the factor U of
+ * pwq_chol_inverse_upper.  Columns (in processing order) are taken in blocks of
+ * block_size; for each column j of a block: at a group's first column, the scale of
+ * every row is absmax(current values of the group) / qmax, rounded to float32 and then
+ * to float16 (per-row mode: from the original row); code = nearest integer to w / s
+ * (exact quotient, ties to even), clamped to +-qmax; e = (w - s * code) / U_jj;
+ * the block's later columns get w_k -= e * U_jk; after the block every later column
+ * gets W -= Err * U[block, later] in one product.
+ *   W          d_out x d_in, w_dtype PWQ_F32 or PWQ_F16, leading dimension ldw; read only
+ *              (the float32 working copy lives in ws).
+ *   U, info    from pwq_chol_inverse_upper (of the permuted H when act_order).
+ *   params     host pointer.
+ *   perm       int32[d_in] from pwq_act_order_perm; required iff params->act_order.
+ *   scales_in  optional fp16 d_out x n_groups: fixed scales instead of computed ones.
+ *   codes      optional int8 d_out x d_in, in ORIGINAL column order.
+ *   packed     optional uint8 d_out x d_in/2 (bits == 4, d_in even): nibble = code + 8,
+ *              even column in the low nibble ([GPTQ-P] "Group Quantization" storage).
+ *              At least one of codes / packed must be given.
+ *   scales_out fp16 d_out x n_groups (groups in processing order), required.
+ *   g_idx      int32[d_in], group of each original column; required iff act_order.
+ *   ws         pwq_gptq_workspace_size(d_out, d_in, params) bytes. */
+size_t pwq_gptq_workspace_size(int64_t d_out, int64_t d_in, const pwq_params* params);
+pwq_status pwq_gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
+                                   const float* U, const int32_t* info, const pwq_params* params,
+                                   const int32_t* perm, const uint16_t* scales_in,
+                                   int8_t* codes, uint8_t* packed, uint16_t* scales_out, int32_t* g_idx,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ RTN -----------
+ * Round-to-nearest ([GPT2-RE] "What this project does"; [MQM] "Affine Quantization"
+ * with Z = 0 and "Group-wise Quantization"): per row (group_size 0) or per group of
+ * group_size consecutive columns, s = fp16(fp32(absmax / qmax)) from the original W,
+ * code = nearest integer to w / s (exact quotient, ties to even), clamped to +-qmax;
+ * s = 0 gives code 0.  Same output formats as pwq_gptq_quantize_layer (no act-order).
+ *   scales_in optional fixed fp16 scales; scales_out required (copied from scales_in
+ *   when given). */
+pwq_status pwq_rtn_quantize(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
+                            int32_t bits, int32_t group_size, const uint16_t* scales_in,
+                            int8_t* codes, uint8_t* packed, uint16_t* scales_out, void* stream);
+
+/* ------------------------------------------------------------------ dequant -------
+ * What[r, c] = s[r, group(c)] * code[r, c] ([MQM] "Affine Quantization", Z = 0), the
+ * product formed exactly in float32 and rounded once to out_dtype (PWQ_F32, PWQ_F16 or
+ * PWQ_BF16).  group(c) = 0 (group_size 0), g_idx[c] (g_idx given), else c / group_size.
+ * Exactly one of packed (bits 4) / codes is given.  W_out is d_out x d_in, dense. */
+pwq_status pwq_dequant(const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
+                       int64_t d_out, int64_t d_in, int32_t bits, int32_t group_size,
+                       void* W_out, int out_dtype, void* stream);
+
+/* ------------------------------------------------------------------ MSE -----------
+ * Per-layer reconstruction error ([GPT2-RE] "What this project does", step 5; the
+ * objective ||WX - What X||^2 of [GPTQ-P] "OBQ Foundation"):
+ *   mse = sum over tokens t and outputs o of (X (W - What)^T)[t, o]^2 / (n_tok * d_out),
+ * with What decoded on the fly from packed or codes (+ scales, g_idx) as in
+ * pwq_dequant; the product is never written out.  Per-tile sums are added in a fixed
+ * order in float64, so the result is reproducible bit for bit.
+ *   X       n_tok x d_in, x_dtype PWQ_F32 or PWQ_BF16, leading dimension ldx.
+ *   W       d_out x d_in, w_dtype PWQ_F32 or PWQ_F16, leading dimension ldw.
+ *   mse     device double.
+ *   ws      pwq_recon_mse_workspace_size(n_tok, d_in, d_out) bytes. */
+size_t pwq_recon_mse_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out);
+pwq_status pwq_recon_mse(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                         const void* W, int w_dtype, int64_t ldw,
+                         const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
+                         int64_t d_out, int32_t bits, int32_t group_size,
+                         double* mse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PWQ_H */

@@ -1,0 +1,313 @@
+// Tiled float32 MFMA contraction engine for gfx950 (v_mfma_f32_32x32x2_f32).
+//
+//   acc(m, n) = sum_{k in [kbeg, kend)} A(m, k) * B(n, k)
+//
+// A workgroup of 256 threads (4 wave64s in a 2 x 2 grid) owns a BM x BN output tile;
+// each wave owns (BM/2) x (BN/2) as 32 x 32 MFMA blocks.  Operand tiles of BK = 32
+// along k are staged through LDS as [k][m] (m contiguous), so every MFMA operand read
+// is 32 consecutive floats per half-wave.  The next k-tile is fetched into registers
+// while the current one is multiplied.  The operand loaders and the epilogue are
+// policy types, so the same engine serves the Hessian build, the Cholesky and
+// triangular-inverse updates, the GPTQ trailing update and the error GEMM.
+#pragma once
+
+#include "pwq_common.h"
+
+namespace pwq {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int GEMM_THREADS = 256;
+constexpr int GEMM_BK = 32;
+
+// ---------------------------------------------------------------- element access
+// DT: 0 = float32, 1 = float16 bits, 2 = bfloat16 bits.  Values widen exactly to float32.
+template <int DT> struct Elem;
+template <> struct Elem<0> {
+    typedef float T;
+    static __device__ __forceinline__ float get(const T* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ float4 get4(const T* p, int64_t i) { return *(const float4*)(p + i); }
+};
+template <> struct Elem<1> {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float get(const T* p, int64_t i) { return f16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ float4 get4(const T* p, int64_t i) {
+        uint2 u = *(const uint2*)(p + i);
+        return make_float4(f16_bits_to_f32((uint16_t)(u.x & 0xffff)), f16_bits_to_f32((uint16_t)(u.x >> 16)),
+                           f16_bits_to_f32((uint16_t)(u.y & 0xffff)), f16_bits_to_f32((uint16_t)(u.y >> 16)));
+    }
+};
+template <> struct Elem<2> {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float get(const T* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ float4 get4(const T* p, int64_t i) {
+        uint2 u = *(const uint2*)(p + i);
+        return make_float4(__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xffff0000u),
+                           __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xffff0000u));
+    }
+};
+
+// ---------------------------------------------------------------- operand loaders
+// Element (m, k) stored at p[k * ld + m]: rows of k, m contiguous.
+template <int DT = 0>
+struct OpKMajor {
+    static constexpr int PAD = 4;
+    typedef typename Elem<DT>::T T;
+    const T* p;
+    int64_t ld, M, K;
+    int vec;            // ld % 4 == 0 and p aligned to 4 elements
+
+    template <int BM>
+    struct Regs { float4 v[BM * GEMM_BK / (4 * GEMM_THREADS)]; };
+
+    template <int BM>
+    __device__ __forceinline__ void load(Regs<BM>& r, int64_t m0, int64_t k0, int tid) const {
+        constexpr int NV = BM * GEMM_BK / (4 * GEMM_THREADS);
+        constexpr int PER_ROW = BM / 4;
+        const bool full = vec && (m0 + BM <= M) && (k0 + GEMM_BK <= K);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            int idx = tid + i * GEMM_THREADS;
+            int kr = idx / PER_ROW, mc = (idx % PER_ROW) * 4;
+            int64_t k = k0 + kr, m = m0 + mc;
+            if (full) {
+                r.v[i] = Elem<DT>::get4(p, k * ld + m);
+            } else {
+                float t[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) t[c] = (k < K && m + c < M) ? Elem<DT>::get(p, k * ld + m + c) : 0.f;
+                r.v[i] = make_float4(t[0], t[1], t[2], t[3]);
+            }
+        }
+    }
+    template <int BM>
+    __device__ __forceinline__ void store(float* S, const Regs<BM>& r, int tid) const {
+        constexpr int NV = BM * GEMM_BK / (4 * GEMM_THREADS);
+        constexpr int PER_ROW = BM / 4;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            int idx = tid + i * GEMM_THREADS;
+            int kr = idx / PER_ROW, mc = (idx % PER_ROW) * 4;
+            *(float4*)(S + kr * (BM + PAD) + mc) = r.v[i];
+        }
+    }
+};
+
+// Element (m, k) stored at p[m * ld + k]: rows of m, k contiguous (transposed into LDS).
+template <int DT = 0>
+struct OpMMajor {
+    static constexpr int PAD = 1;
+    typedef typename Elem<DT>::T T;
+    const T* p;
+    int64_t ld, M, K;
+    int vec;
+
+    template <int BM>
+    struct Regs { float4 v[BM * GEMM_BK / (4 * GEMM_THREADS)]; };
+
+    template <int BM>
+    __device__ __forceinline__ void load(Regs<BM>& r, int64_t m0, int64_t k0, int tid) const {
+        constexpr int NV = BM * GEMM_BK / (4 * GEMM_THREADS);
+        constexpr int PER_ROW = GEMM_BK / 4;
+        const bool full = vec && (m0 + BM <= M) && (k0 + GEMM_BK <= K);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            int idx = tid + i * GEMM_THREADS;
+            int mr = idx / PER_ROW, kc = (idx % PER_ROW) * 4;
+            int64_t m = m0 + mr, k = k0 + kc;
+            if (full) {
+                r.v[i] = Elem<DT>::get4(p, m * ld + k);
+            } else {
+                float t[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) t[c] = (m < M && k + c < K) ? Elem<DT>::get(p, m * ld + k + c) : 0.f;
+                r.v[i] = make_float4(t[0], t[1], t[2], t[3]);
+            }
+        }
+    }
+    template <int BM>
+    __device__ __forceinline__ void store(float* S, const Regs<BM>& r, int tid) const {
+        constexpr int NV = BM * GEMM_BK / (4 * GEMM_THREADS);
+        constexpr int PER_ROW = GEMM_BK / 4;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            int idx = tid + i * GEMM_THREADS;
+            int mr = idx / PER_ROW, kc = (idx % PER_ROW) * 4;
+            S[(kc + 0) * (BM + PAD) + mr] = r.v[i].x;
+            S[(kc + 1) * (BM + PAD) + mr] = r.v[i].y;
+            S[(kc + 2) * (BM + PAD) + mr] = r.v[i].z;
+            S[(kc + 3) * (BM + PAD) + mr] = r.v[i].w;
+        }
+    }
+};
+
+// ---------------------------------------------------------------- tile maps
+struct Tile {
+    int64_t m0, n0, kbeg, kend;
+    int split, tile;
+};
+
+// Rectangular grid of BM x BN tiles over M x N, times `splits` chunks of k.
+// tri_k: the k range of a tile starts at its m0 (A upper triangular: A(m, k) = 0, k < m).
+struct RectMap {
+    int64_t M, N, K;
+    int tiles_m, tiles_n, splits;
+    int64_t kchunk;
+    int tri_k;
+    const int32_t* guard;     // optional: skip all work when *guard != 0
+    __device__ __forceinline__ bool get(int bid, int BM, int BN, Tile& t) const {
+        int ntile = tiles_m * tiles_n;
+        t.split = bid / ntile;
+        t.tile = bid % ntile;
+        int ti = t.tile % tiles_m, tj = t.tile / tiles_m;
+        t.m0 = (int64_t)ti * BM;
+        t.n0 = (int64_t)tj * BN;
+        t.kbeg = (int64_t)t.split * kchunk;
+        t.kend = t.kbeg + kchunk < K ? t.kbeg + kchunk : K;
+        if (tri_k && t.kbeg < t.m0) t.kbeg = (t.m0 / GEMM_BK) * GEMM_BK;
+        return t.kbeg < t.kend;
+    }
+};
+
+// Upper-triangular tile pairs (ti <= tj) of an N x N output, times `splits` k chunks.
+struct UpperMap {
+    int64_t N, K;
+    int tiles, splits;
+    int64_t kchunk;
+    const int32_t* guard;
+    __device__ __forceinline__ bool get(int bid, int BM, int BN, Tile& t) const {
+        int ntile = tiles * (tiles + 1) / 2;
+        t.split = bid / ntile;
+        t.tile = bid % ntile;
+        int r = t.tile, ti = 0;
+        while (r >= tiles - ti) { r -= tiles - ti; ++ti; }
+        int tj = ti + r;
+        t.m0 = (int64_t)ti * BM;
+        t.n0 = (int64_t)tj * BN;
+        t.kbeg = (int64_t)t.split * kchunk;
+        t.kend = t.kbeg + kchunk < K ? t.kbeg + kchunk : K;
+        return t.kbeg < t.kend;
+    }
+};
+
+// ---------------------------------------------------------------- the tile engine
+// Epilogue interface:
+//   __device__ void element(const Tile&, int64_t row, int64_t col, float v)  for every
+//       output element of the tile (row < m-extent and col < n-extent checked by the epilogue)
+//   __device__ void finish(const Tile&, int tid, bool valid)  once per thread at the end
+//       (valid = false: the tile had an empty k range and no element() calls were made).
+// Host side guarantees: kchunk and every kbeg are multiples of GEMM_BK.
+template <int BM, int BN, class LA, class LB>
+struct GemmLds {
+    static constexpr int A_FLOATS = GEMM_BK * (BM + LA::PAD);
+    static constexpr int B_FLOATS = GEMM_BK * (BN + LB::PAD);
+    static constexpr int FLOATS = A_FLOATS + B_FLOATS;
+};
+
+template <int BM, int BN, class LA, class LB, class EPI>
+__device__ __forceinline__ void gemm_tile(const LA& la, const LB& lb, const Tile& t, EPI& epi, float* lds) {
+    constexpr int FM = BM / 64, FN = BN / 64;
+    float* As = lds;
+    float* Bs = lds + GemmLds<BM, BN, LA, LB>::A_FLOATS;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    typename LA::template Regs<BM> ra;
+    typename LB::template Regs<BN> rb;
+    la.template load<BM>(ra, t.m0, t.kbeg, tid);
+    lb.template load<BN>(rb, t.n0, t.kbeg, tid);
+
+    for (int64_t k0 = t.kbeg; k0 < t.kend; k0 += GEMM_BK) {
+        __syncthreads();
+        la.template store<BM>(As, ra, tid);
+        lb.template store<BN>(Bs, rb, tid);
+        __syncthreads();
+        if (k0 + GEMM_BK < t.kend) {
+            la.template load<BM>(ra, t.m0, k0 + GEMM_BK, tid);
+            lb.template load<BN>(rb, t.n0, k0 + GEMM_BK, tid);
+        }
+        // kbeg and every split boundary are multiples of GEMM_BK, so a k-tile never
+        // reaches into the next chunk; past K both operands are zero-filled.
+#pragma unroll 4
+        for (int kk = 0; kk < GEMM_BK; kk += 2) {
+            float a[FM], b[FN];
+            const int kr = kk + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i] = As[kr * (BM + LA::PAD) + wm * (BM / 2) + i * 32 + (lane & 31)];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = Bs[kr * (BN + LB::PAD) + wn * (BN / 2) + j * 32 + (lane & 31)];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                int64_t row = t.m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+                epi.element(t, row, col, acc[i][j][v]);
+            }
+}
+
+template <int BM, int BN, class LA, class LB, class MAP, class EPI>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_f32_kernel(LA la, LB lb, MAP map, EPI epi) {
+    if (map.guard && *map.guard != 0) return;
+    __shared__ __attribute__((aligned(16))) float lds[GemmLds<BM, BN, LA, LB>::FLOATS];
+    Tile t;
+    if (!map.get((int)blockIdx.x, BM, BN, t)) {
+        epi.finish(t, threadIdx.x, false);
+        return;
+    }
+    gemm_tile<BM, BN>(la, lb, t, epi, lds);
+    epi.finish(t, threadIdx.x, true);
+}
+
+// One launch, two independent tile tasks: blocks [0, n1) run task a, the rest task b.
+template <int BM_, int BN_, class LA_, class LB_, class MAP_, class EPI_>
+struct GemmTask {
+    static constexpr int BM = BM_, BN = BN_;
+    typedef LA_ LA;
+    typedef LB_ LB;
+    LA_ la;
+    LB_ lb;
+    MAP_ map;
+    EPI_ epi;
+    static constexpr int LDS = GemmLds<BM_, BN_, LA_, LB_>::FLOATS;
+    __device__ __forceinline__ void run(int bid, float* lds) {
+        Tile t;
+        if (!map.get(bid, BM, BN, t)) {
+            epi.finish(t, threadIdx.x, false);
+            return;
+        }
+        gemm_tile<BM, BN>(la, lb, t, epi, lds);
+        epi.finish(t, threadIdx.x, true);
+    }
+};
+
+template <class TA, class TB>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_f32_dual_kernel(TA a, TB b, int n1, const int32_t* guard) {
+    if (guard && *guard != 0) return;
+    constexpr int L = TA::LDS > TB::LDS ? TA::LDS : TB::LDS;
+    __shared__ __attribute__((aligned(16))) float lds[L];
+    if ((int)blockIdx.x < n1) a.run((int)blockIdx.x, lds);
+    else b.run((int)blockIdx.x - n1, lds);
+}
+
+}  // namespace pwq

@@ -1,0 +1,184 @@
+// Hessian of the layer objective, H = 2 X^T X summed over calibration tokens
+// ("GPTQ: Post-Training INT4", section "Hessian-Based Weight Update"), its damping by
+// damp * mean(diag H) and the act-order permutation (desc_act of the same page,
+// section "Running GPTQ with AutoGPTQ").
+//
+// The contraction runs on the float32 MFMA engine over the upper-triangular tiles of H
+// only.  Small d_in gives few tiles, so the token range is cut into chunks whose partial
+// tiles land in a workspace and are summed in a fixed order (bit-reproducible, no
+// atomics).  A last pass copies the upper triangle onto the lower one.
+#include "gemm_f32.h"
+#include "pwq_internal.h"
+
+namespace pwq {
+
+namespace {
+
+// split > 1: partial tile of chunk `split` -> ws[split][tile][BM*BN]
+// split == 1: H[row][col] += 2 * acc directly (upper tiles only; diagonal tiles whole)
+struct EpiHess {
+    float* H;
+    float* part;
+    int64_t n;
+    int ntile, bm, direct;
+    __device__ __forceinline__ void element(const Tile& t, int64_t row, int64_t col, float v) {
+        if (direct) {
+            if (row < n && col < n) H[row * n + col] += 2.f * v;
+        } else {
+            int64_t lr = row - t.m0, lc = col - t.n0;
+            part[((int64_t)t.split * ntile + t.tile) * (int64_t)(bm * bm) + lr * bm + lc] = v;
+        }
+    }
+    __device__ __forceinline__ void finish(const Tile&, int, bool) {}
+};
+
+// H[tile] += 2 * sum_s part[s][tile], s in increasing order.
+// grid: x = 1024-element chunk of a tile, y = upper tile index
+__global__ __launch_bounds__(256) void hess_reduce_kernel(const float* __restrict__ part, float* __restrict__ H,
+                                                          int64_t n, int tiles, int splits, int bm) {
+    const int ntile = tiles * (tiles + 1) / 2;
+    const int tile = blockIdx.y;
+    int r = tile, ti = 0;
+    while (r >= tiles - ti) { r -= tiles - ti; ++ti; }
+    const int tj = ti + r;
+    const int64_t per_tile = (int64_t)bm * bm;
+    const int64_t le = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
+    if (le >= per_tile) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < splits; ++sp) {
+        const float4 v = *(const float4*)(part + ((int64_t)sp * ntile + tile) * per_tile + le);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const int64_t row = (int64_t)ti * bm + le / bm, col = (int64_t)tj * bm + le % bm;
+    if (row >= n) return;
+    const float a[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (col + c < n) H[row * n + col + c] += 2.f * a[c];
+}
+
+// lower triangle := upper triangle, 32 x 32 blocks through LDS (coalesced both ways)
+__global__ __launch_bounds__(256) void mirror_upper_kernel(float* __restrict__ H, int64_t n) {
+    __shared__ float tile[32][33];
+    const int64_t nb = cdiv(n, 32);
+    // blockIdx.x enumerates block pairs bi <= bj
+    int64_t r = blockIdx.x, bi = 0;
+    while (r >= nb - bi) { r -= nb - bi; ++bi; }
+    const int64_t bj = bi + r;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+    for (int k = ty; k < 32; k += 8) {
+        int64_t i = bi * 32 + k, j = bj * 32 + tx;
+        tile[k][tx] = (i < n && j < n) ? H[i * n + j] : 0.f;
+    }
+    __syncthreads();
+    for (int k = ty; k < 32; k += 8) {
+        int64_t i = bj * 32 + k, j = bi * 32 + tx;      // target H[i][j] = H[j][i], i > j
+        if (i < n && j < n && i > j) H[i * n + j] = tile[tx][k];
+    }
+}
+
+__global__ __launch_bounds__(256) void damp_kernel(float* __restrict__ H, int64_t n, float damp, float* lambda_out) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 256) s += (double)H[i * n + i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    const float lam = (float)((double)damp * (red[0] / (double)n));
+    for (int64_t i = threadIdx.x; i < n; i += 256) H[i * n + i] += lam;
+    if (threadIdx.x == 0 && lambda_out) *lambda_out = lam;
+}
+
+// rank of column i in the descending order of diag H, ties by lower index: a stable,
+// comparison-count sort (each rank is unique, so perm[rank] = i fills perm exactly).
+__global__ __launch_bounds__(256) void act_order_kernel(const float* __restrict__ H, int64_t n, int32_t* __restrict__ perm) {
+    __shared__ float d[1024];
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const float di = i < n ? H[i * n + i] : 0.f;
+    int64_t rank = 0;
+    for (int64_t j0 = 0; j0 < n; j0 += 1024) {
+        __syncthreads();
+        for (int t = threadIdx.x; t < 1024; t += 256) d[t] = (j0 + t < n) ? H[(j0 + t) * n + (j0 + t)] : 0.f;
+        __syncthreads();
+        const int lim = (int)((n - j0) < 1024 ? (n - j0) : 1024);
+        for (int t = 0; t < lim; ++t) {
+            const float dj = d[t];
+            rank += (dj > di) || (dj == di && (j0 + t) < i);
+        }
+    }
+    if (i < n) perm[rank] = (int32_t)i;
+}
+
+template <int BM, int DT>
+hipError_t hess_gemm(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, float* part, const HessPlan& pl,
+                     hipStream_t s) {
+    typedef typename Elem<DT>::T T;
+    OpKMajor<DT> op{(const T*)X, ldx, n, n_tok, (int)((ldx % 4 == 0) && aligned(X, 4 * sizeof(T)))};
+    UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr};
+    const int ntile = pl.tiles * (pl.tiles + 1) / 2;
+    EpiHess epi{H, part, n, ntile, BM, pl.splits == 1};
+    hipLaunchKernelGGL((gemm_f32_kernel<BM, BM, OpKMajor<DT>, OpKMajor<DT>, UpperMap, EpiHess>),
+                       dim3(ntile * pl.splits), dim3(GEMM_THREADS), 0, s, op, op, map, epi);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+HessPlan hessian_plan(int64_t n_tok, int64_t d_in) {
+    HessPlan p{};
+    p.bm = d_in <= 1024 ? 64 : 128;
+    p.tiles = (int)cdiv(d_in, p.bm);
+    const int ntile = p.tiles * (p.tiles + 1) / 2;
+    const int64_t ksteps = cdiv(n_tok, GEMM_BK);
+    const int target = 1024;                         // >= 4 workgroups per CU of 256
+    int64_t splits = ntile >= target ? 1 : cdiv(target, ntile);
+    const int64_t max_splits = ksteps / 8 > 1 ? ksteps / 8 : 1;   // >= 256 tokens per chunk
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    p.kchunk = cdiv(ksteps, splits) * GEMM_BK;
+    p.splits = (int)cdiv(n_tok, p.kchunk);
+    if (p.splits < 1) p.splits = 1;
+    p.ws_bytes = p.splits > 1 ? (size_t)p.splits * ntile * p.bm * p.bm * sizeof(float) : 0;
+    return p;
+}
+
+hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* H, void* ws,
+                          hipStream_t s) {
+    if (n_tok == 0 || d_in == 0) return hipSuccess;
+    const HessPlan pl = hessian_plan(n_tok, d_in);
+    float* part = (float*)ws;
+    hipError_t e;
+    if (x_dtype == 0) {
+        e = pl.bm == 64 ? hess_gemm<64, 0>(X, n_tok, d_in, ldx, H, part, pl, s) : hess_gemm<128, 0>(X, n_tok, d_in, ldx, H, part, pl, s);
+    } else {
+        e = pl.bm == 64 ? hess_gemm<64, 2>(X, n_tok, d_in, ldx, H, part, pl, s) : hess_gemm<128, 2>(X, n_tok, d_in, ldx, H, part, pl, s);
+    }
+    if (e != hipSuccess) return e;
+    if (pl.splits > 1) {
+        const int ntile = pl.tiles * (pl.tiles + 1) / 2;
+        const unsigned chunks = (unsigned)cdiv((int64_t)pl.bm * pl.bm, 1024);
+        hipLaunchKernelGGL(hess_reduce_kernel, dim3(chunks, (unsigned)ntile), dim3(256), 0, s, part, H, d_in, pl.tiles,
+                           pl.splits, pl.bm);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int64_t nb = cdiv(d_in, 32);
+    hipLaunchKernelGGL(mirror_upper_kernel, dim3((unsigned)(nb * (nb + 1) / 2)), dim3(256), 0, s, H, d_in);
+    return hipGetLastError();
+}
+
+hipError_t damp_launch(float* H, int64_t n, float damp, float* lambda_out, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, s, H, n, damp, lambda_out);
+    return hipGetLastError();
+}
+
+hipError_t act_order_launch(const float* H, int64_t n, int32_t* perm, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(act_order_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, H, n, perm);
+    return hipGetLastError();
+}
+
+}  // namespace pwq

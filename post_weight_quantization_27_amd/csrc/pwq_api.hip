@@ -1,0 +1,188 @@
+// C ABI of libpwq: argument checks on the host, then the kernel launchers.
+// Every check runs before the first HIP call, so a rejected call enqueues nothing.
+#include <math.h>
+
+#include "../../include/pwq.h"
+#include "pwq_internal.h"
+
+using namespace pwq;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+pwq_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return PWQ_OK;
+    g_last_hip_error = (int)e;
+    return PWQ_EHIP;
+}
+
+constexpr int64_t MAX_DIM = (int64_t)1 << 30;
+
+bool bad_dim(int64_t v) { return v < 0 || v > MAX_DIM; }
+
+bool group_ok(int32_t g, int64_t d_in) {
+    (void)d_in;
+    return g == 0 || (g >= 2 && g % 2 == 0);
+}
+
+int64_t n_groups(int64_t d_in, int32_t g) { return g == 0 ? 1 : cdiv(d_in, g); }
+
+}  // namespace
+
+extern "C" {
+
+int pwq_version(void) { return PWQ_ABI_VERSION; }
+
+const char* pwq_status_string(int status) {
+    switch (status) {
+        case PWQ_OK: return "ok";
+        case PWQ_EINVAL: return "invalid argument";
+        case PWQ_EDTYPE: return "unsupported dtype";
+        case PWQ_EWORKSPACE: return "workspace missing or too small";
+        case PWQ_EHIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+int pwq_last_hip_error(void) { return g_last_hip_error; }
+
+// ------------------------------------------------------------------ Hessian
+size_t pwq_hessian_workspace_size(int64_t n_tok, int64_t d_in, int x_dtype) {
+    (void)x_dtype;
+    if (n_tok <= 0 || d_in <= 0 || bad_dim(n_tok) || bad_dim(d_in)) return 0;
+    return hessian_plan(n_tok, d_in).ws_bytes;
+}
+
+pwq_status pwq_hessian_accumulate(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* H,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    if (x_dtype != PWQ_F32 && x_dtype != PWQ_BF16) return PWQ_EDTYPE;
+    if (bad_dim(n_tok) || d_in <= 0 || bad_dim(d_in) || ldx < d_in || !H) return PWQ_EINVAL;
+    if (d_in > 65535 * 2) return PWQ_EINVAL;
+    if (n_tok == 0) return PWQ_OK;
+    if (!X) return PWQ_EINVAL;
+    const size_t need = pwq_hessian_workspace_size(n_tok, d_in, x_dtype);
+    if (need && (!ws || ws_bytes < need)) return PWQ_EWORKSPACE;
+    return hip_status(hessian_launch(X, x_dtype, n_tok, d_in, ldx, H, ws, (hipStream_t)stream));
+}
+
+pwq_status pwq_hessian_damp(float* H, int64_t d_in, float damp, float* lambda_out, void* stream) {
+    if (!H || d_in <= 0 || bad_dim(d_in) || !(damp >= 0.f) || isinf(damp)) return PWQ_EINVAL;
+    return hip_status(damp_launch(H, d_in, damp, lambda_out, (hipStream_t)stream));
+}
+
+pwq_status pwq_act_order_perm(const float* H, int64_t d_in, int32_t* perm, void* stream) {
+    if (!H || !perm || d_in <= 0 || bad_dim(d_in) || d_in > INT32_MAX) return PWQ_EINVAL;
+    return hip_status(act_order_launch(H, d_in, perm, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ factor
+size_t pwq_chol_workspace_size(int64_t n) {
+    if (n <= 0 || bad_dim(n)) return 0;
+    return chol_ws_bytes(n);
+}
+
+pwq_status pwq_chol_inverse_upper(const float* H, int64_t n, const int32_t* perm, float* U, int32_t* info, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    if (!H || !U || !info || n <= 0 || n > 65535) return PWQ_EINVAL;
+    if (perm && n > PERM_MAX_N) return PWQ_EINVAL;
+    const size_t need = pwq_chol_workspace_size(n);
+    if (!ws || ws_bytes < need) return PWQ_EWORKSPACE;
+    return hip_status(chol_launch(H, n, perm, U, info, ws, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ GPTQ
+static bool gptq_params_ok(const pwq_params* p) {
+    if (!p) return false;
+    if (p->bits < 2 || p->bits > 8) return false;
+    if (p->block_size != 32 && p->block_size != 64 && p->block_size != 128) return false;
+    const int g = p->group_size;
+    if (g < 0) return false;
+    if (g != 0 && (g % 2 != 0 || !((g % p->block_size) == 0 || (p->block_size % g) == 0))) return false;
+    return true;
+}
+
+size_t pwq_gptq_workspace_size(int64_t d_out, int64_t d_in, const pwq_params* params) {
+    if (d_out <= 0 || d_in <= 0 || bad_dim(d_out) || bad_dim(d_in) || !gptq_params_ok(params)) return 0;
+    return gptq_ws_layout(d_out, d_in, params->block_size, params->act_order != 0).total;
+}
+
+pwq_status pwq_gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
+                                   const float* U, const int32_t* info, const pwq_params* params,
+                                   const int32_t* perm, const uint16_t* scales_in,
+                                   int8_t* codes, uint8_t* packed, uint16_t* scales_out, int32_t* g_idx,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
+    if (!gptq_params_ok(params)) return PWQ_EINVAL;
+    if (bad_dim(d_out) || d_out > INT32_MAX || d_in <= 0 || bad_dim(d_in) || ldw < d_in) return PWQ_EINVAL;
+    if (!U || !info || !scales_out || (!codes && !packed)) return PWQ_EINVAL;
+    if (packed && (params->bits != 4 || d_in % 2 != 0)) return PWQ_EINVAL;
+    const int act = params->act_order != 0;
+    if (act && (!perm || !g_idx || d_in > PERM_MAX_N)) return PWQ_EINVAL;
+    if (d_out == 0) return PWQ_OK;
+    if (!W) return PWQ_EINVAL;
+    const size_t need = pwq_gptq_workspace_size(d_out, d_in, params);
+    if (!ws || ws_bytes < need) return PWQ_EWORKSPACE;
+    return hip_status(gptq_launch(W, w_dtype, d_out, d_in, ldw, U, info, params->bits, params->group_size,
+                                  params->block_size, act, perm, scales_in, codes, packed, scales_out, g_idx, ws,
+                                  (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ RTN / dequant
+pwq_status pwq_rtn_quantize(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
+                            int32_t group_size, const uint16_t* scales_in, int8_t* codes, uint8_t* packed,
+                            uint16_t* scales_out, void* stream) {
+    if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
+    if (bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldw < d_in) return PWQ_EINVAL;
+    if (bits < 2 || bits > 8 || !group_ok(group_size, d_in)) return PWQ_EINVAL;
+    if (!scales_out || (!codes && !packed)) return PWQ_EINVAL;
+    if (packed && (bits != 4 || d_in % 2 != 0)) return PWQ_EINVAL;
+    if (d_out == 0) return PWQ_OK;
+    if (!W) return PWQ_EINVAL;
+    return hip_status(rtn_launch(W, w_dtype, d_out, d_in, ldw, bits, group_size, scales_in, codes, packed, scales_out,
+                                 (hipStream_t)stream));
+}
+
+pwq_status pwq_dequant(const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
+                       int64_t d_out, int64_t d_in, int32_t bits, int32_t group_size, void* W_out, int out_dtype,
+                       void* stream) {
+    if (out_dtype != PWQ_F32 && out_dtype != PWQ_F16 && out_dtype != PWQ_BF16) return PWQ_EDTYPE;
+    if (bad_dim(d_out) || d_in <= 0 || bad_dim(d_in)) return PWQ_EINVAL;
+    if (bits < 2 || bits > 8 || !group_ok(group_size, d_in)) return PWQ_EINVAL;
+    if ((packed != nullptr) == (codes != nullptr)) return PWQ_EINVAL;
+    if (packed && (bits != 4 || d_in % 2 != 0)) return PWQ_EINVAL;
+    if (g_idx && group_size == 0) return PWQ_EINVAL;
+    if (!scales || !W_out) return PWQ_EINVAL;
+    return hip_status(dequant_launch(packed, codes, scales, g_idx, d_out, d_in, bits, group_size, W_out, out_dtype,
+                                     (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ MSE
+size_t pwq_recon_mse_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out) {
+    if (n_tok <= 0 || d_in <= 0 || d_out <= 0 || bad_dim(n_tok) || bad_dim(d_in) || bad_dim(d_out)) return 0;
+    return mse_ws_bytes(n_tok, d_in, d_out);
+}
+
+pwq_status pwq_recon_mse(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                         const void* W, int w_dtype, int64_t ldw,
+                         const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
+                         int64_t d_out, int32_t bits, int32_t group_size,
+                         double* mse, void* ws, size_t ws_bytes, void* stream) {
+    if (x_dtype != PWQ_F32 && x_dtype != PWQ_BF16) return PWQ_EDTYPE;
+    if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
+    if (bad_dim(n_tok) || bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldx < d_in || ldw < d_in) return PWQ_EINVAL;
+    if (bits < 2 || bits > 8 || !group_ok(group_size, d_in)) return PWQ_EINVAL;
+    if ((packed != nullptr) == (codes != nullptr)) return PWQ_EINVAL;
+    if (packed && (bits != 4 || d_in % 2 != 0)) return PWQ_EINVAL;
+    if (g_idx && group_size == 0) return PWQ_EINVAL;
+    if (!mse || !scales) return PWQ_EINVAL;
+    if (n_tok > 0 && d_out > 0) {
+        if (!X || !W) return PWQ_EINVAL;
+        const size_t need = pwq_recon_mse_workspace_size(n_tok, d_in, d_out);
+        if (!ws || ws_bytes < need) return PWQ_EWORKSPACE;
+    }
+    return hip_status(mse_launch(X, x_dtype, n_tok, d_in, ldx, W, w_dtype, ldw, packed, codes, scales, g_idx, d_out, bits,
+                                 group_size, mse, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

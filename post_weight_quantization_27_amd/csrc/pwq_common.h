@@ -1,0 +1,92 @@
+// Shared device helpers for the gfx950 kernels of libpwq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pwq {
+
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------------ 16-bit formats
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {       // one RNE rounding
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {      // one RNE rounding
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ------------------------------------------------------------------ quantizer
+// Scale of a symmetric group: absmax / qmax as one IEEE float32 division, then one RNE
+// rounding to float16 (the stored 16-bit scale of "GPTQ: Post-Training INT4", section
+// "Group Quantization"; symmetric S with Z = 0 of "Model Quantization Mechanics",
+// "Affine Quantization").  The division relies on hipcc's default correctly rounded
+// float32 divide (no fast-math flags anywhere in this library).
+__device__ __forceinline__ uint16_t scale_bits_from_absmax(float absmax, int qmax) {
+    float s32 = absmax / (float)qmax;
+    return f32_to_f16_bits(s32);
+}
+
+// Code of w for scale s (s = a float16 value, > 0): the integer nearest to the EXACT
+// quotient w / s, ties to even, clamped to [-qmax, qmax].
+// k0 = rint(w * (1/s)) is within one of the answer; the signs of w - (k0 +- 1/2) s decide
+// exactly, because (k0 +- 1/2) s has at most 16 significant bits (exact in float32) and a
+// fused multiply-add rounds w - (k0 +- 1/2) s once, which preserves its sign and zero.
+__device__ __forceinline__ int quant_code(float w, float s, float rs, int qmax) {
+    float k = rintf(w * rs);
+    float lim = (float)(qmax + 1);
+    k = fminf(fmaxf(k, -lim), lim);
+    float hi = fmaf(-(k + 0.5f), s, w);
+    float lo = fmaf(-(k - 0.5f), s, w);
+    int ki = (int)k;
+    if (hi > 0.f || (hi == 0.f && (ki & 1))) {
+        ki += 1;
+    } else if (lo < 0.f || (lo == 0.f && (ki & 1))) {
+        ki -= 1;
+    }
+    ki = ki < -qmax ? -qmax : ki;
+    ki = ki > qmax ? qmax : ki;
+    return ki;
+}
+
+// code for a possibly-zero scale (all-zero group -> code 0)
+__device__ __forceinline__ int quant_code_s(float w, float s, int qmax) {
+    return s > 0.f ? quant_code(w, s, 1.0f / s, qmax) : 0;
+}
+
+// ------------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+// max over aligned groups of `width` lanes (width a power of two <= 64)
+__device__ __forceinline__ float group_max(float v, int width) {
+    for (int o = width >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float load_as_f32(const void* p, int dtype, int64_t i) {
+    // dtype: 0 f32, 1 f16, 2 bf16
+    if (dtype == 0) return ((const float*)p)[i];
+    if (dtype == 1) return f16_bits_to_f32(((const uint16_t*)p)[i]);
+    return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+}
+
+}  // namespace pwq

@@ -1,0 +1,60 @@
+// Host-side launchers shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pwq {
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Hessian build: H += 2 X^T X (float32 MFMA, upper tiles, deterministic split-K, mirror).
+struct HessPlan {
+    int bm;            // tile edge (64 or 128)
+    int tiles;         // tiles per edge
+    int splits;        // token chunks
+    int64_t kchunk;    // tokens per chunk (multiple of 32)
+    size_t ws_bytes;   // partial-tile workspace (0 when splits == 1)
+};
+HessPlan hessian_plan(int64_t n_tok, int64_t d_in);
+hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* H,
+                          void* ws, hipStream_t s);
+hipError_t damp_launch(float* H, int64_t n, float damp, float* lambda_out, hipStream_t s);
+hipError_t act_order_launch(const float* H, int64_t n, int32_t* perm, hipStream_t s);
+
+// Inverse-Hessian factor.
+constexpr int CHOL_NB = 128;
+constexpr int64_t PERM_MAX_N = 32768;     // row staging through LDS for permuted copies
+size_t chol_ws_bytes(int64_t n);
+hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U, int32_t* info, void* ws,
+                       hipStream_t s);
+
+// GPTQ column loop.
+struct GptqWs {
+    size_t wf, err, codes, inv, total;
+};
+GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int act_order);
+hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, const float* U,
+                       const int32_t* info, int bits, int group_size, int block_size, int act_order,
+                       const int32_t* perm, const uint16_t* scales_in, int8_t* codes, uint8_t* packed,
+                       uint16_t* scales_out, int32_t* g_idx, void* ws, hipStream_t s);
+
+// RTN, dequant.
+hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, int bits, int group_size,
+                      const uint16_t* scales_in, int8_t* codes, uint8_t* packed, uint16_t* scales_out,
+                      hipStream_t s);
+hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint16_t* scales,
+                          const int32_t* g_idx, int64_t m, int64_t n, int bits, int group_size, void* out,
+                          int out_dtype, hipStream_t s);
+
+// Reconstruction MSE.
+size_t mse_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out);
+hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W,
+                      int w_dtype, int64_t ldw, const uint8_t* packed, const int8_t* codes,
+                      const uint16_t* scales, const int32_t* g_idx, int64_t d_out, int bits, int group_size,
+                      double* mse, void* ws, hipStream_t s);
+
+}  // namespace pwq

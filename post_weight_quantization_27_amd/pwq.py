@@ -1,0 +1,260 @@
+"""Python binding of libpwq (ctypes): argument marshalling only.
+
+Each function takes torch tensors that live on the GPU, checks shapes and dtypes,
+allocates outputs and the workspace with torch (device memory and streams are all torch
+is used for), and calls the C entry point of the same name on the current stream.  Every
+step of the computation runs in the HIP kernels of libpwq.so; if the library is missing
+the import fails loudly instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpwq.so")
+
+PWQ_OK, PWQ_EINVAL, PWQ_EDTYPE, PWQ_EWORKSPACE, PWQ_EHIP = 0, 1, 2, 3, 4
+PWQ_F32, PWQ_F16, PWQ_BF16 = 0, 1, 2
+
+_c_void_p, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+
+
+class PwqParams(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("act_order", ctypes.c_int32)]
+
+
+_SIGS = {
+    "pwq_version": (ctypes.c_int, []),
+    "pwq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pwq_last_hip_error": (ctypes.c_int, []),
+    "pwq_hessian_workspace_size": (_sz, [_i64, _i64, ctypes.c_int]),
+    "pwq_hessian_accumulate": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "pwq_hessian_damp": (ctypes.c_int, [_c_void_p, _i64, _f32, _c_void_p, _c_void_p]),
+    "pwq_act_order_perm": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p]),
+    "pwq_chol_workspace_size": (_sz, [_i64]),
+    "pwq_chol_inverse_upper": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "pwq_gptq_workspace_size": (_sz, [_i64, _i64, ctypes.POINTER(PwqParams)]),
+    "pwq_gptq_quantize_layer": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                               ctypes.POINTER(PwqParams), _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                               _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "pwq_rtn_quantize": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
+                                        _c_void_p, _c_void_p, _c_void_p]),
+    "pwq_dequant": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _c_void_p,
+                                   ctypes.c_int, _c_void_p]),
+    "pwq_recon_mse_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "pwq_recon_mse": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
+                                     _c_void_p, _sz, _c_void_p]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpwq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (post_weight_quantization_27_amd.build_lib.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class PwqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().pwq_status_string(status).decode()
+        if status == PWQ_EHIP:
+            msg += f" (hipError {lib().pwq_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != PWQ_OK:
+        raise PwqError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    return {torch.float32: PWQ_F32, torch.float16: PWQ_F16, torch.bfloat16: PWQ_BF16}[t.dtype]
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a row-major 2-D device tensor (unit column stride)."""
+    if t.dim() != 2 or not t.is_cuda:
+        raise ValueError(f"{name}: expected a 2-D GPU tensor")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError(f"{name}: columns must be contiguous")
+    return max(t.stride(0), t.shape[1])
+
+
+def _ws(nbytes: int, dev) -> Optional[torch.Tensor]:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev) if nbytes else None
+
+
+def _need(t: torch.Tensor, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous GPU {dtype} of shape {tuple(shape)}")
+
+
+# ------------------------------------------------------------------ Hessian
+def hessian_accumulate(X: torch.Tensor, H: torch.Tensor) -> torch.Tensor:
+    """H += 2 X^T X (X: tokens x d_in, float32 or bfloat16; H float32 d_in x d_in)."""
+    ldx = _rows(X, "X")
+    n_tok, d_in = X.shape
+    _need(H, torch.float32, (d_in, d_in), "H")
+    code = _dtype_code(X)
+    nb = lib().pwq_hessian_workspace_size(n_tok, d_in, code)
+    ws = _ws(nb, X.device)
+    _check("pwq_hessian_accumulate", lib().pwq_hessian_accumulate(_p(X), code, n_tok, d_in, ldx, _p(H), _p(ws), nb, _stream(X)))
+    return H
+
+
+def hessian_damp(H: torch.Tensor, damp: float, lambda_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(H, torch.float32, (H.shape[0], H.shape[0]), "H")
+    _check("pwq_hessian_damp", lib().pwq_hessian_damp(_p(H), H.shape[0], float(damp), _p(lambda_out), _stream(H)))
+    return H
+
+
+def act_order_perm(H: torch.Tensor) -> torch.Tensor:
+    n = H.shape[0]
+    _need(H, torch.float32, (n, n), "H")
+    perm = torch.empty(n, dtype=torch.int32, device=H.device)
+    _check("pwq_act_order_perm", lib().pwq_act_order_perm(_p(H), n, _p(perm), _stream(H)))
+    return perm
+
+
+# ------------------------------------------------------------------ factor
+def chol_inverse_upper(H: torch.Tensor, perm: Optional[torch.Tensor] = None, U: Optional[torch.Tensor] = None,
+                       info: Optional[torch.Tensor] = None):
+    """(U, info): U upper with H^-1 = U^T U (of H[perm][:, perm] if perm); info int32 on device."""
+    n = H.shape[0]
+    _need(H, torch.float32, (n, n), "H")
+    if U is None:
+        U = torch.empty((n, n), dtype=torch.float32, device=H.device)
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=H.device)
+    nb = lib().pwq_chol_workspace_size(n)
+    ws = _ws(nb, H.device)
+    _check("pwq_chol_inverse_upper", lib().pwq_chol_inverse_upper(_p(H), n, _p(perm), _p(U), _p(info), _p(ws), nb, _stream(H)))
+    return U, info
+
+
+# ------------------------------------------------------------------ GPTQ / RTN
+def _n_groups(d_in: int, group_size: int) -> int:
+    return 1 if group_size == 0 else -(-d_in // group_size)
+
+
+def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, info: torch.Tensor, bits: int = 4, group_size: int = 128,
+                        block_size: int = 128, perm: Optional[torch.Tensor] = None,
+                        scales_in: Optional[torch.Tensor] = None, want_codes: bool = True, want_packed: bool = True,
+                        out: Optional[dict] = None) -> dict:
+    """GPTQ column loop.  Returns {codes (int8, original order), packed (uint8), scales (float16,
+    groups in processing order), g_idx (int32, act-order only)}."""
+    ldw = _rows(W, "W")
+    d_out, d_in = W.shape
+    act = perm is not None
+    prm = PwqParams(bits, group_size, block_size, 1 if act else 0)
+    dev = W.device
+    ng = _n_groups(d_in, group_size)
+    o = out if out is not None else {}
+    if want_codes and o.get("codes") is None:
+        o["codes"] = torch.empty((d_out, d_in), dtype=torch.int8, device=dev)
+    if want_packed and o.get("packed") is None:
+        o["packed"] = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
+    if o.get("scales") is None:
+        o["scales"] = torch.empty((d_out, ng), dtype=torch.float16, device=dev)
+    if act and o.get("g_idx") is None:
+        o["g_idx"] = torch.empty(d_in, dtype=torch.int32, device=dev)
+    nb = lib().pwq_gptq_workspace_size(d_out, d_in, ctypes.byref(prm))
+    ws = o.get("_ws")
+    if ws is None or ws.numel() < nb:
+        ws = _ws(nb, dev)
+        o["_ws"] = ws
+    _check("pwq_gptq_quantize_layer", lib().pwq_gptq_quantize_layer(
+        _p(W), _dtype_code(W), d_out, d_in, ldw, _p(U), _p(info), ctypes.byref(prm), _p(perm), _p(scales_in),
+        _p(o.get("codes") if want_codes else None), _p(o.get("packed") if want_packed else None), _p(o["scales"]),
+        _p(o.get("g_idx") if act else None), _p(ws), nb, _stream(W)))
+    return o
+
+
+def rtn_quantize(W: torch.Tensor, bits: int = 4, group_size: int = 128, scales_in: Optional[torch.Tensor] = None,
+                 want_codes: bool = True, want_packed: bool = True, out: Optional[dict] = None) -> dict:
+    ldw = _rows(W, "W")
+    d_out, d_in = W.shape
+    dev = W.device
+    o = out if out is not None else {}
+    if want_codes and o.get("codes") is None:
+        o["codes"] = torch.empty((d_out, d_in), dtype=torch.int8, device=dev)
+    if want_packed and o.get("packed") is None:
+        o["packed"] = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
+    if o.get("scales") is None:
+        o["scales"] = torch.empty((d_out, _n_groups(d_in, group_size)), dtype=torch.float16, device=dev)
+    _check("pwq_rtn_quantize", lib().pwq_rtn_quantize(
+        _p(W), _dtype_code(W), d_out, d_in, ldw, bits, group_size, _p(scales_in),
+        _p(o.get("codes") if want_codes else None), _p(o.get("packed") if want_packed else None), _p(o["scales"]), _stream(W)))
+    return o
+
+
+def dequant(scales: torch.Tensor, d_in: int, bits: int = 4, group_size: int = 128, packed: Optional[torch.Tensor] = None,
+            codes: Optional[torch.Tensor] = None, g_idx: Optional[torch.Tensor] = None, out_dtype=torch.float16,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    d_out = scales.shape[0]
+    src = packed if packed is not None else codes
+    if out is None:
+        out = torch.empty((d_out, d_in), dtype=out_dtype, device=src.device)
+    _check("pwq_dequant", lib().pwq_dequant(_p(packed), _p(codes), _p(scales), _p(g_idx), d_out, d_in, bits, group_size,
+                                            _p(out), _dtype_code(out), _stream(src)))
+    return out
+
+
+def recon_mse(X: torch.Tensor, W: torch.Tensor, scales: torch.Tensor, bits: int = 4, group_size: int = 128,
+              packed: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+              g_idx: Optional[torch.Tensor] = None, mse: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device float64 scalar: mean over tokens x outputs of (X (W - What)^T)^2."""
+    ldx, ldw = _rows(X, "X"), _rows(W, "W")
+    n_tok, d_in = X.shape
+    d_out = W.shape[0]
+    if mse is None:
+        mse = torch.empty(1, dtype=torch.float64, device=X.device)
+    nb = lib().pwq_recon_mse_workspace_size(n_tok, d_in, d_out)
+    if ws is None or ws.numel() < nb:
+        ws = _ws(nb, X.device)
+    _check("pwq_recon_mse", lib().pwq_recon_mse(
+        _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
+        _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(X)))
+    return mse
+
+
+# ------------------------------------------------------------------ one layer, end to end
+def gptq_layer(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group_size: int = 128, block_size: int = 128,
+               damp: float = 0.01, act_order: bool = False, want_codes: bool = True, want_packed: bool = True) -> dict:
+    """The calls of one layer in order: Hessian, damping, [act-order], factor, GPTQ."""
+    d_in = W.shape[1]
+    H = torch.zeros((d_in, d_in), dtype=torch.float32, device=W.device)
+    hessian_accumulate(X, H)
+    hessian_damp(H, damp)
+    perm = act_order_perm(H) if act_order else None
+    U, info = chol_inverse_upper(H, perm)
+    res = gptq_quantize_layer(W, U, info, bits, group_size, block_size, perm=perm, want_codes=want_codes,
+                              want_packed=want_packed)
+    res.update({"H": H, "U": U, "info": info, "perm": perm})
+    return res

@@ -1,0 +1,159 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the header
+declares, sizes workspaces on the host, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "pwq.h")
+LIB = os.path.join(ROOT, "post_weight_quantization_27_amd", "libpwq.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpwq.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pwq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from post_weight_quantization_27_amd import pwq
+    return pwq.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    ver = int(re.search(r"#define PWQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.pwq_version() == ver
+    for code, text in ((0, b"ok"), (1, b"invalid argument"), (2, b"unsupported dtype"),
+                       (3, b"workspace missing or too small"), (4, b"HIP launch failure"), (99, b"unknown status")):
+        assert L.pwq_status_string(code) == text
+    assert L.pwq_last_hip_error() == 0
+
+
+def test_workspace_sizes(L):
+    from post_weight_quantization_27_amd import pwq
+    assert L.pwq_hessian_workspace_size(0, 768, 0) == 0
+    # small d_in: token chunks with partial tiles; 64-wide tiles below d_in 1024
+    n_tok, d_in = 8192, 768
+    tiles = 768 // 64
+    ntile = tiles * (tiles + 1) // 2
+    ws = L.pwq_hessian_workspace_size(n_tok, d_in, 0)
+    assert ws > 0 and ws % (ntile * 64 * 64 * 4) == 0
+    # enough upper tiles: no split, no workspace
+    assert L.pwq_hessian_workspace_size(262144, 28672, 2) == 0
+    assert L.pwq_chol_workspace_size(3072) == 3072 * 128 * 4
+    p = pwq.PwqParams(4, 128, 128, 0)
+    m, n = 768, 3072
+    got = L.pwq_gptq_workspace_size(m, n, ctypes.byref(p))
+    def up(x):
+        return (x + 255) // 256 * 256
+    assert got == up(up(m * n * 4) + m * 128 * 4)
+    pa = pwq.PwqParams(4, 128, 128, 1)
+    assert L.pwq_gptq_workspace_size(m, n, ctypes.byref(pa)) == up(up(up(up(m * n * 4) + m * 128 * 4) + m * n) + n * 4)
+    bad = pwq.PwqParams(4, 96, 128, 0)          # group neither divides nor is a multiple of B
+    assert L.pwq_gptq_workspace_size(m, n, ctypes.byref(bad)) == 0
+    assert L.pwq_recon_mse_workspace_size(8192, 768, 3072) > 0
+
+
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below is rejected first
+
+
+def test_hessian_rejects(L):
+    from post_weight_quantization_27_amd import pwq
+    assert L.pwq_hessian_accumulate(FAKE, pwq.PWQ_F16, 16, 16, 16, FAKE, None, 0, None) == pwq.PWQ_EDTYPE
+    assert L.pwq_hessian_accumulate(FAKE, pwq.PWQ_F32, 16, 16, 8, FAKE, None, 0, None) == pwq.PWQ_EINVAL
+    assert L.pwq_hessian_accumulate(FAKE, pwq.PWQ_F32, 16, 0, 16, FAKE, None, 0, None) == pwq.PWQ_EINVAL
+    assert L.pwq_hessian_accumulate(FAKE, pwq.PWQ_F32, -1, 16, 16, FAKE, None, 0, None) == pwq.PWQ_EINVAL
+    assert L.pwq_hessian_accumulate(None, pwq.PWQ_F32, 16, 16, 16, FAKE, None, 0, None) == pwq.PWQ_EINVAL
+    assert L.pwq_hessian_accumulate(FAKE, pwq.PWQ_F32, 16, 16, 16, None, None, 0, None) == pwq.PWQ_EINVAL
+    need = L.pwq_hessian_workspace_size(8192, 768, 0)
+    assert L.pwq_hessian_accumulate(FAKE, pwq.PWQ_F32, 8192, 768, 768, FAKE, None, need, None) == pwq.PWQ_EWORKSPACE
+    assert L.pwq_hessian_accumulate(FAKE, pwq.PWQ_F32, 8192, 768, 768, FAKE, FAKE, need - 1, None) == pwq.PWQ_EWORKSPACE
+    # empty token tile: valid and a no-op (nothing enqueued, no HIP call)
+    assert L.pwq_hessian_accumulate(None, pwq.PWQ_F32, 0, 16, 16, FAKE, None, 0, None) == pwq.PWQ_OK
+    assert L.pwq_hessian_damp(FAKE, 16, -0.1, None, None) == pwq.PWQ_EINVAL
+    assert L.pwq_hessian_damp(FAKE, 16, float("nan"), None, None) == pwq.PWQ_EINVAL
+    assert L.pwq_hessian_damp(None, 16, 0.01, None, None) == pwq.PWQ_EINVAL
+    assert L.pwq_act_order_perm(FAKE, 16, None, None) == pwq.PWQ_EINVAL
+
+
+def test_chol_rejects(L):
+    from post_weight_quantization_27_amd import pwq
+    need = L.pwq_chol_workspace_size(256)
+    assert L.pwq_chol_inverse_upper(FAKE, 256, None, FAKE, None, FAKE, need, None) == pwq.PWQ_EINVAL
+    assert L.pwq_chol_inverse_upper(FAKE, 0, None, FAKE, FAKE, FAKE, need, None) == pwq.PWQ_EINVAL
+    assert L.pwq_chol_inverse_upper(FAKE, 256, None, FAKE, FAKE, FAKE, need - 4, None) == pwq.PWQ_EWORKSPACE
+    assert L.pwq_chol_inverse_upper(FAKE, 40000, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == pwq.PWQ_EINVAL
+
+
+def _gptq(L, pwq, **kw):
+    a = dict(W=FAKE, wt=pwq.PWQ_F32, m=64, n=256, ldw=256, U=FAKE, info=FAKE, p=pwq.PwqParams(4, 128, 128, 0),
+             perm=None, sin=None, codes=FAKE, packed=FAKE, sout=FAKE, gidx=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return L.pwq_gptq_quantize_layer(a["W"], a["wt"], a["m"], a["n"], a["ldw"], a["U"], a["info"], ctypes.byref(a["p"]),
+                                     a["perm"], a["sin"], a["codes"], a["packed"], a["sout"], a["gidx"], a["ws"], a["wsb"], None)
+
+
+def test_gptq_rejects(L):
+    from post_weight_quantization_27_amd import pwq
+    P = pwq.PwqParams
+    assert _gptq(L, pwq, wt=pwq.PWQ_BF16) == pwq.PWQ_EDTYPE
+    for p in (P(1, 128, 128, 0), P(9, 128, 128, 0), P(4, 128, 96, 0), P(4, 3, 128, 0), P(4, 96, 128, 0), P(4, -2, 128, 0)):
+        assert _gptq(L, pwq, p=p) == pwq.PWQ_EINVAL
+    assert _gptq(L, pwq, p=P(3, 128, 128, 0)) == pwq.PWQ_EINVAL           # packed needs 4 bits
+    assert _gptq(L, pwq, n=255, ldw=255, codes=FAKE, packed=None, p=P(4, 0, 128, 0), ws=None) == pwq.PWQ_EWORKSPACE
+    assert _gptq(L, pwq, n=255, ldw=255) == pwq.PWQ_EINVAL                 # packed needs even d_in
+    assert _gptq(L, pwq, codes=None, packed=None) == pwq.PWQ_EINVAL
+    assert _gptq(L, pwq, sout=None) == pwq.PWQ_EINVAL
+    assert _gptq(L, pwq, U=None) == pwq.PWQ_EINVAL
+    assert _gptq(L, pwq, info=None) == pwq.PWQ_EINVAL
+    assert _gptq(L, pwq, ldw=100) == pwq.PWQ_EINVAL
+    assert _gptq(L, pwq, p=P(4, 128, 128, 1)) == pwq.PWQ_EINVAL           # act-order needs perm and g_idx
+    assert _gptq(L, pwq, p=P(4, 128, 128, 1), perm=FAKE) == pwq.PWQ_EINVAL
+    assert _gptq(L, pwq, wsb=10) == pwq.PWQ_EWORKSPACE
+    assert _gptq(L, pwq, ws=None) == pwq.PWQ_EWORKSPACE
+    assert _gptq(L, pwq, W=None) == pwq.PWQ_EINVAL
+    assert _gptq(L, pwq, m=0, W=None) == pwq.PWQ_OK                        # empty layer: nothing to do
+
+
+def test_rtn_dequant_mse_reject(L):
+    from post_weight_quantization_27_amd import pwq
+    r = L.pwq_rtn_quantize
+    assert r(FAKE, pwq.PWQ_BF16, 4, 8, 8, 4, 0, None, FAKE, None, FAKE, None) == pwq.PWQ_EDTYPE
+    assert r(FAKE, pwq.PWQ_F32, 4, 8, 8, 4, 3, None, FAKE, None, FAKE, None) == pwq.PWQ_EINVAL
+    assert r(FAKE, pwq.PWQ_F32, 4, 8, 8, 1, 0, None, FAKE, None, FAKE, None) == pwq.PWQ_EINVAL
+    assert r(FAKE, pwq.PWQ_F32, 4, 8, 8, 8, 0, None, None, FAKE, FAKE, None) == pwq.PWQ_EINVAL
+    assert r(FAKE, pwq.PWQ_F32, 4, 7, 7, 4, 0, None, None, FAKE, FAKE, None) == pwq.PWQ_EINVAL
+    assert r(FAKE, pwq.PWQ_F32, 4, 8, 8, 4, 0, None, FAKE, None, None, None) == pwq.PWQ_EINVAL
+    assert r(None, pwq.PWQ_F32, 0, 8, 8, 4, 0, None, FAKE, None, FAKE, None) == pwq.PWQ_OK
+    d = L.pwq_dequant
+    assert d(FAKE, FAKE, FAKE, None, 4, 8, 4, 0, FAKE, pwq.PWQ_F32, None) == pwq.PWQ_EINVAL    # both sources
+    assert d(None, None, FAKE, None, 4, 8, 4, 0, FAKE, pwq.PWQ_F32, None) == pwq.PWQ_EINVAL    # none
+    assert d(FAKE, None, FAKE, FAKE, 4, 8, 4, 0, FAKE, pwq.PWQ_F32, None) == pwq.PWQ_EINVAL    # g_idx, per-row
+    assert d(FAKE, None, FAKE, None, 4, 8, 4, 0, FAKE, 7, None) == pwq.PWQ_EDTYPE
+    m = L.pwq_recon_mse
+    args = [FAKE, pwq.PWQ_F32, 64, 32, 32, FAKE, pwq.PWQ_F32, 32, FAKE, None, FAKE, None, 16, 4, 0, FAKE, FAKE, 1 << 30, None]
+    bad = list(args); bad[1] = pwq.PWQ_F16
+    assert m(*bad) == pwq.PWQ_EDTYPE
+    bad = list(args); bad[6] = pwq.PWQ_BF16
+    assert m(*bad) == pwq.PWQ_EDTYPE
+    bad = list(args); bad[9] = FAKE
+    assert m(*bad) == pwq.PWQ_EINVAL
+    bad = list(args); bad[16] = None
+    assert m(*bad) == pwq.PWQ_EWORKSPACE
+    bad = list(args); bad[15] = None
+    assert m(*bad) == pwq.PWQ_EINVAL
+    bad = list(args); bad[4] = 16
+    assert m(*bad) == pwq.PWQ_EINVAL
