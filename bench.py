@@ -31,6 +31,7 @@ def parse():
     ap.add_argument("--workload", default="gpt2_block")
     ap.add_argument("--layers", default="", help="comma-separated layer names (default: all)")
     ap.add_argument("--act-order", action="store_true")
+    ap.add_argument("--streams", type=int, default=1, help="1: one stream per layer (default), 0: all on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", default="", help="layers the oracle baseline runs (default: all)")
     return ap.parse_args()
@@ -163,9 +164,21 @@ def main():
     layers = [Layer(s, torch, pwq, synth, a.act_order) for s in specs]
     torch.cuda.synchronize()
 
+    # layers are independent: each runs on its own stream (default priority), so the
+    # single-workgroup and few-workgroup kernels of one layer overlap with the others
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in layers] if a.streams else [main for _ in layers]
+
+    def step():
+        for L, st in zip(layers, streams):
+            st.wait_stream(main)
+            with torch.cuda.stream(st):
+                run_step(L, pwq)
+        for st in streams:
+            main.wait_stream(st)
+
     for _ in range(a.warmup):
-        for L in layers:
-            run_step(L, pwq)
+        step()
     torch.cuda.synchronize()
 
     # timed region: K steps, no per-call events (they would add records between launches)
@@ -174,14 +187,14 @@ def main():
     e0.record()
     t0 = time.perf_counter()
     for _ in range(a.steps):
-        for L in layers:
-            run_step(L, pwq)
+        step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / a.steps
 
-    # per-call durations: the same steps again with events around every call
+    # per-call durations: the same steps again, layers one after another on one stream, with
+    # events around every call
     timers = [dict() for _ in layers]
     for _ in range(a.steps):
         for L, T in zip(layers, timers):
@@ -216,7 +229,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": a.workload, "layers": [f"{s.name}:{s.d_in}->{s.d_out}" for s in specs],
                    "n_tok": specs[0].n_tok, "bits": specs[0].bits, "group_size": specs[0].group_size,
-                   "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order)},
+                   "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order),
+                   "layer_streams": bool(a.streams)},
         "roofline": roof,
         "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
         "mse_gptq_rtn": mses,

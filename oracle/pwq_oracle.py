@@ -399,15 +399,22 @@ def direct_obs(W: np.ndarray, H: np.ndarray, bits: int, group_size: int = 0,
 # ------------------------------------------------------------------ whole layer
 
 def quantize_layer(W: np.ndarray, x_tiles, bits: int = 4, group_size: int = 128, block_size: int = 128,
-                   damp: float = 0.01, act_order: bool = False) -> dict:
-    """Hessian -> damping -> [act-order] -> U -> GPTQ, plus RTN and both MSEs on the same X."""
+                   damp: float = 0.01, act_order: bool = False, perm: Optional[np.ndarray] = None) -> dict:
+    """Hessian -> damping -> [act-order] -> U -> GPTQ, plus RTN and both MSEs on the same X.
+
+    ``perm``: with act_order, a processing order decided elsewhere (the order is an integer
+    decision taken on a floating-point diagonal; near-equal entries may be ordered either
+    way, so a comparison can fix the order and check it separately)."""
     if isinstance(x_tiles, np.ndarray):
         x_tiles = [x_tiles]
     x_tiles = list(x_tiles)
     H = hessian(x_tiles)
     n_tok = sum(int(np.asarray(t).shape[0]) for t in x_tiles)
     Hd, lam = damp_hessian(H, damp)
-    perm = act_order_perm(Hd) if act_order else None
+    if act_order and perm is None:
+        perm = act_order_perm(Hd)
+    elif not act_order:
+        perm = None
     Hp = Hd[np.ix_(perm, perm)] if perm is not None else Hd
     U = chol_inverse_upper(Hp)
     res = gptq(W, U, bits, group_size, block_size, perm=perm)

@@ -54,129 +54,194 @@ __global__ __launch_bounds__(256) void copy_perm_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ diagonal block
-// 256 threads as 16 x 16 (tr, tc); thread (tr, tc) holds the 8 x 8 register tile of rows
-// tr + 16 ii and columns tc + 16 jj (cyclic), so the active part [0, c) x [0, c) shrinks
-// evenly over all threads as pivots retire.  Per pivot, the pivot column (factor) or the
-// pivot row and column (inverse) travel through LDS in a permuted layout ([lane % 16][i / 16],
-// two 16-byte reads per thread), zero outside the active range so the rank-1 update needs
-// no predicates; double buffered, one barrier per pivot.  A ragged block (bs < 128) is
-// padded with the identity, which leaves the real part unchanged.
+// One workgroup of 256 threads factors the 128 x 128 diagonal block A = V V^T (V upper) and
+// inverts V, everything in LDS:
+//   factor, 32-column panels from the right: the panel region (rows above and inside the
+//     panel) sits in 4 x 4 register tiles; per pivot the pivot column goes through LDS
+//     (zero outside the active rows, so the rank-1 update needs no predicates) with one
+//     barrier; after the panel, the rows and columns left of it get one rank-32 update on
+//     MFMA (32 x 32 output tiles spread over the four waves).
+//   inverse Z = V^-1: the four 32 x 32 diagonal blocks are inverted at once, one per wave
+//     (no barriers: a wave's own LDS accesses are in order), then two doubling levels
+//     Z_12 = -Z_11 (V_12 Z_22) on MFMA: 32 -> 64 and 64 -> 128.
+// A ragged block (bs < 128) is padded with the identity, which leaves the real part unchanged.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int LP = CHOL_NB + 1;    // padded LDS row
+
+// 32 x 32 tile of C -= A B^T on MFMA, with A rows [ra, ra+32), B rows [rb, rb+32), k over
+// [k0, k0+32) of the same LDS matrix M (sign = -1) or C = s * A B (B row-major, k-major).
+__device__ __forceinline__ f32x16 mfma_tile_abT(const float (*M)[LP], int ra, int rb, int k0, int kn, int lane) {
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int kp = 0; kp < kn; kp += 2) {
+        const float av = M[ra + (lane & 31)][k0 + kp + (lane >> 5)];
+        const float bv = M[rb + (lane & 31)][k0 + kp + (lane >> 5)];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+    return acc;
+}
+// acc = A[ra.., ka + k] * B[kb + k][cb..], A from MA (row-major [i][k]), B from MB ([k][j])
+__device__ __forceinline__ f32x16 mfma_tile_ab(const float (*MA)[LP], int ra, int ka, const float (*MB)[LP], int kb,
+                                               int cb, int kn, int lane) {
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int kp = 0; kp < kn; kp += 2) {
+        const float av = MA[ra + (lane & 31)][ka + kp + (lane >> 5)];
+        const float bv = MB[kb + kp + (lane >> 5)][cb + (lane & 31)];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+    return acc;
+}
+__device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
 __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, int64_t n, int64_t k0, int bs,
                                                         int32_t* __restrict__ info) {
     if (*info) return;
-    __shared__ __attribute__((aligned(16))) float colb[2][16][8];
-    __shared__ __attribute__((aligned(16))) float rowb[2][16][8];
+    __shared__ float A[CHOL_NB][LP];
+    __shared__ float Z[CHOL_NB][LP];
+    __shared__ __attribute__((aligned(16))) float colb[2][CHOL_NB];
     __shared__ float pivb[2];
-    const int tid = threadIdx.x;
-    const int tr = tid >> 4, tc = tid & 15;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    float a[8][8];
+    for (int e = tid; e < CHOL_NB * CHOL_NB; e += 256) {
+        const int i = e >> 7, j = e & 127;
+        float v = 0.f;
+        if (i <= j) v = j < bs ? U[(k0 + i) * n + k0 + j] : (i == j ? 1.f : 0.f);
+        A[i][j] = v;
+        Z[i][j] = 0.f;
+    }
+    __syncthreads();
+
+    // ---------------- factor
+    const int rb = tid >> 3, cb = tid & 7;       // rows 4rb..4rb+3, panel columns 4cb..4cb+3
+    for (int p = 3; p >= 0; --p) {
+        const int c0 = 32 * p;
+        const bool act = 4 * rb < c0 + 32;
+        float a[4][4];
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii)
+        for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int i = tr + 16 * ii, j = tc + 16 * jj;
-            float v;
-            if (i < bs && j < bs) v = i <= j ? U[(k0 + i) * n + k0 + j] : U[(k0 + j) * n + k0 + i];
-            else v = i == j ? 1.f : 0.f;
-            a[ii][jj] = v;
+            for (int jj = 0; jj < 4; ++jj) a[ii][jj] = act ? A[4 * rb + ii][c0 + 4 * cb + jj] : 0.f;
+        for (int q = 7; q >= 0; --q) {
+#pragma unroll
+            for (int jj = 3; jj >= 0; --jj) {
+                const int c = c0 + 4 * q + jj;
+                const int buf = c & 1;
+                if (act && cb == q) {
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) colb[buf][4 * rb + ii] = (4 * rb + ii < c) ? a[ii][jj] : 0.f;
+                    if (rb == (c >> 2)) pivb[buf] = a[jj][jj];
+                }
+                __syncthreads();
+                const float d = pivb[buf];
+                if (!(d > 0.f)) {                        // same value in every thread
+                    if (tid == 0) *info = (int32_t)(k0 + c + 1);
+                    return;
+                }
+                const float r = __builtin_amdgcn_sqrtf(d);
+                const float inv = __builtin_amdgcn_rcpf(r);
+                if (act) {
+                    const float inv2 = inv * inv;
+                    const float4 vr4 = *(const float4*)&colb[buf][4 * rb];
+                    const float4 vc4 = *(const float4*)&colb[buf][c0 + 4 * cb];
+                    const float vr[4] = {vr4.x, vr4.y, vr4.z, vr4.w};
+                    const float vc[4] = {vc4.x * inv2, vc4.y * inv2, vc4.z * inv2, vc4.w * inv2};
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+                        for (int j2 = 0; j2 < 4; ++j2) a[ii][j2] = fmaf(-vr[ii], vc[j2], a[ii][j2]);
+                    if (cb == q) {
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) {
+                            const int i = 4 * rb + ii;
+                            a[ii][jj] = i < c ? vr[ii] * inv : (i == c ? r : 0.f);
+                        }
+                    }
+                }
+            }
         }
-
-    // ---- factor: for c = 127..0: V_cc = sqrt(a_cc); V_ic = a_ic / V_cc; a_ij -= V_ic V_jc (i, j < c)
+        if (act) {
 #pragma unroll
-    for (int jb = 7; jb >= 0; --jb) {
-        for (int cr = 15; cr >= 0; --cr) {
-            const int c = 16 * jb + cr;
-            const int buf = c & 1;
-            if (tc == cr) {                                   // owners of column c
-                float t[8];
+            for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-                for (int ii = 0; ii < 8; ++ii) t[ii] = (tr + 16 * ii < c) ? a[ii][jb] : 0.f;
-                *(float4*)&colb[buf][tr][0] = make_float4(t[0], t[1], t[2], t[3]);
-                *(float4*)&colb[buf][tr][4] = make_float4(t[4], t[5], t[6], t[7]);
-                if (tr == cr) pivb[buf] = a[jb][jb];
+                for (int jj = 0; jj < 4; ++jj) A[4 * rb + ii][c0 + 4 * cb + jj] = a[ii][jj];
+        }
+        __syncthreads();
+        if (p > 0) {                                     // A[0:c0, 0:c0] -= P P^T, P = V[0:c0, panel]
+            const int ntile = p * (p + 1) / 2;
+            for (int t = wave; t < ntile; t += 4) {
+                int ti = 0, r = t;
+                while (r >= p - ti) { r -= p - ti; ++ti; }
+                const int tj = ti + r;
+                const f32x16 acc = mfma_tile_abT(A, 32 * ti, 32 * tj, c0, 32, lane);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) A[32 * ti + acc_row(v, lane)][32 * tj + (lane & 31)] -= acc[v];
             }
             __syncthreads();
-            const float d = pivb[buf];
-            if (!(d > 0.f)) {                                 // same value in every thread
-                if (tid == 0) *info = (int32_t)(k0 + c + 1);
-                return;
-            }
-            const float r = sqrtf(d);
-            const float inv = 1.0f / r;
-            const float inv2 = inv * inv;
-            const float4 r0 = *(const float4*)&colb[buf][tr][0], r1 = *(const float4*)&colb[buf][tr][4];
-            const float4 c0 = *(const float4*)&colb[buf][tc][0], c1 = *(const float4*)&colb[buf][tc][4];
-            const float vr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-            const float vc[8] = {c0.x * inv2, c0.y * inv2, c0.z * inv2, c0.w * inv2,
-                                 c1.x * inv2, c1.y * inv2, c1.z * inv2, c1.w * inv2};
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii)
-                if (tr + 16 * ii < c) {
-#pragma unroll
-                    for (int jj = 0; jj < jb + 1; ++jj) a[ii][jj] = fmaf(-vr[ii], vc[jj], a[ii][jj]);
-                }
-            if (tc == cr) {
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii) {
-                    const int i = tr + 16 * ii;
-                    a[ii][jb] = i < c ? vr[ii] * inv : (i == c ? r : 0.f);
-                }
-            }
         }
     }
 
-    // ---- inverse Z = V^-1 by rows from the bottom: with R = I initially, for i = 127..0:
-    //      Z_i. = R_i. / V_ii and R_r. -= V_ri Z_i. = (V_ri / V_ii) R_i. for r < i
-    float z[8][8];
+    // ---------------- inverse: leaves (one wave per 32 x 32 diagonal block)
+    {
+        const int o = 32 * wave;
+        const int j = lane & 31, h = lane >> 5;
+        float z[16];
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii)
+        for (int t = 0; t < 16; ++t) z[t] = (16 * h + t == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) z[ii][jj] = (tr + 16 * ii == tc + 16 * jj) ? 1.f : 0.f;
-
+        for (int i = 31; i >= 0; --i) {
+            // row i of R at column j: in register i % 16 of the half that holds row i
+            const float own = z[i & 15];
+            const float other = __shfl_xor(own, 32, 64);
+            const float rij = (h == (i >> 4)) ? own : other;
+            const float inv = __builtin_amdgcn_rcpf(A[o + i][o + i]);
+            const float zi = rij * inv;
 #pragma unroll
-    for (int ib = 7; ib >= 0; --ib) {
-        for (int ir = 15; ir >= 0; --ir) {
-            const int i = 16 * ib + ir;
-            const int buf = i & 1;
-            if (tc == ir) {                                   // column i of V, rows < i
-                float t[8];
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii) t[ii] = (tr + 16 * ii < i) ? a[ii][ib] : 0.f;
-                *(float4*)&colb[buf][tr][0] = make_float4(t[0], t[1], t[2], t[3]);
-                *(float4*)&colb[buf][tr][4] = make_float4(t[4], t[5], t[6], t[7]);
-                if (tr == ir) pivb[buf] = a[ib][ib];
+            for (int t = 0; t < 16; ++t) {
+                const int rr = 16 * h + t;
+                if (rr < i) z[t] = fmaf(-A[o + rr][o + i], zi, z[t]);
             }
-            if (tr == ir) {                                   // row i of R (columns >= i)
-                *(float4*)&rowb[buf][tc][0] = make_float4(z[ib][0], z[ib][1], z[ib][2], z[ib][3]);
-                *(float4*)&rowb[buf][tc][4] = make_float4(z[ib][4], z[ib][5], z[ib][6], z[ib][7]);
-            }
-            __syncthreads();
-            const float inv = 1.0f / pivb[buf];
-            const float4 v0 = *(const float4*)&colb[buf][tr][0], v1 = *(const float4*)&colb[buf][tr][4];
-            const float4 w0 = *(const float4*)&rowb[buf][tc][0], w1 = *(const float4*)&rowb[buf][tc][4];
-            const float vr[8] = {v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv, v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv};
-            const float rz[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii)
-                if (tr + 16 * ii < i) {
-#pragma unroll
-                    for (int jj = ib; jj < 8; ++jj) z[ii][jj] = fmaf(-vr[ii], rz[jj], z[ii][jj]);
-                }
-            if (tr == ir) {
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) z[ib][jj] *= inv;
-            }
+            if (h == (i >> 4)) z[i & 15] = zi;
         }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Z[o + 16 * h + t][o + j] = z[t];   // zeros below the diagonal
     }
+    __syncthreads();
 
+    // ---------------- doubling 32 -> 64: Z_01 = -Z_00 (V_01 Z_11) for the pairs (0,1), (2,3)
+    if (wave < 2) {
+        const int o0 = 64 * wave, o1 = o0 + 32;
+        const int sr = 64 + 32 * wave, sc = 32 * wave;         // scratch in Z's lower-left block
+        f32x16 t = mfma_tile_ab(A, o0, o1, Z, o1, o1, 32, lane);
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii)
+        for (int v = 0; v < 16; ++v) Z[sr + acc_row(v, lane)][sc + (lane & 31)] = t[v];
+        t = mfma_tile_ab(Z, o0, o0, Z, sr, sc, 32, lane);       // k over Z_00 columns, T rows
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int i = tr + 16 * ii, j = tc + 16 * jj;
-            if (i < bs && j < bs) U[(k0 + i) * n + k0 + j] = j >= i ? z[ii][jj] : 0.f;
-        }
+        for (int v = 0; v < 16; ++v) Z[o0 + acc_row(v, lane)][o1 + (lane & 31)] = -t[v];
+    }
+    __syncthreads();
+
+    // ---------------- doubling 64 -> 128: Z_AB = -Z_AA (V_AB Z_BB), A = [0,64), B = [64,128)
+    {
+        const int ti = wave >> 1, tj = wave & 1;
+        const f32x16 t = mfma_tile_ab(A, 32 * ti, 64, Z, 64, 64 + 32 * tj, 64, lane);
+        __syncthreads();                                        // scratch of the level above is free
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Z[64 + 32 * ti + acc_row(v, lane)][32 * tj + (lane & 31)] = t[v];
+        __syncthreads();
+        const f32x16 u = mfma_tile_ab(Z, 32 * ti, 0, Z, 64, 32 * tj, 64, lane);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Z[32 * ti + acc_row(v, lane)][64 + 32 * tj + (lane & 31)] = -u[v];
+    }
+    __syncthreads();
+
+    for (int e = tid; e < CHOL_NB * CHOL_NB; e += 256) {
+        const int i = e >> 7, j = e & 127;
+        if (i < bs && j < bs) U[(k0 + i) * n + k0 + j] = j >= i ? Z[i][j] : 0.f;
+    }
 }
 
 // ------------------------------------------------------------------ epilogues

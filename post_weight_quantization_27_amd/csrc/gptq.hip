@@ -102,26 +102,23 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
     // diagonal block of U, zero outside the bw x bw panel (so padded columns never move)
     {
         constexpr int Q = PW * PW / 4 / NT;          // float4 per thread
-        float4 v[Q];
-        const bool vec = (a.n % 4 == 0);
+        if (a.bw == PW && (a.n % 4 == 0)) {          // full panel: plain 16-byte loads
+            float4 v[Q];
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int e = (tid + q * NT) * 4;
-            const int j = e / PW, c = e % PW;
-            const float* src = a.U + (a.b0 + j) * a.n + a.b0 + c;
-            if (j < a.bw && vec && c + 3 < a.bw) {
-                v[q] = *(const float4*)src;
-            } else {
-                float t[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) t[k] = (j < a.bw && c + k < a.bw) ? src[k] : 0.f;
-                v[q] = make_float4(t[0], t[1], t[2], t[3]);
+            for (int q = 0; q < Q; ++q) {
+                const int e = (tid + q * NT) * 4;
+                v[q] = *(const float4*)(a.U + (a.b0 + e / PW) * a.n + a.b0 + e % PW);
             }
-        }
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int e = (tid + q * NT) * 4;
-            *(float4*)&Ub[e / PW][e % PW] = v[q];
+            for (int q = 0; q < Q; ++q) {
+                const int e = (tid + q * NT) * 4;
+                *(float4*)&Ub[e / PW][e % PW] = v[q];
+            }
+        } else {                                     // ragged last panel
+            for (int e = tid; e < PW * PW; e += NT) {
+                const int j = e / PW, c = e % PW;
+                Ub[j][c] = (j < a.bw && c < a.bw) ? a.U[(a.b0 + j) * a.n + a.b0 + c] : 0.f;
+            }
         }
         for (int j = tid; j < PW; j += NT) dinv[j] = j < a.bw ? 1.0f / a.U[(a.b0 + j) * a.n + a.b0 + j] : 0.f;
     }
@@ -129,6 +126,8 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
 
     const int g = a.group_size;
     const int64_t rbase = (int64_t)blockIdx.x * NW * a.rows_per_wave;
+    // columns sharing one scale inside the panel: a group (g <= B) or the whole panel
+    const int seg = (g != 0 && a.gsmall) ? g : PW;
     for (int rr = 0; rr < a.rows_per_wave; ++rr) {
         const int64_t r = rbase + (int64_t)rr * NW + wave;
         if (r >= a.m) break;
@@ -139,24 +138,20 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
         float s = 0.f, rs = 0.f;
         if (g == 0) {
             s = f16_bits_to_f32(a.scales[r]);
-            rs = s > 0.f ? 1.0f / s : 0.f;
         } else if (!a.gsmall && !a.gstart0) {
             // a group wider than the panel that began in an earlier panel: its scale was
             // fixed (and stored) when the loop reached the group's first column
             s = f16_bits_to_f32(a.scales[r * a.ng + a.gbase]);
-            rs = s > 0.f ? 1.0f / s : 0.f;
         }
-#pragma unroll 4
-        for (int j = 0; j < PW; ++j) {
-            const bool gstart = g != 0 && j < a.bw && (a.gsmall ? ((j & (g - 1)) == 0) : (j == 0 && a.gstart0));
-            if (gstart) {
-                const int64_t col = a.b0 + j;
-                const int64_t G = a.gbase + (a.gsmall ? (j >> a.glog) : 0);
+        for (int j0 = 0; j0 < a.bw; j0 += seg) {
+            if (g != 0 && (a.gsmall || (j0 == 0 && a.gstart0))) {
+                const int64_t col = a.b0 + j0;
+                const int64_t G = a.gbase + (a.gsmall ? (j0 >> a.glog) : 0);
                 uint16_t sb;
                 if (a.fixed_scales) {
                     sb = a.scales[r * a.ng + G];
                 } else {
-                    // current values of the group's columns: panel columns [j, j+g) and, for a
+                    // current values of the group's columns: panel columns [j0, j0+g) and, for a
                     // group wider than the panel (it then starts at the panel's first column),
                     // the columns right of the panel, which hold every earlier update
                     const int64_t gend = col + g < a.n ? col + g : a.n;
@@ -164,7 +159,7 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
 #pragma unroll
                     for (int k = 0; k < NS; ++k) {
                         const int c = lane + 64 * k;
-                        if (c >= j && a.b0 + c < gend && c < a.bw) v = fmaxf(v, fabsf(w[k]));
+                        if (c >= j0 && a.b0 + c < gend && c < a.bw) v = fmaxf(v, fabsf(w[k]));
                     }
                     for (int64_t c = a.b0 + a.bw + lane; c < gend; c += 64) v = fmaxf(v, fabsf(wrow[c]));
                     v = wave_max(v);
@@ -172,27 +167,43 @@ __global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
                     if (lane == 0) a.scales[r * a.ng + G] = sb;
                 }
                 s = f16_bits_to_f32(sb);
-                rs = s > 0.f ? 1.0f / s : 0.f;
             }
-            // wj, s and rs are the same in every lane, so the branches below are uniform
-            const float wj = readlane_f(w[j >> 6], j & 63);
-            int q = 0;
-            if (s > 0.f) {
-                const float t = wj * rs;
-                const float lim = (float)(a.qmax + 1);
-                const float k = fminf(fmaxf(rintf(t), -lim), lim);
-                // |t - w/s| < 2e-6 here, so a distance below 0.49 from k already decides the
-                // nearest integer; only quotients near a half take the exact residual test
-                q = fabsf(t - k) <= 0.49f ? (int)fminf(fmaxf(k, (float)-a.qmax), (float)a.qmax)
-                                          : quant_code(wj, s, rs, a.qmax);
-            }
-            const float e = (wj - s * (float)q) * dinv[j];
-            if (lane == 0) {
-                esh[wave][j] = e;
-                qsh[wave][j] = (int8_t)q;
-            }
+            rs = s > 0.f ? 1.0f / s : 0.f;
+            const int j1 = j0 + seg < a.bw ? j0 + seg : a.bw;
+            // one column per step; wj, s and rs are the same in every lane, so the branches
+            // are uniform.  Columns [0, 64) live in w[0], [64, 128) in w[1].
+            auto column = [&](int j, float wj) {
+                int q = 0;
+                if (s > 0.f) {
+                    const float t = wj * rs;
+                    const float lim = (float)(a.qmax + 1);
+                    const float k = fminf(fmaxf(rintf(t), -lim), lim);
+                    // |t - w/s| < 2e-6 here, so a distance below 0.49 from k already decides the
+                    // nearest integer; only quotients near a half take the exact residual test
+                    q = fabsf(t - k) <= 0.49f ? (int)fminf(fmaxf(k, (float)-a.qmax), (float)a.qmax)
+                                              : quant_code(wj, s, rs, a.qmax);
+                }
+                const float e = (wj - s * (float)q) * dinv[j];
+                if (lane == 0) {
+                    esh[wave][j] = e;
+                    qsh[wave][j] = (int8_t)q;
+                }
+                return e;
+            };
+            const int jm = j1 < 64 ? j1 : 64;
+#pragma unroll 4
+            for (int j = j0; j < jm; ++j) {
+                const float e = column(j, readlane_f(w[0], j));
 #pragma unroll
-            for (int k = 0; k < NS; ++k) w[k] = fmaf(-e, Ub[j][64 * k + lane], w[k]);
+                for (int k = 0; k < NS; ++k) w[k] = fmaf(-e, Ub[j][64 * k + lane], w[k]);
+            }
+            if (NS == 2) {
+#pragma unroll 4
+                for (int j = j0 > 64 ? j0 : 64; j < j1; ++j) {
+                    const float e = column(j, readlane_f(w[NS - 1], j - 64));
+                    w[NS - 1] = fmaf(-e, Ub[j][64 * (NS - 1) + lane], w[NS - 1]);
+                }
+            }
         }
         float e_own[NS];
         int q_own[NS];
