@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--streams", type=int, default=1, help="1: one stream per layer (default), 0: all on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", default="", help="layers the oracle baseline runs (default: all)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (3 times), the reference for HBM traffic counters")
     return ap.parse_args()
 
 
@@ -115,7 +117,7 @@ def work_of(name, spec):
     if name == "gptq_quantize_layer":
         return "mfma_f32", m * n * (n - spec.block_size) + m * n * (spec.block_size - 1), "flop"
     if name == "recon_mse":
-        return "mfma_f32", 2 * (2 * N * n * m), "flop"
+        return ("mfma_bf16" if xb == 2 else "mfma_f32"), 2 * (2 * N * n * m), "flop"
     if name == "rtn_quantize":
         return "hbm", m * n * wb + m * n // 2 + 2 * m * ng, "byte"
     if name == "dequant":
@@ -149,12 +151,33 @@ def cpu_baseline(specs, synth, budget_layers):
             "sample": f"one full step of layers {','.join(names)} in float64 numpy ({dt:.1f} s)"}
 
 
+def copy_calibration(torch):
+    """A plain copy of 1 GiB, three times: each dispatch reads and writes exactly 1 GiB, so a
+    traffic counter's reading for it gives the factor between counter units and bytes."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    print(json.dumps({"copy_bytes_each_way": 4 * n, "ms_per_copy": round(ms, 4),
+                      "read_plus_write_GBps": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print("bench.py: this build measures one GPU; multi-GPU runs are not supported (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if a.copy_calibration:
+        copy_calibration(torch)
+        return
     from post_weight_quantization_27_amd import pwq, synth
     pwq.lib()
     specs = synth.workload(a.workload)
@@ -168,9 +191,11 @@ def main():
     # single-workgroup and few-workgroup kernels of one layer overlap with the others
     main = torch.cuda.current_stream()
     streams = [torch.cuda.Stream() for _ in layers] if a.streams else [main for _ in layers]
+    # the layer with the longest serial chain (largest d_in: most factor blocks) goes first
+    order = sorted(range(len(layers)), key=lambda i: -layers[i].spec.d_in)
 
     def step():
-        for L, st in zip(layers, streams):
+        for L, st in ((layers[i], streams[i]) for i in order):
             st.wait_stream(main)
             with torch.cuda.stream(st):
                 run_step(L, pwq)
@@ -179,6 +204,11 @@ def main():
 
     for _ in range(a.warmup):
         step()
+    torch.cuda.synchronize()
+    # host time to submit one step (no synchronisation inside), to see whether launches keep up
+    t_sub = time.perf_counter()
+    step()
+    submit_ms = (time.perf_counter() - t_sub) * 1e3
     torch.cuda.synchronize()
 
     # timed region: K steps, no per-call events (they would add records between launches)
@@ -233,8 +263,10 @@ def main():
                    "layer_streams": bool(a.streams)},
         "roofline": roof,
         "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
+        "breakdown_ms_by_layer": {f"{ln}/{nm}": round(v, 4) for (ln, nm), v in sorted(per.items(), key=lambda kv: -kv[1])},
         "mse_gptq_rtn": mses,
         "wall_s_timed": round(wall, 3),
+        "host_submit_ms_per_step": round(submit_ms, 3),
     }
     if not a.no_cpu_baseline:
         cl = set(a.cpu_layers.split(",")) if a.cpu_layers else set()

@@ -102,20 +102,38 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
     if (*info) return;
     __shared__ float A[CHOL_NB][LP];
     __shared__ float Z[CHOL_NB][LP];
-    __shared__ __attribute__((aligned(16))) float colb[2][CHOL_NB];
-    __shared__ float pivb[2];
+    __shared__ __attribute__((aligned(16))) float colb[2][4][CHOL_NB];
+    __shared__ __attribute__((aligned(16))) float pb[2][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    for (int e = tid; e < CHOL_NB * CHOL_NB; e += 256) {
-        const int i = e >> 7, j = e & 127;
-        float v = 0.f;
-        if (i <= j) v = j < bs ? U[(k0 + i) * n + k0 + j] : (i == j ? 1.f : 0.f);
-        A[i][j] = v;
-        Z[i][j] = 0.f;
+    // ---------------- load: thread = (row, 64-column half), all loads in flight
+    {
+        const int i = tid >> 1, c0 = 64 * (tid & 1);
+        const float* src = U + (k0 + i) * n + k0 + c0;
+        float v[64];
+        if (bs == CHOL_NB && (n % 4) == 0) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const float4 t = *(const float4*)(src + 4 * q);
+                v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 64; ++q) {
+                const int j = c0 + q;
+                v[q] = (i < bs && j < bs) ? src[q] : (i == j ? 1.f : 0.f);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            const int j = c0 + q;
+            A[i][j] = j >= i ? v[q] : 0.f;
+            Z[i][j] = 0.f;
+        }
     }
     __syncthreads();
 
-    // ---------------- factor
+    // ---------------- factor: 32-column panels from the right, 4 pivots per barrier
     const int rb = tid >> 3, cb = tid & 7;       // rows 4rb..4rb+3, panel columns 4cb..4cb+3
     for (int p = 3; p >= 0; --p) {
         const int c0 = 32 * p;
@@ -125,40 +143,108 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
         for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) a[ii][jj] = act ? A[4 * rb + ii][c0 + 4 * cb + jj] : 0.f;
-        for (int q = 7; q >= 0; --q) {
+        for (int g = 7; g >= 0; --g) {
+            const int clo = c0 + 4 * g;                  // pivots clo .. clo+3
+            const int buf = g & 1;
+            if (act && cb == g) {                        // owners hold all four pivot columns
 #pragma unroll
-            for (int jj = 3; jj >= 0; --jj) {
-                const int c = c0 + 4 * q + jj;
-                const int buf = c & 1;
-                if (act && cb == q) {
+                for (int jj = 0; jj < 4; ++jj) {
+                    float t[4];
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) colb[buf][4 * rb + ii] = (4 * rb + ii < c) ? a[ii][jj] : 0.f;
-                    if (rb == (c >> 2)) pivb[buf] = a[jj][jj];
+                    for (int ii = 0; ii < 4; ++ii) t[ii] = (4 * rb + ii < clo) ? a[ii][jj] : 0.f;
+                    *(float4*)&colb[buf][jj][4 * rb] = make_float4(t[0], t[1], t[2], t[3]);
                 }
-                __syncthreads();
-                const float d = pivb[buf];
-                if (!(d > 0.f)) {                        // same value in every thread
-                    if (tid == 0) *info = (int32_t)(k0 + c + 1);
-                    return;
+                if (rb == (clo >> 2)) {
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        *(float4*)&pb[buf][4 * ii] = make_float4(a[ii][0], a[ii][1], a[ii][2], a[ii][3]);
                 }
+            }
+            __syncthreads();
+            // the 4 x 4 pivot block D = Vd Vd^T (Vd upper), redundantly in every thread, and Zd = Vd^-1
+            float D[4][4], Vd[4][4], Zd[4][4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const float4 t = *(const float4*)&pb[buf][4 * ii];
+                D[ii][0] = t.x; D[ii][1] = t.y; D[ii][2] = t.z; D[ii][3] = t.w;
+            }
+            bool ok = true;
+#pragma unroll
+            for (int k = 3; k >= 0; --k) {
+                const float d = D[k][k];
+                ok = ok && (d > 0.f);
                 const float r = __builtin_amdgcn_sqrtf(d);
                 const float inv = __builtin_amdgcn_rcpf(r);
-                if (act) {
-                    const float inv2 = inv * inv;
-                    const float4 vr4 = *(const float4*)&colb[buf][4 * rb];
-                    const float4 vc4 = *(const float4*)&colb[buf][c0 + 4 * cb];
-                    const float vr[4] = {vr4.x, vr4.y, vr4.z, vr4.w};
-                    const float vc[4] = {vc4.x * inv2, vc4.y * inv2, vc4.z * inv2, vc4.w * inv2};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Vd[i][k] = i < k ? D[i][k] * inv : (i == k ? r : 0.f);
+#pragma unroll
+                for (int i = 0; i < k; ++i)
+#pragma unroll
+                    for (int j = i; j < k; ++j) D[i][j] = fmaf(-Vd[i][k], Vd[j][k], D[i][j]);
+            }
+            if (!ok) {                                   // same decision in every thread
+                if (tid == 0) {
+                    int bad = 0;                         // the last pivot (from the bottom) that failed
+                    float DD[4][4];
 #pragma unroll
                     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-                        for (int j2 = 0; j2 < 4; ++j2) a[ii][j2] = fmaf(-vr[ii], vc[j2], a[ii][j2]);
-                    if (cb == q) {
+                        for (int jj = 0; jj < 4; ++jj) DD[ii][jj] = pb[buf][4 * ii + jj];
+                    for (int k = 3; k >= 0; --k) {
+                        if (!(DD[k][k] > 0.f)) { bad = k; break; }
+                        const float r = sqrtf(DD[k][k]);
+                        for (int i = 0; i < k; ++i)
+                            for (int j = i; j < k; ++j) DD[i][j] -= (DD[i][k] / r) * (DD[j][k] / r);
+                    }
+                    *info = (int32_t)(k0 + clo + bad + 1);
+                }
+                return;
+            }
 #pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) {
-                            const int i = 4 * rb + ii;
-                            a[ii][jj] = i < c ? vr[ii] * inv : (i == c ? r : 0.f);
+            for (int i = 0; i < 4; ++i) {
+                Zd[i][i] = __builtin_amdgcn_rcpf(Vd[i][i]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j != i) Zd[i][j] = 0.f;
+            }
+#pragma unroll
+            for (int i = 2; i >= 0; --i)
+#pragma unroll
+                for (int j = i + 1; j < 4; ++j) {
+                    float sacc = 0.f;
+#pragma unroll
+                    for (int l = i + 1; l <= j; ++l) sacc = fmaf(Vd[i][l], Zd[l][j], sacc);
+                    Zd[i][j] = -sacc * Zd[i][i];
+                }
+            if (act) {
+                // V rows of this thread and of its panel columns: V[., clo+k] = raw[., l] Zd[k][l]
+                float vr[4][4], vc[4][4];
+#pragma unroll
+                for (int l = 0; l < 4; ++l) {
+                    const float4 x = *(const float4*)&colb[buf][l][4 * rb];
+                    const float4 y = *(const float4*)&colb[buf][l][c0 + 4 * cb];
+                    const float xr[4] = {x.x, x.y, x.z, x.w}, yc[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+                        for (int k = 0; k <= l; ++k) {
+                            if (l == k) { vr[ii][k] = xr[ii] * Zd[k][l]; vc[ii][k] = yc[ii] * Zd[k][l]; }
+                            else { vr[ii][k] = fmaf(xr[ii], Zd[k][l], vr[ii][k]); vc[ii][k] = fmaf(yc[ii], Zd[k][l], vc[ii][k]); }
                         }
+                }
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) a[ii][jj] = fmaf(-vr[ii][k], vc[jj][k], a[ii][jj]);
+                if (cb == g) {
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const int row = 4 * rb + ii;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            a[ii][k] = row < clo ? vr[ii][k] : (row - clo <= k && row < clo + 4 ? Vd[ii][k] : 0.f);
                     }
                 }
             }
@@ -184,30 +270,24 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
         }
     }
 
-    // ---------------- inverse: leaves (one wave per 32 x 32 diagonal block)
+    // ---------------- inverse: leaves, one wave per 32 x 32 diagonal block; lane j owns column
+    // j of Z and back-substitutes it from the broadcast rows of V (no cross-lane traffic)
     {
         const int o = 32 * wave;
-        const int j = lane & 31, h = lane >> 5;
-        float z[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) z[t] = (16 * h + t == j) ? 1.f : 0.f;
+        const int j = lane & 31;
+        float z[32];
 #pragma unroll
         for (int i = 31; i >= 0; --i) {
-            // row i of R at column j: in register i % 16 of the half that holds row i
-            const float own = z[i & 15];
-            const float other = __shfl_xor(own, 32, 64);
-            const float rij = (h == (i >> 4)) ? own : other;
-            const float inv = __builtin_amdgcn_rcpf(A[o + i][o + i]);
-            const float zi = rij * inv;
+            const float rv = __builtin_amdgcn_rcpf(A[o + i][o + i]);
+            float sacc = 0.f;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int rr = 16 * h + t;
-                if (rr < i) z[t] = fmaf(-A[o + rr][o + i], zi, z[t]);
-            }
-            if (h == (i >> 4)) z[i & 15] = zi;
+            for (int l = i + 1; l < 32; ++l) sacc = fmaf(A[o + i][o + l], z[l], sacc);
+            z[i] = (i == j) ? rv : (i < j ? -sacc * rv : 0.f);
         }
+        if (lane < 32) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) Z[o + 16 * h + t][o + j] = z[t];   // zeros below the diagonal
+            for (int i = 0; i < 32; ++i) Z[o + i][o + j] = z[i];
+        }
     }
     __syncthreads();
 
@@ -238,9 +318,27 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
     }
     __syncthreads();
 
-    for (int e = tid; e < CHOL_NB * CHOL_NB; e += 256) {
-        const int i = e >> 7, j = e & 127;
-        if (i < bs && j < bs) U[(k0 + i) * n + k0 + j] = j >= i ? Z[i][j] : 0.f;
+    // ---------------- store: thread = (row, 64-column half)
+    {
+        const int i = tid >> 1, c0 = 64 * (tid & 1);
+        float* dst = U + (k0 + i) * n + k0 + c0;
+        if (bs == CHOL_NB && (n % 4) == 0) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                float t[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int j = c0 + 4 * q + c;
+                    t[c] = j >= i ? Z[i][j] : 0.f;
+                }
+                *(float4*)(dst + 4 * q) = make_float4(t[0], t[1], t[2], t[3]);
+            }
+        } else if (i < bs) {
+            for (int q = 0; q < 64; ++q) {
+                const int j = c0 + q;
+                if (j < bs) dst[q] = j >= i ? Z[i][j] : 0.f;
+            }
+        }
     }
 }
 

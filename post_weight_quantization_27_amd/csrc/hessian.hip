@@ -7,7 +7,7 @@
 // only.  Small d_in gives few tiles, so the token range is cut into chunks whose partial
 // tiles land in a workspace and are summed in a fixed order (bit-reproducible, no
 // atomics).  A last pass copies the upper triangle onto the lower one.
-#include "gemm_f32.h"
+#include "gemm_bf16.h"
 #include "pwq_internal.h"
 
 namespace pwq {
@@ -112,6 +112,20 @@ __global__ __launch_bounds__(256) void act_order_kernel(const float* __restrict_
     if (i < n) perm[rank] = (int32_t)i;
 }
 
+// bfloat16 X: native bf16 MFMA (products exact in float32), 128 x 128 upper tiles
+hipError_t hess_gemm_bf16(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, float* part, const HessPlan& pl,
+                          hipStream_t s) {
+    const int vec = (ldx % 8 == 0) && aligned(X, 16);
+    Bf16KMajor a{(const uint16_t*)X, ldx, n, n_tok, vec, 0};
+    Bf16KMajor b{(const uint16_t*)X, ldx, n, n_tok, vec, GEMM_THREADS / 2};
+    UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr};
+    const int ntile = pl.tiles * (pl.tiles + 1) / 2;
+    EpiHess epi{H, part, n, ntile, 128, pl.splits == 1};
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 1, Bf16KMajor, Bf16KMajor, UpperMap, EpiHess>),
+                       dim3(ntile * pl.splits), dim3(GEMM_THREADS), 0, s, a, b, map, epi);
+    return hipGetLastError();
+}
+
 template <int BM, int DT>
 hipError_t hess_gemm(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, float* part, const HessPlan& pl,
                      hipStream_t s) {
@@ -127,18 +141,20 @@ hipError_t hess_gemm(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float
 
 }  // namespace
 
-HessPlan hessian_plan(int64_t n_tok, int64_t d_in) {
+HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype) {
     HessPlan p{};
-    p.bm = d_in <= 1024 ? 64 : 128;
+    const bool bf = x_dtype == 2;
+    p.bm = (!bf && d_in <= 1024) ? 64 : 128;
     p.tiles = (int)cdiv(d_in, p.bm);
     const int ntile = p.tiles * (p.tiles + 1) / 2;
-    const int64_t ksteps = cdiv(n_tok, GEMM_BK);
+    const int kq = bf ? BK16 : GEMM_BK;                  // chunk boundaries on whole k-tiles
+    const int64_t ksteps = cdiv(n_tok, kq);
     const int target = 1024;                         // >= 4 workgroups per CU of 256
     int64_t splits = ntile >= target ? 1 : cdiv(target, ntile);
     const int64_t max_splits = ksteps / 8 > 1 ? ksteps / 8 : 1;   // >= 256 tokens per chunk
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
-    p.kchunk = cdiv(ksteps, splits) * GEMM_BK;
+    p.kchunk = cdiv(ksteps, splits) * kq;
     p.splits = (int)cdiv(n_tok, p.kchunk);
     if (p.splits < 1) p.splits = 1;
     p.ws_bytes = p.splits > 1 ? (size_t)p.splits * ntile * p.bm * p.bm * sizeof(float) : 0;
@@ -148,13 +164,13 @@ HessPlan hessian_plan(int64_t n_tok, int64_t d_in) {
 hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* H, void* ws,
                           hipStream_t s) {
     if (n_tok == 0 || d_in == 0) return hipSuccess;
-    const HessPlan pl = hessian_plan(n_tok, d_in);
+    const HessPlan pl = hessian_plan(n_tok, d_in, x_dtype);
     float* part = (float*)ws;
     hipError_t e;
     if (x_dtype == 0) {
         e = pl.bm == 64 ? hess_gemm<64, 0>(X, n_tok, d_in, ldx, H, part, pl, s) : hess_gemm<128, 0>(X, n_tok, d_in, ldx, H, part, pl, s);
     } else {
-        e = pl.bm == 64 ? hess_gemm<64, 2>(X, n_tok, d_in, ldx, H, part, pl, s) : hess_gemm<128, 2>(X, n_tok, d_in, ldx, H, part, pl, s);
+        e = hess_gemm_bf16(X, n_tok, d_in, ldx, H, part, pl, s);
     }
     if (e != hipSuccess) return e;
     if (pl.splits > 1) {

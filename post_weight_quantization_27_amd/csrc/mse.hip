@@ -8,7 +8,7 @@
 // INT4 nibbles (or int8 codes) and scales and forms dW = W - What while staging the tile,
 // the epilogue squares and sums the output tile in registers; the product is never
 // written.  Per-workgroup partial sums (float64) are added in a fixed order.
-#include "gemm_f32.h"
+#include "gemm_bf16.h"
 #include "pwq_internal.h"
 
 namespace pwq {
@@ -97,6 +97,91 @@ struct OpDeltaW {
     }
 };
 
+// Same dW as OpDeltaW, for the bfloat16 engine: 8 consecutive columns per chunk, each value
+// split as hi = bf16(d), lo = bf16(d - hi); both tiles go to LDS (NSPLIT = 2).
+template <int DTW>
+struct Bf16DeltaWSplit {
+    typedef typename Elem<DTW>::T T;
+    const T* W;
+    int64_t ldw, M, K;
+    const uint8_t* packed;
+    const int8_t* codes;
+    const uint16_t* scales;
+    const int32_t* g_idx;
+    int64_t ng;
+    int g, vec;                      // vec: aligned rows, d_in % 8 == 0, one group per 8 columns
+
+    template <int BM>
+    struct Regs { uint4 hi[BM * BK16 / 8 / GEMM_THREADS], lo[BM * BK16 / 8 / GEMM_THREADS]; };
+
+    __device__ __forceinline__ float delta(int64_t o, int64_t c) const {
+        int q;
+        if (packed) {
+            const uint8_t b = packed[o * (K / 2) + c / 2];
+            q = (int)((c & 1) ? (b >> 4) : (b & 15)) - 8;
+        } else {
+            q = codes[o * K + c];
+        }
+        const int64_t G = g == 0 ? 0 : (g_idx ? (int64_t)g_idx[c] : c / g);
+        return Elem<DTW>::get(W, o * ldw + c) - f16_bits_to_f32(scales[o * ng + G]) * (float)q;
+    }
+
+    template <int BM>
+    __device__ __forceinline__ void load(Regs<BM>& r, int64_t m0, int64_t k0, int tid) const {
+        constexpr int NV = BM * BK16 / 8 / GEMM_THREADS;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = tid + i * GEMM_THREADS;
+            const int row = idx >> 3, kc = (idx & 7) * 8;
+            const int64_t o = m0 + row, c = k0 + kc;
+            float d[8];
+            if (o < M && vec && c + 7 < K) {
+                const float4 w0 = Elem<DTW>::get4(W, o * ldw + c), w1 = Elem<DTW>::get4(W, o * ldw + c + 4);
+                int q[8];
+                if (packed) {
+                    const uint32_t b = *(const uint32_t*)(packed + o * (K / 2) + c / 2);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) q[k] = (int)((b >> (4 * k)) & 15) - 8;
+                } else {
+                    const uint2 b = *(const uint2*)(codes + o * K + c);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        q[k] = (int8_t)((b.x >> (8 * k)) & 0xff);
+                        q[4 + k] = (int8_t)((b.y >> (8 * k)) & 0xff);
+                    }
+                }
+                const float s = f16_bits_to_f32(scales[o * ng + (g == 0 ? 0 : c / g)]);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) d[k] = wv[k] - s * (float)q[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) d[k] = (o < M && c + k < K) ? delta(o, c + k) : 0.f;
+            }
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint16_t h0 = f32_to_bf16_bits(d[2 * k]), h1 = f32_to_bf16_bits(d[2 * k + 1]);
+                h[k] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                l[k] = pack_bf16x2(d[2 * k] - bf16_bits_to_f32(h0), d[2 * k + 1] - bf16_bits_to_f32(h1));
+            }
+            r.hi[i] = make_uint4(h[0], h[1], h[2], h[3]);
+            r.lo[i] = make_uint4(l[0], l[1], l[2], l[3]);
+        }
+    }
+    template <int BM>
+    __device__ __forceinline__ void store(uint16_t* S, const Regs<BM>& r, int tid) const {
+        constexpr int NV = BM * BK16 / 8 / GEMM_THREADS;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = tid + i * GEMM_THREADS;
+            const int row = idx >> 3, kc = (idx & 7) * 8;
+            *(uint4*)(S + row * LROW + kc) = r.hi[i];
+            *(uint4*)(S + BM * LROW + row * LROW + kc) = r.lo[i];
+        }
+    }
+};
+
 // squares of the tile, summed per workgroup into part[blockIdx.x] (float64)
 struct EpiSq {
     double* part;
@@ -165,6 +250,35 @@ hipError_t mse_gemm(const void* X, int64_t n_tok, int64_t d_in, int64_t ldx, con
     return hipGetLastError();
 }
 
+// bfloat16 X: X is exact in bf16, dW rides as a bf16 hi + lo pair (two MFMAs per step)
+template <int DTW>
+hipError_t mse_gemm_bf16(const void* X, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W, int64_t ldw,
+                         const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
+                         int64_t d_out, int group_size, double* part, hipStream_t s, int64_t* nblocks) {
+    typedef typename Elem<DTW>::T TW;
+    Bf16MMajor a{(const uint16_t*)X, ldx, n_tok, d_in, (int)((ldx % 8 == 0) && aligned(X, 16))};
+    Bf16DeltaWSplit<DTW> b{};
+    b.W = (const TW*)W; b.ldw = ldw; b.M = d_out; b.K = d_in;
+    b.packed = packed; b.codes = codes; b.scales = scales; b.g_idx = g_idx;
+    b.ng = group_size == 0 ? 1 : cdiv(d_in, group_size);
+    b.g = group_size;
+    b.vec = (ldw % 8 == 0) && (d_in % 8 == 0) && aligned(W, 8 * sizeof(TW)) && !g_idx &&
+            (group_size == 0 || group_size % 8 == 0) && (!packed || aligned(packed, 4)) && (!codes || aligned(codes, 8));
+    RectMap mp{};
+    mp.M = n_tok; mp.N = d_out; mp.K = d_in;
+    mp.tiles_m = (int)cdiv(n_tok, 128);
+    mp.tiles_n = (int)cdiv(d_out, 128);
+    mp.splits = 1;
+    mp.kchunk = cdiv(d_in, BK16) * BK16;
+    mp.tri_k = 0;
+    mp.guard = nullptr;
+    EpiSq ep{part, n_tok, d_out, 0.f};
+    *nblocks = (int64_t)mp.tiles_m * mp.tiles_n;
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, Bf16MMajor, Bf16DeltaWSplit<DTW>, RectMap, EpiSq>),
+                       dim3((unsigned)*nblocks), dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
+    return hipGetLastError();
+}
+
 template <int BM>
 hipError_t mse_dispatch(int x_dtype, int w_dtype, const void* X, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W,
                         int64_t ldw, const uint8_t* packed, const int8_t* codes, const uint16_t* scales,
@@ -183,7 +297,8 @@ hipError_t mse_dispatch(int x_dtype, int w_dtype, const void* X, int64_t n_tok, 
 size_t mse_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out) {
     (void)d_in;
     const int bm = mse_bm(n_tok, d_out);
-    return (size_t)(cdiv(n_tok, bm) * cdiv(d_out, bm)) * sizeof(double);
+    const int64_t nf = cdiv(n_tok, bm) * cdiv(d_out, bm), nb = cdiv(n_tok, 128) * cdiv(d_out, 128);
+    return (size_t)(nf > nb ? nf : nb) * sizeof(double);
 }
 
 hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W, int w_dtype,
@@ -197,7 +312,10 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
     }
     double* part = (double*)ws;
     int64_t nb = 0;
-    if (mse_bm(n_tok, d_out) == 128)
+    if (x_dtype == 2)
+        e = w_dtype == 0 ? mse_gemm_bf16<0>(X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, &nb)
+                         : mse_gemm_bf16<1>(X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, &nb);
+    else if (mse_bm(n_tok, d_out) == 128)
         e = mse_dispatch<128>(x_dtype, w_dtype, X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, &nb);
     else
         e = mse_dispatch<64>(x_dtype, w_dtype, X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, &nb);

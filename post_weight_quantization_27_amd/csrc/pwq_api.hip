@@ -49,9 +49,8 @@ int pwq_last_hip_error(void) { return g_last_hip_error; }
 
 // ------------------------------------------------------------------ Hessian
 size_t pwq_hessian_workspace_size(int64_t n_tok, int64_t d_in, int x_dtype) {
-    (void)x_dtype;
     if (n_tok <= 0 || d_in <= 0 || bad_dim(n_tok) || bad_dim(d_in)) return 0;
-    return hessian_plan(n_tok, d_in).ws_bytes;
+    return hessian_plan(n_tok, d_in, x_dtype).ws_bytes;
 }
 
 pwq_status pwq_hessian_accumulate(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* H,

@@ -19,7 +19,7 @@ struct HessPlan {
     int64_t kchunk;    // tokens per chunk (multiple of 32)
     size_t ws_bytes;   // partial-tile workspace (0 when splits == 1)
 };
-HessPlan hessian_plan(int64_t n_tok, int64_t d_in);
+HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype);
 hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* H,
                           void* ws, hipStream_t s);
 hipError_t damp_launch(float* H, int64_t n, float damp, float* lambda_out, hipStream_t s);

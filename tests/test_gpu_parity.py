@@ -178,6 +178,16 @@ def test_hessian_bf16_strided_and_tiled(pwq):
     assert rel_frob(H3, want) <= 1e-5
 
 
+@pytest.mark.parametrize("n_tok,d_in", [(1000, 200), (77, 13), (4100, 1030)])
+def test_hessian_bf16_ragged(pwq, n_tok, d_in):
+    rng = np.random.default_rng(n_tok * 3 + d_in)
+    bits = synth.f64_to_bf16_bits(rng.standard_normal((n_tok, d_in)) * np.where(rng.random(d_in) < 0.02, 20.0, 1.0))
+    H = host(_hess(pwq, dev_bf16(bits), d_in))
+    want = O.hessian(synth.as_f64(bits, synth.BF16))
+    assert rel_frob(H, want) <= 1e-5
+    assert np.array_equal(H, H.T)
+
+
 def test_hessian_deterministic_and_empty(pwq):
     rng = np.random.default_rng(9)
     X = dev(rng.standard_normal((4096, 512)).astype(np.float32))
