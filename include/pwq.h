@@ -116,7 +116,9 @@ pwq_status pwq_act_order_perm(const float* H, int64_t d_in, int32_t* perm, void*
  * not NULL the factor is of P H P^T, i.e. of H[perm][:, perm].
  * Computed as H = V V^T (V upper: Cholesky eliminating from the last column to the
  * first) followed by U = V^-1, so H^-1 is never formed.
- *   H     n x n float32, read only (only the upper triangle is read).
+ *   H     n x n float32, read only.  Without perm only the upper triangle is read; with
+ *         perm the full rows perm[i] are read, so H must hold both triangles (as
+ *         pwq_hessian_accumulate writes it).
  *   U     n x n float32 output; the strictly lower triangle is written as 0.
  *   info  device int32: 0 on success; k > 0 if the pivot of column k-1 (in the order
  *         of P H P^T) was not positive, i.e. H is not positive definite.  U is then
