@@ -3,8 +3,8 @@
 // damp * mean(diag H) and the act-order permutation (desc_act of the same page,
 // section "Running GPTQ with AutoGPTQ").
 //
-// The contraction runs on the float32 MFMA engine over the upper-triangular tiles of H
-// only.  Small d_in gives few tiles, so the token range is cut into chunks whose partial
+// The contraction runs over the upper-triangular tiles of H only: float32 X on the float32
+// MFMA engine, bfloat16 X on the bfloat16 one (products exact, float32 accumulate).  Small d_in gives few tiles, so the token range is cut into chunks whose partial
 // tiles land in a workspace and are summed in a fixed order (bit-reproducible, no
 // atomics).  A last pass copies the upper triangle onto the lower one.
 #include "gemm_bf16.h"
@@ -112,16 +112,17 @@ __global__ __launch_bounds__(256) void act_order_kernel(const float* __restrict_
     if (i < n) perm[rank] = (int32_t)i;
 }
 
-// bfloat16 X: native bf16 MFMA (products exact in float32), 128 x 128 upper tiles
+// bfloat16 X: native bf16 MFMA (products exact in float32), 128 x 128 upper tiles; the two
+// operand loaders split the 256 threads (each tile operand has 128 transposing blocks)
 hipError_t hess_gemm_bf16(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, float* part, const HessPlan& pl,
                           hipStream_t s) {
     const int vec = (ldx % 8 == 0) && aligned(X, 16);
-    Bf16KMajor a{(const uint16_t*)X, ldx, n, n_tok, vec, 0};
-    Bf16KMajor b{(const uint16_t*)X, ldx, n, n_tok, vec, GEMM_THREADS / 2};
+    Bf16Cols a{(const uint16_t*)X, ldx, n, n_tok, vec, 0};
+    Bf16Cols b{(const uint16_t*)X, ldx, n, n_tok, vec, GEMM_THREADS / 2};
     UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
     EpiHess epi{H, part, n, ntile, 128, pl.splits == 1};
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 1, Bf16KMajor, Bf16KMajor, UpperMap, EpiHess>),
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, Bf16Cols, Bf16Cols, UpperMap, EpiHess>),
                        dim3(ntile * pl.splits), dim3(GEMM_THREADS), 0, s, a, b, map, epi);
     return hipGetLastError();
 }

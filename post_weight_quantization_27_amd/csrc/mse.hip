@@ -4,10 +4,15 @@
 //
 //   mse = sum_{t, o} (X (W - What)^T)[t, o]^2 / (n_tok * d_out)
 //
-// One fused pass on the float32 MFMA engine: the B operand loader decodes What from the
-// INT4 nibbles (or int8 codes) and scales and forms dW = W - What while staging the tile,
-// the epilogue squares and sums the output tile in registers; the product is never
-// written.  Per-workgroup partial sums (float64) are added in a fixed order.
+// Two passes.  A decode pass forms dW = W - What (What from the INT4 nibbles or int8 codes
+// and the scales, the product exact in float32) and stores it as a bfloat16 pair
+// hi = bf16(dW), lo = bf16(dW - hi), rows padded to a multiple of 64 with zeros.  The
+// contraction then runs on the bfloat16 MFMA engine with k doubled:
+//   X dW^T ~= [X, X] [dW_hi, dW_lo]^T,
+// X rounded once to bfloat16 (exact for bfloat16 X); the epilogue squares and sums the
+// output tile in registers, so the product is never written.  The pair keeps 16
+// significant bits of dW; rounding float32 X to bfloat16 adds about 2^-16 / 3 relative
+// to the mean square.  Per-workgroup partial sums (float64) are added in a fixed order.
 #include "gemm_bf16.h"
 #include "pwq_internal.h"
 
@@ -15,169 +20,110 @@ namespace pwq {
 
 namespace {
 
-// Element (o, c) = W[o][c] - s[o][group(c)] * code[o][c], rows of o with c contiguous.
+// dW[o][c] = W[o][c] - s[o][group(c)] * code[o][c] as a bfloat16 pair, ld = kseg (a multiple
+// of 64, columns d_in .. kseg-1 zero).  One thread per 8 columns of a row.
 template <int DTW>
-struct OpDeltaW {
-    static constexpr int PAD = 1;
+__global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict__ Wv, int64_t ldw, int64_t m, int64_t n,
+                                                         int64_t kseg, const uint8_t* __restrict__ packed,
+                                                         const int8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const int32_t* __restrict__ g_idx, int64_t ng, int g,
+                                                         int vec, uint16_t* __restrict__ dhi, uint16_t* __restrict__ dlo) {
     typedef typename Elem<DTW>::T T;
-    const T* W;
-    int64_t ldw, M, K;          // M = d_out, K = d_in
-    const uint8_t* packed;
-    const int8_t* codes;
-    const uint16_t* scales;
-    const int32_t* g_idx;
-    int64_t ng;
-    int g, vec;                 // vec: aligned W rows, d_in % 4 == 0, one group per quad
-
-    template <int BM>
-    struct Regs { float4 v[BM * GEMM_BK / (4 * GEMM_THREADS)]; };
-
-    __device__ __forceinline__ int code(int64_t o, int64_t c) const {
+    const T* W = (const T*)Wv;
+    const int64_t per_row = kseg / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= m * per_row) return;
+    const int64_t o = idx / per_row, c = (idx - o * per_row) * 8;
+    float d[8];
+    if (vec && c + 8 <= n) {
+        const float4 w0 = Elem<DTW>::get4(W, o * ldw + c), w1 = Elem<DTW>::get4(W, o * ldw + c + 4);
+        int q[8];
         if (packed) {
-            const uint8_t b = packed[o * (K / 2) + c / 2];
-            return (int)((c & 1) ? (b >> 4) : (b & 15)) - 8;
-        }
-        return codes[o * K + c];
-    }
-    __device__ __forceinline__ float scale(int64_t o, int64_t c) const {
-        const int64_t G = g == 0 ? 0 : (g_idx ? (int64_t)g_idx[c] : c / g);
-        return f16_bits_to_f32(scales[o * ng + G]);
-    }
-
-    template <int BM>
-    __device__ __forceinline__ void load(Regs<BM>& r, int64_t m0, int64_t k0, int tid) const {
-        constexpr int NV = BM * GEMM_BK / (4 * GEMM_THREADS);
-        constexpr int PER_ROW = GEMM_BK / 4;
+            const uint32_t b = *(const uint32_t*)(packed + o * (n / 2) + c / 2);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = tid + i * GEMM_THREADS;
-            const int mr = idx / PER_ROW, kc = (idx % PER_ROW) * 4;
-            const int64_t o = m0 + mr, c = k0 + kc;
-            float d[4] = {0.f, 0.f, 0.f, 0.f};
-            if (o < M) {
-                if (vec && c + 3 < K) {
-                    const float4 w = Elem<DTW>::get4(W, o * ldw + c);
-                    int q[4];
-                    if (packed) {
-                        const uint16_t b = *(const uint16_t*)(packed + o * (K / 2) + c / 2);
-                        q[0] = (int)(b & 15) - 8; q[1] = (int)((b >> 4) & 15) - 8;
-                        q[2] = (int)((b >> 8) & 15) - 8; q[3] = (int)((b >> 12) & 15) - 8;
-                    } else {
-                        const uint32_t b = *(const uint32_t*)(codes + o * K + c);
-                        q[0] = (int8_t)(b & 0xff); q[1] = (int8_t)((b >> 8) & 0xff);
-                        q[2] = (int8_t)((b >> 16) & 0xff); q[3] = (int8_t)(b >> 24);
-                    }
-                    const float s = scale(o, c);
-                    d[0] = w.x - s * (float)q[0];
-                    d[1] = w.y - s * (float)q[1];
-                    d[2] = w.z - s * (float)q[2];
-                    d[3] = w.w - s * (float)q[3];
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (c + k < K) d[k] = Elem<DTW>::get(W, o * ldw + c + k) - scale(o, c + k) * (float)code(o, c + k);
-                }
-            }
-            r.v[i] = make_float4(d[0], d[1], d[2], d[3]);
-        }
-    }
-    template <int BM>
-    __device__ __forceinline__ void store(float* S, const Regs<BM>& r, int tid) const {
-        constexpr int NV = BM * GEMM_BK / (4 * GEMM_THREADS);
-        constexpr int PER_ROW = GEMM_BK / 4;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = tid + i * GEMM_THREADS;
-            const int mr = idx / PER_ROW, kc = (idx % PER_ROW) * 4;
-            S[(kc + 0) * (BM + PAD) + mr] = r.v[i].x;
-            S[(kc + 1) * (BM + PAD) + mr] = r.v[i].y;
-            S[(kc + 2) * (BM + PAD) + mr] = r.v[i].z;
-            S[(kc + 3) * (BM + PAD) + mr] = r.v[i].w;
-        }
-    }
-};
-
-// Same dW as OpDeltaW, for the bfloat16 engine: 8 consecutive columns per chunk, each value
-// split as hi = bf16(d), lo = bf16(d - hi); both tiles go to LDS (NSPLIT = 2).
-template <int DTW>
-struct Bf16DeltaWSplit {
-    typedef typename Elem<DTW>::T T;
-    const T* W;
-    int64_t ldw, M, K;
-    const uint8_t* packed;
-    const int8_t* codes;
-    const uint16_t* scales;
-    const int32_t* g_idx;
-    int64_t ng;
-    int g, vec;                      // vec: aligned rows, d_in % 8 == 0, one group per 8 columns
-
-    template <int BM>
-    struct Regs { uint4 hi[BM * BK16 / 8 / GEMM_THREADS], lo[BM * BK16 / 8 / GEMM_THREADS]; };
-
-    __device__ __forceinline__ float delta(int64_t o, int64_t c) const {
-        int q;
-        if (packed) {
-            const uint8_t b = packed[o * (K / 2) + c / 2];
-            q = (int)((c & 1) ? (b >> 4) : (b & 15)) - 8;
+            for (int k = 0; k < 8; ++k) q[k] = (int)((b >> (4 * k)) & 15) - 8;
         } else {
-            q = codes[o * K + c];
-        }
-        const int64_t G = g == 0 ? 0 : (g_idx ? (int64_t)g_idx[c] : c / g);
-        return Elem<DTW>::get(W, o * ldw + c) - f16_bits_to_f32(scales[o * ng + G]) * (float)q;
-    }
-
-    template <int BM>
-    __device__ __forceinline__ void load(Regs<BM>& r, int64_t m0, int64_t k0, int tid) const {
-        constexpr int NV = BM * BK16 / 8 / GEMM_THREADS;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = tid + i * GEMM_THREADS;
-            const int row = idx >> 3, kc = (idx & 7) * 8;
-            const int64_t o = m0 + row, c = k0 + kc;
-            float d[8];
-            if (o < M && vec && c + 7 < K) {
-                const float4 w0 = Elem<DTW>::get4(W, o * ldw + c), w1 = Elem<DTW>::get4(W, o * ldw + c + 4);
-                int q[8];
-                if (packed) {
-                    const uint32_t b = *(const uint32_t*)(packed + o * (K / 2) + c / 2);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) q[k] = (int)((b >> (4 * k)) & 15) - 8;
-                } else {
-                    const uint2 b = *(const uint2*)(codes + o * K + c);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        q[k] = (int8_t)((b.x >> (8 * k)) & 0xff);
-                        q[4 + k] = (int8_t)((b.y >> (8 * k)) & 0xff);
-                    }
-                }
-                const float s = f16_bits_to_f32(scales[o * ng + (g == 0 ? 0 : c / g)]);
-                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-                for (int k = 0; k < 8; ++k) d[k] = wv[k] - s * (float)q[k];
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) d[k] = (o < M && c + k < K) ? delta(o, c + k) : 0.f;
-            }
-            uint32_t h[4], l[4];
+            const uint2 b = *(const uint2*)(codes + o * n + c);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const uint16_t h0 = f32_to_bf16_bits(d[2 * k]), h1 = f32_to_bf16_bits(d[2 * k + 1]);
-                h[k] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                l[k] = pack_bf16x2(d[2 * k] - bf16_bits_to_f32(h0), d[2 * k + 1] - bf16_bits_to_f32(h1));
+                q[k] = (int8_t)((b.x >> (8 * k)) & 0xff);
+                q[4 + k] = (int8_t)((b.y >> (8 * k)) & 0xff);
             }
-            r.hi[i] = make_uint4(h[0], h[1], h[2], h[3]);
-            r.lo[i] = make_uint4(l[0], l[1], l[2], l[3]);
+        }
+        const float sc = f16_bits_to_f32(scales[o * ng + (g == 0 ? 0 : c / g)]);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = wv[k] - sc * (float)q[k];
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t cc = c + k;
+            if (cc >= n) { d[k] = 0.f; continue; }
+            int q;
+            if (packed) {
+                const uint8_t b = packed[o * (n / 2) + cc / 2];
+                q = (int)((cc & 1) ? (b >> 4) : (b & 15)) - 8;
+            } else {
+                q = codes[o * n + cc];
+            }
+            const int64_t G = g == 0 ? 0 : (g_idx ? (int64_t)g_idx[cc] : cc / g);
+            d[k] = Elem<DTW>::get(W, o * ldw + cc) - f16_bits_to_f32(scales[o * ng + G]) * (float)q;
         }
     }
-    template <int BM>
-    __device__ __forceinline__ void store(uint16_t* S, const Regs<BM>& r, int tid) const {
-        constexpr int NV = BM * BK16 / 8 / GEMM_THREADS;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint16_t h0 = f32_to_bf16_bits(d[2 * k]), h1 = f32_to_bf16_bits(d[2 * k + 1]);
+        h[k] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        l[k] = pack_bf16x2(d[2 * k] - bf16_bits_to_f32(h0), d[2 * k + 1] - bf16_bits_to_f32(h1));
+    }
+    *(uint4*)(dhi + o * kseg + c) = make_uint4(h[0], h[1], h[2], h[3]);
+    *(uint4*)(dlo + o * kseg + c) = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// float32 X (element (t, c) at p[t * ld + c]) rounded once to bfloat16 while staging; the
+// logical k range is two copies of [0, kseg) (the two halves of the dW pair).
+struct F32RowsBf16 {
+    const float* p;
+    int64_t ld, M, K, kseg;
+    int vec;                         // ld % 4 == 0 and p 16-byte aligned
+    template <int ROWS>
+    struct Regs { uint4 v[ROWS * 8 / GEMM_THREADS]; };
+    template <int ROWS>
+    __device__ __forceinline__ void load(Regs<ROWS>& r, int64_t m0, int64_t k0, int tid) const {
+        constexpr int NV = ROWS * 8 / GEMM_THREADS;
+        const int64_t kk = k0 >= kseg ? k0 - kseg : k0;
+        const int rl = tid >> 3, c = tid & 7;
+        const uint32_t loff = (uint32_t)(((int64_t)rl * ld + 8 * c) * 4);
+        const bool full = vec && (m0 + ROWS <= M) && (kk + BK16 <= K);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const float* ub = p + (m0 + 32 * i) * ld + kk;
+            float x[8];
+            if (full) {
+                const float4 x0 = *(const float4*)((const char*)ub + loff);
+                const float4 x1 = *(const float4*)((const char*)ub + loff + 16);
+                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+                x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+            } else {
+                const bool rok = m0 + 32 * i + rl < M;
+                const float* e = (const float*)((const char*)ub + loff);
+                const int64_t kc = kk + 8 * c;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) x[q] = (rok && kc + q < K) ? e[q] : 0.f;
+            }
+            r.v[i] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                                pack_bf16x2(x[6], x[7]));
+        }
+    }
+    template <int ROWS>
+    __device__ __forceinline__ void store(uint16_t* S, const Regs<ROWS>& r, int tid) const {
+        constexpr int NV = ROWS * 8 / GEMM_THREADS;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = tid + i * GEMM_THREADS;
-            const int row = idx >> 3, kc = (idx & 7) * 8;
-            *(uint4*)(S + row * LROW + kc) = r.hi[i];
-            *(uint4*)(S + BM * LROW + row * LROW + kc) = r.lo[i];
+            *(uint4*)(S + lds_off(idx >> 3, idx & 7)) = r.v[i];
         }
     }
 };
@@ -219,86 +165,36 @@ __global__ __launch_bounds__(256) void mse_final_kernel(const double* __restrict
 
 __global__ void set_double_kernel(double* p, double v) { *p = v; }
 
-inline int mse_bm(int64_t n_tok, int64_t d_out) { return cdiv(n_tok, 128) * cdiv(d_out, 128) >= 512 ? 128 : 64; }
+constexpr int MSE_TILE = 128;
 
-template <int BM, int DTX, int DTW>
-hipError_t mse_gemm(const void* X, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W, int64_t ldw,
-                    const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx, int64_t d_out,
-                    int group_size, double* part, hipStream_t s, int64_t* nblocks) {
-    typedef typename Elem<DTX>::T TX;
-    typedef typename Elem<DTW>::T TW;
-    OpMMajor<DTX> a{(const TX*)X, ldx, n_tok, d_in, (int)((ldx % 4 == 0) && aligned(X, 4 * sizeof(TX)))};
-    OpDeltaW<DTW> b{};
-    b.W = (const TW*)W; b.ldw = ldw; b.M = d_out; b.K = d_in;
-    b.packed = packed; b.codes = codes; b.scales = scales; b.g_idx = g_idx;
-    b.ng = group_size == 0 ? 1 : cdiv(d_in, group_size);
-    b.g = group_size;
-    b.vec = (ldw % 4 == 0) && (d_in % 4 == 0) && aligned(W, 4 * sizeof(TW)) && !g_idx &&
-            (group_size == 0 || group_size % 4 == 0) && (!packed || aligned(packed, 2)) && (!codes || aligned(codes, 4));
+inline int64_t mse_kseg(int64_t d_in) { return cdiv(d_in, BK16) * BK16; }
+
+template <class LA>
+hipError_t mse_gemm(const LA& a, int64_t n_tok, int64_t d_out, int64_t kseg, const uint16_t* dhi, const uint16_t* dlo,
+                    double* part, hipStream_t s, int64_t* nblocks) {
+    Bf16Rows b{dhi, dlo, kseg, d_out, kseg, kseg, (int)(aligned(dhi, 16) && aligned(dlo, 16))};
     RectMap mp{};
-    mp.M = n_tok; mp.N = d_out; mp.K = d_in;
-    mp.tiles_m = (int)cdiv(n_tok, BM);
-    mp.tiles_n = (int)cdiv(d_out, BM);
+    mp.M = n_tok; mp.N = d_out; mp.K = 2 * kseg;
+    mp.tiles_m = (int)cdiv(n_tok, MSE_TILE);
+    mp.tiles_n = (int)cdiv(d_out, MSE_TILE);
     mp.splits = 1;
-    mp.kchunk = cdiv(d_in, GEMM_BK) * GEMM_BK;
+    mp.kchunk = 2 * kseg;
     mp.tri_k = 0;
     mp.guard = nullptr;
     EpiSq ep{part, n_tok, d_out, 0.f};
     *nblocks = (int64_t)mp.tiles_m * mp.tiles_n;
-    hipLaunchKernelGGL((gemm_f32_kernel<BM, BM, OpMMajor<DTX>, OpDeltaW<DTW>, RectMap, EpiSq>), dim3((unsigned)*nblocks),
+    hipLaunchKernelGGL((gemm_bf16_kernel<MSE_TILE, MSE_TILE, LA, Bf16Rows, RectMap, EpiSq>), dim3((unsigned)*nblocks),
                        dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
     return hipGetLastError();
 }
 
-// bfloat16 X: X is exact in bf16, dW rides as a bf16 hi + lo pair (two MFMAs per step)
-template <int DTW>
-hipError_t mse_gemm_bf16(const void* X, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W, int64_t ldw,
-                         const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
-                         int64_t d_out, int group_size, double* part, hipStream_t s, int64_t* nblocks) {
-    typedef typename Elem<DTW>::T TW;
-    Bf16MMajor a{(const uint16_t*)X, ldx, n_tok, d_in, (int)((ldx % 8 == 0) && aligned(X, 16))};
-    Bf16DeltaWSplit<DTW> b{};
-    b.W = (const TW*)W; b.ldw = ldw; b.M = d_out; b.K = d_in;
-    b.packed = packed; b.codes = codes; b.scales = scales; b.g_idx = g_idx;
-    b.ng = group_size == 0 ? 1 : cdiv(d_in, group_size);
-    b.g = group_size;
-    b.vec = (ldw % 8 == 0) && (d_in % 8 == 0) && aligned(W, 8 * sizeof(TW)) && !g_idx &&
-            (group_size == 0 || group_size % 8 == 0) && (!packed || aligned(packed, 4)) && (!codes || aligned(codes, 8));
-    RectMap mp{};
-    mp.M = n_tok; mp.N = d_out; mp.K = d_in;
-    mp.tiles_m = (int)cdiv(n_tok, 128);
-    mp.tiles_n = (int)cdiv(d_out, 128);
-    mp.splits = 1;
-    mp.kchunk = cdiv(d_in, BK16) * BK16;
-    mp.tri_k = 0;
-    mp.guard = nullptr;
-    EpiSq ep{part, n_tok, d_out, 0.f};
-    *nblocks = (int64_t)mp.tiles_m * mp.tiles_n;
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, Bf16MMajor, Bf16DeltaWSplit<DTW>, RectMap, EpiSq>),
-                       dim3((unsigned)*nblocks), dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
-    return hipGetLastError();
-}
-
-template <int BM>
-hipError_t mse_dispatch(int x_dtype, int w_dtype, const void* X, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W,
-                        int64_t ldw, const uint8_t* packed, const int8_t* codes, const uint16_t* scales,
-                        const int32_t* g_idx, int64_t d_out, int group_size, double* part, hipStream_t s, int64_t* nb) {
-    if (x_dtype == 0 && w_dtype == 0)
-        return mse_gemm<BM, 0, 0>(X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, nb);
-    if (x_dtype == 0)
-        return mse_gemm<BM, 0, 1>(X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, nb);
-    if (w_dtype == 0)
-        return mse_gemm<BM, 2, 0>(X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, nb);
-    return mse_gemm<BM, 2, 1>(X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, nb);
-}
-
 }  // namespace
 
+// workspace: dW pair (2 x d_out x kseg bfloat16), then one float64 partial per tile
 size_t mse_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out) {
-    (void)d_in;
-    const int bm = mse_bm(n_tok, d_out);
-    const int64_t nf = cdiv(n_tok, bm) * cdiv(d_out, bm), nb = cdiv(n_tok, 128) * cdiv(d_out, 128);
-    return (size_t)(nf > nb ? nf : nb) * sizeof(double);
+    const size_t dw = align_up((size_t)(2 * d_out * mse_kseg(d_in)) * sizeof(uint16_t), 256);
+    const int64_t nb = cdiv(n_tok, MSE_TILE) * cdiv(d_out, MSE_TILE);
+    return dw + (size_t)nb * sizeof(double);
 }
 
 hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W, int w_dtype,
@@ -310,15 +206,33 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
         hipLaunchKernelGGL(set_double_kernel, dim3(1), dim3(1), 0, s, mse, 0.0);
         return hipGetLastError();
     }
-    double* part = (double*)ws;
-    int64_t nb = 0;
-    if (x_dtype == 2)
-        e = w_dtype == 0 ? mse_gemm_bf16<0>(X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, &nb)
-                         : mse_gemm_bf16<1>(X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, &nb);
-    else if (mse_bm(n_tok, d_out) == 128)
-        e = mse_dispatch<128>(x_dtype, w_dtype, X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, &nb);
+    const int64_t kseg = mse_kseg(d_in);
+    uint16_t* dhi = (uint16_t*)ws;
+    uint16_t* dlo = dhi + d_out * kseg;
+    double* part = (double*)((char*)ws + align_up((size_t)(2 * d_out * kseg) * sizeof(uint16_t), 256));
+
+    const int64_t ng = group_size == 0 ? 1 : cdiv(d_in, group_size);
+    const size_t wsz = w_dtype == 0 ? 4 : 2;
+    const int vec = (ldw % 8 == 0) && (d_in % 8 == 0) && aligned(W, 8 * wsz) && !g_idx &&
+                    (group_size == 0 || group_size % 8 == 0) && (!packed || aligned(packed, 4)) &&
+                    (!codes || aligned(codes, 8));
+    const unsigned dgrid = (unsigned)cdiv(d_out * (kseg / 8), 256);
+    if (w_dtype == 0)
+        hipLaunchKernelGGL(mse_decode_kernel<0>, dim3(dgrid), dim3(256), 0, s, W, ldw, d_out, d_in, kseg, packed, codes,
+                           scales, g_idx, ng, group_size, vec, dhi, dlo);
     else
-        e = mse_dispatch<64>(x_dtype, w_dtype, X, n_tok, d_in, ldx, W, ldw, packed, codes, scales, g_idx, d_out, group_size, part, s, &nb);
+        hipLaunchKernelGGL(mse_decode_kernel<1>, dim3(dgrid), dim3(256), 0, s, W, ldw, d_out, d_in, kseg, packed, codes,
+                           scales, g_idx, ng, group_size, vec, dhi, dlo);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    int64_t nb = 0;
+    if (x_dtype == 2) {
+        Bf16Rows a{(const uint16_t*)X, (const uint16_t*)X, ldx, n_tok, d_in, kseg, (int)((ldx % 8 == 0) && aligned(X, 16))};
+        e = mse_gemm(a, n_tok, d_out, kseg, dhi, dlo, part, s, &nb);
+    } else {
+        F32RowsBf16 a{(const float*)X, ldx, n_tok, d_in, kseg, (int)((ldx % 4 == 0) && aligned(X, 16))};
+        e = mse_gemm(a, n_tok, d_out, kseg, dhi, dlo, part, s, &nb);
+    }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(256), 0, s, part, nb, (double)n_tok * (double)d_out, mse);
     return hipGetLastError();
