@@ -64,9 +64,9 @@ typedef enum pwq_dtype {
  *   bits        2..8
  *   group_size  0 = one scale per output row ([GPT2-RE]); else an even number >= 2 of
  *               consecutive input columns sharing one scale ([MQM] "Group-wise
- *               Quantization").  For GPTQ, group_size must divide block_size or be a
- *               multiple of it, so a group never starts inside a block and ends
- *               after it.
+ *               Quantization").  For GPTQ, group_size must be a multiple of 32 that
+ *               divides block_size or is a multiple of it, so a group never starts
+ *               inside a block and ends after it.
  *   block_size  GPTQ lazy-batch width B: 32, 64 or 128.
  *   act_order   nonzero: columns were processed in the order `perm` (desc_act). */
 typedef struct pwq_params {

@@ -22,6 +22,9 @@ SOURCES = ["hessian.hip", "chol.hip", "gptq.hip", "rtn.hip", "mse.hip", "pwq_api
 ARCH = os.environ.get("PWQ_OFFLOAD_ARCH", "gfx950")
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # the GPTQ column loop is unrolled in full (static register indices); its body is
+          # larger than LLVM's default limit for pragma-requested unrolling
+          "-mllvm", "-pragma-unroll-threshold=1000000",
           "-I", os.path.join(ROOT, "include")]
 
 

@@ -7,13 +7,18 @@
 // Kernels per layer:
 //   prologue : float32 working copy Wf of W (columns permuted for act-order), per-row
 //              scales from the original row, copy of caller-fixed scales
-//   block    : one wave64 per row; lane l holds panel columns l and l+64 in registers, the
-//              B x B diagonal block of U sits in LDS.  For each column j the owner value is
-//              broadcast with readlane, quantized (exact-quotient rounding), e = (w - s q) /
-//              U_jj, and every lane applies w -= e U[j][col] to its two columns (U is upper
-//              triangular, so columns <= j are unaffected or already final).  Group scales
-//              are a wave max-reduction over the group's current values.  Writes codes (or
-//              INT4 nibbles directly), scales, and the error panel Err (m x B).
+//   block    : four lanes per row (a quad), sixteen rows per wave64: lane p of a quad holds
+//              the panel columns 4 i + p (i < B/4) in registers, and the B x B diagonal block
+//              of U sits in LDS split by p, so every lane reads its U entries of row j with
+//              16-byte broadcast loads.  For column j the owner value is broadcast inside the
+//              quad with one DPP move; all four lanes quantize it (exact-quotient rounding)
+//              and form e = (w - s q) / U_jj redundantly, and each lane applies
+//              w -= e U[j][col] to its columns at or right of j (U is upper triangular, so
+//              finished columns see zeros; the owner's own column is no longer read).  The
+//              loop over j is fully unrolled so the register of column j is static.  Group
+//              scales are a max over the group's registers plus two DPP steps.  Writes the
+//              error panel Err (m x B), codes or INT4 nibbles (staged per wave in LDS) and
+//              scales.
 //   trailing : Wf[:, end:] -= Err U[block, end:]  (float32 MFMA engine)
 //   finish   : act-order only: codes back to the original column order, nibble packing and
 //              g_idx.
@@ -68,8 +73,25 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
     }
 }
 
-__device__ __forceinline__ float readlane_f(float v, int lane) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+// DPP quad permutations: every lane of a quad takes lane P's value / a neighbour's value
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int P>
+__device__ __forceinline__ float quad_bcast(float v) { return dpp_f<P * 0x55>(v); }
+// the lane index folds to a constant once the column loop is unrolled
+__device__ __forceinline__ float quad_bcast_of(float v, int src) {
+    switch (src) {
+        case 0: return quad_bcast<0>(v);
+        case 1: return quad_bcast<1>(v);
+        case 2: return quad_bcast<2>(v);
+        default: return quad_bcast<3>(v);
+    }
+}
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));        // quad_perm [1, 0, 3, 2]
+    return fmaxf(v, dpp_f<0x4E>(v));     // quad_perm [2, 3, 0, 1]
 }
 
 struct BlockArgs {
@@ -77,9 +99,9 @@ struct BlockArgs {
     const float* U;
     const int32_t* info;
     int64_t m, n, b0;
-    int bw, group_size, qmax, fixed_scales, rows_per_wave;
-    int gsmall, glog, gstart0;   // g <= B: groups start where (j & (g-1)) == 0; g > B: at j == 0 iff gstart0
-    int64_t gbase;               // group index of the panel's first column
+    int bw, group_size, qmax, fixed_scales;
+    int gsmall, gstart0;     // g <= B: groups start at panel columns j with j % g == 0; g > B: at j == 0 iff gstart0
+    int64_t gbase;           // group index of the panel's first column
     uint16_t* scales;        // d_out x ng (already holds per-row / fixed scales)
     int64_t ng;
     int8_t* codes;           // processing order, ld n (nullable)
@@ -87,153 +109,374 @@ struct BlockArgs {
     float* err;              // m x GB
 };
 
-// NS = 1: panel of 64 columns (block sizes 32 and 64), NS = 2: 128 columns.
-template <int NT, int NS>
-__global__ __launch_bounds__(NT) void gptq_block_kernel(BlockArgs a) {
-    if (*a.info) return;
-    constexpr int PW = 64 * NS;
-    constexpr int NW = NT / 64;
-    __shared__ __attribute__((aligned(16))) float Ub[PW][PW];
-    __shared__ float dinv[PW];
-    __shared__ float esh[NW][PW];      // per-wave staging of the column results
-    __shared__ int8_t qsh[NW][PW];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    // diagonal block of U, zero outside the bw x bw panel (so padded columns never move)
-    {
-        constexpr int Q = PW * PW / 4 / NT;          // float4 per thread
-        if (a.bw == PW && (a.n % 4 == 0)) {          // full panel: plain 16-byte loads
-            float4 v[Q];
+// The panel's diagonal block of U (zero outside bw x bw), read as float4 rows with every
+// load of a thread in flight before any is used: element e4 = tid + q NT of the PW x PW / 4
+// float4 grid holds U[b0 + j][b0 + c .. c + 3], j = 4 e4 / PW, c = 4 e4 % PW.
+template <int PW, int NT>
+struct UBlock {
+    static constexpr int N4 = PW * PW / 4;
+    static constexpr int Q = (N4 + NT - 1) / NT;
+    float4 v[Q];
+    __device__ __forceinline__ static bool has(int tid, int q) { return N4 % NT == 0 || tid + q * NT < N4; }
+    __device__ __forceinline__ void load(const float* U, int64_t n, int64_t b0, int bw, int tid) {
+        const bool vec = (bw == PW) && (n % 4 == 0);
 #pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                const int e = (tid + q * NT) * 4;
-                v[q] = *(const float4*)(a.U + (a.b0 + e / PW) * a.n + a.b0 + e % PW);
-            }
+        for (int q = 0; q < Q; ++q) {
+            if (!has(tid, q)) break;
+            const int e = 4 * (tid + q * NT);
+            const int j = e / PW, c = e % PW;
+            const float* src = U + (b0 + j) * n + b0 + c;
+            if (vec) {
+                v[q] = *(const float4*)src;
+            } else {
+                float t[4];
 #pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                const int e = (tid + q * NT) * 4;
-                *(float4*)&Ub[e / PW][e % PW] = v[q];
-            }
-        } else {                                     // ragged last panel
-            for (int e = tid; e < PW * PW; e += NT) {
-                const int j = e / PW, c = e % PW;
-                Ub[j][c] = (j < a.bw && c < a.bw) ? a.U[(a.b0 + j) * a.n + a.b0 + c] : 0.f;
+                for (int k = 0; k < 4; ++k) t[k] = (j < bw && c + k < bw) ? src[k] : 0.f;
+                v[q] = make_float4(t[0], t[1], t[2], t[3]);
             }
         }
-        for (int j = tid; j < PW; j += NT) dinv[j] = j < a.bw ? 1.0f / a.U[(a.b0 + j) * a.n + a.b0 + j] : 0.f;
+    }
+};
+
+// PW: panel width (the block size B); NWV: waves per workgroup (16 rows each).
+template <int PW, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
+    if (*a.info) return;
+    constexpr int NT = NWV * 64;
+    constexpr int NC = PW / 4;           // columns per lane
+    constexpr int UST = NC + 4;          // LDS stride of one lane slice of a U row (16-byte aligned, bank spread)
+    __shared__ __attribute__((aligned(16))) float Ub[PW][4][UST];
+    __shared__ float dinv[PW];
+    __shared__ __attribute__((aligned(16))) int8_t cst[NWV][16][PW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int p = lane & 3, rq = lane >> 2;
+
+    // diagonal block of U, zero outside the bw x bw panel (so padded columns never move),
+    // split by quad lane: Ub[j][c & 3][c >> 2] = U[b0 + j][b0 + c]
+    {
+        UBlock<PW, NT> ub;
+        ub.load(a.U, a.n, a.b0, a.bw, tid);
+        float dv = 0.f;
+        if (tid < PW && tid < a.bw) dv = 1.0f / a.U[(a.b0 + tid) * a.n + a.b0 + tid];
+#pragma unroll
+        for (int q = 0; q < UBlock<PW, NT>::Q; ++q) {
+            if (!UBlock<PW, NT>::has(tid, q)) break;
+            const int e = 4 * (tid + q * NT);
+            const int j = e / PW, c = e % PW;        // c % 4 == 0: the four go to lanes 0..3
+            Ub[j][0][c >> 2] = ub.v[q].x;
+            Ub[j][1][c >> 2] = ub.v[q].y;
+            Ub[j][2][c >> 2] = ub.v[q].z;
+            Ub[j][3][c >> 2] = ub.v[q].w;
+        }
+        if (tid < PW) dinv[tid] = dv;
     }
     __syncthreads();
 
+    const int64_t r = (int64_t)blockIdx.x * (NWV * 16) + wave * 16 + rq;
+    const bool live = r < a.m;
+    const float* wrow = a.Wf + (live ? r : 0) * a.n;
+    float w[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) w[i] = (live && 4 * i + p < a.bw) ? wrow[a.b0 + 4 * i + p] : 0.f;
+
     const int g = a.group_size;
-    const int64_t rbase = (int64_t)blockIdx.x * NW * a.rows_per_wave;
-    // columns sharing one scale inside the panel: a group (g <= B) or the whole panel
-    const int seg = (g != 0 && a.gsmall) ? g : PW;
-    for (int rr = 0; rr < a.rows_per_wave; ++rr) {
-        const int64_t r = rbase + (int64_t)rr * NW + wave;
-        if (r >= a.m) break;
-        float* wrow = a.Wf + r * a.n;
+    float s = 0.f;
+    if (g == 0) {
+        s = live ? f16_bits_to_f32(a.scales[r]) : 0.f;
+    } else if (!a.gsmall && !a.gstart0) {
+        // a group wider than the panel that began in an earlier panel: its scale was fixed
+        // (and stored) when the loop reached the group's first column
+        s = live ? f16_bits_to_f32(a.scales[r * a.ng + a.gbase]) : 0.f;
+    }
+    float rs = s > 0.f ? 1.0f / s : 0.f;
+    float eown[NC];
+    uint32_t qb[(NC + 3) / 4];
+#pragma unroll
+    for (int i = 0; i < (NC + 3) / 4; ++i) qb[i] = 0u;
+
+    // All PW columns are processed (a constant trip count keeps the loop unrolled, so every
+    // register index is static): columns at or past bw hold 0 with zero rows of U and dinv,
+    // so they yield q = e = 0 and are never written.  Steps go in windows of four columns
+    // (the four lanes' columns of one register): the window's rows of U are read at its
+    // start, and its results are pinned at its end.  Inside a window the scheduler is free
+    // to hide the next column's dependency chain behind the current column's off-chain
+    // updates; the pins keep the compiler from sinking update chains to their last use
+    // (which would keep every step's e and U values live at once).
+    const bool own[4] = {p == 0, p == 1, p == 2, p == 3};
+    const float qmf = (float)a.qmax;
+    const float qlim = qmf + 1.f;
+#pragma unroll
+    for (int jw = 0; jw < PW; jw += 4) {
+        // this lane's entries of U rows jw .. jw+3 from register jw/4 on (the aligned group
+        // holding column jw: the columns left of a pivot see U = 0, a no-op update)
+        const int i0 = (jw >> 2) & ~3;
+        float u[4][NC];
+        float dj[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int i4 = i0; i4 < NC; i4 += 4) {
+                const float4 v = *(const float4*)&Ub[jw + t][p][i4];
+                u[t][i4] = v.x; u[t][i4 + 1] = v.y; u[t][i4 + 2] = v.z; u[t][i4 + 3] = v.w;
+            }
+            dj[t] = dinv[jw + t];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int j = jw + t;
+            if ((j & 31) == 0 && j < a.bw && g != 0 && (a.gsmall ? (j % g) == 0 : (j == 0 && a.gstart0))) {
+                // a group starts here: its scale comes from the current values of its columns,
+                // panel columns [j, j + g) and, for a group wider than the panel, the columns
+                // right of the panel (which hold every earlier update)
+                const int64_t G = a.gbase + (a.gsmall ? j / g : 0);
+                uint16_t sb;
+                if (a.fixed_scales) {
+                    sb = live ? a.scales[r * a.ng + G] : (uint16_t)0;
+                } else {
+                    const int ilim = a.gsmall ? (j + g) / 4 : NC;
+                    float v = 0.f;
+#pragma unroll
+                    for (int i = j / 4; i < NC; ++i)
+                        if (i < ilim) v = fmaxf(v, fabsf(w[i]));
+                    if (!a.gsmall && live) {
+                        const int64_t col = a.b0;
+                        const int64_t gend = col + g < a.n ? col + g : a.n;
+                        for (int64_t c = a.b0 + a.bw + p; c < gend; c += 4) v = fmaxf(v, fabsf(wrow[c]));
+                    }
+                    v = quad_max(v);
+                    sb = scale_bits_from_absmax(v, a.qmax);
+                    if (p == 0 && live) a.scales[r * a.ng + G] = sb;
+                }
+                s = f16_bits_to_f32(sb);
+                rs = s > 0.f ? 1.0f / s : 0.f;
+            }
+            // column j: owner lane j & 3 (= t), register j >> 2, broadcast inside the quad
+            const float wj = quad_bcast_of(w[j >> 2], t);
+            // nearest integer to the exact quotient w / s, ties to even, without branches:
+            // k = rint(w * rcp(s)) is within one of it, and the signs of the exact residuals
+            // w - (k +- 1/2) s (one rounding each in fma) move it to the right integer.
+            // s = 0 (an all-zero or underflowed group) gives code 0.
+            const float kf = fminf(fmaxf(rintf(wj * rs), -qlim), qlim);
+            const float hi = fmaf(-(kf + 0.5f), s, wj);
+            const float lo = fmaf(-(kf - 0.5f), s, wj);
+            const int ki = (int)kf;
+            const int odd = ki & 1;
+            const int up = (hi > 0.f) | ((hi == 0.f) & odd);
+            const int dn = (lo < 0.f) | ((lo == 0.f) & odd);
+            int q = ki + up - dn;
+            q = q > a.qmax ? a.qmax : (q < -a.qmax ? -a.qmax : q);
+            q = s > 0.f ? q : 0;
+            const float e = (wj - s * (float)q) * dj[t];
+            // the owner lane of column j keeps its error and code (selects, no branches)
+            eown[j >> 2] = own[t] ? e : eown[j >> 2];
+            qb[j >> 4] = own[t] ? (qb[j >> 4] | ((uint32_t)(q & 0xff) << (8 * ((j >> 2) & 3)))) : qb[j >> 4];
+#pragma unroll
+            for (int i = i0; i < NC; ++i) w[i] = fmaf(-e, u[t][i], w[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i) asm volatile("" : "+v"(w[i]));
+#pragma unroll
+        for (int i = 0; i < NC; ++i) asm volatile("" : "+v"(eown[i]));
+#pragma unroll
+        for (int i = 0; i < (NC + 3) / 4; ++i) asm volatile("" : "+v"(qb[i]));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // error panel: Err[r][4 i + p]
+    if (live) {
+        float* erow = a.err + r * GB;
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+            if (4 * i + p < a.bw) erow[4 * i + p] = eown[i];
+    }
+    if (a.codes || a.packed) {
+        // codes through LDS: row rq, column 4 i + p, then 32 consecutive codes per lane
+#pragma unroll
+        for (int i = 0; i < NC; ++i) cst[wave][rq][4 * i + p] = (int8_t)((qb[i >> 2] >> (8 * (i & 3))) & 0xff);
+        __syncthreads();                               // uniform branch: every thread gets here
+        constexpr int PER = PW / 4;                    // codes per lane in the write-out
+        const int c0 = PER * p;
+        if (live) {
+            const int8_t* src = &cst[wave][rq][c0];
+            if (a.codes) {
+                int8_t* crow = a.codes + r * a.n + a.b0;
+                for (int c = 0; c < PER; ++c)
+                    if (c0 + c < a.bw) crow[c0 + c] = src[c];
+            }
+            if (a.packed) {
+                // byte k of the panel holds columns 2k (low nibble) and 2k+1 (high nibble)
+                uint8_t* prow = a.packed + r * (a.n / 2) + a.b0 / 2;
+                for (int c = 0; c < PER; c += 2)
+                    if (c0 + c < a.bw) prow[(c0 + c) / 2] = (uint8_t)(((src[c] + 8) & 15) | (((src[c + 1] + 8) & 15) << 4));
+            }
+        }
+    }
+}
+
+// Nearest integer to the exact quotient w / s, ties to even, clamped to +-qmax, without
+// branches: k = rint(w * rcp(s)) is within one of it, and the signs of the exact residuals
+// w - (k +- 1/2) s (one rounding each in fma) move it to the right integer.  s = 0 (an
+// all-zero or underflowed group) gives 0.
+__device__ __forceinline__ int quant_code_nb(float w, float s, float rs, int qmax) {
+    const float qlim = (float)(qmax + 1);
+    const float kf = fminf(fmaxf(rintf(w * rs), -qlim), qlim);
+    const float hi = fmaf(-(kf + 0.5f), s, w);
+    const float lo = fmaf(-(kf - 0.5f), s, w);
+    const int ki = (int)kf;
+    const int odd = ki & 1;
+    const int up = (hi > 0.f) | ((hi == 0.f) & odd);
+    const int dn = (lo < 0.f) | ((lo == 0.f) & odd);
+    int q = ki + up - dn;
+    q = q > qmax ? qmax : (q < -qmax ? -qmax : q);
+    return s > 0.f ? q : 0;
+}
+
+// a wave-uniform value, marked as such (SGPR), so branches on it are uniform ones
+__device__ __forceinline__ float uniform_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// One wave per row, for layers with few rows (latency matters more than issue slots):
+// lane l holds panel columns l and l + 64.  Column j's value comes from its lane with a
+// readlane at a static lane index (the loop is unrolled), so the quantization runs on a
+// uniform value; every lane then updates its two columns.  The next row of U is read one
+// step ahead, 1 / U_jj comes from a register by readlane, and the owner lane keeps e and
+// the code with selects: no LDS wait and no branch sits on the column-to-column chain.
+template <int PW, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
+    if (*a.info) return;
+    constexpr int NT = NWV * 64;
+    constexpr int NS = PW > 64 ? 2 : 1;              // registers per lane
+    __shared__ __attribute__((aligned(16))) float Ub[PW][PW];
+    __shared__ float esh[NWV][PW];
+    __shared__ int8_t qsh[NWV][PW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    {
+        UBlock<PW, NT> ub;
+        ub.load(a.U, a.n, a.b0, a.bw, tid);
+#pragma unroll
+        for (int q = 0; q < UBlock<PW, NT>::Q; ++q) {
+            if (!UBlock<PW, NT>::has(tid, q)) break;
+            const int e = 4 * (tid + q * NT);
+            *(float4*)&Ub[e / PW][e % PW] = ub.v[q];
+        }
+    }
+    float dreg[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const int j = lane + 64 * k;
+        dreg[k] = (j < a.bw && j < PW) ? 1.0f / a.U[(a.b0 + j) * a.n + a.b0 + j] : 0.f;
+    }
+    __syncthreads();
+
+    const int64_t r = (int64_t)blockIdx.x * NWV + wave;
+    const bool live = r < a.m;                       // uniform per wave
+    if (live) {
+        const float* wrow = a.Wf + r * a.n;
         float w[NS];
 #pragma unroll
-        for (int k = 0; k < NS; ++k) w[k] = lane + 64 * k < a.bw ? wrow[a.b0 + 64 * k + lane] : 0.f;
-        float s = 0.f, rs = 0.f;
-        if (g == 0) {
-            s = f16_bits_to_f32(a.scales[r]);
-        } else if (!a.gsmall && !a.gstart0) {
-            // a group wider than the panel that began in an earlier panel: its scale was
-            // fixed (and stored) when the loop reached the group's first column
-            s = f16_bits_to_f32(a.scales[r * a.ng + a.gbase]);
-        }
-        for (int j0 = 0; j0 < a.bw; j0 += seg) {
-            if (g != 0 && (a.gsmall || (j0 == 0 && a.gstart0))) {
-                const int64_t col = a.b0 + j0;
-                const int64_t G = a.gbase + (a.gsmall ? (j0 >> a.glog) : 0);
+        for (int k = 0; k < NS; ++k) w[k] = (lane + 64 * k < a.bw && lane + 64 * k < PW) ? wrow[a.b0 + 64 * k + lane] : 0.f;
+        const int g = a.group_size;
+        float s = 0.f;
+        if (g == 0) s = f16_bits_to_f32(a.scales[r]);
+        else if (!a.gsmall && !a.gstart0) s = f16_bits_to_f32(a.scales[r * a.ng + a.gbase]);
+        s = uniform_f(s);
+        float rs = uniform_f(s > 0.f ? 1.0f / s : 0.f);
+        const float qmf = (float)a.qmax;
+
+        const bool lane_in = lane < PW;              // PW = 32: lanes 32..63 hold no column
+        float u[NS], un[NS];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) u[k] = lane_in ? Ub[0][64 * k + lane] : 0.f;
+#pragma unroll
+        for (int j = 0; j < PW; ++j) {
+            if (j + 1 < PW) {
+#pragma unroll
+                for (int k = 0; k < NS; ++k) un[k] = lane_in ? Ub[j + 1][64 * k + lane] : 0.f;
+            }
+            if ((j & 31) == 0 && j < a.bw && g != 0 && (a.gsmall ? (j % g) == 0 : (j == 0 && a.gstart0))) {
+                // a group starts here: current values of its columns (panel columns [j, j+g)
+                // and, for a group wider than the panel, the columns right of it)
+                const int64_t G = a.gbase + (a.gsmall ? j / g : 0);
                 uint16_t sb;
                 if (a.fixed_scales) {
                     sb = a.scales[r * a.ng + G];
                 } else {
-                    // current values of the group's columns: panel columns [j0, j0+g) and, for a
-                    // group wider than the panel (it then starts at the panel's first column),
-                    // the columns right of the panel, which hold every earlier update
-                    const int64_t gend = col + g < a.n ? col + g : a.n;
+                    const int cend = a.gsmall ? j + g : PW;
                     float v = 0.f;
 #pragma unroll
                     for (int k = 0; k < NS; ++k) {
                         const int c = lane + 64 * k;
-                        if (c >= j0 && a.b0 + c < gend && c < a.bw) v = fmaxf(v, fabsf(w[k]));
+                        if (c >= j && c < cend) v = fmaxf(v, fabsf(w[k]));
                     }
-                    for (int64_t c = a.b0 + a.bw + lane; c < gend; c += 64) v = fmaxf(v, fabsf(wrow[c]));
+                    if (!a.gsmall) {
+                        const int64_t gend = a.b0 + g < a.n ? a.b0 + g : a.n;
+                        for (int64_t c = a.b0 + a.bw + lane; c < gend; c += 64) v = fmaxf(v, fabsf(wrow[c]));
+                    }
                     v = wave_max(v);
                     sb = scale_bits_from_absmax(v, a.qmax);
                     if (lane == 0) a.scales[r * a.ng + G] = sb;
                 }
-                s = f16_bits_to_f32(sb);
+                s = uniform_f(f16_bits_to_f32(sb));
+                rs = uniform_f(s > 0.f ? 1.0f / s : 0.f);
             }
-            rs = s > 0.f ? 1.0f / s : 0.f;
-            const int j1 = j0 + seg < a.bw ? j0 + seg : a.bw;
-            // one column per step; wj, s and rs are the same in every lane, so the branches
-            // are uniform.  Columns [0, 64) live in w[0], [64, 128) in w[1].
-            auto column = [&](int j, float wj) {
-                int q = 0;
-                if (s > 0.f) {
-                    const float t = wj * rs;
-                    const float lim = (float)(a.qmax + 1);
-                    const float k = fminf(fmaxf(rintf(t), -lim), lim);
-                    // |t - w/s| < 2e-6 here, so a distance below 0.49 from k already decides the
-                    // nearest integer; only quotients near a half take the exact residual test
-                    q = fabsf(t - k) <= 0.49f ? (int)fminf(fmaxf(k, (float)-a.qmax), (float)a.qmax)
-                                              : quant_code(wj, s, rs, a.qmax);
-                }
-                const float e = (wj - s * (float)q) * dinv[j];
-                if (lane == 0) {
-                    esh[wave][j] = e;
-                    qsh[wave][j] = (int8_t)q;
-                }
-                return e;
-            };
-            const int jm = j1 < 64 ? j1 : 64;
-#pragma unroll 4
-            for (int j = j0; j < jm; ++j) {
-                const float e = column(j, readlane_f(w[0], j));
+            // everything from here to e is the same in every lane (wj, s, rs, dj are
+            // wave-uniform), so the rare exact-rounding branch is a uniform one
+            const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w[j >> 6]), j & 63));
+            const float dj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dreg[j >> 6]), j & 63));
+            const float t = wj * rs;
+            const float kf = rintf(t);
+            float qf = fminf(fmaxf(kf, -qmf), qmf);
+            // |t - w/s| < 2e-6 here, so a distance below 0.49 from kf already decides the
+            // nearest integer; only quotients near a half take the exact residual test
+            if (fabsf(t - kf) > 0.49f) qf = (float)quant_code(wj, s, rs, a.qmax);
+            const float e = (wj - s * qf) * dj;
+            // e and the code are wave-uniform: every lane stores the same value to the same
+            // LDS word (no lane select), and each lane reads its own columns back at the end
+            esh[wave][j] = e;
+            qsh[wave][j] = (int8_t)qf;
+            // columns left of j (and j itself) are final: only registers holding columns
+            // >= j need the update, and U is 0 left of j anyway
 #pragma unroll
-                for (int k = 0; k < NS; ++k) w[k] = fmaf(-e, Ub[j][64 * k + lane], w[k]);
-            }
-            if (NS == 2) {
-#pragma unroll 4
-                for (int j = j0 > 64 ? j0 : 64; j < j1; ++j) {
-                    const float e = column(j, readlane_f(w[NS - 1], j - 64));
-                    w[NS - 1] = fmaf(-e, Ub[j][64 * (NS - 1) + lane], w[NS - 1]);
-                }
-            }
+            for (int k = j >> 6; k < NS; ++k) w[k] = fmaf(-e, u[k], w[k]);
+#pragma unroll
+            for (int k = 0; k < NS; ++k) u[k] = un[k];
+            // materialise the step's state (keeps the compiler from sinking the update and
+            // select chains to their last use, which would hold every step's values live)
+#pragma unroll
+            for (int k = 0; k < NS; ++k) asm volatile("" : "+v"(w[k]));
         }
-        float e_own[NS];
-        int q_own[NS];
+        float eown[NS];
+        int qown[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-            e_own[k] = esh[wave][64 * k + lane];
-            q_own[k] = qsh[wave][64 * k + lane];
+            eown[k] = lane_in ? esh[wave][64 * k + lane] : 0.f;
+            qown[k] = lane_in ? qsh[wave][64 * k + lane] : 0;
         }
+
         float* erow = a.err + r * GB;
 #pragma unroll
-        for (int k = 0; k < NS; ++k) erow[64 * k + lane] = e_own[k];
-        if (NS == 1) erow[64 + lane] = 0.f;
+        for (int k = 0; k < NS; ++k)
+            if (lane + 64 * k < a.bw && lane + 64 * k < PW) erow[64 * k + lane] = eown[k];
         if (a.codes) {
             int8_t* crow = a.codes + r * a.n + a.b0;
 #pragma unroll
             for (int k = 0; k < NS; ++k)
-                if (lane + 64 * k < a.bw) crow[64 * k + lane] = (int8_t)q_own[k];
+                if (lane + 64 * k < a.bw && lane + 64 * k < PW) crow[64 * k + lane] = (int8_t)qown[k];
         }
         if (a.packed) {
             // byte l of the panel holds columns 2l (low nibble) and 2l+1 (high nibble)
             const int src = (2 * lane) & 63;
-            const int lo0 = __shfl(q_own[0], src, 64), hi0 = __shfl(q_own[0], src + 1, 64);
+            const int lo0 = __shfl(qown[0], src, 64), hi0 = __shfl(qown[0], src + 1, 64);
             int lo = lo0, hi = hi0;
             if (NS == 2) {
-                const int lo1 = __shfl(q_own[NS - 1], src, 64), hi1 = __shfl(q_own[NS - 1], src + 1, 64);
+                const int lo1 = __shfl(qown[NS - 1], src, 64), hi1 = __shfl(qown[NS - 1], src + 1, 64);
                 lo = lane < 32 ? lo0 : lo1;
                 hi = lane < 32 ? hi0 : hi1;
             }
-            if (2 * lane < a.bw && (NS == 2 || lane < 32))
-                a.packed[r * (a.n / 2) + a.b0 / 2 + lane] = (uint8_t)((lo + 8) | ((hi + 8) << 4));
+            if (2 * lane < a.bw && 2 * lane < PW)
+                a.packed[r * (a.n / 2) + a.b0 / 2 + lane] = (uint8_t)(((lo + 8) & 15) | (((hi + 8) & 15) << 4));
         }
     }
 }
@@ -336,11 +579,12 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
     a.Wf = Wf; a.U = U; a.info = info; a.m = m; a.n = n;
     a.group_size = group_size; a.qmax = qmax; a.fixed_scales = scales_in != nullptr;
     a.scales = scales_out; a.ng = ng; a.codes = cproc; a.packed = act_order ? nullptr : packed; a.err = err;
-    const bool big = m > 4096;
-    a.rows_per_wave = m > 8192 ? 2 : 1;
-    const int nw = big ? 16 : 4;
-    const unsigned nblk = (unsigned)cdiv(m, (int64_t)nw * a.rows_per_wave);
-    const bool wide = block_size > 64;
+    // Few rows: one wave per row (the column chain's latency decides the time), workgroups
+    // sized so the rows spread over the chip.  Many rows: four lanes per row, sixteen rows
+    // per wave (issue slots decide), eight-wave workgroups.
+    const bool quad = m > 4096;
+    const int rwv = m <= 1024 ? 4 : 16;
+    const unsigned nblk = quad ? (unsigned)cdiv(m, 128) : (unsigned)cdiv(m, rwv);
 
     for (int64_t b0 = 0; b0 < n; b0 += block_size) {
         const int bw = (int)((n - b0) < block_size ? (n - b0) : block_size);
@@ -348,15 +592,22 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
         a.bw = bw;
         if (group_size != 0) {
             a.gsmall = group_size <= block_size;
-            a.glog = 0;
-            while ((1 << a.glog) < group_size) ++a.glog;
             a.gstart0 = (b0 % group_size) == 0;
             a.gbase = b0 / group_size;
         }
-        if (big && wide) hipLaunchKernelGGL((gptq_block_kernel<1024, 2>), dim3(nblk), dim3(1024), 0, s, a);
-        else if (big) hipLaunchKernelGGL((gptq_block_kernel<1024, 1>), dim3(nblk), dim3(1024), 0, s, a);
-        else if (wide) hipLaunchKernelGGL((gptq_block_kernel<256, 2>), dim3(nblk), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((gptq_block_kernel<256, 1>), dim3(nblk), dim3(256), 0, s, a);
+        if (quad) {
+            if (block_size == 128) hipLaunchKernelGGL((gptq_block_kernel<128, 8>), dim3(nblk), dim3(512), 0, s, a);
+            else if (block_size == 64) hipLaunchKernelGGL((gptq_block_kernel<64, 8>), dim3(nblk), dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((gptq_block_kernel<32, 8>), dim3(nblk), dim3(512), 0, s, a);
+        } else if (rwv == 4) {
+            if (block_size == 128) hipLaunchKernelGGL((gptq_row_kernel<128, 4>), dim3(nblk), dim3(256), 0, s, a);
+            else if (block_size == 64) hipLaunchKernelGGL((gptq_row_kernel<64, 4>), dim3(nblk), dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((gptq_row_kernel<32, 4>), dim3(nblk), dim3(256), 0, s, a);
+        } else {
+            if (block_size == 128) hipLaunchKernelGGL((gptq_row_kernel<128, 16>), dim3(nblk), dim3(1024), 0, s, a);
+            else if (block_size == 64) hipLaunchKernelGGL((gptq_row_kernel<64, 16>), dim3(nblk), dim3(1024), 0, s, a);
+            else hipLaunchKernelGGL((gptq_row_kernel<32, 16>), dim3(nblk), dim3(1024), 0, s, a);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int64_t b1 = b0 + bw;
         if (b1 < n) {

@@ -97,7 +97,7 @@ static bool gptq_params_ok(const pwq_params* p) {
     if (p->block_size != 32 && p->block_size != 64 && p->block_size != 128) return false;
     const int g = p->group_size;
     if (g < 0) return false;
-    if (g != 0 && (g % 2 != 0 || !((g % p->block_size) == 0 || (p->block_size % g) == 0))) return false;
+    if (g != 0 && (g % 32 != 0 || !((g % p->block_size) == 0 || (p->block_size % g) == 0))) return false;
     return true;
 }
 
