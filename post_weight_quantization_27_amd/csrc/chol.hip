@@ -56,11 +56,10 @@ __global__ __launch_bounds__(256) void copy_perm_kernel(const float* __restrict_
 // ------------------------------------------------------------------ diagonal block
 // One workgroup of 256 threads factors the 128 x 128 diagonal block A = V V^T (V upper) and
 // inverts V, everything in LDS:
-//   factor, 32-column panels from the right: the panel region (rows above and inside the
-//     panel) sits in 4 x 4 register tiles; per pivot the pivot column goes through LDS
-//     (zero outside the active rows, so the rank-1 update needs no predicates) with one
-//     barrier; after the panel, the rows and columns left of it get one rank-32 update on
-//     MFMA (32 x 32 output tiles spread over the four waves).
+//   factor, 32-column panels from the right: one wave holds the panel region (rows above
+//     and inside the panel) in registers and runs its 32 pivots with readlane broadcasts;
+//     after the panel, the rows and columns left of it get one rank-32 update on MFMA
+//     (32 x 32 output tiles spread over the four waves).
 //   inverse Z = V^-1: the four 32 x 32 diagonal blocks are inverted at once, one per wave
 //     (no barriers: a wave's own LDS accesses are in order), then two doubling levels
 //     Z_12 = -Z_11 (V_12 Z_22) on MFMA: 32 -> 64 and 64 -> 128.
@@ -102,8 +101,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
     if (*info) return;
     __shared__ float A[CHOL_NB][LP];
     __shared__ float Z[CHOL_NB][LP];
-    __shared__ __attribute__((aligned(16))) float colb[2][4][CHOL_NB];
-    __shared__ __attribute__((aligned(16))) float pb[2][16];
+    __shared__ int fail;                                 // failed pivot + 1 of the current panel
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // ---------------- load: thread = (row, 64-column half), all loads in flight
@@ -133,129 +131,55 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
     }
     __syncthreads();
 
-    // ---------------- factor: 32-column panels from the right, 4 pivots per barrier
-    const int rb = tid >> 3, cb = tid & 7;       // rows 4rb..4rb+3, panel columns 4cb..4cb+3
+    // ---------------- factor: 32-column panels from the right.  Wave 0 factors a panel in
+    // registers (lane l holds rows l and l + 64 of the panel's 32 columns): the pivot and the
+    // pivot column's entries of the panel rows reach every lane by readlane, so a pivot costs
+    // no LDS round trip and no barrier.  Entries below the diagonal pick up meaningless
+    // values on the way (they only ever feed other entries below the diagonal) and are
+    // written back as 0.  Then all four waves apply the panel's rank-32 update to the rows
+    // and columns left of it on MFMA.
+    // unrolled over the four panels, so every readlane lane index is a constant
+#pragma unroll
     for (int p = 3; p >= 0; --p) {
         const int c0 = 32 * p;
-        const bool act = 4 * rb < c0 + 32;
-        float a[4][4];
+        if (wave == 0) {
+            const int h = c0 >> 6;                       // register holding the panel rows
+            const int lb = c0 & 63;                      // lane of the panel's first row
+            float a0[32], a1[32];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) a[ii][jj] = act ? A[4 * rb + ii][c0 + 4 * cb + jj] : 0.f;
-        for (int g = 7; g >= 0; --g) {
-            const int clo = c0 + 4 * g;                  // pivots clo .. clo+3
-            const int buf = g & 1;
-            if (act && cb == g) {                        // owners hold all four pivot columns
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    float t[4];
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) t[ii] = (4 * rb + ii < clo) ? a[ii][jj] : 0.f;
-                    *(float4*)&colb[buf][jj][4 * rb] = make_float4(t[0], t[1], t[2], t[3]);
-                }
-                if (rb == (clo >> 2)) {
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        *(float4*)&pb[buf][4 * ii] = make_float4(a[ii][0], a[ii][1], a[ii][2], a[ii][3]);
-                }
+            for (int kk = 0; kk < 32; ++kk) {
+                a0[kk] = A[lane][c0 + kk];
+                a1[kk] = A[lane + 64][c0 + kk];
             }
-            __syncthreads();
-            // the 4 x 4 pivot block D = Vd Vd^T (Vd upper), redundantly in every thread, and Zd = Vd^-1
-            float D[4][4], Vd[4][4], Zd[4][4];
+            int bad = -1;                                // first failed pivot (uniform)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const float4 t = *(const float4*)&pb[buf][4 * ii];
-                D[ii][0] = t.x; D[ii][1] = t.y; D[ii][2] = t.z; D[ii][3] = t.w;
-            }
-            bool ok = true;
+            for (int kk = 31; kk >= 0; --kk) {
+                const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                    __builtin_bit_cast(int, h ? a1[kk] : a0[kk]), lb + kk));
+                if (!(d > 0.f) && bad < 0) bad = kk;
+                const float r = __builtin_amdgcn_rsqf(d);
+                a0[kk] *= r;                             // column kk of V (the pivot row gets d r)
+                a1[kk] *= r;
+                const float vc = h ? a1[kk] : a0[kk];
 #pragma unroll
-            for (int k = 3; k >= 0; --k) {
-                const float d = D[k][k];
-                ok = ok && (d > 0.f);
-                const float r = __builtin_amdgcn_sqrtf(d);
-                const float inv = __builtin_amdgcn_rcpf(r);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Vd[i][k] = i < k ? D[i][k] * inv : (i == k ? r : 0.f);
-#pragma unroll
-                for (int i = 0; i < k; ++i)
-#pragma unroll
-                    for (int j = i; j < k; ++j) D[i][j] = fmaf(-Vd[i][k], Vd[j][k], D[i][j]);
-            }
-            if (!ok) {                                   // same decision in every thread
-                if (tid == 0) {
-                    int bad = 0;                         // the last pivot (from the bottom) that failed
-                    float DD[4][4];
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) DD[ii][jj] = pb[buf][4 * ii + jj];
-                    for (int k = 3; k >= 0; --k) {
-                        if (!(DD[k][k] > 0.f)) { bad = k; break; }
-                        const float r = sqrtf(DD[k][k]);
-                        for (int i = 0; i < k; ++i)
-                            for (int j = i; j < k; ++j) DD[i][j] -= (DD[i][k] / r) * (DD[j][k] / r);
-                    }
-                    *info = (int32_t)(k0 + clo + bad + 1);
-                }
-                return;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Zd[i][i] = __builtin_amdgcn_rcpf(Vd[i][i]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (j != i) Zd[i][j] = 0.f;
-            }
-#pragma unroll
-            for (int i = 2; i >= 0; --i)
-#pragma unroll
-                for (int j = i + 1; j < 4; ++j) {
-                    float sacc = 0.f;
-#pragma unroll
-                    for (int l = i + 1; l <= j; ++l) sacc = fmaf(Vd[i][l], Zd[l][j], sacc);
-                    Zd[i][j] = -sacc * Zd[i][i];
-                }
-            if (act) {
-                // V rows of this thread and of its panel columns: V[., clo+k] = raw[., l] Zd[k][l]
-                float vr[4][4], vc[4][4];
-#pragma unroll
-                for (int l = 0; l < 4; ++l) {
-                    const float4 x = *(const float4*)&colb[buf][l][4 * rb];
-                    const float4 y = *(const float4*)&colb[buf][l][c0 + 4 * cb];
-                    const float xr[4] = {x.x, x.y, x.z, x.w}, yc[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-                        for (int k = 0; k <= l; ++k) {
-                            if (l == k) { vr[ii][k] = xr[ii] * Zd[k][l]; vc[ii][k] = yc[ii] * Zd[k][l]; }
-                            else { vr[ii][k] = fmaf(xr[ii], Zd[k][l], vr[ii][k]); vc[ii][k] = fmaf(yc[ii], Zd[k][l], vc[ii][k]); }
-                        }
-                }
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) a[ii][jj] = fmaf(-vr[ii][k], vc[jj][k], a[ii][jj]);
-                if (cb == g) {
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        const int row = 4 * rb + ii;
-#pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            a[ii][k] = row < clo ? vr[ii][k] : (row - clo <= k && row < clo + 4 ? Vd[ii][k] : 0.f);
-                    }
+                for (int jj = 0; jj < kk; ++jj) {
+                    const float vjk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vc), lb + jj));
+                    a0[jj] = fmaf(-a0[kk], vjk, a0[jj]);
+                    a1[jj] = fmaf(-a1[kk], vjk, a1[jj]);
                 }
             }
-        }
-        if (act) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) A[4 * rb + ii][c0 + 4 * cb + jj] = a[ii][jj];
+            for (int kk = 0; kk < 32; ++kk) {
+                A[lane][c0 + kk] = lane <= c0 + kk ? a0[kk] : 0.f;
+                A[lane + 64][c0 + kk] = lane + 64 <= c0 + kk ? a1[kk] : 0.f;
+            }
+            if (lane == 0) fail = bad >= 0 ? (int)(k0 + c0 + bad + 1) : 0;
         }
         __syncthreads();
+        if (fail) {                                      // same decision in every thread
+            if (tid == 0) *info = fail;
+            return;
+        }
         if (p > 0) {                                     // A[0:c0, 0:c0] -= P P^T, P = V[0:c0, panel]
             const int ntile = p * (p + 1) / 2;
             for (int t = wave; t < ntile; t += 4) {

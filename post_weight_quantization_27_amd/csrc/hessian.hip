@@ -7,7 +7,7 @@
 // MFMA engine, bfloat16 X on the bfloat16 one (products exact, float32 accumulate).  Small d_in gives few tiles, so the token range is cut into chunks whose partial
 // tiles land in a workspace and are summed in a fixed order (bit-reproducible, no
 // atomics).  A last pass copies the upper triangle onto the lower one.
-#include "gemm_bf16.h"
+#include "gemm_bf16_dl.h"
 #include "pwq_internal.h"
 
 namespace pwq {
@@ -127,6 +127,64 @@ hipError_t hess_gemm_bf16(const void* X, int64_t n_tok, int64_t n, int64_t ldx, 
     return hipGetLastError();
 }
 
+// XT[c][t] = X[t][c] for t < n_tok, 0 for n_tok <= t < npad: 64 tokens x 64 columns per
+// workgroup through LDS, 16-byte reads and writes (bfloat16 bits are moved, not converted)
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ X, int64_t n_tok, int64_t n,
+                                                             int64_t ldx, int vec, uint16_t* __restrict__ XT,
+                                                             int64_t npad) {
+    __shared__ uint16_t tile[64][64 + 8];
+    const int64_t t0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = tid + 256 * h;
+        const int r = idx >> 3, ch = (idx & 7) * 8;        // token row r, columns ch .. ch+7
+        const int64_t t = t0 + r, c = c0 + ch;
+        uint16_t v[8];
+        if (vec && t < n_tok && c + 8 <= n) {
+            const uint4 q = *(const uint4*)(X + t * ldx + c);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { v[2 * k] = (uint16_t)(w[k] & 0xffff); v[2 * k + 1] = (uint16_t)(w[k] >> 16); }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = (t < n_tok && c + k < n) ? X[t * ldx + c + k] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tile[r][ch + k] = v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = tid + 256 * h;
+        const int cr = idx >> 3, tch = (idx & 7) * 8;      // output row = column cr, tokens tch .. +7
+        const int64_t c = c0 + cr;
+        if (c >= n) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = (uint32_t)tile[tch + 2 * k][cr] | ((uint32_t)tile[tch + 2 * k + 1][cr] << 16);
+        *(uint4*)(XT + c * npad + t0 + tch) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// bfloat16 X on the direct-load engine: both operands are rows of the transposed copy
+// (tokens contiguous, zero past n_tok), 256 x 256 upper tiles
+hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, uint16_t* XT, float* part,
+                        const HessPlan& pl, hipStream_t s) {
+    const int vec = (ldx % 8 == 0) && aligned(X, 16);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(pl.npad / 64), (unsigned)cdiv(n, 64)), dim3(256), 0, s,
+                       (const uint16_t*)X, n_tok, n, ldx, vec, XT, pl.npad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    DlRows op{XT, nullptr, pl.npad, n, pl.npad, 0};
+    UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr};
+    const int ntile = pl.tiles * (pl.tiles + 1) / 2;
+    EpiHess epi{H, part, n, ntile, DL_TILE, pl.splits == 1};
+    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(ntile * pl.splits), dim3(GEMM_THREADS),
+                       0, s, op, op, map, epi);
+    return hipGetLastError();
+}
+
 template <int BM, int DT>
 hipError_t hess_gemm(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, float* part, const HessPlan& pl,
                      hipStream_t s) {
@@ -145,20 +203,26 @@ hipError_t hess_gemm(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float
 HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype) {
     HessPlan p{};
     const bool bf = x_dtype == 2;
-    p.bm = (!bf && d_in <= 1024) ? 64 : 128;
+    // bfloat16 X with enough 256-wide tiles (and tokens) goes through the transposed copy
+    p.dl = bf && d_in >= 1024 && n_tok >= 256;
+    p.bm = p.dl ? DL_TILE : ((!bf && d_in <= 1024) ? 64 : 128);
     p.tiles = (int)cdiv(d_in, p.bm);
     const int ntile = p.tiles * (p.tiles + 1) / 2;
-    const int kq = bf ? BK16 : GEMM_BK;                  // chunk boundaries on whole k-tiles
-    const int64_t ksteps = cdiv(n_tok, kq);
-    const int target = 1024;                         // >= 4 workgroups per CU of 256
+    const int kq = (bf || p.dl) ? BK16 : GEMM_BK;       // chunk boundaries on whole k-tiles
+    p.npad = p.dl ? cdiv(n_tok, 64) * 64 : n_tok;
+    const int64_t ksteps = cdiv(p.npad, kq);
+    // one 256-wide workgroup per CU (LDS), else >= 4 workgroups per CU of 256
+    const int target = p.dl ? 512 : 1024;
     int64_t splits = ntile >= target ? 1 : cdiv(target, ntile);
-    const int64_t max_splits = ksteps / 8 > 1 ? ksteps / 8 : 1;   // >= 256 tokens per chunk
+    const int64_t max_splits = ksteps / 8 > 1 ? ksteps / 8 : 1;   // >= 8 k-tiles per chunk
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
     p.kchunk = cdiv(ksteps, splits) * kq;
-    p.splits = (int)cdiv(n_tok, p.kchunk);
+    p.splits = (int)cdiv(p.npad, p.kchunk);
     if (p.splits < 1) p.splits = 1;
-    p.ws_bytes = p.splits > 1 ? (size_t)p.splits * ntile * p.bm * p.bm * sizeof(float) : 0;
+    p.xt_bytes = p.dl ? align_up((size_t)d_in * p.npad * sizeof(uint16_t), 256) : 0;
+    const size_t parts = p.splits > 1 ? (size_t)p.splits * ntile * p.bm * p.bm * sizeof(float) : 0;
+    p.ws_bytes = p.xt_bytes + parts;
     return p;
 }
 
@@ -166,10 +230,12 @@ hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_i
                           hipStream_t s) {
     if (n_tok == 0 || d_in == 0) return hipSuccess;
     const HessPlan pl = hessian_plan(n_tok, d_in, x_dtype);
-    float* part = (float*)ws;
+    float* part = (float*)((char*)ws + pl.xt_bytes);
     hipError_t e;
     if (x_dtype == 0) {
         e = pl.bm == 64 ? hess_gemm<64, 0>(X, n_tok, d_in, ldx, H, part, pl, s) : hess_gemm<128, 0>(X, n_tok, d_in, ldx, H, part, pl, s);
+    } else if (pl.dl) {
+        e = hess_gemm_dl(X, n_tok, d_in, ldx, H, (uint16_t*)ws, part, pl, s);
     } else {
         e = hess_gemm_bf16(X, n_tok, d_in, ldx, H, part, pl, s);
     }

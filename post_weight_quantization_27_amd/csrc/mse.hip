@@ -9,11 +9,12 @@
 // hi = bf16(dW), lo = bf16(dW - hi), rows padded to a multiple of 64 with zeros.  The
 // contraction then runs on the bfloat16 MFMA engine with k doubled:
 //   X dW^T ~= [X, X] [dW_hi, dW_lo]^T,
-// X rounded once to bfloat16 (exact for bfloat16 X); the epilogue squares and sums the
+// X rounded once to bfloat16 (exact for bfloat16 X; large bfloat16 problems run on the
+// 256 x 256 direct-load engine); the epilogue squares and sums the
 // output tile in registers, so the product is never written.  The pair keeps 16
 // significant bits of dW; rounding float32 X to bfloat16 adds about 2^-16 / 3 relative
 // to the mean square.  Per-workgroup partial sums (float64) are added in a fixed order.
-#include "gemm_bf16.h"
+#include "gemm_bf16_dl.h"
 #include "pwq_internal.h"
 
 namespace pwq {
@@ -226,7 +227,27 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     int64_t nb = 0;
-    if (x_dtype == 2) {
+    const bool dl = x_dtype == 2 && (ldx % 8 == 0) && aligned(X, 16) && (d_in % 8 == 0) &&
+                    cdiv(n_tok, DL_TILE) * cdiv(d_out, DL_TILE) >= 256;
+    if (dl) {
+        // large bfloat16 problems: direct-load engine, 256 x 256 tiles (dW's zero tail covers
+        // the clamped X chunks past d_in)
+        DlRows a{(const uint16_t*)X, (const uint16_t*)X, ldx, n_tok, d_in, kseg};
+        DlRows b{dhi, dlo, kseg, d_out, kseg, kseg};
+        RectMap mp{};
+        mp.M = n_tok; mp.N = d_out; mp.K = 2 * kseg;
+        mp.tiles_m = (int)cdiv(n_tok, DL_TILE);
+        mp.tiles_n = (int)cdiv(d_out, DL_TILE);
+        mp.splits = 1;
+        mp.kchunk = 2 * kseg;
+        mp.tri_k = 0;
+        mp.guard = nullptr;
+        EpiSq ep{part, n_tok, d_out, 0.f};
+        nb = (int64_t)mp.tiles_m * mp.tiles_n;
+        hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, RectMap, EpiSq>), dim3((unsigned)nb), dim3(GEMM_THREADS), 0, s,
+                           a, b, mp, ep);
+        e = hipGetLastError();
+    } else if (x_dtype == 2) {
         Bf16Rows a{(const uint16_t*)X, (const uint16_t*)X, ldx, n_tok, d_in, kseg, (int)((ldx % 8 == 0) && aligned(X, 16))};
         e = mse_gemm(a, n_tok, d_out, kseg, dhi, dlo, part, s, &nb);
     } else {

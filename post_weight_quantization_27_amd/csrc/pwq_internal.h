@@ -13,11 +13,14 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Hessian build: H += 2 X^T X (float32 MFMA, upper tiles, deterministic split-K, mirror).
 struct HessPlan {
-    int bm;            // tile edge (64 or 128)
+    int bm;            // tile edge (64, 128, or 256 on the direct-load engine)
     int tiles;         // tiles per edge
     int splits;        // token chunks
-    int64_t kchunk;    // tokens per chunk (multiple of 32)
-    size_t ws_bytes;   // partial-tile workspace (0 when splits == 1)
+    int64_t kchunk;    // tokens per chunk (multiple of the engine's k tile)
+    int dl;            // bfloat16 X through a transposed copy on the direct-load engine
+    int64_t npad;      // tokens of the transposed copy (multiple of 64, zero tail)
+    size_t xt_bytes;   // transposed copy (0 unless dl)
+    size_t ws_bytes;   // transposed copy + partial tiles (0 when neither is needed)
 };
 HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype);
 hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* H,

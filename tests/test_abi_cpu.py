@@ -52,7 +52,8 @@ def test_workspace_sizes(L):
     ws = L.pwq_hessian_workspace_size(n_tok, d_in, 0)
     assert ws > 0 and ws % (ntile * 64 * 64 * 4) == 0
     # enough upper tiles: no split, no workspace
-    assert L.pwq_hessian_workspace_size(262144, 28672, 2) == 0
+    # bfloat16 X of a wide layer: a transposed copy (tokens contiguous), no partial tiles
+    assert L.pwq_hessian_workspace_size(262144, 28672, 2) == 28672 * 262144 * 2
     assert L.pwq_chol_workspace_size(3072) == 3072 * 128 * 4
     p = pwq.PwqParams(4, 128, 128, 0)
     m, n = 768, 3072

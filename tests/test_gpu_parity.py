@@ -178,7 +178,7 @@ def test_hessian_bf16_strided_and_tiled(pwq):
     assert rel_frob(H3, want) <= 1e-5
 
 
-@pytest.mark.parametrize("n_tok,d_in", [(1000, 200), (77, 13), (4100, 1030)])
+@pytest.mark.parametrize("n_tok,d_in", [(1000, 200), (77, 13), (4100, 1030), (700, 1027), (256, 1024)])
 def test_hessian_bf16_ragged(pwq, n_tok, d_in):
     rng = np.random.default_rng(n_tok * 3 + d_in)
     bits = synth.f64_to_bf16_bits(rng.standard_normal((n_tok, d_in)) * np.where(rng.random(d_in) < 0.02, 20.0, 1.0))
@@ -405,6 +405,21 @@ def test_recon_mse_given_codes(pwq, xdt, wdt, g, src):
     want = O.recon_mse(X64, W, r["What"])
     kw = {"packed": dev(O.pack_int4(r["codes"]))} if src == "packed" else {"codes": dev(r["codes"])}
     got = float(host(pwq.recon_mse(Xd, dev(W), dev(r["scales"]), 4, g, **kw))[0])
+    assert abs(got - want) <= 1e-4 * want
+
+
+@pytest.mark.parametrize("n_tok,n,m", [(8192, 512, 2048), (8000, 520, 2100)])
+def test_recon_mse_large_bf16(pwq, n_tok, n, m):
+    """Enough 256 x 256 output tiles for the large-tile engine; the second case has ragged
+    tokens, outputs and inputs (X chunks past d_in are clamped, dW's zero tail covers them)."""
+    rng = np.random.default_rng(n_tok + n + m)
+    W = rand_w(rng, m, n, np.float16)
+    r = O.rtn(W, 4, 128 if n % 128 == 0 else 0)
+    g = 128 if n % 128 == 0 else 0
+    bits = synth.f64_to_bf16_bits(rng.standard_normal((n_tok, n)) * np.where(rng.random(n) < 0.01, 20.0, 1.0))
+    want = O.recon_mse(synth.as_f64(bits, synth.BF16), W, r["What"])
+    got = float(host(pwq.recon_mse(dev_bf16(bits), dev(W), dev(r["scales"]), 4, g,
+                                   packed=dev(O.pack_int4(r["codes"]))))[0])
     assert abs(got - want) <= 1e-4 * want
 
 
