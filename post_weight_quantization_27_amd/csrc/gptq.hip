@@ -19,7 +19,9 @@
 //              scales are a max over the group's registers plus two DPP steps.  Writes the
 //              error panel Err (m x B), codes or INT4 nibbles (staged per wave in LDS) and
 //              scales.
-//   trailing : Wf[:, end:] -= Err U[block, end:]  (float32 MFMA engine)
+//   trailing : Wf[:, end:super] -= Err U[block, end:super] after each block, and
+//              Wf[:, super:] -= Err_S U[super block, super:] after each super-block of
+//              LAZY_COLS columns (float32 MFMA engine)
 //   finish   : act-order only: codes back to the original column order, nibble packing and
 //              g_idx.
 #include "gemm_f32.h"
@@ -29,7 +31,17 @@ namespace pwq {
 
 namespace {
 
-constexpr int GB = 128;   // panel width held per wave (two columns per lane)
+constexpr int GB = 128;   // widest panel (block size)
+// Error panels are kept for a super-block of columns: a block updates only the columns left
+// in its super-block, and the columns past it get one product as deep as the super-block when
+// it is done (the lazy batching of the column loop, one level up).  512 columns, except that a
+// group wider than a block must start a super-block (its scale reads the columns past the
+// panel, which are current only at a super-block's start): then the super-block is the group
+// (up to 2048 columns; wider groups update every column after each block).
+inline int lazy_cols(int group_size, int block_size) {
+    if (group_size == 0 || group_size <= block_size) return 512;
+    return group_size <= 2048 ? group_size : block_size;
+}
 
 template <int DT, bool PERM>
 __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restrict__ W, int64_t ldw, int64_t m, int64_t n,
@@ -106,7 +118,8 @@ struct BlockArgs {
     int64_t ng;
     int8_t* codes;           // processing order, ld n (nullable)
     uint8_t* packed;         // ld n/2 (nullable; only without act-order)
-    float* err;              // m x GB
+    float* err;              // this block's columns of the super-block's Err (m x err_ld)
+    int err_ld;
 };
 
 // The panel's diagonal block of U (zero outside bw x bw), read as float4 rows with every
@@ -284,7 +297,7 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
 
     // error panel: Err[r][4 i + p]
     if (live) {
-        float* erow = a.err + r * GB;
+        float* erow = a.err + r * a.err_ld;
 #pragma unroll
         for (int i = 0; i < NC; ++i)
             if (4 * i + p < a.bw) erow[4 * i + p] = eown[i];
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
             qown[k] = lane_in ? qsh[wave][64 * k + lane] : 0;
         }
 
-        float* erow = a.err + r * GB;
+        float* erow = a.err + r * a.err_ld;
 #pragma unroll
         for (int k = 0; k < NS; ++k)
             if (lane + 64 * k < a.bw && lane + 64 * k < PW) erow[64 * k + lane] = eown[k];
@@ -518,34 +531,41 @@ __global__ __launch_bounds__(256) void unpermute_codes_kernel(const int8_t* __re
         }
 }
 
+// Wf[:, c0:c1] -= Err[:, 0:kw] U[kb0:kb0+kw, c0:c1]  (Err with row stride ld)
 template <int BM, int BN>
-hipError_t trailing(float* Wf, const float* err, const float* U, const int32_t* info, int64_t m, int64_t n, int64_t b0,
-                    int64_t b1, int bw, hipStream_t s) {
-    const int64_t N = n - b1;
-    OpMMajor<0> a{err, GB, m, bw, 1};
-    OpKMajor<0> b{U + b0 * n + b1, n, N, bw, (int)((n % 4 == 0) && aligned(U, 16) && (b1 % 4 == 0))};
+hipError_t trailing(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
+                    int64_t kb0, int kw, int64_t c0, int64_t c1, hipStream_t s) {
+    const int64_t N = c1 - c0;
+    OpMMajor<0> a{err, ld, m, kw, (int)(aligned(err, 16) && ld % 4 == 0)};
+    OpKMajor<0> b{U + kb0 * n + c0, n, N, kw, (int)((n % 4 == 0) && aligned(U, 16) && (c0 % 4 == 0))};
     RectMap mp{};
-    mp.M = m; mp.N = N; mp.K = bw;
+    mp.M = m; mp.N = N; mp.K = kw;
     mp.tiles_m = (int)cdiv(m, BM);
     mp.tiles_n = (int)cdiv(N, BN);
     mp.splits = 1;
-    mp.kchunk = cdiv(bw, GEMM_BK) * GEMM_BK;
+    mp.kchunk = cdiv(kw, GEMM_BK) * GEMM_BK;
     mp.tri_k = 0;
     mp.guard = info;
-    EpiSub ep{Wf + b1, n, m, N};
+    EpiSub ep{Wf + c0, n, m, N};
     hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, OpMMajor<0>, OpKMajor<0>, RectMap, EpiSub>),
                        dim3(mp.tiles_m * mp.tiles_n), dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
     return hipGetLastError();
 }
 
+hipError_t update(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
+                  int64_t kb0, int kw, int64_t c0, int64_t c1, hipStream_t s) {
+    const int64_t big_tiles = cdiv(m, 128) * cdiv(c1 - c0, 128);
+    return big_tiles >= 512 ? trailing<128, 128>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
+                            : trailing<64, 64>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s);
+}
+
 }  // namespace
 
-GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int act_order) {
-    (void)block_size;
+GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int group_size, int act_order) {
     GptqWs w{};
     size_t off = 0;
     w.wf = off;    off = align_up(off + (size_t)d_out * d_in * sizeof(float), 256);
-    w.err = off;   off = align_up(off + (size_t)d_out * GB * sizeof(float), 256);
+    w.err = off;   off = align_up(off + (size_t)d_out * lazy_cols(group_size, block_size) * sizeof(float), 256);
     w.codes = off; if (act_order) off = align_up(off + (size_t)d_out * d_in, 256);
     w.inv = off;   if (act_order) off = align_up(off + (size_t)d_in * sizeof(int32_t), 256);
     w.total = off;
@@ -558,7 +578,8 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
                        void* ws, hipStream_t s) {
     if (m == 0 || n == 0) return hipSuccess;
     hipError_t e;
-    const GptqWs L = gptq_ws_layout(m, n, block_size, act_order);
+    const GptqWs L = gptq_ws_layout(m, n, block_size, group_size, act_order);
+    const int lz = lazy_cols(group_size, block_size);
     char* base = (char*)ws;
     float* Wf = (float*)(base + L.wf);
     float* err = (float*)(base + L.err);
@@ -588,8 +609,12 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
 
     for (int64_t b0 = 0; b0 < n; b0 += block_size) {
         const int bw = (int)((n - b0) < block_size ? (n - b0) : block_size);
+        const int64_t s0 = b0 / lz * lz;                               // super-block of this block
+        const int64_t s1 = s0 + lz < n ? s0 + lz : n;
         a.b0 = b0;
         a.bw = bw;
+        a.err = err + (b0 - s0);
+        a.err_ld = lz;
         if (group_size != 0) {
             a.gsmall = group_size <= block_size;
             a.gstart0 = (b0 % group_size) == 0;
@@ -610,11 +635,10 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int64_t b1 = b0 + bw;
-        if (b1 < n) {
-            const int64_t big_tiles = cdiv(m, 128) * cdiv(n - b1, 128);
-            e = big_tiles >= 512 ? trailing<128, 128>(Wf, err, U, info, m, n, b0, b1, bw, s)
-                                 : trailing<64, 64>(Wf, err, U, info, m, n, b0, b1, bw, s);
-            if (e != hipSuccess) return e;
+        if (b1 < s1) {                     // the rest of the super-block, from this block's errors
+            if ((e = update(Wf, err + (b0 - s0), lz, U, info, m, n, b0, bw, b1, s1, s)) != hipSuccess) return e;
+        } else if (s1 < n) {               // super-block done: every column past it, depth s1 - s0
+            if ((e = update(Wf, err, lz, U, info, m, n, s0, (int)(s1 - s0), s1, n, s)) != hipSuccess) return e;
         }
     }
     if (act_order) {

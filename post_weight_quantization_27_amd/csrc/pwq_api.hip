@@ -103,7 +103,7 @@ static bool gptq_params_ok(const pwq_params* p) {
 
 size_t pwq_gptq_workspace_size(int64_t d_out, int64_t d_in, const pwq_params* params) {
     if (d_out <= 0 || d_in <= 0 || bad_dim(d_out) || bad_dim(d_in) || !gptq_params_ok(params)) return 0;
-    return gptq_ws_layout(d_out, d_in, params->block_size, params->act_order != 0).total;
+    return gptq_ws_layout(d_out, d_in, params->block_size, params->group_size, params->act_order != 0).total;
 }
 
 pwq_status pwq_gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,

@@ -39,7 +39,7 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
 struct GptqWs {
     size_t wf, err, codes, inv, total;
 };
-GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int act_order);
+GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int group_size, int act_order);
 hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, const float* U,
                        const int32_t* info, int bits, int group_size, int block_size, int act_order,
                        const int32_t* perm, const uint16_t* scales_in, int8_t* codes, uint8_t* packed,

@@ -60,9 +60,9 @@ def test_workspace_sizes(L):
     got = L.pwq_gptq_workspace_size(m, n, ctypes.byref(p))
     def up(x):
         return (x + 255) // 256 * 256
-    assert got == up(up(m * n * 4) + m * 128 * 4)
+    assert got == up(up(m * n * 4) + m * 512 * 4)
     pa = pwq.PwqParams(4, 128, 128, 1)
-    assert L.pwq_gptq_workspace_size(m, n, ctypes.byref(pa)) == up(up(up(up(m * n * 4) + m * 128 * 4) + m * n) + n * 4)
+    assert L.pwq_gptq_workspace_size(m, n, ctypes.byref(pa)) == up(up(up(up(m * n * 4) + m * 512 * 4) + m * n) + n * 4)
     bad = pwq.PwqParams(4, 96, 128, 0)          # group neither divides nor is a multiple of B
     assert L.pwq_gptq_workspace_size(m, n, ctypes.byref(bad)) == 0
     assert L.pwq_recon_mse_workspace_size(8192, 768, 3072) > 0

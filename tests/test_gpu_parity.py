@@ -305,6 +305,10 @@ GPTQ_CASES = [
     ("g256_B64", 48, 768, 1600, 256, 64, False, np.float16),
     ("act_g128", 160, 640, 1500, 128, 128, True, np.float16),
     ("act_row", 60, 256, 600, 0, 64, True, np.float32),
+    # columns past 512 receive their updates in batches; a group wider than a block and not
+    # dividing 512 starts its own batch
+    ("row_n1300", 64, 1300, 1500, 0, 128, False, np.float32),
+    ("g384_B128", 40, 1000, 1200, 384, 128, False, np.float32),
 ]
 
 
