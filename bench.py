@@ -5,8 +5,10 @@ resident in HBM: Hessian from X, damping, [act-order], H^-1 factor, GPTQ (INT4 p
 fp16 scales), RTN, dequant of the GPTQ result, and the reconstruction MSE of both.
 The value is weights quantized per second (sum of d_out * d_in over the layers / step).
 
-Prints ONE JSON line.  Per-call durations are taken with HIP events on the stream the
-kernels run on (torch's current stream, which the binding passes to libpwq).
+Prints ONE JSON line.  The value comes from K timed steps with no events between the
+launches; per-call durations come from K more steps with HIP events recorded around every
+call on the stream it runs on (each layer has its own stream, which the binding passes to
+libpwq).  The roofline object describes the longest (layer, call) launch.
 """
 from __future__ import annotations
 
@@ -105,24 +107,54 @@ def run_step(L, pwq, timers=None):
 
 
 def work_of(name, spec):
-    """(bound, algorithmic amount per call, unit) of one library call on one layer."""
+    """(peak key, algorithmic amount of one call on one layer, unit).  Contractions count
+    the flops the method needs (not what the kernels execute); codec passes the bytes they
+    must move."""
     m, n, N = spec.d_out, spec.d_in, spec.n_tok
     xb = 4 if spec.x_dtype == "f32" else 2
     wb = 4 if spec.w_dtype == "f32" else 2
     ng = 1 if spec.group_size == 0 else -(-n // spec.group_size)
-    if name == "hessian_accumulate":
+    if name == "hessian_accumulate":            # symmetric X^T X: upper triangle + diagonal
         return ("mfma_bf16" if xb == 2 else "mfma_f32"), N * n * (n + 1), "flop"
-    if name == "chol_inverse_upper":
+    if name == "chol_inverse_upper":            # Cholesky n^3/3 + triangular inverse n^3/3
         return "mfma_f32", 2 * n ** 3 / 3, "flop"
-    if name == "gptq_quantize_layer":
+    if name == "gptq_quantize_layer":           # trailing products + in-block rank-1 updates
         return "mfma_f32", m * n * (n - spec.block_size) + m * n * (spec.block_size - 1), "flop"
-    if name == "recon_mse":
-        return ("mfma_bf16" if xb == 2 else "mfma_f32"), 2 * (2 * N * n * m), "flop"
+    if name == "recon_mse":                     # two calls (GPTQ and RTN) of 2 N n m, bf16 MFMA
+        return "mfma_bf16", 2 * (2 * N * n * m), "flop"
     if name == "rtn_quantize":
         return "hbm", m * n * wb + m * n // 2 + 2 * m * ng, "byte"
     if name == "dequant":
         return "hbm", m * n // 2 + 2 * m * ng + 2 * m * n, "byte"
     return "hbm", 0, "byte"
+
+
+# kernels one call launches, for the roofline's description (chol and gptq per 128 columns)
+def launches_of(name, spec):
+    nb = -(-spec.d_in // 128)
+    if name == "chol_inverse_upper":
+        return 2 + 3 * nb
+    if name == "gptq_quantize_layer":
+        return 1 + 2 * nb
+    if name == "recon_mse":
+        return 6
+    return None
+
+
+def traffic_of(workload, layer, call):
+    """HBM bytes per call from the committed counter summary, if it was taken on the kernel
+    sources as they are now (else None)."""
+    try:
+        from post_weight_quantization_27_amd import profile_summary
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            data = json.load(f)
+        e = data.get(f"{workload}/{layer}")
+        if not e or e.get("source_hash") != profile_summary.source_hash():
+            return None
+        c = e["per_call"].get(call)
+        return None if c is None else c["hbm_bytes"]
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def cpu_baseline(specs, synth, budget_layers):
@@ -194,11 +226,12 @@ def main():
     # the layer with the longest serial chain (largest d_in: most factor blocks) goes first
     order = sorted(range(len(layers)), key=lambda i: -layers[i].spec.d_in)
 
-    def step():
-        for L, st in ((layers[i], streams[i]) for i in order):
+    def step(timers=None):
+        for i in order:
+            L, st = layers[i], streams[i]
             st.wait_stream(main)
             with torch.cuda.stream(st):
-                run_step(L, pwq)
+                run_step(L, pwq, None if timers is None else timers[i])
         for st in streams:
             main.wait_stream(st)
 
@@ -223,12 +256,12 @@ def main():
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / a.steps
 
-    # per-call durations: the same steps again, layers one after another on one stream, with
-    # events around every call
+    # per-call durations: the same K steps again, on the same streams, with HIP events around
+    # every call on the stream it runs on (kept out of the first timed region, which gives the
+    # value, so the event records do not sit between its launches)
     timers = [dict() for _ in layers]
     for _ in range(a.steps):
-        for L, T in zip(layers, timers):
-            run_step(L, pwq, T)
+        step(timers)
     torch.cuda.synchronize()
     per = {}
     for L, T in zip(layers, timers):
@@ -238,16 +271,24 @@ def main():
     breakdown = {}
     for (lname, name), d in per.items():
         breakdown[name] = breakdown.get(name, 0.0) + d
-    dom = max(per.items(), key=lambda kv: kv[1])
-    (dl, dn), dms = dom
+    # roofline of the dominant launch: the (layer, call) with the longest duration
+    (dl, dn), dms = max(per.items(), key=lambda kv: kv[1])
     dspec = next(L.spec for L in layers if L.spec.name == dl)
     bound, amount, unit = work_of(dn, dspec)
     achieved = amount / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
     peak = PEAK[bound]
     roof = {"bound": "hbm" if bound == "hbm" else "mfma", "kernel": f"pwq_{dn}", "layer": dl,
+            "kernels_per_call": launches_of(dn, dspec),
             "achieved": round(achieved, 3), "peak": peak, "unit": "GB/s" if unit == "byte" else "TFLOP/s",
-            "frac": round(achieved / peak, 5), "traffic": None, "launch_ms": round(dms, 4),
-            "algorithmic": amount}
+            "frac": round(achieved / peak, 5), "traffic": traffic_of(a.workload, dl, dn), "launch_ms": round(dms, 4),
+            "algorithmic": amount, "peak_kind": bound}
+    # the metric's X^T X MFMA utilisation, per layer
+    xtx = {}
+    for L in layers:
+        bnd, amt, _ = work_of("hessian_accumulate", L.spec)
+        d = per.get((L.spec.name, "hessian_accumulate"))
+        if d:
+            xtx[L.spec.name] = round(amt / (d * 1e-3) / 1e12 / PEAK[bnd], 4)
     mses = {L.spec.name: [float(x) for x in L.mse.cpu().tolist()] for L in layers}
 
     weights = sum(s.n_weights for s in specs)
@@ -262,6 +303,7 @@ def main():
                    "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order),
                    "layer_streams": bool(a.streams)},
         "roofline": roof,
+        "xtx_mfma_util": xtx,
         "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
         "breakdown_ms_by_layer": {f"{ln}/{nm}": round(v, 4) for (ln, nm), v in sorted(per.items(), key=lambda kv: -kv[1])},
         "mse_gptq_rtn": mses,

@@ -1,0 +1,156 @@
+"""Summaries of rocprofv3 output for the pwq library calls.
+
+Maps each GPU kernel of a run to the library call that launched it, and writes:
+
+* ``stats``   : a Markdown table of the kernel-trace statistics (one row per kernel, with
+  its call), plus per-call kernel time per step of the path (a step calls recon_mse twice,
+  every other call once), to set beside the per-call durations the bench measures with HIP
+  events;
+* ``traffic`` : HBM bytes per call from two counter runs (``FETCH_SIZE``, then
+  ``WRITE_SIZE``, KiB per dispatch), each scaled by what the same counter reads for a plain
+  1 GiB device copy; stored as JSON with a hash of the kernel sources, so a reader can tell
+  when the kernels have changed since the counters were taken.
+
+Usage (the CSV files are rocprofv3's ``--output-format csv`` results)::
+
+    python -m post_weight_quantization_27_amd.profile_summary stats STATS.csv \\
+        --steps N --cmd "..." --out profiles/NAME.md
+    python -m post_weight_quantization_27_amd.profile_summary traffic FETCH.csv WRITE.csv \\
+        CFETCH.csv CWRITE.csv --steps N --workload W --layer L --cmd "..." --out profiles/traffic.json
+
+N is the number of steps of the path the profiled run executed (bench.py runs warmup + 1 +
+2 x steps of them: warm-up, one step timed on the host, the timed steps, and the same number
+again with per-call events).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# kernel-name fragments -> library call (first match wins; the bench's own H.zero_() fill
+# is timed inside its hessian_accumulate events, so it is attributed there)
+CALL_OF = [
+    ("EpiHess", "hessian_accumulate"), ("hess_reduce", "hessian_accumulate"),
+    ("mirror_upper", "hessian_accumulate"), ("transpose_bf16", "hessian_accumulate"),
+    ("FillFunctor", "hessian_accumulate"),
+    ("damp_kernel", "hessian_damp"), ("act_order_kernel", "act_order_perm"),
+    ("copy_upper", "chol_inverse_upper"), ("copy_perm", "chol_inverse_upper"), ("set_int", "chol_inverse_upper"),
+    ("chol_diag", "chol_inverse_upper"), ("EpiStore", "chol_inverse_upper"), ("EpiSyrk", "chol_inverse_upper"),
+    ("EpiPush", "chol_inverse_upper"),
+    ("gptq_", "gptq_quantize_layer"), ("EpiSub", "gptq_quantize_layer"), ("inv_perm", "gptq_quantize_layer"),
+    ("unpermute_codes", "gptq_quantize_layer"),
+    ("rtn_kernel", "rtn_quantize"), ("dequant_kernel", "dequant"),
+    ("mse_", "recon_mse"), ("EpiSq", "recon_mse"), ("set_double", "recon_mse"),
+]
+
+
+def call_of(name: str) -> str:
+    for frag, call in CALL_OF:
+        if frag in name:
+            return call
+    return "other"
+
+
+def source_hash() -> str:
+    """sha256 over the kernel sources (csrc/*.hip, *.h) and the public header."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) + glob.glob(os.path.join(HERE, "csrc", "*.h")))
+    files.append(os.path.join(os.path.dirname(HERE), "include", "pwq.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short(name: str, n: int = 110) -> str:
+    name = name.replace("pwq::(anonymous namespace)::", "").replace("pwq::", "")
+    return name if len(name) <= n else name[: n - 3] + "..."
+
+
+def stats(a) -> None:
+    rows = list(csv.DictReader(open(a.stats_csv)))
+    per_call = defaultdict(float)
+    launches = defaultdict(int)
+    lines = [f"# Kernel trace summary\n", f"Command: `{a.cmd}`\n",
+             f"Kernel sources hash: `{source_hash()}`\n",
+             "| kernel | call | launches | avg us | total us | % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        c = call_of(r["Name"])
+        tot = float(r["TotalDurationNs"]) / 1e3
+        per_call[c] += tot
+        launches[c] += int(r["Calls"])
+        lines.append(f"| `{short(r['Name'])}` | {c} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{tot:.1f} | {float(r['Percentage']):.2f} |")
+    lines += ["", f"Per library call, per step of the path ({a.steps} steps ran; kernel time summed):", "",
+              "| call | kernel launches per step | kernel ms per step |", "|---|---|---|"]
+    for c, t in sorted(per_call.items(), key=lambda kv: -kv[1]):
+        lines.append(f"| {c} | {launches[c] / a.steps:.1f} | {t / a.steps / 1e3:.4f} |")
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counter_sum(path: str) -> dict:
+    """call -> summed counter value (KiB) over all dispatches."""
+    out = defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        out[call_of(r["Kernel_Name"])] += float(r["Counter_Value"])
+    return out
+
+
+def _copy_factor(path: str, nbytes: int) -> float:
+    """bytes per counter unit, from the 1 GiB copy dispatches of the calibration run."""
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if "copyBuffer" in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no copy dispatch in {path}")
+    return nbytes / (sum(vals) / len(vals))
+
+
+def traffic(a) -> None:
+    fetch, write = _counter_sum(a.fetch_csv), _counter_sum(a.write_csv)
+    ff = _copy_factor(a.cfetch_csv, 1 << 30)
+    fw = _copy_factor(a.cwrite_csv, 1 << 30)
+    calls = {}
+    for c in sorted(set(fetch) | set(write)):
+        calls[c] = {"fetch_bytes": fetch.get(c, 0.0) * ff / a.steps, "write_bytes": write.get(c, 0.0) * fw / a.steps}
+        calls[c]["hbm_bytes"] = calls[c]["fetch_bytes"] + calls[c]["write_bytes"]
+    data = {}
+    if os.path.exists(a.out):
+        data = json.load(open(a.out))
+    data[f"{a.workload}/{a.layer}"] = {
+        "command": a.cmd, "source_hash": source_hash(), "steps_run": a.steps,
+        "fetch_bytes_per_counter_unit": ff, "write_bytes_per_counter_unit": fw, "per_call": calls}
+    with open(a.out, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("--steps", type=int, required=True, help="steps of the path the run executed")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for k in ("fetch_csv", "write_csv", "cfetch_csv", "cwrite_csv"):
+        t.add_argument(k)
+    t.add_argument("--steps", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--layer", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args()
+    stats(a) if a.mode == "stats" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()
