@@ -115,7 +115,9 @@ def work_of(name, spec):
     wb = 4 if spec.w_dtype == "f32" else 2
     ng = 1 if spec.group_size == 0 else -(-n // spec.group_size)
     if name == "hessian_accumulate":            # symmetric X^T X: upper triangle + diagonal
-        return ("mfma_bf16" if xb == 2 else "mfma_f32"), N * n * (n + 1), "flop"
+        # float32 X with >= 1024 tokens and d_in >= 256 runs as four bfloat16 products
+        bf = xb == 2 or (n >= 256 and N >= 1024)
+        return ("mfma_bf16" if bf else "mfma_f32"), N * n * (n + 1), "flop"
     if name == "chol_inverse_upper":            # Cholesky n^3/3 + triangular inverse n^3/3
         return "mfma_f32", 2 * n ** 3 / 3, "flop"
     if name == "gptq_quantize_layer":           # trailing products + in-block rank-1 updates

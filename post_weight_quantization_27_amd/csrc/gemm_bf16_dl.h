@@ -12,7 +12,7 @@
 // chunk c of row r at position c ^ (r & 7), the same swizzle the fragment reads undo.  Two
 // LDS stages: the loads of tile t + 1 are in flight while tile t is multiplied.
 //
-// Operand requirements (checked by the host side): ld % 8 == 0, 16-byte aligned base, and
+// Operand requirements (checked by the host side): ld % 8 == 0, 16-byte aligned bases, and
 // for every k at or past an operand's K inside a segment the OTHER operand is 0 there (a
 // chunk start is clamped to K - 8, so reads stay inside the row; rows at or past M are
 // clamped to M - 1, and their outputs are discarded by the epilogue).
@@ -31,17 +31,22 @@ __device__ __forceinline__ void dl_load16(const uint16_t* g, uint16_t* lds_wave_
     __builtin_amdgcn_global_load_lds((const void*)g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
 }
 
-// Rows of bfloat16, optionally two k segments of kseg (the second reading p2).
+// Rows of bfloat16 over up to four k segments of kseg each (a multiple of BK16): logical k in
+// [s kseg, (s+1) kseg) reads seg[s] at k - s kseg.  One segment: kseg is unused.
 struct DlRows {
-    const uint16_t* p;
-    const uint16_t* p2;
+    const uint16_t* seg[4];
+    int nseg;
     int64_t ld, M, K, kseg;
     // 256 rows x 64 k of logical k0 into LDS tile S (256 x 64, swizzled): wave w issues the
     // eight 8-row groups g = w + 4 q
     __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
-        const uint16_t* base = p;
+        const uint16_t* base = seg[0];
         int64_t kk = k0;
-        if (p2 && k0 >= kseg) { base = p2; kk = k0 - kseg; }
+        if (nseg > 1) {
+            const int sg = (int)(k0 / kseg);
+            base = seg[sg];
+            kk = k0 - (int64_t)sg * kseg;
+        }
         const int pc = lane & 7, rl = lane >> 3;           // position in the row, row in the group
         const int lc = pc ^ rl;                            // logical chunk landing at pc
         int64_t kc = kk + 8 * lc;

@@ -3,8 +3,11 @@
 // damp * mean(diag H) and the act-order permutation (desc_act of the same page,
 // section "Running GPTQ with AutoGPTQ").
 //
-// The contraction runs over the upper-triangular tiles of H only: float32 X on the float32
-// MFMA engine, bfloat16 X on the bfloat16 one (products exact, float32 accumulate).  Small d_in gives few tiles, so the token range is cut into chunks whose partial
+// The contraction runs over the upper-triangular tiles of H only, accumulating in float32.
+// bfloat16 X: bfloat16 MFMA (products exact), large problems on the 256 x 256 direct-load
+// engine through a transposed copy.  float32 X: small problems on the float32 MFMA engine;
+// larger ones as the four products of a bfloat16 pair X = XH + XL on the direct-load engine
+// (each product exact; only X's residual below 2^-17 relative is dropped).  Small d_in gives few tiles, so the token range is cut into chunks whose partial
 // tiles land in a workspace and are summed in a fixed order (bit-reproducible, no
 // atomics).  A last pass copies the upper triangle onto the lower one.
 #include "gemm_bf16_dl.h"
@@ -167,6 +170,53 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
     }
 }
 
+// float32 X split into a bfloat16 pair, transposed: XH[c][t] = bf16(X[t][c]), XL[c][t] =
+// bf16(X[t][c] - XH[c][t]), zero for n_tok <= t < npad (64 x 64 per workgroup through LDS)
+__global__ __launch_bounds__(256) void transpose_split_f32_kernel(const float* __restrict__ X, int64_t n_tok, int64_t n,
+                                                                  int64_t ldx, int vec, uint16_t* __restrict__ XH,
+                                                                  uint16_t* __restrict__ XL, int64_t npad) {
+    __shared__ uint16_t th[64][64 + 8];
+    __shared__ uint16_t tl[64][64 + 8];
+    const int64_t t0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int idx = tid + 256 * h;
+        const int r = idx >> 4, ch = (idx & 15) * 4;       // token row r, columns ch .. ch+3
+        const int64_t t = t0 + r, c = c0 + ch;
+        float v[4];
+        if (vec && t < n_tok && c + 4 <= n) {
+            const float4 q = *(const float4*)(X + t * ldx + c);
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = (t < n_tok && c + k < n) ? X[t * ldx + c + k] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint16_t hb = f32_to_bf16_bits(v[k]);
+            th[r][ch + k] = hb;
+            tl[r][ch + k] = f32_to_bf16_bits(v[k] - bf16_bits_to_f32(hb));
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = tid + 256 * h;
+        const int cr = idx >> 3, tch = (idx & 7) * 8;
+        const int64_t c = c0 + cr;
+        if (c >= n) continue;
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            wh[k] = (uint32_t)th[tch + 2 * k][cr] | ((uint32_t)th[tch + 2 * k + 1][cr] << 16);
+            wl[k] = (uint32_t)tl[tch + 2 * k][cr] | ((uint32_t)tl[tch + 2 * k + 1][cr] << 16);
+        }
+        *(uint4*)(XH + c * npad + t0 + tch) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+        *(uint4*)(XL + c * npad + t0 + tch) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    }
+}
+
 // bfloat16 X on the direct-load engine: both operands are rows of the transposed copy
 // (tokens contiguous, zero past n_tok), 256 x 256 upper tiles
 hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, uint16_t* XT, float* part,
@@ -176,12 +226,33 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
                        (const uint16_t*)X, n_tok, n, ldx, vec, XT, pl.npad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    DlRows op{XT, nullptr, pl.npad, n, pl.npad, 0};
+    DlRows op{{XT, nullptr, nullptr, nullptr}, 1, pl.npad, n, pl.npad, 0};
     UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
     EpiHess epi{H, part, n, ntile, DL_TILE, pl.splits == 1};
     hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(ntile * pl.splits), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
+    return hipGetLastError();
+}
+
+// float32 X on the direct-load engine: X = XH + XL (+ a residual below 2^-17 |x|), and
+// X^T X = XH XH^T + XH XL^T + XL XH^T + XL XL^T, all four products exact in float32, summed
+// by one contraction over four k segments (A: XH XH XL XL, B: XH XL XH XL)
+hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, uint16_t* XH, float* part,
+                         const HessPlan& pl, hipStream_t s) {
+    uint16_t* XL = XH + n * pl.npad;
+    const int vec = (ldx % 4 == 0) && aligned(X, 16);
+    hipLaunchKernelGGL(transpose_split_f32_kernel, dim3((unsigned)(pl.npad / 64), (unsigned)cdiv(n, 64)), dim3(256), 0,
+                       s, (const float*)X, n_tok, n, ldx, vec, XH, XL, pl.npad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    DlRows a{{XH, XH, XL, XL}, 4, pl.npad, n, pl.npad, pl.npad};
+    DlRows b{{XH, XL, XH, XL}, 4, pl.npad, n, pl.npad, pl.npad};
+    UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr};
+    const int ntile = pl.tiles * (pl.tiles + 1) / 2;
+    EpiHess epi{H, part, n, ntile, DL_TILE, pl.splits == 1};
+    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(ntile * pl.splits), dim3(GEMM_THREADS),
+                       0, s, a, b, map, epi);
     return hipGetLastError();
 }
 
@@ -203,14 +274,16 @@ hipError_t hess_gemm(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float
 HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype) {
     HessPlan p{};
     const bool bf = x_dtype == 2;
-    // bfloat16 X with enough 256-wide tiles (and tokens) goes through the transposed copy
-    p.dl = bf && d_in >= 1024 && n_tok >= 256;
+    // bfloat16 X with enough 256-wide tiles (and tokens) goes through a transposed copy;
+    // float32 X through a transposed bfloat16 pair (four products), once there are enough
+    // tokens for the split to pay
+    p.dl = (bf && d_in >= 1024 && n_tok >= 256) ? 1 : ((!bf && d_in >= 256 && n_tok >= 1024) ? 4 : 0);
     p.bm = p.dl ? DL_TILE : ((!bf && d_in <= 1024) ? 64 : 128);
     p.tiles = (int)cdiv(d_in, p.bm);
     const int ntile = p.tiles * (p.tiles + 1) / 2;
     const int kq = (bf || p.dl) ? BK16 : GEMM_BK;       // chunk boundaries on whole k-tiles
     p.npad = p.dl ? cdiv(n_tok, 64) * 64 : n_tok;
-    const int64_t ksteps = cdiv(p.npad, kq);
+    const int64_t ksteps = cdiv(p.npad * (p.dl == 4 ? 4 : 1), kq);
     // one 256-wide workgroup per CU (LDS), else >= 4 workgroups per CU of 256
     const int target = p.dl ? 512 : 1024;
     int64_t splits = ntile >= target ? 1 : cdiv(target, ntile);
@@ -218,9 +291,10 @@ HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype) {
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
     p.kchunk = cdiv(ksteps, splits) * kq;
-    p.splits = (int)cdiv(p.npad, p.kchunk);
+    p.splits = (int)cdiv(p.npad * (p.dl == 4 ? 4 : 1), p.kchunk);
     if (p.splits < 1) p.splits = 1;
-    p.xt_bytes = p.dl ? align_up((size_t)d_in * p.npad * sizeof(uint16_t), 256) : 0;
+    const int copies = p.dl == 4 ? 2 : (p.dl ? 1 : 0);   // transposed X, or its bfloat16 pair
+    p.xt_bytes = align_up((size_t)copies * d_in * p.npad * sizeof(uint16_t), 256);
     const size_t parts = p.splits > 1 ? (size_t)p.splits * ntile * p.bm * p.bm * sizeof(float) : 0;
     p.ws_bytes = p.xt_bytes + parts;
     return p;
@@ -232,7 +306,9 @@ hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_i
     const HessPlan pl = hessian_plan(n_tok, d_in, x_dtype);
     float* part = (float*)((char*)ws + pl.xt_bytes);
     hipError_t e;
-    if (x_dtype == 0) {
+    if (pl.dl == 4) {
+        e = hess_gemm_dl4(X, n_tok, d_in, ldx, H, (uint16_t*)ws, part, pl, s);
+    } else if (x_dtype == 0) {
         e = pl.bm == 64 ? hess_gemm<64, 0>(X, n_tok, d_in, ldx, H, part, pl, s) : hess_gemm<128, 0>(X, n_tok, d_in, ldx, H, part, pl, s);
     } else if (pl.dl) {
         e = hess_gemm_dl(X, n_tok, d_in, ldx, H, (uint16_t*)ws, part, pl, s);

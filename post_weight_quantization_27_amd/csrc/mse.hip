@@ -232,8 +232,8 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
     if (dl) {
         // large bfloat16 problems: direct-load engine, 256 x 256 tiles (dW's zero tail covers
         // the clamped X chunks past d_in)
-        DlRows a{(const uint16_t*)X, (const uint16_t*)X, ldx, n_tok, d_in, kseg};
-        DlRows b{dhi, dlo, kseg, d_out, kseg, kseg};
+        DlRows a{{(const uint16_t*)X, (const uint16_t*)X, nullptr, nullptr}, 2, ldx, n_tok, d_in, kseg};
+        DlRows b{{dhi, dlo, nullptr, nullptr}, 2, kseg, d_out, kseg, kseg};
         RectMap mp{};
         mp.M = n_tok; mp.N = d_out; mp.K = 2 * kseg;
         mp.tiles_m = (int)cdiv(n_tok, DL_TILE);

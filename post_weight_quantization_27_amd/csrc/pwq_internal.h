@@ -17,9 +17,10 @@ struct HessPlan {
     int tiles;         // tiles per edge
     int splits;        // token chunks
     int64_t kchunk;    // tokens per chunk (multiple of the engine's k tile)
-    int dl;            // bfloat16 X through a transposed copy on the direct-load engine
+    int dl;            // direct-load engine: 1 = bfloat16 X transposed, 4 = float32 X as a transposed
+                       // bfloat16 pair (four products), 0 = register-staged engines
     int64_t npad;      // tokens of the transposed copy (multiple of 64, zero tail)
-    size_t xt_bytes;   // transposed copy (0 unless dl)
+    size_t xt_bytes;   // transposed copy or pair (0 unless dl)
     size_t ws_bytes;   // transposed copy + partial tiles (0 when neither is needed)
 };
 HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype);
