@@ -286,6 +286,15 @@ struct EpiSyrk {                  // A[row][col] -= acc on the upper triangle of
     __device__ __forceinline__ void finish(const Tile&, int, bool) {}
 };
 
+struct EpiSyrkRect {              // A[row][col0 + col] -= acc on the upper triangle (row <= col0 + col)
+    float* U;                     // = A + col0
+    int64_t ld, col0, N;
+    __device__ __forceinline__ void element(const Tile&, int64_t row, int64_t col, float v) {
+        if (row <= col0 + col && col < N) U[row * ld + col] -= v;
+    }
+    __device__ __forceinline__ void finish(const Tile&, int, bool) {}
+};
+
 struct EpiPush {                  // R[row][col] (+)= acc; the first `fresh` columns are overwritten
     float* out;
     int64_t ld, M, N, fresh;
@@ -318,31 +327,66 @@ template <int T>
 using SyrkTask = GemmTask<T, T, OpMMajor<0>, OpMMajor<0>, UpperMap, EpiSyrk>;
 template <int T>
 using PushTask = GemmTask<T, T, OpMMajor<0>, OpKMajor<0>, RectMap, EpiPush>;
+template <int T>
+using SyrkRectTask = GemmTask<T, T, OpMMajor<0>, OpMMajor<0>, RectMap, EpiSyrkRect>;
 
 int ntiles(const RectMap& m) { return m.tiles_m * m.tiles_n; }
 int ntiles(const UpperMap& m) { return m.tiles * (m.tiles + 1) / 2; }
 
+// Panels of a super-block: P holds the V columns of its chol_sb(n) blocks side by side (row
+// stride pld = chol_sb(n) * CHOL_NB, the workspace's width); block slot t at column t * CHOL_NB.
+constexpr int CHOL_SB = 4;
+constexpr int64_t CHOL_LAZY_N = 4096;            // batch the updates from this size on
+inline int chol_sb(int64_t n) { return n >= CHOL_LAZY_N ? CHOL_SB : 1; }
+
+// After the last block of a super-block [s0, s1) (depth kf = s1 - s0 of panels in P):
+//   A[0:s0, 0:s0] -= P P^T           (upper triangle; P = V[0:s0, s0:s1])
+//   R[0:s0, s0:n] (+)= P U[s0:s1, s0:n]   (columns s0..s1 overwritten: they held A)
 template <int T>
-hipError_t launch_update(float* U, float* P, int64_t n, int64_t k0, int bs, int32_t* info, int vu, hipStream_t s) {
+hipError_t launch_far(float* U, const float* P, int pld, int64_t n, int64_t s0, int kf, int32_t* info, int vu,
+                      hipStream_t s) {
     SyrkTask<T> sy{};
-    sy.la = OpMMajor<0>{P, CHOL_NB, k0, bs, 1};
+    sy.la = OpMMajor<0>{P, pld, s0, kf, 1};
     sy.lb = sy.la;
-    sy.map = UpperMap{k0, bs, (int)cdiv(k0, T), 1, cdiv(bs, GEMM_BK) * GEMM_BK, nullptr};
-    sy.epi = EpiSyrk{U, n, k0};
+    sy.map = UpperMap{s0, kf, (int)cdiv(s0, T), 1, cdiv(kf, GEMM_BK) * GEMM_BK, nullptr};
+    sy.epi = EpiSyrk{U, n, s0};
     PushTask<T> pu{};
-    pu.la = OpMMajor<0>{P, CHOL_NB, k0, bs, 1};
-    pu.lb = OpKMajor<0>{U + k0 * n + k0, n, n - k0, bs, vu && (k0 % 4 == 0)};
-    pu.map = rect(T, T, k0, n - k0, bs);
-    pu.epi = EpiPush{U + k0, n, k0, n - k0, bs};
+    pu.la = OpMMajor<0>{P, pld, s0, kf, 1};
+    pu.lb = OpKMajor<0>{U + s0 * n + s0, n, n - s0, kf, vu && (s0 % 4 == 0)};
+    pu.map = rect(T, T, s0, n - s0, kf);
+    pu.epi = EpiPush{U + s0, n, s0, n - s0, kf};
     const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
     hipLaunchKernelGGL((gemm_f32_dual_kernel<SyrkTask<T>, PushTask<T>>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy, pu, n1,
                        info);
     return hipGetLastError();
 }
 
+// After block [k0, k0 + bs) of a super-block starting at s0 < k0, for the blocks of the
+// super-block still to come (its panel Pk = V[0:k0, block] in P):
+//   A[0:k0, s0:k0] -= Pk Pk[s0:k0]^T       (their columns, every row above)
+//   R[s0:k0, k0:n] (+)= Pk[s0:k0] U[block, k0:n]   (their rows; columns k0..k0+bs overwritten)
+template <int T>
+hipError_t launch_near(float* U, const float* Pk, int pld, int64_t n, int64_t s0, int64_t k0, int bs, int32_t* info,
+                       int vu, hipStream_t s) {
+    SyrkRectTask<T> sy{};
+    sy.la = OpMMajor<0>{Pk, pld, k0, bs, 1};
+    sy.lb = OpMMajor<0>{Pk + s0 * pld, pld, k0 - s0, bs, 1};
+    sy.map = rect(T, T, k0, k0 - s0, bs);
+    sy.epi = EpiSyrkRect{U + s0, n, s0, k0 - s0};
+    PushTask<T> pu{};
+    pu.la = OpMMajor<0>{Pk + s0 * pld, pld, k0 - s0, bs, 1};
+    pu.lb = OpKMajor<0>{U + k0 * n + k0, n, n - k0, bs, vu && (k0 % 4 == 0)};
+    pu.map = rect(T, T, k0 - s0, n - k0, bs);
+    pu.epi = EpiPush{U + s0 * n + k0, n, k0 - s0, n - k0, bs};
+    const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
+    hipLaunchKernelGGL((gemm_f32_dual_kernel<SyrkRectTask<T>, PushTask<T>>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy,
+                       pu, n1, info);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-size_t chol_ws_bytes(int64_t n) { return (size_t)n * CHOL_NB * sizeof(float); }
+size_t chol_ws_bytes(int64_t n) { return (size_t)n * (chol_sb(n) * CHOL_NB) * sizeof(float); }
 
 hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U, int32_t* info, void* ws, hipStream_t s) {
     if (n == 0) return hipSuccess;
@@ -354,13 +398,21 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
     else hipLaunchKernelGGL(copy_upper_kernel, dim3((unsigned)cdiv(n, 1024), (unsigned)n), dim3(256), 0, s, H, U, n);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    float* P = (float*)ws;     // n x CHOL_NB panel
+    // Blocks of CHOL_NB columns from the last to the first, in super-blocks of chol_sb(n)
+    // blocks aligned to their size: the updates a block owes to the matrix above and left of
+    // its super-block wait until the super-block is done, and then go as one deeper product.
+    float* P = (float*)ws;     // n x pld: the super-block's V panels
     const int nt = (int)cdiv(n, CHOL_NB);
+    const int sb = chol_sb(n);
+    const int pld = sb * CHOL_NB;
     const int vu = vec_ok(U, n);
     for (int kb = nt - 1; kb >= 0; --kb) {
         const int64_t k0 = (int64_t)kb * CHOL_NB;
         const int bs = (int)((n - k0) < CHOL_NB ? (n - k0) : CHOL_NB);
         const int64_t r = n - k0 - bs;
+        const int kb_lo = kb / sb * sb;                  // first block of this super-block
+        const int64_t s0 = (int64_t)kb_lo * CHOL_NB;
+        float* Pk = P + (kb - kb_lo) * CHOL_NB;          // this block's panel slot
         hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, U, n, k0, bs, info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -369,7 +421,7 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
         tt.la = OpMMajor<0>{U + k0, n, k0, bs, vu && (k0 % 4 == 0)};
         tt.lb = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
         tt.map = rect(64, 64, k0, bs, bs);
-        tt.epi = EpiStore{P, CHOL_NB, k0, bs, 1.f};
+        tt.epi = EpiStore{Pk, pld, k0, bs, 1.f};
         FinalizeTask ft{};
         ft.la = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
         ft.lb = OpKMajor<0>{U + k0 * n + k0 + bs, n, r, bs, vu && ((k0 + bs) % 4 == 0)};
@@ -383,9 +435,18 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         if (k0 == 0) break;
-        // syrk (top-left, upper) + push (top-right R)
-        const int64_t big = cdiv(k0, 128) * cdiv(n, 128);
-        e = big >= 512 ? launch_update<128>(U, P, n, k0, bs, info, vu, s) : launch_update<64>(U, P, n, k0, bs, info, vu, s);
+        if (kb > kb_lo) {
+            // more blocks of this super-block follow: only what they need now
+            const int64_t big = cdiv(k0, 128) * cdiv(k0 - s0, 128) + cdiv(k0 - s0, 128) * cdiv(n - k0, 128);
+            e = big >= 512 ? launch_near<128>(U, Pk, pld, n, s0, k0, bs, info, vu, s)
+                           : launch_near<64>(U, Pk, pld, n, s0, k0, bs, info, vu, s);
+        } else {
+            // super-block done: everything above and right of it, depth = its width
+            const int kf = (int)((kb_lo + sb) * (int64_t)CHOL_NB < n ? sb * CHOL_NB : n - s0);
+            const int64_t big = cdiv(s0, 128) * cdiv(n, 128);
+            e = big >= 512 ? launch_far<128>(U, P, pld, n, s0, kf, info, vu, s)
+                           : launch_far<64>(U, P, pld, n, s0, kf, info, vu, s);
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -226,7 +226,9 @@ def _spd(rng, n, n_tok=None, outliers=20.0):
     return Hd.astype(np.float32)
 
 
-@pytest.mark.parametrize("n", [1, 2, 77, 128, 200, 768, 1000, 3072])
+# from 4096 on, the updates are batched per super-block of four blocks (4200: ragged last
+# block; 4608: a super-block boundary inside the matrix, ragged none)
+@pytest.mark.parametrize("n", [1, 2, 77, 128, 200, 768, 1000, 3072, 4096, 4200, 4608])
 def test_chol_inverse_upper(pwq, n):
     rng = np.random.default_rng(n)
     H32 = _spd(rng, n)
@@ -240,9 +242,9 @@ def test_chol_inverse_upper(pwq, n):
     assert np.max(np.abs(R - np.eye(n))) <= 5e-3
 
 
-def test_chol_perm(pwq):
+@pytest.mark.parametrize("n", [520, 4300])
+def test_chol_perm(pwq, n):
     rng = np.random.default_rng(12)
-    n = 520
     H32 = _spd(rng, n)
     perm = O.act_order_perm(H32.astype(np.float64))
     U, info = pwq.chol_inverse_upper(dev(H32), dev(perm))
