@@ -278,31 +278,40 @@ struct EpiStore {                 // out[row][col] = alpha * acc
 };
 
 struct EpiSyrk {                  // A[row][col] -= acc on the upper triangle of the leading N x N
+    static constexpr bool kRmw = true;
     float* U;
     int64_t ld, N;
-    __device__ __forceinline__ void element(const Tile&, int64_t row, int64_t col, float v) {
-        if (row <= col && col < N) U[row * ld + col] -= v;
+    __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
+        return (row <= col && col < N) ? U[row * ld + col] : 0.f;
+    }
+    __device__ __forceinline__ void put(const Tile&, int64_t row, int64_t col, float v, float o) {
+        if (row <= col && col < N) U[row * ld + col] = o - v;
     }
     __device__ __forceinline__ void finish(const Tile&, int, bool) {}
 };
 
 struct EpiSyrkRect {              // A[row][col0 + col] -= acc on the upper triangle (row <= col0 + col)
+    static constexpr bool kRmw = true;
     float* U;                     // = A + col0
     int64_t ld, col0, N;
-    __device__ __forceinline__ void element(const Tile&, int64_t row, int64_t col, float v) {
-        if (row <= col0 + col && col < N) U[row * ld + col] -= v;
+    __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
+        return (row <= col0 + col && col < N) ? U[row * ld + col] : 0.f;
+    }
+    __device__ __forceinline__ void put(const Tile&, int64_t row, int64_t col, float v, float o) {
+        if (row <= col0 + col && col < N) U[row * ld + col] = o - v;
     }
     __device__ __forceinline__ void finish(const Tile&, int, bool) {}
 };
 
 struct EpiPush {                  // R[row][col] (+)= acc; the first `fresh` columns are overwritten
+    static constexpr bool kRmw = true;
     float* out;
     int64_t ld, M, N, fresh;
-    __device__ __forceinline__ void element(const Tile&, int64_t row, int64_t col, float v) {
-        if (row < M && col < N) {
-            float* p = out + row * ld + col;
-            *p = col < fresh ? v : *p + v;
-        }
+    __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
+        return (row < M && col < N && col >= fresh) ? out[row * ld + col] : 0.f;
+    }
+    __device__ __forceinline__ void put(const Tile&, int64_t row, int64_t col, float v, float o) {
+        if (row < M && col < N) out[row * ld + col] = col < fresh ? v : o + v;
     }
     __device__ __forceinline__ void finish(const Tile&, int, bool) {}
 };

@@ -240,13 +240,11 @@ __device__ __forceinline__ void gemm_bf16_tile(const LA& la, const LB& lb, const
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = t.m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-                epi.element(t, row, col, acc[i][j][v]);
-            }
+        for (int j = 0; j < FN; ++j) {
+            const int64_t r0 = t.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
+            const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+            epi_block16(epi, t, acc[i][j], [&](int v) { return r0 + 8 * (v >> 2) + (v & 3); }, col);
+        }
 }
 
 template <int BM, int BN, class LA, class LB, class MAP, class EPI>

@@ -146,13 +146,11 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = t.m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                const int64_t col = t.n0 + wn * 128 + j * 32 + (lane & 31);
-                epi.element(t, row, col, acc[i][j][v]);
-            }
+        for (int j = 0; j < FN; ++j) {
+            const int64_t r0 = t.m0 + wm * 128 + i * 32 + 4 * (lane >> 5);
+            const int64_t col = t.n0 + wn * 128 + j * 32 + (lane & 31);
+            epi_block16(epi, t, acc[i][j], [&](int v) { return r0 + 8 * (v >> 2) + (v & 3); }, col);
+        }
 }
 
 template <class LA, class LB, class MAP, class EPI>

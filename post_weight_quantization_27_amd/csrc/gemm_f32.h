@@ -190,6 +190,33 @@ struct UpperMap {
     }
 };
 
+// ---------------------------------------------------------------- epilogue protocol
+// Plain epilogues take element(t, row, col, v) for every output.  Epilogues that read the
+// output before writing it declare `static constexpr bool kRmw = true` and give
+// old(t, row, col) (the value read; 0 when out of range or not needed) and
+// put(t, row, col, v, old).  The engines read the 16 values of an accumulator block before
+// writing any of them: the compiler cannot prove that one element's write does not alias
+// the next element's read, so element-wise read-modify-writes would wait one memory latency
+// each.
+template <class EPI, class = void>
+struct EpiIsRmw { static constexpr bool value = false; };
+template <class EPI>
+struct EpiIsRmw<EPI, decltype((void)EPI::kRmw)> { static constexpr bool value = EPI::kRmw; };
+
+template <class EPI, class ROW>
+__device__ __forceinline__ void epi_block16(EPI& epi, const Tile& t, const f32x16& acc, ROW row_of, int64_t col) {
+    if constexpr (EpiIsRmw<EPI>::value) {
+        float old[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) old[v] = epi.old(t, row_of(v), col);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) epi.put(t, row_of(v), col, acc[v], old[v]);
+    } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) epi.element(t, row_of(v), col, acc[v]);
+    }
+}
+
 // ---------------------------------------------------------------- the tile engine
 // Epilogue interface:
 //   __device__ void element(const Tile&, int64_t row, int64_t col, float v)  for every
@@ -203,6 +230,32 @@ struct GemmLds {
     static constexpr int B_FLOATS = GEMM_BK * (BN + LB::PAD);
     static constexpr int FLOATS = A_FLOATS + B_FLOATS;
 };
+
+// one k-tile of MFMAs from the operand tiles in LDS
+template <int BM, int BN, class LA, class LB>
+__device__ __forceinline__ void gemm_ktile(const float* As, const float* Bs, f32x16 (&acc)[BM / 64][BN / 64], int lane,
+                                           int wm, int wn) {
+    constexpr int FM = BM / 64, FN = BN / 64;
+#pragma unroll 4
+    for (int kk = 0; kk < GEMM_BK; kk += 2) {
+        float a[FM], b[FN];
+        const int kr = kk + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = As[kr * (BM + LA::PAD) + wm * (BM / 2) + i * 32 + (lane & 31)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[j] = Bs[kr * (BN + LB::PAD) + wn * (BN / 2) + j * 32 + (lane & 31)];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// Short k ranges (at most SHORT_KT k-tiles, e.g. the depth-128 updates of the factor and of
+// the GPTQ loop) on small tiles: every k-tile's global loads are issued at the start, so the
+// tile waits for one memory latency instead of one per k-tile.
+constexpr int SHORT_KT = 4;
 
 template <int BM, int BN, class LA, class LB, class EPI>
 __device__ __forceinline__ void gemm_tile(const LA& la, const LB& lb, const Tile& t, EPI& epi, float* lds) {
@@ -222,48 +275,60 @@ __device__ __forceinline__ void gemm_tile(const LA& la, const LB& lb, const Tile
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    typename LA::template Regs<BM> ra;
-    typename LB::template Regs<BN> rb;
-    la.template load<BM>(ra, t.m0, t.kbeg, tid);
-    lb.template load<BN>(rb, t.n0, t.kbeg, tid);
-
-    for (int64_t k0 = t.kbeg; k0 < t.kend; k0 += GEMM_BK) {
-        __syncthreads();
-        la.template store<BM>(As, ra, tid);
-        lb.template store<BN>(Bs, rb, tid);
-        __syncthreads();
-        if (k0 + GEMM_BK < t.kend) {
-            la.template load<BM>(ra, t.m0, k0 + GEMM_BK, tid);
-            lb.template load<BN>(rb, t.n0, k0 + GEMM_BK, tid);
+    // kbeg and every split boundary are multiples of GEMM_BK, so a k-tile never reaches into
+    // the next chunk; past K both operands are zero-filled.
+    bool done = false;
+    if constexpr (BM * BN <= 64 * 64) {
+        const int nk = (int)((t.kend - t.kbeg + GEMM_BK - 1) / GEMM_BK);
+        if (nk <= SHORT_KT) {
+            typename LA::template Regs<BM> ra[SHORT_KT];
+            typename LB::template Regs<BN> rb[SHORT_KT];
+#pragma unroll
+            for (int i = 0; i < SHORT_KT; ++i) {
+                if (i < nk) {
+                    la.template load<BM>(ra[i], t.m0, t.kbeg + i * GEMM_BK, tid);
+                    lb.template load<BN>(rb[i], t.n0, t.kbeg + i * GEMM_BK, tid);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < SHORT_KT; ++i) {
+                if (i < nk) {
+                    __syncthreads();
+                    la.template store<BM>(As, ra[i], tid);
+                    lb.template store<BN>(Bs, rb[i], tid);
+                    __syncthreads();
+                    gemm_ktile<BM, BN, LA, LB>(As, Bs, acc, lane, wm, wn);
+                }
+            }
+            done = true;
         }
-        // kbeg and every split boundary are multiples of GEMM_BK, so a k-tile never
-        // reaches into the next chunk; past K both operands are zero-filled.
-#pragma unroll 4
-        for (int kk = 0; kk < GEMM_BK; kk += 2) {
-            float a[FM], b[FN];
-            const int kr = kk + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) a[i] = As[kr * (BM + LA::PAD) + wm * (BM / 2) + i * 32 + (lane & 31)];
-#pragma unroll
-            for (int j = 0; j < FN; ++j) b[j] = Bs[kr * (BN + LB::PAD) + wn * (BN / 2) + j * 32 + (lane & 31)];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (!done) {
+        typename LA::template Regs<BM> ra;
+        typename LB::template Regs<BN> rb;
+        la.template load<BM>(ra, t.m0, t.kbeg, tid);
+        lb.template load<BN>(rb, t.n0, t.kbeg, tid);
+        for (int64_t k0 = t.kbeg; k0 < t.kend; k0 += GEMM_BK) {
+            __syncthreads();
+            la.template store<BM>(As, ra, tid);
+            lb.template store<BN>(Bs, rb, tid);
+            __syncthreads();
+            if (k0 + GEMM_BK < t.kend) {
+                la.template load<BM>(ra, t.m0, k0 + GEMM_BK, tid);
+                lb.template load<BN>(rb, t.n0, k0 + GEMM_BK, tid);
+            }
+            gemm_ktile<BM, BN, LA, LB>(As, Bs, acc, lane, wm, wn);
         }
     }
 
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                int64_t row = t.m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-                epi.element(t, row, col, acc[i][j][v]);
-            }
+        for (int j = 0; j < FN; ++j) {
+            const int64_t r0 = t.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
+            const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+            epi_block16(epi, t, acc[i][j], [&](int v) { return r0 + 8 * (v >> 2) + (v & 3); }, col);
+        }
 }
 
 template <int BM, int BN, class LA, class LB, class MAP, class EPI>

@@ -496,10 +496,14 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
 
 // Wf[r][c0 + col] -= acc
 struct EpiSub {
+    static constexpr bool kRmw = true;
     float* out;
     int64_t ld, M, N;
-    __device__ __forceinline__ void element(const Tile&, int64_t row, int64_t col, float v) {
-        if (row < M && col < N) out[row * ld + col] -= v;
+    __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
+        return (row < M && col < N) ? out[row * ld + col] : 0.f;
+    }
+    __device__ __forceinline__ void put(const Tile&, int64_t row, int64_t col, float v, float o) {
+        if (row < M && col < N) out[row * ld + col] = o - v;
     }
     __device__ __forceinline__ void finish(const Tile&, int, bool) {}
 };

@@ -20,13 +20,17 @@ namespace {
 // split > 1: partial tile of chunk `split` -> ws[split][tile][BM*BN]
 // split == 1: H[row][col] += 2 * acc directly (upper tiles only; diagonal tiles whole)
 struct EpiHess {
+    static constexpr bool kRmw = true;
     float* H;
     float* part;
     int64_t n;
     int ntile, bm, direct;
-    __device__ __forceinline__ void element(const Tile& t, int64_t row, int64_t col, float v) {
+    __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
+        return (direct && row < n && col < n) ? H[row * n + col] : 0.f;
+    }
+    __device__ __forceinline__ void put(const Tile& t, int64_t row, int64_t col, float v, float o) {
         if (direct) {
-            if (row < n && col < n) H[row * n + col] += 2.f * v;
+            if (row < n && col < n) H[row * n + col] = o + 2.f * v;
         } else {
             int64_t lr = row - t.m0, lc = col - t.n0;
             part[((int64_t)t.split * ntile + t.tile) * (int64_t)(bm * bm) + lr * bm + lc] = v;
