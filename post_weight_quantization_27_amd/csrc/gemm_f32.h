@@ -149,17 +149,21 @@ struct Tile {
 
 // Rectangular grid of BM x BN tiles over M x N, times `splits` chunks of k.
 // tri_k: the k range of a tile starts at its m0 (A upper triangular: A(m, k) = 0, k < m).
+// Workgroups run in block order: tiles_m fastest (m-blocks of one n-block run together and
+// share that B block), or with nfast set, tiles_n fastest (n-blocks of one m-block share A).
 struct RectMap {
     int64_t M, N, K;
     int tiles_m, tiles_n, splits;
     int64_t kchunk;
     int tri_k;
     const int32_t* guard;     // optional: skip all work when *guard != 0
+    int nfast;
     __device__ __forceinline__ bool get(int bid, int BM, int BN, Tile& t) const {
         int ntile = tiles_m * tiles_n;
         t.split = bid / ntile;
         t.tile = bid % ntile;
-        int ti = t.tile % tiles_m, tj = t.tile / tiles_m;
+        int ti = nfast ? t.tile / tiles_n : t.tile % tiles_m;
+        int tj = nfast ? t.tile % tiles_n : t.tile / tiles_m;
         t.m0 = (int64_t)ti * BM;
         t.n0 = (int64_t)tj * BN;
         t.kbeg = (int64_t)t.split * kchunk;

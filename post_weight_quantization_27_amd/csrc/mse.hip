@@ -242,6 +242,9 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
         mp.kchunk = 2 * kseg;
         mp.tri_k = 0;
         mp.guard = nullptr;
+        // output columns fastest: the workgroups in flight share a few X row blocks (X is
+        // the large operand, tokens x d_in), and dW's blocks are the ones re-read
+        mp.nfast = 1;
         EpiSq ep{part, n_tok, d_out, 0.f};
         nb = (int64_t)mp.tiles_m * mp.tiles_n;
         hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, RectMap, EpiSq>), dim3((unsigned)nb), dim3(GEMM_THREADS), 0, s,
