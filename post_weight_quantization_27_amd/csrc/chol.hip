@@ -138,18 +138,22 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
     // values on the way (they only ever feed other entries below the diagonal) and are
     // written back as 0.  Then all four waves apply the panel's rank-32 update to the rows
     // and columns left of it on MFMA.
-    // unrolled over the four panels, so every readlane lane index is a constant
+    // unrolled over the four panels, so every readlane lane index is a constant.  A pivot's
+    // broadcasts all go out before its FMAs (each into its own SGPR, fenced by a scheduling
+    // barrier): interleaved, every FMA pair would wait out the latency of its own readlane.
+    // Rows 64..127 lie below the diagonal of the two left panels, which skip them.
 #pragma unroll
     for (int p = 3; p >= 0; --p) {
         const int c0 = 32 * p;
         if (wave == 0) {
             const int h = c0 >> 6;                       // register holding the panel rows
             const int lb = c0 & 63;                      // lane of the panel's first row
+            const bool hi = c0 + 32 > 64;                // rows 64.. reach the panel's diagonal
             float a0[32], a1[32];
 #pragma unroll
             for (int kk = 0; kk < 32; ++kk) {
                 a0[kk] = A[lane][c0 + kk];
-                a1[kk] = A[lane + 64][c0 + kk];
+                a1[kk] = hi ? A[lane + 64][c0 + kk] : 0.f;
             }
             int bad = -1;                                // first failed pivot (uniform)
 #pragma unroll
@@ -159,14 +163,20 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
                 if (!(d > 0.f) && bad < 0) bad = kk;
                 const float r = __builtin_amdgcn_rsqf(d);
                 a0[kk] *= r;                             // column kk of V (the pivot row gets d r)
-                a1[kk] *= r;
+                if (hi) a1[kk] *= r;
                 const float vc = h ? a1[kk] : a0[kk];
+                float vj[32];
 #pragma unroll
-                for (int jj = 0; jj < kk; ++jj) {
-                    const float vjk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vc), lb + jj));
-                    a0[jj] = fmaf(-a0[kk], vjk, a0[jj]);
-                    a1[jj] = fmaf(-a1[kk], vjk, a1[jj]);
+                for (int jj = 0; jj < kk; ++jj)
+                    vj[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vc), lb + jj));
+                __builtin_amdgcn_sched_barrier(0);
+                // the next pivot's column first, so its readlane finds it done
+#pragma unroll
+                for (int jj = kk - 1; jj >= 0; --jj) {
+                    a0[jj] = fmaf(-a0[kk], vj[jj], a0[jj]);
+                    if (hi) a1[jj] = fmaf(-a1[kk], vj[jj], a1[jj]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int kk = 0; kk < 32; ++kk) {
