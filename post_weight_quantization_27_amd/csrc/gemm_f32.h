@@ -174,22 +174,38 @@ struct RectMap {
 };
 
 // Upper-triangular tile pairs (ti <= tj) of an N x N output, times `splits` k chunks.
+// Upper-triangle tiles (ti <= tj) of an N x N output.  Workgroups [0, full) take tiles
+// [0, full) over the whole k range (t.split = -1); the tiles after them are split into
+// `splits` k chunks of kchunk, workgroup full + s * (ntile - full) + j taking chunk s of tile
+// full + j.  With full = 0 every tile is split.
 struct UpperMap {
     int64_t N, K;
     int tiles, splits;
     int64_t kchunk;
     const int32_t* guard;
+    int full;
     __device__ __forceinline__ bool get(int bid, int BM, int BN, Tile& t) const {
-        int ntile = tiles * (tiles + 1) / 2;
-        t.split = bid / ntile;
-        t.tile = bid % ntile;
+        const int ntile = tiles * (tiles + 1) / 2;
+        if (bid < full) {
+            t.split = -1;
+            t.tile = bid;
+        } else {
+            const int nt = ntile - full, b = bid - full;
+            t.split = b / nt;
+            t.tile = full + b % nt;
+        }
         int r = t.tile, ti = 0;
         while (r >= tiles - ti) { r -= tiles - ti; ++ti; }
         int tj = ti + r;
         t.m0 = (int64_t)ti * BM;
         t.n0 = (int64_t)tj * BN;
-        t.kbeg = (int64_t)t.split * kchunk;
-        t.kend = t.kbeg + kchunk < K ? t.kbeg + kchunk : K;
+        if (t.split < 0) {
+            t.kbeg = 0;
+            t.kend = K;
+        } else {
+            t.kbeg = (int64_t)t.split * kchunk;
+            t.kend = t.kbeg + kchunk < K ? t.kbeg + kchunk : K;
+        }
         return t.kbeg < t.kend;
     }
 };

@@ -24,27 +24,27 @@ struct EpiHess {
     float* H;
     float* part;
     int64_t n;
-    int ntile, bm, direct;
-    __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
-        return (direct && row < n && col < n) ? H[row * n + col] : 0.f;
+    int full, ntail, bm;       // whole-k tiles [0, full) add into H; split tiles write partials
+    __device__ __forceinline__ float old(const Tile& t, int64_t row, int64_t col) const {
+        return (t.split < 0 && row < n && col < n) ? H[row * n + col] : 0.f;
     }
     __device__ __forceinline__ void put(const Tile& t, int64_t row, int64_t col, float v, float o) {
-        if (direct) {
+        if (t.split < 0) {
             if (row < n && col < n) H[row * n + col] = o + 2.f * v;
         } else {
             int64_t lr = row - t.m0, lc = col - t.n0;
-            part[((int64_t)t.split * ntile + t.tile) * (int64_t)(bm * bm) + lr * bm + lc] = v;
+            part[((int64_t)t.split * ntail + (t.tile - full)) * (int64_t)(bm * bm) + lr * bm + lc] = v;
         }
     }
     __device__ __forceinline__ void finish(const Tile&, int, bool) {}
 };
 
-// H[tile] += 2 * sum_s part[s][tile], s in increasing order.
-// grid: x = 1024-element chunk of a tile, y = upper tile index
+// H[tile] += 2 * sum_s part[s][tile - full] over the split tiles, s in increasing order.
+// grid: x = 1024-element chunk of a tile, y = split tile index (tile - full)
 __global__ __launch_bounds__(256) void hess_reduce_kernel(const float* __restrict__ part, float* __restrict__ H,
-                                                          int64_t n, int tiles, int splits, int bm) {
-    const int ntile = tiles * (tiles + 1) / 2;
-    const int tile = blockIdx.y;
+                                                          int64_t n, int tiles, int full, int splits, int bm) {
+    const int ntail = tiles * (tiles + 1) / 2 - full;
+    const int tile = full + (int)blockIdx.y;
     int r = tile, ti = 0;
     while (r >= tiles - ti) { r -= tiles - ti; ++ti; }
     const int tj = ti + r;
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(const float* __restric
     if (le >= per_tile) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int sp = 0; sp < splits; ++sp) {
-        const float4 v = *(const float4*)(part + ((int64_t)sp * ntile + tile) * per_tile + le);
+        const float4 v = *(const float4*)(part + ((int64_t)sp * ntail + blockIdx.y) * per_tile + le);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     const int64_t row = (int64_t)ti * bm + le / bm, col = (int64_t)tj * bm + le % bm;
@@ -126,11 +126,11 @@ hipError_t hess_gemm_bf16(const void* X, int64_t n_tok, int64_t n, int64_t ldx, 
     const int vec = (ldx % 8 == 0) && aligned(X, 16);
     Bf16Cols a{(const uint16_t*)X, ldx, n, n_tok, vec, 0};
     Bf16Cols b{(const uint16_t*)X, ldx, n, n_tok, vec, GEMM_THREADS / 2};
-    UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr};
+    UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
-    EpiHess epi{H, part, n, ntile, 128, pl.splits == 1};
+    EpiHess epi{H, part, n, pl.full, ntile - pl.full, 128};
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, Bf16Cols, Bf16Cols, UpperMap, EpiHess>),
-                       dim3(ntile * pl.splits), dim3(GEMM_THREADS), 0, s, a, b, map, epi);
+                       dim3(pl.full + (ntile - pl.full) * pl.splits), dim3(GEMM_THREADS), 0, s, a, b, map, epi);
     return hipGetLastError();
 }
 
@@ -231,10 +231,10 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     DlRows op{{XT, nullptr, nullptr, nullptr}, 1, pl.npad, n, pl.npad, 0};
-    UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr};
+    UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
-    EpiHess epi{H, part, n, ntile, DL_TILE, pl.splits == 1};
-    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(ntile * pl.splits), dim3(GEMM_THREADS),
+    EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
+    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(pl.full + (ntile - pl.full) * pl.splits), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
     return hipGetLastError();
 }
@@ -252,10 +252,10 @@ hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, f
     if (e != hipSuccess) return e;
     DlRows a{{XH, XH, XL, XL}, 4, pl.npad, n, pl.npad, pl.npad};
     DlRows b{{XH, XL, XH, XL}, 4, pl.npad, n, pl.npad, pl.npad};
-    UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr};
+    UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
-    EpiHess epi{H, part, n, ntile, DL_TILE, pl.splits == 1};
-    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(ntile * pl.splits), dim3(GEMM_THREADS),
+    EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
+    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(pl.full + (ntile - pl.full) * pl.splits), dim3(GEMM_THREADS),
                        0, s, a, b, map, epi);
     return hipGetLastError();
 }
@@ -265,11 +265,11 @@ hipError_t hess_gemm(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float
                      hipStream_t s) {
     typedef typename Elem<DT>::T T;
     OpKMajor<DT> op{(const T*)X, ldx, n, n_tok, (int)((ldx % 4 == 0) && aligned(X, 4 * sizeof(T)))};
-    UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr};
+    UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
-    EpiHess epi{H, part, n, ntile, BM, pl.splits == 1};
+    EpiHess epi{H, part, n, pl.full, ntile - pl.full, BM};
     hipLaunchKernelGGL((gemm_f32_kernel<BM, BM, OpKMajor<DT>, OpKMajor<DT>, UpperMap, EpiHess>),
-                       dim3(ntile * pl.splits), dim3(GEMM_THREADS), 0, s, op, op, map, epi);
+                       dim3(pl.full + (ntile - pl.full) * pl.splits), dim3(GEMM_THREADS), 0, s, op, op, map, epi);
     return hipGetLastError();
 }
 
@@ -289,17 +289,41 @@ HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype) {
     p.npad = p.dl ? cdiv(n_tok, 64) * 64 : n_tok;
     const int64_t ksteps = cdiv(p.npad * (p.dl == 4 ? 4 : 1), kq);
     // one 256-wide workgroup per CU (LDS), else >= 4 workgroups per CU of 256
-    const int target = p.dl ? 512 : 1024;
-    int64_t splits = ntile >= target ? 1 : cdiv(target, ntile);
-    const int64_t max_splits = ksteps / 8 > 1 ? ksteps / 8 : 1;   // >= 8 k-tiles per chunk
-    if (splits > max_splits) splits = max_splits;
-    if (splits < 1) splits = 1;
+    // Workgroups resident at once: one 256-wide tile per CU (LDS), else about four per CU.
+    // Whole rounds of tiles run over all tokens; the tiles left over (all of them when there
+    // are fewer than a round) are split into token chunks so that the last round is not a
+    // handful of full-length workgroups on an idle chip.  The split count minimises rounds x
+    // workgroup length (a fixed cost of about four k tiles each), preferring fewer chunks
+    // unless more are at least 2 % faster; a chunk holds at least 8 k tiles.  Splitting
+    // (partial tiles in the workspace, one more pass) must save 3 % of the whole call.
+    const int conc = p.dl ? 256 : 1024;
+    int full = (ntile / conc) * conc;
+    const int tail = ntile - full;
+    const int64_t max_splits = ksteps / 8 > 1 ? ksteps / 8 : 1;
+    int64_t splits = 1;
+    if (tail > 0) {
+        double best = 0.0, whole = 0.0;
+        for (int64_t sp = 1; sp <= max_splits; ++sp) {
+            const double cost = (double)cdiv(tail * sp, conc) * (double)(cdiv(ksteps, sp) + 4);
+            if (sp == 1) whole = cost;
+            if (sp == 1 || cost < 0.98 * best) {
+                best = cost;
+                splits = sp;
+            }
+        }
+        const double rounds_full = (double)(full / conc) * (double)(ksteps + 4);
+        if (rounds_full + best > 0.97 * (rounds_full + whole)) splits = 1;
+    }
     p.kchunk = cdiv(ksteps, splits) * kq;
     p.splits = (int)cdiv(p.npad * (p.dl == 4 ? 4 : 1), p.kchunk);
-    if (p.splits < 1) p.splits = 1;
+    if (p.splits <= 1) {
+        p.splits = 1;
+        full = ntile;                                    // nothing split: every tile adds into H
+    }
+    p.full = full;
     const int copies = p.dl == 4 ? 2 : (p.dl ? 1 : 0);   // transposed X, or its bfloat16 pair
     p.xt_bytes = align_up((size_t)copies * d_in * p.npad * sizeof(uint16_t), 256);
-    const size_t parts = p.splits > 1 ? (size_t)p.splits * ntile * p.bm * p.bm * sizeof(float) : 0;
+    const size_t parts = p.splits > 1 ? (size_t)p.splits * (ntile - full) * p.bm * p.bm * sizeof(float) : 0;
     p.ws_bytes = p.xt_bytes + parts;
     return p;
 }
@@ -321,10 +345,10 @@ hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_i
     }
     if (e != hipSuccess) return e;
     if (pl.splits > 1) {
-        const int ntile = pl.tiles * (pl.tiles + 1) / 2;
+        const int ntail = pl.tiles * (pl.tiles + 1) / 2 - pl.full;
         const unsigned chunks = (unsigned)cdiv((int64_t)pl.bm * pl.bm, 1024);
-        hipLaunchKernelGGL(hess_reduce_kernel, dim3(chunks, (unsigned)ntile), dim3(256), 0, s, part, H, d_in, pl.tiles,
-                           pl.splits, pl.bm);
+        hipLaunchKernelGGL(hess_reduce_kernel, dim3(chunks, (unsigned)ntail), dim3(256), 0, s, part, H, d_in, pl.tiles,
+                           pl.full, pl.splits, pl.bm);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int64_t nb = cdiv(d_in, 32);

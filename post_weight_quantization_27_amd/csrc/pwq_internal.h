@@ -15,7 +15,8 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 struct HessPlan {
     int bm;            // tile edge (64, 128, or 256 on the direct-load engine)
     int tiles;         // tiles per edge
-    int splits;        // token chunks
+    int splits;        // token chunks of the split tiles
+    int full;          // tiles [0, full) run over all tokens; the rest are split
     int64_t kchunk;    // tokens per chunk (multiple of the engine's k tile)
     int dl;            // direct-load engine: 1 = bfloat16 X transposed, 4 = float32 X as a transposed
                        // bfloat16 pair (four products), 0 = register-staged engines

@@ -188,6 +188,23 @@ def test_hessian_bf16_ragged(pwq, n_tok, d_in):
     assert np.array_equal(H, H.T)
 
 
+def test_hessian_bf16_whole_and_split_tiles(pwq):
+    """23 x 23 tiles of 256 give 276 upper tiles: the first 256 run over all tokens and add
+    into H directly, the last 20 run in token chunks added by the reduction.  H starts
+    non-zero (the call accumulates).  Checked on a column sample S that meets every tile:
+    H[S, S] of the full problem is the oracle's Hessian of X[:, S]."""
+    rng = np.random.default_rng(58)
+    n_tok, d_in = 2048, 5888
+    bits = synth.f64_to_bf16_bits(rng.standard_normal((n_tok, d_in)) * np.where(rng.random(d_in) < 0.01, 20.0, 1.0))
+    H = torch.ones((d_in, d_in), dtype=torch.float32, device=DEV)
+    pwq.hessian_accumulate(dev_bf16(bits), H)
+    Hh = host(H)
+    assert np.array_equal(Hh, Hh.T)
+    S = np.sort(rng.choice(d_in, 640, replace=False))
+    want = O.hessian(synth.as_f64(bits, synth.BF16)[:, S])
+    assert rel_frob(Hh[np.ix_(S, S)].astype(np.float64) - 1.0, want) <= 1e-5
+
+
 def test_hessian_deterministic_and_empty(pwq):
     rng = np.random.default_rng(9)
     X = dev(rng.standard_normal((4096, 512)).astype(np.float32))
