@@ -56,6 +56,24 @@ __device__ __forceinline__ int quant_code(float w, float s, float rs, int qmax) 
 }
 
 // code for a possibly-zero scale (all-zero group -> code 0)
+// The same code as quant_code, without branches and with one residual.  k = rint(w * rs)
+// (rs any approximation of 1 / s that leaves w * rs within 1/2 of w / s) is the answer or
+// its neighbour on the side where w * rs lies; h = k +- 1/2 is the half-integer between
+// them.  The exact residual e = w - h s (h s has at most 20 significant bits for
+// qmax <= 127, so the fma's one rounding keeps the sign and the zero of w - h s) says
+// whether w / s lies past h, on it, or short of it, and rint(h + sign(e) / 4) is then the
+// integer past h, the even neighbour (a tie), or k.  Finite inputs give exactly
+// quant_code's result.
+__device__ __forceinline__ int quant_code_sel(float w, float s, float rs, int qmax) {
+    const float t = w * rs;
+    const float k = rintf(t);
+    const float h = k + copysignf(0.5f, t - k);
+    const float e = fmaf(-h, s, w);
+    const float d = e != 0.f ? copysignf(0.25f, e) : 0.f;
+    const float q = rintf(h + d);
+    return (int)__builtin_amdgcn_fmed3f(q, -(float)qmax, (float)qmax);
+}
+
 __device__ __forceinline__ int quant_code_s(float w, float s, int qmax) {
     return s > 0.f ? quant_code(w, s, 1.0f / s, qmax) : 0;
 }

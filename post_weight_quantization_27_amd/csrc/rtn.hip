@@ -6,11 +6,19 @@
 // "Affine Quantization"): s = fp16(fp32(absmax / qmax)), code = round(w / s).
 // Dequant: What = s * code, formed exactly in float32, rounded once to the output type.
 //
-// Both passes are HBM-bound.  RTN: a segment (row, group) is handled by L lanes of a
-// wave (L = g/4 rounded up to a power of two, at most 64), each lane holding 4 consecutive
-// weights per step in registers (float4 / 4 x half loads), so a wave64 covers 256
-// weights per load and several g = 128 groups at once; the group max is an L-lane
-// shuffle reduction.  Codes go out as 4 bytes per lane, INT4 nibbles as 2 bytes per lane.
+// Both passes are HBM-bound, so what matters is bytes in flight per CU.
+// RTN, groups that tile their rows (n % g == 0, 16-byte aligned rows, g * element size a
+// power-of-two multiple of 16 bytes up to 1 KiB): a lane holds one 16-byte vector of its
+// group (8 float16 or 4 float32 weights), LG = g * size / 16 lanes make a group, and each
+// lane issues four independent loads (four sets of 64 / LG groups) before reducing.  The
+// group max is a DPP reduction within rows of 16 lanes, the code a branch-free exact
+// rounding; codes go out as 8 or 4 bytes per lane, INT4 nibbles as 4 or 2.
+// RTN, other shapes (one scale per row, ragged or unaligned groups): a segment (row,
+// group) is handled by L lanes (L = g/4 rounded up to a power of two, at most 64), each
+// holding 4 consecutive weights per step.
+// Dequant (n and g multiples of 8, no g_idx): 8-column chunks, a lane's four chunks 64
+// apart so that loads and stores are contiguous across the wave, all four loads in flight.
+// Grid-stride kernels are launched with as many workgroups as fit on the device at once.
 #include "gemm_f32.h"
 #include "pwq_internal.h"
 
@@ -35,6 +43,8 @@ struct RtnArgs {
     int gl;            // group length in columns (n for one scale per row)
     int L;             // lanes per segment (power of two, <= 64)
     int qmax, vec;
+    uint64_t dmul;     // segment -> row: row = (seg * dmul) >> dsh (exact for seg < 2^31)
+    int dsh;
     const uint16_t* scales_in;
     int8_t* codes;
     uint8_t* packed;
@@ -108,6 +118,107 @@ __global__ __launch_bounds__(256) void rtn_kernel(RtnArgs a) {
     }
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// max over aligned groups of LG lanes: swaps within quads, then the mirror of each 8-lane
+// half-row and of each 16-lane row (DPP, no LDS), then lane shuffles across rows
+template <int LG>
+__device__ __forceinline__ float lanes_max(float v) {
+    if (LG >= 2) v = fmaxf(v, dpp_mov<0xB1>(v));       // quad_perm [1, 0, 3, 2]
+    if (LG >= 4) v = fmaxf(v, dpp_mov<0x4E>(v));       // quad_perm [2, 3, 0, 1]
+    if (LG >= 8) v = fmaxf(v, dpp_mov<0x141>(v));      // row_half_mirror
+    if (LG >= 16) v = fmaxf(v, dpp_mov<0x140>(v));     // row_mirror
+    if (LG >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+    if (LG >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+// Groups that tile their rows, LG lanes per group (LG = g * sizeof(T) / 16).  The host
+// guarantees that W, the codes and the nibbles each span less than 4 GiB, so addresses are
+// 32-bit offsets from the (uniform) base pointers, and that there are fewer than 2^31
+// groups; the scale index of a group is its segment number.
+template <int DT, int LG>
+__global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
+    typedef typename Elem<DT>::T T;
+    constexpr int ES = (int)sizeof(T);
+    constexpr int EPV = 16 / ES;                           // weights per 16-byte vector
+    constexpr int SPW = 64 / LG;                           // groups per wave load
+    constexpr int U = 4;                                   // loads in flight per lane
+    const int lane = threadIdx.x & 63;
+    const int sub = lane / LG, li = lane % LG;
+    const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const char* Wb = (const char*)a.W;
+    const uint32_t ng = (uint32_t)a.ng, nseg = (uint32_t)a.nseg;
+    const uint32_t ldb = (uint32_t)(a.ldw * ES), glb = (uint32_t)(a.gl * ES), n = (uint32_t)a.n;
+    const int64_t iters = cdiv(a.nseg, (int64_t)SPW * U);
+    for (int64_t it = wave_id; it < iters; it += nwaves) {
+        uint4 raw[U];
+        uint32_t rr[U], seg[U];
+        bool live[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t sg0 = (uint32_t)((it * U + u) * SPW) + (uint32_t)sub;
+            live[u] = sg0 < nseg;
+            seg[u] = live[u] ? sg0 : 0u;                   // a dead slot reads group 0
+            rr[u] = (uint32_t)(((uint64_t)seg[u] * a.dmul) >> a.dsh);
+            const uint32_t G = seg[u] - rr[u] * ng;
+            raw[u] = *(const uint4*)(Wb + (rr[u] * ldb + G * glb + (uint32_t)li * 16u));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v[EPV];
+            const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+            if (DT == 0) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(float, w4[k]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    v[2 * k] = f16_bits_to_f32((uint16_t)(w4[k] & 0xffff));
+                    v[2 * k + 1] = f16_bits_to_f32((uint16_t)(w4[k] >> 16));
+                }
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) amax = fmaxf(amax, fabsf(v[k]));
+            amax = lanes_max<LG>(amax);
+            uint16_t sb;
+            if (a.scales_in) sb = live[u] ? a.scales_in[seg[u]] : 0;
+            else sb = scale_bits_from_absmax(amax, a.qmax);
+            if (live[u] && li == 0) a.scales_out[seg[u]] = sb;
+            const float sc = f16_bits_to_f32(sb);
+            const float rs = __builtin_amdgcn_rcpf(sc);       // only a first guess: the fma check is exact
+            int q[EPV];
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) q[k] = sc > 0.f ? quant_code_sel(v[k], sc, rs, a.qmax) : 0;
+            if (!live[u]) continue;
+            const uint32_t c = (seg[u] - rr[u] * ng) * (uint32_t)a.gl + (uint32_t)(li * EPV);
+            if (a.codes) {
+                int8_t* dst = a.codes + (rr[u] * n + c);
+                uint32_t b[EPV / 4];
+#pragma unroll
+                for (int k = 0; k < EPV / 4; ++k)
+                    b[k] = (uint32_t)(q[4 * k] & 0xff) | ((uint32_t)(q[4 * k + 1] & 0xff) << 8) |
+                           ((uint32_t)(q[4 * k + 2] & 0xff) << 16) | ((uint32_t)(q[4 * k + 3] & 0xff) << 24);
+                if (EPV == 8) *(uint2*)dst = make_uint2(b[0], b[EPV / 4 - 1]);
+                else *(uint32_t*)dst = b[0];
+            }
+            if (a.packed) {
+                uint8_t* dst = a.packed + (rr[u] * (n / 2) + c / 2);
+                uint32_t nib = 0;
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) nib |= (uint32_t)(q[k] + 8) << (4 * k);
+                if (EPV == 8) *(uint32_t*)dst = nib;
+                else *(uint16_t*)dst = (uint16_t)nib;
+            }
+        }
+    }
+}
+
 struct DqArgs {
     const uint8_t* packed;
     const int8_t* codes;
@@ -136,6 +247,70 @@ __device__ __forceinline__ void dq_store(void* out, int64_t i, float v) {
     if (OT == 0) ((float*)out)[i] = v;
     else if (OT == 1) ((uint16_t*)out)[i] = f32_to_f16_bits(v);
     else ((uint16_t*)out)[i] = f32_to_bf16_bits(v);
+}
+
+// n % 8 == 0, one group per 8-column chunk (g == 0 or g % 8 == 0, no g_idx), aligned
+// buffers.  Chunks of 8 columns are numbered row-major; a wave takes 256 consecutive chunks
+// per pass, lane l the chunks 64 j + l (j < 4): each load instruction reads 4 (nibbles) or 8
+// (codes) contiguous bytes per lane, each store writes 16 or 32 contiguous bytes per lane,
+// and the four loads of a lane are in flight together.
+template <int OT>
+__global__ __launch_bounds__(256) void dequant_vec_kernel(DqArgs a) {
+    constexpr int U = 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t cpr = a.n / 8;
+    const int64_t total = a.m * cpr;
+    const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t base = wave_id * 64 * U; base < total; base += nwaves * 64 * U) {
+        uint2 w[U];
+        float sc[U];
+        int64_t r[U], c0[U];
+        bool live[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = base + 64 * u + lane;
+            live[u] = t < total;
+            const int64_t tt = live[u] ? t : 0;
+            r[u] = tt / cpr;
+            c0[u] = (tt - r[u] * cpr) * 8;
+            if (a.packed) w[u] = make_uint2(*(const uint32_t*)(a.packed + r[u] * (a.n / 2) + c0[u] / 2), 0u);
+            else w[u] = *(const uint2*)(a.codes + r[u] * a.n + c0[u]);
+            sc[u] = f16_bits_to_f32(a.scales[r[u] * a.ng + (a.g == 0 ? 0 : c0[u] / a.g)]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!live[u]) continue;
+            int q[8];
+            if (a.packed) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) q[k] = (int)((w[u].x >> (4 * k)) & 15) - 8;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    q[k] = (int8_t)((w[u].x >> (8 * k)) & 0xff);
+                    q[4 + k] = (int8_t)((w[u].y >> (8 * k)) & 0xff);
+                }
+            }
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = sc[u] * (float)q[k];     // exact: 11 x 4 significant bits
+            if (OT == 0) {
+                float4* o = (float4*)((float*)a.out + r[u] * a.n + c0[u]);
+                o[0] = make_float4(v[0], v[1], v[2], v[3]);
+                o[1] = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
+                uint32_t h[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint16_t lo = OT == 1 ? f32_to_f16_bits(v[2 * k]) : f32_to_bf16_bits(v[2 * k]);
+                    const uint16_t hi = OT == 1 ? f32_to_f16_bits(v[2 * k + 1]) : f32_to_bf16_bits(v[2 * k + 1]);
+                    h[k] = (uint32_t)lo | ((uint32_t)hi << 16);
+                }
+                *(uint4*)((uint16_t*)a.out + r[u] * a.n + c0[u]) = make_uint4(h[0], h[1], h[2], h[3]);
+            }
+        }
+    }
 }
 
 template <int OT>
@@ -186,6 +361,21 @@ __global__ __launch_bounds__(256) void dequant_kernel(DqArgs a) {
     }
 }
 
+// Workgroups of 256 that fit on the device at once for kernel K (all CUs at K's occupancy),
+// at most `want`: grid-stride kernels launched with this many take one round.  Both
+// figures are taken once per kernel.
+template <auto K>
+int64_t resident_blocks(int64_t want) {
+    static const int64_t cap = [] {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)K, 256, 0) != hipSuccess || per <= 0) per = 1;
+        return (int64_t)cus * per;
+    }();
+    return want < cap ? (want > 0 ? want : 1) : cap;
+}
+
 }  // namespace
 
 hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, int bits, int group_size,
@@ -204,6 +394,41 @@ hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
     a.vec = (ldw % 4 == 0) && (a.gl % 4 == 0) && aligned(W, 4 * es) && (!codes || aligned(codes, 4)) &&
             (!packed || aligned(packed, 2));
     a.scales_in = scales_in; a.codes = codes; a.packed = packed; a.scales_out = scales_out;
+    // group path: whole groups per row, 16-byte vectors, LG a power of two <= 64
+    const int64_t gbytes = group_size * (int64_t)es;
+    int lg = (int)(gbytes / 16);
+    const bool pow2 = lg > 0 && (lg & (lg - 1)) == 0;
+    const int epv = w_dtype == 0 ? 4 : 8;
+    if (group_size > 0 && n % group_size == 0 && gbytes % 16 == 0 && pow2 && lg <= 64 && (ldw % epv) == 0 &&
+        aligned(W, 16) && (!codes || (n % epv == 0 && aligned(codes, epv))) && (!packed || aligned(packed, epv / 2)) &&
+        a.nseg < ((int64_t)1 << 31) && m * ldw * (int64_t)es < ((int64_t)1 << 32) && m * n < ((int64_t)1 << 32)) {
+        // row = floor(seg / ng) as (seg * dmul) >> (31 + l), dmul = ceil(2^(31 + l) / ng),
+        // l = ceil(log2 ng): exact for every seg < 2^31 (division by an invariant integer)
+        int l = 0;
+        while (((int64_t)1 << l) < a.ng) ++l;
+        a.dsh = 31 + l;
+        a.dmul = (uint64_t)((((unsigned __int128)1 << a.dsh) + (unsigned __int128)a.ng - 1) / (unsigned __int128)a.ng);
+        const int64_t waves = cdiv(a.nseg, (int64_t)(64 / lg) * 4);
+        const int64_t want = cdiv(waves, 4);
+#define PWQ_RTN_G(DT, LGV)                                                                                  \
+        hipLaunchKernelGGL((rtn_group_kernel<DT, LGV>), dim3((unsigned)resident_blocks<rtn_group_kernel<DT, LGV>>(want)), \
+                           dim3(256), 0, s, a)
+#define PWQ_RTN_LG(DT)                                      \
+        switch (lg) {                                       \
+        case 1: PWQ_RTN_G(DT, 1); break;                    \
+        case 2: PWQ_RTN_G(DT, 2); break;                    \
+        case 4: PWQ_RTN_G(DT, 4); break;                    \
+        case 8: PWQ_RTN_G(DT, 8); break;                    \
+        case 16: PWQ_RTN_G(DT, 16); break;                  \
+        case 32: PWQ_RTN_G(DT, 32); break;                  \
+        default: PWQ_RTN_G(DT, 64); break;                  \
+        }
+        if (w_dtype == 0) { PWQ_RTN_LG(0) }
+        else { PWQ_RTN_LG(1) }
+#undef PWQ_RTN_LG
+#undef PWQ_RTN_G
+        return hipGetLastError();
+    }
     const int64_t waves = cdiv(a.nseg, 64 / L);
     int64_t blocks = cdiv(waves, 4);
     if (blocks > 65536) blocks = 65536;
@@ -225,6 +450,16 @@ hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint
     const size_t os = out_dtype == 0 ? 4 : 2;
     a.vec = (n % 8 == 0) && (group_size == 0 || (group_size % 8 == 0 && !g_idx)) && aligned(out, 8 * os) &&
             (!packed || aligned(packed, 4)) && (!codes || aligned(codes, 8));
+    if (a.vec) {
+        const int64_t want = cdiv(m * a.chunks, 4 * 256);
+        if (out_dtype == 0)
+            hipLaunchKernelGGL(dequant_vec_kernel<0>, dim3((unsigned)resident_blocks<dequant_vec_kernel<0>>(want)), dim3(256), 0, s, a);
+        else if (out_dtype == 1)
+            hipLaunchKernelGGL(dequant_vec_kernel<1>, dim3((unsigned)resident_blocks<dequant_vec_kernel<1>>(want)), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(dequant_vec_kernel<2>, dim3((unsigned)resident_blocks<dequant_vec_kernel<2>>(want)), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     int64_t blocks = cdiv(m * a.chunks, 256);
     if (blocks > 65536) blocks = 65536;
     if (out_dtype == 0) hipLaunchKernelGGL(dequant_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a);

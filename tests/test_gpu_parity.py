@@ -68,6 +68,14 @@ RTN_CASES = [
     (768, 3072, 128, np.float32),
     (3072, 768, 0, np.float32),
     (50257, 768, 0, np.float32),      # lm_head shape, one scale per row
+    # groups that tile their rows, by lanes per group (g x element size / 16 bytes)
+    (9, 64, 8, np.float16),           # 1 lane
+    (12, 128, 16, np.float16),        # 2 lanes
+    (7, 192, 8, np.float32),          # 2 lanes
+    (20, 512, 64, np.float16),        # 8 lanes
+    (6, 1024, 512, np.float16),       # 64 lanes
+    (10, 512, 256, np.float32),       # 64 lanes
+    (4099, 1024, 128, np.float16),    # a partial last load set
 ]
 
 
@@ -110,7 +118,8 @@ def test_rtn_strided_rows(pwq):
 
 # =============================================================================== dequant
 @pytest.mark.parametrize("m,n,g,src", [(64, 256, 128, "packed"), (64, 256, 0, "codes"), (21, 250, 10, "packed"),
-                                       (30, 96, 32, "codes"), (768, 3072, 128, "packed")])
+                                       (30, 96, 32, "codes"), (768, 3072, 128, "packed"), (33, 96, 0, "packed"),
+                                       (40, 512, 32, "packed"), (3, 64, 64, "packed")])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16, torch.bfloat16])
 def test_dequant_exact(pwq, m, n, g, src, out_dtype):
     rng = np.random.default_rng(3)
