@@ -16,7 +16,10 @@
 //   finalize : U_{k, >k} = -Z_kk R_{k, >k}          (from V U = I: V_kk U_kj = -sum_l V_kl U_lj)
 //   syrk     : A_{<k, <k} -= P P^T                                    (upper tiles)
 //   push     : R_{<k, >=k} += P U_{k, >=k}   (overwrite for the block column k itself)
-// trsm + finalize share one launch, syrk + push another: three launches per block.
+// trsm + finalize share one launch, syrk + push another: three launches per block.  Below
+// n = 4096 the diagonal factor of block k - 1 joins block k's syrk + push launch (one
+// workgroup applies its share of the update itself): two launches per block, and the
+// serial factor overlaps the update.  From n = 4096 on, updates are batched per super-block.
 // Every kernel reads `info` first and does nothing once a pivot has failed.
 #include "gemm_f32.h"
 #include "pwq_internal.h"
@@ -96,12 +99,17 @@ __device__ __forceinline__ f32x16 mfma_tile_ab(const float (*MA)[LP], int ra, in
 }
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
-__global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, int64_t n, int64_t k0, int bs,
-                                                        int32_t* __restrict__ info) {
-    if (*info) return;
-    __shared__ float A[CHOL_NB][LP];
-    __shared__ float Z[CHOL_NB][LP];
-    __shared__ int fail;                                 // failed pivot + 1 of the current panel
+constexpr int DIAG_FLOATS = 2 * CHOL_NB * LP + 4;       // A, Z, the failed-pivot word
+
+// The diagonal block [k0, k0 + bs) in one workgroup, in the LDS buffer smem (DIAG_FLOATS
+// floats).  With Pu (the pending panel rows of the block: Pu[i * pld + c], c < kdepth), the
+// block first takes that panel's update A -= Pu Pu^T, which the caller's launch leaves out.
+__device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int64_t k0, int bs,
+                                           int32_t* __restrict__ info, float* smem, const float* __restrict__ Pu,
+                                           int pld, int kdepth) {
+    float (*A)[LP] = (float (*)[LP])smem;
+    float (*Z)[LP] = (float (*)[LP])(smem + CHOL_NB * LP);
+    int& fail = *(int*)(smem + 2 * CHOL_NB * LP);       // failed pivot + 1 of the current panel
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // ---------------- load: thread = (row, 64-column half), all loads in flight
@@ -130,6 +138,35 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
         }
     }
     __syncthreads();
+
+    // ---------------- pending update: Z <- panel rows, A -= Z Z^T on the ten upper 32 x 32
+    // tiles (MFMA, k = 128, zero columns past kdepth), then Z cleared again
+    if (Pu) {
+        {
+            const int i = tid >> 1, c0 = 64 * (tid & 1);
+            const float* src = Pu + (int64_t)i * pld + c0;
+#pragma unroll 16
+            for (int q = 0; q < 64; ++q) Z[i][c0 + q] = c0 + q < kdepth ? src[q] : 0.f;
+        }
+        __syncthreads();
+        for (int t = wave; t < 10; t += 4) {
+            const int ti = t < 4 ? 0 : (t < 7 ? 1 : (t < 9 ? 2 : 3));
+            const int tj = ti + t - (ti == 0 ? 0 : (ti == 1 ? 4 : (ti == 2 ? 7 : 9)));
+            const f32x16 acc = mfma_tile_abT(Z, 32 * ti, 32 * tj, 0, CHOL_NB, lane);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * ti + acc_row(v, lane), c = 32 * tj + (lane & 31);
+                if (c >= r) A[r][c] -= acc[v];
+            }
+        }
+        __syncthreads();
+        {
+            const int i = tid >> 1, c0 = 64 * (tid & 1);
+#pragma unroll 16
+            for (int q = 0; q < 64; ++q) Z[i][c0 + q] = 0.f;
+        }
+        __syncthreads();
+    }
 
     // ---------------- factor: 32-column panels from the right.  Wave 0 factors a panel in
     // registers (lane l holds rows l and l + 64 of the panel's 32 columns): the pivot and the
@@ -276,6 +313,13 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
     }
 }
 
+__global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, int64_t n, int64_t k0, int bs,
+                                                        int32_t* __restrict__ info) {
+    if (*info) return;
+    __shared__ __attribute__((aligned(16))) float smem[DIAG_FLOATS];
+    diag_block(U, n, k0, bs, info, smem, nullptr, 0, 0);
+}
+
 // ------------------------------------------------------------------ epilogues
 struct EpiStore {                 // out[row][col] = alpha * acc
     float* out;
@@ -403,6 +447,48 @@ hipError_t launch_near(float* U, const float* Pk, int pld, int64_t n, int64_t s0
     return hipGetLastError();
 }
 
+// One launch for the update of block k (syrk + push tiles, workgroups 1 ..) and the
+// factor of the next diagonal block [kd0, kd0 + NB) (workgroup 0): that block needs only
+// its own share of the update, which workgroup 0 applies itself (the syrk tiles covering it
+// are left out of the grid), so the serial diagonal factor overlaps the rest of the update.
+template <class TA, class TB>
+__global__ __launch_bounds__(GEMM_THREADS) void chol_update_diag_kernel(TA a, TB b, int n1, int32_t* __restrict__ info,
+                                                                        float* __restrict__ U, int64_t n, int64_t kd0,
+                                                                        const float* __restrict__ Pu, int pld,
+                                                                        int kdepth) {
+    if (*info) return;
+    constexpr int L0 = TA::LDS > TB::LDS ? TA::LDS : TB::LDS;
+    constexpr int L = L0 > DIAG_FLOATS ? L0 : DIAG_FLOATS;
+    __shared__ __attribute__((aligned(16))) float lds[L];
+    const int bid = (int)blockIdx.x;
+    if (bid == 0) diag_block(U, n, kd0, CHOL_NB, info, lds, Pu, pld, kdepth);
+    else if (bid - 1 < n1) a.run(bid - 1, lds);
+    else b.run(bid - 1 - n1, lds);
+}
+
+// syrk + push of block [k0, k0 + bs) (no super-blocks: depth bs, panel P = V[0:k0, block])
+// together with the factor of the diagonal block [k0 - NB, k0)
+template <int T>
+hipError_t launch_update_diag(float* U, const float* P, int pld, int64_t n, int64_t k0, int bs, int32_t* info, int vu,
+                              hipStream_t s) {
+    SyrkTask<T> sy{};
+    sy.la = OpMMajor<0>{P, pld, k0, bs, 1};
+    sy.lb = sy.la;
+    sy.map = UpperMap{k0, bs, (int)cdiv(k0, T), 1, cdiv(bs, GEMM_BK) * GEMM_BK, nullptr};
+    sy.epi = EpiSyrk{U, n, k0};
+    PushTask<T> pu{};
+    pu.la = OpMMajor<0>{P, pld, k0, bs, 1};
+    pu.lb = OpKMajor<0>{U + k0 * n + k0, n, n - k0, bs, vu && (k0 % 4 == 0)};
+    pu.map = rect(T, T, k0, n - k0, bs);
+    pu.epi = EpiPush{U + k0, n, k0, n - k0, bs};
+    // the last upper tiles in map order are the ones inside [k0 - NB, k0)^2: one of 128, three of 64
+    const int n1 = ntiles(sy.map) - (T == 128 ? 1 : 3);
+    const int n2 = ntiles(pu.map);
+    hipLaunchKernelGGL((chol_update_diag_kernel<SyrkTask<T>, PushTask<T>>), dim3(1 + n1 + n2), dim3(GEMM_THREADS), 0, s,
+                       sy, pu, n1, info, U, n, k0 - CHOL_NB, P + (k0 - CHOL_NB) * pld, pld, bs);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t chol_ws_bytes(int64_t n) { return (size_t)n * (chol_sb(n) * CHOL_NB) * sizeof(float); }
@@ -425,6 +511,41 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
     const int sb = chol_sb(n);
     const int pld = sb * CHOL_NB;
     const int vu = vec_ok(U, n);
+    if (sb == 1) {
+        // two launches per block: trsm + finalize of block k, then its syrk + push together
+        // with the factor of block k - 1
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, U, n, (int64_t)(nt - 1) * CHOL_NB,
+                           (int)(n - (int64_t)(nt - 1) * CHOL_NB), info);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        for (int kb = nt - 1; kb >= 0; --kb) {
+            const int64_t k0 = (int64_t)kb * CHOL_NB;
+            const int bs = (int)((n - k0) < CHOL_NB ? (n - k0) : CHOL_NB);
+            const int64_t r = n - k0 - bs;
+            TrsmTask tt{};
+            tt.la = OpMMajor<0>{U + k0, n, k0, bs, vu && (k0 % 4 == 0)};
+            tt.lb = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
+            tt.map = rect(64, 64, k0, bs, bs);
+            tt.epi = EpiStore{P, pld, k0, bs, 1.f};
+            FinalizeTask ft{};
+            ft.la = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
+            ft.lb = OpKMajor<0>{U + k0 * n + k0 + bs, n, r, bs, vu && ((k0 + bs) % 4 == 0)};
+            ft.map = rect(128, 64, bs, r, bs);
+            ft.epi = EpiStore{U + k0 * n + k0 + bs, n, bs, r, -1.f};
+            const int n1 = k0 > 0 ? ntiles(tt.map) : 0;
+            const int n2 = r > 0 ? ntiles(ft.map) : 0;
+            if (n1 + n2 > 0) {
+                hipLaunchKernelGGL((gemm_f32_dual_kernel<TrsmTask, FinalizeTask>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s,
+                                   tt, ft, n1, info);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
+            if (k0 == 0) break;
+            const int64_t big = cdiv(k0, 128) * cdiv(n, 128);
+            e = big >= 512 ? launch_update_diag<128>(U, P, pld, n, k0, bs, info, vu, s)
+                           : launch_update_diag<64>(U, P, pld, n, k0, bs, info, vu, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     for (int kb = nt - 1; kb >= 0; --kb) {
         const int64_t k0 = (int64_t)kb * CHOL_NB;
         const int bs = (int)((n - k0) < CHOL_NB ? (n - k0) : CHOL_NB);
