@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--layers", default="", help="comma-separated layer names (default: all)")
     ap.add_argument("--act-order", action="store_true")
     ap.add_argument("--streams", type=int, default=1, help="1: one stream per layer (default), 0: all on one stream")
+    ap.add_argument("--stagger", type=int, default=1,
+                    help="1: the layer with the longest chain starts alone and the others once its Hessian is "
+                         "formed (default), 0: all layers start together")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", default="", help="layers the oracle baseline runs (default: all)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -67,8 +70,9 @@ class Layer:
         del X, W
 
 
-def run_step(L, pwq, timers=None):
-    """One pass of the whole path over one layer.  timers: dict name -> list of (start, end) events."""
+def run_step(L, pwq, timers=None, after_hessian=None):
+    """One pass of the whole path over one layer.  timers: dict name -> list of (start, end) events;
+    after_hessian: called once the Hessian's kernels are enqueued."""
     import torch
     s = L.spec
 
@@ -88,6 +92,8 @@ def run_step(L, pwq, timers=None):
         timers[name][-1][1] = e1
 
     k = t("hessian_accumulate"); L.H.zero_(); pwq.hessian_accumulate(L.X, L.H); done(k)
+    if after_hessian is not None:
+        after_hessian()
     k = t("hessian_damp"); pwq.hessian_damp(L.H, s.damp); done(k)
     perm = None
     if L.act:
@@ -228,12 +234,22 @@ def main():
     # the layer with the longest serial chain (largest d_in: most factor blocks) goes first
     order = sorted(range(len(layers)), key=lambda i: -layers[i].spec.d_in)
 
+    # The step is as long as its longest chain (the factor of the widest layer is a serial
+    # sequence of small launches).  With staggering, that layer's Hessian runs alone, and
+    # the other layers start once it is formed, so their large contractions overlap the
+    # widest layer's latency-bound factor instead of its Hessian.
+    stagger = bool(a.stagger) and bool(a.streams) and len(layers) > 1
+    first_done = torch.cuda.Event()
+
     def step(timers=None):
-        for i in order:
+        for pos, i in enumerate(order):
             L, st = layers[i], streams[i]
             st.wait_stream(main)
+            if stagger and pos > 0:
+                st.wait_event(first_done)
             with torch.cuda.stream(st):
-                run_step(L, pwq, None if timers is None else timers[i])
+                hook = (lambda: first_done.record()) if (stagger and pos == 0) else None
+                run_step(L, pwq, None if timers is None else timers[i], after_hessian=hook)
         for st in streams:
             main.wait_stream(st)
 
@@ -303,7 +319,7 @@ def main():
         "config": {"workload": a.workload, "layers": [f"{s.name}:{s.d_in}->{s.d_out}" for s in specs],
                    "n_tok": specs[0].n_tok, "bits": specs[0].bits, "group_size": specs[0].group_size,
                    "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order),
-                   "layer_streams": bool(a.streams)},
+                   "layer_streams": bool(a.streams), "stagger": stagger},
         "roofline": roof,
         "xtx_mfma_util": xtx,
         "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
