@@ -120,6 +120,8 @@ struct BlockArgs {
     uint8_t* packed;         // ld n/2 (nullable; only without act-order)
     float* err;              // this block's columns of the super-block's Err (m x err_ld)
     int err_ld;
+    int pend;                // row kernels: columns of the super-block before this block, whose
+    const float* err_sb;     // update the kernel applies itself (errors at err_sb, ld err_ld)
 };
 
 // The panel's diagonal block of U (zero outside bw x bw), read as float4 rows with every
@@ -131,23 +133,27 @@ struct UBlock {
     static constexpr int Q = (N4 + NT - 1) / NT;
     float4 v[Q];
     __device__ __forceinline__ static bool has(int tid, int q) { return N4 % NT == 0 || tid + q * NT < N4; }
-    __device__ __forceinline__ void load(const float* U, int64_t n, int64_t b0, int bw, int tid) {
-        const bool vec = (bw == PW) && (n % 4 == 0);
+    // rows [r0, r0 + PW) x columns [c0, c0 + PW) of U, zero outside rv rows and cv columns
+    __device__ __forceinline__ void load_rect(const float* U, int64_t n, int64_t r0, int64_t c0, int rv, int cv, int tid) {
+        const bool vec = (rv == PW) && (cv == PW) && (n % 4 == 0) && (c0 % 4 == 0);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             if (!has(tid, q)) break;
             const int e = 4 * (tid + q * NT);
             const int j = e / PW, c = e % PW;
-            const float* src = U + (b0 + j) * n + b0 + c;
+            const float* src = U + (r0 + j) * n + c0 + c;
             if (vec) {
                 v[q] = *(const float4*)src;
             } else {
                 float t[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) t[k] = (j < bw && c + k < bw) ? src[k] : 0.f;
+                for (int k = 0; k < 4; ++k) t[k] = (j < rv && c + k < cv) ? src[k] : 0.f;
                 v[q] = make_float4(t[0], t[1], t[2], t[3]);
             }
         }
+    }
+    __device__ __forceinline__ void load(const float* U, int64_t n, int64_t b0, int bw, int tid) {
+        load_rect(U, n, b0, b0, bw, bw, tid);
     }
 };
 
@@ -364,16 +370,70 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
     __shared__ float esh[NWV][PW];
     __shared__ int8_t qsh[NWV][PW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r = (int64_t)blockIdx.x * NWV + wave;
+    const bool live = r < a.m;                       // uniform per wave
+    const bool lane_in = lane < PW;                  // PW = 32: lanes 32..63 hold no column
+    float w[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+        w[k] = (live && lane + 64 * k < a.bw && lane_in) ? a.Wf[r * a.n + a.b0 + 64 * k + lane] : 0.f;
 
-    {
-        UBlock<PW, NT> ub;
-        ub.load(a.U, a.n, a.b0, a.bw, tid);
+    // the update still owed by this block's columns from the earlier blocks of its
+    // super-block: w -= Err[r, s0 .. b0) U[s0 .. b0, block], one block's U rows at a time
+    // staged in Ub (each block's sum is formed on its own and taken off once, as a product
+    // per block would).  The next slice, and finally the diagonal block, is read into
+    // registers while the current one is used; the row's errors are read before that, so
+    // waiting for them does not wait for the prefetch.
+    UBlock<PW, NT> ub;
+    if (a.pend > 0) ub.load_rect(a.U, a.n, a.b0 - a.pend, a.b0, PW, a.bw, tid);
+    else ub.load(a.U, a.n, a.b0, a.bw, tid);
+    for (int c0 = 0; c0 < a.pend; c0 += PW) {
+        __syncthreads();                             // the previous slice is consumed
 #pragma unroll
         for (int q = 0; q < UBlock<PW, NT>::Q; ++q) {
             if (!UBlock<PW, NT>::has(tid, q)) break;
             const int e = 4 * (tid + q * NT);
             *(float4*)&Ub[e / PW][e % PW] = ub.v[q];
         }
+        __syncthreads();
+        float ev[NS], acc[NS];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            ev[k] = (live && lane_in) ? a.err_sb[r * a.err_ld + c0 + 64 * k + lane] : 0.f;
+            acc[k] = 0.f;
+        }
+        if (c0 + PW < a.pend) ub.load_rect(a.U, a.n, a.b0 - a.pend + c0 + PW, a.b0, PW, a.bw, tid);
+        else ub.load(a.U, a.n, a.b0, a.bw, tid);
+        if (live) {
+            // sixteen rows' reads go out together, then their FMAs (same summation order)
+#pragma unroll
+            for (int j0 = 0; j0 < PW; j0 += 16) {
+                float uu[16][NS];
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj)
+#pragma unroll
+                    for (int k = 0; k < NS; ++k) uu[jj][k] = lane_in ? Ub[j0 + jj][64 * k + lane] : 0.f;
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const int j = j0 + jj;
+                    const float ej =
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ev[j >> 6]), j & 63));
+#pragma unroll
+                    for (int k = 0; k < NS; ++k) acc[k] = fmaf(ej, uu[jj][k], acc[k]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int k = 0; k < NS; ++k) w[k] -= acc[k];
+        }
+    }
+    if (a.pend > 0) __syncthreads();                 // the last slice is consumed before Ub is reused
+#pragma unroll
+    for (int q = 0; q < UBlock<PW, NT>::Q; ++q) {
+        if (!UBlock<PW, NT>::has(tid, q)) break;
+        const int e = 4 * (tid + q * NT);
+        *(float4*)&Ub[e / PW][e % PW] = ub.v[q];
     }
     float dreg[NS];
 #pragma unroll
@@ -383,13 +443,8 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
     }
     __syncthreads();
 
-    const int64_t r = (int64_t)blockIdx.x * NWV + wave;
-    const bool live = r < a.m;                       // uniform per wave
     if (live) {
         const float* wrow = a.Wf + r * a.n;
-        float w[NS];
-#pragma unroll
-        for (int k = 0; k < NS; ++k) w[k] = (lane + 64 * k < a.bw && lane + 64 * k < PW) ? wrow[a.b0 + 64 * k + lane] : 0.f;
         const int g = a.group_size;
         float s = 0.f;
         if (g == 0) s = f16_bits_to_f32(a.scales[r]);
@@ -398,7 +453,6 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
         float rs = uniform_f(s > 0.f ? 1.0f / s : 0.f);
         const float qmf = (float)a.qmax;
 
-        const bool lane_in = lane < PW;              // PW = 32: lanes 32..63 hold no column
         float u[NS], un[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) u[k] = lane_in ? Ub[0][64 * k + lane] : 0.f;
@@ -438,12 +492,9 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
             // wave-uniform), so the rare exact-rounding branch is a uniform one
             const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w[j >> 6]), j & 63));
             const float dj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dreg[j >> 6]), j & 63));
-            const float t = wj * rs;
-            const float kf = rintf(t);
-            float qf = fminf(fmaxf(kf, -qmf), qmf);
-            // |t - w/s| < 2e-6 here, so a distance below 0.49 from kf already decides the
-            // nearest integer; only quotients near a half take the exact residual test
-            if (fabsf(t - kf) > 0.49f) qf = (float)quant_code(wj, s, rs, a.qmax);
+            // branch-free exact rounding: no uniform branch (and no refilled instruction
+            // buffer) on the column-to-column chain
+            const float qf = s > 0.f ? quant_code_self(wj, s, rs, qmf) : 0.f;
             const float e = (wj - s * qf) * dj;
             // e and the code are wave-uniform: every lane stores the same value to the same
             // LDS word (no lane select), and each lane reads its own columns back at the end
@@ -624,6 +675,10 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
             a.gstart0 = (b0 % group_size) == 0;
             a.gbase = b0 / group_size;
         }
+        // row kernels take the update owed from the earlier blocks of the super-block
+        // themselves; the quad kernel's block receives it from a product after each block
+        a.pend = quad ? 0 : (int)(b0 - s0);
+        a.err_sb = err;
         if (quad) {
             if (block_size == 128) hipLaunchKernelGGL((gptq_block_kernel<128, 8>), dim3(nblk), dim3(512), 0, s, a);
             else if (block_size == 64) hipLaunchKernelGGL((gptq_block_kernel<64, 8>), dim3(nblk), dim3(512), 0, s, a);
@@ -640,7 +695,7 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int64_t b1 = b0 + bw;
         if (b1 < s1) {                     // the rest of the super-block, from this block's errors
-            if ((e = update(Wf, err + (b0 - s0), lz, U, info, m, n, b0, bw, b1, s1, s)) != hipSuccess) return e;
+            if (quad && (e = update(Wf, err + (b0 - s0), lz, U, info, m, n, b0, bw, b1, s1, s)) != hipSuccess) return e;
         } else if (s1 < n) {               // super-block done: every column past it, depth s1 - s0
             if ((e = update(Wf, err, lz, U, info, m, n, s0, (int)(s1 - s0), s1, n, s)) != hipSuccess) return e;
         }

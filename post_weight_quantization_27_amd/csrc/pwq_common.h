@@ -63,15 +63,18 @@ __device__ __forceinline__ int quant_code(float w, float s, float rs, int qmax) 
 // qmax <= 127, so the fma's one rounding keeps the sign and the zero of w - h s) says
 // whether w / s lies past h, on it, or short of it, and rint(h + sign(e) / 4) is then the
 // integer past h, the even neighbour (a tie), or k.  Finite inputs give exactly
-// quant_code's result.
-__device__ __forceinline__ int quant_code_sel(float w, float s, float rs, int qmax) {
+// quant_code's result (s > 0; the callers give s = 0 the code 0).  quant_code_self returns
+// the code as a float.
+__device__ __forceinline__ float quant_code_self(float w, float s, float rs, float qmaxf) {
     const float t = w * rs;
     const float k = rintf(t);
     const float h = k + copysignf(0.5f, t - k);
     const float e = fmaf(-h, s, w);
     const float d = e != 0.f ? copysignf(0.25f, e) : 0.f;
-    const float q = rintf(h + d);
-    return (int)__builtin_amdgcn_fmed3f(q, -(float)qmax, (float)qmax);
+    return __builtin_amdgcn_fmed3f(rintf(h + d), -qmaxf, qmaxf);
+}
+__device__ __forceinline__ int quant_code_sel(float w, float s, float rs, int qmax) {
+    return (int)quant_code_self(w, s, rs, (float)qmax);
 }
 
 __device__ __forceinline__ int quant_code_s(float w, float s, int qmax) {
