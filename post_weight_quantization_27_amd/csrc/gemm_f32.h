@@ -174,29 +174,75 @@ struct RectMap {
 };
 
 // Upper-triangular tile pairs (ti <= tj) of an N x N output, times `splits` k chunks.
+// Position L of the upper tiles in bands of G tile-rows: within a band, columns left to
+// right and the band's rows (at most tj) fastest.  Consecutive positions then share a few
+// operand blocks of both kinds.
+__device__ __forceinline__ void upper_band_tile(int L, int tiles, int G, int& ti, int& tj) {
+    int r0 = 0;
+    while (r0 < tiles) {
+        const int R = tiles - r0 < G ? tiles - r0 : G;
+        const int head = R * (R + 1) / 2;                // columns r0 .. r0 + R - 1: 1 .. R rows
+        const int cnt = head + R * (tiles - r0 - R);
+        if (L < cnt) {
+            if (L < head) {
+                int c = 0;
+                while ((c + 1) * (c + 2) / 2 <= L) ++c;
+                ti = r0 + (L - c * (c + 1) / 2);
+                tj = r0 + c;
+            } else {
+                const int p = L - head;
+                tj = r0 + R + p / R;
+                ti = r0 + p % R;
+            }
+            return;
+        }
+        L -= cnt;
+        r0 += R;
+    }
+    ti = tj = 0;
+}
+
 // Upper-triangle tiles (ti <= tj) of an N x N output.  Workgroups [0, full) take tiles
 // [0, full) over the whole k range (t.split = -1); the tiles after them are split into
 // `splits` k chunks of kchunk, workgroup full + s * (ntile - full) + j taking chunk s of tile
 // full + j.  With full = 0 every tile is split.
+// xcd (only with full == ntile, nothing split): workgroup b runs on XCD b % 8, which takes a
+// contiguous run of the tiles in bands of four rows (upper_band_tile), so the tiles in flight
+// on one XCD share a few operand blocks in its L2; the grid is padded to a multiple of 8 and
+// the padding workgroups have no tile.
 struct UpperMap {
     int64_t N, K;
     int tiles, splits;
     int64_t kchunk;
     const int32_t* guard;
     int full;
+    int xcd;
     __device__ __forceinline__ bool get(int bid, int BM, int BN, Tile& t) const {
         const int ntile = tiles * (tiles + 1) / 2;
-        if (bid < full) {
+        int ti = 0, tj = 0;
+        if (xcd) {
+            const int per = (ntile + 7) / 8;
+            const int L = (bid % 8) * per + bid / 8;
             t.split = -1;
-            t.tile = bid;
+            t.tile = L;
+            if (L >= ntile) {
+                t.kbeg = t.kend = 0;
+                return false;
+            }
+            upper_band_tile(L, tiles, 4, ti, tj);
         } else {
-            const int nt = ntile - full, b = bid - full;
-            t.split = b / nt;
-            t.tile = full + b % nt;
+            if (bid < full) {
+                t.split = -1;
+                t.tile = bid;
+            } else {
+                const int nt = ntile - full, b = bid - full;
+                t.split = b / nt;
+                t.tile = full + b % nt;
+            }
+            int r = t.tile;
+            while (r >= tiles - ti) { r -= tiles - ti; ++ti; }
+            tj = ti + r;
         }
-        int r = t.tile, ti = 0;
-        while (r >= tiles - ti) { r -= tiles - ti; ++ti; }
-        int tj = ti + r;
         t.m0 = (int64_t)ti * BM;
         t.n0 = (int64_t)tj * BN;
         if (t.split < 0) {

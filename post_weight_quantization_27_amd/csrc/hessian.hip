@@ -231,10 +231,13 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     DlRows op{{XT, nullptr, nullptr, nullptr}, 1, pl.npad, n, pl.npad, 0};
-    UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
+    // nothing split: tiles in L2-friendly bands per XCD
+    const int xcd = pl.full == ntile;
+    UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, xcd};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
-    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(pl.full + (ntile - pl.full) * pl.splits), dim3(GEMM_THREADS),
+    const int nwg = xcd ? (ntile + 7) / 8 * 8 : pl.full + (ntile - pl.full) * pl.splits;
+    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
     return hipGetLastError();
 }
@@ -252,10 +255,13 @@ hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, f
     if (e != hipSuccess) return e;
     DlRows a{{XH, XH, XL, XL}, 4, pl.npad, n, pl.npad, pl.npad};
     DlRows b{{XH, XL, XH, XL}, 4, pl.npad, n, pl.npad, pl.npad};
-    UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
+    // nothing split: tiles in L2-friendly bands per XCD
+    const int xcd = pl.full == ntile;
+    UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, xcd};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
-    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(pl.full + (ntile - pl.full) * pl.splits), dim3(GEMM_THREADS),
+    const int nwg = xcd ? (ntile + 7) / 8 * 8 : pl.full + (ntile - pl.full) * pl.splits;
+    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, a, b, map, epi);
     return hipGetLastError();
 }
