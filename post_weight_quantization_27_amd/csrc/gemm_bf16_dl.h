@@ -73,6 +73,39 @@ struct DlRows {
     }
 };
 
+// Rows stored tile-major: the k-tile kt (32 k) of the 256-row panel P is one contiguous
+// 256 x 32 block, element (r, k) of a segment at ((r / 256) kpan + k / 32) 8192 +
+// (r % 256) 32 + k % 32, kpan = kseg / 32.  A tile's load then reads 16 KiB in one piece
+// (each instruction 1 KiB), instead of 256 rows a whole row length apart.  Rows are padded
+// to whole panels and k to whole segments (the writer zeroes both), so nothing is clamped.
+// Up to four k segments as in DlRows; tile row offsets m0 are multiples of 256.
+struct DlTiled {
+    const uint16_t* seg[4];
+    int nseg;
+    int64_t kseg;
+    __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
+        const uint16_t* base = seg[0];
+        int64_t kk = k0;
+        if (nseg > 1) {
+            const int sg = (int)(k0 / kseg);
+            base = seg[sg];
+            kk = k0 - (int64_t)sg * kseg;
+        }
+        const uint16_t* blk = base + ((m0 >> 8) * (kseg >> 5) + (kk >> 5)) * (int64_t)(DL_TILE * DL_BK);
+        const int pc = lane & 3, rl = lane >> 2;
+        const int lc = pc ^ ((rl >> 2) & 3);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r0 = 16 * (wave + 4 * q);
+            dl_load16(blk + (r0 + rl) * DL_BK + 8 * lc, S + r0 * DL_BK);
+        }
+    }
+};
+// element (r, k) of one segment in the tile-major layout
+__host__ __device__ __forceinline__ int64_t dl_tiled_index(int64_t r, int64_t k, int64_t kseg) {
+    return ((r >> 8) * (kseg >> 5) + (k >> 5)) * (int64_t)(DL_TILE * DL_BK) + (r & 255) * DL_BK + (k & 31);
+}
+
 // s_waitcnt with only the vector-memory count constrained: vmcnt <= N (N < 64)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

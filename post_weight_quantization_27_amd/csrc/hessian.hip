@@ -165,12 +165,12 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
     for (int h = 0; h < 2; ++h) {
         const int idx = tid + 256 * h;
         const int cr = idx >> 3, tch = (idx & 7) * 8;      // output row = column cr, tokens tch .. +7
-        const int64_t c = c0 + cr;
-        if (c >= n) continue;
+        const int64_t c = c0 + cr;                         // rows past n (panel padding) get zeros
         uint32_t w[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = (uint32_t)tile[tch + 2 * k][cr] | ((uint32_t)tile[tch + 2 * k + 1][cr] << 16);
-        *(uint4*)(XT + c * npad + t0 + tch) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int k = 0; k < 4; ++k)
+            w[k] = c < n ? ((uint32_t)tile[tch + 2 * k][cr] | ((uint32_t)tile[tch + 2 * k + 1][cr] << 16)) : 0u;
+        *(uint4*)(XT + dl_tiled_index(c, t0 + tch, npad)) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
@@ -208,36 +208,36 @@ __global__ __launch_bounds__(256) void transpose_split_f32_kernel(const float* _
     for (int h = 0; h < 2; ++h) {
         const int idx = tid + 256 * h;
         const int cr = idx >> 3, tch = (idx & 7) * 8;
-        const int64_t c = c0 + cr;
-        if (c >= n) continue;
+        const int64_t c = c0 + cr;                         // rows past n (panel padding) get zeros
         uint32_t wh[4], wl[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            wh[k] = (uint32_t)th[tch + 2 * k][cr] | ((uint32_t)th[tch + 2 * k + 1][cr] << 16);
-            wl[k] = (uint32_t)tl[tch + 2 * k][cr] | ((uint32_t)tl[tch + 2 * k + 1][cr] << 16);
+            wh[k] = c < n ? ((uint32_t)th[tch + 2 * k][cr] | ((uint32_t)th[tch + 2 * k + 1][cr] << 16)) : 0u;
+            wl[k] = c < n ? ((uint32_t)tl[tch + 2 * k][cr] | ((uint32_t)tl[tch + 2 * k + 1][cr] << 16)) : 0u;
         }
-        *(uint4*)(XH + c * npad + t0 + tch) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-        *(uint4*)(XL + c * npad + t0 + tch) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+        const int64_t o = dl_tiled_index(c, t0 + tch, npad);
+        *(uint4*)(XH + o) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+        *(uint4*)(XL + o) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
     }
 }
 
 // bfloat16 X on the direct-load engine: both operands are rows of the transposed copy
-// (tokens contiguous, zero past n_tok), 256 x 256 upper tiles
+// (stored tile-major, zero past n_tok and past n), 256 x 256 upper tiles
 hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, uint16_t* XT, float* part,
                         const HessPlan& pl, hipStream_t s) {
     const int vec = (ldx % 8 == 0) && aligned(X, 16);
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(pl.npad / 64), (unsigned)cdiv(n, 64)), dim3(256), 0, s,
-                       (const uint16_t*)X, n_tok, n, ldx, vec, XT, pl.npad);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(pl.npad / 64), (unsigned)(cdiv(n, DL_TILE) * (DL_TILE / 64))),
+                       dim3(256), 0, s, (const uint16_t*)X, n_tok, n, ldx, vec, XT, pl.npad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    DlRows op{{XT, nullptr, nullptr, nullptr}, 1, pl.npad, n, pl.npad, 0};
+    DlTiled op{{XT, nullptr, nullptr, nullptr}, 1, pl.npad};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
     // nothing split: tiles in L2-friendly bands per XCD
     const int xcd = pl.full == ntile;
     UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, xcd};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
     const int nwg = xcd ? (ntile + 7) / 8 * 8 : pl.full + (ntile - pl.full) * pl.splits;
-    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
+    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
     return hipGetLastError();
 }
@@ -247,21 +247,21 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
 // by one contraction over four k segments (A: XH XH XL XL, B: XH XL XH XL)
 hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, uint16_t* XH, float* part,
                          const HessPlan& pl, hipStream_t s) {
-    uint16_t* XL = XH + n * pl.npad;
+    uint16_t* XL = XH + cdiv(n, DL_TILE) * DL_TILE * pl.npad;
     const int vec = (ldx % 4 == 0) && aligned(X, 16);
-    hipLaunchKernelGGL(transpose_split_f32_kernel, dim3((unsigned)(pl.npad / 64), (unsigned)cdiv(n, 64)), dim3(256), 0,
-                       s, (const float*)X, n_tok, n, ldx, vec, XH, XL, pl.npad);
+    hipLaunchKernelGGL(transpose_split_f32_kernel, dim3((unsigned)(pl.npad / 64), (unsigned)(cdiv(n, DL_TILE) * (DL_TILE / 64))),
+                       dim3(256), 0, s, (const float*)X, n_tok, n, ldx, vec, XH, XL, pl.npad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    DlRows a{{XH, XH, XL, XL}, 4, pl.npad, n, pl.npad, pl.npad};
-    DlRows b{{XH, XL, XH, XL}, 4, pl.npad, n, pl.npad, pl.npad};
+    DlTiled a{{XH, XH, XL, XL}, 4, pl.npad};
+    DlTiled b{{XH, XL, XH, XL}, 4, pl.npad};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
     // nothing split: tiles in L2-friendly bands per XCD
     const int xcd = pl.full == ntile;
     UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, xcd};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
     const int nwg = xcd ? (ntile + 7) / 8 * 8 : pl.full + (ntile - pl.full) * pl.splits;
-    hipLaunchKernelGGL((gemm_dl_kernel<DlRows, DlRows, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
+    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, a, b, map, epi);
     return hipGetLastError();
 }
@@ -328,7 +328,8 @@ HessPlan hessian_plan(int64_t n_tok, int64_t d_in, int x_dtype) {
     }
     p.full = full;
     const int copies = p.dl == 4 ? 2 : (p.dl ? 1 : 0);   // transposed X, or its bfloat16 pair
-    p.xt_bytes = align_up((size_t)copies * d_in * p.npad * sizeof(uint16_t), 256);
+    // the transposed copy is tile-major, rows padded to whole 256-row panels
+    p.xt_bytes = align_up((size_t)copies * cdiv(d_in, DL_TILE) * DL_TILE * p.npad * sizeof(uint16_t), 256);
     const size_t parts = p.splits > 1 ? (size_t)p.splits * (ntile - full) * p.bm * p.bm * sizeof(float) : 0;
     p.ws_bytes = p.xt_bytes + parts;
     return p;
