@@ -206,9 +206,11 @@ __device__ __forceinline__ void upper_band_tile(int L, int tiles, int G, int& ti
 // [0, full) over the whole k range (t.split = -1); the tiles after them are split into
 // `splits` k chunks of kchunk, workgroup full + s * (ntile - full) + j taking chunk s of tile
 // full + j.  With full = 0 every tile is split.
-// xcd (only with full == ntile, nothing split): workgroup b runs on XCD b % 8, which takes a
-// contiguous run of the tiles in bands of four rows (upper_band_tile), so the tiles in flight
-// on one XCD share a few operand blocks in its L2; the grid is padded to a multiple of 8 and
+// xcd (only with full == ntile, nothing split, or full == 0, everything split): the work
+// items are (chunk, tile) with the tiles in bands of four rows (upper_band_tile), chunk
+// slowest; workgroup b runs on XCD b % 8, which takes a contiguous run of them, so the
+// workgroups in flight on one XCD share a few operand blocks (and one k range) in its L2.
+// t.tile stays the tile's index in the plain order.  The grid is padded to a multiple of 8;
 // the padding workgroups have no tile.
 struct UpperMap {
     int64_t N, K;
@@ -221,15 +223,19 @@ struct UpperMap {
         const int ntile = tiles * (tiles + 1) / 2;
         int ti = 0, tj = 0;
         if (xcd) {
-            const int per = (ntile + 7) / 8;
+            const bool whole = full == ntile;
+            const int nwork = whole ? ntile : ntile * splits;
+            const int per = (nwork + 7) / 8;
             const int L = (bid % 8) * per + bid / 8;
-            t.split = -1;
-            t.tile = L;
-            if (L >= ntile) {
+            if (L >= nwork) {
+                t.split = -1;
+                t.tile = 0;
                 t.kbeg = t.kend = 0;
                 return false;
             }
-            upper_band_tile(L, tiles, 4, ti, tj);
+            t.split = whole ? -1 : L / ntile;
+            upper_band_tile(L % ntile, tiles, 4, ti, tj);
+            t.tile = ti * tiles - ti * (ti - 1) / 2 + (tj - ti);
         } else {
             if (bid < full) {
                 t.split = -1;

@@ -232,11 +232,12 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
     if (e != hipSuccess) return e;
     DlTiled op{{XT, nullptr, nullptr, nullptr}, 1, pl.npad};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
-    // nothing split: tiles in L2-friendly bands per XCD
-    const int xcd = pl.full == ntile;
+    // nothing or everything split: work items in L2-friendly bands per XCD
+    const int xcd = pl.full == ntile || pl.full == 0;
     UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, xcd};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
-    const int nwg = xcd ? (ntile + 7) / 8 * 8 : pl.full + (ntile - pl.full) * pl.splits;
+    const int nwork = pl.full == ntile ? ntile : pl.full + (ntile - pl.full) * pl.splits;
+    const int nwg = xcd ? (nwork + 7) / 8 * 8 : nwork;
     hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
     return hipGetLastError();
@@ -256,11 +257,12 @@ hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, f
     DlTiled a{{XH, XH, XL, XL}, 4, pl.npad};
     DlTiled b{{XH, XL, XH, XL}, 4, pl.npad};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
-    // nothing split: tiles in L2-friendly bands per XCD
-    const int xcd = pl.full == ntile;
+    // nothing or everything split: work items in L2-friendly bands per XCD
+    const int xcd = pl.full == ntile || pl.full == 0;
     UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, xcd};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
-    const int nwg = xcd ? (ntile + 7) / 8 * 8 : pl.full + (ntile - pl.full) * pl.splits;
+    const int nwork = pl.full == ntile ? ntile : pl.full + (ntile - pl.full) * pl.splits;
+    const int nwg = xcd ? (nwork + 7) / 8 * 8 : nwork;
     hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, a, b, map, epi);
     return hipGetLastError();

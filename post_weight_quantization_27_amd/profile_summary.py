@@ -39,14 +39,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CALL_OF = [
     ("EpiHess", "hessian_accumulate"), ("hess_reduce", "hessian_accumulate"),
     ("mirror_upper", "hessian_accumulate"), ("transpose_bf16", "hessian_accumulate"),
-    ("FillFunctor", "hessian_accumulate"),
+    ("transpose_split", "hessian_accumulate"), ("FillFunctor", "hessian_accumulate"),
     ("damp_kernel", "hessian_damp"), ("act_order_kernel", "act_order_perm"),
     ("copy_upper", "chol_inverse_upper"), ("copy_perm", "chol_inverse_upper"), ("set_int", "chol_inverse_upper"),
-    ("chol_diag", "chol_inverse_upper"), ("EpiStore", "chol_inverse_upper"), ("EpiSyrk", "chol_inverse_upper"),
-    ("EpiPush", "chol_inverse_upper"),
+    ("chol_diag", "chol_inverse_upper"), ("chol_update_diag", "chol_inverse_upper"),
+    ("EpiStore", "chol_inverse_upper"), ("EpiSyrk", "chol_inverse_upper"), ("EpiPush", "chol_inverse_upper"),
     ("gptq_", "gptq_quantize_layer"), ("EpiSub", "gptq_quantize_layer"), ("inv_perm", "gptq_quantize_layer"),
     ("unpermute_codes", "gptq_quantize_layer"),
-    ("rtn_kernel", "rtn_quantize"), ("dequant_kernel", "dequant"),
+    ("rtn_kernel", "rtn_quantize"), ("rtn_group", "rtn_quantize"),
+    ("dequant_kernel", "dequant"), ("dequant_vec", "dequant"),
     ("mse_", "recon_mse"), ("EpiSq", "recon_mse"), ("set_double", "recon_mse"),
 ]
 
