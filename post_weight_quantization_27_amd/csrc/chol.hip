@@ -99,6 +99,19 @@ __device__ __forceinline__ f32x16 mfma_tile_ab(const float (*MA)[LP], int ra, in
 }
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 x 16 tile of A B^T, A rows [ra, ra+16), B rows [rb, rb+16), k over [0, kn) of the LDS
+// matrix M; output element i of lane l is (4 (l / 16) + i, l % 16)
+__device__ __forceinline__ f32x4 mfma16_tile_abT(const float (*M)[LP], int ra, int rb, int kn, int lane) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kp = 0; kp < kn; kp += 4) {
+        const float av = M[ra + (lane & 15)][kp + (lane >> 4)];
+        const float bv = M[rb + (lane & 15)][kp + (lane >> 4)];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 constexpr int DIAG_FLOATS = 2 * CHOL_NB * LP + 4;       // A, Z, the failed-pivot word
 
 // The diagonal block [k0, k0 + bs) in one workgroup, in the LDS buffer smem (DIAG_FLOATS
@@ -139,31 +152,47 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
     }
     __syncthreads();
 
-    // ---------------- pending update: Z <- panel rows, A -= Z Z^T on the ten upper 32 x 32
-    // tiles (MFMA, k = 128, zero columns past kdepth), then Z cleared again
+    // ---------------- pending update: Z <- panel rows, A -= Z Z^T on the 36 upper 16 x 16
+    // tiles (nine per wave, MFMA, k = 128, zero columns past kdepth).  Afterwards only the
+    // two lower blocks that the inverse reads as zeros are cleared (the rest of Z is written
+    // before it is read).
     if (Pu) {
         {
             const int i = tid >> 1, c0 = 64 * (tid & 1);
             const float* src = Pu + (int64_t)i * pld + c0;
+            if (kdepth == CHOL_NB && pld % 4 == 0 && ((uintptr_t)Pu & 15) == 0) {
+                float4 v[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) v[q] = *(const float4*)(src + 4 * q);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    Z[i][c0 + 4 * q] = v[q].x; Z[i][c0 + 4 * q + 1] = v[q].y;
+                    Z[i][c0 + 4 * q + 2] = v[q].z; Z[i][c0 + 4 * q + 3] = v[q].w;
+                }
+            } else {
 #pragma unroll 16
-            for (int q = 0; q < 64; ++q) Z[i][c0 + q] = c0 + q < kdepth ? src[q] : 0.f;
+                for (int q = 0; q < 64; ++q) Z[i][c0 + q] = c0 + q < kdepth ? src[q] : 0.f;
+            }
         }
         __syncthreads();
-        for (int t = wave; t < 10; t += 4) {
-            const int ti = t < 4 ? 0 : (t < 7 ? 1 : (t < 9 ? 2 : 3));
-            const int tj = ti + t - (ti == 0 ? 0 : (ti == 1 ? 4 : (ti == 2 ? 7 : 9)));
-            const f32x16 acc = mfma_tile_abT(Z, 32 * ti, 32 * tj, 0, CHOL_NB, lane);
+        for (int t = wave; t < 36; t += 4) {
+            int ti = 0, r = t;
+            while (r >= 8 - ti) { r -= 8 - ti; ++ti; }
+            const int tj = ti + r;
+            const f32x4 acc = mfma16_tile_abT(Z, 16 * ti, 16 * tj, CHOL_NB, lane);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 32 * ti + acc_row(v, lane), c = 32 * tj + (lane & 31);
-                if (c >= r) A[r][c] -= acc[v];
+            for (int v = 0; v < 4; ++v) {
+                const int rr = 16 * ti + 4 * (lane >> 4) + v, cc = 16 * tj + (lane & 15);
+                if (cc >= rr) A[rr][cc] -= acc[v];
             }
         }
         __syncthreads();
         {
-            const int i = tid >> 1, c0 = 64 * (tid & 1);
-#pragma unroll 16
-            for (int q = 0; q < 64; ++q) Z[i][c0 + q] = 0.f;
+            const int i = tid >> 3, c = 4 * (tid & 7);     // 32 rows x 32 columns, two blocks
+            for (int q = 0; q < 4; ++q) {
+                Z[32 + i][c + q] = 0.f;
+                Z[96 + i][64 + c + q] = 0.f;
+            }
         }
         __syncthreads();
     }
@@ -173,8 +202,9 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
     // pivot column's entries of the panel rows reach every lane by readlane, so a pivot costs
     // no LDS round trip and no barrier.  Entries below the diagonal pick up meaningless
     // values on the way (they only ever feed other entries below the diagonal) and are
-    // written back as 0.  Then all four waves apply the panel's rank-32 update to the rows
-    // and columns left of it on MFMA.
+    // written back as 0.  The panel's rank-32 update of the rows and columns left of it runs
+    // on MFMA in two parts: the next panel's column block at once (all four waves), the rest
+    // on waves 1..3 while wave 0 factors that next panel.
     // unrolled over the four panels, so every readlane lane index is a constant.  A pivot's
     // broadcasts all go out before its FMAs (each into its own SGPR, fenced by a scheduling
     // barrier): interleaved, every FMA pair would wait out the latency of its own readlane.
@@ -221,21 +251,32 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
                 A[lane + 64][c0 + kk] = lane + 64 <= c0 + kk ? a1[kk] : 0.f;
             }
             if (lane == 0) fail = bad >= 0 ? (int)(k0 + c0 + bad + 1) : 0;
+        } else if (p < 3) {
+            // the rest of panel p + 1's update (column blocks left of this panel), on waves
+            // 1..3 while wave 0 factors panel p: disjoint columns
+            const int cp = 32 * (p + 1);
+            const int nd = p * (p + 1) / 2;
+            for (int t = wave - 1; t < nd; t += 3) {
+                int ti = 0, r = t;
+                while (r >= p - ti) { r -= p - ti; ++ti; }
+                const int tj = ti + r;
+                const f32x16 acc = mfma_tile_abT(A, 32 * ti, 32 * tj, cp, 32, lane);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) A[32 * ti + acc_row(v, lane)][32 * tj + (lane & 31)] -= acc[v];
+            }
         }
         __syncthreads();
         if (fail) {                                      // same decision in every thread
             if (tid == 0) *info = fail;
             return;
         }
-        if (p > 0) {                                     // A[0:c0, 0:c0] -= P P^T, P = V[0:c0, panel]
-            const int ntile = p * (p + 1) / 2;
-            for (int t = wave; t < ntile; t += 4) {
-                int ti = 0, r = t;
-                while (r >= p - ti) { r -= p - ti; ++ti; }
-                const int tj = ti + r;
-                const f32x16 acc = mfma_tile_abT(A, 32 * ti, 32 * tj, c0, 32, lane);
+        if (p > 0) {
+            // A[0:c0, 0:c0] -= P P^T, P = V[0:c0, panel]: now only the next panel's column
+            // block (its tiles (ti, p - 1)); the rest runs beside that panel's factor
+            for (int t = wave; t < p; t += 4) {
+                const f32x16 acc = mfma_tile_abT(A, 32 * t, 32 * (p - 1), c0, 32, lane);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) A[32 * ti + acc_row(v, lane)][32 * tj + (lane & 31)] -= acc[v];
+                for (int v = 0; v < 16; ++v) A[32 * t + acc_row(v, lane)][32 * (p - 1) + (lane & 31)] -= acc[v];
             }
             __syncthreads();
         }
