@@ -197,66 +197,58 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
         __syncthreads();
     }
 
-    // ---------------- factor: 32-column panels from the right.  Wave 0 factors a panel in
-    // registers (lane l holds rows l and l + 64 of the panel's 32 columns): the pivot and the
-    // pivot column's entries of the panel rows reach every lane by readlane, so a pivot costs
-    // no LDS round trip and no barrier.  Entries below the diagonal pick up meaningless
+    // ---------------- factor: 32-column panels from the right.  The waves holding rows at or
+    // above the panel's diagonal factor it in registers (32 rows each, plus a copy of the
+    // panel's rows): the pivot and the pivot column's entries of the panel rows reach every
+    // lane by readlane, so a pivot costs no LDS round trip and no barrier.  Entries below the diagonal pick up meaningless
     // values on the way (they only ever feed other entries below the diagonal) and are
     // written back as 0.  The panel's rank-32 update of the rows and columns left of it runs
     // on MFMA in two parts: the next panel's column block at once (all four waves), the rest
-    // on waves 1..3 while wave 0 factors that next panel.
+    // on the waves that hold no rows of that next panel while the others factor it.
     // unrolled over the four panels, so every readlane lane index is a constant.  A pivot's
     // broadcasts all go out before its FMAs (each into its own SGPR, fenced by a scheduling
     // barrier): interleaved, every FMA pair would wait out the latency of its own readlane.
-    // Rows 64..127 lie below the diagonal of the two left panels, which skip them.
+    // Waves whose rows all lie below the panel's diagonal take no part in its factor.
 #pragma unroll
     for (int p = 3; p >= 0; --p) {
         const int c0 = 32 * p;
-        if (wave == 0) {
-            const int h = c0 >> 6;                       // register holding the panel rows
-            const int lb = c0 & 63;                      // lane of the panel's first row
-            const bool hi = c0 + 32 > 64;                // rows 64.. reach the panel's diagonal
-            float a0[32], a1[32];
+        if (wave <= p) {
+            // waves 0..p factor the panel together, each on its own 32 rows (lanes 0..31: row
+            // 32 wave + lane) and a private copy of the panel's 32 rows (lanes 32..63: row
+            // c0 + lane - 32), so every broadcast comes from its own lanes; all waves take the
+            // same pivots
+            const int row = lane < 32 ? 32 * wave + lane : c0 + lane - 32;
+            float a[32];
 #pragma unroll
-            for (int kk = 0; kk < 32; ++kk) {
-                a0[kk] = A[lane][c0 + kk];
-                a1[kk] = hi ? A[lane + 64][c0 + kk] : 0.f;
-            }
+            for (int kk = 0; kk < 32; ++kk) a[kk] = A[row][c0 + kk];
             int bad = -1;                                // first failed pivot (uniform)
 #pragma unroll
             for (int kk = 31; kk >= 0; --kk) {
-                const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                    __builtin_bit_cast(int, h ? a1[kk] : a0[kk]), lb + kk));
+                const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[kk]), 32 + kk));
                 if (!(d > 0.f) && bad < 0) bad = kk;
                 const float r = __builtin_amdgcn_rsqf(d);
-                a0[kk] *= r;                             // column kk of V (the pivot row gets d r)
-                if (hi) a1[kk] *= r;
-                const float vc = h ? a1[kk] : a0[kk];
+                a[kk] *= r;                              // column kk of V (the pivot row gets d r)
                 float vj[32];
 #pragma unroll
                 for (int jj = 0; jj < kk; ++jj)
-                    vj[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vc), lb + jj));
+                    vj[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[kk]), 32 + jj));
                 __builtin_amdgcn_sched_barrier(0);
                 // the next pivot's column first, so its readlane finds it done
 #pragma unroll
-                for (int jj = kk - 1; jj >= 0; --jj) {
-                    a0[jj] = fmaf(-a0[kk], vj[jj], a0[jj]);
-                    if (hi) a1[jj] = fmaf(-a1[kk], vj[jj], a1[jj]);
-                }
+                for (int jj = kk - 1; jj >= 0; --jj) a[jj] = fmaf(-a[kk], vj[jj], a[jj]);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (lane < 32) {
 #pragma unroll
-            for (int kk = 0; kk < 32; ++kk) {
-                A[lane][c0 + kk] = lane <= c0 + kk ? a0[kk] : 0.f;
-                A[lane + 64][c0 + kk] = lane + 64 <= c0 + kk ? a1[kk] : 0.f;
+                for (int kk = 0; kk < 32; ++kk) A[row][c0 + kk] = row <= c0 + kk ? a[kk] : 0.f;
             }
-            if (lane == 0) fail = bad >= 0 ? (int)(k0 + c0 + bad + 1) : 0;
+            if (wave == 0 && lane == 0) fail = bad >= 0 ? (int)(k0 + c0 + bad + 1) : 0;
         } else if (p < 3) {
-            // the rest of panel p + 1's update (column blocks left of this panel), on waves
-            // 1..3 while wave 0 factors panel p: disjoint columns
+            // the rest of panel p + 1's update (column blocks left of this panel), on the waves
+            // p + 1 .. 3 while the others factor panel p: disjoint columns
             const int cp = 32 * (p + 1);
             const int nd = p * (p + 1) / 2;
-            for (int t = wave - 1; t < nd; t += 3) {
+            for (int t = wave - (p + 1); t < nd; t += 3 - p) {
                 int ti = 0, r = t;
                 while (r >= p - ti) { r -= p - ti; ++ti; }
                 const int tj = ti + r;
