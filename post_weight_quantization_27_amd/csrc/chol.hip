@@ -418,7 +418,7 @@ RectMap rect(int bm, int bn, int64_t M, int64_t N, int64_t K) {
 inline int vec_ok(const float* p, int64_t ld) { return (ld % 4 == 0) && aligned(p, 16); }
 
 typedef GemmTask<64, 64, OpMMajor<0>, OpMMajor<0>, RectMap, EpiStore> TrsmTask;
-typedef GemmTask<128, 64, OpMMajor<0>, OpKMajor<0>, RectMap, EpiStore> FinalizeTask;
+typedef GemmTask<64, 64, OpMMajor<0>, OpKMajor<0>, RectMap, EpiStore> FinalizeTask;   // short k: all loads up front
 template <int T>
 using SyrkTask = GemmTask<T, T, OpMMajor<0>, OpMMajor<0>, UpperMap, EpiSyrk>;
 template <int T>
@@ -562,7 +562,7 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
             FinalizeTask ft{};
             ft.la = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
             ft.lb = OpKMajor<0>{U + k0 * n + k0 + bs, n, r, bs, vu && ((k0 + bs) % 4 == 0)};
-            ft.map = rect(128, 64, bs, r, bs);
+            ft.map = rect(64, 64, bs, r, bs);
             ft.epi = EpiStore{U + k0 * n + k0 + bs, n, bs, r, -1.f};
             const int n1 = k0 > 0 ? ntiles(tt.map) : 0;
             const int n2 = r > 0 ? ntiles(ft.map) : 0;
@@ -598,7 +598,7 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
         FinalizeTask ft{};
         ft.la = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
         ft.lb = OpKMajor<0>{U + k0 * n + k0 + bs, n, r, bs, vu && ((k0 + bs) % 4 == 0)};
-        ft.map = rect(128, 64, bs, r, bs);
+        ft.map = rect(64, 64, bs, r, bs);
         ft.epi = EpiStore{U + k0 * n + k0 + bs, n, bs, r, -1.f};
         const int n1 = k0 > 0 ? ntiles(tt.map) : 0;
         const int n2 = r > 0 ? ntiles(ft.map) : 0;
