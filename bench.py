@@ -140,8 +140,8 @@ def work_of(name, spec):
 # kernels one call launches, for the roofline's description (chol and gptq per 128 columns)
 def launches_of(name, spec):
     nb = -(-spec.d_in // 128)
-    if name == "chol_inverse_upper":
-        return 2 + 3 * nb
+    if name == "chol_inverse_upper":            # below 4096 the next diagonal factor joins the update launch
+        return 2 + (2 if spec.d_in < 4096 else 3) * nb
     if name == "gptq_quantize_layer":
         return 1 + 2 * nb
     if name == "recon_mse":
