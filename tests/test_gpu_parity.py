@@ -371,6 +371,24 @@ def test_gptq_end_to_end(pwq, name, m, n, n_tok, g, B, act, wdt):
     print(f"{name}: code agreement {agree:.6f}")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 8])
+@pytest.mark.parametrize("m", [96, 4100])
+def test_gptq_bit_widths(pwq, bits, m):
+    """Other widths than 4 (codes only; nibbles are 4-bit): 2^(b-1) - 1 levels each side, on
+    the one-wave-per-row kernel (96 rows) and the four-lanes-per-row kernel (4100 rows)."""
+    rng = np.random.default_rng(40 + bits + m)
+    n, n_tok = 256, 700
+    W = rand_w(rng, m, n)
+    X = rng.standard_normal((n_tok, n)).astype(np.float32)
+    X[:, 1:] += 0.5 * X[:, :-1]
+    res = pwq.gptq_layer(dev(W), dev(X), bits, 128, 128, 0.01, want_packed=False)
+    want = _oracle_layer(W, X.astype(np.float64), bits, 128, 128, 0.01, False)
+    got = host(res["codes"])
+    qmax = (1 << (bits - 1)) - 1
+    assert got.min() >= -qmax and got.max() <= qmax
+    _check_gptq(got, want["codes"])
+
+
 def test_gptq_given_oracle_factor(pwq):
     """Stage check: the column loop alone, fed the oracle's U rounded to float32."""
     rng = np.random.default_rng(20)
