@@ -56,6 +56,19 @@ listed in the design notes):
 * R11 Reconstruction MSE: mean over all tokens x outputs of (X (W - What)^T)^2 with the
       same X for both and the original W ([GPT2-RE] step 5, per layer).
 * R12 A non positive definite H raises NotPositiveDefinite (no automatic re-damping).
+* A1  Zero-point (asymmetric) quantization, [MQM] "Affine Quantization": code =
+      round(w / S) + Z, dequantized S (code - Z).  The pages give no rule for S and Z;
+      the plainest one that keeps real 0 exact: a group's range [lo, hi] = [min(w, 0),
+      max(w, 0)] is mapped onto the codes 0 .. 2^b - 1.
+* A2  S = fp16( fp32( fp32(hi - lo) / (2^b - 1) ) ) (one float32 subtraction and one
+      float32 division, then float16, as R7).
+* A3  Z = round(-lo / S) (exact quotient, ties to even), clamped to [0, 2^b - 1]; stored in
+      16 bits as [GPTQ-P] "Group Quantization" counts it (4 + 32/g bits per weight).  S = 0
+      (an all-zero group, or a range below float16) gives Z = 0 and every code 0.
+* A4  Codes: clamp(round(w / S) + Z, 0, 2^b - 1), round = nearest integer to the exact
+      quotient, ties to even (R8); INT4 nibble = code itself (R10's layout otherwise).
+* A5  GPTQ with zero-points takes S and Z at a group's first column from the current
+      values of the group's columns (R5), and the dequantized value S (code - Z) (R6).
 
 Pins (tests/test_oracle_pins.py):
   rtn / quantize_codes / group_scales : golden tie-to-even rows, code range, error bound,
@@ -69,6 +82,9 @@ Pins (tests/test_oracle_pins.py):
   act_order_perm                      : already-sorted diagonal == no act-order; g_idx round trip
   pack_int4 / dequant                 : golden bytes, storage bits/weight of [GPTQ-P]
   recon_mse                           : trace identity with the undamped Hessian
+  asym_scale_zero / rtn_asym / gptq(sym=False) : golden worked group (A1-A4), exact zero,
+                                        error bound, range end points, 4.25 bits/weight,
+                                        diagonal-H == rtn_asym, block-size invariance
 """
 from __future__ import annotations
 
@@ -81,7 +97,8 @@ __all__ = [
     "hessian", "damp_hessian", "act_order_perm", "chol_inverse_upper",
     "gptq", "gptq_unblocked", "rtn", "pack_int4", "unpack_int4", "dequant",
     "recon_mse", "recon_mse_trace", "direct_obs", "quantize_layer", "n_groups",
-    "storage_bytes",
+    "storage_bytes", "asym_scale_zero", "quantize_codes_asym", "rtn_asym", "dequant_asym",
+    "pack_uint4", "unpack_uint4",
 ]
 
 
@@ -127,6 +144,57 @@ def quantize_codes(w: np.ndarray, s16: np.ndarray, bits: int) -> np.ndarray:
     q = np.clip(q, -qmax(bits), qmax(bits))
     q = np.where(s > 0, q, 0.0)
     return q.astype(np.int8)
+
+
+def asym_scale_zero(lo: np.ndarray, hi: np.ndarray, bits: int):
+    """Scale and zero-point of [MQM] "Affine Quantization" for a range [lo, hi] that holds 0
+    (A1-A3): S = fp16(fp32(fp32(hi - lo) / (2^b - 1))), Z = round(-lo / S) clamped to
+    [0, 2^b - 1], Z = 0 where S = 0.  Returns (S float16, Z uint16)."""
+    top = (1 << bits) - 1
+    lo32 = np.asarray(lo, dtype=np.float64).astype(np.float32)
+    hi32 = np.asarray(hi, dtype=np.float64).astype(np.float32)
+    span = (hi32 - lo32).astype(np.float32)
+    s16 = (span / np.float32(top)).astype(np.float32).astype(np.float16)
+    s = s16.astype(np.float64)
+    safe = np.where(s > 0, s, 1.0)
+    z = np.clip(np.rint(-lo32.astype(np.float64) / safe), 0, top)
+    z = np.where(s > 0, z, 0.0)
+    return s16, z.astype(np.uint16)
+
+
+def quantize_codes_asym(w: np.ndarray, s16: np.ndarray, z: np.ndarray, bits: int) -> np.ndarray:
+    """Codes round(w / S) + Z clamped to [0, 2^b - 1] (A4); the quotient is decided exactly
+    as in ``quantize_codes``.  S = 0 gives code 0.  Returns uint8."""
+    top = (1 << bits) - 1
+    w = np.asarray(w, dtype=np.float64)
+    s = np.asarray(s16, dtype=np.float16).astype(np.float64)
+    zz = np.asarray(z, dtype=np.float64)
+    safe = np.where(s > 0, s, 1.0)
+    q = np.clip(np.rint(w / safe) + zz, 0, top)
+    q = np.where(s > 0, q, 0.0)
+    return q.astype(np.uint8)
+
+
+def _group_params(vals: np.ndarray, bits: int, sym: bool):
+    """Per-row quantizer of a group from its current values (rows x columns): the
+    symmetric scale (R7), or the zero-point pair of A1-A3."""
+    if sym:
+        return group_scales_from_absmax(np.max(np.abs(vals), axis=1), bits), None
+    lo = np.minimum(np.min(vals, axis=1), 0.0)
+    hi = np.maximum(np.max(vals, axis=1), 0.0)
+    return asym_scale_zero(lo, hi, bits)
+
+
+def _codes(w, s16, z, bits: int, sym: bool):
+    return quantize_codes(w, s16, bits) if sym else quantize_codes_asym(w, s16, z, bits)
+
+
+def _value(s16, z, q) -> np.ndarray:
+    """The dequantized value S (q - Z) in float64 (exact)."""
+    v = np.asarray(q, dtype=np.float64)
+    if z is not None:
+        v = v - np.asarray(z, dtype=np.float64)
+    return np.asarray(s16, dtype=np.float16).astype(np.float64) * v
 
 
 # ------------------------------------------------------------------ Hessian, damping, order
@@ -185,7 +253,7 @@ def _group_len(n: int, group_size: int) -> int:
     return n if group_size == 0 else group_size
 
 
-def _finish(codes_p, scales, perm, group_size, bits):
+def _finish(codes_p, scales, perm, group_size, bits, zeros=None):
     m, n = codes_p.shape
     if perm is None:
         codes, g_idx = codes_p, None
@@ -195,13 +263,24 @@ def _finish(codes_p, scales, perm, group_size, bits):
         g = _group_len(n, group_size)
         g_idx = np.empty(n, dtype=np.int32)
         g_idx[perm] = (np.arange(n) // g).astype(np.int32)
-    What = dequant(codes, scales, group_size, g_idx=g_idx, out_dtype=np.float64)
-    return {"codes": codes, "scales": scales, "g_idx": g_idx, "What": What, "bits": bits,
-            "group_size": group_size}
+    What = dequant(codes, scales, group_size, g_idx=g_idx, out_dtype=np.float64, zeros=zeros)
+    return {"codes": codes, "scales": scales, "zeros": zeros, "g_idx": g_idx, "What": What,
+            "bits": bits, "group_size": group_size}
+
+
+def _init_params(m, ng, scales_in, zeros_in, sym):
+    scales = np.zeros((m, ng), dtype=np.float16) if scales_in is None else np.array(scales_in, dtype=np.float16).reshape(m, ng)
+    if sym:
+        return scales, None
+    if scales_in is not None and zeros_in is None:
+        raise ValueError("zero-point quantization with given scales needs the zeros too")
+    zeros = np.zeros((m, ng), dtype=np.uint16) if zeros_in is None else np.array(zeros_in, dtype=np.uint16).reshape(m, ng)
+    return scales, zeros
 
 
 def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, block_size: int = 128,
-         perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None) -> dict:
+         perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None,
+         sym: bool = True, zeros_in: Optional[np.ndarray] = None) -> dict:
     """GPTQ with lazy block updates ([GPTQ-P] "The GPTQ Algorithm", R1-R9).
 
     W: d_out x d_in (any float dtype, promoted to float64).  U: the factor of
@@ -217,15 +296,19 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
     right of the block, the updates still pending from the block's earlier columns
     (the pages' group = block = 128 case never needs this).
 
-    Returns codes (int8, original column order), scales (float16, d_out x groups, in
-    processing order), g_idx (int32 or None) and What (float64)."""
+    ``sym=False``: zero-point quantization (A1-A5); the group's scale and zero come from
+    the same current values the symmetric scale would.
+
+    Returns codes (int8, or uint8 with zero-points; original column order), scales
+    (float16, d_out x groups, in processing order), zeros (uint16 like scales, or None),
+    g_idx (int32 or None) and What (float64)."""
     W = np.asarray(W, dtype=np.float64)
     m, n = W.shape
     Wp = W[:, perm].copy() if perm is not None else W.copy()
     g = _group_len(n, group_size)
     ng = n_groups(n, group_size)
-    scales = np.zeros((m, ng), dtype=np.float16) if scales_in is None else np.array(scales_in, dtype=np.float16).reshape(m, ng)
-    codes_p = np.zeros((m, n), dtype=np.int8)
+    scales, zeros = _init_params(m, ng, scales_in, zeros_in, sym)
+    codes_p = np.zeros((m, n), dtype=np.int8 if sym else np.uint8)
     B = int(block_size)
     for b0 in range(0, n, B):
         b1 = min(b0 + B, n)
@@ -240,60 +323,78 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
                 if ge > b1:
                     pending = Wp[:, b1:ge] - err[:, :jj] @ U[b0:j, b1:ge]
                     vals = np.concatenate([vals, pending], axis=1)
-                scales[:, G] = group_scales_from_absmax(np.max(np.abs(vals), axis=1), bits)
+                sG, zG = _group_params(vals, bits, sym)
+                scales[:, G] = sG
+                if not sym:
+                    zeros[:, G] = zG
+            zc = None if sym else zeros[:, G]
             w = panel[:, jj]
-            q = quantize_codes(w, scales[:, G], bits)
+            q = _codes(w, scales[:, G], zc, bits, sym)
             codes_p[:, j] = q
-            what = scales[:, G].astype(np.float64) * q
+            what = _value(scales[:, G], zc, q)
             e = (w - what) / U[j, j]
             err[:, jj] = e
             panel[:, jj + 1:] -= np.outer(e, U[j, j + 1:b1])
         if b1 < n:
             Wp[:, b1:] -= err @ U[b0:b1, b1:]
-    return _finish(codes_p, scales, perm, group_size, bits)
+    return _finish(codes_p, scales, perm, group_size, bits, zeros)
 
 
 def gptq_unblocked(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128,
-                   perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None) -> dict:
+                   perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None,
+                   sym: bool = True, zeros_in: Optional[np.ndarray] = None) -> dict:
     """The column loop without lazy batching: every error goes to all later columns at once."""
     W = np.asarray(W, dtype=np.float64)
     m, n = W.shape
     Wp = W[:, perm].copy() if perm is not None else W.copy()
     g = _group_len(n, group_size)
     ng = n_groups(n, group_size)
-    scales = np.zeros((m, ng), dtype=np.float16) if scales_in is None else np.array(scales_in, dtype=np.float16).reshape(m, ng)
-    codes_p = np.zeros((m, n), dtype=np.int8)
+    scales, zeros = _init_params(m, ng, scales_in, zeros_in, sym)
+    codes_p = np.zeros((m, n), dtype=np.int8 if sym else np.uint8)
     for j in range(n):
         G = j // g
         if j % g == 0 and scales_in is None:
-            scales[:, G] = group_scales_from_absmax(np.max(np.abs(Wp[:, j:j + g]), axis=1), bits)
+            sG, zG = _group_params(Wp[:, j:j + g], bits, sym)
+            scales[:, G] = sG
+            if not sym:
+                zeros[:, G] = zG
+        zc = None if sym else zeros[:, G]
         w = Wp[:, j]
-        q = quantize_codes(w, scales[:, G], bits)
+        q = _codes(w, scales[:, G], zc, bits, sym)
         codes_p[:, j] = q
-        e = (w - scales[:, G].astype(np.float64) * q) / U[j, j]
+        e = (w - _value(scales[:, G], zc, q)) / U[j, j]
         Wp[:, j + 1:] -= np.outer(e, U[j, j + 1:])
-    return _finish(codes_p, scales, perm, group_size, bits)
+    return _finish(codes_p, scales, perm, group_size, bits, zeros)
 
 
-def rtn(W: np.ndarray, bits: int = 4, group_size: int = 128, scales_in: Optional[np.ndarray] = None) -> dict:
+def rtn(W: np.ndarray, bits: int = 4, group_size: int = 128, scales_in: Optional[np.ndarray] = None,
+        sym: bool = True, zeros_in: Optional[np.ndarray] = None) -> dict:
     """Round-to-nearest: scales from the original W per row ([GPT2-RE]) or per group of
-    ``group_size`` consecutive columns ([MQM] "Group-wise Quantization"), then codes."""
+    ``group_size`` consecutive columns ([MQM] "Group-wise Quantization"), then codes.
+    ``sym=False``: the zero-point quantizer of A1-A4 (scale and zero per row and group)."""
     W = np.asarray(W, dtype=np.float64)
     m, n = W.shape
     g = _group_len(n, group_size)
     ng = n_groups(n, group_size)
+    scales, zeros = _init_params(m, ng, scales_in, zeros_in, sym)
     if scales_in is None:
-        scales = np.zeros((m, ng), dtype=np.float16)
         for G in range(ng):
-            scales[:, G] = group_scales_from_absmax(np.max(np.abs(W[:, G * g:(G + 1) * g]), axis=1), bits)
-    else:
-        scales = np.array(scales_in, dtype=np.float16).reshape(m, ng)
-    codes = np.zeros((m, n), dtype=np.int8)
+            sG, zG = _group_params(W[:, G * g:(G + 1) * g], bits, sym)
+            scales[:, G] = sG
+            if not sym:
+                zeros[:, G] = zG
+    codes = np.zeros((m, n), dtype=np.int8 if sym else np.uint8)
     for G in range(ng):
-        codes[:, G * g:(G + 1) * g] = quantize_codes(W[:, G * g:(G + 1) * g], scales[:, G:G + 1], bits)
-    What = dequant(codes, scales, group_size, out_dtype=np.float64)
-    return {"codes": codes, "scales": scales, "g_idx": None, "What": What, "bits": bits,
-            "group_size": group_size}
+        zc = None if sym else zeros[:, G:G + 1]
+        codes[:, G * g:(G + 1) * g] = _codes(W[:, G * g:(G + 1) * g], scales[:, G:G + 1], zc, bits, sym)
+    What = dequant(codes, scales, group_size, out_dtype=np.float64, zeros=zeros)
+    return {"codes": codes, "scales": scales, "zeros": zeros, "g_idx": None, "What": What,
+            "bits": bits, "group_size": group_size}
+
+
+def rtn_asym(W: np.ndarray, bits: int = 4, group_size: int = 128) -> dict:
+    """``rtn`` with the zero-point quantizer (A1-A4)."""
+    return rtn(W, bits, group_size, sym=False)
 
 
 # ------------------------------------------------------------------ storage
@@ -316,16 +417,39 @@ def unpack_int4(packed: np.ndarray, d_in: int) -> np.ndarray:
     return codes
 
 
-def storage_bytes(d_out: int, d_in: int, group_size: int) -> int:
-    """Bytes of the packed INT4 codes plus one float16 scale per row and group
-    ([GPTQ-P] "Group Quantization": 4 bits + 16 / group_size bits per weight)."""
-    return d_out * d_in // 2 + 2 * d_out * n_groups(d_in, group_size)
+def pack_uint4(codes: np.ndarray) -> np.ndarray:
+    """Zero-point codes 0..15, two per byte, nibble = code, even column low (A4)."""
+    c = np.asarray(codes, dtype=np.int16)
+    m, n = c.shape
+    if n % 2:
+        raise ValueError("d_in must be even to pack two codes per byte")
+    if c.size and (c.min() < 0 or c.max() > 15):
+        raise ValueError("zero-point 4-bit codes lie in 0..15")
+    u = c.astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_uint4(packed: np.ndarray, d_in: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty((p.shape[0], d_in), dtype=np.uint8)
+    codes[:, 0::2] = p & 0x0F
+    codes[:, 1::2] = p >> 4
+    return codes
+
+
+def storage_bytes(d_out: int, d_in: int, group_size: int, zero_point: bool = False) -> int:
+    """Bytes of the packed INT4 codes plus one float16 scale (and, with zero-points, one
+    16-bit zero) per row and group ([GPTQ-P] "Group Quantization": 4 bits + 16 / group_size
+    bits per weight for the scale, as many again for a zero)."""
+    per_group = 4 if zero_point else 2
+    return d_out * d_in // 2 + per_group * d_out * n_groups(d_in, group_size)
 
 
 def dequant(codes: np.ndarray, scales: np.ndarray, group_size: int, g_idx: Optional[np.ndarray] = None,
-            out_dtype=np.float64) -> np.ndarray:
-    """What[r, c] = s[r, group(c)] * code[r, c] ([MQM] "Affine Quantization" with Z = 0),
-    exact in float64, then rounded once to ``out_dtype``."""
+            out_dtype=np.float64, zeros: Optional[np.ndarray] = None) -> np.ndarray:
+    """What[r, c] = s[r, group(c)] * (code[r, c] - z[r, group(c)]) ([MQM] "Affine
+    Quantization"; z = 0 without zero-points), exact in float64, then rounded once to
+    ``out_dtype``."""
     codes = np.asarray(codes)
     m, n = codes.shape
     s = np.asarray(scales, dtype=np.float16).astype(np.float64).reshape(m, -1)
@@ -335,8 +459,17 @@ def dequant(codes: np.ndarray, scales: np.ndarray, group_size: int, g_idx: Optio
         gi = np.asarray(g_idx, dtype=np.int64)
     else:
         gi = np.arange(n) // group_size
-    What = s[:, gi] * codes.astype(np.float64)
+    q = codes.astype(np.float64)
+    if zeros is not None:
+        q = q - np.asarray(zeros, dtype=np.float64).reshape(m, -1)[:, gi]
+    What = s[:, gi] * q
     return What.astype(out_dtype)
+
+
+def dequant_asym(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group_size: int,
+                 g_idx: Optional[np.ndarray] = None, out_dtype=np.float64) -> np.ndarray:
+    """``dequant`` with zero-points."""
+    return dequant(codes, scales, group_size, g_idx=g_idx, out_dtype=out_dtype, zeros=zeros)
 
 
 # ------------------------------------------------------------------ error measures
@@ -366,7 +499,8 @@ def recon_mse_trace(H_undamped: np.ndarray, n_tok: int, W: np.ndarray, What: np.
 # ------------------------------------------------------------------ OBS reference (tiny sizes)
 
 def direct_obs(W: np.ndarray, H: np.ndarray, bits: int, group_size: int = 0,
-               scales_in: Optional[np.ndarray] = None) -> dict:
+               scales_in: Optional[np.ndarray] = None, sym: bool = True,
+               zeros_in: Optional[np.ndarray] = None) -> dict:
     """Sequential OBS in fixed left-to-right order, with no Cholesky factor at all.
 
     After column j is fixed at what_j, the still-free columns F = j+1.. move by the
@@ -377,29 +511,34 @@ def direct_obs(W: np.ndarray, H: np.ndarray, bits: int, group_size: int = 0,
     m, n = W.shape
     g = _group_len(n, group_size)
     ng = n_groups(n, group_size)
-    scales = np.zeros((m, ng), dtype=np.float16) if scales_in is None else np.array(scales_in, dtype=np.float16).reshape(m, ng)
-    codes = np.zeros((m, n), dtype=np.int8)
+    scales, zeros = _init_params(m, ng, scales_in, zeros_in, sym)
+    codes = np.zeros((m, n), dtype=np.int8 if sym else np.uint8)
     Wc = W.copy()
     for j in range(n):
         G = j // g
         if j % g == 0 and scales_in is None:
-            scales[:, G] = group_scales_from_absmax(np.max(np.abs(Wc[:, j:j + g]), axis=1), bits)
-        q = quantize_codes(Wc[:, j], scales[:, G], bits)
+            sG, zG = _group_params(Wc[:, j:j + g], bits, sym)
+            scales[:, G] = sG
+            if not sym:
+                zeros[:, G] = zG
+        zc = None if sym else zeros[:, G]
+        q = _codes(Wc[:, j], scales[:, G], zc, bits, sym)
         codes[:, j] = q
-        delta = scales[:, G].astype(np.float64) * q - Wc[:, j]
+        delta = _value(scales[:, G], zc, q) - Wc[:, j]
         Wc[:, j] += delta
         if j + 1 < n:
             F = slice(j + 1, n)
             step = np.linalg.solve(H[F, F], H[F, j])
             Wc[:, F] -= np.outer(delta, step)
-    What = dequant(codes, scales, group_size, out_dtype=np.float64)
-    return {"codes": codes, "scales": scales, "What": What}
+    What = dequant(codes, scales, group_size, out_dtype=np.float64, zeros=zeros)
+    return {"codes": codes, "scales": scales, "zeros": zeros, "What": What}
 
 
 # ------------------------------------------------------------------ whole layer
 
 def quantize_layer(W: np.ndarray, x_tiles, bits: int = 4, group_size: int = 128, block_size: int = 128,
-                   damp: float = 0.01, act_order: bool = False, perm: Optional[np.ndarray] = None) -> dict:
+                   damp: float = 0.01, act_order: bool = False, perm: Optional[np.ndarray] = None,
+                   sym: bool = True) -> dict:
     """Hessian -> damping -> [act-order] -> U -> GPTQ, plus RTN and both MSEs on the same X.
 
     ``perm``: with act_order, a processing order decided elsewhere (the order is an integer
@@ -417,8 +556,8 @@ def quantize_layer(W: np.ndarray, x_tiles, bits: int = 4, group_size: int = 128,
         perm = None
     Hp = Hd[np.ix_(perm, perm)] if perm is not None else Hd
     U = chol_inverse_upper(Hp)
-    res = gptq(W, U, bits, group_size, block_size, perm=perm)
-    r = rtn(W, bits, group_size)
+    res = gptq(W, U, bits, group_size, block_size, perm=perm, sym=sym)
+    r = rtn(W, bits, group_size, sym=sym)
     res.update({
         "H": H, "lambda": lam, "perm": perm, "U": U,
         "rtn": r,

@@ -99,3 +99,79 @@ def test_scale_rule_mistakes_change_codes(bad):
         s = a / 7.5                                   # 16 levels instead of 15
         wrong = O.rtn(W, 4, 128, scales_in=s.astype(np.float16))
         assert not np.array_equal(wrong["codes"], good["codes"])
+
+
+# ---------------------------------------------------------------------------------- zero-points
+import oracle.pwq_oracle as OM
+import test_oracle_pins as P
+
+
+def _wrong_zero_sign(lo, hi, bits):
+    s, z = _good_scale_zero(lo, hi, bits)
+    top = (1 << bits) - 1
+    lo32 = np.asarray(lo, dtype=np.float64).astype(np.float32).astype(np.float64)
+    safe = np.where(s.astype(np.float64) > 0, s.astype(np.float64), 1.0)
+    return s, np.clip(np.rint(lo32 / safe), 0, top).astype(np.uint16)
+
+
+def _wrong_zero_floor(lo, hi, bits):
+    s, _ = _good_scale_zero(lo, hi, bits)
+    lo32 = np.asarray(lo, dtype=np.float64).astype(np.float32).astype(np.float64)
+    safe = np.where(s.astype(np.float64) > 0, s.astype(np.float64), 1.0)
+    z = np.where(s.astype(np.float64) > 0, np.floor(-lo32 / safe), 0)
+    return s, np.clip(z, 0, (1 << bits) - 1).astype(np.uint16)
+
+
+def _wrong_levels(lo, hi, bits):
+    """2^b levels spaced by range / 2^b (one level too many)."""
+    span = (np.asarray(hi, np.float64) - np.asarray(lo, np.float64)).astype(np.float32)
+    s = (span / np.float32(1 << bits)).astype(np.float16)
+    sf = s.astype(np.float64)
+    z = np.where(sf > 0, np.rint(-np.asarray(lo, np.float64) / np.where(sf > 0, sf, 1)), 0)
+    return s, np.clip(z, 0, (1 << bits) - 1).astype(np.uint16)
+
+
+def _wrong_codes_no_zero(w, s16, z, bits):
+    return _good_codes(w, s16, np.zeros_like(np.asarray(z)), bits)
+
+
+_good_scale_zero = OM.asym_scale_zero
+_good_codes = OM.quantize_codes_asym
+
+
+@pytest.mark.parametrize("target,bad", [
+    ("asym_scale_zero", _wrong_zero_sign),
+    ("asym_scale_zero", _wrong_zero_floor),
+    ("asym_scale_zero", _wrong_levels),
+    ("quantize_codes_asym", _wrong_codes_no_zero),
+])
+def test_zero_point_mistakes_fail_a_pin(monkeypatch, target, bad):
+    monkeypatch.setattr(OM, target, bad)
+    failed = 0
+    for pin in (P.test_asym_worked_group, P.test_asym_scale_zero_closed_form):
+        try:
+            if pin is P.test_asym_scale_zero_closed_form and target != "asym_scale_zero":
+                continue
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1
+
+
+def test_dequant_without_zero_fails_nearest_level_pin(monkeypatch):
+    def bad_dequant(codes, scales, group_size, g_idx=None, out_dtype=np.float64, zeros=None):
+        return _good_dequant(codes, scales, group_size, g_idx=g_idx, out_dtype=out_dtype, zeros=None)
+    _good_dequant = OM.dequant
+    monkeypatch.setattr(OM, "dequant", bad_dequant)
+    with pytest.raises(AssertionError):
+        P.test_asym_worked_group()
+
+
+def test_offset_nibble_fails_unsigned_pack_pin(monkeypatch):
+    """Zero-point codes packed with the symmetric layout's +8 offset."""
+    def bad_pack(c):
+        u = ((np.asarray(c, np.int16) + 8) & 15).astype(np.uint8)
+        return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    monkeypatch.setattr(O, "pack_uint4", bad_pack)
+    with pytest.raises(AssertionError):
+        P.test_asym_pack_layout_and_storage()

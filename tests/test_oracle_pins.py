@@ -418,3 +418,138 @@ def test_dequant_rounds_once():
         assert Fraction(float(got)) == _rne_to_precision(ex, 11, -14)
     out32 = O.dequant(codes, s, 0, out_dtype=np.float32)
     assert [Fraction(float(v)) for v in out32[0]] == exact
+
+
+# ---------------------------------------------------------------------------------- f1: zero-points
+# [MQM] "Affine Quantization" / "Group-wise Quantization": code = round(w / S) + Z and
+# w ~ S (code - Z), one (S, Z) per row and group; [GPTQ-P] "Group Quantization": a 16-bit
+# zero per group beside the 16-bit scale.
+
+def _asym_closed_form(lo, hi, bits=4):
+    """Scale and zero in exact rational arithmetic: S = fp16(fp32(fp32(hi - lo) / top)),
+    Z = nearest integer to -lo / S (ties to even), clamped to [0, top]."""
+    top = (1 << bits) - 1
+    span = _rne_to_precision(Fraction(float(np.float32(hi))) - Fraction(float(np.float32(lo))), 24, -126)
+    s = _rne_to_precision(_rne_to_precision(span / top, 24, -126), 11, -14)
+    if s == 0:
+        return s, 0
+    q = -Fraction(float(np.float32(lo))) / s
+    f = q.numerator // q.denominator
+    rem = q - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return s, min(max(f, 0), top)
+
+
+def test_asym_worked_group():
+    # range [-1, 2]: S = fp16(3 / 15) = 0.199951171875; -lo / S = 5.0012.. -> Z = 5;
+    # -1 / S = -5.0012 -> -5 + 5 = 0; -0.5 / S = -2.5006 -> -3 + 5 = 2; 0 -> 5;
+    # 2 / S = 10.0024 -> 10 + 5 = 15.
+    W = np.array([[-1.0, -0.5, 0.0, 2.0]], dtype=np.float32)
+    r = O.rtn(W, 4, 4, sym=False)
+    assert float(r["scales"][0, 0]) == 0.199951171875
+    assert r["zeros"].tolist() == [[5]]
+    assert r["codes"].tolist() == [[0, 2, 5, 15]]
+    assert r["What"][0, 2] == 0.0
+    # range [-7.5, 7.5]: S = 1 exactly, -lo / S = 7.5 is a tie -> Z = 8 (even);
+    # 0.5 -> 0 + 8; -7.5 -> -8 + 8 = 0; 7.5 -> 8 + 8 = 16, clamped to 15; 2.5 -> 2 + 8
+    W2 = np.array([[-7.5, 7.5, 0.5, 2.5]], dtype=np.float32)
+    r2 = O.rtn(W2, 4, 0, sym=False)
+    assert float(r2["scales"][0, 0]) == 1.0 and r2["zeros"].tolist() == [[8]]
+    assert r2["codes"].tolist() == [[0, 15, 8, 10]]
+    # one-signed groups: lo = 0 gives Z = 0; hi = 0 gives Z = top; an all-zero group S = 0
+    W3 = np.array([[0.0, 1.5, 3.0, 0.1, -3.0, -1.5, 0.0, -0.1, 0, 0, 0, 0]], dtype=np.float32)
+    r3 = O.rtn(W3, 4, 4, sym=False)
+    assert r3["zeros"].tolist() == [[0, 15, 0]]
+    assert float(r3["scales"][0, 2]) == 0.0 and not r3["codes"][0, 8:].any()
+    # S = fp16(0.2) = 0.199951171875 for both: 1.5 / S = 7.5018 -> 8, 0.1 / S = 0.50012 -> 1;
+    # -3 / S = -15.004 -> -15 + 15 = 0, -1.5 / S -> -8 + 15 = 7, -0.1 / S -> -1 + 15 = 14
+    assert r3["codes"][0, :4].tolist() == [0, 8, 15, 1]
+    assert r3["codes"][0, 4:8].tolist() == [0, 7, 15, 14]
+
+
+def test_asym_scale_zero_closed_form():
+    rng = np.random.default_rng(30)
+    lo = np.minimum(rng.normal(0, 0.05, size=300), 0).astype(np.float32)
+    hi = np.maximum(rng.normal(0, 0.05, size=300), 0).astype(np.float32)
+    lo[:5] = 0.0
+    hi[5:10] = 0.0
+    lo[10], hi[10] = 0.0, 0.0
+    for bits in (2, 3, 4, 8):
+        s, z = O.asym_scale_zero(lo, hi, bits)
+        for i in range(300):
+            ws, wz = _asym_closed_form(float(lo[i]), float(hi[i]), bits)
+            assert Fraction(float(s[i])) == ws and int(z[i]) == wz
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 30), st.integers(1, 30), st.sampled_from([0, 4, 8]), st.sampled_from([2, 3, 4]),
+       st.integers(0, 2**31 - 1))
+def test_asym_nearest_level_bound_and_pack(m, half_n, gs, bits, seed):
+    """Every code is a nearest one of the group's 2^b levels S (q - Z), q = 0 .. top (brute
+    force); real 0 is a level, so a 0 weight comes back exactly; an unclamped weight is
+    within S / 2; the codes survive unsigned packing."""
+    n = 2 * half_n
+    if gs and n % gs:
+        n = gs * max(1, n // gs)
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_t(3, size=(m, n)) * 0.02 + rng.normal(0, 0.01, size=(m, 1))).astype(np.float32)
+    W[rng.random((m, n)) < 0.05] = 0.0
+    r = O.rtn(W, bits, gs, sym=False)
+    top = (1 << bits) - 1
+    gi = np.zeros(n, int) if gs == 0 else np.arange(n) // gs
+    s = r["scales"].astype(np.float64)[:, gi]
+    z = r["zeros"].astype(np.float64)[:, gi]
+    w = W.astype(np.float64)
+    levels = s[..., None] * (np.arange(top + 1)[None, None, :] - z[..., None])
+    dist = np.abs(w[..., None] - levels)
+    got = np.take_along_axis(dist, r["codes"].astype(np.int64)[..., None], axis=2)[..., 0]
+    assert np.all(got <= dist.min(axis=2))
+    assert np.all(r["What"][W == 0] == 0)
+    inner = (r["codes"] > 0) & (r["codes"] < top)
+    assert np.all(np.abs(w - r["What"])[inner] <= s[inner] / 2)
+    assert np.all(np.abs(w - r["What"]) <= s * (0.5 + 2.0 ** -7))
+    if bits == 4:
+        assert np.array_equal(O.unpack_uint4(O.pack_uint4(r["codes"]), n), r["codes"])
+
+
+def test_asym_pack_layout_and_storage():
+    codes = np.array([[0, 15, 5, 10, 1, 8]], dtype=np.uint8)
+    assert O.pack_uint4(codes).tolist() == [[0xF0, 0xA5, 0x81]]       # nibble = code, even low
+    g = read_golden("gptq_page_storage.txt")
+    gs = int(g["group_size"])
+    m, n = 32, 4 * gs
+    assert O.storage_bytes(m, n, gs, zero_point=True) * 8 / (m * n) == g["bits_per_weight_with_zero_point"]
+
+
+@pytest.mark.parametrize("gs", [0, 128])
+def test_asym_diagonal_hessian_gptq_equals_rtn(gs):
+    rng = np.random.default_rng(31)
+    n, m = 256, 48
+    W = (rng.normal(0, 0.02, size=(m, n)) + 0.01).astype(np.float32)
+    X = np.diag(rng.uniform(0.5, 3.0, size=n))
+    Hd, _ = O.damp_hessian(O.hessian(X), 0.01)
+    res = O.gptq(W, O.chol_inverse_upper(Hd), 4, gs, 128, sym=False)
+    r = O.rtn(W, 4, gs, sym=False)
+    assert np.array_equal(res["codes"], r["codes"])
+    assert np.array_equal(res["zeros"], r["zeros"])
+    assert np.array_equal(res["scales"].view(np.uint16), r["scales"].view(np.uint16))
+
+
+@pytest.mark.parametrize("gs", [0, 8])
+def test_asym_u_form_loop_equals_direct_obs(gs):
+    """The factor form with zero-points against sequential OBS solves (no factor at all)."""
+    rng = np.random.default_rng(32)
+    n, m = 24, 60
+    X = ar1_x(rng, 96, n, 0.8)
+    W = rng.normal(0.005, 0.02, size=(m, n))
+    Hd, _ = O.damp_hessian(O.hessian(X), 0.01)
+    ref = O.direct_obs(W, Hd, 4, gs, sym=False)
+    U = O.chol_inverse_upper(Hd)
+    for B in (1, 5, 128):
+        res = O.gptq(W, U, 4, gs, B, sym=False)
+        assert np.array_equal(res["codes"], ref["codes"])
+        assert np.array_equal(res["zeros"], ref["zeros"])
+        assert np.allclose(res["scales"].astype(np.float64), ref["scales"].astype(np.float64), rtol=0, atol=0)
+    un = O.gptq_unblocked(W, U, 4, gs, sym=False)
+    assert np.array_equal(un["codes"], ref["codes"])
