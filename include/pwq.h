@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PWQ_ABI_VERSION 1
+#define PWQ_ABI_VERSION 2
 
 typedef enum pwq_status {
     PWQ_OK = 0,
@@ -60,7 +60,8 @@ typedef enum pwq_dtype {
 
 /* Quantizer settings, the knobs of [GPTQ-P] "Running GPTQ with AutoGPTQ" (bits,
  * group_size, desc_act) plus the lazy-batch width of [GPTQ-P] "The GPTQ Algorithm".
- * Symmetric only: codes in [-(2^(bits-1)-1), 2^(bits-1)-1], no zero-point.
+ * The plain calls are symmetric (sym=True there): codes in [-(2^(bits-1)-1), 2^(bits-1)-1],
+ * no zero-point.  The *_zp calls are the zero-point form (see "Zero-point form" below).
  *   bits        2..8
  *   group_size  0 = one scale per output row ([GPT2-RE]); else an even number >= 2 of
  *               consecutive input columns sharing one scale ([MQM] "Group-wise
@@ -195,6 +196,54 @@ pwq_status pwq_recon_mse(const void* X, int x_dtype, int64_t n_tok, int64_t d_in
                          const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
                          int64_t d_out, int32_t bits, int32_t group_size,
                          double* mse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ Zero-point form
+ * The affine quantizer of [MQM] "Affine Quantization" and "Group-wise Quantization": per
+ * row and group a float16 scale S and a zero Z, code = round(w / S) + Z and value
+ * S (code - Z); [GPTQ-P] "Group Quantization" stores Z in 16 bits beside S (4 + 32 / g
+ * bits per weight).  A group's range [lo, hi] = [min(w, 0), max(w, 0)] (so that real 0 is
+ * a level) is mapped onto the codes 0 .. top = 2^bits - 1:
+ *   S = fp16(fp32(hi - lo) / top)      (one float32 subtraction and division, one rounding)
+ *   Z = nearest integer to -lo / S (exact quotient, ties to even), clamped to [0, top];
+ *       S = 0 gives Z = 0
+ *   code = nearest integer to w / S (exact quotient, ties to even) plus Z, clamped to
+ *       [0, top]; S = 0 gives code 0.
+ * Codes are unsigned bytes (uint8_t); INT4 nibbles hold the code itself (no offset), even
+ * column in the low nibble.  Zeros travel as uint16_t, d_out x n_groups like the scales.
+ * Fixed quantizers are given as scales_in and zeros_in together (both or neither); zeros_in
+ * entries above top are taken as top (and written so to zeros_out).  The decoding calls
+ * (dequant, MSE) expect zeros in 0 .. top, as the quantizing calls write them.
+ * Everything else - arguments, checks, workspaces, layouts - is that of the plain call of
+ * the same name, and the workspace size queries are shared.
+ *
+ * GPTQ: at a group's first column S and Z come from the current values of the group's
+ * columns, where the plain call takes its absmax; the error of column j is
+ * e = (w - S (code - Z)) / U_jj.  zeros_out is required. */
+pwq_status pwq_gptq_quantize_layer_zp(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
+                                      const float* U, const int32_t* info, const pwq_params* params,
+                                      const int32_t* perm, const uint16_t* scales_in, const uint16_t* zeros_in,
+                                      uint8_t* codes, uint8_t* packed, uint16_t* scales_out, uint16_t* zeros_out,
+                                      int32_t* g_idx, void* ws, size_t ws_bytes, void* stream);
+
+/* RTN with zero-points: S and Z from the original W per row or group.  zeros_out required. */
+pwq_status pwq_rtn_quantize_zp(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
+                               int32_t bits, int32_t group_size, const uint16_t* scales_in, const uint16_t* zeros_in,
+                               uint8_t* codes, uint8_t* packed, uint16_t* scales_out, uint16_t* zeros_out,
+                               void* stream);
+
+/* What[r, c] = S[r, group(c)] * (code[r, c] - Z[r, group(c)]), exact in float32 (for zeros
+ * in 0 .. top), rounded once to out_dtype.  zeros required. */
+pwq_status pwq_dequant_zp(const uint8_t* packed, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                          const int32_t* g_idx, int64_t d_out, int64_t d_in, int32_t bits, int32_t group_size,
+                          void* W_out, int out_dtype, void* stream);
+
+/* pwq_recon_mse with What decoded as in pwq_dequant_zp.  zeros required; the workspace is
+ * pwq_recon_mse_workspace_size(n_tok, d_in, d_out) bytes. */
+pwq_status pwq_recon_mse_zp(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                            const void* W, int w_dtype, int64_t ldw,
+                            const uint8_t* packed, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                            const int32_t* g_idx, int64_t d_out, int32_t bits, int32_t group_size,
+                            double* mse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

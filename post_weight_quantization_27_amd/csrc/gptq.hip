@@ -2,7 +2,11 @@
 // processing order, blocks of B, per column quantize / scaled error / in-block rank-1
 // update, then one trailing product per block.  Scales follow "Group Quantization" of the
 // same page (one float16 scale per row and group) and the per-row quantizer of
-// "GPT-2 Quantization Reconstruction Error".
+// "GPT-2 Quantization Reconstruction Error".  The zero-point form ("Model Quantization
+// Mechanics", "Affine Quantization") takes each group's scale and zero from the range
+// [min(w, 0), max(w, 0)] of the same current values; its codes are the clamped quotient
+// round(w / S) in [-Z, 2^b - 1 - Z] plus Z, so the per-column step is the symmetric one with
+// other clamp bounds (symmetric: +-qmax, Z = 0) and one add for the stored code.
 //
 // Kernels per layer:
 //   prologue : float32 working copy Wf of W (columns permuted for act-order), per-row
@@ -43,25 +47,30 @@ inline int lazy_cols(int group_size, int block_size) {
     return group_size <= 2048 ? group_size : block_size;
 }
 
+// zero-point form (zeros_out given): top = 2^bits - 1; fixed zeros are copied clamped to top
 template <int DT, bool PERM>
 __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restrict__ W, int64_t ldw, int64_t m, int64_t n,
                                                             const int32_t* __restrict__ perm, float* __restrict__ Wf,
                                                             int row_scales, int qmax, const uint16_t* __restrict__ scales_in,
                                                             uint16_t* __restrict__ scales_out, int64_t ng,
-                                                            const int32_t* __restrict__ info) {
+                                                            const int32_t* __restrict__ info, int top,
+                                                            const uint16_t* __restrict__ zeros_in,
+                                                            uint16_t* __restrict__ zeros_out) {
     if (*info) return;
     typedef typename Elem<DT>::T T;
     __shared__ float row[PERM ? PERM_MAX_N : 1];
-    __shared__ float red[4];
+    __shared__ float red[8];
     const int64_t r = blockIdx.x;
     const T* src = (const T*)W + r * ldw;
     float* dst = Wf + r * n;
-    float amax = 0.f;
+    float amax = 0.f, hi = 0.f, nlo = 0.f;    // max |w|; max(w, 0), max(-w, 0)
     if (PERM) {
         for (int64_t j = threadIdx.x; j < n; j += 256) {
             const float v = Elem<DT>::get(src, j);
             row[j] = v;
             amax = fmaxf(amax, fabsf(v));
+            hi = fmaxf(hi, v);
+            nlo = fmaxf(nlo, -v);
         }
         __syncthreads();
         for (int64_t p = threadIdx.x; p < n; p += 256) dst[p] = row[perm[p]];
@@ -70,17 +79,34 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
             const float v = Elem<DT>::get(src, j);
             dst[j] = v;
             amax = fmaxf(amax, fabsf(v));
+            hi = fmaxf(hi, v);
+            nlo = fmaxf(nlo, -v);
         }
     }
     if (scales_in) {
         for (int64_t g = threadIdx.x; g < ng; g += 256) scales_out[r * ng + g] = scales_in[r * ng + g];
+        if (zeros_out)
+            for (int64_t g = threadIdx.x; g < ng; g += 256) zeros_out[r * ng + g] = (uint16_t)min((int)zeros_in[r * ng + g], top);
     } else if (row_scales) {
-        amax = wave_max(amax);
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+        if (zeros_out) {
+            hi = wave_max(hi);
+            nlo = wave_max(nlo);
+            if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = hi; red[4 + (threadIdx.x >> 6)] = nlo; }
+        } else {
+            amax = wave_max(amax);
+            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+        }
         __syncthreads();
         if (threadIdx.x == 0) {
             const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-            scales_out[r] = scale_bits_from_absmax(a, qmax);
+            if (zeros_out) {
+                const float nl = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+                const uint16_t sb = zp_scale_bits(nl, a, top);
+                scales_out[r] = sb;
+                zeros_out[r] = (uint16_t)zp_zero(nl, f16_bits_to_f32(sb), (float)top);
+            } else {
+                scales_out[r] = scale_bits_from_absmax(a, qmax);
+            }
         }
     }
 }
@@ -122,7 +148,23 @@ struct BlockArgs {
     int err_ld;
     int pend;                // row kernels: columns of the super-block before this block, whose
     const float* err_sb;     // update the kernel applies itself (errors at err_sb, ld err_ld)
+    uint16_t* zeros;         // zero-point form: d_out x ng zeros (like scales); NULL if symmetric
+    int top;                 // zero-point form: largest code 2^bits - 1
+    int nib_off;             // INT4 nibble = code + nib_off (8 symmetric, 0 zero-point)
 };
+
+// Clamp bounds of the rounded quotient and the offset of the stored code for a group with
+// zero z: symmetric [-qmax, qmax] and 0, zero-point [-z, top - z] and z.
+struct QBounds {
+    float lo, hi, z;
+};
+__device__ __forceinline__ QBounds qbounds(const BlockArgs& a, float z) {
+    if (a.zeros) return QBounds{-z, (float)a.top - z, z};
+    return QBounds{-(float)a.qmax, (float)a.qmax, 0.f};
+}
+__device__ __forceinline__ float stored_zero(const BlockArgs& a, int64_t idx) {
+    return a.zeros ? (float)a.zeros[idx] : 0.f;
+}
 
 // The panel's diagonal block of U (zero outside bw x bw), read as float4 rows with every
 // load of a thread in flight before any is used: element e4 = tid + q NT of the PW x PW / 4
@@ -199,15 +241,18 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
     for (int i = 0; i < NC; ++i) w[i] = (live && 4 * i + p < a.bw) ? wrow[a.b0 + 4 * i + p] : 0.f;
 
     const int g = a.group_size;
-    float s = 0.f;
+    float s = 0.f, z = 0.f;
     if (g == 0) {
         s = live ? f16_bits_to_f32(a.scales[r]) : 0.f;
+        z = live ? stored_zero(a, r) : 0.f;
     } else if (!a.gsmall && !a.gstart0) {
         // a group wider than the panel that began in an earlier panel: its scale was fixed
         // (and stored) when the loop reached the group's first column
         s = live ? f16_bits_to_f32(a.scales[r * a.ng + a.gbase]) : 0.f;
+        z = live ? stored_zero(a, r * a.ng + a.gbase) : 0.f;
     }
     float rs = s > 0.f ? 1.0f / s : 0.f;
+    QBounds qb_ = qbounds(a, z);
     float eown[NC];
     uint32_t qb[(NC + 3) / 4];
 #pragma unroll
@@ -222,8 +267,6 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
     // updates; the pins keep the compiler from sinking update chains to their last use
     // (which would keep every step's e and U values live at once).
     const bool own[4] = {p == 0, p == 1, p == 2, p == 3};
-    const float qmf = (float)a.qmax;
-    const float qlim = qmf + 1.f;
 #pragma unroll
     for (int jw = 0; jw < PW; jw += 4) {
         // this lane's entries of U rows jw .. jw+3 from register jw/4 on (the aligned group
@@ -251,23 +294,41 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
                 uint16_t sb;
                 if (a.fixed_scales) {
                     sb = live ? a.scales[r * a.ng + G] : (uint16_t)0;
+                    z = live ? stored_zero(a, r * a.ng + G) : 0.f;
                 } else {
+                    // symmetric: v = max |w|; zero-point: v = max(w, 0), nl = max(-w, 0)
+                    const bool zp = a.zeros != nullptr;
                     const int ilim = a.gsmall ? (j + g) / 4 : NC;
-                    float v = 0.f;
+                    float v = 0.f, nl = 0.f;
 #pragma unroll
                     for (int i = j / 4; i < NC; ++i)
-                        if (i < ilim) v = fmaxf(v, fabsf(w[i]));
+                        if (i < ilim) {
+                            v = fmaxf(v, zp ? w[i] : fabsf(w[i]));
+                            nl = fmaxf(nl, -w[i]);
+                        }
                     if (!a.gsmall && live) {
                         const int64_t col = a.b0;
                         const int64_t gend = col + g < a.n ? col + g : a.n;
-                        for (int64_t c = a.b0 + a.bw + p; c < gend; c += 4) v = fmaxf(v, fabsf(wrow[c]));
+                        for (int64_t c = a.b0 + a.bw + p; c < gend; c += 4) {
+                            const float x = wrow[c];
+                            v = fmaxf(v, zp ? x : fabsf(x));
+                            nl = fmaxf(nl, -x);
+                        }
                     }
                     v = quad_max(v);
-                    sb = scale_bits_from_absmax(v, a.qmax);
+                    if (zp) {
+                        nl = quad_max(nl);
+                        sb = zp_scale_bits(nl, v, a.top);
+                        z = zp_zero(nl, f16_bits_to_f32(sb), (float)a.top);
+                        if (p == 0 && live) a.zeros[r * a.ng + G] = (uint16_t)z;
+                    } else {
+                        sb = scale_bits_from_absmax(v, a.qmax);
+                    }
                     if (p == 0 && live) a.scales[r * a.ng + G] = sb;
                 }
                 s = f16_bits_to_f32(sb);
                 rs = s > 0.f ? 1.0f / s : 0.f;
+                qb_ = qbounds(a, z);
             }
             // column j: owner lane j & 3 (= t), register j >> 2, broadcast inside the quad
             const float wj = quad_bcast_of(w[j >> 2], t);
@@ -275,17 +336,18 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
             // k = rint(w * rcp(s)) is within one of it, and the signs of the exact residuals
             // w - (k +- 1/2) s (one rounding each in fma) move it to the right integer.
             // s = 0 (an all-zero or underflowed group) gives code 0.
-            const float kf = fminf(fmaxf(rintf(wj * rs), -qlim), qlim);
+            // The quotient is clamped to [lo, hi] (symmetric +-qmax; zero-point [-z, top - z])
+            // and the stored code is it plus z.
+            const float kf = fminf(fmaxf(rintf(wj * rs), qb_.lo - 1.f), qb_.hi + 1.f);
             const float hi = fmaf(-(kf + 0.5f), s, wj);
             const float lo = fmaf(-(kf - 0.5f), s, wj);
             const int ki = (int)kf;
             const int odd = ki & 1;
             const int up = (hi > 0.f) | ((hi == 0.f) & odd);
             const int dn = (lo < 0.f) | ((lo == 0.f) & odd);
-            int q = ki + up - dn;
-            q = q > a.qmax ? a.qmax : (q < -a.qmax ? -a.qmax : q);
-            q = s > 0.f ? q : 0;
-            const float e = (wj - s * (float)q) * dj[t];
+            const float qf = s > 0.f ? __builtin_amdgcn_fmed3f((float)(ki + up - dn), qb_.lo, qb_.hi) : 0.f;
+            const float e = (wj - s * qf) * dj[t];
+            const int q = s > 0.f ? (int)(qf + qb_.z) : 0;       // s = 0: code 0 whatever the zero
             // the owner lane of column j keeps its error and code (selects, no branches)
             eown[j >> 2] = own[t] ? e : eown[j >> 2];
             qb[j >> 4] = own[t] ? (qb[j >> 4] | ((uint32_t)(q & 0xff) << (8 * ((j >> 2) & 3)))) : qb[j >> 4];
@@ -326,28 +388,11 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
                 // byte k of the panel holds columns 2k (low nibble) and 2k+1 (high nibble)
                 uint8_t* prow = a.packed + r * (a.n / 2) + a.b0 / 2;
                 for (int c = 0; c < PER; c += 2)
-                    if (c0 + c < a.bw) prow[(c0 + c) / 2] = (uint8_t)(((src[c] + 8) & 15) | (((src[c + 1] + 8) & 15) << 4));
+                    if (c0 + c < a.bw)
+                        prow[(c0 + c) / 2] = (uint8_t)(((src[c] + a.nib_off) & 15) | (((src[c + 1] + a.nib_off) & 15) << 4));
             }
         }
     }
-}
-
-// Nearest integer to the exact quotient w / s, ties to even, clamped to +-qmax, without
-// branches: k = rint(w * rcp(s)) is within one of it, and the signs of the exact residuals
-// w - (k +- 1/2) s (one rounding each in fma) move it to the right integer.  s = 0 (an
-// all-zero or underflowed group) gives 0.
-__device__ __forceinline__ int quant_code_nb(float w, float s, float rs, int qmax) {
-    const float qlim = (float)(qmax + 1);
-    const float kf = fminf(fmaxf(rintf(w * rs), -qlim), qlim);
-    const float hi = fmaf(-(kf + 0.5f), s, w);
-    const float lo = fmaf(-(kf - 0.5f), s, w);
-    const int ki = (int)kf;
-    const int odd = ki & 1;
-    const int up = (hi > 0.f) | ((hi == 0.f) & odd);
-    const int dn = (lo < 0.f) | ((lo == 0.f) & odd);
-    int q = ki + up - dn;
-    q = q > qmax ? qmax : (q < -qmax ? -qmax : q);
-    return s > 0.f ? q : 0;
 }
 
 // a wave-uniform value, marked as such (SGPR), so branches on it are uniform ones
@@ -446,12 +491,17 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
     if (live) {
         const float* wrow = a.Wf + r * a.n;
         const int g = a.group_size;
-        float s = 0.f;
-        if (g == 0) s = f16_bits_to_f32(a.scales[r]);
-        else if (!a.gsmall && !a.gstart0) s = f16_bits_to_f32(a.scales[r * a.ng + a.gbase]);
+        float s = 0.f, z = 0.f;
+        if (g == 0) {
+            s = f16_bits_to_f32(a.scales[r]);
+            z = stored_zero(a, r);
+        } else if (!a.gsmall && !a.gstart0) {
+            s = f16_bits_to_f32(a.scales[r * a.ng + a.gbase]);
+            z = stored_zero(a, r * a.ng + a.gbase);
+        }
         s = uniform_f(s);
         float rs = uniform_f(s > 0.f ? 1.0f / s : 0.f);
-        const float qmf = (float)a.qmax;
+        QBounds qb_ = qbounds(a, uniform_f(z));
 
         float u[NS], un[NS];
 #pragma unroll
@@ -467,26 +517,45 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
                 // and, for a group wider than the panel, the columns right of it)
                 const int64_t G = a.gbase + (a.gsmall ? j / g : 0);
                 uint16_t sb;
+                float zg = 0.f;
                 if (a.fixed_scales) {
                     sb = a.scales[r * a.ng + G];
+                    zg = stored_zero(a, r * a.ng + G);
                 } else {
+                    // symmetric: v = max |w|; zero-point: v = max(w, 0), nl = max(-w, 0)
+                    const bool zp = a.zeros != nullptr;
                     const int cend = a.gsmall ? j + g : PW;
-                    float v = 0.f;
+                    float v = 0.f, nl = 0.f;
 #pragma unroll
                     for (int k = 0; k < NS; ++k) {
                         const int c = lane + 64 * k;
-                        if (c >= j && c < cend) v = fmaxf(v, fabsf(w[k]));
+                        if (c >= j && c < cend) {
+                            v = fmaxf(v, zp ? w[k] : fabsf(w[k]));
+                            nl = fmaxf(nl, -w[k]);
+                        }
                     }
                     if (!a.gsmall) {
                         const int64_t gend = a.b0 + g < a.n ? a.b0 + g : a.n;
-                        for (int64_t c = a.b0 + a.bw + lane; c < gend; c += 64) v = fmaxf(v, fabsf(wrow[c]));
+                        for (int64_t c = a.b0 + a.bw + lane; c < gend; c += 64) {
+                            const float x = wrow[c];
+                            v = fmaxf(v, zp ? x : fabsf(x));
+                            nl = fmaxf(nl, -x);
+                        }
                     }
                     v = wave_max(v);
-                    sb = scale_bits_from_absmax(v, a.qmax);
+                    if (zp) {
+                        nl = wave_max(nl);
+                        sb = zp_scale_bits(nl, v, a.top);
+                        zg = zp_zero(nl, f16_bits_to_f32(sb), (float)a.top);
+                        if (lane == 0) a.zeros[r * a.ng + G] = (uint16_t)zg;
+                    } else {
+                        sb = scale_bits_from_absmax(v, a.qmax);
+                    }
                     if (lane == 0) a.scales[r * a.ng + G] = sb;
                 }
                 s = uniform_f(f16_bits_to_f32(sb));
                 rs = uniform_f(s > 0.f ? 1.0f / s : 0.f);
+                qb_ = qbounds(a, uniform_f(zg));
             }
             // everything from here to e is the same in every lane (wj, s, rs, dj are
             // wave-uniform), so the rare exact-rounding branch is a uniform one
@@ -494,12 +563,14 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
             const float dj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dreg[j >> 6]), j & 63));
             // branch-free exact rounding: no uniform branch (and no refilled instruction
             // buffer) on the column-to-column chain
-            const float qf = s > 0.f ? quant_code_self(wj, s, rs, qmf) : 0.f;
+            // (the quotient clamped to [lo, hi]; the stored code adds the zero, and s = 0 gives
+            // code 0 whatever the zero)
+            const float qf = s > 0.f ? round_quot_clamp(wj, s, rs, qb_.lo, qb_.hi) : 0.f;
             const float e = (wj - s * qf) * dj;
             // e and the code are wave-uniform: every lane stores the same value to the same
             // LDS word (no lane select), and each lane reads its own columns back at the end
             esh[wave][j] = e;
-            qsh[wave][j] = (int8_t)qf;
+            qsh[wave][j] = (int8_t)(s > 0.f ? (int)(qf + qb_.z) : 0);
             // columns left of j (and j itself) are final: only registers holding columns
             // >= j need the update, and U is 0 left of j anyway
 #pragma unroll
@@ -540,7 +611,8 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
                 hi = lane < 32 ? hi0 : hi1;
             }
             if (2 * lane < a.bw && 2 * lane < PW)
-                a.packed[r * (a.n / 2) + a.b0 / 2 + lane] = (uint8_t)(((lo + 8) & 15) | (((hi + 8) & 15) << 4));
+                a.packed[r * (a.n / 2) + a.b0 / 2 + lane] =
+                    (uint8_t)(((lo + a.nib_off) & 15) | (((hi + a.nib_off) & 15) << 4));
         }
     }
 }
@@ -571,7 +643,7 @@ __global__ __launch_bounds__(256) void inv_perm_kernel(const int32_t* __restrict
 // codes back to original column order (row staged in LDS) + optional nibble packing
 __global__ __launch_bounds__(256) void unpermute_codes_kernel(const int8_t* __restrict__ cp, const int32_t* __restrict__ inv,
                                                               int64_t n, int8_t* __restrict__ codes, uint8_t* __restrict__ packed,
-                                                              const int32_t* __restrict__ info) {
+                                                              int nib_off, const int32_t* __restrict__ info) {
     if (*info) return;
     __shared__ int8_t row[PERM_MAX_N];
     const int64_t r = blockIdx.x;
@@ -582,7 +654,7 @@ __global__ __launch_bounds__(256) void unpermute_codes_kernel(const int8_t* __re
     if (packed)
         for (int64_t b = threadIdx.x; b < n / 2; b += 256) {
             const int lo = row[inv[2 * b]], hi = row[inv[2 * b + 1]];
-            packed[r * (n / 2) + b] = (uint8_t)((lo + 8) | ((hi + 8) << 4));
+            packed[r * (n / 2) + b] = (uint8_t)(((lo + nib_off) & 15) | (((hi + nib_off) & 15) << 4));
         }
 }
 
@@ -630,7 +702,7 @@ GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int group_siz
 hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, const float* U, const int32_t* info,
                        int bits, int group_size, int block_size, int act_order, const int32_t* perm,
                        const uint16_t* scales_in, int8_t* codes, uint8_t* packed, uint16_t* scales_out, int32_t* g_idx,
-                       void* ws, hipStream_t s) {
+                       void* ws, hipStream_t s, const uint16_t* zeros_in, uint16_t* zeros_out) {
     if (m == 0 || n == 0) return hipSuccess;
     hipError_t e;
     const GptqWs L = gptq_ws_layout(m, n, block_size, group_size, act_order);
@@ -647,7 +719,8 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
         auto k = w_dtype == 0 ? (act_order ? gptq_prologue_kernel<0, true> : gptq_prologue_kernel<0, false>)
                               : (act_order ? gptq_prologue_kernel<1, true> : gptq_prologue_kernel<1, false>);
         hipLaunchKernelGGL(k, dim3((unsigned)m), dim3(256), 0, s, W, ldw, m, n, act_order ? perm : nullptr, Wf,
-                           (int)(group_size == 0), qmax, scales_in, scales_out, ng, info);
+                           (int)(group_size == 0), qmax, scales_in, scales_out, ng, info, (1 << bits) - 1, zeros_in,
+                           zeros_out);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -655,6 +728,7 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
     a.Wf = Wf; a.U = U; a.info = info; a.m = m; a.n = n;
     a.group_size = group_size; a.qmax = qmax; a.fixed_scales = scales_in != nullptr;
     a.scales = scales_out; a.ng = ng; a.codes = cproc; a.packed = act_order ? nullptr : packed; a.err = err;
+    a.zeros = zeros_out; a.top = (1 << bits) - 1; a.nib_off = zeros_out ? 0 : 8;
     // Few rows: one wave per row (the column chain's latency decides the time), workgroups
     // sized so the rows spread over the chip.  Many rows: four lanes per row, sixteen rows
     // per wave (issue slots decide), eight-wave workgroups.
@@ -703,7 +777,8 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
     if (act_order) {
         hipLaunchKernelGGL(inv_perm_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, perm, n, group_size, inv, g_idx);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(unpermute_codes_kernel, dim3((unsigned)m), dim3(256), 0, s, cproc, inv, n, codes, packed, info);
+        hipLaunchKernelGGL(unpermute_codes_kernel, dim3((unsigned)m), dim3(256), 0, s, cproc, inv, n, codes, packed,
+                           zeros_out ? 0 : 8, info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -4,8 +4,8 @@
 //
 //   mse = sum_{t, o} (X (W - What)^T)[t, o]^2 / (n_tok * d_out)
 //
-// Two passes.  A decode pass forms dW = W - What (What from the INT4 nibbles or int8 codes
-// and the scales, the product exact in float32) and rounds it once to bfloat16, rows padded
+// Two passes.  A decode pass forms dW = W - What (What from the INT4 nibbles or 8-bit codes
+// and the scales, and the zeros of the zero-point form, the product exact in float32) and rounds it once to bfloat16, rows padded
 // to a multiple of 64 with zeros.  The contraction X dW^T then runs on the bfloat16 MFMA
 // engine, X rounded once to bfloat16 (exact for bfloat16 X; large bfloat16 problems run on
 // the 256 x 256 direct-load engine); the epilogue squares and sums the output tile in
@@ -21,13 +21,15 @@ namespace pwq {
 
 namespace {
 
-// dW[o][c] = bf16(W[o][c] - s[o][group(c)] * code[o][c]), ld = kseg (a multiple of 64,
-// columns d_in .. kseg-1 zero).  One thread per 8 columns of a row.
-template <int DTW>
+// dW[o][c] = bf16(W[o][c] - s[o][group(c)] * (code[o][c] - z[o][group(c)])), z = 0 for
+// symmetric codes, ld = kseg (a multiple of 64, columns d_in .. kseg-1 zero).  One thread per
+// 8 columns of a row.
+template <int DTW, bool ZP>
 __global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict__ Wv, int64_t ldw, int64_t m, int64_t n,
                                                          int64_t kseg, const uint8_t* __restrict__ packed,
                                                          const int8_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ scales,
+                                                         const uint16_t* __restrict__ zeros,
                                                          const int32_t* __restrict__ g_idx, int64_t ng, int g,
                                                          int vec, uint16_t* __restrict__ dw) {
     typedef typename Elem<DTW>::T T;
@@ -39,20 +41,27 @@ __global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict_
     float d[8];
     if (vec && c + 8 <= n) {
         const float4 w0 = Elem<DTW>::get4(W, o * ldw + c), w1 = Elem<DTW>::get4(W, o * ldw + c + 4);
+        const int64_t gi = o * ng + (g == 0 ? 0 : c / g);
+        const int z = ZP ? (int)zeros[gi] : 0;
         int q[8];
         if (packed) {
             const uint32_t b = *(const uint32_t*)(packed + o * (n / 2) + c / 2);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) q[k] = (int)((b >> (4 * k)) & 15) - 8;
+            for (int k = 0; k < 8; ++k) q[k] = (int)((b >> (4 * k)) & 15) - (ZP ? z : 8);
         } else {
             const uint2 b = *(const uint2*)(codes + o * n + c);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                q[k] = (int8_t)((b.x >> (8 * k)) & 0xff);
-                q[4 + k] = (int8_t)((b.y >> (8 * k)) & 0xff);
+                if (ZP) {
+                    q[k] = (int)((b.x >> (8 * k)) & 0xff) - z;
+                    q[4 + k] = (int)((b.y >> (8 * k)) & 0xff) - z;
+                } else {
+                    q[k] = (int8_t)((b.x >> (8 * k)) & 0xff);
+                    q[4 + k] = (int8_t)((b.y >> (8 * k)) & 0xff);
+                }
             }
         }
-        const float sc = f16_bits_to_f32(scales[o * ng + (g == 0 ? 0 : c / g)]);
+        const float sc = f16_bits_to_f32(scales[gi]);
         const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
         for (int k = 0; k < 8; ++k) d[k] = wv[k] - sc * (float)q[k];
@@ -61,14 +70,15 @@ __global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict_
         for (int k = 0; k < 8; ++k) {
             const int64_t cc = c + k;
             if (cc >= n) { d[k] = 0.f; continue; }
+            const int64_t G = g == 0 ? 0 : (g_idx ? (int64_t)g_idx[cc] : cc / g);
             int q;
             if (packed) {
                 const uint8_t b = packed[o * (n / 2) + cc / 2];
-                q = (int)((cc & 1) ? (b >> 4) : (b & 15)) - 8;
+                q = (int)((cc & 1) ? (b >> 4) : (b & 15)) - (ZP ? 0 : 8);
             } else {
-                q = codes[o * n + cc];
+                q = ZP ? (int)(uint8_t)codes[o * n + cc] : (int)codes[o * n + cc];
             }
-            const int64_t G = g == 0 ? 0 : (g_idx ? (int64_t)g_idx[cc] : cc / g);
+            if (ZP) q -= (int)zeros[o * ng + G];
             d[k] = Elem<DTW>::get(W, o * ldw + cc) - f16_bits_to_f32(scales[o * ng + G]) * (float)q;
         }
     }
@@ -192,7 +202,8 @@ size_t mse_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out) {
 
 hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W, int w_dtype,
                       int64_t ldw, const uint8_t* packed, const int8_t* codes, const uint16_t* scales,
-                      const int32_t* g_idx, int64_t d_out, int bits, int group_size, double* mse, void* ws, hipStream_t s) {
+                      const int32_t* g_idx, int64_t d_out, int bits, int group_size, double* mse, void* ws, hipStream_t s,
+                      const uint16_t* zeros) {
     (void)bits;
     hipError_t e;
     if (n_tok == 0 || d_out == 0) {
@@ -209,12 +220,10 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
                     (group_size == 0 || group_size % 8 == 0) && (!packed || aligned(packed, 4)) &&
                     (!codes || aligned(codes, 8));
     const unsigned dgrid = (unsigned)cdiv(d_out * (kseg / 8), 256);
-    if (w_dtype == 0)
-        hipLaunchKernelGGL(mse_decode_kernel<0>, dim3(dgrid), dim3(256), 0, s, W, ldw, d_out, d_in, kseg, packed, codes,
-                           scales, g_idx, ng, group_size, vec, dw);
-    else
-        hipLaunchKernelGGL(mse_decode_kernel<1>, dim3(dgrid), dim3(256), 0, s, W, ldw, d_out, d_in, kseg, packed, codes,
-                           scales, g_idx, ng, group_size, vec, dw);
+    auto dec = w_dtype == 0 ? (zeros ? mse_decode_kernel<0, true> : mse_decode_kernel<0, false>)
+                            : (zeros ? mse_decode_kernel<1, true> : mse_decode_kernel<1, false>);
+    hipLaunchKernelGGL(dec, dim3(dgrid), dim3(256), 0, s, W, ldw, d_out, d_in, kseg, packed, codes, scales, zeros, g_idx,
+                       ng, group_size, vec, dw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     int64_t nb = 0;

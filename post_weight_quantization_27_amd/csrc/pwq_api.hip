@@ -106,11 +106,11 @@ size_t pwq_gptq_workspace_size(int64_t d_out, int64_t d_in, const pwq_params* pa
     return gptq_ws_layout(d_out, d_in, params->block_size, params->group_size, params->act_order != 0).total;
 }
 
-pwq_status pwq_gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
-                                   const float* U, const int32_t* info, const pwq_params* params,
-                                   const int32_t* perm, const uint16_t* scales_in,
-                                   int8_t* codes, uint8_t* packed, uint16_t* scales_out, int32_t* g_idx,
-                                   void* ws, size_t ws_bytes, void* stream) {
+static pwq_status gptq_checked(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, const float* U,
+                               const int32_t* info, const pwq_params* params, const int32_t* perm,
+                               const uint16_t* scales_in, int8_t* codes, uint8_t* packed, uint16_t* scales_out,
+                               int32_t* g_idx, void* ws, size_t ws_bytes, void* stream, const uint16_t* zeros_in,
+                               uint16_t* zeros_out) {
     if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
     if (!gptq_params_ok(params)) return PWQ_EINVAL;
     if (bad_dim(d_out) || d_out > INT32_MAX || d_in <= 0 || bad_dim(d_in) || ldw < d_in) return PWQ_EINVAL;
@@ -124,13 +124,32 @@ pwq_status pwq_gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, in
     if (!ws || ws_bytes < need) return PWQ_EWORKSPACE;
     return hip_status(gptq_launch(W, w_dtype, d_out, d_in, ldw, U, info, params->bits, params->group_size,
                                   params->block_size, act, perm, scales_in, codes, packed, scales_out, g_idx, ws,
-                                  (hipStream_t)stream));
+                                  (hipStream_t)stream, zeros_in, zeros_out));
+}
+
+pwq_status pwq_gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
+                                   const float* U, const int32_t* info, const pwq_params* params,
+                                   const int32_t* perm, const uint16_t* scales_in,
+                                   int8_t* codes, uint8_t* packed, uint16_t* scales_out, int32_t* g_idx,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    return gptq_checked(W, w_dtype, d_out, d_in, ldw, U, info, params, perm, scales_in, codes, packed, scales_out,
+                        g_idx, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+pwq_status pwq_gptq_quantize_layer_zp(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
+                                      const float* U, const int32_t* info, const pwq_params* params,
+                                      const int32_t* perm, const uint16_t* scales_in, const uint16_t* zeros_in,
+                                      uint8_t* codes, uint8_t* packed, uint16_t* scales_out, uint16_t* zeros_out,
+                                      int32_t* g_idx, void* ws, size_t ws_bytes, void* stream) {
+    if (!zeros_out || ((scales_in != nullptr) != (zeros_in != nullptr))) return PWQ_EINVAL;
+    return gptq_checked(W, w_dtype, d_out, d_in, ldw, U, info, params, perm, scales_in, (int8_t*)codes, packed,
+                        scales_out, g_idx, ws, ws_bytes, stream, zeros_in, zeros_out);
 }
 
 // ------------------------------------------------------------------ RTN / dequant
-pwq_status pwq_rtn_quantize(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
-                            int32_t group_size, const uint16_t* scales_in, int8_t* codes, uint8_t* packed,
-                            uint16_t* scales_out, void* stream) {
+static pwq_status rtn_checked(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
+                              int32_t group_size, const uint16_t* scales_in, int8_t* codes, uint8_t* packed,
+                              uint16_t* scales_out, void* stream, const uint16_t* zeros_in, uint16_t* zeros_out) {
     if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
     if (bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldw < d_in) return PWQ_EINVAL;
     if (bits < 2 || bits > 8 || !group_ok(group_size, d_in)) return PWQ_EINVAL;
@@ -139,12 +158,28 @@ pwq_status pwq_rtn_quantize(const void* W, int w_dtype, int64_t d_out, int64_t d
     if (d_out == 0) return PWQ_OK;
     if (!W) return PWQ_EINVAL;
     return hip_status(rtn_launch(W, w_dtype, d_out, d_in, ldw, bits, group_size, scales_in, codes, packed, scales_out,
-                                 (hipStream_t)stream));
+                                 (hipStream_t)stream, zeros_in, zeros_out));
 }
 
-pwq_status pwq_dequant(const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
-                       int64_t d_out, int64_t d_in, int32_t bits, int32_t group_size, void* W_out, int out_dtype,
-                       void* stream) {
+pwq_status pwq_rtn_quantize(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
+                            int32_t group_size, const uint16_t* scales_in, int8_t* codes, uint8_t* packed,
+                            uint16_t* scales_out, void* stream) {
+    return rtn_checked(W, w_dtype, d_out, d_in, ldw, bits, group_size, scales_in, codes, packed, scales_out, stream,
+                       nullptr, nullptr);
+}
+
+pwq_status pwq_rtn_quantize_zp(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
+                               int32_t group_size, const uint16_t* scales_in, const uint16_t* zeros_in,
+                               uint8_t* codes, uint8_t* packed, uint16_t* scales_out, uint16_t* zeros_out,
+                               void* stream) {
+    if (!zeros_out || ((scales_in != nullptr) != (zeros_in != nullptr))) return PWQ_EINVAL;
+    return rtn_checked(W, w_dtype, d_out, d_in, ldw, bits, group_size, scales_in, (int8_t*)codes, packed, scales_out,
+                       stream, zeros_in, zeros_out);
+}
+
+static pwq_status dequant_checked(const uint8_t* packed, const int8_t* codes, const uint16_t* scales,
+                                  const uint16_t* zeros, const int32_t* g_idx, int64_t d_out, int64_t d_in, int32_t bits,
+                                  int32_t group_size, void* W_out, int out_dtype, void* stream) {
     if (out_dtype != PWQ_F32 && out_dtype != PWQ_F16 && out_dtype != PWQ_BF16) return PWQ_EDTYPE;
     if (bad_dim(d_out) || d_in <= 0 || bad_dim(d_in)) return PWQ_EINVAL;
     if (bits < 2 || bits > 8 || !group_ok(group_size, d_in)) return PWQ_EINVAL;
@@ -153,7 +188,22 @@ pwq_status pwq_dequant(const uint8_t* packed, const int8_t* codes, const uint16_
     if (g_idx && group_size == 0) return PWQ_EINVAL;
     if (!scales || !W_out) return PWQ_EINVAL;
     return hip_status(dequant_launch(packed, codes, scales, g_idx, d_out, d_in, bits, group_size, W_out, out_dtype,
-                                     (hipStream_t)stream));
+                                     (hipStream_t)stream, zeros));
+}
+
+pwq_status pwq_dequant(const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
+                       int64_t d_out, int64_t d_in, int32_t bits, int32_t group_size, void* W_out, int out_dtype,
+                       void* stream) {
+    return dequant_checked(packed, codes, scales, nullptr, g_idx, d_out, d_in, bits, group_size, W_out, out_dtype,
+                           stream);
+}
+
+pwq_status pwq_dequant_zp(const uint8_t* packed, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                          const int32_t* g_idx, int64_t d_out, int64_t d_in, int32_t bits, int32_t group_size,
+                          void* W_out, int out_dtype, void* stream) {
+    if (!zeros) return PWQ_EINVAL;
+    return dequant_checked(packed, (const int8_t*)codes, scales, zeros, g_idx, d_out, d_in, bits, group_size, W_out,
+                           out_dtype, stream);
 }
 
 // ------------------------------------------------------------------ MSE
@@ -162,11 +212,10 @@ size_t pwq_recon_mse_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out) 
     return mse_ws_bytes(n_tok, d_in, d_out);
 }
 
-pwq_status pwq_recon_mse(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
-                         const void* W, int w_dtype, int64_t ldw,
-                         const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
-                         int64_t d_out, int32_t bits, int32_t group_size,
-                         double* mse, void* ws, size_t ws_bytes, void* stream) {
+static pwq_status mse_checked(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W,
+                              int w_dtype, int64_t ldw, const uint8_t* packed, const int8_t* codes,
+                              const uint16_t* scales, const uint16_t* zeros, const int32_t* g_idx, int64_t d_out,
+                              int32_t bits, int32_t group_size, double* mse, void* ws, size_t ws_bytes, void* stream) {
     if (x_dtype != PWQ_F32 && x_dtype != PWQ_BF16) return PWQ_EDTYPE;
     if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
     if (bad_dim(n_tok) || bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldx < d_in || ldw < d_in) return PWQ_EINVAL;
@@ -181,7 +230,26 @@ pwq_status pwq_recon_mse(const void* X, int x_dtype, int64_t n_tok, int64_t d_in
         if (!ws || ws_bytes < need) return PWQ_EWORKSPACE;
     }
     return hip_status(mse_launch(X, x_dtype, n_tok, d_in, ldx, W, w_dtype, ldw, packed, codes, scales, g_idx, d_out, bits,
-                                 group_size, mse, ws, (hipStream_t)stream));
+                                 group_size, mse, ws, (hipStream_t)stream, zeros));
+}
+
+pwq_status pwq_recon_mse(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                         const void* W, int w_dtype, int64_t ldw,
+                         const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
+                         int64_t d_out, int32_t bits, int32_t group_size,
+                         double* mse, void* ws, size_t ws_bytes, void* stream) {
+    return mse_checked(X, x_dtype, n_tok, d_in, ldx, W, w_dtype, ldw, packed, codes, scales, nullptr, g_idx, d_out, bits,
+                       group_size, mse, ws, ws_bytes, stream);
+}
+
+pwq_status pwq_recon_mse_zp(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                            const void* W, int w_dtype, int64_t ldw,
+                            const uint8_t* packed, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                            const int32_t* g_idx, int64_t d_out, int32_t bits, int32_t group_size,
+                            double* mse, void* ws, size_t ws_bytes, void* stream) {
+    if (!zeros) return PWQ_EINVAL;
+    return mse_checked(X, x_dtype, n_tok, d_in, ldx, W, w_dtype, ldw, packed, (const int8_t*)codes, scales, zeros, g_idx,
+                       d_out, bits, group_size, mse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

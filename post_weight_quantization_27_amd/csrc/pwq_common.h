@@ -65,13 +65,32 @@ __device__ __forceinline__ int quant_code(float w, float s, float rs, int qmax) 
 // integer past h, the even neighbour (a tie), or k.  Finite inputs give exactly
 // quant_code's result (s > 0; the callers give s = 0 the code 0).  quant_code_self returns
 // the code as a float.
-__device__ __forceinline__ float quant_code_self(float w, float s, float rs, float qmaxf) {
+// round_quot_clamp is the same rounding clamped to [lo, hi] (integers with |lo|, |hi| <= 256,
+// lo <= hi): the quotient only needs to be exact where it is not clamped, and there
+// |k| <= 257 keeps h s exact.
+__device__ __forceinline__ float round_quot_clamp(float w, float s, float rs, float lo, float hi) {
     const float t = w * rs;
     const float k = rintf(t);
     const float h = k + copysignf(0.5f, t - k);
     const float e = fmaf(-h, s, w);
     const float d = e != 0.f ? copysignf(0.25f, e) : 0.f;
-    return __builtin_amdgcn_fmed3f(rintf(h + d), -qmaxf, qmaxf);
+    return __builtin_amdgcn_fmed3f(rintf(h + d), lo, hi);
+}
+__device__ __forceinline__ float quant_code_self(float w, float s, float rs, float qmaxf) {
+    return round_quot_clamp(w, s, rs, -qmaxf, qmaxf);
+}
+
+// Zero-point quantizer of a group ("Model Quantization Mechanics", "Affine Quantization":
+// code = round(w / S) + Z, value S (code - Z)).  The range [lo, hi] = [min(w, 0), max(w, 0)]
+// is mapped onto the codes 0 .. top = 2^b - 1: S = fp16(fp32(hi - lo) / top) (one float32
+// subtraction, one float32 division, one rounding to float16), Z = the integer nearest to
+// -lo / S (exact quotient, ties to even) clamped to [0, top], and Z = 0 when S = 0.  The
+// callers pass nlo = -lo >= 0 (a maximum of -w, like hi a maximum of w).
+__device__ __forceinline__ uint16_t zp_scale_bits(float nlo, float hi, int top) {
+    return f32_to_f16_bits((hi + nlo) / (float)top);
+}
+__device__ __forceinline__ float zp_zero(float nlo, float s, float topf) {
+    return s > 0.f ? round_quot_clamp(nlo, s, __builtin_amdgcn_rcpf(s), 0.f, topf) : 0.f;
 }
 __device__ __forceinline__ int quant_code_sel(float w, float s, float rs, int qmax) {
     return (int)quant_code_self(w, s, rs, (float)qmax);

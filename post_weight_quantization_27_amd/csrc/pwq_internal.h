@@ -37,7 +37,9 @@ size_t chol_ws_bytes(int64_t n);
 hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U, int32_t* info, void* ws,
                        hipStream_t s);
 
-// GPTQ column loop.
+// GPTQ column loop.  The quantize, dequant and MSE launchers take the zero-point form when
+// given zeros (zeros_out for the quantizers, zeros for the decoders): codes are then the
+// unsigned bytes 0 .. 2^bits - 1 and nibbles hold the code itself.
 struct GptqWs {
     size_t wf, err, codes, inv, total;
 };
@@ -45,21 +47,22 @@ GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int group_siz
 hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, const float* U,
                        const int32_t* info, int bits, int group_size, int block_size, int act_order,
                        const int32_t* perm, const uint16_t* scales_in, int8_t* codes, uint8_t* packed,
-                       uint16_t* scales_out, int32_t* g_idx, void* ws, hipStream_t s);
+                       uint16_t* scales_out, int32_t* g_idx, void* ws, hipStream_t s,
+                       const uint16_t* zeros_in = nullptr, uint16_t* zeros_out = nullptr);
 
 // RTN, dequant.
 hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, int bits, int group_size,
                       const uint16_t* scales_in, int8_t* codes, uint8_t* packed, uint16_t* scales_out,
-                      hipStream_t s);
+                      hipStream_t s, const uint16_t* zeros_in = nullptr, uint16_t* zeros_out = nullptr);
 hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint16_t* scales,
                           const int32_t* g_idx, int64_t m, int64_t n, int bits, int group_size, void* out,
-                          int out_dtype, hipStream_t s);
+                          int out_dtype, hipStream_t s, const uint16_t* zeros = nullptr);
 
 // Reconstruction MSE.
 size_t mse_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out);
 hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W,
                       int w_dtype, int64_t ldw, const uint8_t* packed, const int8_t* codes,
                       const uint16_t* scales, const int32_t* g_idx, int64_t d_out, int bits, int group_size,
-                      double* mse, void* ws, hipStream_t s);
+                      double* mse, void* ws, hipStream_t s, const uint16_t* zeros = nullptr);
 
 }  // namespace pwq

@@ -3,8 +3,11 @@
 // RTN: per output row ("GPT-2 Quantization Reconstruction Error", "What this project
 // does": one scale per output channel, 15 levels) or per group of g consecutive weights
 // ("Model Quantization Mechanics", "Group-wise Quantization"), symmetric (Z = 0 in
-// "Affine Quantization"): s = fp16(fp32(absmax / qmax)), code = round(w / s).
-// Dequant: What = s * code, formed exactly in float32, rounded once to the output type.
+// "Affine Quantization"): s = fp16(fp32(absmax / qmax)), code = round(w / s); or with a
+// zero-point per row and group (the same section's Z): the range [min(w, 0), max(w, 0)]
+// onto codes 0 .. 2^b - 1, code = round(w / S) + Z.  Each kernel takes the choice as a
+// template argument, so the symmetric code is unchanged by the zero-point one.
+// Dequant: What = s * (code - z), formed exactly in float32, rounded once to the output type.
 //
 // Both passes are HBM-bound, so what matters is bytes in flight per CU.
 // RTN, groups that tile their rows (n % g == 0, 16-byte aligned rows, g * element size a
@@ -49,9 +52,18 @@ struct RtnArgs {
     int8_t* codes;
     uint8_t* packed;
     uint16_t* scales_out;
+    const uint16_t* zeros_in;   // zero-point form: fixed zeros (with scales_in) or NULL
+    uint16_t* zeros_out;        // zero-point form: the zero of every (row, group)
+    int top;                    // zero-point form: largest code, 2^bits - 1
 };
 
-template <int DT>
+// Zero of a group in the zero-point form: fixed (clamped to [0, top]) or from the range.
+__device__ __forceinline__ float rtn_zero(const RtnArgs& a, bool live, int64_t idx, float nlo, float s) {
+    if (a.zeros_in) return live ? (float)min((int)a.zeros_in[idx], a.top) : 0.f;
+    return zp_zero(nlo, s, (float)a.top);
+}
+
+template <int DT, bool ZP>
 __global__ __launch_bounds__(256) void rtn_kernel(RtnArgs a) {
     typedef typename Elem<DT>::T T;
     const int lane = threadIdx.x & 63;
@@ -69,29 +81,44 @@ __global__ __launch_bounds__(256) void rtn_kernel(RtnArgs a) {
         const T* row = (const T*)a.W + r * a.ldw;
 
         float4 cache[RTN_CACHE];
-        float amax = 0.f;
+        float amax = 0.f, nlo = 0.f;     // symmetric: max |w|; zero-point: max(w, 0), max(-w, 0)
         int qi = 0;
         for (int64_t c = c0 + 4 * li; c < c1; c += 4 * L, ++qi) {
             const float4 v = load_quad<DT>(row, c, c1, a.vec);
             if (qi < RTN_CACHE) cache[qi] = v;
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            if (ZP) {
+                amax = fmaxf(amax, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+                nlo = fmaxf(nlo, fmaxf(fmaxf(-v.x, -v.y), fmaxf(-v.z, -v.w)));
+            } else {
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
         }
         amax = group_max(amax, L);
+        if (ZP) nlo = group_max(nlo, L);
         uint16_t sb;
         if (a.scales_in) sb = live ? a.scales_in[r * a.ng + G] : 0;
-        else sb = scale_bits_from_absmax(amax, a.qmax);
+        else sb = ZP ? zp_scale_bits(nlo, amax, a.top) : scale_bits_from_absmax(amax, a.qmax);
         if (live && li == 0) a.scales_out[r * a.ng + G] = sb;
         const float s = f16_bits_to_f32(sb);
         const float rs = s > 0.f ? 1.0f / s : 0.f;
+        const float z = ZP ? rtn_zero(a, live, r * a.ng + G, nlo, s) : 0.f;
+        if (ZP && live && li == 0) a.zeros_out[r * a.ng + G] = (uint16_t)z;
+        const float qlo = ZP ? -z : -(float)a.qmax, qhi = ZP ? (float)a.top - z : (float)a.qmax;
 
         qi = 0;
         for (int64_t c = c0 + 4 * li; c < c1; c += 4 * L, ++qi) {
             const float4 v = qi < RTN_CACHE ? cache[qi] : load_quad<DT>(row, c, c1, a.vec);
             int q[4];
-            q[0] = s > 0.f ? quant_code(v.x, s, rs, a.qmax) : 0;
-            q[1] = s > 0.f ? quant_code(v.y, s, rs, a.qmax) : 0;
-            q[2] = s > 0.f ? quant_code(v.z, s, rs, a.qmax) : 0;
-            q[3] = s > 0.f ? quant_code(v.w, s, rs, a.qmax) : 0;
+            if (ZP) {
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) q[k] = s > 0.f ? (int)(round_quot_clamp(vv[k], s, rs, qlo, qhi) + z) : 0;
+            } else {
+                q[0] = s > 0.f ? quant_code(v.x, s, rs, a.qmax) : 0;
+                q[1] = s > 0.f ? quant_code(v.y, s, rs, a.qmax) : 0;
+                q[2] = s > 0.f ? quant_code(v.z, s, rs, a.qmax) : 0;
+                q[3] = s > 0.f ? quant_code(v.w, s, rs, a.qmax) : 0;
+            }
             const bool full = c + 3 < c1;
             if (a.codes) {
                 int8_t* dst = a.codes + r * a.n + c;
@@ -105,8 +132,9 @@ __global__ __launch_bounds__(256) void rtn_kernel(RtnArgs a) {
             }
             if (a.packed) {
                 uint8_t* dst = a.packed + r * (a.n / 2) + c / 2;
-                const uint8_t b0 = (uint8_t)((q[0] + 8) | ((q[1] + 8) << 4));
-                const uint8_t b1 = (uint8_t)((q[2] + 8) | ((q[3] + 8) << 4));
+                constexpr int OFF = ZP ? 0 : 8;           // nibble = code (+ 8 for signed codes)
+                const uint8_t b0 = (uint8_t)((q[0] + OFF) | ((q[1] + OFF) << 4));
+                const uint8_t b1 = (uint8_t)((q[2] + OFF) | ((q[3] + OFF) << 4));
                 if (full && a.vec && (a.n % 4 == 0)) {
                     *(uint16_t*)dst = (uint16_t)(b0 | (b1 << 8));
                 } else {
@@ -140,7 +168,7 @@ __device__ __forceinline__ float lanes_max(float v) {
 // guarantees that W, the codes and the nibbles each span less than 4 GiB, so addresses are
 // 32-bit offsets from the (uniform) base pointers, and that there are fewer than 2^31
 // groups; the scale index of a group is its segment number.
-template <int DT, int LG>
+template <int DT, int LG, bool ZP>
 __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
     typedef typename Elem<DT>::T T;
     constexpr int ES = (int)sizeof(T);
@@ -182,19 +210,34 @@ __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
                     v[2 * k + 1] = f16_bits_to_f32((uint16_t)(w4[k] >> 16));
                 }
             }
-            float amax = 0.f;
+            float amax = 0.f, nlo = 0.f;
+            if (ZP) {
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) amax = fmaxf(amax, fabsf(v[k]));
-            amax = lanes_max<LG>(amax);
+                for (int k = 0; k < EPV; ++k) { amax = fmaxf(amax, v[k]); nlo = fmaxf(nlo, -v[k]); }
+                amax = lanes_max<LG>(amax);
+                nlo = lanes_max<LG>(nlo);
+            } else {
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) amax = fmaxf(amax, fabsf(v[k]));
+                amax = lanes_max<LG>(amax);
+            }
             uint16_t sb;
             if (a.scales_in) sb = live[u] ? a.scales_in[seg[u]] : 0;
-            else sb = scale_bits_from_absmax(amax, a.qmax);
+            else sb = ZP ? zp_scale_bits(nlo, amax, a.top) : scale_bits_from_absmax(amax, a.qmax);
             if (live[u] && li == 0) a.scales_out[seg[u]] = sb;
             const float sc = f16_bits_to_f32(sb);
             const float rs = __builtin_amdgcn_rcpf(sc);       // only a first guess: the fma check is exact
             int q[EPV];
+            if (ZP) {
+                const float z = rtn_zero(a, live[u], seg[u], nlo, sc);
+                if (live[u] && li == 0) a.zeros_out[seg[u]] = (uint16_t)z;
+                const float qlo = -z, qhi = (float)a.top - z;
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) q[k] = sc > 0.f ? quant_code_sel(v[k], sc, rs, a.qmax) : 0;
+                for (int k = 0; k < EPV; ++k) q[k] = sc > 0.f ? (int)(round_quot_clamp(v[k], sc, rs, qlo, qhi) + z) : 0;
+            } else {
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) q[k] = sc > 0.f ? quant_code_sel(v[k], sc, rs, a.qmax) : 0;
+            }
             if (!live[u]) continue;
             const uint32_t c = (seg[u] - rr[u] * ng) * (uint32_t)a.gl + (uint32_t)(li * EPV);
             if (a.codes) {
@@ -211,7 +254,7 @@ __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
                 uint8_t* dst = a.packed + (rr[u] * (n / 2) + c / 2);
                 uint32_t nib = 0;
 #pragma unroll
-                for (int k = 0; k < EPV; ++k) nib |= (uint32_t)(q[k] + 8) << (4 * k);
+                for (int k = 0; k < EPV; ++k) nib |= (uint32_t)(q[k] + (ZP ? 0 : 8)) << (4 * k);
                 if (EPV == 8) *(uint32_t*)dst = nib;
                 else *(uint16_t*)dst = (uint16_t)nib;
             }
@@ -221,8 +264,9 @@ __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
 
 struct DqArgs {
     const uint8_t* packed;
-    const int8_t* codes;
+    const int8_t* codes;        // zero-point form: the bytes are unsigned codes
     const uint16_t* scales;
+    const uint16_t* zeros;      // zero-point form: d_out x ng zeros; NULL for symmetric codes
     const int32_t* g_idx;
     int64_t m, n, ng, chunks;   // chunks of 8 columns per row
     int g;                      // 0 = one scale per row
@@ -230,12 +274,43 @@ struct DqArgs {
     void* out;
 };
 
-__device__ __forceinline__ int dq_code(const DqArgs& a, int64_t r, int64_t c) {
+// code relative to the group's zero: q - z (zero-point form) or q (symmetric, nibble - 8)
+template <bool ZP>
+__device__ __forceinline__ int dq_code(const DqArgs& a, int64_t r, int64_t c, int64_t G) {
+    if (ZP) {
+        const int z = a.zeros[r * a.ng + G];
+        if (a.packed) {
+            const uint8_t b = a.packed[r * (a.n / 2) + c / 2];
+            return (int)((c & 1) ? (b >> 4) : (b & 15)) - z;
+        }
+        return (int)(uint8_t)a.codes[r * a.n + c] - z;
+    }
     if (a.packed) {
         const uint8_t b = a.packed[r * (a.n / 2) + c / 2];
         return (int)((c & 1) ? (b >> 4) : (b & 15)) - 8;
     }
     return a.codes[r * a.n + c];
+}
+
+// eight codes of one chunk, relative to the zero z (symmetric: z = 0, nibbles offset by 8)
+template <bool ZP>
+__device__ __forceinline__ void dq_unpack8(const DqArgs& a, uint2 w, int z, int q[8]) {
+    if (a.packed) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = (int)((w.x >> (4 * k)) & 15) - (ZP ? z : 8);
+    } else if (ZP) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            q[k] = (int)((w.x >> (8 * k)) & 0xff) - z;
+            q[4 + k] = (int)((w.y >> (8 * k)) & 0xff) - z;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            q[k] = (int8_t)((w.x >> (8 * k)) & 0xff);
+            q[4 + k] = (int8_t)((w.y >> (8 * k)) & 0xff);
+        }
+    }
 }
 
 __device__ __forceinline__ int64_t dq_group(const DqArgs& a, int64_t c) {
@@ -254,7 +329,7 @@ __device__ __forceinline__ void dq_store(void* out, int64_t i, float v) {
 // per pass, lane l the chunks 64 j + l (j < 4): each load instruction reads 4 (nibbles) or 8
 // (codes) contiguous bytes per lane, each store writes 16 or 32 contiguous bytes per lane,
 // and the four loads of a lane are in flight together.
-template <int OT>
+template <int OT, bool ZP>
 __global__ __launch_bounds__(256) void dequant_vec_kernel(DqArgs a) {
     constexpr int U = 4;
     const int lane = threadIdx.x & 63;
@@ -265,6 +340,7 @@ __global__ __launch_bounds__(256) void dequant_vec_kernel(DqArgs a) {
     for (int64_t base = wave_id * 64 * U; base < total; base += nwaves * 64 * U) {
         uint2 w[U];
         float sc[U];
+        int zz[U];
         int64_t r[U], c0[U];
         bool live[U];
 #pragma unroll
@@ -276,25 +352,18 @@ __global__ __launch_bounds__(256) void dequant_vec_kernel(DqArgs a) {
             c0[u] = (tt - r[u] * cpr) * 8;
             if (a.packed) w[u] = make_uint2(*(const uint32_t*)(a.packed + r[u] * (a.n / 2) + c0[u] / 2), 0u);
             else w[u] = *(const uint2*)(a.codes + r[u] * a.n + c0[u]);
-            sc[u] = f16_bits_to_f32(a.scales[r[u] * a.ng + (a.g == 0 ? 0 : c0[u] / a.g)]);
+            const int64_t gi = r[u] * a.ng + (a.g == 0 ? 0 : c0[u] / a.g);
+            sc[u] = f16_bits_to_f32(a.scales[gi]);
+            zz[u] = ZP ? (int)a.zeros[gi] : 0;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (!live[u]) continue;
             int q[8];
-            if (a.packed) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) q[k] = (int)((w[u].x >> (4 * k)) & 15) - 8;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    q[k] = (int8_t)((w[u].x >> (8 * k)) & 0xff);
-                    q[4 + k] = (int8_t)((w[u].y >> (8 * k)) & 0xff);
-                }
-            }
+            dq_unpack8<ZP>(a, w[u], zz[u], q);
             float v[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = sc[u] * (float)q[k];     // exact: 11 x 4 significant bits
+            for (int k = 0; k < 8; ++k) v[k] = sc[u] * (float)q[k];     // exact: 11 x at most 8 significant bits (zeros within the code range)
             if (OT == 0) {
                 float4* o = (float4*)((float*)a.out + r[u] * a.n + c0[u]);
                 o[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -313,7 +382,7 @@ __global__ __launch_bounds__(256) void dequant_vec_kernel(DqArgs a) {
     }
 }
 
-template <int OT>
+template <int OT, bool ZP>
 __global__ __launch_bounds__(256) void dequant_kernel(DqArgs a) {
     const int64_t total = a.m * a.chunks;
     for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
@@ -321,21 +390,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DqArgs a) {
         if (a.vec) {
             float v[8];
             int q[8];
-            if (a.packed) {
-                const uint32_t w = *(const uint32_t*)(a.packed + r * (a.n / 2) + c0 / 2);
+            const uint2 w = a.packed ? make_uint2(*(const uint32_t*)(a.packed + r * (a.n / 2) + c0 / 2), 0u)
+                                     : *(const uint2*)(a.codes + r * a.n + c0);
+            const int64_t gi = r * a.ng + dq_group(a, c0);
+            dq_unpack8<ZP>(a, w, ZP ? (int)a.zeros[gi] : 0, q);
+            const float s = f16_bits_to_f32(a.scales[gi]);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) q[k] = (int)((w >> (4 * k)) & 15) - 8;
-            } else {
-                const uint2 w = *(const uint2*)(a.codes + r * a.n + c0);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    q[k] = (int8_t)((w.x >> (8 * k)) & 0xff);
-                    q[4 + k] = (int8_t)((w.y >> (8 * k)) & 0xff);
-                }
-            }
-            const float s = f16_bits_to_f32(a.scales[r * a.ng + dq_group(a, c0)]);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = s * (float)q[k];      // exact: 11 x 4 significant bits
+            for (int k = 0; k < 8; ++k) v[k] = s * (float)q[k];      // exact: 11 x at most 8 significant bits (zeros within the code range)
             if (OT == 0) {
                 float4* o = (float4*)((float*)a.out + r * a.n + c0);
                 o[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -354,8 +415,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(DqArgs a) {
             for (int k = 0; k < 8; ++k) {
                 const int64_t c = c0 + k;
                 if (c >= a.n) break;
-                const float s = f16_bits_to_f32(a.scales[r * a.ng + dq_group(a, c)]);
-                dq_store<OT>(a.out, r * a.n + c, s * (float)dq_code(a, r, c));
+                const int64_t G = dq_group(a, c);
+                const float s = f16_bits_to_f32(a.scales[r * a.ng + G]);
+                dq_store<OT>(a.out, r * a.n + c, s * (float)dq_code<ZP>(a, r, c, G));
             }
         }
     }
@@ -379,7 +441,8 @@ int64_t resident_blocks(int64_t want) {
 }  // namespace
 
 hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, int bits, int group_size,
-                      const uint16_t* scales_in, int8_t* codes, uint8_t* packed, uint16_t* scales_out, hipStream_t s) {
+                      const uint16_t* scales_in, int8_t* codes, uint8_t* packed, uint16_t* scales_out, hipStream_t s,
+                      const uint16_t* zeros_in, uint16_t* zeros_out) {
     if (m == 0 || n == 0) return hipSuccess;
     RtnArgs a{};
     a.W = W; a.ldw = ldw; a.m = m; a.n = n;
@@ -394,6 +457,8 @@ hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
     a.vec = (ldw % 4 == 0) && (a.gl % 4 == 0) && aligned(W, 4 * es) && (!codes || aligned(codes, 4)) &&
             (!packed || aligned(packed, 2));
     a.scales_in = scales_in; a.codes = codes; a.packed = packed; a.scales_out = scales_out;
+    a.zeros_in = zeros_in; a.zeros_out = zeros_out; a.top = (1 << bits) - 1;
+    const bool zp = zeros_out != nullptr;
     // group path: whole groups per row, 16-byte vectors, LG a power of two <= 64
     const int64_t gbytes = group_size * (int64_t)es;
     int lg = (int)(gbytes / 16);
@@ -411,8 +476,14 @@ hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
         const int64_t waves = cdiv(a.nseg, (int64_t)(64 / lg) * 4);
         const int64_t want = cdiv(waves, 4);
 #define PWQ_RTN_G(DT, LGV)                                                                                  \
-        hipLaunchKernelGGL((rtn_group_kernel<DT, LGV>), dim3((unsigned)resident_blocks<rtn_group_kernel<DT, LGV>>(want)), \
-                           dim3(256), 0, s, a)
+        do {                                                                                                    \
+            if (zp) hipLaunchKernelGGL((rtn_group_kernel<DT, LGV, true>),                                       \
+                                       dim3((unsigned)resident_blocks<rtn_group_kernel<DT, LGV, true>>(want)),  \
+                                       dim3(256), 0, s, a);                                                     \
+            else hipLaunchKernelGGL((rtn_group_kernel<DT, LGV, false>),                                         \
+                                    dim3((unsigned)resident_blocks<rtn_group_kernel<DT, LGV, false>>(want)),    \
+                                    dim3(256), 0, s, a);                                                        \
+        } while (0)
 #define PWQ_RTN_LG(DT)                                      \
         switch (lg) {                                       \
         case 1: PWQ_RTN_G(DT, 1); break;                    \
@@ -432,17 +503,24 @@ hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
     const int64_t waves = cdiv(a.nseg, 64 / L);
     int64_t blocks = cdiv(waves, 4);
     if (blocks > 65536) blocks = 65536;
-    if (w_dtype == 0) hipLaunchKernelGGL(rtn_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(rtn_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if (w_dtype == 0) {
+        if (zp) hipLaunchKernelGGL((rtn_kernel<0, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((rtn_kernel<0, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    } else {
+        if (zp) hipLaunchKernelGGL((rtn_kernel<1, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((rtn_kernel<1, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
-                          int64_t m, int64_t n, int bits, int group_size, void* out, int out_dtype, hipStream_t s) {
+                          int64_t m, int64_t n, int bits, int group_size, void* out, int out_dtype, hipStream_t s,
+                          const uint16_t* zeros) {
     (void)bits;
     if (m == 0 || n == 0) return hipSuccess;
     DqArgs a{};
-    a.packed = packed; a.codes = codes; a.scales = scales; a.g_idx = g_idx;
+    a.packed = packed; a.codes = codes; a.scales = scales; a.zeros = zeros; a.g_idx = g_idx;
+    const bool zp = zeros != nullptr;
     a.m = m; a.n = n; a.g = group_size;
     a.ng = group_size == 0 ? 1 : cdiv(n, group_size);
     a.chunks = cdiv(n, 8);
@@ -452,19 +530,22 @@ hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint
             (!packed || aligned(packed, 4)) && (!codes || aligned(codes, 8));
     if (a.vec) {
         const int64_t want = cdiv(m * a.chunks, 4 * 256);
-        if (out_dtype == 0)
-            hipLaunchKernelGGL(dequant_vec_kernel<0>, dim3((unsigned)resident_blocks<dequant_vec_kernel<0>>(want)), dim3(256), 0, s, a);
-        else if (out_dtype == 1)
-            hipLaunchKernelGGL(dequant_vec_kernel<1>, dim3((unsigned)resident_blocks<dequant_vec_kernel<1>>(want)), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL(dequant_vec_kernel<2>, dim3((unsigned)resident_blocks<dequant_vec_kernel<2>>(want)), dim3(256), 0, s, a);
+#define PWQ_DQV(OT, ZPV) \
+        hipLaunchKernelGGL((dequant_vec_kernel<OT, ZPV>), dim3((unsigned)resident_blocks<dequant_vec_kernel<OT, ZPV>>(want)), \
+                           dim3(256), 0, s, a)
+        if (out_dtype == 0) { if (zp) PWQ_DQV(0, true); else PWQ_DQV(0, false); }
+        else if (out_dtype == 1) { if (zp) PWQ_DQV(1, true); else PWQ_DQV(1, false); }
+        else { if (zp) PWQ_DQV(2, true); else PWQ_DQV(2, false); }
+#undef PWQ_DQV
         return hipGetLastError();
     }
     int64_t blocks = cdiv(m * a.chunks, 256);
     if (blocks > 65536) blocks = 65536;
-    if (out_dtype == 0) hipLaunchKernelGGL(dequant_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else if (out_dtype == 1) hipLaunchKernelGGL(dequant_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(dequant_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+#define PWQ_DQ(OT, ZPV) hipLaunchKernelGGL((dequant_kernel<OT, ZPV>), dim3((unsigned)blocks), dim3(256), 0, s, a)
+    if (out_dtype == 0) { if (zp) PWQ_DQ(0, true); else PWQ_DQ(0, false); }
+    else if (out_dtype == 1) { if (zp) PWQ_DQ(1, true); else PWQ_DQ(1, false); }
+    else { if (zp) PWQ_DQ(2, true); else PWQ_DQ(2, false); }
+#undef PWQ_DQ
     return hipGetLastError();
 }
 

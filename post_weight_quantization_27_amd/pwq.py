@@ -46,6 +46,17 @@ _SIGS = {
                                         _c_void_p, _c_void_p, _c_void_p]),
     "pwq_dequant": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _c_void_p,
                                    ctypes.c_int, _c_void_p]),
+    "pwq_gptq_quantize_layer_zp": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                                  ctypes.POINTER(PwqParams), _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz,
+                                                  _c_void_p]),
+    "pwq_rtn_quantize_zp": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
+                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "pwq_dequant_zp": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32,
+                                      _c_void_p, ctypes.c_int, _c_void_p]),
+    "pwq_recon_mse_zp": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
+                                        _c_void_p, _c_void_p, _sz, _c_void_p]),
     "pwq_recon_mse_workspace_size": (_sz, [_i64, _i64, _i64]),
     "pwq_recon_mse": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
@@ -168,6 +179,19 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, info: torch.Tensor, bi
                         out: Optional[dict] = None) -> dict:
     """GPTQ column loop.  Returns {codes (int8, original order), packed (uint8), scales (float16,
     groups in processing order), g_idx (int32, act-order only)}."""
+    return _gptq(W, U, info, bits, group_size, block_size, perm, scales_in, None, want_codes, want_packed, out, False)
+
+
+def gptq_quantize_layer_zp(W: torch.Tensor, U: torch.Tensor, info: torch.Tensor, bits: int = 4, group_size: int = 128,
+                           block_size: int = 128, perm: Optional[torch.Tensor] = None,
+                           scales_in: Optional[torch.Tensor] = None, zeros_in: Optional[torch.Tensor] = None,
+                           want_codes: bool = True, want_packed: bool = True, out: Optional[dict] = None) -> dict:
+    """GPTQ with zero-points.  As gptq_quantize_layer, with codes uint8 and zeros (uint16 as
+    int16 storage, like the scales) in the result."""
+    return _gptq(W, U, info, bits, group_size, block_size, perm, scales_in, zeros_in, want_codes, want_packed, out, True)
+
+
+def _gptq(W, U, info, bits, group_size, block_size, perm, scales_in, zeros_in, want_codes, want_packed, out, zp):
     ldw = _rows(W, "W")
     d_out, d_in = W.shape
     act = perm is not None
@@ -176,11 +200,13 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, info: torch.Tensor, bi
     ng = _n_groups(d_in, group_size)
     o = out if out is not None else {}
     if want_codes and o.get("codes") is None:
-        o["codes"] = torch.empty((d_out, d_in), dtype=torch.int8, device=dev)
+        o["codes"] = torch.empty((d_out, d_in), dtype=torch.uint8 if zp else torch.int8, device=dev)
     if want_packed and o.get("packed") is None:
         o["packed"] = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
     if o.get("scales") is None:
         o["scales"] = torch.empty((d_out, ng), dtype=torch.float16, device=dev)
+    if zp and o.get("zeros") is None:
+        o["zeros"] = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
     if act and o.get("g_idx") is None:
         o["g_idx"] = torch.empty(d_in, dtype=torch.int32, device=dev)
     nb = lib().pwq_gptq_workspace_size(d_out, d_in, ctypes.byref(prm))
@@ -188,28 +214,56 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, info: torch.Tensor, bi
     if ws is None or ws.numel() < nb:
         ws = _ws(nb, dev)
         o["_ws"] = ws
-    _check("pwq_gptq_quantize_layer", lib().pwq_gptq_quantize_layer(
-        _p(W), _dtype_code(W), d_out, d_in, ldw, _p(U), _p(info), ctypes.byref(prm), _p(perm), _p(scales_in),
-        _p(o.get("codes") if want_codes else None), _p(o.get("packed") if want_packed else None), _p(o["scales"]),
-        _p(o.get("g_idx") if act else None), _p(ws), nb, _stream(W)))
+    codes = _p(o.get("codes") if want_codes else None)
+    packed = _p(o.get("packed") if want_packed else None)
+    g_idx = _p(o.get("g_idx") if act else None)
+    if zp:
+        _check("pwq_gptq_quantize_layer_zp", lib().pwq_gptq_quantize_layer_zp(
+            _p(W), _dtype_code(W), d_out, d_in, ldw, _p(U), _p(info), ctypes.byref(prm), _p(perm), _p(scales_in),
+            _p(zeros_in), codes, packed, _p(o["scales"]), _p(o["zeros"]), g_idx, _p(ws), nb, _stream(W)))
+    else:
+        _check("pwq_gptq_quantize_layer", lib().pwq_gptq_quantize_layer(
+            _p(W), _dtype_code(W), d_out, d_in, ldw, _p(U), _p(info), ctypes.byref(prm), _p(perm), _p(scales_in),
+            codes, packed, _p(o["scales"]), g_idx, _p(ws), nb, _stream(W)))
     return o
 
 
 def rtn_quantize(W: torch.Tensor, bits: int = 4, group_size: int = 128, scales_in: Optional[torch.Tensor] = None,
                  want_codes: bool = True, want_packed: bool = True, out: Optional[dict] = None) -> dict:
+    return _rtn(W, bits, group_size, scales_in, None, want_codes, want_packed, out, False)
+
+
+def rtn_quantize_zp(W: torch.Tensor, bits: int = 4, group_size: int = 128, scales_in: Optional[torch.Tensor] = None,
+                    zeros_in: Optional[torch.Tensor] = None, want_codes: bool = True, want_packed: bool = True,
+                    out: Optional[dict] = None) -> dict:
+    """RTN with zero-points: codes uint8, zeros (uint16 bits in int16 storage) per row and group."""
+    return _rtn(W, bits, group_size, scales_in, zeros_in, want_codes, want_packed, out, True)
+
+
+def _rtn(W, bits, group_size, scales_in, zeros_in, want_codes, want_packed, out, zp):
     ldw = _rows(W, "W")
     d_out, d_in = W.shape
     dev = W.device
+    ng = _n_groups(d_in, group_size)
     o = out if out is not None else {}
     if want_codes and o.get("codes") is None:
-        o["codes"] = torch.empty((d_out, d_in), dtype=torch.int8, device=dev)
+        o["codes"] = torch.empty((d_out, d_in), dtype=torch.uint8 if zp else torch.int8, device=dev)
     if want_packed and o.get("packed") is None:
         o["packed"] = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
     if o.get("scales") is None:
-        o["scales"] = torch.empty((d_out, _n_groups(d_in, group_size)), dtype=torch.float16, device=dev)
-    _check("pwq_rtn_quantize", lib().pwq_rtn_quantize(
-        _p(W), _dtype_code(W), d_out, d_in, ldw, bits, group_size, _p(scales_in),
-        _p(o.get("codes") if want_codes else None), _p(o.get("packed") if want_packed else None), _p(o["scales"]), _stream(W)))
+        o["scales"] = torch.empty((d_out, ng), dtype=torch.float16, device=dev)
+    if zp and o.get("zeros") is None:
+        o["zeros"] = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
+    codes = _p(o.get("codes") if want_codes else None)
+    packed = _p(o.get("packed") if want_packed else None)
+    if zp:
+        _check("pwq_rtn_quantize_zp", lib().pwq_rtn_quantize_zp(
+            _p(W), _dtype_code(W), d_out, d_in, ldw, bits, group_size, _p(scales_in), _p(zeros_in), codes, packed,
+            _p(o["scales"]), _p(o["zeros"]), _stream(W)))
+    else:
+        _check("pwq_rtn_quantize", lib().pwq_rtn_quantize(
+            _p(W), _dtype_code(W), d_out, d_in, ldw, bits, group_size, _p(scales_in), codes, packed, _p(o["scales"]),
+            _stream(W)))
     return o
 
 
@@ -225,11 +279,26 @@ def dequant(scales: torch.Tensor, d_in: int, bits: int = 4, group_size: int = 12
     return out
 
 
+def dequant_zp(scales: torch.Tensor, zeros: torch.Tensor, d_in: int, bits: int = 4, group_size: int = 128,
+               packed: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+               g_idx: Optional[torch.Tensor] = None, out_dtype=torch.float16,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """What = S (code - Z) from unsigned codes or nibbles, scales and zeros."""
+    d_out = scales.shape[0]
+    src = packed if packed is not None else codes
+    if out is None:
+        out = torch.empty((d_out, d_in), dtype=out_dtype, device=src.device)
+    _check("pwq_dequant_zp", lib().pwq_dequant_zp(_p(packed), _p(codes), _p(scales), _p(zeros), _p(g_idx), d_out, d_in,
+                                                  bits, group_size, _p(out), _dtype_code(out), _stream(src)))
+    return out
+
+
 def recon_mse(X: torch.Tensor, W: torch.Tensor, scales: torch.Tensor, bits: int = 4, group_size: int = 128,
               packed: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
               g_idx: Optional[torch.Tensor] = None, mse: Optional[torch.Tensor] = None,
-              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Device float64 scalar: mean over tokens x outputs of (X (W - What)^T)^2."""
+              ws: Optional[torch.Tensor] = None, zeros: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device float64 scalar: mean over tokens x outputs of (X (W - What)^T)^2.  With
+    ``zeros``, the codes are those of the zero-point form (pwq_recon_mse_zp)."""
     ldx, ldw = _rows(X, "X"), _rows(W, "W")
     n_tok, d_in = X.shape
     d_out = W.shape[0]
@@ -238,23 +307,30 @@ def recon_mse(X: torch.Tensor, W: torch.Tensor, scales: torch.Tensor, bits: int 
     nb = lib().pwq_recon_mse_workspace_size(n_tok, d_in, d_out)
     if ws is None or ws.numel() < nb:
         ws = _ws(nb, X.device)
-    _check("pwq_recon_mse", lib().pwq_recon_mse(
-        _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
-        _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(X)))
+    if zeros is not None:
+        _check("pwq_recon_mse_zp", lib().pwq_recon_mse_zp(
+            _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
+            _p(zeros), _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(X)))
+    else:
+        _check("pwq_recon_mse", lib().pwq_recon_mse(
+            _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
+            _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(X)))
     return mse
 
 
 # ------------------------------------------------------------------ one layer, end to end
 def gptq_layer(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group_size: int = 128, block_size: int = 128,
-               damp: float = 0.01, act_order: bool = False, want_codes: bool = True, want_packed: bool = True) -> dict:
-    """The calls of one layer in order: Hessian, damping, [act-order], factor, GPTQ."""
+               damp: float = 0.01, act_order: bool = False, want_codes: bool = True, want_packed: bool = True,
+               sym: bool = True) -> dict:
+    """The calls of one layer in order: Hessian, damping, [act-order], factor, GPTQ
+    (``sym=False``: the zero-point form)."""
     d_in = W.shape[1]
     H = torch.zeros((d_in, d_in), dtype=torch.float32, device=W.device)
     hessian_accumulate(X, H)
     hessian_damp(H, damp)
     perm = act_order_perm(H) if act_order else None
     U, info = chol_inverse_upper(H, perm)
-    res = gptq_quantize_layer(W, U, info, bits, group_size, block_size, perm=perm, want_codes=want_codes,
-                              want_packed=want_packed)
+    q = gptq_quantize_layer if sym else gptq_quantize_layer_zp
+    res = q(W, U, info, bits, group_size, block_size, perm=perm, want_codes=want_codes, want_packed=want_packed)
     res.update({"H": H, "U": U, "info": info, "perm": perm})
     return res
