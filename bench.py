@@ -33,6 +33,7 @@ def parse():
     ap.add_argument("--workload", default="gpt2_block")
     ap.add_argument("--layers", default="", help="comma-separated layer names (default: all)")
     ap.add_argument("--act-order", action="store_true")
+    ap.add_argument("--zero-point", action="store_true", help="the asymmetric form (a scale and a zero per group)")
     ap.add_argument("--streams", type=int, default=1, help="1: one stream per layer (default), 0: all on one stream")
     ap.add_argument("--stagger", type=int, default=1,
                     help="1: the layer with the longest chain starts alone and the others once its Hessian is "
@@ -47,7 +48,7 @@ def parse():
 class Layer:
     """Device-resident inputs and preallocated outputs of one layer."""
 
-    def __init__(self, spec, torch, pwq, synth, act_order):
+    def __init__(self, spec, torch, pwq, synth, act_order, zero_point=False):
         import numpy as np
         self.spec = spec
         dev = "cuda:0"
@@ -67,6 +68,7 @@ class Layer:
         self.what = torch.empty((m, n), dtype=torch.float16, device=dev)
         self.mse = torch.empty(2, dtype=torch.float64, device=dev)
         self.act = act_order
+        self.zp = zero_point
         del X, W
 
 
@@ -100,19 +102,28 @@ def run_step(L, pwq, timers=None, after_hessian=None):
         k = t("act_order_perm"); perm = pwq.act_order_perm(L.H); done(k)
     k = t("chol_inverse_upper"); pwq.chol_inverse_upper(L.H, perm, U=L.U, info=L.info); done(k)
     k = t("gptq_quantize_layer")
-    pwq.gptq_quantize_layer(L.W, L.U, L.info, s.bits, s.group_size, s.block_size, perm=perm, want_codes=False,
-                            want_packed=True, out=L.gq)
+    gq = pwq.gptq_quantize_layer_zp if L.zp else pwq.gptq_quantize_layer
+    gq(L.W, L.U, L.info, s.bits, s.group_size, s.block_size, perm=perm, want_codes=False, want_packed=True, out=L.gq)
     done(k)
-    k = t("rtn_quantize"); pwq.rtn_quantize(L.W, s.bits, s.group_size, want_codes=False, out=L.rq); done(k)
-    k = t("dequant"); pwq.dequant(L.gq["scales"], s.d_in, s.bits, s.group_size, packed=L.gq["packed"],
-                                  g_idx=L.gq.get("g_idx"), out=L.what); done(k)
+    rq = pwq.rtn_quantize_zp if L.zp else pwq.rtn_quantize
+    k = t("rtn_quantize"); rq(L.W, s.bits, s.group_size, want_codes=False, out=L.rq); done(k)
+    k = t("dequant")
+    if L.zp:
+        pwq.dequant_zp(L.gq["scales"], L.gq["zeros"], s.d_in, s.bits, s.group_size, packed=L.gq["packed"],
+                       g_idx=L.gq.get("g_idx"), out=L.what)
+    else:
+        pwq.dequant(L.gq["scales"], s.d_in, s.bits, s.group_size, packed=L.gq["packed"], g_idx=L.gq.get("g_idx"),
+                    out=L.what)
+    done(k)
     k = t("recon_mse")
-    pwq.recon_mse(L.X, L.W, L.gq["scales"], s.bits, s.group_size, packed=L.gq["packed"], g_idx=L.gq.get("g_idx"), mse=L.mse[0:1])
-    pwq.recon_mse(L.X, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"], mse=L.mse[1:2])
+    pwq.recon_mse(L.X, L.W, L.gq["scales"], s.bits, s.group_size, packed=L.gq["packed"], g_idx=L.gq.get("g_idx"),
+                  mse=L.mse[0:1], zeros=L.gq.get("zeros"))
+    pwq.recon_mse(L.X, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"], mse=L.mse[1:2],
+                  zeros=L.rq.get("zeros"))
     done(k)
 
 
-def work_of(name, spec):
+def work_of(name, spec, zero_point=False):
     """(peak key, algorithmic amount of one call on one layer, unit).  Contractions count
     the flops the method needs (not what the kernels execute); codec passes the bytes they
     must move."""
@@ -120,6 +131,7 @@ def work_of(name, spec):
     xb = 4 if spec.x_dtype == "f32" else 2
     wb = 4 if spec.w_dtype == "f32" else 2
     ng = 1 if spec.group_size == 0 else -(-n // spec.group_size)
+    pg = 4 if zero_point else 2                  # bytes per group: scale (and zero)
     if name == "hessian_accumulate":            # symmetric X^T X: upper triangle + diagonal
         # float32 X with >= 1024 tokens and d_in >= 256 runs as four bfloat16 products
         bf = xb == 2 or (n >= 256 and N >= 1024)
@@ -131,9 +143,9 @@ def work_of(name, spec):
     if name == "recon_mse":                     # two calls (GPTQ and RTN) of 2 N n m, bf16 MFMA
         return "mfma_bf16", 2 * (2 * N * n * m), "flop"
     if name == "rtn_quantize":
-        return "hbm", m * n * wb + m * n // 2 + 2 * m * ng, "byte"
+        return "hbm", m * n * wb + m * n // 2 + pg * m * ng, "byte"
     if name == "dequant":
-        return "hbm", m * n // 2 + 2 * m * ng + 2 * m * n, "byte"
+        return "hbm", m * n // 2 + pg * m * ng + 2 * m * n, "byte"
     return "hbm", 0, "byte"
 
 
@@ -165,7 +177,7 @@ def traffic_of(workload, layer, call):
         return None
 
 
-def cpu_baseline(specs, synth, budget_layers):
+def cpu_baseline(specs, synth, budget_layers, zero_point=False):
     """The oracle, as it stands, on one full step of the selected layers."""
     import numpy as np
     import oracle as O
@@ -182,8 +194,8 @@ def cpu_baseline(specs, synth, budget_layers):
         W = synth.weight(s)
         X = synth.x_full(s)
         X64 = synth.as_f64(X, s.x_dtype)
-        r = O.quantize_layer(W, [X64], s.bits, s.group_size, s.block_size, s.damp, False)
-        O.dequant(r["codes"], r["scales"], s.group_size, g_idx=r["g_idx"], out_dtype=np.float16)
+        r = O.quantize_layer(W, [X64], s.bits, s.group_size, s.block_size, s.damp, False, sym=not zero_point)
+        O.dequant(r["codes"], r["scales"], s.group_size, g_idx=r["g_idx"], out_dtype=np.float16, zeros=r["zeros"])
         weights += s.n_weights
     dt = time.perf_counter() - t0
     names = [s.name for s in specs if not budget_layers or s.name in budget_layers]
@@ -224,7 +236,7 @@ def main():
     if a.layers:
         keep = set(a.layers.split(","))
         specs = [s for s in specs if s.name in keep]
-    layers = [Layer(s, torch, pwq, synth, a.act_order) for s in specs]
+    layers = [Layer(s, torch, pwq, synth, a.act_order, a.zero_point) for s in specs]
     torch.cuda.synchronize()
 
     # layers are independent: each runs on its own stream (default priority), so the
@@ -292,13 +304,13 @@ def main():
     # roofline of the dominant launch: the (layer, call) with the longest duration
     (dl, dn), dms = max(per.items(), key=lambda kv: kv[1])
     dspec = next(L.spec for L in layers if L.spec.name == dl)
-    bound, amount, unit = work_of(dn, dspec)
+    bound, amount, unit = work_of(dn, dspec, a.zero_point)
     achieved = amount / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
     peak = PEAK[bound]
     roof = {"bound": "hbm" if bound == "hbm" else "mfma", "kernel": f"pwq_{dn}", "layer": dl,
             "kernels_per_call": launches_of(dn, dspec),
             "achieved": round(achieved, 3), "peak": peak, "unit": "GB/s" if unit == "byte" else "TFLOP/s",
-            "frac": round(achieved / peak, 5), "traffic": traffic_of(a.workload, dl, dn), "launch_ms": round(dms, 4),
+            "frac": round(achieved / peak, 5), "traffic": None if a.zero_point else traffic_of(a.workload, dl, dn), "launch_ms": round(dms, 4),
             "algorithmic": amount, "peak_kind": bound}
     # the metric's X^T X MFMA utilisation, per layer
     xtx = {}
@@ -319,7 +331,7 @@ def main():
         "config": {"workload": a.workload, "layers": [f"{s.name}:{s.d_in}->{s.d_out}" for s in specs],
                    "n_tok": specs[0].n_tok, "bits": specs[0].bits, "group_size": specs[0].group_size,
                    "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order),
-                   "layer_streams": bool(a.streams), "stagger": stagger},
+                   "zero_point": bool(a.zero_point), "layer_streams": bool(a.streams), "stagger": stagger},
         "roofline": roof,
         "xtx_mfma_util": xtx,
         "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
@@ -330,7 +342,7 @@ def main():
     }
     if not a.no_cpu_baseline:
         cl = set(a.cpu_layers.split(",")) if a.cpu_layers else set()
-        out["cpu_baseline"] = cpu_baseline(specs, synth, cl)
+        out["cpu_baseline"] = cpu_baseline(specs, synth, cl, a.zero_point)
     print(json.dumps(out), flush=True)
 
 

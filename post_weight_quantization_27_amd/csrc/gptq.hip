@@ -267,7 +267,9 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
     // updates; the pins keep the compiler from sinking update chains to their last use
     // (which would keep every step's e and U values live at once).
     const bool own[4] = {p == 0, p == 1, p == 2, p == 3};
-#pragma unroll
+    // full unrolling is forced: left to its cost model the compiler keeps this loop rolled
+    // for PW = 64 and 128, and the register arrays indexed by jw then live in scratch memory
+#pragma clang loop unroll(full)
     for (int jw = 0; jw < PW; jw += 4) {
         // this lane's entries of U rows jw .. jw+3 from register jw/4 on (the aligned group
         // holding column jw: the columns left of a pivot see U = 0, a no-op update)
