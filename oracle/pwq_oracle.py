@@ -69,6 +69,9 @@ listed in the design notes):
       quotient, ties to even (R8); INT4 nibble = code itself (R10's layout otherwise).
 * A5  GPTQ with zero-points takes S and Z at a group's first column from the current
       values of the group's columns (R5), and the dequantized value S (code - Z) (R6).
+* G1  The product with the quantized weights ([GPTQ-P] "Running GPTQ with AutoGPTQ": the
+      quantized model runs inference on them) is Y = X What^T, What decoded exactly as in
+      ``dequant``; tokens x d_in times d_out x d_in gives tokens x d_out.
 
 Pins (tests/test_oracle_pins.py):
   rtn / quantize_codes / group_scales : golden tie-to-even rows, code range, error bound,
@@ -85,6 +88,8 @@ Pins (tests/test_oracle_pins.py):
   asym_scale_zero / rtn_asym / gptq(sym=False) : golden worked group (A1-A4), exact zero,
                                         error bound, range end points, 4.25 bits/weight,
                                         diagonal-H == rtn_asym, block-size invariance
+  quantized_matmul                    : brute-force sums on tiny inputs, identity X gives
+                                        What^T, rows of X against hand-dequantized rows
 """
 from __future__ import annotations
 
@@ -98,7 +103,7 @@ __all__ = [
     "gptq", "gptq_unblocked", "rtn", "pack_int4", "unpack_int4", "dequant",
     "recon_mse", "recon_mse_trace", "direct_obs", "quantize_layer", "n_groups",
     "storage_bytes", "asym_scale_zero", "quantize_codes_asym", "rtn_asym", "dequant_asym",
-    "pack_uint4", "unpack_uint4",
+    "pack_uint4", "unpack_uint4", "quantized_matmul",
 ]
 
 
@@ -470,6 +475,16 @@ def dequant_asym(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group
                  g_idx: Optional[np.ndarray] = None, out_dtype=np.float64) -> np.ndarray:
     """``dequant`` with zero-points."""
     return dequant(codes, scales, group_size, g_idx=g_idx, out_dtype=out_dtype, zeros=zeros)
+
+
+# ------------------------------------------------------------------ inference product
+
+def quantized_matmul(X: np.ndarray, codes: np.ndarray, scales: np.ndarray, group_size: int,
+                     zeros: Optional[np.ndarray] = None, g_idx: Optional[np.ndarray] = None) -> np.ndarray:
+    """Y = X What^T in float64 (G1): X tokens x d_in, codes d_out x d_in with their scales
+    (and zeros); What exact, the sum over d_in in float64."""
+    What = dequant(codes, scales, group_size, g_idx=g_idx, out_dtype=np.float64, zeros=zeros)
+    return np.asarray(X, dtype=np.float64) @ What.T
 
 
 # ------------------------------------------------------------------ error measures

@@ -553,3 +553,25 @@ def test_asym_u_form_loop_equals_direct_obs(gs):
         assert np.allclose(res["scales"].astype(np.float64), ref["scales"].astype(np.float64), rtol=0, atol=0)
     un = O.gptq_unblocked(W, U, 4, gs, sym=False)
     assert np.array_equal(un["codes"], ref["codes"])
+
+
+# ---------------------------------------------------------------------------------- f2: Y = X What^T
+def test_quantized_matmul_brute_force_and_identity():
+    rng = np.random.default_rng(70)
+    m, n, T, g = 5, 16, 3, 8
+    W = rng.normal(0, 0.02, size=(m, n))
+    for sym in (True, False):
+        r = O.rtn(W, 4, g, sym=sym)
+        X = rng.standard_normal((T, n)).astype(np.float16).astype(np.float64)
+        Y = O.quantized_matmul(X, r["codes"], r["scales"], g, zeros=r["zeros"])
+        # brute force: every output as a plain sum of x * s * (code - z), s and z looked up by hand
+        for t in range(T):
+            for o in range(m):
+                tot = 0.0
+                for c in range(n):
+                    s = float(r["scales"][o, c // g])
+                    z = 0.0 if sym else float(r["zeros"][o, c // g])
+                    tot += X[t, c] * s * (float(r["codes"][o, c]) - z)
+                assert abs(Y[t, o] - tot) <= 1e-15 * max(1.0, abs(tot))
+        # X = I gives What^T exactly
+        assert np.array_equal(O.quantized_matmul(np.eye(n), r["codes"], r["scales"], g, zeros=r["zeros"]), r["What"].T)
