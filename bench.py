@@ -39,6 +39,8 @@ def parse():
                     help="1: the layer with the longest chain starts alone and the others once its Hessian is "
                          "formed (default), 0: all layers start together")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--matmul-tokens", default="1,16",
+                    help="token counts at which Y = X What^T is timed on each layer's GPTQ output ('' to skip)")
     ap.add_argument("--cpu-layers", default="", help="layers the oracle baseline runs (default: all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (3 times), the reference for HBM traffic counters")
@@ -175,6 +177,40 @@ def traffic_of(workload, layer, call):
         return None if c is None else c["hbm_bytes"]
     except (OSError, ValueError, KeyError):
         return None
+
+
+def time_quantized_matmul(layers, pwq, torch, tokens, iters=20):
+    """Y = X What^T on each layer's packed GPTQ result (float16 X: the layer's first tokens),
+    timed with HIP events on the current stream.  Algorithmic bytes: the nibbles, the scales
+    (and zeros), X and Y, each once."""
+    out = {}
+    for L in layers:
+        s = L.spec
+        m, n = s.d_out, s.d_in
+        if n % 32 or (s.group_size and s.group_size % 128):
+            continue
+        ng = 1 if s.group_size == 0 else -(-n // s.group_size)
+        res = {}
+        for T in tokens:
+            X = L.X[:T].to(torch.float16).contiguous()
+            Y = torch.empty((T, m), dtype=torch.float16, device=X.device)
+            nb = pwq.lib().pwq_quantized_matmul_workspace_size(T, n, m)
+            ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
+            zeros = L.gq.get("zeros")
+            for _ in range(3):
+                pwq.quantized_matmul(X, L.gq["packed"], L.gq["scales"], s.group_size, zeros=zeros, out=Y, ws=ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                pwq.quantized_matmul(X, L.gq["packed"], L.gq["scales"], s.group_size, zeros=zeros, out=Y, ws=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / iters * 1e3
+            byt = m * n // 2 + m * ng * (4 if zeros is not None else 2) + T * n * 2 + T * m * 2
+            gbs = byt / (us * 1e-6) / 1e9
+            res[f"T{T}"] = {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / 8000.0, 4)}
+        out[s.name] = res
+    return out
 
 
 def cpu_baseline(specs, synth, budget_layers, zero_point=False):
@@ -320,6 +356,8 @@ def main():
         if d:
             xtx[L.spec.name] = round(amt / (d * 1e-3) / 1e12 / PEAK[bnd], 4)
     mses = {L.spec.name: [float(x) for x in L.mse.cpu().tolist()] for L in layers}
+    toks = [int(x) for x in a.matmul_tokens.split(",") if x.strip()]
+    qmm = time_quantized_matmul(layers, pwq, torch, toks) if toks else {}
 
     weights = sum(s.n_weights for s in specs)
     value = weights / (ms * 1e-3)
@@ -337,6 +375,7 @@ def main():
         "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
         "breakdown_ms_by_layer": {f"{ln}/{nm}": round(v, 4) for (ln, nm), v in sorted(per.items(), key=lambda kv: -kv[1])},
         "mse_gptq_rtn": mses,
+        "quantized_matmul": qmm,
         "wall_s_timed": round(wall, 3),
         "host_submit_ms_per_step": round(submit_ms, 3),
     }

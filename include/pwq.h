@@ -245,6 +245,31 @@ pwq_status pwq_recon_mse_zp(const void* X, int x_dtype, int64_t n_tok, int64_t d
                             const int32_t* g_idx, int64_t d_out, int32_t bits, int32_t group_size,
                             double* mse, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ product with What
+ * Y = X What^T: the quantized layer applied to activations, the inference use of the result
+ * ([GPTQ-P] "Running GPTQ with AutoGPTQ"), with What decoded on the fly from packed INT4
+ * nibbles and scales (symmetric: What = s (nibble - 8)) or, when zeros is not NULL, from
+ * the zero-point form (What = S (nibble - Z)), as pwq_dequant / pwq_dequant_zp define it.
+ * What is never rounded: each group's sum of x (code - zero) is formed from exact products
+ * (float16 MFMA on the small integer codes) and scaled once by its scale, in float32; the
+ * result is rounded once to y_dtype.
+ *   X       n_tok x d_in float16 (x_dtype PWQ_F16), leading dimension ldx (a multiple of 8),
+ *           16-byte aligned.
+ *   packed  d_out x d_in/2 (d_in a multiple of 32), 16-byte aligned; columns in their
+ *           original order (no g_idx: a layer quantized with act-order is served by its
+ *           dequantized weights).
+ *   scales, zeros  d_out x n_groups; group_size 0 (one scale per row) or a multiple of 128.
+ *   Y       n_tok x d_out, y_dtype PWQ_F32 / PWQ_F16 / PWQ_BF16, leading dimension ldy.
+ *   ws      pwq_quantized_matmul_workspace_size(n_tok, d_in, d_out) bytes (0 when the columns
+ *           are not split; then ws may be NULL).
+ * Built for few tokens (the weights are the traffic); any n_tok up to 65535 * 16 works, the
+ * weights being read once per 16 tokens. */
+size_t pwq_quantized_matmul_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out);
+pwq_status pwq_quantized_matmul(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                                const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                                int64_t d_out, int32_t group_size, void* Y, int y_dtype, int64_t ldy,
+                                void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -252,4 +252,28 @@ pwq_status pwq_recon_mse_zp(const void* X, int x_dtype, int64_t n_tok, int64_t d
                        d_out, bits, group_size, mse, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------------------------ product with What
+size_t pwq_quantized_matmul_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out) {
+    if (n_tok <= 0 || d_in <= 0 || d_out <= 0 || bad_dim(n_tok) || bad_dim(d_in) || bad_dim(d_out)) return 0;
+    return w4a16_ws_bytes(n_tok, d_in, d_out);
+}
+
+pwq_status pwq_quantized_matmul(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                                const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                                int64_t d_out, int32_t group_size, void* Y, int y_dtype, int64_t ldy,
+                                void* ws, size_t ws_bytes, void* stream) {
+    if (x_dtype != PWQ_F16) return PWQ_EDTYPE;
+    if (y_dtype != PWQ_F32 && y_dtype != PWQ_F16 && y_dtype != PWQ_BF16) return PWQ_EDTYPE;
+    if (bad_dim(n_tok) || bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldx < d_in || ldy < d_out) return PWQ_EINVAL;
+    if (n_tok > (int64_t)65535 * 16 || d_in % 32 != 0 || ldx % 8 != 0) return PWQ_EINVAL;
+    if (group_size != 0 && (group_size < 0 || group_size % 128 != 0)) return PWQ_EINVAL;
+    if (n_tok == 0 || d_out == 0) return PWQ_OK;
+    if (!packed || !scales || !Y) return PWQ_EINVAL;
+    if (!X || !aligned(X, 16) || !aligned(packed, 16)) return PWQ_EINVAL;
+    const size_t need = pwq_quantized_matmul_workspace_size(n_tok, d_in, d_out);
+    if (need && (!ws || ws_bytes < need)) return PWQ_EWORKSPACE;
+    return hip_status(w4a16_launch((const uint16_t*)X, n_tok, d_in, ldx, packed, scales, zeros, d_out, group_size, Y,
+                                   y_dtype, ldy, ws, (hipStream_t)stream));
+}
+
 }  // extern "C"

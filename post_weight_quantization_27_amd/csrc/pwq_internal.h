@@ -58,6 +58,12 @@ hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint
                           const int32_t* g_idx, int64_t m, int64_t n, int bits, int group_size, void* out,
                           int out_dtype, hipStream_t s, const uint16_t* zeros = nullptr);
 
+// Y = X What^T with the quantized weights (float16 X, decode regime).
+size_t w4a16_ws_bytes(int64_t T, int64_t n, int64_t m);
+hipError_t w4a16_launch(const uint16_t* X, int64_t T, int64_t n, int64_t ldx, const uint8_t* packed,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t m, int group_size, void* Y,
+                        int y_dtype, int64_t ldy, void* ws, hipStream_t s);
+
 // Reconstruction MSE.
 size_t mse_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out);
 hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W,

@@ -49,6 +49,7 @@ CALL_OF = [
     ("rtn_kernel", "rtn_quantize"), ("rtn_group", "rtn_quantize"),
     ("dequant_kernel", "dequant"), ("dequant_vec", "dequant"),
     ("mse_", "recon_mse"), ("EpiSq", "recon_mse"), ("set_double", "recon_mse"),
+    ("w4a16", "quantized_matmul"),
 ]
 
 

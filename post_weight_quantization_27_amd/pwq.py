@@ -57,6 +57,9 @@ _SIGS = {
     "pwq_recon_mse_zp": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
                                         _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "pwq_quantized_matmul_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "pwq_quantized_matmul": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                            _i64, _i32, _c_void_p, ctypes.c_int, _i64, _c_void_p, _sz, _c_void_p]),
     "pwq_recon_mse_workspace_size": (_sz, [_i64, _i64, _i64]),
     "pwq_recon_mse": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
@@ -316,6 +319,26 @@ def recon_mse(X: torch.Tensor, W: torch.Tensor, scales: torch.Tensor, bits: int 
             _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
             _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(X)))
     return mse
+
+
+# ------------------------------------------------------------------ product with What
+def quantized_matmul(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, group_size: int = 128,
+                     zeros: Optional[torch.Tensor] = None, out_dtype=torch.float16, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X What^T (X float16 tokens x d_in; What from packed nibbles, scales and optional zeros)."""
+    ldx = _rows(X, "X")
+    n_tok, d_in = X.shape
+    d_out = packed.shape[0]
+    if out is None:
+        out = torch.empty((n_tok, d_out), dtype=out_dtype, device=X.device)
+    ldy = _rows(out, "Y") if n_tok > 0 else d_out
+    nb = lib().pwq_quantized_matmul_workspace_size(n_tok, d_in, d_out)
+    if nb and (ws is None or ws.numel() < nb):
+        ws = _ws(nb, X.device)
+    _check("pwq_quantized_matmul", lib().pwq_quantized_matmul(
+        _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(packed), _p(scales), _p(zeros), d_out, group_size, _p(out),
+        _dtype_code(out), ldy, _p(ws) if nb else None, nb, _stream(X)))
+    return out
 
 
 # ------------------------------------------------------------------ one layer, end to end
