@@ -69,6 +69,10 @@ listed in the design notes):
       quotient, ties to even (R8); INT4 nibble = code itself (R10's layout otherwise).
 * A5  GPTQ with zero-points takes S and Z at a group's first column from the current
       values of the group's columns (R5), and the dequantized value S (code - Z) (R6).
+* T1  Per-tensor quantization ([GPT2-RE] "Possible extensions": per-channel against a single
+      global scale): one quantizer for the whole matrix, taken from the original W like the
+      per-row one (R5), by the per-row rules (R7, A2-A3) applied to the whole tensor; it is
+      stored as the per-row format with every row holding the same scale (and zero).
 * G1  The product with the quantized weights ([GPTQ-P] "Running GPTQ with AutoGPTQ": the
       quantized model runs inference on them) is Y = X What^T, What decoded exactly as in
       ``dequant``; tokens x d_in times d_out x d_in gives tokens x d_out.
@@ -90,6 +94,9 @@ Pins (tests/test_oracle_pins.py):
                                         diagonal-H == rtn_asym, block-size invariance
   quantized_matmul                    : brute-force sums on tiny inputs, identity X gives
                                         What^T, rows of X against hand-dequantized rows
+  tensor_scales                       : the per-row rule on the flattened matrix; the
+                                        tensor's absmax element maps to +-qmax; GPTQ with a
+                                        diagonal H and these scales equals RTN with them
 """
 from __future__ import annotations
 
@@ -103,7 +110,7 @@ __all__ = [
     "gptq", "gptq_unblocked", "rtn", "pack_int4", "unpack_int4", "dequant",
     "recon_mse", "recon_mse_trace", "direct_obs", "quantize_layer", "n_groups",
     "storage_bytes", "asym_scale_zero", "quantize_codes_asym", "rtn_asym", "dequant_asym",
-    "pack_uint4", "unpack_uint4", "quantized_matmul",
+    "pack_uint4", "unpack_uint4", "quantized_matmul", "tensor_scales",
 ]
 
 
@@ -188,6 +195,18 @@ def _group_params(vals: np.ndarray, bits: int, sym: bool):
     lo = np.minimum(np.min(vals, axis=1), 0.0)
     hi = np.maximum(np.max(vals, axis=1), 0.0)
     return asym_scale_zero(lo, hi, bits)
+
+
+def tensor_scales(W: np.ndarray, bits: int, sym: bool = True):
+    """One quantizer for the whole matrix (T1), replicated per row: (scales d_out x 1
+    float16, zeros d_out x 1 uint16 or None).  Use with group_size 0 and fixed scales."""
+    W = np.asarray(W, dtype=np.float64)
+    m = W.shape[0]
+    flat = W.reshape(1, -1)
+    s, z = _group_params(flat, bits, sym)
+    scales = np.full((m, 1), s[0], dtype=np.float16)
+    zeros = None if sym else np.full((m, 1), z[0], dtype=np.uint16)
+    return scales, zeros
 
 
 def _codes(w, s16, z, bits: int, sym: bool):

@@ -575,3 +575,27 @@ def test_quantized_matmul_brute_force_and_identity():
                 assert abs(Y[t, o] - tot) <= 1e-15 * max(1.0, abs(tot))
         # X = I gives What^T exactly
         assert np.array_equal(O.quantized_matmul(np.eye(n), r["codes"], r["scales"], g, zeros=r["zeros"]), r["What"].T)
+
+
+# ---------------------------------------------------------------------------------- f4: per tensor
+def test_tensor_scales_closed_form_and_reductions():
+    rng = np.random.default_rng(90)
+    W = rng.normal(0, 0.02, size=(48, 256)).astype(np.float32)
+    W[7, 100] = 0.3                                         # the tensor's absmax
+    s, z = O.tensor_scales(W, 4)
+    assert z is None and s.shape == (48, 1) and np.all(s == s[0, 0])
+    q32 = _rne_to_precision(Fraction(float(np.float32(0.3))) / 7, 24, -126)
+    assert Fraction(float(s[0, 0])) == _rne_to_precision(q32, 11, -14)
+    r = O.rtn(W, 4, 0, scales_in=s)
+    assert r["codes"][7, 100] == 7 and np.abs(r["codes"]).max() == 7
+    # the tensor's absmax sets the scale, so no weight is clamped: every error is within s / 2
+    err_t = np.abs(W - r["What"]).max(axis=1)
+    assert np.all(err_t <= float(s[0, 0]) / 2 + 1e-12)
+    # zero-point form: the flattened range, exact rationals
+    s2, z2 = O.tensor_scales(W, 4, sym=False)
+    ws, wz = _asym_closed_form(float(W.min()), float(W.max()), 4)
+    assert Fraction(float(s2[0, 0])) == ws and int(z2[0, 0]) == wz and np.all(z2 == z2[0, 0])
+    # GPTQ with a diagonal H and the tensor's scales equals RTN with them
+    Hd, _ = O.damp_hessian(O.hessian(np.diag(rng.uniform(0.5, 3.0, 256))), 0.01)
+    g = O.gptq(W, O.chol_inverse_upper(Hd), 4, 0, 128, scales_in=s)
+    assert np.array_equal(g["codes"], r["codes"])
