@@ -213,6 +213,25 @@ def time_quantized_matmul(layers, pwq, torch, tokens, iters=20):
     return out
 
 
+def time_tensor_scales(layers, pwq, torch, iters=20):
+    """The per-tensor quantizer's pass over each layer's W (algorithmic bytes: W once)."""
+    out = {}
+    for L in layers:
+        s = L.spec
+        for _ in range(3):
+            pwq.tensor_scales(L.W, s.bits, zero_point=L.zp)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            pwq.tensor_scales(L.W, s.bits, zero_point=L.zp)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        byt = s.d_out * s.d_in * L.W.element_size()
+        out[s.name] = {"us": round(us, 2), "GB/s": round(byt / (us * 1e-6) / 1e9, 1)}
+    return out
+
+
 def cpu_baseline(specs, synth, budget_layers, zero_point=False):
     """The oracle, as it stands, on one full step of the selected layers."""
     import numpy as np
@@ -358,6 +377,7 @@ def main():
     mses = {L.spec.name: [float(x) for x in L.mse.cpu().tolist()] for L in layers}
     toks = [int(x) for x in a.matmul_tokens.split(",") if x.strip()]
     qmm = time_quantized_matmul(layers, pwq, torch, toks) if toks else {}
+    pts = time_tensor_scales(layers, pwq, torch) if toks else {}
 
     weights = sum(s.n_weights for s in specs)
     value = weights / (ms * 1e-3)
@@ -376,6 +396,7 @@ def main():
         "breakdown_ms_by_layer": {f"{ln}/{nm}": round(v, 4) for (ln, nm), v in sorted(per.items(), key=lambda kv: -kv[1])},
         "mse_gptq_rtn": mses,
         "quantized_matmul": qmm,
+        "tensor_scales": pts,
         "wall_s_timed": round(wall, 3),
         "host_submit_ms_per_step": round(submit_ms, 3),
     }

@@ -245,6 +245,19 @@ pwq_status pwq_recon_mse_zp(const void* X, int x_dtype, int64_t n_tok, int64_t d
                             const int32_t* g_idx, int64_t d_out, int32_t bits, int32_t group_size,
                             double* mse, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ per-tensor quantizer
+ * One quantizer for the whole matrix, the per-tensor alternative to per-channel scales of
+ * [GPT2-RE] "Possible extensions": from the original W, s = fp16(fp32(max |w|) / qmax)
+ * (zeros_out NULL), or the zero-point pair of the range [min(w, 0), max(w, 0)] of the whole
+ * tensor (zeros_out given), by the same rules as the per-row quantizers.  It is written in
+ * the per-row format, every row holding the same value: scales_out (and zeros_out) are
+ * d_out x 1, to be passed as fixed scales (and zeros) with group_size 0 to the RTN and GPTQ
+ * calls; dequant and the MSE then read them unchanged.
+ *   ws   pwq_tensor_scales_workspace_size() bytes. */
+size_t pwq_tensor_scales_workspace_size(void);
+pwq_status pwq_tensor_scales(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
+                             uint16_t* scales_out, uint16_t* zeros_out, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ product with What
  * Y = X What^T: the quantized layer applied to activations, the inference use of the result
  * ([GPTQ-P] "Running GPTQ with AutoGPTQ"), with What decoded on the fly from packed INT4

@@ -252,6 +252,21 @@ pwq_status pwq_recon_mse_zp(const void* X, int x_dtype, int64_t n_tok, int64_t d
                        d_out, bits, group_size, mse, ws, ws_bytes, stream);
 }
 
+// ------------------------------------------------------------------ per-tensor quantizer
+size_t pwq_tensor_scales_workspace_size(void) { return tensor_scales_ws_bytes(); }
+
+pwq_status pwq_tensor_scales(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
+                             uint16_t* scales_out, uint16_t* zeros_out, void* ws, size_t ws_bytes, void* stream) {
+    if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
+    if (bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldw < d_in || bits < 2 || bits > 8) return PWQ_EINVAL;
+    if (!scales_out) return PWQ_EINVAL;
+    if (d_out == 0) return PWQ_OK;
+    if (!W) return PWQ_EINVAL;
+    if (!ws || ws_bytes < tensor_scales_ws_bytes()) return PWQ_EWORKSPACE;
+    return hip_status(tensor_scales_launch(W, w_dtype, d_out, d_in, ldw, bits, scales_out, zeros_out, ws,
+                                           (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ product with What
 size_t pwq_quantized_matmul_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out) {
     if (n_tok <= 0 || d_in <= 0 || d_out <= 0 || bad_dim(n_tok) || bad_dim(d_in) || bad_dim(d_out)) return 0;

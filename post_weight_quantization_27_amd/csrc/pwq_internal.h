@@ -58,6 +58,11 @@ hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint
                           const int32_t* g_idx, int64_t m, int64_t n, int bits, int group_size, void* out,
                           int out_dtype, hipStream_t s, const uint16_t* zeros = nullptr);
 
+// Per-tensor quantizer, replicated per row.
+size_t tensor_scales_ws_bytes();
+hipError_t tensor_scales_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, int bits,
+                                uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t s);
+
 // Y = X What^T with the quantized weights (float16 X, decode regime).
 size_t w4a16_ws_bytes(int64_t T, int64_t n, int64_t m);
 hipError_t w4a16_launch(const uint16_t* X, int64_t T, int64_t n, int64_t ldx, const uint8_t* packed,

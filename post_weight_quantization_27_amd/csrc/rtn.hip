@@ -438,7 +438,97 @@ int64_t resident_blocks(int64_t want) {
     return want < cap ? (want > 0 ? want : 1) : cap;
 }
 
+// Per-tensor quantizer, first pass: the maxima of |w| (symmetric) or of w and -w (zero-point,
+// each at least 0) over rows blockIdx.x, blockIdx.x + gridDim.x, ...; one pair per workgroup.
+template <int DT>
+__global__ __launch_bounds__(256) void tensor_max_kernel(const void* __restrict__ Wv, int64_t ldw, int64_t m, int64_t n,
+                                                         int vec, float2* __restrict__ part) {
+    typedef typename Elem<DT>::T T;
+    __shared__ float2 red[4];
+    float hi = 0.f, nlo = 0.f;
+    for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
+        const T* row = (const T*)Wv + r * ldw;
+        if (vec) {
+            for (int64_t c = 4 * (int64_t)threadIdx.x; c < n; c += 4 * 256) {
+                const float4 v = Elem<DT>::get4(row, c);
+                hi = fmaxf(hi, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+                nlo = fmaxf(nlo, fmaxf(fmaxf(-v.x, -v.y), fmaxf(-v.z, -v.w)));
+            }
+        } else {
+            for (int64_t c = threadIdx.x; c < n; c += 256) {
+                const float v = Elem<DT>::get(row, c);
+                hi = fmaxf(hi, v);
+                nlo = fmaxf(nlo, -v);
+            }
+        }
+    }
+    hi = wave_max(hi);
+    nlo = wave_max(nlo);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(hi, nlo);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float2 t = red[0];
+        for (int w = 1; w < 4; ++w) t = make_float2(fmaxf(t.x, red[w].x), fmaxf(t.y, red[w].y));
+        part[blockIdx.x] = t;
+    }
+}
+
+// Second pass (one workgroup): the tensor's quantizer from the partial maxima, written to
+// every row (the per-row format with one shared value).  Maxima are order-independent, so
+// the result does not depend on the split into workgroups.
+__global__ __launch_bounds__(256) void tensor_scale_kernel(const float2* __restrict__ part, int nparts, int64_t m, int bits,
+                                                           uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
+    __shared__ float2 red[4];
+    __shared__ uint16_t sz[2];
+    float hi = 0.f, nlo = 0.f;
+    for (int k = threadIdx.x; k < nparts; k += 256) {
+        hi = fmaxf(hi, part[k].x);
+        nlo = fmaxf(nlo, part[k].y);
+    }
+    hi = wave_max(hi);
+    nlo = wave_max(nlo);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(hi, nlo);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float2 t = red[0];
+        for (int w = 1; w < 4; ++w) t = make_float2(fmaxf(t.x, red[w].x), fmaxf(t.y, red[w].y));
+        if (zeros) {
+            const int top = (1 << bits) - 1;
+            const uint16_t sb = zp_scale_bits(t.y, t.x, top);
+            sz[0] = sb;
+            sz[1] = (uint16_t)zp_zero(t.y, f16_bits_to_f32(sb), (float)top);
+        } else {
+            sz[0] = scale_bits_from_absmax(fmaxf(t.x, t.y), (1 << (bits - 1)) - 1);
+            sz[1] = 0;
+        }
+    }
+    __syncthreads();
+    for (int64_t r = threadIdx.x; r < m; r += 256) {
+        scales[r] = sz[0];
+        if (zeros) zeros[r] = sz[1];
+    }
+}
+
 }  // namespace
+
+constexpr int TENSOR_PARTS = 1024;
+
+size_t tensor_scales_ws_bytes() { return TENSOR_PARTS * sizeof(float2); }
+
+hipError_t tensor_scales_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, int bits,
+                                uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t s) {
+    if (m == 0) return hipSuccess;
+    const int nb = (int)(m < TENSOR_PARTS ? m : TENSOR_PARTS);
+    const size_t es = w_dtype == 0 ? 4 : 2;
+    const int vec = (n % 4 == 0) && (ldw % 4 == 0) && aligned(W, 4 * es);
+    float2* part = (float2*)ws;
+    if (w_dtype == 0) hipLaunchKernelGGL(tensor_max_kernel<0>, dim3(nb), dim3(256), 0, s, W, ldw, m, n, vec, part);
+    else hipLaunchKernelGGL(tensor_max_kernel<1>, dim3(nb), dim3(256), 0, s, W, ldw, m, n, vec, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, s, part, nb, m, bits, scales, zeros);
+    return hipGetLastError();
+}
 
 hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, int bits, int group_size,
                       const uint16_t* scales_in, int8_t* codes, uint8_t* packed, uint16_t* scales_out, hipStream_t s,

@@ -57,6 +57,9 @@ _SIGS = {
     "pwq_recon_mse_zp": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
                                         _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "pwq_tensor_scales_workspace_size": (_sz, []),
+    "pwq_tensor_scales": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _i32, _c_void_p, _c_void_p,
+                                         _c_void_p, _sz, _c_void_p]),
     "pwq_quantized_matmul_workspace_size": (_sz, [_i64, _i64, _i64]),
     "pwq_quantized_matmul": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                             _i64, _i32, _c_void_p, ctypes.c_int, _i64, _c_void_p, _sz, _c_void_p]),
@@ -319,6 +322,21 @@ def recon_mse(X: torch.Tensor, W: torch.Tensor, scales: torch.Tensor, bits: int 
             _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
             _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(X)))
     return mse
+
+
+# ------------------------------------------------------------------ per-tensor quantizer
+def tensor_scales(W: torch.Tensor, bits: int = 4, zero_point: bool = False):
+    """(scales d_out x 1 float16, zeros d_out x 1 int16 or None): one quantizer for the whole
+    matrix, replicated per row; pass them as fixed scales (and zeros) with group_size 0."""
+    ldw = _rows(W, "W")
+    d_out, d_in = W.shape
+    scales = torch.empty((d_out, 1), dtype=torch.float16, device=W.device)
+    zeros = torch.empty((d_out, 1), dtype=torch.int16, device=W.device) if zero_point else None
+    nb = lib().pwq_tensor_scales_workspace_size()
+    ws = _ws(nb, W.device)
+    _check("pwq_tensor_scales", lib().pwq_tensor_scales(_p(W), _dtype_code(W), d_out, d_in, ldw, bits, _p(scales),
+                                                        _p(zeros), _p(ws), nb, _stream(W)))
+    return scales, zeros
 
 
 # ------------------------------------------------------------------ product with What
