@@ -73,6 +73,15 @@ listed in the design notes):
       global scale): one quantizer for the whole matrix, taken from the original W like the
       per-row one (R5), by the per-row rules (R7, A2-A3) applied to the whole tensor; it is
       stored as the per-row format with every row holding the same scale (and zero).
+* W1  Activation-aware channel scaling ([MQM] 2.2 "AWQ": salience from the size of a column's
+      input activations; W's column multiplied and X's column divided by a per-channel s, the
+      layer output unchanged; [GPT2-RE] "Possible extensions": scale up the important
+      channels before quantizing).  The pages give no rule for s.  Reading taken: the size
+      of input channel c is a_c = mean over tokens of |X_tc| (a_c = 0 gives s_c = 1),
+      s_c = a_c^alpha, alpha on the grid k / (K - 1), k = 0 .. K - 1 (alpha = 0 is plain
+      RTN); for each alpha, RTN of W diag(s), What = dequant / s column-wise, scored by the
+      reconstruction MSE with the original W and X (R11); the least MSE wins, ties to the
+      smaller alpha.
 * G1  The product with the quantized weights ([GPTQ-P] "Running GPTQ with AutoGPTQ": the
       quantized model runs inference on them) is Y = X What^T, What decoded exactly as in
       ``dequant``; tokens x d_in times d_out x d_in gives tokens x d_out.
@@ -94,6 +103,10 @@ Pins (tests/test_oracle_pins.py):
                                         diagonal-H == rtn_asym, block-size invariance
   quantized_matmul                    : brute-force sums on tiny inputs, identity X gives
                                         What^T, rows of X against hand-dequantized rows
+  channel_abs_mean / awq_search       : brute-force column means; alpha = 0 reproduces RTN
+                                        exactly; every candidate's score equals the trace
+                                        identity with H; the output of X / s through W s is
+                                        X W^T; an outlier channel is protected
   tensor_scales                       : the per-row rule on the flattened matrix; the
                                         tensor's absmax element maps to +-qmax; GPTQ with a
                                         diagonal H and these scales equals RTN with them
@@ -110,7 +123,8 @@ __all__ = [
     "gptq", "gptq_unblocked", "rtn", "pack_int4", "unpack_int4", "dequant",
     "recon_mse", "recon_mse_trace", "direct_obs", "quantize_layer", "n_groups",
     "storage_bytes", "asym_scale_zero", "quantize_codes_asym", "rtn_asym", "dequant_asym",
-    "pack_uint4", "unpack_uint4", "quantized_matmul", "tensor_scales",
+    "pack_uint4", "unpack_uint4", "quantized_matmul", "tensor_scales", "channel_abs_mean",
+    "awq_scales", "awq_search",
 ]
 
 
@@ -494,6 +508,50 @@ def dequant_asym(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group
                  g_idx: Optional[np.ndarray] = None, out_dtype=np.float64) -> np.ndarray:
     """``dequant`` with zero-points."""
     return dequant(codes, scales, group_size, g_idx=g_idx, out_dtype=out_dtype, zeros=zeros)
+
+
+# ------------------------------------------------------------------ activation-aware scaling
+
+def channel_abs_mean(x_tiles: Union[np.ndarray, Iterable[np.ndarray]]) -> np.ndarray:
+    """a_c = mean over all tokens of |X_tc| (W1), float64."""
+    if isinstance(x_tiles, np.ndarray):
+        x_tiles = [x_tiles]
+    tot, ntok = None, 0
+    for xt in x_tiles:
+        x = np.abs(np.asarray(xt, dtype=np.float64))
+        tot = x.sum(axis=0) if tot is None else tot + x.sum(axis=0)
+        ntok += x.shape[0]
+    return tot / ntok
+
+
+def awq_scales(a: np.ndarray, alpha: float) -> np.ndarray:
+    """s_c = a_c^alpha, 1 where a_c = 0 (W1)."""
+    a = np.asarray(a, dtype=np.float64)
+    return np.where(a > 0, np.power(np.where(a > 0, a, 1.0), alpha), 1.0)
+
+
+def awq_search(W: np.ndarray, x_tiles, bits: int = 4, group_size: int = 128, n_alpha: int = 21,
+               sym: bool = True) -> dict:
+    """The grid search of W1 with RTN as the quantizer.  Returns the scores of every alpha,
+    the winner's index, alpha and s, and the RTN result of W diag(s) (codes, scales, zeros)
+    with What = its dequantization divided by s."""
+    if isinstance(x_tiles, np.ndarray):
+        x_tiles = [x_tiles]
+    x_tiles = list(x_tiles)
+    W = np.asarray(W, dtype=np.float64)
+    a = channel_abs_mean(x_tiles)
+    mses, results = [], []
+    for k in range(n_alpha):
+        alpha = k / (n_alpha - 1) if n_alpha > 1 else 0.0
+        s = awq_scales(a, alpha)
+        r = rtn(W * s[None, :], bits, group_size, sym=sym)
+        What = r["What"] / s[None, :]
+        mses.append(recon_mse(x_tiles, W, What))
+        results.append((alpha, s, r, What))
+    best = int(np.argmin(mses))                      # first minimum: ties to the smaller alpha
+    alpha, s, r, What = results[best]
+    return {"mse": np.array(mses), "best": best, "alpha": alpha, "s": s, "abs_mean": a,
+            "codes": r["codes"], "scales": r["scales"], "zeros": r["zeros"], "What": What}
 
 
 # ------------------------------------------------------------------ inference product

@@ -175,3 +175,27 @@ def test_offset_nibble_fails_unsigned_pack_pin(monkeypatch):
     monkeypatch.setattr(O, "pack_uint4", bad_pack)
     with pytest.raises(AssertionError):
         P.test_asym_pack_layout_and_storage()
+
+
+def test_awq_wrong_scale_direction_fails_pin(monkeypatch):
+    """Shrinking the salient channel (s = a^-alpha) instead of growing it."""
+    good = OM.awq_scales
+    monkeypatch.setattr(OM, "awq_scales", lambda a, alpha: good(a, -alpha))
+    with pytest.raises(AssertionError):
+        P.test_awq_search_pins()
+
+
+def test_awq_unscaled_reconstruction_fails_pin(monkeypatch):
+    """Scoring W diag(s)'s quantization without dividing by s again."""
+    def bad_search(W, x_tiles, bits=4, group_size=128, n_alpha=21, sym=True):
+        res = good(W, x_tiles, bits, group_size, n_alpha, sym)
+        X = x_tiles if isinstance(x_tiles, np.ndarray) else np.concatenate(list(x_tiles))
+        a = OM.channel_abs_mean(X)
+        for k in range(n_alpha):
+            s = OM.awq_scales(a, k / (n_alpha - 1))
+            res["mse"][k] = OM.recon_mse(X, W, OM.rtn(np.asarray(W) * s, bits, group_size, sym=sym)["What"])
+        return res
+    good = OM.awq_search
+    monkeypatch.setattr(O, "awq_search", bad_search)
+    with pytest.raises(AssertionError):
+        P.test_awq_search_pins()

@@ -599,3 +599,37 @@ def test_tensor_scales_closed_form_and_reductions():
     Hd, _ = O.damp_hessian(O.hessian(np.diag(rng.uniform(0.5, 3.0, 256))), 0.01)
     g = O.gptq(W, O.chol_inverse_upper(Hd), 4, 0, 128, scales_in=s)
     assert np.array_equal(g["codes"], r["codes"])
+
+
+# ---------------------------------------------------------------------------------- f3: AWQ scaling
+def test_awq_search_pins():
+    rng = np.random.default_rng(95)
+    n, m, N = 64, 40, 500
+    X = rng.standard_normal((N, n))
+    X[:, 5] *= 30.0                                          # one salient input channel
+    X[:, 9] = 0.0                                            # a dead channel: s = 1
+    W = rng.normal(0, 0.02, size=(m, n))
+    # channel means by brute force
+    a = O.channel_abs_mean([X[:200], X[200:]])
+    for c in (0, 5, 9):
+        assert abs(a[c] - sum(abs(X[t, c]) for t in range(N)) / N) <= 1e-12 * max(1.0, a[c])
+    res = O.awq_search(W, X, 4, 16, n_alpha=11)
+    # alpha = 0 is plain RTN, exactly
+    r0 = O.rtn(W, 4, 16)
+    assert res["mse"][0] == O.recon_mse(X, W, r0["What"])
+    assert res["mse"][res["best"]] <= res["mse"][0]
+    # every candidate's score is the trace identity with H
+    H = O.hessian(X)
+    for k in (0, 4, 10):
+        s = O.awq_scales(a, k / 10)
+        rk = O.rtn(W * s, 4, 16)
+        dW_what = rk["What"] / s
+        assert abs(res["mse"][k] - O.recon_mse_trace(H, N, W, dW_what)) <= 1e-9 * res["mse"][k]
+    # the transformation leaves the layer unchanged before quantization: (X / s) (W s)^T = X W^T
+    s = res["s"]
+    assert np.allclose((X / s) @ (W * s).T, X @ W.T, rtol=1e-12, atol=1e-12)
+    assert s[9] == 1.0
+    # the salient channel is protected: its weights' error shrinks against plain RTN
+    e_awq = np.abs(W[:, 5] - res["What"][:, 5]).mean()
+    e_rtn = np.abs(W[:, 5] - r0["What"][:, 5]).mean()
+    assert res["best"] > 0 and e_awq < e_rtn
