@@ -39,6 +39,8 @@ def parse():
                     help="1: the layer with the longest chain starts alone and the others once its Hessian is "
                          "formed (default), 0: all layers start together")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--awq-alphas", type=int, default=21,
+                    help="grid size of the activation-aware scaling search timed per layer (0 to skip)")
     ap.add_argument("--matmul-tokens", default="1,16",
                     help="token counts at which Y = X What^T is timed on each layer's GPTQ output ('' to skip)")
     ap.add_argument("--cpu-layers", default="", help="layers the oracle baseline runs (default: all)")
@@ -213,6 +215,33 @@ def time_quantized_matmul(layers, pwq, torch, tokens, iters=20):
     return out
 
 
+def time_awq(layers, pwq, torch, K):
+    """Activation-aware scaling per layer: channel means of |X| and the K-candidate search
+    (undamped H formed first, outside the timed span).  Algorithmic work of the scoring
+    products: 2 m n^2 flop per candidate on the float32 MFMA engine."""
+    out = {}
+    for L in layers:
+        s = L.spec
+        L.H.zero_()
+        pwq.hessian_accumulate(L.X, L.H)
+        pwq.awq_search(L.W, L.H, s.n_tok, pwq.channel_abs_mean(L.X), s.bits, s.group_size, K, zero_point=L.zp)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        a = pwq.channel_abs_mean(L.X)
+        r = pwq.awq_search(L.W, L.H, s.n_tok, a, s.bits, s.group_size, K, zero_point=L.zp)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        mse = r["mse"].cpu().tolist()
+        best = int(r["best"].item())
+        flop = 2.0 * s.d_out * s.d_in * s.d_in * K
+        out[s.name] = {"ms": round(ms, 3), "alpha": round(best / (K - 1), 3) if K > 1 else 0.0,
+                       "mse_rtn": mse[0], "mse_awq": mse[best],
+                       "score_tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                       "score_frac_fp32": round(flop / (ms * 1e-3) / 1e12 / PEAK["mfma_f32"], 4)}
+    return out
+
+
 def time_tensor_scales(layers, pwq, torch, iters=20):
     """The per-tensor quantizer's pass over each layer's W (algorithmic bytes: W once)."""
     out = {}
@@ -378,6 +407,7 @@ def main():
     toks = [int(x) for x in a.matmul_tokens.split(",") if x.strip()]
     qmm = time_quantized_matmul(layers, pwq, torch, toks) if toks else {}
     pts = time_tensor_scales(layers, pwq, torch) if toks else {}
+    awq = time_awq(layers, pwq, torch, a.awq_alphas) if a.awq_alphas > 0 else {}
 
     weights = sum(s.n_weights for s in specs)
     value = weights / (ms * 1e-3)
@@ -397,6 +427,7 @@ def main():
         "mse_gptq_rtn": mses,
         "quantized_matmul": qmm,
         "tensor_scales": pts,
+        "awq": awq,
         "wall_s_timed": round(wall, 3),
         "host_submit_ms_per_step": round(submit_ms, 3),
     }

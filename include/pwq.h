@@ -258,6 +258,43 @@ size_t pwq_tensor_scales_workspace_size(void);
 pwq_status pwq_tensor_scales(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
                              uint16_t* scales_out, uint16_t* zeros_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ activation-aware scaling
+ * [MQM] 2.2 "AWQ": salience of a weight comes from the size of its input activations; a
+ * per-channel s multiplies W's column and divides X's column, leaving the layer output
+ * unchanged, so that salient channels lose less to rounding ([GPT2-RE] "Possible
+ * extensions": scale up the important channels before quantizing).  The pages give no rule
+ * for s; these calls take s_c = a_c^alpha with a_c the mean over tokens of |X_tc| (s_c = 1
+ * where a_c = 0) and choose alpha on a grid by the reconstruction MSE.
+ *
+ * pwq_channel_abs_mean: abs_mean[c] = mean over the n_tok tokens of |X[t][c]| (float32
+ * result of float64 sums; X float32 or bfloat16, leading dimension ldx).
+ *   ws  pwq_channel_abs_mean_workspace_size(n_tok, d_in) bytes. */
+size_t pwq_channel_abs_mean_workspace_size(int64_t n_tok, int64_t d_in);
+pwq_status pwq_channel_abs_mean(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* abs_mean,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* pwq_awq_search: for alpha_k = k / (n_alpha - 1), k = 0 .. n_alpha - 1 (alpha_0 = 0 is
+ * plain RTN), s = abs_mean^alpha_k (double pow rounded once to float32), What = RTN of
+ * W diag(s) (the rules of pwq_rtn_quantize, or of pwq_rtn_quantize_zp when zero_point)
+ * divided column-wise by s, and
+ *   mse_out[k] = tr((W - What) H (W - What)^T) / (2 n_tok d_out),
+ * the reconstruction MSE of pwq_recon_mse through H = 2 X^T X.  best_out = the first k of
+ * least score; s_out = its s (float32, d_in); codes / packed / scales_out (/ zeros_out) =
+ * RTN of W diag(s_out) in the output formats of the RTN calls (codes are int8 symmetric or
+ * uint8 zero-point bytes).  At inference X is divided by s_out column-wise.
+ *   H         d_in x d_in float32 from pwq_hessian_accumulate BEFORE damping (the score
+ *             is the reconstruction error of the calibration set), both triangles.
+ *   abs_mean  from pwq_channel_abs_mean over the same tokens; n_tok their number.
+ *   mse_out   device double[n_alpha]; best_out device int32.
+ *   ws        pwq_awq_search_workspace_size(d_out, d_in) bytes.
+ * Each candidate costs one d_out x d_in x d_in float32 MFMA product. */
+size_t pwq_awq_search_workspace_size(int64_t d_out, int64_t d_in);
+pwq_status pwq_awq_search(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, const float* H,
+                          int64_t n_tok, const float* abs_mean, int32_t bits, int32_t group_size, int32_t n_alpha,
+                          int32_t zero_point, double* mse_out, int32_t* best_out, float* s_out, void* codes,
+                          uint8_t* packed, uint16_t* scales_out, uint16_t* zeros_out, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* ------------------------------------------------------------------ product with What
  * Y = X What^T: the quantized layer applied to activations, the inference use of the result
  * ([GPTQ-P] "Running GPTQ with AutoGPTQ"), with What decoded on the fly from packed INT4

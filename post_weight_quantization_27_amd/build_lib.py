@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpwq.so")
 
-SOURCES = ["hessian.hip", "chol.hip", "gptq.hip", "rtn.hip", "mse.hip", "w4a16.hip", "pwq_api.hip"]
+SOURCES = ["hessian.hip", "chol.hip", "gptq.hip", "rtn.hip", "mse.hip", "w4a16.hip", "awq.hip", "pwq_api.hip"]
 ARCH = os.environ.get("PWQ_OFFLOAD_ARCH", "gfx950")
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

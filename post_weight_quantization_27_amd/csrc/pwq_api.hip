@@ -267,6 +267,45 @@ pwq_status pwq_tensor_scales(const void* W, int w_dtype, int64_t d_out, int64_t 
                                            (hipStream_t)stream));
 }
 
+// ------------------------------------------------------------------ activation-aware scaling
+size_t pwq_channel_abs_mean_workspace_size(int64_t n_tok, int64_t d_in) {
+    if (n_tok <= 0 || d_in <= 0 || bad_dim(n_tok) || bad_dim(d_in)) return 0;
+    return chan_abs_ws_bytes(n_tok, d_in);
+}
+
+pwq_status pwq_channel_abs_mean(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, float* abs_mean,
+                                void* ws, size_t ws_bytes, void* stream) {
+    if (x_dtype != PWQ_F32 && x_dtype != PWQ_BF16) return PWQ_EDTYPE;
+    if (n_tok <= 0 || bad_dim(n_tok) || n_tok > (int64_t)65535 * 1024 || d_in <= 0 || bad_dim(d_in) || ldx < d_in)
+        return PWQ_EINVAL;
+    if (!X || !abs_mean) return PWQ_EINVAL;
+    if (!ws || ws_bytes < pwq_channel_abs_mean_workspace_size(n_tok, d_in)) return PWQ_EWORKSPACE;
+    return hip_status(chan_abs_launch(X, x_dtype, n_tok, d_in, ldx, abs_mean, ws, (hipStream_t)stream));
+}
+
+size_t pwq_awq_search_workspace_size(int64_t d_out, int64_t d_in) {
+    if (d_out <= 0 || d_in <= 0 || bad_dim(d_out) || bad_dim(d_in)) return 0;
+    return awq_ws_bytes(d_out, d_in);
+}
+
+pwq_status pwq_awq_search(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, const float* H,
+                          int64_t n_tok, const float* abs_mean, int32_t bits, int32_t group_size, int32_t n_alpha,
+                          int32_t zero_point, double* mse_out, int32_t* best_out, float* s_out, void* codes,
+                          uint8_t* packed, uint16_t* scales_out, uint16_t* zeros_out, void* ws, size_t ws_bytes,
+                          void* stream) {
+    if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
+    if (d_out <= 0 || bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldw < d_in || n_tok <= 0) return PWQ_EINVAL;
+    if (bits < 2 || bits > 8 || !group_ok(group_size, d_in) || n_alpha < 1 || n_alpha > 1024) return PWQ_EINVAL;
+    if (!W || !H || !abs_mean || !mse_out || !best_out || !s_out || !scales_out || (!codes && !packed))
+        return PWQ_EINVAL;
+    if (zero_point && !zeros_out) return PWQ_EINVAL;
+    if (packed && (bits != 4 || d_in % 2 != 0)) return PWQ_EINVAL;
+    if (!ws || ws_bytes < pwq_awq_search_workspace_size(d_out, d_in)) return PWQ_EWORKSPACE;
+    return hip_status(awq_launch(W, w_dtype, d_out, d_in, ldw, H, n_tok, abs_mean, bits, group_size, n_alpha,
+                                 zero_point != 0, mse_out, best_out, s_out, (int8_t*)codes, packed, scales_out,
+                                 zero_point ? zeros_out : nullptr, ws, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ product with What
 size_t pwq_quantized_matmul_workspace_size(int64_t n_tok, int64_t d_in, int64_t d_out) {
     if (n_tok <= 0 || d_in <= 0 || d_out <= 0 || bad_dim(n_tok) || bad_dim(d_in) || bad_dim(d_out)) return 0;

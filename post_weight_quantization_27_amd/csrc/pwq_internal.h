@@ -63,6 +63,16 @@ size_t tensor_scales_ws_bytes();
 hipError_t tensor_scales_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, int bits,
                                 uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t s);
 
+// Activation-aware channel scaling.
+size_t chan_abs_ws_bytes(int64_t N, int64_t n);
+hipError_t chan_abs_launch(const void* X, int x_dtype, int64_t N, int64_t n, int64_t ldx, float* a, void* ws,
+                           hipStream_t s);
+size_t awq_ws_bytes(int64_t m, int64_t n);
+hipError_t awq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, const float* H, int64_t N,
+                      const float* absmean, int bits, int group_size, int K, int zp, double* mse, int32_t* best,
+                      float* s_out, int8_t* codes, uint8_t* packed, uint16_t* scales, uint16_t* zeros, void* ws,
+                      hipStream_t s);
+
 // Y = X What^T with the quantized weights (float16 X, decode regime).
 size_t w4a16_ws_bytes(int64_t T, int64_t n, int64_t m);
 hipError_t w4a16_launch(const uint16_t* X, int64_t T, int64_t n, int64_t ldx, const uint8_t* packed,

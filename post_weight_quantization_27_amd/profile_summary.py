@@ -50,6 +50,9 @@ CALL_OF = [
     ("dequant_kernel", "dequant"), ("dequant_vec", "dequant"),
     ("mse_", "recon_mse"), ("EpiSq", "recon_mse"), ("set_double", "recon_mse"),
     ("w4a16", "quantized_matmul"),
+    ("chan_abs", "channel_abs_mean"), ("chan_mean", "channel_abs_mean"),
+    ("awq_", "awq_search"), ("EpiDot", "awq_search"),
+    ("tensor_max", "tensor_scales"), ("tensor_scale", "tensor_scales"),
 ]
 
 

@@ -57,6 +57,13 @@ _SIGS = {
     "pwq_recon_mse_zp": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
                                         _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "pwq_channel_abs_mean_workspace_size": (_sz, [_i64, _i64]),
+    "pwq_channel_abs_mean": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _c_void_p, _sz,
+                                            _c_void_p]),
+    "pwq_awq_search_workspace_size": (_sz, [_i64, _i64]),
+    "pwq_awq_search": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _i32, _i32,
+                                      _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                      _c_void_p, _c_void_p, _sz, _c_void_p]),
     "pwq_tensor_scales_workspace_size": (_sz, []),
     "pwq_tensor_scales": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _i32, _c_void_p, _c_void_p,
                                          _c_void_p, _sz, _c_void_p]),
@@ -322,6 +329,47 @@ def recon_mse(X: torch.Tensor, W: torch.Tensor, scales: torch.Tensor, bits: int 
             _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
             _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(X)))
     return mse
+
+
+# ------------------------------------------------------------------ activation-aware scaling
+def channel_abs_mean(X: torch.Tensor) -> torch.Tensor:
+    """float32 d_in: mean over tokens of |X| per input channel."""
+    ldx = _rows(X, "X")
+    n_tok, d_in = X.shape
+    a = torch.empty(d_in, dtype=torch.float32, device=X.device)
+    nb = lib().pwq_channel_abs_mean_workspace_size(n_tok, d_in)
+    ws = _ws(nb, X.device)
+    _check("pwq_channel_abs_mean", lib().pwq_channel_abs_mean(_p(X), _dtype_code(X), n_tok, d_in, ldx, _p(a), _p(ws), nb,
+                                                              _stream(X)))
+    return a
+
+
+def awq_search(W: torch.Tensor, H: torch.Tensor, n_tok: int, abs_mean: torch.Tensor, bits: int = 4,
+               group_size: int = 128, n_alpha: int = 21, zero_point: bool = False, want_codes: bool = True,
+               want_packed: bool = True) -> dict:
+    """Grid search of s = abs_mean^alpha (H undamped).  Returns {mse (float64 n_alpha), best (int32),
+    s (float32 d_in), codes, packed, scales, zeros} with the RTN result of W diag(s)."""
+    ldw = _rows(W, "W")
+    d_out, d_in = W.shape
+    dev = W.device
+    ng = _n_groups(d_in, group_size)
+    o = {"mse": torch.empty(n_alpha, dtype=torch.float64, device=dev),
+         "best": torch.empty(1, dtype=torch.int32, device=dev),
+         "s": torch.empty(d_in, dtype=torch.float32, device=dev),
+         "scales": torch.empty((d_out, ng), dtype=torch.float16, device=dev)}
+    if want_codes:
+        o["codes"] = torch.empty((d_out, d_in), dtype=torch.uint8 if zero_point else torch.int8, device=dev)
+    if want_packed:
+        o["packed"] = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
+    if zero_point:
+        o["zeros"] = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
+    nb = lib().pwq_awq_search_workspace_size(d_out, d_in)
+    ws = _ws(nb, dev)
+    _check("pwq_awq_search", lib().pwq_awq_search(
+        _p(W), _dtype_code(W), d_out, d_in, ldw, _p(H), n_tok, _p(abs_mean), bits, group_size, n_alpha,
+        1 if zero_point else 0, _p(o["mse"]), _p(o["best"]), _p(o["s"]), _p(o.get("codes")), _p(o.get("packed")),
+        _p(o["scales"]), _p(o.get("zeros")), _p(ws), nb, _stream(W)))
+    return o
 
 
 # ------------------------------------------------------------------ per-tensor quantizer
