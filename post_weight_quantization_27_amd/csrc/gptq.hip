@@ -154,11 +154,15 @@ struct BlockArgs {
 };
 
 // Clamp bounds of the rounded quotient and the offset of the stored code for a group with
-// zero z: symmetric [-qmax, qmax] and 0, zero-point [-z, top - z] and z.
+// scale s and zero z: symmetric [-qmax, qmax] and 0, zero-point [-z, top - z] and z.  A
+// zero scale gives [0, 0] and 0, so the rounding itself yields code 0 (with rs = 0 it
+// returns a value within one of 0, which the clamp turns into 0): no select, and no branch
+// the compiler could make of one, on the column-to-column chain.
 struct QBounds {
     float lo, hi, z;
 };
-__device__ __forceinline__ QBounds qbounds(const BlockArgs& a, float z) {
+__device__ __forceinline__ QBounds qbounds(const BlockArgs& a, float z, float s) {
+    if (!(s > 0.f)) return QBounds{0.f, 0.f, 0.f};
     if (a.zeros) return QBounds{-z, (float)a.top - z, z};
     return QBounds{-(float)a.qmax, (float)a.qmax, 0.f};
 }
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
         z = live ? stored_zero(a, r * a.ng + a.gbase) : 0.f;
     }
     float rs = s > 0.f ? 1.0f / s : 0.f;
-    QBounds qb_ = qbounds(a, z);
+    QBounds qb_ = qbounds(a, z, s);
     float eown[NC];
     uint32_t qb[(NC + 3) / 4];
 #pragma unroll
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
                 }
                 s = f16_bits_to_f32(sb);
                 rs = s > 0.f ? 1.0f / s : 0.f;
-                qb_ = qbounds(a, z);
+                qb_ = qbounds(a, z, s);
             }
             // column j: owner lane j & 3 (= t), register j >> 2, broadcast inside the quad
             const float wj = quad_bcast_of(w[j >> 2], t);
@@ -347,9 +351,9 @@ __global__ __launch_bounds__(NWV * 64) void gptq_block_kernel(BlockArgs a) {
             const int odd = ki & 1;
             const int up = (hi > 0.f) | ((hi == 0.f) & odd);
             const int dn = (lo < 0.f) | ((lo == 0.f) & odd);
-            const float qf = s > 0.f ? __builtin_amdgcn_fmed3f((float)(ki + up - dn), qb_.lo, qb_.hi) : 0.f;
+            const float qf = __builtin_amdgcn_fmed3f((float)(ki + up - dn), qb_.lo, qb_.hi);
             const float e = (wj - s * qf) * dj[t];
-            const int q = s > 0.f ? (int)(qf + qb_.z) : 0;       // s = 0: code 0 whatever the zero
+            const int q = (int)(qf + qb_.z);
             // the owner lane of column j keeps its error and code (selects, no branches)
             eown[j >> 2] = own[t] ? e : eown[j >> 2];
             qb[j >> 4] = own[t] ? (qb[j >> 4] | ((uint32_t)(q & 0xff) << (8 * ((j >> 2) & 3)))) : qb[j >> 4];
@@ -503,12 +507,14 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
         }
         s = uniform_f(s);
         float rs = uniform_f(s > 0.f ? 1.0f / s : 0.f);
-        QBounds qb_ = qbounds(a, uniform_f(z));
+        QBounds qb_ = qbounds(a, uniform_f(z), s);
 
         float u[NS], un[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) u[k] = lane_in ? Ub[0][64 * k + lane] : 0.f;
-#pragma unroll
+        // fully unrolled (forced: the compiler's cost model keeps PW = 64 and 128 rolled),
+        // so the lane of every readlane and the register of every column are static
+#pragma clang loop unroll(full)
         for (int j = 0; j < PW; ++j) {
             if (j + 1 < PW) {
 #pragma unroll
@@ -557,7 +563,7 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
                 }
                 s = uniform_f(f16_bits_to_f32(sb));
                 rs = uniform_f(s > 0.f ? 1.0f / s : 0.f);
-                qb_ = qbounds(a, uniform_f(zg));
+                qb_ = qbounds(a, uniform_f(zg), s);
             }
             // everything from here to e is the same in every lane (wj, s, rs, dj are
             // wave-uniform), so the rare exact-rounding branch is a uniform one
@@ -567,12 +573,12 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
             // buffer) on the column-to-column chain
             // (the quotient clamped to [lo, hi]; the stored code adds the zero, and s = 0 gives
             // code 0 whatever the zero)
-            const float qf = s > 0.f ? round_quot_clamp(wj, s, rs, qb_.lo, qb_.hi) : 0.f;
+            const float qf = round_quot_clamp(wj, s, rs, qb_.lo, qb_.hi);
             const float e = (wj - s * qf) * dj;
             // e and the code are wave-uniform: every lane stores the same value to the same
             // LDS word (no lane select), and each lane reads its own columns back at the end
             esh[wave][j] = e;
-            qsh[wave][j] = (int8_t)(s > 0.f ? (int)(qf + qb_.z) : 0);
+            qsh[wave][j] = (int8_t)(int)(qf + qb_.z);
             // columns left of j (and j itself) are final: only registers holding columns
             // >= j need the update, and U is 0 left of j anyway
 #pragma unroll
