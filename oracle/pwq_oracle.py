@@ -318,7 +318,9 @@ def _init_params(m, ng, scales_in, zeros_in, sym):
 
 def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, block_size: int = 128,
          perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None,
-         sym: bool = True, zeros_in: Optional[np.ndarray] = None) -> dict:
+         sym: bool = True, zeros_in: Optional[np.ndarray] = None,
+         forced_codes: Optional[np.ndarray] = None, forced_scales: Optional[np.ndarray] = None,
+         forced_zeros: Optional[np.ndarray] = None) -> dict:
     """GPTQ with lazy block updates ([GPTQ-P] "The GPTQ Algorithm", R1-R9).
 
     W: d_out x d_in (any float dtype, promoted to float64).  U: the factor of
@@ -337,6 +339,15 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
     ``sym=False``: zero-point quantization (A1-A5); the group's scale and zero come from
     the same current values the symmetric scale would.
 
+    ``forced_codes`` (d_out x d_in, processing order): a replay of another run's decisions.
+    Every column is quantized as above, but the code taken - and so the error carried on -
+    is the given one; where it differs from this function's own, ``forced`` records the
+    distance of the exact quotient (plus the zero) from the rounding boundary between the
+    two codes, in units of the scale (0 at an exact tie).  ``forced_scales`` (and
+    ``forced_zeros``) likewise replace each group's quantizer once this function has taken
+    its own and recorded how far apart the two are.  The arithmetic is otherwise unchanged;
+    it checks that the other run decided like this one given the same history.
+
     Returns codes (int8, or uint8 with zero-points; original column order), scales
     (float16, d_out x groups, in processing order), zeros (uint16 like scales, or None),
     g_idx (int32 or None) and What (float64)."""
@@ -348,6 +359,10 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
     scales, zeros = _init_params(m, ng, scales_in, zeros_in, sym)
     codes_p = np.zeros((m, n), dtype=np.int8 if sym else np.uint8)
     B = int(block_size)
+    forced = None
+    if forced_codes is not None:
+        forced = {"count": 0, "max_distance": 0.0, "max_step": 0, "groups": 0, "scale_mismatch": 0,
+                  "scale_max_ulp": 0, "zero_mismatch": 0, "zero_max_step": 0}
     for b0 in range(0, n, B):
         b1 = min(b0 + B, n)
         panel = Wp[:, b0:b1].copy()
@@ -362,12 +377,37 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
                     pending = Wp[:, b1:ge] - err[:, :jj] @ U[b0:j, b1:ge]
                     vals = np.concatenate([vals, pending], axis=1)
                 sG, zG = _group_params(vals, bits, sym)
+                if forced is not None and forced_scales is not None:
+                    fs = np.asarray(forced_scales, dtype=np.float16).reshape(m, ng)[:, G]
+                    d = np.abs(fs.view(np.uint16).astype(np.int64) - sG.view(np.uint16).astype(np.int64))
+                    forced["groups"] += m
+                    forced["scale_mismatch"] += int((d != 0).sum())
+                    forced["scale_max_ulp"] = max(forced["scale_max_ulp"], int(d.max()))
+                    sG = fs
+                    if not sym and forced_zeros is not None:
+                        fz = np.asarray(forced_zeros).astype(np.int64).reshape(m, ng)[:, G]
+                        dz = np.abs(fz - zG.astype(np.int64))
+                        forced["zero_mismatch"] += int((dz != 0).sum())
+                        forced["zero_max_step"] = max(forced["zero_max_step"], int(dz.max()))
+                        zG = fz.astype(np.uint16)
                 scales[:, G] = sG
                 if not sym:
                     zeros[:, G] = zG
             zc = None if sym else zeros[:, G]
             w = panel[:, jj]
             q = _codes(w, scales[:, G], zc, bits, sym)
+            if forced is not None:
+                qf = np.asarray(forced_codes[:, j]).astype(q.dtype)
+                diff = qf.astype(np.int64) != q.astype(np.int64)
+                if diff.any():
+                    sd = scales[diff, G].astype(np.float64)
+                    zd = 0.0 if sym else zeros[diff, G].astype(np.float64)
+                    tq = np.where(sd > 0, w[diff] / np.where(sd > 0, sd, 1.0), 0.0) + zd
+                    lo = np.minimum(qf[diff].astype(np.float64), q[diff].astype(np.float64))
+                    forced["count"] += int(diff.sum())
+                    forced["max_distance"] = max(forced["max_distance"], float(np.max(np.abs(tq - (lo + 0.5)))))
+                    forced["max_step"] = max(forced["max_step"], int(np.max(np.abs(qf[diff].astype(np.int64) - q[diff].astype(np.int64)))))
+                q = qf
             codes_p[:, j] = q
             what = _value(scales[:, G], zc, q)
             e = (w - what) / U[j, j]
@@ -375,7 +415,10 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
             panel[:, jj + 1:] -= np.outer(e, U[j, j + 1:b1])
         if b1 < n:
             Wp[:, b1:] -= err @ U[b0:b1, b1:]
-    return _finish(codes_p, scales, perm, group_size, bits, zeros)
+    res = _finish(codes_p, scales, perm, group_size, bits, zeros)
+    if forced is not None:
+        res["forced"] = forced
+    return res
 
 
 def gptq_unblocked(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128,

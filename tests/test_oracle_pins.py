@@ -633,3 +633,27 @@ def test_awq_search_pins():
     e_awq = np.abs(W[:, 5] - res["What"][:, 5]).mean()
     e_rtn = np.abs(W[:, 5] - r0["What"][:, 5]).mean()
     assert res["best"] > 0 and e_awq < e_rtn
+
+
+def test_forced_replay_of_own_codes_is_silent_and_flags_a_planted_flip():
+    """Replaying the oracle's own decisions changes nothing; a planted code flip is reported
+    with its distance from the rounding boundary."""
+    rng = np.random.default_rng(98)
+    m, n = 40, 96
+    X = ar1_x(rng, 300, n, 0.8)
+    W = rng.normal(0, 0.02, size=(m, n))
+    Hd, _ = O.damp_hessian(O.hessian(X), 0.01)
+    U = O.chol_inverse_upper(Hd)
+    for sym in (True, False):
+        ref = O.gptq(W, U, 4, 32, 32, sym=sym)
+        rep = O.gptq(W, U, 4, 32, 32, sym=sym, forced_codes=ref["codes"], forced_scales=ref["scales"],
+                     forced_zeros=ref["zeros"])
+        assert rep["forced"]["count"] == 0 and np.array_equal(rep["codes"], ref["codes"])
+        assert rep["forced"]["scale_mismatch"] == 0 and rep["forced"]["groups"] == m * 3
+        bad = ref["codes"].astype(np.int64).copy()
+        hi = 7 if sym else 15
+        bad[3, 40] = bad[3, 40] - 1 if bad[3, 40] > (-7 if sym else 0) else bad[3, 40] + 1
+        rep2 = O.gptq(W, U, 4, 32, 32, sym=sym, forced_codes=bad)
+        assert rep2["forced"]["count"] >= 1 and rep2["forced"]["max_step"] == 1
+        assert 0.0 <= rep2["forced"]["max_distance"] <= 1.0 + 1e-9
+        assert rep2["codes"][3, 40] == bad[3, 40] and abs(int(bad[3, 40])) <= hi
