@@ -308,7 +308,7 @@ def copy_calibration(torch):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py: this build measures one GPU; multi-GPU runs are not supported (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU; runs on several GPUs are not supported (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     if a.copy_calibration:

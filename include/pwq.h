@@ -77,7 +77,7 @@ typedef struct pwq_params {
     int32_t act_order;
 } pwq_params;
 
-/* ABI version (PWQ_ABI_VERSION of the build). */
+/* ABI version the library was compiled with (PWQ_ABI_VERSION). */
 int pwq_version(void);
 
 /* Static text for a status code. */
