@@ -76,9 +76,11 @@ class Layer:
         del X, W
 
 
-def run_step(L, pwq, timers=None, after_hessian=None):
+def run_step(L, pwq, timers=None, after_hessian=None, parts="all"):
     """One pass of the whole path over one layer.  timers: dict name -> list of (start, end) events;
-    after_hessian: called once the Hessian's kernels are enqueued."""
+    after_hessian: called once the Hessian's kernels are enqueued.  parts: "all", or the two
+    halves that do not depend on each other: "rtn" (round-to-nearest and its error, which need
+    only W and X) and "gptq" (everything else)."""
     import torch
     s = L.spec
 
@@ -97,6 +99,14 @@ def run_step(L, pwq, timers=None, after_hessian=None):
         e1.record()
         timers[name][-1][1] = e1
 
+    rq = pwq.rtn_quantize_zp if L.zp else pwq.rtn_quantize
+    if parts == "rtn":
+        k = t("rtn_quantize"); rq(L.W, s.bits, s.group_size, want_codes=False, out=L.rq); done(k)
+        k = t("recon_mse")
+        pwq.recon_mse(L.X, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"], mse=L.mse[1:2],
+                      zeros=L.rq.get("zeros"))
+        done(k)
+        return
     k = t("hessian_accumulate"); L.H.zero_(); pwq.hessian_accumulate(L.X, L.H); done(k)
     if after_hessian is not None:
         after_hessian()
@@ -109,8 +119,8 @@ def run_step(L, pwq, timers=None, after_hessian=None):
     gq = pwq.gptq_quantize_layer_zp if L.zp else pwq.gptq_quantize_layer
     gq(L.W, L.U, L.info, s.bits, s.group_size, s.block_size, perm=perm, want_codes=False, want_packed=True, out=L.gq)
     done(k)
-    rq = pwq.rtn_quantize_zp if L.zp else pwq.rtn_quantize
-    k = t("rtn_quantize"); rq(L.W, s.bits, s.group_size, want_codes=False, out=L.rq); done(k)
+    if parts == "all":
+        k = t("rtn_quantize"); rq(L.W, s.bits, s.group_size, want_codes=False, out=L.rq); done(k)
     k = t("dequant")
     if L.zp:
         pwq.dequant_zp(L.gq["scales"], L.gq["zeros"], s.d_in, s.bits, s.group_size, packed=L.gq["packed"],
@@ -122,8 +132,9 @@ def run_step(L, pwq, timers=None, after_hessian=None):
     k = t("recon_mse")
     pwq.recon_mse(L.X, L.W, L.gq["scales"], s.bits, s.group_size, packed=L.gq["packed"], g_idx=L.gq.get("g_idx"),
                   mse=L.mse[0:1], zeros=L.gq.get("zeros"))
-    pwq.recon_mse(L.X, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"], mse=L.mse[1:2],
-                  zeros=L.rq.get("zeros"))
+    if parts == "all":
+        pwq.recon_mse(L.X, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"], mse=L.mse[1:2],
+                      zeros=L.rq.get("zeros"))
     done(k)
 
 
@@ -336,6 +347,9 @@ def main():
     # widest layer's latency-bound factor instead of its Hessian.
     stagger = bool(a.stagger) and bool(a.streams) and len(layers) > 1
     first_done = torch.cuda.Event()
+    # The widest layer's round-to-nearest and its error need only W and X: they go to the
+    # front of the second layer's stream, off the widest layer's chain.
+    side = bool(a.streams) and len(layers) > 1
 
     def step(timers=None):
         for pos, i in enumerate(order):
@@ -344,8 +358,12 @@ def main():
             if stagger and pos > 0:
                 st.wait_event(first_done)
             with torch.cuda.stream(st):
+                if side and pos == 1:
+                    lead = order[0]
+                    run_step(layers[lead], pwq, None if timers is None else timers[lead], parts="rtn")
                 hook = (lambda: first_done.record()) if (stagger and pos == 0) else None
-                run_step(L, pwq, None if timers is None else timers[i], after_hessian=hook)
+                run_step(L, pwq, None if timers is None else timers[i], after_hessian=hook,
+                         parts="gptq" if (side and pos == 0) else "all")
         for st in streams:
             main.wait_stream(st)
 
@@ -372,7 +390,8 @@ def main():
 
     # per-call durations: the same K steps again, on the same streams, with HIP events around
     # every call on the stream it runs on (kept out of the first timed region, which gives the
-    # value, so the event records do not sit between its launches)
+    # value, so the event records do not sit between its launches); a name's time per step is
+    # the sum over its calls in the step (recon_mse: the GPTQ and the RTN error)
     timers = [dict() for _ in layers]
     for _ in range(a.steps):
         step(timers)
@@ -380,7 +399,7 @@ def main():
     per = {}
     for L, T in zip(layers, timers):
         for name, ev in T.items():
-            d = sum(x[0].elapsed_time(x[1]) for x in ev) / len(ev)
+            d = sum(x[0].elapsed_time(x[1]) for x in ev) / a.steps
             per[(L.spec.name, name)] = d
     breakdown = {}
     for (lname, name), d in per.items():
@@ -419,7 +438,8 @@ def main():
         "config": {"workload": a.workload, "layers": [f"{s.name}:{s.d_in}->{s.d_out}" for s in specs],
                    "n_tok": specs[0].n_tok, "bits": specs[0].bits, "group_size": specs[0].group_size,
                    "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order),
-                   "zero_point": bool(a.zero_point), "layer_streams": bool(a.streams), "stagger": stagger},
+                   "zero_point": bool(a.zero_point), "layer_streams": bool(a.streams), "stagger": stagger,
+                   "rtn_off_chain": side},
         "roofline": roof,
         "xtx_mfma_util": xtx,
         "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
