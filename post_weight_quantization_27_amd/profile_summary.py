@@ -30,6 +30,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,16 +64,25 @@ def call_of(name: str) -> str:
     return "other"
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def source_hash() -> str:
-    """sha256 over the kernel sources (csrc/*.hip, *.h) and the public header."""
+    """sha256 over the kernel sources (csrc/*.hip, *.h) and the public header, with comments
+    and blank space removed, so an edit of the prose alone keeps the counters valid."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) + glob.glob(os.path.join(HERE, "csrc", "*.h")))
     files.append(os.path.join(os.path.dirname(HERE), "include", "pwq.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
+
+
+def code_only(text: str) -> str:
+    """C/HIP source text without its comments, runs of blank space made one space."""
+    return " ".join(_COMMENT.sub(" ", text).split())
 
 
 def short(name: str, n: int = 110) -> str:
