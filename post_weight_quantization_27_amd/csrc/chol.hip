@@ -17,9 +17,11 @@
 //   syrk     : A_{<k, <k} -= P P^T                                    (upper tiles)
 //   push     : R_{<k, >=k} += P U_{k, >=k}   (overwrite for the block column k itself)
 // trsm + finalize share one launch, syrk + push another: three launches per block.  Below
-// n = 4096 the diagonal factor of block k - 1 joins block k's syrk + push launch (one
-// workgroup applies its share of the update itself): two launches per block, and the
-// serial factor overlaps the update.  From n = 4096 on, updates are batched per super-block.
+// n = 4096 the diagonal factor of block k - 1 joins block k's syrk + push launch: two
+// launches per block, and the serial factor overlaps the update.  Block k's update of that
+// diagonal block is then done ahead, in block k's trsm + finalize launch: ten workgroups,
+// one per upper 32 x 32 tile, each forming the rows of P it needs from A and Z_kk.  From
+// n = 4096 on, updates are batched per super-block.
 // Every kernel reads `info` first and does nothing once a pivot has failed.
 #include "gemm_f32.h"
 #include "pwq_internal.h"
@@ -58,7 +60,8 @@ __global__ __launch_bounds__(256) void copy_perm_kernel(const float* __restrict_
 
 // ------------------------------------------------------------------ diagonal block
 // One workgroup of 256 threads factors the 128 x 128 diagonal block A = V V^T (V upper) and
-// inverts V, everything in LDS:
+// inverts V, everything in one 128 x 129 LDS matrix (66 KB, so that two workgroups of the
+// update launch it shares fit on a CU):
 //   factor, 32-column panels from the right: one wave holds the panel region (rows above
 //     and inside the panel) in registers and runs its 32 pivots with readlane broadcasts;
 //     after the panel, the rows and columns left of it get one rank-32 update on MFMA
@@ -71,8 +74,22 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int LP = CHOL_NB + 1;    // padded LDS row
 
-// 32 x 32 tile of C -= A B^T on MFMA, with A rows [ra, ra+32), B rows [rb, rb+32), k over
-// [k0, k0+32) of the same LDS matrix M (sign = -1) or C = s * A B (B row-major, k-major).
+// 32 x 32 tile of A B^T on MFMA: A rows [ra, ra+32) of the LDS matrix MA, B rows [rb, rb+32)
+// of MB, k over [k0, k0 + kn) (kn even)
+__device__ __forceinline__ f32x16 mfma_tile_abT2(const float (*MA)[LP], int ra, const float (*MB)[LP], int rb, int k0,
+                                                 int kn, int lane) {
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll 4
+    for (int kp = 0; kp < kn; kp += 2) {
+        const float av = MA[ra + (lane & 31)][k0 + kp + (lane >> 5)];
+        const float bv = MB[rb + (lane & 31)][k0 + kp + (lane >> 5)];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+    return acc;
+}
+// the same with both operands in one LDS matrix M
 __device__ __forceinline__ f32x16 mfma_tile_abT(const float (*M)[LP], int ra, int rb, int k0, int kn, int lane) {
     f32x16 acc;
 #pragma unroll
@@ -99,30 +116,14 @@ __device__ __forceinline__ f32x16 mfma_tile_ab(const float (*MA)[LP], int ra, in
 }
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-// 16 x 16 tile of A B^T, A rows [ra, ra+16), B rows [rb, rb+16), k over [0, kn) of the LDS
-// matrix M; output element i of lane l is (4 (l / 16) + i, l % 16)
-__device__ __forceinline__ f32x4 mfma16_tile_abT(const float (*M)[LP], int ra, int rb, int kn, int lane) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kp = 0; kp < kn; kp += 4) {
-        const float av = M[ra + (lane & 15)][kp + (lane >> 4)];
-        const float bv = M[rb + (lane & 15)][kp + (lane >> 4)];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-    }
-    return acc;
-}
-
-constexpr int DIAG_FLOATS = 2 * CHOL_NB * LP + 4;       // A, Z, the failed-pivot word
+constexpr int DIAG_FLOATS = CHOL_NB * LP + 4;           // A (then Z in its place), the failed-pivot word
 
 // The diagonal block [k0, k0 + bs) in one workgroup, in the LDS buffer smem (DIAG_FLOATS
-// floats).  With Pu (the pending panel rows of the block: Pu[i * pld + c], c < kdepth), the
-// block first takes that panel's update A -= Pu Pu^T, which the caller's launch leaves out.
+// floats).
 __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int64_t k0, int bs,
-                                           int32_t* __restrict__ info, float* smem, const float* __restrict__ Pu,
-                                           int pld, int kdepth) {
+                                           int32_t* __restrict__ info, float* smem) {
     float (*A)[LP] = (float (*)[LP])smem;
-    float (*Z)[LP] = (float (*)[LP])(smem + CHOL_NB * LP);
-    int& fail = *(int*)(smem + 2 * CHOL_NB * LP);       // failed pivot + 1 of the current panel
+    int& fail = *(int*)(smem + CHOL_NB * LP);           // failed pivot + 1 of the current panel
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // ---------------- load: thread = (row, 64-column half), all loads in flight
@@ -147,55 +148,9 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
         for (int q = 0; q < 64; ++q) {
             const int j = c0 + q;
             A[i][j] = j >= i ? v[q] : 0.f;
-            Z[i][j] = 0.f;
         }
     }
     __syncthreads();
-
-    // ---------------- pending update: Z <- panel rows, A -= Z Z^T on the 36 upper 16 x 16
-    // tiles (nine per wave, MFMA, k = 128, zero columns past kdepth).  Afterwards only the
-    // two lower blocks that the inverse reads as zeros are cleared (the rest of Z is written
-    // before it is read).
-    if (Pu) {
-        {
-            const int i = tid >> 1, c0 = 64 * (tid & 1);
-            const float* src = Pu + (int64_t)i * pld + c0;
-            if (kdepth == CHOL_NB && pld % 4 == 0 && ((uintptr_t)Pu & 15) == 0) {
-                float4 v[16];
-#pragma unroll
-                for (int q = 0; q < 16; ++q) v[q] = *(const float4*)(src + 4 * q);
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    Z[i][c0 + 4 * q] = v[q].x; Z[i][c0 + 4 * q + 1] = v[q].y;
-                    Z[i][c0 + 4 * q + 2] = v[q].z; Z[i][c0 + 4 * q + 3] = v[q].w;
-                }
-            } else {
-#pragma unroll 16
-                for (int q = 0; q < 64; ++q) Z[i][c0 + q] = c0 + q < kdepth ? src[q] : 0.f;
-            }
-        }
-        __syncthreads();
-        for (int t = wave; t < 36; t += 4) {
-            int ti = 0, r = t;
-            while (r >= 8 - ti) { r -= 8 - ti; ++ti; }
-            const int tj = ti + r;
-            const f32x4 acc = mfma16_tile_abT(Z, 16 * ti, 16 * tj, CHOL_NB, lane);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int rr = 16 * ti + 4 * (lane >> 4) + v, cc = 16 * tj + (lane & 15);
-                if (cc >= rr) A[rr][cc] -= acc[v];
-            }
-        }
-        __syncthreads();
-        {
-            const int i = tid >> 3, c = 4 * (tid & 7);     // 32 rows x 32 columns, two blocks
-            for (int q = 0; q < 4; ++q) {
-                Z[32 + i][c + q] = 0.f;
-                Z[96 + i][64 + c + q] = 0.f;
-            }
-        }
-        __syncthreads();
-    }
 
     // ---------------- factor: 32-column panels from the right.  The waves holding rows at or
     // above the panel's diagonal factor it in registers (32 rows each, plus a copy of the
@@ -274,8 +229,12 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
         }
     }
 
-    // ---------------- inverse: leaves, one wave per 32 x 32 diagonal block; lane j owns column
-    // j of Z and back-substitutes it from the broadcast rows of V (no cross-lane traffic)
+    // ---------------- inverse, in place: Z = V^-1 overwrites V block by block; the products'
+    // intermediates go to the lower-left blocks (rows 64.., columns ..63), which hold nothing.
+    // Every block read as a factor of Z keeps its zeros below the diagonal.
+    // Leaves: one wave per 32 x 32 diagonal block; lane j owns column j of Z and
+    // back-substitutes it from the broadcast rows of V (no cross-lane traffic), then writes
+    // the block (zeros below its diagonal) over V's, which only this wave reads.
     {
         const int o = 32 * wave;
         const int j = lane & 31;
@@ -290,35 +249,38 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
         }
         if (lane < 32) {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) Z[o + i][o + j] = z[i];
+            for (int i = 0; i < 32; ++i) A[o + i][o + j] = z[i];
         }
     }
     __syncthreads();
 
-    // ---------------- doubling 32 -> 64: Z_01 = -Z_00 (V_01 Z_11) for the pairs (0,1), (2,3)
+    // ---------------- doubling 32 -> 64: Z_01 = -Z_00 (V_01 Z_11) for the pairs (0,1), (2,3),
+    // one wave each; T = V_01 Z_11 goes to rows 64 + 32 w, columns 32 w (read by no other
+    // wave), and Z_01 over V_01 once this wave has read it
     if (wave < 2) {
         const int o0 = 64 * wave, o1 = o0 + 32;
-        const int sr = 64 + 32 * wave, sc = 32 * wave;         // scratch in Z's lower-left block
-        f32x16 t = mfma_tile_ab(A, o0, o1, Z, o1, o1, 32, lane);
+        const int sr = 64 + 32 * wave, sc = 32 * wave;
+        f32x16 t = mfma_tile_ab(A, o0, o1, A, o1, o1, 32, lane);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Z[sr + acc_row(v, lane)][sc + (lane & 31)] = t[v];
-        t = mfma_tile_ab(Z, o0, o0, Z, sr, sc, 32, lane);       // k over Z_00 columns, T rows
+        for (int v = 0; v < 16; ++v) A[sr + acc_row(v, lane)][sc + (lane & 31)] = t[v];
+        t = mfma_tile_ab(A, o0, o0, A, sr, sc, 32, lane);       // k over Z_00 columns, T rows
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Z[o0 + acc_row(v, lane)][o1 + (lane & 31)] = -t[v];
+        for (int v = 0; v < 16; ++v) A[o0 + acc_row(v, lane)][o1 + (lane & 31)] = -t[v];
     }
     __syncthreads();
 
-    // ---------------- doubling 64 -> 128: Z_AB = -Z_AA (V_AB Z_BB), A = [0,64), B = [64,128)
+    // ---------------- doubling 64 -> 128: Z_AB = -Z_AA (V_AB Z_BB), A = [0,64), B = [64,128);
+    // T = V_AB Z_BB to the lower-left 64 x 64 block (read by nobody while T is formed), then
+    // Z_AB over V_AB after the barrier that ends every read of it
     {
         const int ti = wave >> 1, tj = wave & 1;
-        const f32x16 t = mfma_tile_ab(A, 32 * ti, 64, Z, 64, 64 + 32 * tj, 64, lane);
-        __syncthreads();                                        // scratch of the level above is free
+        const f32x16 t = mfma_tile_ab(A, 32 * ti, 64, A, 64, 64 + 32 * tj, 64, lane);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Z[64 + 32 * ti + acc_row(v, lane)][32 * tj + (lane & 31)] = t[v];
+        for (int v = 0; v < 16; ++v) A[64 + 32 * ti + acc_row(v, lane)][32 * tj + (lane & 31)] = t[v];
         __syncthreads();
-        const f32x16 u = mfma_tile_ab(Z, 32 * ti, 0, Z, 64, 32 * tj, 64, lane);
+        const f32x16 u = mfma_tile_ab(A, 32 * ti, 0, A, 64, 32 * tj, 64, lane);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Z[32 * ti + acc_row(v, lane)][64 + 32 * tj + (lane & 31)] = -u[v];
+        for (int v = 0; v < 16; ++v) A[32 * ti + acc_row(v, lane)][64 + 32 * tj + (lane & 31)] = -u[v];
     }
     __syncthreads();
 
@@ -333,14 +295,14 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int j = c0 + 4 * q + c;
-                    t[c] = j >= i ? Z[i][j] : 0.f;
+                    t[c] = j >= i ? A[i][j] : 0.f;
                 }
                 *(float4*)(dst + 4 * q) = make_float4(t[0], t[1], t[2], t[3]);
             }
         } else if (i < bs) {
             for (int q = 0; q < 64; ++q) {
                 const int j = c0 + q;
-                if (j < bs) dst[q] = j >= i ? Z[i][j] : 0.f;
+                if (j < bs) dst[q] = j >= i ? A[i][j] : 0.f;
             }
         }
     }
@@ -350,7 +312,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ U, i
                                                         int32_t* __restrict__ info) {
     if (*info) return;
     __shared__ __attribute__((aligned(16))) float smem[DIAG_FLOATS];
-    diag_block(U, n, k0, bs, info, smem, nullptr, 0, 0);
+    diag_block(U, n, k0, bs, info, smem);
 }
 
 // ------------------------------------------------------------------ epilogues
@@ -481,22 +443,193 @@ hipError_t launch_near(float* U, const float* Pk, int pld, int64_t n, int64_t s0
 }
 
 // One launch for the update of block k (syrk + push tiles, workgroups 1 ..) and the
-// factor of the next diagonal block [kd0, kd0 + NB) (workgroup 0): that block needs only
-// its own share of the update, which workgroup 0 applies itself (the syrk tiles covering it
-// are left out of the grid), so the serial diagonal factor overlaps the rest of the update.
+// factor of the next diagonal block [kd0, kd0 + NB) (workgroup 0): block k's update of that
+// block was applied by block k's trsm launch (pre_update_tile), and the syrk tiles covering
+// it are left out of this grid, so the serial diagonal factor overlaps the rest of the update.
 template <class TA, class TB>
 __global__ __launch_bounds__(GEMM_THREADS) void chol_update_diag_kernel(TA a, TB b, int n1, int32_t* __restrict__ info,
-                                                                        float* __restrict__ U, int64_t n, int64_t kd0,
-                                                                        const float* __restrict__ Pu, int pld,
-                                                                        int kdepth) {
+                                                                        float* __restrict__ U, int64_t n, int64_t kd0) {
     if (*info) return;
     constexpr int L0 = TA::LDS > TB::LDS ? TA::LDS : TB::LDS;
     constexpr int L = L0 > DIAG_FLOATS ? L0 : DIAG_FLOATS;
     __shared__ __attribute__((aligned(16))) float lds[L];
     const int bid = (int)blockIdx.x;
-    if (bid == 0) diag_block(U, n, kd0, CHOL_NB, info, lds, Pu, pld, kdepth);
+    if (bid == 0) diag_block(U, n, kd0, CHOL_NB, info, lds);
     else if (bid - 1 < n1) a.run(bid - 1, lds);
     else b.run(bid - 1 - n1, lds);
+}
+
+// Block k's update of the next diagonal block D = A[k1:k0, k1:k0] (k1 = k0 - NB), done in
+// block k's trsm launch: D -= P_D P_D^T with P_D = A[k1:k0, k0:k0+bs] Z_kk^T, the rows of
+// block k's panel P that fall in D.  Workgroup t takes the upper 32 x 32 tile (ti, tj) of D
+// and forms the two 32-row slices of P_D it needs itself (one on the diagonal), from A and
+// Z_kk (upper triangular: column block cb of P takes k from 32 cb on).  Nothing else in
+// the launch reads or writes D.
+constexpr int PRE_TILES = 10;
+constexpr int PP = CHOL_NB + 4;                        // LDS pitch: rows 16-byte aligned
+constexpr int PRE_FLOATS = CHOL_NB * PP + 64 * PP;     // Z_kk, two 32-row slices
+
+// 32 x 32 tile of A B^T: A rows [ra, ra+32) of MA, B rows [rb, rb+32) of MB, k over
+// [k0, k0 + KN).  Both operands take the k values in the same order: in step s, lane half
+// h supplies k0 + 8 s + 4 h + i to MFMA i, so each lane reads its four with one 16-byte load.
+template <int KN>
+__device__ __forceinline__ f32x16 mfma_abT_x4(const float (*MA)[PP], int ra, const float (*MB)[PP], int rb, int k0,
+                                              int lane) {
+    static_assert(KN % 8 == 0, "k in steps of 8");
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    const int r = lane & 31, kh = k0 + 4 * (lane >> 5);
+#pragma unroll
+    for (int st = 0; st < KN / 8; ++st) {
+        const float4 a = *(const float4*)&MA[ra + r][kh + 8 * st];
+        const float4 b = *(const float4*)&MB[rb + r][kh + 8 * st];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// column block cb of a P slice: k over [32 cb, NB)
+__device__ __forceinline__ f32x16 p_block(const float (*As)[PP], int ra, const float (*Zs)[PP], int cb, int lane) {
+    switch (cb) {
+        case 0: return mfma_abT_x4<CHOL_NB>(As, ra, Zs, 0, 0, lane);
+        case 1: return mfma_abT_x4<CHOL_NB - 32>(As, ra, Zs, 32, 32, lane);
+        case 2: return mfma_abT_x4<CHOL_NB - 64>(As, ra, Zs, 64, 64, lane);
+        default: return mfma_abT_x4<CHOL_NB - 96>(As, ra, Zs, 96, 96, lane);
+    }
+}
+
+__device__ __forceinline__ void pre_update_tile(float* __restrict__ U, int64_t n, int64_t k0, int bs, int t,
+                                                float* smem) {
+    float (*Zs)[PP] = (float (*)[PP])smem;
+    float (*As)[PP] = (float (*)[PP])(smem + CHOL_NB * PP);   // slice of tile row ti, then of tj
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int ti = 0, r = t;
+    while (r >= 4 - ti) { r -= 4 - ti; ++ti; }
+    const int tj = ti + r;
+    const bool diag = ti == tj;
+    const int64_t k1 = k0 - CHOL_NB;
+    const bool vec = bs == CHOL_NB && (n % 4) == 0 && ((uintptr_t)U & 15) == 0;
+    // this thread's four elements of D's tile, read now (nothing in the launch writes them)
+    const int dr = tid >> 3, dc = 4 * (tid & 7);
+    float* dst = U + (k1 + 32 * ti + dr) * n + k1 + 32 * tj + dc;
+    float dold[4];
+
+    // ---------------- load: Z_kk (upper, zero past bs), the slices' columns [k0, k0 + bs), D's tile
+    {
+        const int i = tid >> 1, c0 = 64 * (tid & 1);
+        const float* src = U + (k0 + i) * n + k0 + c0;
+        float4 v[16];
+        const int ns = diag ? 1 : 2;
+        const int rr = tid >> 3, a0 = 16 * (tid & 7);
+        float4 w[2][4];
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = *(const float4*)(src + 4 * q);
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                if (sl < ns) {
+                    const float* a = U + (k1 + 32 * (sl ? tj : ti) + rr) * n + k0 + a0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[sl][q] = *(const float4*)(a + 4 * q);
+                }
+            }
+            const float4 d = *(const float4*)dst;
+            dold[0] = d.x; dold[1] = d.y; dold[2] = d.z; dold[3] = d.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                float e[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) e[c] = (i < bs && c0 + 4 * q + c < bs) ? src[4 * q + c] : 0.f;
+                v[q] = make_float4(e[0], e[1], e[2], e[3]);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                if (sl < ns) {
+                    const float* a = U + (k1 + 32 * (sl ? tj : ti) + rr) * n + k0 + a0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float e[4];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) e[c] = a0 + 4 * q + c < bs ? a[4 * q + c] : 0.f;
+                        w[sl][q] = make_float4(e[0], e[1], e[2], e[3]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dold[q] = dst[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int j = c0 + 4 * q;
+            float4 x = v[q];
+            if (j < i) x.x = 0.f;
+            if (j + 1 < i) x.y = 0.f;
+            if (j + 2 < i) x.z = 0.f;
+            if (j + 3 < i) x.w = 0.f;
+            *(float4*)&Zs[i][j] = x;
+        }
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            if (sl < ns) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) *(float4*)&As[32 * sl + rr][a0 + 4 * q] = w[sl][q];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---------------- P slices on MFMA: job (slice, column block), balanced over the waves
+    // (80 MFMAs each off the diagonal: column blocks 0 + 3 and 1 + 2 of a slice)
+    int js0, jc0, js1, jc1;
+    if (diag) { js0 = 0; jc0 = wave; js1 = -1; jc1 = 0; }
+    else { js0 = js1 = wave & 1; jc0 = wave < 2 ? 0 : 1; jc1 = wave < 2 ? 3 : 2; }
+    const f32x16 p0 = p_block(As, 32 * js0, Zs, jc0, lane);
+    f32x16 p1;
+    if (js1 >= 0) p1 = p_block(As, 32 * js1, Zs, jc1, lane);
+    __syncthreads();                                   // every read of As and Zs done
+#pragma unroll
+    for (int v = 0; v < 16; ++v) As[32 * js0 + acc_row(v, lane)][32 * jc0 + (lane & 31)] = p0[v];
+    if (js1 >= 0) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) As[32 * js1 + acc_row(v, lane)][32 * jc1 + (lane & 31)] = p1[v];
+    }
+    __syncthreads();
+
+    // ---------------- C = P_ti P_tj^T, k split over the waves (32 each); the four partial
+    // tiles (in Z's place) are summed in a fixed order, and D's tile takes -C (upper part
+    // on the diagonal)
+    const f32x16 c = mfma_abT_x4<32>(As, 0, As, diag ? 0 : 32, 32 * wave, lane);
+    float (*Cp)[33] = (float (*)[33])smem;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) Cp[32 * wave + acc_row(v, lane)][lane & 31] = c[v];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int cc = dc + q;
+        const float sum = ((Cp[dr][cc] + Cp[32 + dr][cc]) + Cp[64 + dr][cc]) + Cp[96 + dr][cc];
+        if (!diag || cc >= dr) dst[q] = dold[q] - sum;
+    }
+}
+
+// Block k's trsm + finalize launch: workgroups [0, n0) update the next diagonal block
+// (pre_update_tile; n0 = 0 for the last block), then n1 trsm tiles, then finalize tiles.
+template <class TA, class TB>
+__global__ __launch_bounds__(GEMM_THREADS) void chol_panel_kernel(TA a, TB b, int n0, int n1,
+                                                                  const int32_t* __restrict__ info,
+                                                                  float* __restrict__ U, int64_t n, int64_t k0, int bs) {
+    if (*info) return;
+    constexpr int L0 = TA::LDS > TB::LDS ? TA::LDS : TB::LDS;
+    constexpr int L = L0 > PRE_FLOATS ? L0 : PRE_FLOATS;
+    __shared__ __attribute__((aligned(16))) float lds[L];
+    const int bid = (int)blockIdx.x;
+    if (bid < n0) pre_update_tile(U, n, k0, bs, bid, lds);
+    else if (bid - n0 < n1) a.run(bid - n0, lds);
+    else b.run(bid - n0 - n1, lds);
 }
 
 // syrk + push of block [k0, k0 + bs) (no super-blocks: depth bs, panel P = V[0:k0, block])
@@ -518,7 +651,7 @@ hipError_t launch_update_diag(float* U, const float* P, int pld, int64_t n, int6
     const int n1 = ntiles(sy.map) - (T == 128 ? 1 : 3);
     const int n2 = ntiles(pu.map);
     hipLaunchKernelGGL((chol_update_diag_kernel<SyrkTask<T>, PushTask<T>>), dim3(1 + n1 + n2), dim3(GEMM_THREADS), 0, s,
-                       sy, pu, n1, info, U, n, k0 - CHOL_NB, P + (k0 - CHOL_NB) * pld, pld, bs);
+                       sy, pu, n1, info, U, n, k0 - CHOL_NB);
     return hipGetLastError();
 }
 
@@ -545,8 +678,8 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
     const int pld = sb * CHOL_NB;
     const int vu = vec_ok(U, n);
     if (sb == 1) {
-        // two launches per block: trsm + finalize of block k, then its syrk + push together
-        // with the factor of block k - 1
+        // two launches per block: trsm + finalize of block k (with its update of the diagonal
+        // block k - 1), then its syrk + push together with the factor of block k - 1
         hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, U, n, (int64_t)(nt - 1) * CHOL_NB,
                            (int)(n - (int64_t)(nt - 1) * CHOL_NB), info);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -564,11 +697,12 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
             ft.lb = OpKMajor<0>{U + k0 * n + k0 + bs, n, r, bs, vu && ((k0 + bs) % 4 == 0)};
             ft.map = rect(64, 64, bs, r, bs);
             ft.epi = EpiStore{U + k0 * n + k0 + bs, n, bs, r, -1.f};
+            const int n0 = k0 > 0 ? PRE_TILES : 0;
             const int n1 = k0 > 0 ? ntiles(tt.map) : 0;
             const int n2 = r > 0 ? ntiles(ft.map) : 0;
-            if (n1 + n2 > 0) {
-                hipLaunchKernelGGL((gemm_f32_dual_kernel<TrsmTask, FinalizeTask>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s,
-                                   tt, ft, n1, info);
+            if (n0 + n1 + n2 > 0) {
+                hipLaunchKernelGGL((chol_panel_kernel<TrsmTask, FinalizeTask>), dim3(n0 + n1 + n2), dim3(GEMM_THREADS), 0, s,
+                                   tt, ft, n0, n1, info, U, n, k0, bs);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
             if (k0 == 0) break;
