@@ -74,6 +74,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int LP = CHOL_NB + 1;    // padded LDS row
 
+// Empty asm statements that fix where a value is computed: pin(x) needs x computed before
+// it, pass(x) makes later uses of x wait for it.  Volatile asm keeps its order, so together
+// they keep arithmetic from being moved past one another.
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pass(float& x) { asm volatile("" : "+v"(x)); }
+
+// v's value in lane l (l a constant), broadcast through an SGPR
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 // 32 x 32 tile of A B^T on MFMA: A rows [ra, ra+32) of the LDS matrix MA, B rows [rb, rb+32)
 // of MB, k over [k0, k0 + kn) (kn even)
 __device__ __forceinline__ f32x16 mfma_tile_abT2(const float (*MA)[LP], int ra, const float (*MB)[LP], int rb, int k0,
@@ -177,21 +188,50 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
 #pragma unroll
             for (int kk = 0; kk < 32; ++kk) a[kk] = A[row][c0 + kk];
             int bad = -1;                                // first failed pivot (uniform)
+            {
+                const float d = lane_f(a[31], 63);
+                if (!(d > 0.f)) bad = 31;
+                a[31] *= __builtin_amdgcn_rsqf(d);       // column 31 of V (the pivot row gets d r)
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // Pivot kk's column is scaled when its turn comes.  Its broadcasts go out first,
+            // the next pivot's entry first; then the FMA into the next pivot's column, and the
+            // next pivot's readlane, rsq and scaling are spread between this pivot's other FMAs,
+            // so their latencies overlap them.  Scheduling barriers keep that order.
 #pragma unroll
             for (int kk = 31; kk >= 0; --kk) {
-                const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[kk]), 32 + kk));
-                if (!(d > 0.f) && bad < 0) bad = kk;
-                const float r = __builtin_amdgcn_rsqf(d);
-                a[kk] *= r;                              // column kk of V (the pivot row gets d r)
                 float vj[32];
 #pragma unroll
-                for (int jj = 0; jj < kk; ++jj)
-                    vj[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[kk]), 32 + jj));
+                for (int jj = kk - 1; jj >= 0; --jj) vj[jj] = lane_f(a[kk], 32 + jj);
                 __builtin_amdgcn_sched_barrier(0);
-                // the next pivot's column first, so its readlane finds it done
+                if (kk > 0) {
+                    constexpr int G = 3;                 // FMAs between the next pivot's steps
+                    a[kk - 1] = fmaf(-a[kk], vj[kk - 1], a[kk - 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const float dn = lane_f(a[kk - 1], 32 + kk - 1);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int jj = kk - 1; jj >= 0; --jj) a[jj] = fmaf(-a[kk], vj[jj], a[jj]);
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int jj = kk - 2; jj >= 0 && jj > kk - 2 - G; --jj) {
+                        a[jj] = fmaf(-a[kk], vj[jj], a[jj]);
+                        pin(a[jj]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    bad = max(bad, dn > 0.f ? -1 : kk - 1);  // pivots run downwards: the first is the largest
+                    float rn = __builtin_amdgcn_rsqf(dn);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int jj = kk - 2 - G; jj >= 0 && jj > kk - 2 - 2 * G; --jj) {
+                        a[jj] = fmaf(-a[kk], vj[jj], a[jj]);
+                        pin(a[jj]);
+                    }
+                    pass(rn);
+                    __builtin_amdgcn_sched_barrier(0);
+                    a[kk - 1] *= rn;
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int jj = kk - 2 - 2 * G; jj >= 0; --jj) a[jj] = fmaf(-a[kk], vj[jj], a[jj]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             if (lane < 32) {
 #pragma unroll
