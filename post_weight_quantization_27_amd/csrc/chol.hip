@@ -66,9 +66,10 @@ __global__ __launch_bounds__(256) void copy_perm_kernel(const float* __restrict_
 //     and inside the panel) in registers and runs its 32 pivots with readlane broadcasts;
 //     after the panel, the rows and columns left of it get one rank-32 update on MFMA
 //     (32 x 32 output tiles spread over the four waves).
-//   inverse Z = V^-1: the four 32 x 32 diagonal blocks are inverted at once, one per wave
-//     (no barriers: a wave's own LDS accesses are in order), then two doubling levels
-//     Z_12 = -Z_11 (V_12 Z_22) on MFMA: 32 -> 64 and 64 -> 128.
+//   inverse Z = V^-1, in place: each 32 x 32 diagonal block by one wave as soon as its panel
+//     is done (no barriers: a wave's own LDS accesses are in order), most of the products
+//     that join them on the waves the last two panels leave free; after the last panel,
+//     the last leaf and one round of MFMA products.
 // A ragged block (bs < 128) is padded with the identity, which leaves the real part unchanged.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -126,6 +127,62 @@ __device__ __forceinline__ f32x16 mfma_tile_ab(const float (*MA)[LP], int ra, in
     return acc;
 }
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// Z = V^-1 of the 32 x 32 diagonal block o = 32 w, in place, by one wave: lane j owns column
+// j of Z and back-substitutes it from the broadcast columns of V (no cross-lane traffic).
+// Right-looking: once z_l is known, it leaves the pending sums s_i (i < l) as independent
+// FMAs, so the dependent chain is two operations per row.  The block (zeros below its
+// diagonal) is written over V's, which only this wave reads.
+__device__ __forceinline__ void leaf_inverse(float (*A)[LP], int o, int lane) {
+    const int j = lane & 31;
+    float s[32], z[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s[i] = i == j ? 1.f : 0.f;
+#pragma unroll
+    for (int l = 31; l >= 0; --l) {
+        z[l] = s[l] * __builtin_amdgcn_rcpf(A[o + l][o + l]);
+#pragma unroll
+        for (int i = 0; i < l; ++i) s[i] = fmaf(-A[o + i][o + l], z[l], s[i]);
+    }
+    if (lane < 32) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) A[o + i][o + j] = z[i];
+    }
+}
+
+// 32 x 32 result of mfma_tile_ab stored at (r0, c0), times s
+__device__ __forceinline__ void put_tile(float (*A)[LP], int r0, int c0, const f32x16& t, float s, int lane) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) A[r0 + acc_row(v, lane)][c0 + (lane & 31)] = s * t[v];
+}
+
+// Z = V^-1 of the 128 x 128 block, in place, in 32 x 32 blocks (V_ij, Z_ij; A = blocks 0-1,
+// B = blocks 2-3), from the blocks inverted:
+//   Z_23 = -Z_22 T23,  T23 = V_23 Z_33;     Z_01 = -Z_00 T01,  T01 = V_01 Z_11
+//   Z_AB = -Z_AA T_AB, T_AB = V_AB Z_BB, so with W(tj) = T_AB(0, tj) - T01 T_AB(1, tj):
+//   Z_AB(1, tj) = -Z_11 T_AB(1, tj),  Z_AB(0, tj) = -Z_00 W(tj).
+// The intermediates live below the diagonal, where Z and V are zero and never stored:
+// T_AB (then W) in rows 64.., columns ..63, T01 in rows 96.., columns 64..95 (after T_AB
+// has been formed: T_AB(., 0) takes k over Z_22's rows only, so it never reads that zero
+// block), T23 in rows 96.., columns 32..63 before T_AB(1, 1) goes there.  Z_22 and Z_33
+// are inverted during panel 1's factor; during panel 0's, the waves it leaves free do this:
+//   wave 1: Z_11, then T01;  wave 2: T23, Z_23, then T_AB(., 1);  wave 3: T_AB(., 0).
+__device__ __forceinline__ void inverse_early(float (*A)[LP], int wave, int lane) {
+    if (wave == 1) {
+        leaf_inverse(A, 32, lane);
+        put_tile(A, 96, 64, mfma_tile_ab(A, 0, 32, A, 32, 32, 32, lane), 1.f, lane);
+    } else if (wave == 2) {
+        put_tile(A, 96, 32, mfma_tile_ab(A, 64, 96, A, 96, 96, 32, lane), 1.f, lane);
+        put_tile(A, 64, 96, mfma_tile_ab(A, 64, 64, A, 96, 32, 32, lane), -1.f, lane);
+        const f32x16 t0 = mfma_tile_ab(A, 0, 64, A, 64, 96, 64, lane);
+        const f32x16 t1 = mfma_tile_ab(A, 32, 64, A, 64, 96, 64, lane);
+        put_tile(A, 64, 32, t0, 1.f, lane);
+        put_tile(A, 96, 32, t1, 1.f, lane);
+    } else if (wave == 3) {
+        put_tile(A, 64, 0, mfma_tile_ab(A, 0, 64, A, 64, 64, 32, lane), 1.f, lane);
+        put_tile(A, 96, 0, mfma_tile_ab(A, 32, 64, A, 64, 64, 32, lane), 1.f, lane);
+    }
+}
 
 constexpr int DIAG_FLOATS = CHOL_NB * LP + 4;           // A (then Z in its place), the failed-pivot word
 
@@ -251,6 +308,9 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
 #pragma unroll
                 for (int v = 0; v < 16; ++v) A[32 * ti + acc_row(v, lane)][32 * tj + (lane & 31)] -= acc[v];
             }
+            // the inverse, as far as the finished blocks allow (see below)
+            if (p == 1) leaf_inverse(A, 32 * wave, lane);          // Z_22, Z_33
+            if (p == 0) inverse_early(A, wave, lane);
         }
         __syncthreads();
         if (fail) {                                      // same decision in every thread
@@ -269,58 +329,27 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
         }
     }
 
-    // ---------------- inverse, in place: Z = V^-1 overwrites V block by block; the products'
-    // intermediates go to the lower-left blocks (rows 64.., columns ..63), which hold nothing.
-    // Every block read as a factor of Z keeps its zeros below the diagonal.
-    // Leaves: one wave per 32 x 32 diagonal block; lane j owns column j of Z and
-    // back-substitutes it from the broadcast rows of V (no cross-lane traffic), then writes
-    // the block (zeros below its diagonal) over V's, which only this wave reads.
-    {
-        const int o = 32 * wave;
-        const int j = lane & 31;
-        float z[32];
+    // ---------------- inverse, rest: Z_00 (wave 0); meanwhile, per column block tj of the
+    // upper right (wave 3 - tj): Z_AB(1, tj) = -Z_11 T_AB(1, tj) and
+    // W(tj) = T_AB(0, tj) - T01 T_AB(1, tj) over T_AB(0, tj); then everything left of Z's top
+    // row block is -Z_00 [T01 | W(0) | W(1)].
+    if (wave == 0) {
+        leaf_inverse(A, 0, lane);
+    } else if (wave >= 2) {
+        const int tj = 3 - wave;
+        put_tile(A, 32, 64 + 32 * tj, mfma_tile_ab(A, 32, 32, A, 96, 32 * tj, 32, lane), -1.f, lane);
+        const f32x16 pr = mfma_tile_ab(A, 96, 64, A, 96, 32 * tj, 32, lane);
 #pragma unroll
-        for (int i = 31; i >= 0; --i) {
-            const float rv = __builtin_amdgcn_rcpf(A[o + i][o + i]);
-            float sacc = 0.f;
-#pragma unroll
-            for (int l = i + 1; l < 32; ++l) sacc = fmaf(A[o + i][o + l], z[l], sacc);
-            z[i] = (i == j) ? rv : (i < j ? -sacc * rv : 0.f);
-        }
-        if (lane < 32) {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) A[o + i][o + j] = z[i];
+        for (int v = 0; v < 16; ++v) {
+            float& w = A[64 + acc_row(v, lane)][32 * tj + (lane & 31)];
+            w = w - pr[v];
         }
     }
     __syncthreads();
-
-    // ---------------- doubling 32 -> 64: Z_01 = -Z_00 (V_01 Z_11) for the pairs (0,1), (2,3),
-    // one wave each; T = V_01 Z_11 goes to rows 64 + 32 w, columns 32 w (read by no other
-    // wave), and Z_01 over V_01 once this wave has read it
-    if (wave < 2) {
-        const int o0 = 64 * wave, o1 = o0 + 32;
-        const int sr = 64 + 32 * wave, sc = 32 * wave;
-        f32x16 t = mfma_tile_ab(A, o0, o1, A, o1, o1, 32, lane);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) A[sr + acc_row(v, lane)][sc + (lane & 31)] = t[v];
-        t = mfma_tile_ab(A, o0, o0, A, sr, sc, 32, lane);       // k over Z_00 columns, T rows
-#pragma unroll
-        for (int v = 0; v < 16; ++v) A[o0 + acc_row(v, lane)][o1 + (lane & 31)] = -t[v];
-    }
-    __syncthreads();
-
-    // ---------------- doubling 64 -> 128: Z_AB = -Z_AA (V_AB Z_BB), A = [0,64), B = [64,128);
-    // T = V_AB Z_BB to the lower-left 64 x 64 block (read by nobody while T is formed), then
-    // Z_AB over V_AB after the barrier that ends every read of it
-    {
-        const int ti = wave >> 1, tj = wave & 1;
-        const f32x16 t = mfma_tile_ab(A, 32 * ti, 64, A, 64, 64 + 32 * tj, 64, lane);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) A[64 + 32 * ti + acc_row(v, lane)][32 * tj + (lane & 31)] = t[v];
-        __syncthreads();
-        const f32x16 u = mfma_tile_ab(A, 32 * ti, 0, A, 64, 32 * tj, 64, lane);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) A[32 * ti + acc_row(v, lane)][64 + 32 * tj + (lane & 31)] = -u[v];
+    if (wave < 3) {
+        // wave 0: Z_01 from T01 (rows 96.., columns 64..); waves 1, 2: Z_AB(0, wave - 1)
+        const int sr = wave == 0 ? 96 : 64, sc = wave == 0 ? 64 : 32 * (wave - 1);
+        put_tile(A, 0, 32 + 32 * wave, mfma_tile_ab(A, 0, 0, A, sr, sc, 32, lane), -1.f, lane);
     }
     __syncthreads();
 
@@ -487,7 +516,7 @@ hipError_t launch_near(float* U, const float* Pk, int pld, int64_t n, int64_t s0
 // block was applied by block k's trsm launch (pre_update_tile), and the syrk tiles covering
 // it are left out of this grid, so the serial diagonal factor overlaps the rest of the update.
 template <class TA, class TB>
-__global__ __launch_bounds__(GEMM_THREADS) void chol_update_diag_kernel(TA a, TB b, int n1, int32_t* __restrict__ info,
+__global__ __launch_bounds__(GEMM_THREADS, 2) void chol_update_diag_kernel(TA a, TB b, int n1, int32_t* __restrict__ info,
                                                                         float* __restrict__ U, int64_t n, int64_t kd0) {
     if (*info) return;
     constexpr int L0 = TA::LDS > TB::LDS ? TA::LDS : TB::LDS;
