@@ -194,7 +194,10 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
     int& fail = *(int*)(smem + CHOL_NB * LP);           // failed pivot + 1 of the current panel
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // ---------------- load: thread = (row, 64-column half), all loads in flight
+    // ---------------- load: thread = (row, 64-column half), all loads in flight.  Below the
+    // diagonal, U holds zeros (every writer of U keeps it so); nothing here reads those
+    // entries as factors anyway: the panels carry them along as meaningless values and
+    // write them back as zeros, the inverse reads only blocks on or above the diagonal.
     {
         const int i = tid >> 1, c0 = 64 * (tid & 1);
         const float* src = U + (k0 + i) * n + k0 + c0;
@@ -213,10 +216,7 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
             }
         }
 #pragma unroll
-        for (int q = 0; q < 64; ++q) {
-            const int j = c0 + q;
-            A[i][j] = j >= i ? v[q] : 0.f;
-        }
+        for (int q = 0; q < 64; ++q) A[i][c0 + q] = v[q];
     }
     __syncthreads();
 
@@ -353,20 +353,21 @@ __device__ __forceinline__ void diag_block(float* __restrict__ U, int64_t n, int
     }
     __syncthreads();
 
-    // ---------------- store: thread = (row, 64-column half)
+    // ---------------- store: thread = (row, 64-column half).  Below the diagonal the block
+    // holds zeros (leaves, and rows 32.. of columns ..31, never written) except in the
+    // intermediates' places, rows 64.. of columns ..63 and rows 96.. of columns 64..95;
+    // those are skipped (U keeps its zeros there), everything else is stored as it is.
     {
         const int i = tid >> 1, c0 = 64 * (tid & 1);
         float* dst = U + (k0 + i) * n + k0 + c0;
         if (bs == CHOL_NB && (n % 4) == 0) {
+            const int q0 = c0 == 0 ? (i >= 64 ? 16 : 0) : (i >= 96 ? 8 : 0);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                float t[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int j = c0 + 4 * q + c;
-                    t[c] = j >= i ? A[i][j] : 0.f;
+                if (q >= q0) {
+                    const int j = c0 + 4 * q;
+                    *(float4*)(dst + 4 * q) = make_float4(A[i][j], A[i][j + 1], A[i][j + 2], A[i][j + 3]);
                 }
-                *(float4*)(dst + 4 * q) = make_float4(t[0], t[1], t[2], t[3]);
             }
         } else if (i < bs) {
             for (int q = 0; q < 64; ++q) {
