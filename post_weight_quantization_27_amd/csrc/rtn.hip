@@ -55,6 +55,7 @@ struct RtnArgs {
     const uint16_t* zeros_in;   // zero-point form: fixed zeros (with scales_in) or NULL
     uint16_t* zeros_out;        // zero-point form: the zero of every (row, group)
     int top;                    // zero-point form: largest code, 2^bits - 1
+    float near;                 // 2^(bits - 20): the rounding's margin from half-integers
 };
 
 // Zero of a group in the zero-point form: fixed (clamped to [0, top]) or from the range.
@@ -152,23 +153,33 @@ __device__ __forceinline__ float dpp_mov(float v) {
 }
 
 // max over aligned groups of LG lanes: swaps within quads, then the mirror of each 8-lane
-// half-row and of each 16-lane row (DPP, no LDS), then lane shuffles across rows
+// half-row and of each 16-lane row (DPP, no LDS), then lane shuffles across rows.  The
+// values are maxima of |w| (or of w, -w and 0): at least 0 or -0, whose bit patterns as
+// signed integers order as the floats do (-0 below +0), so an integer max serves.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
 template <int LG>
-__device__ __forceinline__ float lanes_max(float v) {
-    if (LG >= 2) v = fmaxf(v, dpp_mov<0xB1>(v));       // quad_perm [1, 0, 3, 2]
-    if (LG >= 4) v = fmaxf(v, dpp_mov<0x4E>(v));       // quad_perm [2, 3, 0, 1]
-    if (LG >= 8) v = fmaxf(v, dpp_mov<0x141>(v));      // row_half_mirror
-    if (LG >= 16) v = fmaxf(v, dpp_mov<0x140>(v));     // row_mirror
-    if (LG >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
-    if (LG >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+__device__ __forceinline__ float lanes_max(float f) {
+    int v = __builtin_bit_cast(int, f);
+    if (LG >= 2) v = max(v, dpp_mov_i<0xB1>(v));       // quad_perm [1, 0, 3, 2]
+    if (LG >= 4) v = max(v, dpp_mov_i<0x4E>(v));       // quad_perm [2, 3, 0, 1]
+    if (LG >= 8) v = max(v, dpp_mov_i<0x141>(v));      // row_half_mirror
+    if (LG >= 16) v = max(v, dpp_mov_i<0x140>(v));     // row_mirror
+    if (LG >= 32) v = max(v, __shfl_xor(v, 16, 64));
+    if (LG >= 64) v = max(v, __shfl_xor(v, 32, 64));
+    return __builtin_bit_cast(float, v);
 }
 
 // Groups that tile their rows, LG lanes per group (LG = g * sizeof(T) / 16).  The host
 // guarantees that W, the codes and the nibbles each span less than 4 GiB, so addresses are
 // 32-bit offsets from the (uniform) base pointers, and that there are fewer than 2^31
 // groups; the scale index of a group is its segment number.
-template <int DT, int LG, bool ZP>
+// FAST: rows contiguous (ldw = n) and scales (and zeros) computed here, the common case:
+// a group's offsets are multiples of its segment number, and a zero scale needs no branch
+// (reciprocal 0 and clamp bounds [0, 0] give the code 0, or Z = 0).
+template <int DT, int LG, bool ZP, bool FAST>
 __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
     typedef typename Elem<DT>::T T;
     constexpr int ES = (int)sizeof(T);
@@ -192,9 +203,14 @@ __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
             const uint32_t sg0 = (uint32_t)((it * U + u) * SPW) + (uint32_t)sub;
             live[u] = sg0 < nseg;
             seg[u] = live[u] ? sg0 : 0u;                   // a dead slot reads group 0
-            rr[u] = (uint32_t)(((uint64_t)seg[u] * a.dmul) >> a.dsh);
-            const uint32_t G = seg[u] - rr[u] * ng;
-            raw[u] = *(const uint4*)(Wb + (rr[u] * ldb + G * glb + (uint32_t)li * 16u));
+            if (FAST) {
+                rr[u] = 0;
+                raw[u] = *(const uint4*)(Wb + (seg[u] * glb + (uint32_t)li * 16u));
+            } else {
+                rr[u] = (uint32_t)(((uint64_t)seg[u] * a.dmul) >> a.dsh);
+                const uint32_t G = seg[u] - rr[u] * ng;
+                raw[u] = *(const uint4*)(Wb + (rr[u] * ldb + G * glb + (uint32_t)li * 16u));
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -222,31 +238,75 @@ __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
                 amax = lanes_max<LG>(amax);
             }
             uint16_t sb;
-            if (a.scales_in) sb = live[u] ? a.scales_in[seg[u]] : 0;
+            if (!FAST && a.scales_in) sb = live[u] ? a.scales_in[seg[u]] : 0;
             else sb = ZP ? zp_scale_bits(nlo, amax, a.top) : scale_bits_from_absmax(amax, a.qmax);
             if (live[u] && li == 0) a.scales_out[seg[u]] = sb;
             const float sc = f16_bits_to_f32(sb);
-            const float rs = __builtin_amdgcn_rcpf(sc);       // only a first guess: the fma check is exact
             int q[EPV];
-            if (ZP) {
-                const float z = rtn_zero(a, live[u], seg[u], nlo, sc);
-                if (live[u] && li == 0) a.zeros_out[seg[u]] = (uint16_t)z;
-                const float qlo = -z, qhi = (float)a.top - z;
+            if (FAST) {
+                // stored code = clamp(rne(w / s) + off, lo, hi): off = Z (zero-point form) or
+                // qmax + 1 (the nibble's offset; the signed code is 8 less)
+                const bool pos = sc > 0.f;
+                const float rs = pos ? __builtin_amdgcn_rcpf(sc) : 0.f;
+                float off, lo, hi;
+                if (ZP) {
+                    const float topf = (float)a.top;
+                    off = pos ? round_quot_clamp(nlo, sc, rs, 0.f, topf) : 0.f;
+                    if (live[u] && li == 0) a.zeros_out[seg[u]] = (uint16_t)off;
+                    lo = 0.f;
+                    hi = pos ? topf : 0.f;
+                } else {
+                    off = (float)(a.qmax + 1);
+                    lo = pos ? off - (float)a.qmax : off;
+                    hi = pos ? off + (float)a.qmax : off;
+                }
+                // t = fma(w, 1/s, off) is within 2^(bits - 21) of w / s + off wherever the
+                // clamp leaves it unchanged (|t| < 2^(bits + 1), the reciprocal within one
+                // ulp), so rint(t) is exact unless t lies within near = 2^(bits - 20) of a
+                // half-integer; then (rarely, one branch per wave) the vector takes the
+                // exact rounding
+                float kf[EPV];
+                float dev = 0.f;                         // largest |t - rint(t)| of the vector
 #pragma unroll
-                for (int k = 0; k < EPV; ++k) q[k] = sc > 0.f ? (int)(round_quot_clamp(v[k], sc, rs, qlo, qhi) + z) : 0;
+                for (int k = 0; k < EPV; ++k) {
+                    const float t = fmaf(v[k], rs, off);
+                    kf[k] = rintf(t);
+                    dev = fmaxf(dev, fabsf(t - kf[k]));
+                }
+                if (__builtin_amdgcn_ballot_w64(dev > 0.5f - a.near) != 0) {
+#pragma unroll
+                    for (int k = 0; k < EPV; ++k) kf[k] = round_quot_clamp(v[k], sc, rs, lo - off, hi - off) + off;
+                }
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) q[k] = (int)__builtin_amdgcn_fmed3f(kf[k], lo, hi);
             } else {
+                const float rs = __builtin_amdgcn_rcpf(sc);   // only a first guess: the fma check is exact
+                if (ZP) {
+                    const float z = rtn_zero(a, live[u], seg[u], nlo, sc);
+                    if (live[u] && li == 0) a.zeros_out[seg[u]] = (uint16_t)z;
+                    const float qlo = -z, qhi = (float)a.top - z;
 #pragma unroll
-                for (int k = 0; k < EPV; ++k) q[k] = sc > 0.f ? quant_code_sel(v[k], sc, rs, a.qmax) : 0;
+                    for (int k = 0; k < EPV; ++k)
+                        q[k] = sc > 0.f ? (int)(round_quot_clamp(v[k], sc, rs, qlo, qhi) + z) : 0;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < EPV; ++k) q[k] = sc > 0.f ? quant_code_sel(v[k], sc, rs, a.qmax) : 0;
+                }
             }
             if (!live[u]) continue;
-            const uint32_t c = (seg[u] - rr[u] * ng) * (uint32_t)a.gl + (uint32_t)(li * EPV);
+            // FAST: row rr * n + column c of the group = seg * gl + li * EPV (rows contiguous)
+            const uint32_t c = FAST ? seg[u] * (uint32_t)a.gl + (uint32_t)(li * EPV)
+                                    : (seg[u] - rr[u] * ng) * (uint32_t)a.gl + (uint32_t)(li * EPV);
+            // FAST leaves the stored code (the nibble) in q; the signed code is 8 less
+            const int qo = FAST && !ZP ? a.qmax + 1 : 0;
             if (a.codes) {
                 int8_t* dst = a.codes + (rr[u] * n + c);
                 uint32_t b[EPV / 4];
 #pragma unroll
                 for (int k = 0; k < EPV / 4; ++k)
-                    b[k] = (uint32_t)(q[4 * k] & 0xff) | ((uint32_t)(q[4 * k + 1] & 0xff) << 8) |
-                           ((uint32_t)(q[4 * k + 2] & 0xff) << 16) | ((uint32_t)(q[4 * k + 3] & 0xff) << 24);
+                    b[k] = (uint32_t)((q[4 * k] - qo) & 0xff) | ((uint32_t)((q[4 * k + 1] - qo) & 0xff) << 8) |
+                           ((uint32_t)((q[4 * k + 2] - qo) & 0xff) << 16) |
+                           ((uint32_t)((q[4 * k + 3] - qo) & 0xff) << 24);
                 if (EPV == 8) *(uint2*)dst = make_uint2(b[0], b[EPV / 4 - 1]);
                 else *(uint32_t*)dst = b[0];
             }
@@ -254,7 +314,7 @@ __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
                 uint8_t* dst = a.packed + (rr[u] * (n / 2) + c / 2);
                 uint32_t nib = 0;
 #pragma unroll
-                for (int k = 0; k < EPV; ++k) nib |= (uint32_t)(q[k] + (ZP ? 0 : 8)) << (4 * k);
+                for (int k = 0; k < EPV; ++k) nib |= (uint32_t)(q[k] + (ZP || FAST ? 0 : 8)) << (4 * k);
                 if (EPV == 8) *(uint32_t*)dst = nib;
                 else *(uint16_t*)dst = (uint16_t)nib;
             }
@@ -548,6 +608,7 @@ hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
             (!packed || aligned(packed, 2));
     a.scales_in = scales_in; a.codes = codes; a.packed = packed; a.scales_out = scales_out;
     a.zeros_in = zeros_in; a.zeros_out = zeros_out; a.top = (1 << bits) - 1;
+    a.near = ldexpf(1.f, bits - 20);
     const bool zp = zeros_out != nullptr;
     // group path: whole groups per row, 16-byte vectors, LG a power of two <= 64
     const int64_t gbytes = group_size * (int64_t)es;
@@ -565,14 +626,14 @@ hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
         a.dmul = (uint64_t)((((unsigned __int128)1 << a.dsh) + (unsigned __int128)a.ng - 1) / (unsigned __int128)a.ng);
         const int64_t waves = cdiv(a.nseg, (int64_t)(64 / lg) * 4);
         const int64_t want = cdiv(waves, 4);
+        const bool fast = !scales_in && !zeros_in && ldw == n;
+#define PWQ_RTN_K(DT, LGV, ZPV, FV)                                                                            \
+        hipLaunchKernelGGL((rtn_group_kernel<DT, LGV, ZPV, FV>),                                               \
+                           dim3((unsigned)resident_blocks<rtn_group_kernel<DT, LGV, ZPV, FV>>(want)), dim3(256), 0, s, a)
 #define PWQ_RTN_G(DT, LGV)                                                                                  \
         do {                                                                                                    \
-            if (zp) hipLaunchKernelGGL((rtn_group_kernel<DT, LGV, true>),                                       \
-                                       dim3((unsigned)resident_blocks<rtn_group_kernel<DT, LGV, true>>(want)),  \
-                                       dim3(256), 0, s, a);                                                     \
-            else hipLaunchKernelGGL((rtn_group_kernel<DT, LGV, false>),                                         \
-                                    dim3((unsigned)resident_blocks<rtn_group_kernel<DT, LGV, false>>(want)),    \
-                                    dim3(256), 0, s, a);                                                        \
+            if (zp) { if (fast) PWQ_RTN_K(DT, LGV, true, true); else PWQ_RTN_K(DT, LGV, true, false); }        \
+            else { if (fast) PWQ_RTN_K(DT, LGV, false, true); else PWQ_RTN_K(DT, LGV, false, false); }         \
         } while (0)
 #define PWQ_RTN_LG(DT)                                      \
         switch (lg) {                                       \
@@ -588,6 +649,7 @@ hipError_t rtn_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
         else { PWQ_RTN_LG(1) }
 #undef PWQ_RTN_LG
 #undef PWQ_RTN_G
+#undef PWQ_RTN_K
         return hipGetLastError();
     }
     const int64_t waves = cdiv(a.nseg, 64 / L);

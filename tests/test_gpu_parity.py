@@ -86,6 +86,8 @@ def test_rtn_bit_exact(pwq, m, n, g, dt):
     W[0, :] = 0.0                                                # all-zero row -> s = 0, codes 0
     if n >= 8:
         W[1, :8] = np.array([7, -3.5, 0.5, 2.5, -1.5, 0, 1, -7], dtype=dt)   # exact ties
+    if m > 2:
+        W[2, :] = dt(1e-7)                                       # nonzero, but s underflows to 0 in fp16
     want = O.rtn(W, 4, g)
     out = pwq.rtn_quantize(dev(W), 4, g, want_packed=(n % 2 == 0))
     assert np.array_equal(host(out["scales"]).view(np.uint16), want["scales"].view(np.uint16))
