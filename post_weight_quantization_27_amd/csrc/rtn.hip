@@ -442,6 +442,54 @@ __global__ __launch_bounds__(256) void dequant_vec_kernel(DqArgs a) {
     }
 }
 
+// Float16 output from nibbles whose groups tile the rows (g = 8 * 2^gsh, no g_idx), rows
+// contiguous: chunk t of 8 columns is nibble word t, output vector t, group t >> gsh.  The
+// arithmetic is packed float16: 1024 + n is exact (the bits 0x6400 | n), so is
+// (1024 + n) - (1024 + z) = n - z, and the product with the scale is rounded once, like the
+// float32 product (exact) rounded to float16.  Fewer than 2^31 chunks (host check).
+typedef _Float16 dq_h2 __attribute__((ext_vector_type(2)));
+typedef unsigned int dq_u4 __attribute__((ext_vector_type(4)));
+template <bool ZP>
+__global__ __launch_bounds__(256) void dequant_f16_kernel(DqArgs a, int gsh) {
+    constexpr int U = 4;
+    const uint32_t total = (uint32_t)(a.m * a.chunks);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave_id = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t nwaves = (gridDim.x * blockDim.x) >> 6;
+    const uint32_t* P = (const uint32_t*)a.packed;
+    dq_u4* O = (dq_u4*)a.out;
+    for (uint32_t base = wave_id * 64 * U; base < total; base += nwaves * 64 * U) {
+        uint32_t w[U], s2[U], o2[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t t = base + 64 * u + lane;
+            const uint32_t tt = t < total ? t : 0u;
+            w[u] = P[tt];
+            const uint32_t gi = tt >> gsh;
+            const uint32_t sb = a.scales[gi];
+            s2[u] = sb | (sb << 16);
+            const uint32_t ob = 0x6400u | (ZP ? (uint32_t)a.zeros[gi] : 8u);
+            o2[u] = ob | (ob << 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t t = base + 64 * u + lane;
+            if (t >= total) continue;
+            const uint32_t lo = w[u] & 0x0F0F0F0Fu, hi = (w[u] >> 4) & 0x0F0F0F0Fu;
+            dq_u4 r;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // low half: byte j of lo (nibble 2j), high half: byte j of hi (nibble 2j + 1)
+                const uint32_t sel = (uint32_t)j | 0x0C00u | ((uint32_t)(4 + j) << 16) | 0x0C000000u;
+                const uint32_t h = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+                const dq_h2 x = __builtin_bit_cast(dq_h2, h) - __builtin_bit_cast(dq_h2, o2[u]);
+                r[j] = __builtin_bit_cast(uint32_t, x * __builtin_bit_cast(dq_h2, s2[u]));
+            }
+            __builtin_nontemporal_store(r, O + t);
+        }
+    }
+}
+
 template <int OT, bool ZP>
 __global__ __launch_bounds__(256) void dequant_kernel(DqArgs a) {
     const int64_t total = a.m * a.chunks;
@@ -680,6 +728,18 @@ hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint
     const size_t os = out_dtype == 0 ? 4 : 2;
     a.vec = (n % 8 == 0) && (group_size == 0 || (group_size % 8 == 0 && !g_idx)) && aligned(out, 8 * os) &&
             (!packed || aligned(packed, 4)) && (!codes || aligned(codes, 8));
+    const int64_t gc = group_size / 8;
+    if (packed && out_dtype == 1 && group_size > 0 && group_size % 8 == 0 && (gc & (gc - 1)) == 0 &&
+        n % group_size == 0 && !g_idx && aligned(packed, 4) && aligned(out, 16) && m * a.chunks < ((int64_t)1 << 31)) {
+        int gsh = 0;
+        while (((int64_t)1 << gsh) < gc) ++gsh;
+        const int64_t want = cdiv(m * a.chunks, 4 * 256);
+        if (zp) hipLaunchKernelGGL((dequant_f16_kernel<true>), dim3((unsigned)resident_blocks<dequant_f16_kernel<true>>(want)),
+                                   dim3(256), 0, s, a, gsh);
+        else hipLaunchKernelGGL((dequant_f16_kernel<false>), dim3((unsigned)resident_blocks<dequant_f16_kernel<false>>(want)),
+                                dim3(256), 0, s, a, gsh);
+        return hipGetLastError();
+    }
     if (a.vec) {
         const int64_t want = cdiv(m * a.chunks, 4 * 256);
 #define PWQ_DQV(OT, ZPV) \

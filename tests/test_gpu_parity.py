@@ -96,6 +96,30 @@ def test_rtn_bit_exact(pwq, m, n, g, dt):
         assert np.array_equal(host(out["packed"]), O.pack_int4(want["codes"]))
 
 
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("s", [1.0, 0.75])
+def test_rtn_near_half_integers(pwq, s, sym):
+    """Weights (k + 1/2 + d) s with tiny d of either sign, some inside and some outside the
+    margin the kernel uses to trust its reciprocal-based rounding; the exact answer depends
+    only on the sign of d (scale s exact in fp16: the group's extremes are +-7.5 s)."""
+    deltas = [0.0, 2.0 ** -24, -2.0 ** -24, 2.0 ** -22, -2.0 ** -22, 2.0 ** -20, -2.0 ** -20,
+              2.0 ** -18, -2.0 ** -18, 2.0 ** -16, -2.0 ** -16, 2.0 ** -14, -2.0 ** -14]
+    rows = []
+    for k in range(-7, 7):
+        row = [(k + 0.5 + d) * s for d in deltas]
+        row += [7.5 * s, -7.5 * s] if not sym else [7.0 * s, -7.0 * s]
+        rows.append(row + [0.0] * (128 - len(row)))
+    W = np.array(rows, dtype=np.float32)
+    Wr = np.repeat(W, 4, axis=0)                                 # enough rows for several waves
+    want = O.rtn(Wr, 4, 128, sym=sym)
+    f = pwq.rtn_quantize if sym else pwq.rtn_quantize_zp
+    out = f(dev(Wr), 4, 128)
+    assert np.array_equal(host(out["scales"]).view(np.uint16), want["scales"].view(np.uint16))
+    if not sym:
+        assert np.array_equal(host(out["zeros"]).view(np.uint16), want["zeros"])
+    assert np.array_equal(host(out["codes"]), want["codes"])
+
+
 def test_rtn_fixed_scales_and_bits(pwq):
     rng = np.random.default_rng(1)
     W = rand_w(rng, 40, 256)
