@@ -2,7 +2,8 @@
 
 One step = every step of the path for every layer of the workload, on inputs already
 resident in HBM: Hessian from X, damping, [act-order], H^-1 factor, GPTQ (INT4 packed +
-fp16 scales), RTN, dequant of the GPTQ result, and the reconstruction MSE of both.
+fp16 scales), RTN, dequant of the GPTQ result, and the reconstruction MSE of both (through
+the tokens, or through H when n_tok >= 16 d_in, where that product is the cheaper one).
 The value is weights quantized per second (sum of d_out * d_in over the layers / step).
 
 Prints ONE JSON line.  The value comes from K timed steps with no events between the
@@ -71,9 +72,17 @@ class Layer:
         self.rq = {}
         self.what = torch.empty((m, n), dtype=torch.float16, device=dev)
         self.mse = torch.empty(2, dtype=torch.float64, device=dev)
+        self.lam = torch.zeros(1, dtype=torch.float32, device=dev)     # what damping adds to diag H
         self.act = act_order
         self.zp = zero_point
+        # the reconstruction MSE through H (d_out x d_in^2 float32 MFMA) when that is cheaper
+        # than through the tokens (n_tok x d_in x d_out bfloat16 MFMA, sixteen times the rate)
+        self.mse_h = mse_through_hessian(spec)
         del X, W
+
+
+def mse_through_hessian(spec):
+    return spec.n_tok >= 16 * spec.d_in
 
 
 def run_step(L, pwq, timers=None, after_hessian=None, parts="all"):
@@ -110,7 +119,7 @@ def run_step(L, pwq, timers=None, after_hessian=None, parts="all"):
     k = t("hessian_accumulate"); L.H.zero_(); pwq.hessian_accumulate(L.X, L.H); done(k)
     if after_hessian is not None:
         after_hessian()
-    k = t("hessian_damp"); pwq.hessian_damp(L.H, s.damp); done(k)
+    k = t("hessian_damp"); pwq.hessian_damp(L.H, s.damp, lambda_out=L.lam); done(k)
     perm = None
     if L.act:
         k = t("act_order_perm"); perm = pwq.act_order_perm(L.H); done(k)
@@ -130,11 +139,19 @@ def run_step(L, pwq, timers=None, after_hessian=None, parts="all"):
                     out=L.what)
     done(k)
     k = t("recon_mse")
-    pwq.recon_mse(L.X, L.W, L.gq["scales"], s.bits, s.group_size, packed=L.gq["packed"], g_idx=L.gq.get("g_idx"),
-                  mse=L.mse[0:1], zeros=L.gq.get("zeros"))
-    if parts == "all":
-        pwq.recon_mse(L.X, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"], mse=L.mse[1:2],
-                      zeros=L.rq.get("zeros"))
+    if L.mse_h:
+        # H is damped by now: its damping is taken off as the shift
+        pwq.recon_mse_hessian(L.H, s.n_tok, L.W, L.gq["scales"], s.bits, s.group_size, packed=L.gq["packed"],
+                              g_idx=L.gq.get("g_idx"), zeros=L.gq.get("zeros"), shift=L.lam, mse=L.mse[0:1])
+        if parts == "all":
+            pwq.recon_mse_hessian(L.H, s.n_tok, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"],
+                                  zeros=L.rq.get("zeros"), shift=L.lam, mse=L.mse[1:2])
+    else:
+        pwq.recon_mse(L.X, L.W, L.gq["scales"], s.bits, s.group_size, packed=L.gq["packed"], g_idx=L.gq.get("g_idx"),
+                      mse=L.mse[0:1], zeros=L.gq.get("zeros"))
+        if parts == "all":
+            pwq.recon_mse(L.X, L.W, L.rq["scales"], s.bits, s.group_size, packed=L.rq["packed"], mse=L.mse[1:2],
+                          zeros=L.rq.get("zeros"))
     done(k)
 
 
@@ -155,8 +172,10 @@ def work_of(name, spec, zero_point=False):
         return "mfma_f32", 2 * n ** 3 / 3, "flop"
     if name == "gptq_quantize_layer":           # trailing products + in-block rank-1 updates
         return "mfma_f32", m * n * (n - spec.block_size) + m * n * (spec.block_size - 1), "flop"
-    if name == "recon_mse":                     # two calls (GPTQ and RTN) of 2 N n m, bf16 MFMA
-        return "mfma_bf16", 2 * (2 * N * n * m), "flop"
+    if name == "recon_mse":                     # two calls (GPTQ and RTN)
+        if mse_through_hessian(spec):           # 2 m n^2 each, float32 MFMA
+            return "mfma_f32", 2 * (2 * m * n * n), "flop"
+        return "mfma_bf16", 2 * (2 * N * n * m), "flop"     # 2 N n m each, bf16 MFMA
     if name == "rtn_quantize":
         return "hbm", m * n * wb + m * n // 2 + pg * m * ng, "byte"
     if name == "dequant":
@@ -439,6 +458,7 @@ def main():
                    "n_tok": specs[0].n_tok, "bits": specs[0].bits, "group_size": specs[0].group_size,
                    "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order),
                    "zero_point": bool(a.zero_point), "layer_streams": bool(a.streams), "stagger": stagger,
+                   "mse_route": {L.spec.name: ("hessian" if L.mse_h else "tokens") for L in layers},
                    "rtn_off_chain": side},
         "roofline": roof,
         "xtx_mfma_util": xtx,

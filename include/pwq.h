@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PWQ_ABI_VERSION 2
+#define PWQ_ABI_VERSION 3
 
 typedef enum pwq_status {
     PWQ_OK = 0,
@@ -196,6 +196,32 @@ pwq_status pwq_recon_mse(const void* X, int x_dtype, int64_t n_tok, int64_t d_in
                          const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,
                          int64_t d_out, int32_t bits, int32_t group_size,
                          double* mse, void* ws, size_t ws_bytes, void* stream);
+
+/* pwq_recon_mse_hessian: the same mean square, through the Hessian the path has formed:
+ * sum over tokens and outputs of (X (W - What)^T)^2 = tr((W - What) X^T X (W - What)^T)
+ * = tr((W - What) H (W - What)^T) / 2 for H = 2 X^T X ([GPTQ-P] "OBQ Foundation": the layer
+ * error as a quadratic form in H), so
+ *   mse = tr((W - What) (H - shift I) (W - What)^T) / (2 n_tok d_out),
+ * equal to pwq_recon_mse's in exact arithmetic.  One d_out x d_in x d_in float32 MFMA
+ * product instead of n_tok x d_in x d_out: the cheaper route when n_tok is well above d_in
+ * (float32 MFMA runs at a sixteenth of the bfloat16 rate).
+ *   H        d_in x d_in float32, both triangles (pwq_hessian_accumulate's output), row
+ *            stride ldh >= d_in; may already be damped: h_shift (device float, or NULL for
+ *            0) is what damping added to its diagonal (pwq_hessian_damp's lambda_out).
+ *   n_tok    the number of tokens H was accumulated over.
+ *   W, codes / packed, scales, g_idx, bits, group_size: as pwq_recon_mse; zeros NULL for
+ *            symmetric codes (int8, nibble - 8), else the zero-point form (uint8 codes,
+ *            nibble = code, What = S (code - Z)).
+ *   mse      device double.
+ *   ws       pwq_recon_mse_hessian_workspace_size(d_in, d_out) bytes.
+ * n_tok == 0 or d_out == 0 writes 0 to *mse; then only mse is read (the other pointers may
+ * be NULL). */
+size_t pwq_recon_mse_hessian_workspace_size(int64_t d_in, int64_t d_out);
+pwq_status pwq_recon_mse_hessian(const float* H, int64_t ldh, int64_t d_in, int64_t n_tok, const float* h_shift,
+                                 const void* W, int w_dtype, int64_t ldw,
+                                 const uint8_t* packed, const void* codes, const uint16_t* scales,
+                                 const uint16_t* zeros, const int32_t* g_idx, int64_t d_out, int32_t bits,
+                                 int32_t group_size, double* mse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ Zero-point form
  * The affine quantizer of [MQM] "Affine Quantization" and "Group-wise Quantization": per

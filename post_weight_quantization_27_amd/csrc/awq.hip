@@ -139,30 +139,6 @@ __global__ __launch_bounds__(256) void awq_delta_kernel(AwqArgs a) {
     }
 }
 
-// part[tile] = sum over the tile of (dW H)[row][col] * dW[row][col] (float64 per workgroup)
-struct EpiDot {
-    static constexpr bool kRmw = true;
-    const float* dW;
-    int64_t ld, M, N;
-    double* part;
-    float acc;
-    __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
-        return (row < M && col < N) ? dW[row * ld + col] : 0.f;
-    }
-    __device__ __forceinline__ void put(const Tile&, int64_t, int64_t, float v, float o) { acc = fmaf(v, o, acc); }
-    __device__ __forceinline__ void finish(const Tile&, int tid, bool) {
-        __shared__ double red[GEMM_THREADS / 64];
-        const double d = wave_sum_d((double)acc);
-        if ((tid & 63) == 0) red[tid >> 6] = d;
-        __syncthreads();
-        if (tid == 0) {
-            double s = 0.0;
-            for (int w = 0; w < GEMM_THREADS / 64; ++w) s += red[w];
-            part[blockIdx.x] = s;
-        }
-    }
-};
-
 // mse[k] = sum of the parts in order / denom
 __global__ __launch_bounds__(256) void awq_score_kernel(const double* __restrict__ part, int64_t nparts, double denom,
                                                         double* __restrict__ mse) {
@@ -200,9 +176,9 @@ hipError_t awq_product(const float* dW, const float* H, int64_t m, int64_t n, do
     mp.kchunk = cdiv(n, GEMM_BK) * GEMM_BK;
     mp.tri_k = 0;
     mp.guard = nullptr;
-    EpiDot ep{dW, n, m, n, part, 0.f};
+    EpiTrace ep{dW, n, m, n, part, nullptr, 0.f};
     *nparts = (int64_t)mp.tiles_m * mp.tiles_n;
-    hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, OpMMajor<0>, OpKMajor<0>, RectMap, EpiDot>), dim3((unsigned)*nparts),
+    hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, OpMMajor<0>, OpKMajor<0>, RectMap, EpiTrace>), dim3((unsigned)*nparts),
                        dim3(GEMM_THREADS), 0, s, la, lb, mp, ep);
     return hipGetLastError();
 }

@@ -438,6 +438,37 @@ struct GemmTask {
     }
 };
 
+// Trace epilogue for acc = A B with A = dW (element (row, k) at dW[row * ld + k], M x N):
+// part[workgroup] = sum over its tile of (acc[row][col] - shift * dW[row][col]) * dW[row][col]
+// in float64, so the parts sum to tr(dW (B - shift I) dW^T); shift is a device float
+// (NULL: 0) read by the kernel.
+struct EpiTrace {
+    static constexpr bool kRmw = true;
+    const float* dW;
+    int64_t ld, M, N;
+    double* part;
+    const float* shift;
+    float acc;
+    __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
+        return (row < M && col < N) ? dW[row * ld + col] : 0.f;
+    }
+    __device__ __forceinline__ void put(const Tile&, int64_t, int64_t, float v, float o) {
+        const float lam = shift ? *shift : 0.f;
+        acc = fmaf(fmaf(-lam, o, v), o, acc);
+    }
+    __device__ __forceinline__ void finish(const Tile&, int tid, bool) {
+        __shared__ double red[GEMM_THREADS / 64];
+        const double d = wave_sum_d((double)acc);
+        if ((tid & 63) == 0) red[tid >> 6] = d;
+        __syncthreads();
+        if (tid == 0) {
+            double s = 0.0;
+            for (int w = 0; w < GEMM_THREADS / 64; ++w) s += red[w];
+            part[blockIdx.x] = s;
+        }
+    }
+};
+
 template <class TA, class TB>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_f32_dual_kernel(TA a, TB b, int n1, const int32_t* guard) {
     if (guard && *guard != 0) return;

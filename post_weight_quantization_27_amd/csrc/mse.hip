@@ -21,17 +21,18 @@ namespace pwq {
 
 namespace {
 
-// dW[o][c] = bf16(W[o][c] - s[o][group(c)] * (code[o][c] - z[o][group(c)])), z = 0 for
-// symmetric codes, ld = kseg (a multiple of 64, columns d_in .. kseg-1 zero).  One thread per
-// 8 columns of a row.
-template <int DTW, bool ZP>
+// dW[o][c] = W[o][c] - s[o][group(c)] * (code[o][c] - z[o][group(c)]) (float32: the product
+// is exact, the difference rounded once), z = 0 for symmetric codes, stored as bf16 (rounded
+// once more) or, F32, as float32; ld = kseg (a multiple of 8, columns d_in .. kseg-1 zero).
+// One thread per 8 columns of a row.
+template <int DTW, bool ZP, bool F32 = false>
 __global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict__ Wv, int64_t ldw, int64_t m, int64_t n,
                                                          int64_t kseg, const uint8_t* __restrict__ packed,
                                                          const int8_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint16_t* __restrict__ zeros,
                                                          const int32_t* __restrict__ g_idx, int64_t ng, int g,
-                                                         int vec, uint16_t* __restrict__ dw) {
+                                                         int vec, void* __restrict__ dwv) {
     typedef typename Elem<DTW>::T T;
     const T* W = (const T*)Wv;
     const int64_t per_row = kseg / 8;
@@ -82,8 +83,15 @@ __global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict_
             d[k] = Elem<DTW>::get(W, o * ldw + cc) - f16_bits_to_f32(scales[o * ng + G]) * (float)q;
         }
     }
-    *(uint4*)(dw + o * kseg + c) = make_uint4(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]),
-                                              pack_bf16x2(d[4], d[5]), pack_bf16x2(d[6], d[7]));
+    if (F32) {
+        float* dw = (float*)dwv + o * kseg + c;
+        *(float4*)dw = make_float4(d[0], d[1], d[2], d[3]);
+        *(float4*)(dw + 4) = make_float4(d[4], d[5], d[6], d[7]);
+    } else {
+        uint16_t* dw = (uint16_t*)dwv;
+        *(uint4*)(dw + o * kseg + c) = make_uint4(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]),
+                                                  pack_bf16x2(d[4], d[5]), pack_bf16x2(d[6], d[7]));
+    }
 }
 
 // float32 X (element (t, c) at p[t * ld + c]) rounded once to bfloat16 while staging
@@ -259,6 +267,77 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(256), 0, s, part, nb, (double)n_tok * (double)d_out, mse);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ through the Hessian
+// sum over tokens and outputs of (X dW^T)^2 = tr(dW X^T X dW^T) = tr(dW H dW^T) / 2 with
+// H = 2 X^T X: one d_out x d_in x d_in float32 product instead of n_tok x d_in x d_out, for
+// H already formed (its damping, shift, taken off in the epilogue).
+namespace {
+inline int64_t mse_h_k8(int64_t d_in) { return cdiv(d_in, 8) * 8; }
+inline bool mse_h_big(int64_t d_out, int64_t d_in) { return cdiv(d_out, 128) * cdiv(d_in, 128) >= 512; }
+inline int64_t mse_h_tiles(int64_t d_out, int64_t d_in) {
+    return mse_h_big(d_out, d_in) ? cdiv(d_out, 128) * cdiv(d_in, 128) : cdiv(d_out, 64) * cdiv(d_in, 64);
+}
+
+template <int T>
+hipError_t mse_h_product(const float* dW, int64_t lddw, const float* H, int64_t ldh, int64_t m, int64_t n,
+                         const float* shift, double* part, int64_t* nparts, hipStream_t s) {
+    const int va = (int)((lddw % 4 == 0) && aligned(dW, 16));
+    const int vb = (int)((ldh % 4 == 0) && aligned(H, 16));
+    OpMMajor<0> la{dW, lddw, m, n, va};
+    OpKMajor<0> lb{H, ldh, n, n, vb};
+    RectMap mp{};
+    mp.M = m; mp.N = n; mp.K = n;
+    mp.tiles_m = (int)cdiv(m, T);
+    mp.tiles_n = (int)cdiv(n, T);
+    mp.splits = 1;
+    mp.kchunk = cdiv(n, GEMM_BK) * GEMM_BK;
+    mp.tri_k = 0;
+    mp.guard = nullptr;
+    EpiTrace ep{dW, lddw, m, n, part, shift, 0.f};
+    *nparts = (int64_t)mp.tiles_m * mp.tiles_n;
+    hipLaunchKernelGGL((gemm_f32_kernel<T, T, OpMMajor<0>, OpKMajor<0>, RectMap, EpiTrace>), dim3((unsigned)*nparts),
+                       dim3(GEMM_THREADS), 0, s, la, lb, mp, ep);
+    return hipGetLastError();
+}
+}  // namespace
+
+// workspace: dW (d_out x k8 float32), then one float64 partial per tile
+size_t mse_h_ws_bytes(int64_t d_in, int64_t d_out) {
+    return align_up((size_t)(d_out * mse_h_k8(d_in)) * sizeof(float), 256) +
+           (size_t)mse_h_tiles(d_out, d_in) * sizeof(double);
+}
+
+hipError_t mse_h_launch(const float* H, int64_t ldh, int64_t d_in, int64_t n_tok, const float* shift, const void* W,
+                        int w_dtype, int64_t ldw, const uint8_t* packed, const int8_t* codes, const uint16_t* scales,
+                        const uint16_t* zeros, const int32_t* g_idx, int64_t d_out, int group_size, double* mse,
+                        void* ws, hipStream_t s) {
+    hipError_t e;
+    if (n_tok == 0 || d_out == 0) {
+        hipLaunchKernelGGL(set_double_kernel, dim3(1), dim3(1), 0, s, mse, 0.0);
+        return hipGetLastError();
+    }
+    const int64_t k8 = mse_h_k8(d_in);
+    float* dw = (float*)ws;
+    double* part = (double*)((char*)ws + align_up((size_t)(d_out * k8) * sizeof(float), 256));
+    const int64_t ng = group_size == 0 ? 1 : cdiv(d_in, group_size);
+    const size_t wsz = w_dtype == 0 ? 4 : 2;
+    const int vec = (ldw % 8 == 0) && (d_in % 8 == 0) && aligned(W, 8 * wsz) && !g_idx &&
+                    (group_size == 0 || group_size % 8 == 0) && (!packed || aligned(packed, 4)) &&
+                    (!codes || aligned(codes, 8));
+    const unsigned dgrid = (unsigned)cdiv(d_out * (k8 / 8), 256);
+    auto dec = w_dtype == 0 ? (zeros ? mse_decode_kernel<0, true, true> : mse_decode_kernel<0, false, true>)
+                            : (zeros ? mse_decode_kernel<1, true, true> : mse_decode_kernel<1, false, true>);
+    hipLaunchKernelGGL(dec, dim3(dgrid), dim3(256), 0, s, W, ldw, d_out, d_in, k8, packed, codes, scales, zeros, g_idx,
+                       ng, group_size, vec, (void*)dw);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    int64_t np = 0;
+    e = mse_h_big(d_out, d_in) ? mse_h_product<128>(dw, k8, H, ldh, d_out, d_in, shift, part, &np, s)
+                               : mse_h_product<64>(dw, k8, H, ldh, d_out, d_in, shift, part, &np, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(256), 0, s, part, np, 2.0 * (double)n_tok * (double)d_out, mse);
     return hipGetLastError();
 }
 

@@ -252,6 +252,30 @@ pwq_status pwq_recon_mse_zp(const void* X, int x_dtype, int64_t n_tok, int64_t d
                        d_out, bits, group_size, mse, ws, ws_bytes, stream);
 }
 
+size_t pwq_recon_mse_hessian_workspace_size(int64_t d_in, int64_t d_out) {
+    if (d_in <= 0 || d_out <= 0 || bad_dim(d_in) || bad_dim(d_out)) return 0;
+    return mse_h_ws_bytes(d_in, d_out);
+}
+
+pwq_status pwq_recon_mse_hessian(const float* H, int64_t ldh, int64_t d_in, int64_t n_tok, const float* h_shift,
+                                 const void* W, int w_dtype, int64_t ldw, const uint8_t* packed, const void* codes,
+                                 const uint16_t* scales, const uint16_t* zeros, const int32_t* g_idx, int64_t d_out,
+                                 int32_t bits, int32_t group_size, double* mse, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    if (w_dtype != PWQ_F32 && w_dtype != PWQ_F16) return PWQ_EDTYPE;
+    if (bad_dim(n_tok) || bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldh < d_in || ldw < d_in) return PWQ_EINVAL;
+    if (bits < 2 || bits > 8 || !group_ok(group_size, d_in)) return PWQ_EINVAL;
+    if (packed && (bits != 4 || d_in % 2 != 0)) return PWQ_EINVAL;
+    if (g_idx && group_size == 0) return PWQ_EINVAL;
+    if (!mse) return PWQ_EINVAL;
+    if (n_tok > 0 && d_out > 0) {                // the data pointers only matter when read
+        if (!H || !W || !scales || (packed != nullptr) == (codes != nullptr)) return PWQ_EINVAL;
+        if (!ws || ws_bytes < pwq_recon_mse_hessian_workspace_size(d_in, d_out)) return PWQ_EWORKSPACE;
+    }
+    return hip_status(mse_h_launch(H, ldh, d_in, n_tok, h_shift, W, w_dtype, ldw, packed, (const int8_t*)codes, scales,
+                                   zeros, g_idx, d_out, group_size, mse, ws, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ per-tensor quantizer
 size_t pwq_tensor_scales_workspace_size(void) { return tensor_scales_ws_bytes(); }
 

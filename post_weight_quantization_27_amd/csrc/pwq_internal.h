@@ -81,6 +81,11 @@ hipError_t w4a16_launch(const uint16_t* X, int64_t T, int64_t n, int64_t ldx, co
 
 // Reconstruction MSE.
 size_t mse_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out);
+size_t mse_h_ws_bytes(int64_t d_in, int64_t d_out);
+hipError_t mse_h_launch(const float* H, int64_t ldh, int64_t d_in, int64_t n_tok, const float* shift, const void* W,
+                        int w_dtype, int64_t ldw, const uint8_t* packed, const int8_t* codes, const uint16_t* scales,
+                        const uint16_t* zeros, const int32_t* g_idx, int64_t d_out, int group_size, double* mse,
+                        void* ws, hipStream_t s);
 hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx, const void* W,
                       int w_dtype, int64_t ldw, const uint8_t* packed, const int8_t* codes,
                       const uint16_t* scales, const int32_t* g_idx, int64_t d_out, int bits, int group_size,

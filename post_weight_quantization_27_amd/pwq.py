@@ -70,6 +70,10 @@ _SIGS = {
     "pwq_quantized_matmul_workspace_size": (_sz, [_i64, _i64, _i64]),
     "pwq_quantized_matmul": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                             _i64, _i32, _c_void_p, ctypes.c_int, _i64, _c_void_p, _sz, _c_void_p]),
+    "pwq_recon_mse_hessian_workspace_size": (_sz, [_i64, _i64]),
+    "pwq_recon_mse_hessian": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, ctypes.c_int, _i64,
+                                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
+                                             _c_void_p, _c_void_p, _sz, _c_void_p]),
     "pwq_recon_mse_workspace_size": (_sz, [_i64, _i64, _i64]),
     "pwq_recon_mse": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
@@ -328,6 +332,30 @@ def recon_mse(X: torch.Tensor, W: torch.Tensor, scales: torch.Tensor, bits: int 
         _check("pwq_recon_mse", lib().pwq_recon_mse(
             _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
             _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(X)))
+    return mse
+
+
+def recon_mse_hessian(H: torch.Tensor, n_tok: int, W: torch.Tensor, scales: torch.Tensor, bits: int = 4,
+                      group_size: int = 128, packed: Optional[torch.Tensor] = None,
+                      codes: Optional[torch.Tensor] = None, g_idx: Optional[torch.Tensor] = None,
+                      zeros: Optional[torch.Tensor] = None, shift: Optional[torch.Tensor] = None,
+                      mse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device float64 scalar: the same mean square as recon_mse, through H = 2 X^T X formed over
+    n_tok tokens (pwq_recon_mse_hessian); ``shift`` (device float32, e.g. hessian_damp's
+    lambda_out) is what damping added to H's diagonal."""
+    ldh, ldw = _rows(H, "H"), _rows(W, "W")
+    d_in = H.shape[0]
+    d_out = W.shape[0]
+    if H.dtype != torch.float32 or H.shape != (d_in, d_in) or W.shape[1] != d_in:
+        raise ValueError("H: float32 d_in x d_in matching W's columns")
+    if mse is None:
+        mse = torch.empty(1, dtype=torch.float64, device=W.device)
+    nb = lib().pwq_recon_mse_hessian_workspace_size(d_in, d_out)
+    if ws is None or ws.numel() < nb:
+        ws = _ws(nb, W.device)
+    _check("pwq_recon_mse_hessian", lib().pwq_recon_mse_hessian(
+        _p(H), ldh, d_in, int(n_tok), _p(shift), _p(W), _dtype_code(W), ldw, _p(packed), _p(codes), _p(scales),
+        _p(zeros), _p(g_idx), d_out, bits, group_size, _p(mse), _p(ws), nb, _stream(W)))
     return mse
 
 
