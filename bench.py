@@ -3,7 +3,7 @@
 One step = every step of the path for every layer of the workload, on inputs already
 resident in HBM: Hessian from X, damping, [act-order], H^-1 factor, GPTQ (INT4 packed +
 fp16 scales), RTN, dequant of the GPTQ result, and the reconstruction MSE of both (through
-the tokens, or through H when n_tok >= 16 d_in, where that product is the cheaper one).
+the tokens, or through H when n_tok >= 10 d_in, where that product is the cheaper one).
 The value is weights quantized per second (sum of d_out * d_in over the layers / step).
 
 Prints ONE JSON line.  The value comes from K timed steps with no events between the
@@ -76,13 +76,16 @@ class Layer:
         self.act = act_order
         self.zp = zero_point
         # the reconstruction MSE through H (d_out x d_in^2 float32 MFMA) when that is cheaper
-        # than through the tokens (n_tok x d_in x d_out bfloat16 MFMA, sixteen times the rate)
+        # than through the tokens (n_tok x d_in x d_out bfloat16 MFMA)
         self.mse_h = mse_through_hessian(spec)
         del X, W
 
 
 def mse_through_hessian(spec):
-    return spec.n_tok >= 16 * spec.d_in
+    # float32 MFMA runs at a sixteenth of the bfloat16 rate, but the token route reaches only
+    # part of its peak on small contractions: measured, the Hessian route is the faster one
+    # from n_tok = 10 d_in on (GPT-2's 768-input layers; 70B q, k, v, o, gate, up)
+    return spec.n_tok >= 10 * spec.d_in
 
 
 def run_step(L, pwq, timers=None, after_hessian=None, parts="all"):
