@@ -444,10 +444,11 @@ def gptq_layer(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group_size: int 
     d_in = W.shape[1]
     H = torch.zeros((d_in, d_in), dtype=torch.float32, device=W.device)
     hessian_accumulate(X, H)
-    hessian_damp(H, damp)
+    lam = torch.empty(1, dtype=torch.float32, device=W.device)
+    hessian_damp(H, damp, lambda_out=lam)
     perm = act_order_perm(H) if act_order else None
     U, info = chol_inverse_upper(H, perm)
     q = gptq_quantize_layer if sym else gptq_quantize_layer_zp
     res = q(W, U, info, bits, group_size, block_size, perm=perm, want_codes=want_codes, want_packed=want_packed)
-    res.update({"H": H, "U": U, "info": info, "perm": perm})
+    res.update({"H": H, "lambda": lam, "U": U, "info": info, "perm": perm})
     return res

@@ -536,6 +536,14 @@ def test_workload_layer_end_to_end(pwq, wl, layer):
     mse_r = float(host(pwq.recon_mse(Xd, Wd, r["scales"], spec.bits, spec.group_size, packed=r["packed"]))[0])
     assert abs(mse_r - want["rtn_mse"]) <= 1e-4 * want["rtn_mse"]
     assert abs(mse_g - want["gptq_mse"]) <= 5e-3 * want["gptq_mse"]
+    # the same errors through the damped Hessian, as the benchmark computes them from 10 tokens
+    # per input on
+    hg = float(host(pwq.recon_mse_hessian(res["H"], spec.n_tok, Wd, res["scales"], spec.bits, spec.group_size,
+                                          packed=res["packed"], shift=res["lambda"]))[0])
+    hr = float(host(pwq.recon_mse_hessian(res["H"], spec.n_tok, Wd, r["scales"], spec.bits, spec.group_size,
+                                          packed=r["packed"], shift=res["lambda"]))[0])
+    assert abs(hr - want["rtn_mse"]) <= 1e-4 * want["rtn_mse"]
+    assert abs(hg - mse_g) <= 1e-4 * mse_g
     print(f"{layer}: agreement {agree:.6f} mse rtn {mse_r:.5g} gptq {mse_g:.5g} (oracle {want['gptq_mse']:.5g})")
 
 
