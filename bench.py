@@ -75,16 +75,26 @@ class Layer:
         self.lam = torch.zeros(1, dtype=torch.float32, device=dev)     # what damping adds to diag H
         self.act = act_order
         self.zp = zero_point
-        # the reconstruction MSE through H (d_out x d_in^2 float32 MFMA) when that is cheaper
-        # than through the tokens (n_tok x d_in x d_out bfloat16 MFMA)
+        # the reconstruction MSE through H (d_out x d_in^2) when that is cheaper than through
+        # the tokens (n_tok x d_in x d_out bfloat16 MFMA)
         self.mse_h = mse_through_hessian(spec)
         del X, W
 
 
+def mse_split_route(spec):
+    # layers of at least 256 output tiles of 256 x 256: the library forms tr(dW H dW^T) as a
+    # bfloat16 hi/lo split product over one triangle of H, about 3 d_out d_in^2 bfloat16 flops
+    return -(-spec.d_out // 256) * -(-spec.d_in // 256) >= 256
+
+
 def mse_through_hessian(spec):
-    # float32 MFMA runs at a sixteenth of the bfloat16 rate, but the token route reaches only
-    # part of its peak on small contractions: measured, the Hessian route is the faster one
-    # from n_tok = 10 d_in on (GPT-2's 768-input layers; 70B q, k, v, o, gate, up)
+    # split route: cheaper than the token route (2 n_tok d_in d_out bfloat16 flops) from
+    # n_tok >= 1.5 (d_in + 256) on; taken from n_tok >= 2 d_in (70B q, k, v, o, gate, up, down).
+    # Smaller layers form it on float32 MFMA, a sixteenth of the bfloat16 rate, but the token
+    # route reaches only part of its peak on small contractions: measured, the float32 route
+    # is the faster one from n_tok = 10 d_in on (GPT-2's 768-input layers)
+    if mse_split_route(spec):
+        return spec.n_tok >= 2 * spec.d_in
     return spec.n_tok >= 10 * spec.d_in
 
 
@@ -176,8 +186,8 @@ def work_of(name, spec, zero_point=False):
     if name == "gptq_quantize_layer":           # trailing products + in-block rank-1 updates
         return "mfma_f32", m * n * (n - spec.block_size) + m * n * (spec.block_size - 1), "flop"
     if name == "recon_mse":                     # two calls (GPTQ and RTN)
-        if mse_through_hessian(spec):           # 2 m n^2 each, float32 MFMA
-            return "mfma_f32", 2 * (2 * m * n * n), "flop"
+        if mse_through_hessian(spec):           # 2 m n^2 each (dW H), bfloat16 split or float32 MFMA
+            return ("mfma_bf16" if mse_split_route(spec) else "mfma_f32"), 2 * (2 * m * n * n), "flop"
         return "mfma_bf16", 2 * (2 * N * n * m), "flop"     # 2 N n m each, bf16 MFMA
     if name == "rtn_quantize":
         return "hbm", m * n * wb + m * n // 2 + pg * m * ng, "byte"
@@ -193,8 +203,8 @@ def launches_of(name, spec):
         return 2 + (2 if spec.d_in < 4096 else 3) * nb
     if name == "gptq_quantize_layer":
         return 1 + 2 * nb
-    if name == "recon_mse":
-        return 6
+    if name == "recon_mse":                     # decode, (split H,) product, final sum; two calls
+        return 8 if mse_through_hessian(spec) and mse_split_route(spec) else 6
     return None
 
 

@@ -73,6 +73,19 @@ struct DlRows {
     }
 };
 
+// one 256 x 32 tile-major block (16 KiB in one piece) into the stage tile S, swizzled: wave
+// w issues the four 16-row groups g = w + 4 q, lane i carrying row i / 4 and the chunk that
+// lands at position i % 4
+__device__ __forceinline__ void dl_load_block(const uint16_t* blk, uint16_t* S, int wave, int lane) {
+    const int pc = lane & 3, rl = lane >> 2;
+    const int lc = pc ^ ((rl >> 2) & 3);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r0 = 16 * (wave + 4 * q);
+        dl_load16(blk + (r0 + rl) * DL_BK + 8 * lc, S + r0 * DL_BK);
+    }
+}
+
 // Rows stored tile-major: the k-tile kt (32 k) of the 256-row panel P is one contiguous
 // 256 x 32 block, element (r, k) of a segment at ((r / 256) kpan + k / 32) 8192 +
 // (r % 256) 32 + k % 32, kpan = kseg / 32.  A tile's load then reads 16 KiB in one piece
@@ -91,14 +104,20 @@ struct DlTiled {
             base = seg[sg];
             kk = k0 - (int64_t)sg * kseg;
         }
-        const uint16_t* blk = base + ((m0 >> 8) * (kseg >> 5) + (kk >> 5)) * (int64_t)(DL_TILE * DL_BK);
-        const int pc = lane & 3, rl = lane >> 2;
-        const int lc = pc ^ ((rl >> 2) & 3);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r0 = 16 * (wave + 4 * q);
-            dl_load16(blk + (r0 + rl) * DL_BK + 8 * lc, S + r0 * DL_BK);
-        }
+        dl_load_block(base + ((m0 >> 8) * (kseg >> 5) + (kk >> 5)) * (int64_t)(DL_TILE * DL_BK), S, wave, lane);
+    }
+};
+
+// Rows of a lower-triangular operand stored as whole tile-major panels of growing length:
+// panel p (rows 256 p .. 256 p + 255) holds its k-tiles 0 .. KT (p + 1) - 1 of 32 k each,
+// panel after panel (panel p starts at k-tile KT p (p + 1) / 2).  Tiles of panel p only read
+// k below 32 KT (p + 1).
+struct DlTri {
+    const uint16_t* p;
+    int kt;                                             // KT: k-tiles per 256 columns of the band
+    __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
+        const int64_t pan = m0 >> 8;
+        dl_load_block(p + ((int64_t)kt * (pan * (pan + 1) / 2) + (k0 >> 5)) * (int64_t)(DL_TILE * DL_BK), S, wave, lane);
     }
 };
 // element (r, k) of one segment in the tile-major layout

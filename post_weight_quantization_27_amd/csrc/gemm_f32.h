@@ -206,12 +206,14 @@ __device__ __forceinline__ void upper_band_tile(int L, int tiles, int G, int& ti
 // [0, full) over the whole k range (t.split = -1); the tiles after them are split into
 // `splits` k chunks of kchunk, workgroup full + s * (ntile - full) + j taking chunk s of tile
 // full + j.  With full = 0 every tile is split.
-// xcd (only with full == ntile, nothing split, or full == 0, everything split): the work
-// items are (chunk, tile) with the tiles in bands of four rows (upper_band_tile), chunk
-// slowest; workgroup b runs on XCD b % 8, which takes a contiguous run of them, so the
-// workgroups in flight on one XCD share a few operand blocks (and one k range) in its L2.
-// t.tile stays the tile's index in the plain order.  The grid is padded to a multiple of 8;
-// the padding workgroups have no tile.
+// xcd: tiles taken in bands of four rows (upper_band_tile); t.tile is then the tile's position
+// L in that order (the whole tiles are L < full, the split ones full <= L < ntile).  Workgroup
+// b runs on XCD b % 8 and takes the b / 8-th item of that XCD's list: first its share of the
+// whole tiles (a contiguous run of ceil(full / 8)), then its share of the split items (chunk
+// slowest, a contiguous run of ceil((ntile - full) splits / 8)).  Every XCD then has the same
+// work, and the workgroups in flight on one XCD share a few operand blocks (and one k range)
+// in its L2.  The grid is 8 (ceil(full / 8) + ceil((ntile - full) splits / 8)); padding
+// workgroups have no tile.
 struct UpperMap {
     int64_t N, K;
     int tiles, splits;
@@ -223,19 +225,26 @@ struct UpperMap {
         const int ntile = tiles * (tiles + 1) / 2;
         int ti = 0, tj = 0;
         if (xcd) {
-            const bool whole = full == ntile;
-            const int nwork = whole ? ntile : ntile * splits;
-            const int per = (nwork + 7) / 8;
-            const int L = (bid % 8) * per + bid / 8;
-            if (L >= nwork) {
+            const int ntail = ntile - full, nsplit = ntail > 0 ? ntail * splits : 0;
+            const int wpx = (full + 7) / 8, x = bid % 8, p = bid / 8;
+            int L;
+            if (p < wpx) {
+                L = x * wpx + p;
+                t.split = -1;
+                if (L >= full) L = -1;
+            } else {
+                const int j = x * ((nsplit + 7) / 8) + (p - wpx);
+                t.split = j / (ntail > 0 ? ntail : 1);
+                L = j < nsplit ? full + j % ntail : -1;
+            }
+            if (L < 0) {
                 t.split = -1;
                 t.tile = 0;
                 t.kbeg = t.kend = 0;
                 return false;
             }
-            t.split = whole ? -1 : L / ntile;
-            upper_band_tile(L % ntile, tiles, 4, ti, tj);
-            t.tile = ti * tiles - ti * (ti - 1) / 2 + (tj - ti);
+            upper_band_tile(L, tiles, 4, ti, tj);
+            t.tile = L;
         } else {
             if (bid < full) {
                 t.split = -1;

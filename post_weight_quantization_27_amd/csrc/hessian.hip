@@ -39,15 +39,21 @@ struct EpiHess {
     __device__ __forceinline__ void finish(const Tile&, int, bool) {}
 };
 
-// H[tile] += 2 * sum_s part[s][tile - full] over the split tiles, s in increasing order.
+// H[tile] += 2 * sum_s part[s][tile - full] over the split tiles, s in increasing order;
+// tile numbers in the plain order, or (band) in the band order of upper_band_tile.
 // grid: x = 1024-element chunk of a tile, y = split tile index (tile - full)
 __global__ __launch_bounds__(256) void hess_reduce_kernel(const float* __restrict__ part, float* __restrict__ H,
-                                                          int64_t n, int tiles, int full, int splits, int bm) {
+                                                          int64_t n, int tiles, int full, int splits, int bm, int band) {
     const int ntail = tiles * (tiles + 1) / 2 - full;
     const int tile = full + (int)blockIdx.y;
-    int r = tile, ti = 0;
-    while (r >= tiles - ti) { r -= tiles - ti; ++ti; }
-    const int tj = ti + r;
+    int ti = 0, tj = 0;
+    if (band) {
+        upper_band_tile(tile, tiles, 4, ti, tj);
+    } else {
+        int r = tile;
+        while (r >= tiles - ti) { r -= tiles - ti; ++ti; }
+        tj = ti + r;
+    }
     const int64_t per_tile = (int64_t)bm * bm;
     const int64_t le = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
     if (le >= per_tile) return;
@@ -221,6 +227,12 @@ __global__ __launch_bounds__(256) void transpose_split_f32_kernel(const float* _
     }
 }
 
+// workgroups of the direct-load Hessian in the per-XCD order of UpperMap (xcd set)
+int hess_dl_grid(const HessPlan& pl, int ntile) {
+    const int nsplit = pl.full < ntile ? (ntile - pl.full) * pl.splits : 0;
+    return 8 * ((pl.full + 7) / 8 + (nsplit + 7) / 8);
+}
+
 // bfloat16 X on the direct-load engine: both operands are rows of the transposed copy
 // (stored tile-major, zero past n_tok and past n), 256 x 256 upper tiles
 hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, uint16_t* XT, float* part,
@@ -232,12 +244,10 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
     if (e != hipSuccess) return e;
     DlTiled op{{XT, nullptr, nullptr, nullptr}, 1, pl.npad};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
-    // nothing or everything split: work items in L2-friendly bands per XCD
-    const int xcd = pl.full == ntile || pl.full == 0;
-    UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, xcd};
+    // work items in L2-friendly bands, an equal share per XCD
+    UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, 1};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
-    const int nwork = pl.full == ntile ? ntile : pl.full + (ntile - pl.full) * pl.splits;
-    const int nwg = xcd ? (nwork + 7) / 8 * 8 : nwork;
+    const int nwg = hess_dl_grid(pl, ntile);
     hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
     return hipGetLastError();
@@ -257,12 +267,10 @@ hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, f
     DlTiled a{{XH, XH, XL, XL}, 4, pl.npad};
     DlTiled b{{XH, XL, XH, XL}, 4, pl.npad};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
-    // nothing or everything split: work items in L2-friendly bands per XCD
-    const int xcd = pl.full == ntile || pl.full == 0;
-    UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, xcd};
+    // work items in L2-friendly bands, an equal share per XCD
+    UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, 1};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
-    const int nwork = pl.full == ntile ? ntile : pl.full + (ntile - pl.full) * pl.splits;
-    const int nwg = xcd ? (nwork + 7) / 8 * 8 : nwork;
+    const int nwg = hess_dl_grid(pl, ntile);
     hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, a, b, map, epi);
     return hipGetLastError();
@@ -357,7 +365,7 @@ hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_i
         const int ntail = pl.tiles * (pl.tiles + 1) / 2 - pl.full;
         const unsigned chunks = (unsigned)cdiv((int64_t)pl.bm * pl.bm, 1024);
         hipLaunchKernelGGL(hess_reduce_kernel, dim3(chunks, (unsigned)ntail), dim3(256), 0, s, part, H, d_in, pl.tiles,
-                           pl.full, pl.splits, pl.bm);
+                           pl.full, pl.splits, pl.bm, pl.dl ? 1 : 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int64_t nb = cdiv(d_in, 32);

@@ -25,21 +25,14 @@ namespace {
 // is exact, the difference rounded once), z = 0 for symmetric codes, stored as bf16 (rounded
 // once more) or, F32, as float32; ld = kseg (a multiple of 8, columns d_in .. kseg-1 zero).
 // One thread per 8 columns of a row.
-template <int DTW, bool ZP, bool F32 = false>
-__global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict__ Wv, int64_t ldw, int64_t m, int64_t n,
-                                                         int64_t kseg, const uint8_t* __restrict__ packed,
-                                                         const int8_t* __restrict__ codes,
-                                                         const uint16_t* __restrict__ scales,
-                                                         const uint16_t* __restrict__ zeros,
-                                                         const int32_t* __restrict__ g_idx, int64_t ng, int g,
-                                                         int vec, void* __restrict__ dwv) {
+template <int DTW, bool ZP>
+__device__ __forceinline__ void dw8(const void* __restrict__ Wv, int64_t ldw, int64_t n,
+                                    const uint8_t* __restrict__ packed, const int8_t* __restrict__ codes,
+                                    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
+                                    const int32_t* __restrict__ g_idx, int64_t ng, int g, int vec, int64_t o, int64_t c,
+                                    float (&d)[8]) {
     typedef typename Elem<DTW>::T T;
     const T* W = (const T*)Wv;
-    const int64_t per_row = kseg / 8;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= m * per_row) return;
-    const int64_t o = idx / per_row, c = (idx - o * per_row) * 8;
-    float d[8];
     if (vec && c + 8 <= n) {
         const float4 w0 = Elem<DTW>::get4(W, o * ldw + c), w1 = Elem<DTW>::get4(W, o * ldw + c + 4);
         const int64_t gi = o * ng + (g == 0 ? 0 : c / g);
@@ -83,6 +76,22 @@ __global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict_
             d[k] = Elem<DTW>::get(W, o * ldw + cc) - f16_bits_to_f32(scales[o * ng + G]) * (float)q;
         }
     }
+}
+
+template <int DTW, bool ZP, bool F32 = false>
+__global__ __launch_bounds__(256) void mse_decode_kernel(const void* __restrict__ Wv, int64_t ldw, int64_t m, int64_t n,
+                                                         int64_t kseg, const uint8_t* __restrict__ packed,
+                                                         const int8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint16_t* __restrict__ zeros,
+                                                         const int32_t* __restrict__ g_idx, int64_t ng, int g,
+                                                         int vec, void* __restrict__ dwv) {
+    const int64_t per_row = kseg / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= m * per_row) return;
+    const int64_t o = idx / per_row, c = (idx - o * per_row) * 8;
+    float d[8];
+    dw8<DTW, ZP>(Wv, ldw, n, packed, codes, scales, zeros, g_idx, ng, g, vec, o, c, d);
     if (F32) {
         float* dw = (float*)dwv + o * kseg + c;
         *(float4*)dw = make_float4(d[0], d[1], d[2], d[3]);
@@ -272,13 +281,149 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
 
 // ------------------------------------------------------------------ through the Hessian
 // sum over tokens and outputs of (X dW^T)^2 = tr(dW X^T X dW^T) = tr(dW H dW^T) / 2 with
-// H = 2 X^T X: one d_out x d_in x d_in float32 product instead of n_tok x d_in x d_out, for
-// H already formed (its damping, shift, taken off in the epilogue).
+// H = 2 X^T X: one d_out x d_in x d_in product instead of n_tok x d_in x d_out, for H already
+// formed (its damping, shift, taken off in the epilogue).
+//
+// Small layers: the float32 engine over the whole of H.  Layers of at least 256 output tiles
+// of 256 x 256: H symmetric gives tr(dW H dW^T) = sum_i sum_c dW[i][c] (dW G)[i][c] with
+// G = diag(H) + 2 (strict upper part of H), so output column block cb only contracts over
+// the column blocks 0 .. cb (half the products).  That product runs on the bfloat16
+// direct-load engine as a three-term split: a = a_hi + a_lo (each bfloat16, a_hi = bf16(a),
+// a_lo = bf16(a - a_hi), so |a - a_hi - a_lo| <= 2^-18 |a|), and
+// a b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi, each product exact in float32, the dropped terms
+// (a_lo b_lo and the residuals) below 2^-16 |a b| and of either sign.  The three pieces are
+// interleaved per 256-column block jb along k (k = 768 jb + 256 s + offset, pieces s = 0, 1,
+// 2 of dW = hi, hi, lo and of G = hi, lo, hi), so a tile's k range is the prefix
+// k < 768 (cb + 1).  G is stored as the lower-triangular B(c, j) = G[j][c] (row c of H, j <= c).
 namespace {
 inline int64_t mse_h_k8(int64_t d_in) { return cdiv(d_in, 8) * 8; }
 inline bool mse_h_big(int64_t d_out, int64_t d_in) { return cdiv(d_out, 128) * cdiv(d_in, 128) >= 512; }
 inline int64_t mse_h_tiles(int64_t d_out, int64_t d_in) {
     return mse_h_big(d_out, d_in) ? cdiv(d_out, 128) * cdiv(d_in, 128) : cdiv(d_out, 64) * cdiv(d_in, 64);
+}
+inline bool mse_h_split(int64_t d_out, int64_t d_in) { return cdiv(d_out, DL_TILE) * cdiv(d_in, DL_TILE) >= 256; }
+
+constexpr int SPLIT_KT = 3 * DL_TILE / DL_BK;            // k-tiles per 256-column block (three pieces)
+
+__device__ __forceinline__ void bf16_hi_lo(float v, uint16_t& hi, uint16_t& lo) {
+    hi = f32_to_bf16_bits(v);
+    lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+}
+
+// dW in float32 (row-major, ld k8, for the epilogue) and as the pieces hi, hi, lo, tile-major
+// over 256-row panels with k per row 3 npad; rows past m and columns past n are zero.
+// One thread per 8 columns of a row (npad a multiple of 256, so 8 columns share a block).
+template <int DTW, bool ZP>
+__global__ __launch_bounds__(256) void mse_decode3_kernel(const void* __restrict__ Wv, int64_t ldw, int64_t m, int64_t n,
+                                                          int64_t mpad, int64_t npad, int64_t k8,
+                                                          const uint8_t* __restrict__ packed,
+                                                          const int8_t* __restrict__ codes,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint16_t* __restrict__ zeros,
+                                                          const int32_t* __restrict__ g_idx, int64_t ng, int g, int vec,
+                                                          float* __restrict__ dw, uint16_t* __restrict__ a3) {
+    const int64_t per_row = npad / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= mpad * per_row) return;
+    const int64_t o = idx / per_row, c = (idx - o * per_row) * 8;
+    float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (o < m && c < n) dw8<DTW, ZP>(Wv, ldw, n, packed, codes, scales, zeros, g_idx, ng, g, vec, o, c, d);
+    if (o < m && c < k8) {
+        float* p = dw + o * k8 + c;
+        *(float4*)p = make_float4(d[0], d[1], d[2], d[3]);
+        *(float4*)(p + 4) = make_float4(d[4], d[5], d[6], d[7]);
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint16_t h0, l0, h1, l1;
+        bf16_hi_lo(d[2 * k], h0, l0);
+        bf16_hi_lo(d[2 * k + 1], h1, l1);
+        hw[k] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lw[k] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    const int64_t kl = 3 * npad, k0 = (c >> 8) * (3 * DL_TILE) + (c & (DL_TILE - 1));
+    *(uint4*)(a3 + dl_tiled_index(o, k0, kl)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *(uint4*)(a3 + dl_tiled_index(o, k0 + DL_TILE, kl)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *(uint4*)(a3 + dl_tiled_index(o, k0 + 2 * DL_TILE, kl)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+}
+
+// B(c, j) = G[j][c] = 2 H[c][j] (j < c), H[c][c] (j = c), 0 (j > c, or past n), as the
+// pieces hi, lo, hi in the triangular tile-major layout (panel p = c / 256 holds k-tiles
+// 0 .. SPLIT_KT (p + 1) - 1).  One thread per 8 columns j; blocks past the diagonal block are
+// not stored.
+__global__ __launch_bounds__(256) void mse_gsplit_kernel(const float* __restrict__ H, int64_t ldh, int64_t n, int64_t npad,
+                                                         int vec, uint16_t* __restrict__ b3) {
+    const int64_t per_row = npad / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= npad * per_row) return;
+    const int64_t c = idx / per_row, j = (idx - c * per_row) * 8;
+    const int64_t pan = c >> 8;
+    if ((j >> 8) > pan) return;
+    float h[8];
+    if (vec && c < n && j + 8 <= n) {
+        const float4 h0 = *(const float4*)(H + c * ldh + j), h1 = *(const float4*)(H + c * ldh + j + 4);
+        h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w; h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) h[k] = (c < n && j + k < n) ? H[c * ldh + j + k] : 0.f;
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint16_t hb[2], lb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t jj = j + 2 * k + u;
+            const float gv = jj < c ? 2.f * h[2 * k + u] : (jj == c ? h[2 * k + u] : 0.f);
+            bf16_hi_lo(gv, hb[u], lb[u]);
+        }
+        hw[k] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+        lw[k] = (uint32_t)lb[0] | ((uint32_t)lb[1] << 16);
+    }
+    const int64_t k0 = (j >> 8) * (3 * DL_TILE) + (j & (DL_TILE - 1));
+    uint16_t* base = b3 + (int64_t)SPLIT_KT * (pan * (pan + 1) / 2) * (DL_TILE * DL_BK) + (c & (DL_TILE - 1)) * DL_BK;
+    const int64_t ks[3] = {k0, k0 + DL_TILE, k0 + 2 * DL_TILE};
+    const uint4 v[3] = {make_uint4(hw[0], hw[1], hw[2], hw[3]), make_uint4(lw[0], lw[1], lw[2], lw[3]),
+                        make_uint4(hw[0], hw[1], hw[2], hw[3])};
+#pragma unroll
+    for (int s = 0; s < 3; ++s) *(uint4*)(base + (ks[s] >> 5) * (DL_TILE * DL_BK) + (ks[s] & 31)) = v[s];
+}
+
+// Output tiles (ib, cb) of dW G, the longest k ranges first: column blocks from the last,
+// row blocks fastest (a workgroup b runs on XCD b % 8, which then holds a few row blocks of
+// dW and the column blocks in flight).  Tile (ib, cb) contracts k < 768 (cb + 1).
+struct SplitTriMap {
+    int tiles_m, tiles_n;
+    const int32_t* guard;
+    __device__ __forceinline__ bool get(int bid, int BM, int BN, Tile& t) const {
+        const int ib = bid % tiles_m, cb = tiles_n - 1 - bid / tiles_m;
+        t.m0 = (int64_t)ib * BM;
+        t.n0 = (int64_t)cb * BN;
+        t.kbeg = 0;
+        t.kend = (int64_t)SPLIT_KT * DL_BK * (cb + 1);
+        t.split = -1;
+        t.tile = bid;
+        return true;
+    }
+};
+
+struct SplitWs {
+    int64_t mpad, npad;
+    size_t dw_bytes, a3_bytes, b3_bytes;
+    int64_t tiles;
+};
+
+SplitWs split_ws(int64_t d_out, int64_t d_in) {
+    SplitWs w{};
+    w.mpad = cdiv(d_out, DL_TILE) * DL_TILE;
+    w.npad = cdiv(d_in, DL_TILE) * DL_TILE;
+    const int64_t nb = w.npad / DL_TILE;
+    w.dw_bytes = align_up((size_t)(d_out * mse_h_k8(d_in)) * sizeof(float), 256);
+    w.a3_bytes = align_up((size_t)(w.mpad * 3 * w.npad) * sizeof(uint16_t), 256);
+    w.b3_bytes = align_up((size_t)SPLIT_KT * (size_t)(nb * (nb + 1) / 2) * DL_TILE * DL_BK * sizeof(uint16_t), 256);
+    w.tiles = (w.mpad / DL_TILE) * nb;
+    return w;
 }
 
 template <int T>
@@ -304,8 +449,13 @@ hipError_t mse_h_product(const float* dW, int64_t lddw, const float* H, int64_t 
 }
 }  // namespace
 
-// workspace: dW (d_out x k8 float32), then one float64 partial per tile
+// workspace: float32 route: dW (d_out x k8 float32), then one float64 partial per tile;
+// split route: dW float32, dW's pieces, G's pieces, then one float64 partial per tile
 size_t mse_h_ws_bytes(int64_t d_in, int64_t d_out) {
+    if (mse_h_split(d_out, d_in)) {
+        const SplitWs w = split_ws(d_out, d_in);
+        return w.dw_bytes + w.a3_bytes + w.b3_bytes + (size_t)w.tiles * sizeof(double);
+    }
     return align_up((size_t)(d_out * mse_h_k8(d_in)) * sizeof(float), 256) +
            (size_t)mse_h_tiles(d_out, d_in) * sizeof(double);
 }
@@ -321,22 +471,47 @@ hipError_t mse_h_launch(const float* H, int64_t ldh, int64_t d_in, int64_t n_tok
     }
     const int64_t k8 = mse_h_k8(d_in);
     float* dw = (float*)ws;
-    double* part = (double*)((char*)ws + align_up((size_t)(d_out * k8) * sizeof(float), 256));
     const int64_t ng = group_size == 0 ? 1 : cdiv(d_in, group_size);
     const size_t wsz = w_dtype == 0 ? 4 : 2;
     const int vec = (ldw % 8 == 0) && (d_in % 8 == 0) && aligned(W, 8 * wsz) && !g_idx &&
                     (group_size == 0 || group_size % 8 == 0) && (!packed || aligned(packed, 4)) &&
                     (!codes || aligned(codes, 8));
-    const unsigned dgrid = (unsigned)cdiv(d_out * (k8 / 8), 256);
-    auto dec = w_dtype == 0 ? (zeros ? mse_decode_kernel<0, true, true> : mse_decode_kernel<0, false, true>)
-                            : (zeros ? mse_decode_kernel<1, true, true> : mse_decode_kernel<1, false, true>);
-    hipLaunchKernelGGL(dec, dim3(dgrid), dim3(256), 0, s, W, ldw, d_out, d_in, k8, packed, codes, scales, zeros, g_idx,
-                       ng, group_size, vec, (void*)dw);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     int64_t np = 0;
-    e = mse_h_big(d_out, d_in) ? mse_h_product<128>(dw, k8, H, ldh, d_out, d_in, shift, part, &np, s)
-                               : mse_h_product<64>(dw, k8, H, ldh, d_out, d_in, shift, part, &np, s);
-    if (e != hipSuccess) return e;
+    double* part;
+    if (mse_h_split(d_out, d_in)) {
+        const SplitWs w = split_ws(d_out, d_in);
+        uint16_t* a3 = (uint16_t*)((char*)ws + w.dw_bytes);
+        uint16_t* b3 = (uint16_t*)((char*)a3 + w.a3_bytes);
+        part = (double*)((char*)b3 + w.b3_bytes);
+        auto dec = w_dtype == 0 ? (zeros ? mse_decode3_kernel<0, true> : mse_decode3_kernel<0, false>)
+                                : (zeros ? mse_decode3_kernel<1, true> : mse_decode3_kernel<1, false>);
+        hipLaunchKernelGGL(dec, dim3((unsigned)cdiv(w.mpad * (w.npad / 8), 256)), dim3(256), 0, s, W, ldw, d_out, d_in,
+                           w.mpad, w.npad, k8, packed, codes, scales, zeros, g_idx, ng, group_size, vec, dw, a3);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int hvec = (ldh % 4 == 0) && aligned(H, 16);
+        hipLaunchKernelGGL(mse_gsplit_kernel, dim3((unsigned)cdiv(w.npad * (w.npad / 8), 256)), dim3(256), 0, s, H, ldh,
+                           d_in, w.npad, hvec, b3);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        DlTiled a{{a3, nullptr, nullptr, nullptr}, 1, 3 * w.npad};
+        DlTri b{b3, SPLIT_KT};
+        SplitTriMap mp{(int)(w.mpad / DL_TILE), (int)(w.npad / DL_TILE), nullptr};
+        EpiTrace ep{dw, k8, d_out, d_in, part, shift, 0.f};
+        np = w.tiles;
+        hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTri, SplitTriMap, EpiTrace>), dim3((unsigned)np),
+                           dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        part = (double*)((char*)ws + align_up((size_t)(d_out * k8) * sizeof(float), 256));
+        const unsigned dgrid = (unsigned)cdiv(d_out * (k8 / 8), 256);
+        auto dec = w_dtype == 0 ? (zeros ? mse_decode_kernel<0, true, true> : mse_decode_kernel<0, false, true>)
+                                : (zeros ? mse_decode_kernel<1, true, true> : mse_decode_kernel<1, false, true>);
+        hipLaunchKernelGGL(dec, dim3(dgrid), dim3(256), 0, s, W, ldw, d_out, d_in, k8, packed, codes, scales, zeros,
+                           g_idx, ng, group_size, vec, (void*)dw);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = mse_h_big(d_out, d_in) ? mse_h_product<128>(dw, k8, H, ldh, d_out, d_in, shift, part, &np, s)
+                                   : mse_h_product<64>(dw, k8, H, ldh, d_out, d_in, shift, part, &np, s);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(256), 0, s, part, np, 2.0 * (double)n_tok * (double)d_out, mse);
     return hipGetLastError();
 }

@@ -113,3 +113,35 @@ def test_mse_hessian_empty_and_strided(pwq):
     assert float(host(z)[0]) == 0.0
     z = pwq.recon_mse_hessian(H, n_tok, dev(W)[:0], dev(r["scales"])[:0], 4, g, codes=dev(r["codes"])[:0])
     assert float(host(z)[0]) == 0.0
+
+
+@pytest.mark.parametrize("m,n,g,sym,wdt,corr", [(4100, 4200, 128, True, np.float16, 0.5),     # ragged panels
+                                                (8192, 2048, 128, False, np.float32, 0.9),
+                                                (2048, 8192, 0, True, np.float32, 0.0),
+                                                (1000, 16500, 64, False, np.float16, 0.9)])   # ragged, 4 x 65 tiles
+def test_mse_hessian_split_route(pwq, m, n, g, sym, wdt, corr):
+    """Layers of at least 256 output tiles of 256 x 256 take the bfloat16 hi/lo split product
+    over one triangle of H (each output column block contracting only up to its diagonal
+    block).  H is formed on the host from bfloat16 X (float64 sum, rounded once to float32) and
+    damped; the expected value is the oracle's X-based mean square."""
+    rng = np.random.default_rng(m + n)
+    n_tok = 1024
+    Z = rng.standard_normal((n_tok, n))
+    if corr:
+        Z = np.sqrt(1 - corr) * Z + np.sqrt(corr) * rng.standard_normal((n_tok, 1))
+    Z *= np.where(rng.random(n) < 0.02, 20.0, 1.0)
+    X64 = synth.as_f64(synth.f64_to_bf16_bits(Z), synth.BF16)
+    H64 = 2.0 * (X64.T @ X64)
+    lam = np.float32(0.01 * np.mean(np.diag(H64)))
+    H32 = H64.astype(np.float32)
+    H32[np.diag_indices(n)] += lam
+    W = rand_w(rng, m, n, wdt)
+    r = O.rtn(W, 4, g, sym=sym)
+    want = O.recon_mse(X64, W, r["What"])
+    kw = {"packed": dev(O.pack_int4(r["codes"]) if sym else O.pack_uint4(r["codes"]))}
+    if not sym:
+        kw["zeros"] = dev(r["zeros"].view(np.int16))
+    shift = torch.tensor([lam], dtype=torch.float32, device=DEV)
+    got = float(host(pwq.recon_mse_hessian(dev(H32), n_tok, dev(W), dev(r["scales"]), 4, g, shift=shift, **kw))[0])
+    print(f"{m}x{n}: relative error {abs(got - want) / want:.2e}")
+    assert abs(got - want) <= 1e-4 * want
