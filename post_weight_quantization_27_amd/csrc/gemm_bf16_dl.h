@@ -43,6 +43,17 @@ __device__ __forceinline__ void dl_load16(const uint16_t* g, uint16_t* lds_wave_
 // element offset of row r's logical 16-byte chunk c in a 256 x 32 stage tile
 __device__ __forceinline__ int dl_off(int r, int c) { return r * DL_BK + 8 * (c ^ ((r >> 2) & 3)); }
 
+// The segment holding logical k (updated to the offset inside it).  Static indices and
+// compares only: a dynamic index into the kernel-argument array would load it from memory
+// on every tile, and the wait for that scalar load also waits for the LDS reads in flight.
+__device__ __forceinline__ const uint16_t* dl_segment(const uint16_t* const (&seg)[4], int nseg, int64_t kseg,
+                                                      int64_t& k) {
+    if (nseg == 1) return seg[0];
+    const int sg = (int)(k >= kseg) + (int)(k >= 2 * kseg) + (int)(k >= 3 * kseg);
+    k -= (int64_t)sg * kseg;
+    return sg == 0 ? seg[0] : (sg == 1 ? seg[1] : (sg == 2 ? seg[2] : seg[3]));
+}
+
 // Rows of bfloat16 over up to four k segments of kseg each (a multiple of 64): logical k in
 // [s kseg, (s+1) kseg) reads seg[s] at k - s kseg.  One segment: kseg is unused.
 struct DlRows {
@@ -52,13 +63,8 @@ struct DlRows {
     // 256 rows x 32 k of logical k0 into the stage tile S (256 x 32, swizzled): wave w issues
     // the four 16-row groups g = w + 4 q
     __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
-        const uint16_t* base = seg[0];
         int64_t kk = k0;
-        if (nseg > 1) {
-            const int sg = (int)(k0 / kseg);
-            base = seg[sg];
-            kk = k0 - (int64_t)sg * kseg;
-        }
+        const uint16_t* base = dl_segment(seg, nseg, kseg, kk);
         const int pc = lane & 3, rl = lane >> 2;           // position in the row, row in the group
         const int lc = pc ^ ((rl >> 2) & 3);               // logical chunk landing at pc
         int64_t kc = kk + 8 * lc;
@@ -97,13 +103,8 @@ struct DlTiled {
     int nseg;
     int64_t kseg;
     __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
-        const uint16_t* base = seg[0];
         int64_t kk = k0;
-        if (nseg > 1) {
-            const int sg = (int)(k0 / kseg);
-            base = seg[sg];
-            kk = k0 - (int64_t)sg * kseg;
-        }
+        const uint16_t* base = dl_segment(seg, nseg, kseg, kk);
         dl_load_block(base + ((m0 >> 8) * (kseg >> 5) + (kk >> 5)) * (int64_t)(DL_TILE * DL_BK), S, wave, lane);
     }
 };
@@ -140,6 +141,18 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// Issue order of one half tile: MFMA, fragment read, eight times, then the last eight MFMAs.
+// With one wave per SIMD the order is what overlaps the reads with the matrix pipe; the
+// first MFMA of a half only waits for reads issued during the half before.
+__device__ __forceinline__ void dl_interleave() {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
 template <class LA, class LB, class EPI>
@@ -190,6 +203,7 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+        dl_interleave();
         if (it + 1 < nk) {
             // this wave's share of tile it + 1 has landed (tile it + 2 may still fly); past the
             // barrier every wave's has, and every wave is done with tile it - 1
@@ -201,17 +215,27 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
                 la.load(Sn, t.m0, t.kbeg + (it + 3) * DL_BK, wave, lane);
                 lb.load(Sn + AB, t.n0, t.kbeg + (it + 3) * DL_BK, wave, lane);
             }
-            const uint16_t* An = lds + ((it + 1) & 3) * DL_STAGE;
-#pragma unroll
-            for (int i = 0; i < FM; ++i) a0[i] = *(const bf16x8*)(An + dl_off(arow + 32 * i, half));
-#pragma unroll
-            for (int j = 0; j < FN; ++j) b0[j] = *(const bf16x8*)(An + AB + dl_off(brow + 32 * j, half));
         }
+        // the next tile's first fragments (after the last tile they read a stage no copy
+        // targets any more, and go unused), issued between this half's MFMAs
+        const uint16_t* An = lds + ((it + 1) & 3) * DL_STAGE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a0[i] = *(const bf16x8*)(An + dl_off(arow + 32 * i, half));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b0[j] = *(const bf16x8*)(An + AB + dl_off(brow + 32 * j, half));
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+        dl_interleave();
+        // keep those reads in this iteration (not sunk into the next one's first MFMAs), and
+        // their wait after this half's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(a0[i]));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b0[j]));
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
