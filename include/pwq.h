@@ -202,10 +202,15 @@ pwq_status pwq_recon_mse(const void* X, int x_dtype, int64_t n_tok, int64_t d_in
  * = tr((W - What) H (W - What)^T) / 2 for H = 2 X^T X ([GPTQ-P] "OBQ Foundation": the layer
  * error as a quadratic form in H), so
  *   mse = tr((W - What) (H - shift I) (W - What)^T) / (2 n_tok d_out),
- * equal to pwq_recon_mse's in exact arithmetic.  One d_out x d_in x d_in float32 MFMA
- * product instead of n_tok x d_in x d_out: the cheaper route when n_tok is well above d_in
- * (float32 MFMA runs at a sixteenth of the bfloat16 rate).
- *   H        d_in x d_in float32, both triangles (pwq_hessian_accumulate's output), row
+ * equal to pwq_recon_mse's in exact arithmetic.  One d_out x d_in x d_in product instead of
+ * n_tok x d_in x d_out: the cheaper route when n_tok is well above d_in.  Small layers run it
+ * on float32 MFMA; from 256 output tiles of 256 x 256 on (ceil(d_out/256) ceil(d_in/256)
+ * >= 256) it uses H's symmetry (each 256-column block of the output contracts only up to the
+ * diagonal block) and a bfloat16 hi/lo split of both operands (three products, each exact
+ * in float32; the dropped terms are below 2^-16 of each product), about 3 d_out d_in^2
+ * bfloat16 flops.
+ *   H        d_in x d_in float32, symmetric (pwq_hessian_accumulate's output): the float32
+ *            route reads both triangles, the split route the lower one and the diagonal; row
  *            stride ldh >= d_in; may already be damped: h_shift (device float, or NULL for
  *            0) is what damping added to its diagonal (pwq_hessian_damp's lambda_out).
  *   n_tok    the number of tokens H was accumulated over.

@@ -48,8 +48,9 @@ CALL_OF = [
     ("gptq_", "gptq_quantize_layer"), ("EpiSub", "gptq_quantize_layer"), ("inv_perm", "gptq_quantize_layer"),
     ("unpermute_codes", "gptq_quantize_layer"),
     ("rtn_kernel", "rtn_quantize"), ("rtn_group", "rtn_quantize"),
-    ("dequant_kernel", "dequant"), ("dequant_vec", "dequant"),
+    ("dequant_kernel", "dequant"), ("dequant_vec", "dequant"), ("dequant_f16", "dequant"),
     ("mse_", "recon_mse"), ("EpiSq", "recon_mse"), ("set_double", "recon_mse"),
+    ("SplitTriMap", "recon_mse"), ("EpiTrace", "recon_mse"),
     ("w4a16", "quantized_matmul"),
     ("chan_abs", "channel_abs_mean"), ("chan_mean", "channel_abs_mean"),
     ("awq_", "awq_search"), ("EpiDot", "awq_search"),
