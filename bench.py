@@ -280,8 +280,11 @@ def time_awq(layers, pwq, torch, K):
         flop = 2.0 * s.d_out * s.d_in * s.d_in * K
         out[s.name] = {"ms": round(ms, 3), "alpha": round(best / (K - 1), 3) if K > 1 else 0.0,
                        "mse_rtn": mse[0], "mse_awq": mse[best],
-                       "score_tflops": round(flop / (ms * 1e-3) / 1e12, 2),
-                       "score_frac_fp32": round(flop / (ms * 1e-3) / 1e12 / PEAK["mfma_f32"], 4)}
+                       "score_tflops": round(flop / (ms * 1e-3) / 1e12, 2)}
+        # the scores' product: the split bfloat16 route on large layers, else float32 MFMA
+        pk = "mfma_bf16" if mse_split_route(s) else "mfma_f32"
+        out[s.name]["score_peak"] = pk
+        out[s.name]["score_frac"] = round(flop / (ms * 1e-3) / 1e12 / PEAK[pk], 4)
     return out
 
 

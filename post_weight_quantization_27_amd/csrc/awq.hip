@@ -6,8 +6,9 @@
 // s_c = a_c^alpha (1 where a_c = 0), and is scored by the reconstruction MSE of
 // What = RTN(W diag(s)) diag(1/s) against W on the calibration set.  With H = 2 X^T X that
 // MSE is tr(dW H dW^T) / (2 N m), dW = W - What, so each candidate costs one m x n x n
-// product on the float32 MFMA engine instead of a pass over the N tokens (N >> n for the
-// large layers).  The grid is alpha = k / (K - 1); the least score wins, ties to the smaller
+// product instead of a pass over the N tokens (N >> n for the large layers): on the float32
+// MFMA engine, or from 256 output tiles of 256 x 256 on as the MSE's split bfloat16 product
+// over one triangle of H (H's pieces formed once per search).  The grid is alpha = k / (K - 1); the least score wins, ties to the smaller
 // alpha; the winner's W diag(s) is then quantized by the RTN kernels.
 //
 // Kernels: channel sums of |X| (float64 per token chunk, chunks added in order), the scale
@@ -205,10 +206,15 @@ hipError_t chan_abs_launch(const void* X, int x_dtype, int64_t N, int64_t n, int
     return hipGetLastError();
 }
 
-// workspace: dW / W diag(s) (m x n float32), s (n float32), the product's partial sums
+// workspace: dW / W diag(s) (m x n float32), s (n float32), the product's partial sums; on
+// the split route (large layers) then dW's and G's bfloat16 pieces
 size_t awq_ws_bytes(int64_t m, int64_t n) {
-    return align_up((size_t)m * n * sizeof(float), 256) + align_up((size_t)n * sizeof(float), 256) +
-           (size_t)awq_tiles(m, n) * sizeof(double);
+    const bool sp = split_route(m, n);
+    const int64_t tiles = sp ? split_tiles(m, n) : awq_tiles(m, n);
+    size_t b = align_up((size_t)m * n * sizeof(float), 256) + align_up((size_t)n * sizeof(float), 256) +
+               align_up((size_t)tiles * sizeof(double), 256);
+    if (sp) b += split_pieces_bytes(m, n) + split_g_bytes(n);
+    return b;
 }
 
 hipError_t awq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, const float* H, int64_t N,
@@ -220,6 +226,14 @@ hipError_t awq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
     float* dW = (float*)base;
     float* sv = (float*)(base + align_up((size_t)m * n * sizeof(float), 256));
     double* part = (double*)(base + align_up((size_t)m * n * sizeof(float), 256) + align_up((size_t)n * sizeof(float), 256));
+    const bool sp = split_route(m, n);
+    uint16_t* a3 = nullptr;
+    uint16_t* b3 = nullptr;
+    if (sp) {
+        a3 = (uint16_t*)((char*)part + align_up((size_t)split_tiles(m, n) * sizeof(double), 256));
+        b3 = (uint16_t*)((char*)a3 + split_pieces_bytes(m, n));
+        if ((e = split_g_launch(H, n, n, b3, s)) != hipSuccess) return e;
+    }
 
     AwqArgs a{};
     a.W = W; a.ldw = ldw; a.m = m; a.n = n;
@@ -255,7 +269,14 @@ hipError_t awq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
         a.scaled_only = 0;
         if ((e = delta()) != hipSuccess) return e;
         int64_t np = 0;
-        e = big ? awq_product<128, 128>(dW, H, m, n, part, &np, s) : awq_product<64, 64>(dW, H, m, n, part, &np, s);
+        if (sp) {
+            // large layers: the split bfloat16 product over one triangle of H (G's pieces formed once)
+            if ((e = split_pieces_launch(dW, n, m, n, a3, s)) != hipSuccess) return e;
+            np = split_tiles(m, n);
+            e = split_trace_launch(a3, b3, dW, n, m, n, nullptr, part, s);
+        } else {
+            e = big ? awq_product<128, 128>(dW, H, m, n, part, &np, s) : awq_product<64, 64>(dW, H, m, n, part, &np, s);
+        }
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(awq_score_kernel, dim3(1), dim3(256), 0, s, part, np, 2.0 * (double)N * (double)m, mse + k);
         if ((e = hipGetLastError()) != hipSuccess) return e;

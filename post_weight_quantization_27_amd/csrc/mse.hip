@@ -310,6 +310,25 @@ __device__ __forceinline__ void bf16_hi_lo(float v, uint16_t& hi, uint16_t& lo) 
     lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
 }
 
+// row o, columns c .. c+7 (c % 8 == 0) of dW as the pieces hi, hi, lo in the tile-major layout
+// of k per row 3 npad
+__device__ __forceinline__ void put_pieces(uint16_t* __restrict__ a3, int64_t o, int64_t c, int64_t npad,
+                                           const float (&d)[8]) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint16_t h0, l0, h1, l1;
+        bf16_hi_lo(d[2 * k], h0, l0);
+        bf16_hi_lo(d[2 * k + 1], h1, l1);
+        hw[k] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lw[k] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    const int64_t kl = 3 * npad, k0 = (c >> 8) * (3 * DL_TILE) + (c & (DL_TILE - 1));
+    *(uint4*)(a3 + dl_tiled_index(o, k0, kl)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *(uint4*)(a3 + dl_tiled_index(o, k0 + DL_TILE, kl)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *(uint4*)(a3 + dl_tiled_index(o, k0 + 2 * DL_TILE, kl)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+}
+
 // dW in float32 (row-major, ld k8, for the epilogue) and as the pieces hi, hi, lo, tile-major
 // over 256-row panels with k per row 3 npad; rows past m and columns past n are zero.
 // One thread per 8 columns of a row (npad a multiple of 256, so 8 columns share a block).
@@ -333,19 +352,25 @@ __global__ __launch_bounds__(256) void mse_decode3_kernel(const void* __restrict
         *(float4*)p = make_float4(d[0], d[1], d[2], d[3]);
         *(float4*)(p + 4) = make_float4(d[4], d[5], d[6], d[7]);
     }
-    uint32_t hw[4], lw[4];
+    put_pieces(a3, o, c, npad, d);
+}
+
+// the pieces of a float32 dW (row-major, ld) that is already formed; zero past m and n
+__global__ __launch_bounds__(256) void mse_pieces_kernel(const float* __restrict__ dw, int64_t ld, int64_t m, int64_t n,
+                                                         int64_t mpad, int64_t npad, int vec, uint16_t* __restrict__ a3) {
+    const int64_t per_row = npad / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= mpad * per_row) return;
+    const int64_t o = idx / per_row, c = (idx - o * per_row) * 8;
+    float d[8];
+    if (vec && o < m && c + 8 <= n) {
+        const float4 v0 = *(const float4*)(dw + o * ld + c), v1 = *(const float4*)(dw + o * ld + c + 4);
+        d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w; d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint16_t h0, l0, h1, l1;
-        bf16_hi_lo(d[2 * k], h0, l0);
-        bf16_hi_lo(d[2 * k + 1], h1, l1);
-        hw[k] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lw[k] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        for (int k = 0; k < 8; ++k) d[k] = (o < m && c + k < n) ? dw[o * ld + c + k] : 0.f;
     }
-    const int64_t kl = 3 * npad, k0 = (c >> 8) * (3 * DL_TILE) + (c & (DL_TILE - 1));
-    *(uint4*)(a3 + dl_tiled_index(o, k0, kl)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    *(uint4*)(a3 + dl_tiled_index(o, k0 + DL_TILE, kl)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    *(uint4*)(a3 + dl_tiled_index(o, k0 + 2 * DL_TILE, kl)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    put_pieces(a3, o, c, npad, d);
 }
 
 // B(c, j) = G[j][c] = 2 H[c][j] (j < c), H[c][c] (j = c), 0 (j > c, or past n), as the
@@ -449,6 +474,41 @@ hipError_t mse_h_product(const float* dW, int64_t lddw, const float* H, int64_t 
 }
 }  // namespace
 
+// ---- the split product, also used by the AWQ search (per candidate dW, G formed once)
+bool split_route(int64_t d_out, int64_t d_in) { return mse_h_split(d_out, d_in); }
+size_t split_pieces_bytes(int64_t d_out, int64_t d_in) { return split_ws(d_out, d_in).a3_bytes; }
+size_t split_g_bytes(int64_t d_in) { return split_ws(1, d_in).b3_bytes; }
+int64_t split_tiles(int64_t d_out, int64_t d_in) { return split_ws(d_out, d_in).tiles; }
+
+hipError_t split_g_launch(const float* H, int64_t ldh, int64_t n, uint16_t* b3, hipStream_t s) {
+    const int64_t npad = cdiv(n, DL_TILE) * DL_TILE;
+    const int hvec = (ldh % 4 == 0) && aligned(H, 16);
+    hipLaunchKernelGGL(mse_gsplit_kernel, dim3((unsigned)cdiv(npad * (npad / 8), 256)), dim3(256), 0, s, H, ldh, n, npad,
+                       hvec, b3);
+    return hipGetLastError();
+}
+
+hipError_t split_pieces_launch(const float* dW, int64_t ld, int64_t m, int64_t n, uint16_t* a3, hipStream_t s) {
+    const int64_t mpad = cdiv(m, DL_TILE) * DL_TILE, npad = cdiv(n, DL_TILE) * DL_TILE;
+    const int vec = (ld % 4 == 0) && aligned(dW, 16);
+    hipLaunchKernelGGL(mse_pieces_kernel, dim3((unsigned)cdiv(mpad * (npad / 8), 256)), dim3(256), 0, s, dW, ld, m, n,
+                       mpad, npad, vec, a3);
+    return hipGetLastError();
+}
+
+// part[t] = sum over output tile t of ((dW G) - shift dW) dW, t < split_tiles(m, n)
+hipError_t split_trace_launch(const uint16_t* a3, const uint16_t* b3, const float* dW, int64_t ld, int64_t m, int64_t n,
+                              const float* shift, double* part, hipStream_t s) {
+    const int64_t mpad = cdiv(m, DL_TILE) * DL_TILE, npad = cdiv(n, DL_TILE) * DL_TILE;
+    DlTiled a{{a3, nullptr, nullptr, nullptr}, 1, 3 * npad};
+    DlTri b{b3, SPLIT_KT};
+    SplitTriMap mp{(int)(mpad / DL_TILE), (int)(npad / DL_TILE), nullptr};
+    EpiTrace ep{dW, ld, m, n, part, shift, 0.f};
+    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTri, SplitTriMap, EpiTrace>), dim3((unsigned)((mpad / DL_TILE) * (npad / DL_TILE))),
+                       dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
+    return hipGetLastError();
+}
+
 // workspace: float32 route: dW (d_out x k8 float32), then one float64 partial per tile;
 // split route: dW float32, dW's pieces, G's pieces, then one float64 partial per tile
 size_t mse_h_ws_bytes(int64_t d_in, int64_t d_out) {
@@ -488,18 +548,9 @@ hipError_t mse_h_launch(const float* H, int64_t ldh, int64_t d_in, int64_t n_tok
         hipLaunchKernelGGL(dec, dim3((unsigned)cdiv(w.mpad * (w.npad / 8), 256)), dim3(256), 0, s, W, ldw, d_out, d_in,
                            w.mpad, w.npad, k8, packed, codes, scales, zeros, g_idx, ng, group_size, vec, dw, a3);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int hvec = (ldh % 4 == 0) && aligned(H, 16);
-        hipLaunchKernelGGL(mse_gsplit_kernel, dim3((unsigned)cdiv(w.npad * (w.npad / 8), 256)), dim3(256), 0, s, H, ldh,
-                           d_in, w.npad, hvec, b3);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        DlTiled a{{a3, nullptr, nullptr, nullptr}, 1, 3 * w.npad};
-        DlTri b{b3, SPLIT_KT};
-        SplitTriMap mp{(int)(w.mpad / DL_TILE), (int)(w.npad / DL_TILE), nullptr};
-        EpiTrace ep{dw, k8, d_out, d_in, part, shift, 0.f};
+        if ((e = split_g_launch(H, ldh, d_in, b3, s)) != hipSuccess) return e;
         np = w.tiles;
-        hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTri, SplitTriMap, EpiTrace>), dim3((unsigned)np),
-                           dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = split_trace_launch(a3, b3, dw, k8, d_out, d_in, shift, part, s)) != hipSuccess) return e;
     } else {
         part = (double*)((char*)ws + align_up((size_t)(d_out * k8) * sizeof(float), 256));
         const unsigned dgrid = (unsigned)cdiv(d_out * (k8 / 8), 256);

@@ -81,6 +81,16 @@ hipError_t w4a16_launch(const uint16_t* X, int64_t T, int64_t n, int64_t ldx, co
 
 // Reconstruction MSE.
 size_t mse_ws_bytes(int64_t n_tok, int64_t d_in, int64_t d_out);
+// the split product of the Hessian-route MSE (layers of >= 256 output tiles of 256 x 256):
+// G's pieces from H once, dW's pieces per dW, then per-tile trace sums
+bool split_route(int64_t d_out, int64_t d_in);
+size_t split_pieces_bytes(int64_t d_out, int64_t d_in);
+size_t split_g_bytes(int64_t d_in);
+int64_t split_tiles(int64_t d_out, int64_t d_in);
+hipError_t split_g_launch(const float* H, int64_t ldh, int64_t n, uint16_t* b3, hipStream_t s);
+hipError_t split_pieces_launch(const float* dW, int64_t ld, int64_t m, int64_t n, uint16_t* a3, hipStream_t s);
+hipError_t split_trace_launch(const uint16_t* a3, const uint16_t* b3, const float* dW, int64_t ld, int64_t m, int64_t n,
+                              const float* shift, double* part, hipStream_t s);
 size_t mse_h_ws_bytes(int64_t d_in, int64_t d_out);
 hipError_t mse_h_launch(const float* H, int64_t ldh, int64_t d_in, int64_t n_tok, const float* shift, const void* W,
                         int w_dtype, int64_t ldw, const uint8_t* packed, const int8_t* codes, const uint16_t* scales,

@@ -105,3 +105,16 @@ def test_awq_search_gpt2_layer(pwq):
     X = synth.x_full(spec)
     best, want = _run(pwq, W, X, spec.group_size, 21, True)
     print(f"c_fc: best alpha {want['alpha']:.2f}, RTN mse {want['mse'][0]:.5g} -> {want['mse'][want['best']]:.5g}")
+
+
+@pytest.mark.parametrize("m,n,N,sym", [(4096, 4096, 1024, True), (4352, 4100, 768, False)])
+def test_awq_search_split_route(pwq, m, n, N, sym):
+    """Layers of at least 256 output tiles of 256 x 256 score the candidates with the split
+    bfloat16 product over one triangle of H (ragged panels in the second case)."""
+    rng = np.random.default_rng(m + n)
+    W = rand_w(rng, m, n)
+    X = rng.standard_normal((N, n)).astype(np.float32)
+    X[:, rng.choice(n, n // 50, replace=False)] *= 20
+    X[:, 7] = 0.0
+    best, want = _run(pwq, W, X, 128, 4, sym)
+    print(f"m={m} n={n}: best alpha index {best}, scores {np.round(want['mse'] / want['mse'][0], 4)}")
