@@ -145,3 +145,25 @@ def test_mse_hessian_split_route(pwq, m, n, g, sym, wdt, corr):
     got = float(host(pwq.recon_mse_hessian(dev(H32), n_tok, dev(W), dev(r["scales"]), 4, g, shift=shift, **kw))[0])
     print(f"{m}x{n}: relative error {abs(got - want) / want:.2e}")
     assert abs(got - want) <= 1e-4 * want
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_mse_hessian_split_route_70b_q_shape(pwq, sym):
+    """The 70B q projection's shape (8192 x 8192, 1024 tiles of 256 x 256) on the split route,
+    H from the library's own Hessian call over 4096 bfloat16 tokens and damped; the expected
+    value is the oracle's X-based mean square."""
+    rng = np.random.default_rng(8192 + sym)
+    n_tok, n, m = 4096, 8192, 8192
+    Xd, X64 = x_pair(rng, n_tok, n, "bf16", 0.5)
+    W = rand_w(rng, m, n, np.float16)
+    r = O.rtn(W, 4, 128, sym=sym)
+    want = O.recon_mse(X64, W, r["What"])
+    H = gpu_hessian(pwq, Xd)
+    lam = torch.zeros(1, dtype=torch.float32, device=DEV)
+    pwq.hessian_damp(H, 0.01, lambda_out=lam)
+    kw = {"packed": dev(O.pack_int4(r["codes"]) if sym else O.pack_uint4(r["codes"]))}
+    if not sym:
+        kw["zeros"] = dev(r["zeros"].view(np.int16))
+    got = float(host(pwq.recon_mse_hessian(H, n_tok, dev(W), dev(r["scales"]), 4, 128, shift=lam, **kw))[0])
+    print(f"8192x8192 sym={sym}: relative error {abs(got - want) / want:.2e}")
+    assert abs(got - want) <= 1e-4 * want
