@@ -89,9 +89,10 @@ listed in the design notes):
 Pins (tests/test_oracle_pins.py):
   rtn / quantize_codes / group_scales : golden tie-to-even rows, code range, error bound,
                                         level count
-  gptq                                : [LESSON17] worked examples (golden), diagonal-H == rtn,
-                                        direct_obs agreement, block-size invariance,
-                                        scale invariance, brute-force optimum on tiny rows
+  gptq / gptq_unblocked               : [LESSON17] worked examples (golden) and the carry
+                                        rule's closed form, diagonal-H == rtn, direct_obs
+                                        agreement, batched == unblocked for every block
+                                        size, scale invariance, brute-force optimum on tiny rows
   chol_inverse_upper                  : U^T U H = I, triangular, positive diagonal,
                                         reverse-order Cholesky + triangular inverse route
   hessian / damp                      : brute force on tiny X, trace identity, symmetry
@@ -107,6 +108,12 @@ Pins (tests/test_oracle_pins.py):
                                         exactly; every candidate's score equals the trace
                                         identity with H; the output of X / s through W s is
                                         X W^T; an outlier channel is protected
+  quantize_layer                      : (tests/test_oracle_layer_pins.py) the OBS compensation
+                                        on a two-column block in exact rationals, with and
+                                        without act-order; diagonal H == RTN (of the permuted
+                                        matrix with act-order); a sorted diagonal leaves
+                                        act-order a no-op; both errors by brute-force sums;
+                                        rank-deficient X factorable only with damping
   tensor_scales                       : the per-row rule on the flattened matrix; the
                                         tensor's absmax element maps to +-qmax; GPTQ with a
                                         diagonal H and these scales equals RTN with them
@@ -268,21 +275,29 @@ def act_order_perm(H: np.ndarray) -> np.ndarray:
 def chol_inverse_upper(H: np.ndarray) -> np.ndarray:
     """U upper triangular with H^-1 = U^T U and U_jj > 0 ([MQM] 2.1, R1).
 
-    Textbook route: invert H, take the lower Cholesky factor L of H^-1, U = L^T.
-    Raises NotPositiveDefinite when H is not positive definite (R12); the pivot is
-    located by LAPACK's Cholesky of H in reversed index order."""
+    Textbook route: the Cholesky factor of H (H = R^T R), H^-1 from it (LAPACK potri),
+    then the lower Cholesky factor L of H^-1, U = L^T.  Raises NotPositiveDefinite when H
+    is not positive definite (R12); the pivot is then located by LAPACK's Cholesky of H in
+    reversed index order, the order the GPU factorization eliminates in."""
     from scipy.linalg import lapack
 
     n = H.shape[0]
-    rev = H[::-1, ::-1]
-    _, info = lapack.dpotrf(np.array(rev, dtype=np.float64, order="F"), lower=1)
+    R, info = lapack.dpotrf(np.array(H, dtype=np.float64, order="F"), lower=0, clean=1, overwrite_a=1)
     if info != 0:
-        k = int(info) - 1 if info > 0 else 0
+        rev = H[::-1, ::-1]
+        _, info_r = lapack.dpotrf(np.array(rev, dtype=np.float64, order="F"), lower=1)
+        k = int(info_r) - 1 if info_r > 0 else max(int(info) - 1, 0)
         raise NotPositiveDefinite(n - 1 - k)
-    Hinv = np.linalg.inv(H)
-    Hinv = 0.5 * (Hinv + Hinv.T)
-    L = np.linalg.cholesky(Hinv)
-    return np.triu(L.T)
+    S, info = lapack.dpotri(R, lower=0, overwrite_c=1)      # upper triangle of H^-1
+    if info != 0:
+        raise NotPositiveDefinite(n - 1)
+    del R
+    S = np.triu(S)
+    S += np.triu(S, 1).T                                     # H^-1, both triangles
+    L, info = lapack.dpotrf(S, lower=1, clean=1, overwrite_a=1)
+    if info != 0:
+        raise NotPositiveDefinite(n - 1)
+    return np.ascontiguousarray(L.T)
 
 
 # ------------------------------------------------------------------ GPTQ column loop
@@ -316,25 +331,34 @@ def _init_params(m, ng, scales_in, zeros_in, sym):
     return scales, zeros
 
 
+def _current(Wp: np.ndarray, E: np.ndarray, U: np.ndarray, j: int, c0: int, c1: int) -> np.ndarray:
+    """Values of columns c0..c1-1 once columns 0..j-1 are fixed: each fixed column i has
+    moved every later column k by -e_i U_ik (R1, R2), so the current value is the original
+    one less sum_i e_i U_ik over the fixed columns."""
+    if j == 0:
+        return Wp[:, c0:c1].copy()
+    return Wp[:, c0:c1] - E[:, :j] @ U[:j, c0:c1]
+
+
 def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, block_size: int = 128,
          perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None,
          sym: bool = True, zeros_in: Optional[np.ndarray] = None,
          forced_codes: Optional[np.ndarray] = None, forced_scales: Optional[np.ndarray] = None,
          forced_zeros: Optional[np.ndarray] = None) -> dict:
-    """GPTQ with lazy block updates ([GPTQ-P] "The GPTQ Algorithm", R1-R9).
+    """GPTQ in fixed left-to-right order with the updates applied in batches ([GPTQ-P] "The
+    GPTQ Algorithm", R1-R9).
 
     W: d_out x d_in (any float dtype, promoted to float64).  U: the factor of
     ``chol_inverse_upper`` of the (damped, permuted if ``perm``) Hessian.
 
-    Columns are taken left to right in blocks of ``block_size``.  For each column j of
-    a block: (at a group's first column) the group's scales; codes = round(w_j / s);
-    e_j = (w_j - s * code) / U_jj is stored in the block's error panel; the columns
-    j+1..block end of the panel get w_k -= e_j U_jk at once.  After the block, all
-    columns right of it get W -= Err @ U[block, right] in one product.
-
-    A group that starts inside a block and reaches past its end sees, for its columns
-    right of the block, the updates still pending from the block's earlier columns
-    (the pages' group = block = 128 case never needs this).
+    Column j is quantized at its current value: the original value less e_i U_ij for every
+    column i < j already fixed, where e_i = (w_i - what_i) / U_ii is column i's error scaled
+    by the factor's diagonal.  This is ``gptq_unblocked`` (every error pushed to all later
+    columns at once) with the sums regrouped, which the pages' lazy batching amounts to:
+    the errors of all earlier blocks of ``block_size`` columns reach a block in one product
+    when the block starts; inside the block each column adds the terms of the block's
+    earlier columns.  A group's scale (and zero) is taken at its first column from the
+    current values of all its columns, including any past the block (R5).
 
     ``sym=False``: zero-point quantization (A1-A5); the group's scale and zero come from
     the same current values the symmetric scale would.
@@ -348,6 +372,9 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
     its own and recorded how far apart the two are.  The arithmetic is otherwise unchanged;
     it checks that the other run decided like this one given the same history.
 
+    Rows are independent (each row has its own scales and sees the same U), so a subset of
+    rows gives the same result for those rows as the whole matrix.
+
     Returns codes (int8, or uint8 with zero-points; original column order), scales
     (float16, d_out x groups, in processing order), zeros (uint16 like scales, or None),
     g_idx (int32 or None) and What (float64)."""
@@ -358,6 +385,7 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
     ng = n_groups(n, group_size)
     scales, zeros = _init_params(m, ng, scales_in, zeros_in, sym)
     codes_p = np.zeros((m, n), dtype=np.int8 if sym else np.uint8)
+    E = np.zeros((m, n))
     B = int(block_size)
     forced = None
     if forced_codes is not None:
@@ -365,17 +393,11 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
                   "scale_max_ulp": 0, "zero_mismatch": 0, "zero_max_step": 0}
     for b0 in range(0, n, B):
         b1 = min(b0 + B, n)
-        panel = Wp[:, b0:b1].copy()
-        err = np.zeros((m, b1 - b0))
+        cur = _current(Wp, E, U, b0, b0, b1)            # every earlier block's errors, one product
         for j in range(b0, b1):
-            jj = j - b0
             G = j // g
             if j % g == 0 and scales_in is None:
-                ge = min(j + g, n)
-                vals = panel[:, jj:min(ge, b1) - b0]
-                if ge > b1:
-                    pending = Wp[:, b1:ge] - err[:, :jj] @ U[b0:j, b1:ge]
-                    vals = np.concatenate([vals, pending], axis=1)
+                vals = _current(Wp, E, U, j, j, min(j + g, n))
                 sG, zG = _group_params(vals, bits, sym)
                 if forced is not None and forced_scales is not None:
                     fs = np.asarray(forced_scales, dtype=np.float16).reshape(m, ng)[:, G]
@@ -394,7 +416,7 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
                 if not sym:
                     zeros[:, G] = zG
             zc = None if sym else zeros[:, G]
-            w = panel[:, jj]
+            w = cur[:, j - b0] - E[:, b0:j] @ U[b0:j, j]      # this block's earlier columns
             q = _codes(w, scales[:, G], zc, bits, sym)
             if forced is not None:
                 qf = np.asarray(forced_codes[:, j]).astype(q.dtype)
@@ -409,12 +431,7 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
                     forced["max_step"] = max(forced["max_step"], int(np.max(np.abs(qf[diff].astype(np.int64) - q[diff].astype(np.int64)))))
                 q = qf
             codes_p[:, j] = q
-            what = _value(scales[:, G], zc, q)
-            e = (w - what) / U[j, j]
-            err[:, jj] = e
-            panel[:, jj + 1:] -= np.outer(e, U[j, j + 1:b1])
-        if b1 < n:
-            Wp[:, b1:] -= err @ U[b0:b1, b1:]
+            E[:, j] = (w - _value(scales[:, G], zc, q)) / U[j, j]
     res = _finish(codes_p, scales, perm, group_size, bits, zeros)
     if forced is not None:
         res["forced"] = forced
@@ -424,7 +441,11 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
 def gptq_unblocked(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128,
                    perm: Optional[np.ndarray] = None, scales_in: Optional[np.ndarray] = None,
                    sym: bool = True, zeros_in: Optional[np.ndarray] = None) -> dict:
-    """The column loop without lazy batching: every error goes to all later columns at once."""
+    """The column loop as the method defines it, one column at a time ([GPTQ-P] "The GPTQ
+    Algorithm", R1-R9): at a group's first column its scale (and zero) from the group's
+    current values; the column's code; its error scaled by U_jj, e_j = (w_j - what_j) / U_jj;
+    then every later column k moves by -e_j U_jk at once.  ``gptq`` computes the same
+    result with the updates batched."""
     W = np.asarray(W, dtype=np.float64)
     m, n = W.shape
     Wp = W[:, perm].copy() if perm is not None else W.copy()

@@ -379,6 +379,10 @@ def awq_search(W: torch.Tensor, H: torch.Tensor, n_tok: int, abs_mean: torch.Ten
     s (float32 d_in), codes, packed, scales, zeros} with the RTN result of W diag(s)."""
     ldw = _rows(W, "W")
     d_out, d_in = W.shape
+    # the library reads H as a dense d_in x d_in float32 matrix (row pitch d_in) and abs_mean
+    # as d_in float32 values
+    _need(H, torch.float32, (d_in, d_in), "H")
+    _need(abs_mean, torch.float32, (d_in,), "abs_mean")
     dev = W.device
     ng = _n_groups(d_in, group_size)
     o = {"mse": torch.empty(n_alpha, dtype=torch.float64, device=dev),

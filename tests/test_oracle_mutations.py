@@ -199,3 +199,65 @@ def test_awq_unscaled_reconstruction_fails_pin(monkeypatch):
     monkeypatch.setattr(O, "awq_search", bad_search)
     with pytest.raises(AssertionError):
         P.test_awq_search_pins()
+
+
+# ---------------------------------------------------------------------------------- whole layer
+import test_oracle_layer_pins as LP
+
+
+def _layer_with(mistake):
+    """quantize_layer's composition with one planted mistake."""
+    def layer(W, x_tiles, bits=4, group_size=128, block_size=128, damp=0.01, act_order=False, perm=None,
+              sym=True):
+        if isinstance(x_tiles, np.ndarray):
+            x_tiles = [x_tiles]
+        x_tiles = list(x_tiles)
+        H = OM.hessian(x_tiles)
+        n_tok = sum(int(np.asarray(t).shape[0]) for t in x_tiles)
+        Hd, lam = OM.damp_hessian(H, damp)
+        if mistake == "undamped_factor":
+            Hd = H + 1e-300 * np.eye(H.shape[0])
+        if act_order and perm is None:
+            perm = OM.act_order_perm(Hd)
+        elif not act_order:
+            perm = None
+        Hp = Hd[np.ix_(perm, perm)] if (perm is not None and mistake != "perm_on_w_only") else Hd
+        U = OM.chol_inverse_upper(Hp)
+        res = OM.gptq(W, U, bits, group_size, block_size, perm=perm, sym=sym)
+        r = OM.rtn(W, bits, group_size, sym=sym)
+        What = res["What"]
+        if mistake == "what_in_processing_order" and perm is not None:
+            What = What[:, perm]
+        res.update({"H": H, "lambda": lam, "perm": perm, "U": U, "rtn": r, "n_tok": n_tok,
+                    "gptq_mse": OM.recon_mse(x_tiles, W, What), "rtn_mse": OM.recon_mse(x_tiles, W, r["What"])})
+        return res
+    return layer
+
+
+LAYER_PINS = [LP.test_layer_diagonal_hessian_is_rtn, LP.test_layer_sorted_diagonal_act_order_is_identity,
+              LP.test_layer_errors_brute_force, LP.test_layer_two_column_compensation_closed_form,
+              LP.test_layer_damping_makes_rank_deficient_inputs_factorable]
+PIN_ARGS = {LP.test_layer_diagonal_hessian_is_rtn: [(0,), (32,)], LP.test_layer_errors_brute_force: [(False,), (True,)],
+            LP.test_layer_two_column_compensation_closed_form: [(1,), (128,)]}
+
+
+def _failing_layer_pins():
+    failed = []
+    for pin in LAYER_PINS:
+        for args in PIN_ARGS.get(pin, [()]):
+            try:
+                pin(*args)
+            except (AssertionError, ArithmeticError, np.linalg.LinAlgError):
+                failed.append(pin.__name__)
+    return failed
+
+
+def test_unmutated_layer_passes_every_layer_pin(monkeypatch):
+    monkeypatch.setattr(O, "quantize_layer", _layer_with(None))
+    assert _failing_layer_pins() == []
+
+
+@pytest.mark.parametrize("mistake", ["perm_on_w_only", "undamped_factor", "what_in_processing_order"])
+def test_layer_composition_mistakes_fail_a_pin(monkeypatch, mistake):
+    monkeypatch.setattr(O, "quantize_layer", _layer_with(mistake))
+    assert _failing_layer_pins(), mistake

@@ -78,21 +78,20 @@ def test_lesson17_two_weight_exercise():
 
 
 def test_error_carry_rule_equals_gptq_on_random_rows():
-    """For X = lower-triangular ones the U-form loop is exactly the carry rule of Example 1.1
-    (round (v + carry), carry the residual) on any row and grid step."""
+    """For X = lower-triangular ones the U-form loop is exactly the error-carry rule of the
+    lesson's Example 1.1 on any row and grid step.  That rule keeps every prefix sum of the
+    rounded weights at the grid point nearest the prefix sum of the weights (each step rounds
+    the running sum less what is already placed, a multiple of the step), so the compensated
+    weights are the differences of round(cumsum(w) / step) * step (no ties occur here)."""
     rng = np.random.default_rng(11)
     n = 12
     W = rng.normal(0, 0.3, size=(40, n))
     s = np.full((40, 1), 0.0625, dtype=np.float16)     # power-of-two grid: all values exact
     res, *_ = gptq_full(W, tril_ones(n), bits=8, group_size=0, block_size=5, damp=0.0, scales_in=s)
     step = float(s[0, 0])
-    for r in range(W.shape[0]):
-        carry, comp = 0.0, []
-        for v in W[r]:
-            q = round((v + carry) / step) * step
-            carry = v + carry - q
-            comp.append(q)
-        assert np.allclose(res["What"][r], comp, atol=0, rtol=0)
+    placed = np.rint(np.cumsum(W, axis=1) / step) * step
+    comp = np.diff(np.concatenate([np.zeros((W.shape[0], 1)), placed], axis=1), axis=1)
+    assert np.array_equal(res["What"], comp)
 
 
 # ---------------------------------------------------------------------------------- p2 / p13 / R7 / R8
