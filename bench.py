@@ -3,13 +3,19 @@
 One step = every step of the path for every layer of the workload, on inputs already
 resident in HBM: Hessian from X, damping, [act-order], H^-1 factor, GPTQ (INT4 packed +
 fp16 scales), RTN, dequant of the GPTQ result, and the reconstruction MSE of both (through
-the tokens, or through H when n_tok >= 10 d_in, where that product is the cheaper one).
-The value is weights quantized per second (sum of d_out * d_in over the layers / step).
+the tokens, or through H where that product is the cheaper one).  The value is weights
+quantized per second (sum of d_out * d_in over the layers / step).
 
-Prints ONE JSON line.  The value comes from K timed steps with no events between the
-launches; per-call durations come from K more steps with HIP events recorded around every
-call on the stream it runs on (each layer has its own stream, which the binding passes to
-libpwq).  The roofline object describes the longest (layer, call) launch.
+The default workload is the 70B-shaped layer set (q 8192 -> 8192, gate/up 8192 -> 28672,
+down 28672 -> 8192, 262144 bfloat16 tokens each), measured with act-order off (the line's
+value) and on (a second object in the same line).
+
+Prints ONE JSON line.  For each act-order setting: the value comes from K timed steps with
+no events between the launches; per-call durations from K more steps with HIP events
+recorded around every call on the stream it runs on (each layer has its own stream, which
+the binding passes to libpwq); per-kernel durations from the library's own events around
+its large kernels (pwq_profile_enable), one layer at a time.  The roofline object describes
+the kernel with the most time per step.
 """
 from __future__ import annotations
 
@@ -31,9 +37,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gpt2_block")
+    ap.add_argument("--workload", default="llama70b")
     ap.add_argument("--layers", default="", help="comma-separated layer names (default: all)")
-    ap.add_argument("--act-order", action="store_true")
+    ap.add_argument("--act-order", choices=("off", "on", "both"), default="both",
+                    help="act-order off, on, or both (the line's value is the first; 'both' adds an act_order_on object)")
     ap.add_argument("--zero-point", action="store_true", help="the asymmetric form (a scale and a zero per group)")
     ap.add_argument("--streams", type=int, default=1, help="1: one stream per layer (default), 0: all on one stream")
     ap.add_argument("--stagger", type=int, default=1,
@@ -44,7 +51,10 @@ def parse():
                     help="grid size of the activation-aware scaling search timed per layer (0 to skip)")
     ap.add_argument("--matmul-tokens", default="1,16",
                     help="token counts at which Y = X What^T is timed on each layer's GPTQ output ('' to skip)")
-    ap.add_argument("--cpu-layers", default="", help="layers the oracle baseline runs (default: all)")
+    ap.add_argument("--cpu-layer", default="", help="layer the oracle baseline samples (default: the one with the "
+                    "fewest inputs, then the fewest weights)")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of W the oracle's column loop runs on")
+    ap.add_argument("--prof-reps", type=int, default=2, help="steps per layer in the per-kernel timing pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (3 times), the reference for HBM traffic counters")
     return ap.parse_args()
@@ -196,18 +206,6 @@ def work_of(name, spec, zero_point=False):
     return "hbm", 0, "byte"
 
 
-# kernels one call launches, for the roofline's description (chol and gptq per 128 columns)
-def launches_of(name, spec):
-    nb = -(-spec.d_in // 128)
-    if name == "chol_inverse_upper":            # below 4096 the next diagonal factor joins the update launch
-        return 2 + (2 if spec.d_in < 4096 else 3) * nb
-    if name == "gptq_quantize_layer":
-        return 1 + 2 * nb
-    if name == "recon_mse":                     # decode, (split H,) product, final sum; two calls
-        return 8 if mse_through_hessian(spec) and mse_split_route(spec) else 6
-    return None
-
-
 def traffic_of(workload, layer, call):
     """HBM bytes per call from the committed counter summary, if it was taken on the kernel
     sources as they are now (else None)."""
@@ -307,30 +305,74 @@ def time_tensor_scales(layers, pwq, torch, iters=20):
     return out
 
 
-def cpu_baseline(specs, synth, budget_layers, zero_point=False):
-    """The oracle, as it stands, on one full step of the selected layers."""
-    import numpy as np
-    import oracle as O
+def _cpu_info():
+    """(threads the BLAS uses, CPU model name)."""
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    weights = 0
-    for s in specs:
-        if budget_layers and s.name not in budget_layers:
-            continue
-        W = synth.weight(s)
-        X = synth.x_full(s)
-        X64 = synth.as_f64(X, s.x_dtype)
-        r = O.quantize_layer(W, [X64], s.bits, s.group_size, s.block_size, s.damp, False, sym=not zero_point)
-        O.dequant(r["codes"], r["scales"], s.group_size, g_idx=r["g_idx"], out_dtype=np.float16, zeros=r["zeros"])
-        weights += s.n_weights
-    dt = time.perf_counter() - t0
-    names = [s.name for s in specs if not budget_layers or s.name in budget_layers]
-    return {"value": weights / dt, "unit": "weights/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"one full step of layers {','.join(names)} in float64 numpy ({dt:.1f} s)"}
+        threads = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return int(threads), model
+
+
+def cpu_baseline(specs, synth, layer_name="", rows=256, zero_point=False):
+    """The oracle as it stands, timed on a bounded sample of one layer of the workload: the
+    Hessian over the first 8192-token tile, damping and the factor of that H (full size),
+    GPTQ on ``rows`` seeded rows of W, RTN on every row, dequant of the sampled rows and both
+    reconstruction errors of the sampled rows over the tile.  Steps that grow with the tokens
+    (Hessian, errors) or the rows (GPTQ, dequant, errors) are scaled linearly to the whole
+    layer; damping, the factor and RTN ran whole.  value = the layer's weights / that time."""
+    import numpy as np
+    import oracle as O
+    if layer_name:
+        s = next(x for x in specs if x.name == layer_name)
+    else:
+        s = min(specs, key=lambda x: (x.d_in, x.n_weights))
+    sym = not zero_point
+    W = synth.weight(s)
+    X64 = synth.as_f64(synth.x_tile(s, 0), s.x_dtype)
+    ntile = X64.shape[0]
+    r = min(rows, s.d_out)
+    sel = np.sort(np.random.default_rng([27, s.d_out, s.d_in]).choice(s.d_out, r, replace=False))
+    t = {}
+
+    def tick(name, f):
+        t0 = time.perf_counter()
+        out = f()
+        t[name] = time.perf_counter() - t0
+        return out
+
+    H = tick("hessian", lambda: O.hessian([X64]))
+    Hd, _ = tick("damp", lambda: O.damp_hessian(H, s.damp))
+    U = tick("factor", lambda: O.chol_inverse_upper(Hd))
+    g = tick("gptq", lambda: O.gptq(W[sel], U, s.bits, s.group_size, s.block_size, sym=sym))
+    rt = tick("rtn", lambda: O.rtn(W, s.bits, s.group_size, sym=sym))
+    tick("dequant", lambda: O.dequant(g["codes"], g["scales"], s.group_size, out_dtype=np.float16, zeros=g["zeros"]))
+    tick("mse", lambda: (O.recon_mse([X64], W[sel], g["What"]), O.recon_mse([X64], W[sel], rt["What"][sel])))
+    f_tok, f_row = s.n_tok / ntile, s.d_out / r
+    scale = {"hessian": f_tok, "damp": 1.0, "factor": 1.0, "gptq": f_row, "rtn": 1.0, "dequant": f_row,
+             "mse": f_tok * f_row}
+    layer_s = {k: t[k] * scale[k] for k in t}
+    total = sum(layer_s.values())
+    threads, model = _cpu_info()
+    return {"value": round(s.n_weights / total, 1), "unit": "weights/s", "cores": threads, "kind": "oracle",
+            "sample": (f"layer {s.name} ({s.d_in}->{s.d_out}), act-order off: float64 numpy oracle on "
+                       f"{ntile} of {s.n_tok} tokens and {r} of {s.d_out} rows (GPTQ, dequant, errors), factor "
+                       f"and RTN whole; token- and row-proportional steps scaled to the layer; "
+                       f"{sum(t.values()):.1f} s of CPU work"),
+            "cpu_model": model, "blas_threads": threads,
+            "sample_s": {k: round(v, 3) for k, v in t.items()},
+            "layer_s": {k: round(v, 2) for k, v in layer_s.items()},
+            "scale": {k: round(v, 3) for k, v in scale.items()}}
 
 
 def copy_calibration(torch):
@@ -351,31 +393,27 @@ def copy_calibration(torch):
                       "read_plus_write_GBps": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print("bench.py measures one GPU; runs on several GPUs are not supported (use --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    if a.copy_calibration:
-        copy_calibration(torch)
-        return
-    from post_weight_quantization_27_amd import pwq, synth
-    pwq.lib()
-    specs = synth.workload(a.workload)
-    if a.layers:
-        keep = set(a.layers.split(","))
-        specs = [s for s in specs if s.name in keep]
-    layers = [Layer(s, torch, pwq, synth, a.act_order, a.zero_point) for s in specs]
-    torch.cuda.synchronize()
+def kernel_traffic(workload, layer, cls):
+    """HBM bytes per launch of a kernel class from the committed counter summary, if it was
+    taken on the kernel sources as they are now (else None)."""
+    try:
+        from post_weight_quantization_27_amd import profile_summary
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            data = json.load(f)
+        e = data.get(f"{workload}/{layer}")
+        if not e or e.get("source_hash") != profile_summary.source_hash():
+            return None
+        k = e.get("per_kernel", {}).get(cls)
+        return None if not k or not k.get("launches") else k["hbm_bytes"] / k["launches"]
+    except (OSError, ValueError, KeyError):
+        return None
 
-    # layers are independent: each runs on its own stream (default priority), so the
-    # single-workgroup and few-workgroup kernels of one layer overlap with the others
-    main = torch.cuda.current_stream()
-    streams = [torch.cuda.Stream() for _ in layers] if a.streams else [main for _ in layers]
-    # the layer with the longest serial chain (largest d_in: most factor blocks) goes first
+
+def measure(a, layers, streams, main_stream, pwq, torch, act):
+    """Timed steps, per-call events and the per-kernel pass for one act-order setting."""
+    for L in layers:
+        L.act = act
     order = sorted(range(len(layers)), key=lambda i: -layers[i].spec.d_in)
-
     # The step is as long as its longest chain (the factor of the widest layer is a serial
     # sequence of small launches).  With staggering, that layer's Hessian runs alone, and
     # the other layers start once it is formed, so their large contractions overlap the
@@ -389,7 +427,7 @@ def main():
     def step(timers=None):
         for pos, i in enumerate(order):
             L, st = layers[i], streams[i]
-            st.wait_stream(main)
+            st.wait_stream(main_stream)
             if stagger and pos > 0:
                 st.wait_event(first_done)
             with torch.cuda.stream(st):
@@ -400,7 +438,7 @@ def main():
                 run_step(L, pwq, None if timers is None else timers[i], after_hessian=hook,
                          parts="gptq" if (side and pos == 0) else "all")
         for st in streams:
-            main.wait_stream(st)
+            main_stream.wait_stream(st)
 
     for _ in range(a.warmup):
         step()
@@ -424,9 +462,8 @@ def main():
     ms = e0.elapsed_time(e1) / a.steps
 
     # per-call durations: the same K steps again, on the same streams, with HIP events around
-    # every call on the stream it runs on (kept out of the first timed region, which gives the
-    # value, so the event records do not sit between its launches); a name's time per step is
-    # the sum over its calls in the step (recon_mse: the GPTQ and the RTN error)
+    # every call on the stream it runs on; a name's time per step is the sum over its calls in
+    # the step (recon_mse: the GPTQ and the RTN error)
     timers = [dict() for _ in layers]
     for _ in range(a.steps):
         step(timers)
@@ -434,62 +471,187 @@ def main():
     per = {}
     for L, T in zip(layers, timers):
         for name, ev in T.items():
-            d = sum(x[0].elapsed_time(x[1]) for x in ev) / a.steps
-            per[(L.spec.name, name)] = d
+            per[(L.spec.name, name)] = sum(x[0].elapsed_time(x[1]) for x in ev) / a.steps
+
+    # per-kernel durations: each layer alone on its stream, the library's events around its
+    # large kernels (the Hessian's contraction, the trailing updates, the column blocks)
+    kern = {}
+    for i, L in enumerate(layers):
+        with torch.cuda.stream(streams[i]):
+            pwq.profile_enable(True)
+            for _ in range(a.prof_reps):
+                run_step(L, pwq)
+            torch.cuda.synchronize()
+            got = pwq.profile_read()
+            pwq.profile_enable(False)
+        kern[L.spec.name] = {c: {"ms_per_step": v[0] / a.prof_reps, "work_per_step": v[1] / a.prof_reps,
+                                 "launches_per_step": v[2] / a.prof_reps} for c, v in got.items()}
+    return {"ms": ms, "wall": wall, "submit_ms": submit_ms, "per": per, "kern": kern, "stagger": stagger,
+            "side": side}
+
+
+def report(a, layers, m, zero_point):
+    """The measured figures of one act-order setting as JSON-ready objects."""
+    per, kern = m["per"], m["kern"]
+    specs = [L.spec for L in layers]
+    weights = sum(s.n_weights for s in specs)
     breakdown = {}
     for (lname, name), d in per.items():
         breakdown[name] = breakdown.get(name, 0.0) + d
-    # roofline of the dominant launch: the (layer, call) with the longest duration
-    (dl, dn), dms = max(per.items(), key=lambda kv: kv[1])
-    dspec = next(L.spec for L in layers if L.spec.name == dl)
-    bound, amount, unit = work_of(dn, dspec, a.zero_point)
-    achieved = amount / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
-    peak = PEAK[bound]
-    roof = {"bound": "hbm" if bound == "hbm" else "mfma", "kernel": f"pwq_{dn}", "layer": dl,
-            "kernels_per_call": launches_of(dn, dspec),
-            "achieved": round(achieved, 3), "peak": peak, "unit": "GB/s" if unit == "byte" else "TFLOP/s",
-            "frac": round(achieved / peak, 5), "traffic": None if a.zero_point else traffic_of(a.workload, dl, dn), "launch_ms": round(dms, 4),
-            "algorithmic": amount, "peak_kind": bound}
-    # the metric's X^T X MFMA utilisation, per layer
-    xtx = {}
-    for L in layers:
-        bnd, amt, _ = work_of("hessian_accumulate", L.spec)
-        d = per.get((L.spec.name, "hessian_accumulate"))
+    out = {"value": round(weights / (m["ms"] * 1e-3), 1), "ms_per_step": round(m["ms"], 4),
+           "wall_s_timed": round(m["wall"], 3), "host_submit_ms_per_step": round(m["submit_ms"], 3)}
+
+    # candidate kernels for the roofline: the profiled kernel classes per layer, and the calls
+    # that are a single kernel (RTN, dequant) with their HBM bytes
+    cands = []
+    for s in specs:
+        k = kern[s.name]
+        x = k["xtx"]
+        if x["launches_per_step"]:
+            pk = "mfma_bf16" if work_of("hessian_accumulate", s)[0] == "mfma_bf16" else "mfma_f32"
+            cands.append(("xtx", s, x["ms_per_step"], x["work_per_step"], x["launches_per_step"], pk, "flop"))
+        u = k["update"]
+        if u["launches_per_step"]:
+            cands.append(("update", s, u["ms_per_step"], u["work_per_step"], u["launches_per_step"], "mfma_f32",
+                          "flop"))
+        for call in ("rtn_quantize", "dequant"):
+            d = per.get((s.name, call))
+            if d:
+                b, amt, unit = work_of(call, s, zero_point)
+                cands.append((call, s, d, amt, 1, b, unit))
+    dom = max(cands, key=lambda c: c[2])
+    cls, s, dms, amt, nl, pk, unit = dom
+    achieved = amt / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
+    names = {"xtx": "gemm_dl_kernel<..., EpiHess> (pwq_hessian_accumulate's contraction)",
+             "update": "gemm_f32_kernel<..., EpiSub> (pwq_gptq_quantize_layer's trailing updates)",
+             "rtn_quantize": "pwq_rtn_quantize", "dequant": "pwq_dequant"}
+    traffic = None
+    if not zero_point and cls in ("xtx", "update"):
+        tb = kernel_traffic(a.workload, s.name, cls)
+        traffic = None if tb is None else tb * nl
+    elif not zero_point:
+        traffic = traffic_of(a.workload, s.name, cls)
+    out["roofline"] = {"bound": "hbm" if pk == "hbm" else "mfma", "kernel": names[cls], "layer": s.name,
+                       "achieved": round(achieved, 3), "peak": PEAK[pk],
+                       "unit": "GB/s" if unit == "byte" else "TFLOP/s", "frac": round(achieved / PEAK[pk], 5),
+                       "traffic": traffic, "launch_ms": round(dms / nl, 4), "launches_per_step": nl,
+                       "algorithmic": amt / nl, "peak_kind": pk}
+    # the metric's MFMA utilisations: X^T X (the kernel, and the whole call with its
+    # transposed copy) and the trailing update, per layer
+    xtx, xtx_call, upd, upd_detail, cols = {}, {}, {}, {}, {}
+    for s in specs:
+        k = kern[s.name]
+        pk = work_of("hessian_accumulate", s)[0]
+        if k["xtx"]["ms_per_step"]:
+            xtx[s.name] = round(k["xtx"]["work_per_step"] / (k["xtx"]["ms_per_step"] * 1e-3) / 1e12 / PEAK[pk], 4)
+        d = per.get((s.name, "hessian_accumulate"))
         if d:
-            xtx[L.spec.name] = round(amt / (d * 1e-3) / 1e12 / PEAK[bnd], 4)
-    mses = {L.spec.name: [float(x) for x in L.mse.cpu().tolist()] for L in layers}
+            xtx_call[s.name] = round(work_of("hessian_accumulate", s)[1] / (d * 1e-3) / 1e12 / PEAK[pk], 4)
+        u = k["update"]
+        if u["ms_per_step"]:
+            tf = u["work_per_step"] / (u["ms_per_step"] * 1e-3) / 1e12
+            upd[s.name] = round(tf / PEAK["mfma_f32"], 4)
+            alg = s.d_out * s.d_in * (s.d_in - s.block_size)
+            upd_detail[s.name] = {"ms": round(u["ms_per_step"], 3), "launches": u["launches_per_step"],
+                                  "flops": u["work_per_step"], "algorithmic_flops": alg, "TFLOP/s": round(tf, 2)}
+            tb = None if zero_point else kernel_traffic(a.workload, s.name, "update")
+            if tb is not None:
+                hb = tb * u["launches_per_step"]
+                # without lazy batching every column's error would be applied to all later
+                # columns of the float32 working copy at once: a read and a write of each
+                # (d_out x (d_in - j - 1)) slab, 8 d_out (d_in - j - 1) bytes for column j
+                per_col = 8.0 * s.d_out * s.d_in * (s.d_in - 1) / 2
+                upd_detail[s.name].update({"hbm_bytes": hb, "per_column_update_bytes": per_col,
+                                           "traffic_reduction": round(per_col / hb, 1)})
+        c = k["columns"]
+        if c["ms_per_step"]:
+            cols[s.name] = {"ms": round(c["ms_per_step"], 3), "launches": c["launches_per_step"]}
+    out["xtx_mfma_util"] = xtx
+    out["xtx_call_mfma_util"] = xtx_call
+    out["update_mfma_util"] = upd
+    out["update"] = upd_detail
+    out["column_blocks"] = cols
+    codec = {}
+    for s in specs:
+        for call in ("rtn_quantize", "dequant"):
+            d = per.get((s.name, call))
+            if d:
+                _, byt, _ = work_of(call, s, zero_point)
+                gbs = byt / (d * 1e-3) / 1e9
+                codec[f"{s.name}/{call}"] = {"us": round(d * 1e3, 1), "GB/s": round(gbs, 1),
+                                             "frac_hbm": round(gbs / PEAK["hbm"], 4)}
+    out["codec_hbm"] = codec
+    out["breakdown_ms"] = {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])}
+    out["breakdown_ms_by_layer"] = {f"{ln}/{nm}": round(v, 4) for (ln, nm), v in sorted(per.items(), key=lambda kv: -kv[1])}
+    out["mse_gptq_rtn"] = {L.spec.name: [float(x) for x in L.mse.cpu().tolist()] for L in layers}
+    return out
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU; runs on several GPUs are not supported (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if a.copy_calibration:
+        copy_calibration(torch)
+        return
+    from post_weight_quantization_27_amd import pwq, synth
+    pwq.lib()
+    specs = synth.workload(a.workload)
+    if a.layers:
+        keep = set(a.layers.split(","))
+        specs = [s for s in specs if s.name in keep]
+    settings = {"off": [False], "on": [True], "both": [False, True]}[a.act_order]
+    t_in = time.perf_counter()
+    layers = [Layer(s, torch, pwq, synth, settings[0], a.zero_point) for s in specs]
+    torch.cuda.synchronize()
+    print(f"inputs resident after {time.perf_counter() - t_in:.1f} s", file=sys.stderr, flush=True)
+
+    # layers are independent: each runs on its own stream (default priority), so the
+    # single-workgroup and few-workgroup kernels of one layer overlap with the others
+    main_stream = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in layers] if a.streams else [main_stream for _ in layers]
+
+    results = []
+    for act in settings:
+        m = measure(a, layers, streams, main_stream, pwq, torch, act)
+        results.append((act, m, report(a, layers, m, a.zero_point)))
+        print(f"act-order {'on' if act else 'off'}: {m['ms']:.3f} ms per step", file=sys.stderr, flush=True)
+    act0, m0, r0 = results[0]
     toks = [int(x) for x in a.matmul_tokens.split(",") if x.strip()]
     qmm = time_quantized_matmul(layers, pwq, torch, toks) if toks else {}
     pts = time_tensor_scales(layers, pwq, torch) if toks else {}
     awq = time_awq(layers, pwq, torch, a.awq_alphas) if a.awq_alphas > 0 else {}
 
-    weights = sum(s.n_weights for s in specs)
-    value = weights / (ms * 1e-3)
+    bf = specs[0].x_dtype == "bf16"
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "weights/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if specs[0].x_dtype == "f32" else "bf16-in/f32-acc",
+        "metric": METRIC, "value": r0["value"], "unit": "weights/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": r0["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ("bf16 X: bf16 MFMA with f32 accumulation (X^T X); f32 factor and GPTQ loop" if bf else
+                  "f32 X as bf16 hi/lo pairs on bf16 MFMA, f32 accumulation (X^T X); f32 factor and GPTQ loop"),
         "data": "synthetic",
         "config": {"workload": a.workload, "layers": [f"{s.name}:{s.d_in}->{s.d_out}" for s in specs],
                    "n_tok": specs[0].n_tok, "bits": specs[0].bits, "group_size": specs[0].group_size,
-                   "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": bool(a.act_order),
-                   "zero_point": bool(a.zero_point), "layer_streams": bool(a.streams), "stagger": stagger,
+                   "block_size": specs[0].block_size, "damp": specs[0].damp, "act_order": act0,
+                   "zero_point": bool(a.zero_point), "layer_streams": bool(a.streams), "stagger": m0["stagger"],
                    "mse_route": {L.spec.name: ("hessian" if L.mse_h else "tokens") for L in layers},
-                   "rtn_off_chain": side},
-        "roofline": roof,
-        "xtx_mfma_util": xtx,
-        "breakdown_ms": {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])},
-        "breakdown_ms_by_layer": {f"{ln}/{nm}": round(v, 4) for (ln, nm), v in sorted(per.items(), key=lambda kv: -kv[1])},
-        "mse_gptq_rtn": mses,
-        "quantized_matmul": qmm,
-        "tensor_scales": pts,
-        "awq": awq,
-        "wall_s_timed": round(wall, 3),
-        "host_submit_ms_per_step": round(submit_ms, 3),
+                   "rtn_off_chain": m0["side"]},
     }
+    for k, v in r0.items():
+        if k not in ("value", "ms_per_step"):
+            out[k] = v
+    for act, m, r in results[1:]:
+        out["act_order_on" if act else "act_order_off"] = r
+    out["quantized_matmul"] = qmm
+    out["tensor_scales"] = pts
+    out["awq"] = awq
+    # steps of the path each layer ran (for counter summaries): per setting, warm-up, one
+    # submit-timed step, K timed, K with per-call events, and the per-kernel pass
+    out["path_steps_run"] = len(settings) * (a.warmup + 1 + 2 * a.steps + a.prof_reps)
     if not a.no_cpu_baseline:
-        cl = set(a.cpu_layers.split(",")) if a.cpu_layers else set()
-        out["cpu_baseline"] = cpu_baseline(specs, synth, cl, a.zero_point)
+        out["cpu_baseline"] = cpu_baseline(specs, synth, a.cpu_layer, a.cpu_rows, a.zero_point)
     print(json.dumps(out), flush=True)
 
 

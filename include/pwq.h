@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PWQ_ABI_VERSION 3
+#define PWQ_ABI_VERSION 4
 
 typedef enum pwq_status {
     PWQ_OK = 0,
@@ -85,6 +85,36 @@ const char* pwq_status_string(int status);
 
 /* hipError_t of the last PWQ_EHIP on the calling thread (0 if none). */
 int pwq_last_hip_error(void);
+
+/* ------------------------------------------------------------------ kernel timing -----
+ * Opt-in timing of the path's large kernels, to measure each against its roofline: the
+ * Hessian's contraction, and GPTQ's lazily batched trailing updates and column blocks
+ * ([GPTQ-P] "The GPTQ Algorithm", block-wise processing: one batched update per block
+ * in place of one per column).  While enabled, every launch of a listed class records a
+ * pair of HIP events on the stream it runs on, with the launch's algorithmic work:
+ *   PWQ_PROF_XTX      the MFMA contraction of pwq_hessian_accumulate: n_tok d_in (d_in + 1)
+ *                     flops per call (the symmetric half of 2 n_tok d_in^2);
+ *   PWQ_PROF_UPDATE   the products W[:, c0:c1] -= Err U[rows, c0:c1] of
+ *                     pwq_gptq_quantize_layer(_zp): 2 d_out k (c1 - c0) flops each (k error
+ *                     columns); over a layer they sum to d_out d_in (d_in - B) when the
+ *                     kernel with four lanes per row runs (d_out > 4096);
+ *   PWQ_PROF_COLUMNS  the column-block kernels (quantize, error, in-block rank-1 updates):
+ *                     d_out B (B - 1) flops per block of B columns.
+ * The record is process-wide and guarded by a mutex.  The events add a little time
+ * between launches: time throughput with timing disabled.
+ *   pwq_profile_enable  nonzero starts recording (discarding anything unread), 0 stops.
+ *   pwq_profile_read    waits for the recorded events and writes, for classes
+ *                       0 .. n_classes - 1, the summed milliseconds, summed work and launch
+ *                       count into host arrays; clears the record.  PWQ_EINVAL for
+ *                       n_classes < 1 or a NULL array; PWQ_EHIP if an event failed. */
+typedef enum pwq_prof_class {
+    PWQ_PROF_XTX = 0,
+    PWQ_PROF_UPDATE = 1,
+    PWQ_PROF_COLUMNS = 2,
+    PWQ_PROF_CLASSES = 3
+} pwq_prof_class;
+pwq_status pwq_profile_enable(int on);
+pwq_status pwq_profile_read(double* ms, double* work, int64_t* launches, int n_classes);
 
 /* ------------------------------------------------------------------ Hessian -------
  * H += 2 * X^T X, summed over the n_tok tokens of this call ([GPTQ-P] "Hessian-Based

@@ -29,6 +29,7 @@
 //   finish   : act-order only: codes back to the original column order, nibble packing and
 //              g_idx.
 #include "gemm_f32.h"
+#include "../../include/pwq.h"
 #include "pwq_internal.h"
 
 namespace pwq {
@@ -690,8 +691,11 @@ hipError_t trailing(float* Wf, const float* err, int ld, const float* U, const i
 hipError_t update(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
                   int64_t kb0, int kw, int64_t c0, int64_t c1, hipStream_t s) {
     const int64_t big_tiles = cdiv(m, 128) * cdiv(c1 - c0, 128);
-    return big_tiles >= 512 ? trailing<128, 128>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
-                            : trailing<64, 64>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s);
+    prof_begin(PWQ_PROF_UPDATE, s);
+    const hipError_t e = big_tiles >= 512 ? trailing<128, 128>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
+                                          : trailing<64, 64>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s);
+    prof_end(PWQ_PROF_UPDATE, s, 2.0 * m * kw * (c1 - c0));
+    return e;
 }
 
 }  // namespace
@@ -761,6 +765,7 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
         // themselves; the quad kernel's block receives it from a product after each block
         a.pend = quad ? 0 : (int)(b0 - s0);
         a.err_sb = err;
+        prof_begin(PWQ_PROF_COLUMNS, s);
         if (quad) {
             if (block_size == 128) hipLaunchKernelGGL((gptq_block_kernel<128, 8>), dim3(nblk), dim3(512), 0, s, a);
             else if (block_size == 64) hipLaunchKernelGGL((gptq_block_kernel<64, 8>), dim3(nblk), dim3(512), 0, s, a);
@@ -774,6 +779,7 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
             else if (block_size == 64) hipLaunchKernelGGL((gptq_row_kernel<64, 16>), dim3(nblk), dim3(1024), 0, s, a);
             else hipLaunchKernelGGL((gptq_row_kernel<32, 16>), dim3(nblk), dim3(1024), 0, s, a);
         }
+        prof_end(PWQ_PROF_COLUMNS, s, (double)m * bw * (bw - 1));
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int64_t b1 = b0 + bw;
         if (b1 < s1) {                     // the rest of the super-block, from this block's errors

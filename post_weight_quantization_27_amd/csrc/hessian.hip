@@ -11,6 +11,7 @@
 // tiles land in a workspace and are summed in a fixed order (bit-reproducible, no
 // atomics).  A last pass copies the upper triangle onto the lower one.
 #include "gemm_bf16_dl.h"
+#include "../../include/pwq.h"
 #include "pwq_internal.h"
 
 namespace pwq {
@@ -135,8 +136,10 @@ hipError_t hess_gemm_bf16(const void* X, int64_t n_tok, int64_t n, int64_t ldx, 
     UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, 128};
+    prof_begin(PWQ_PROF_XTX, s);
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, Bf16Cols, Bf16Cols, UpperMap, EpiHess>),
                        dim3(pl.full + (ntile - pl.full) * pl.splits), dim3(GEMM_THREADS), 0, s, a, b, map, epi);
+    prof_end(PWQ_PROF_XTX, s, (double)n_tok * n * (n + 1));
     return hipGetLastError();
 }
 
@@ -248,8 +251,10 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
     UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, 1};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
     const int nwg = hess_dl_grid(pl, ntile);
+    prof_begin(PWQ_PROF_XTX, s);
     hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
+    prof_end(PWQ_PROF_XTX, s, (double)n_tok * n * (n + 1));
     return hipGetLastError();
 }
 
@@ -271,8 +276,10 @@ hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, f
     UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, 1};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
     const int nwg = hess_dl_grid(pl, ntile);
+    prof_begin(PWQ_PROF_XTX, s);
     hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, a, b, map, epi);
+    prof_end(PWQ_PROF_XTX, s, (double)n_tok * n * (n + 1));
     return hipGetLastError();
 }
 
@@ -284,8 +291,10 @@ hipError_t hess_gemm(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float
     UpperMap map{n, n_tok, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, BM};
+    prof_begin(PWQ_PROF_XTX, s);
     hipLaunchKernelGGL((gemm_f32_kernel<BM, BM, OpKMajor<DT>, OpKMajor<DT>, UpperMap, EpiHess>),
                        dim3(pl.full + (ntile - pl.full) * pl.splits), dim3(GEMM_THREADS), 0, s, op, op, map, epi);
+    prof_end(PWQ_PROF_XTX, s, (double)n_tok * n * (n + 1));
     return hipGetLastError();
 }
 

@@ -2,6 +2,10 @@
 // Every check runs before the first HIP call, so a rejected call enqueues nothing.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 #include "../../include/pwq.h"
 #include "pwq_internal.h"
 
@@ -28,9 +32,102 @@ bool group_ok(int32_t g, int64_t d_in) {
 
 int64_t n_groups(int64_t d_in, int32_t g) { return g == 0 ? 1 : cdiv(d_in, g); }
 
+// ------------------------------------------------------------------ kernel timing
+struct ProfRec {
+    int cls;
+    hipEvent_t a, b;
+    double work;
+};
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof_recs;          // recorded, not yet read
+std::vector<hipEvent_t> g_prof_pool;       // events free for reuse
+thread_local hipEvent_t t_prof_open[PWQ_PROF_CLASSES] = {};
+
+hipEvent_t prof_event() {                  // g_prof_mu held
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
+
+void prof_recycle() {                      // g_prof_mu held
+    for (auto& r : g_prof_recs) {
+        g_prof_pool.push_back(r.a);
+        g_prof_pool.push_back(r.b);
+    }
+    g_prof_recs.clear();
+}
+
 }  // namespace
 
+namespace pwq {
+
+void prof_begin(int cls, hipStream_t s) {
+    if (!g_prof_on.load(std::memory_order_relaxed) || cls < 0 || cls >= PWQ_PROF_CLASSES) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t e = prof_event();
+    if (e && hipEventRecord(e, s) != hipSuccess) {
+        g_prof_pool.push_back(e);
+        e = nullptr;
+    }
+    t_prof_open[cls] = e;
+}
+
+void prof_end(int cls, hipStream_t s, double work) {
+    if (!g_prof_on.load(std::memory_order_relaxed) || cls < 0 || cls >= PWQ_PROF_CLASSES) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t a = t_prof_open[cls];
+    t_prof_open[cls] = nullptr;
+    if (!a) return;
+    hipEvent_t b = prof_event();
+    if (!b || hipEventRecord(b, s) != hipSuccess) {
+        g_prof_pool.push_back(a);
+        if (b) g_prof_pool.push_back(b);
+        return;
+    }
+    g_prof_recs.push_back({cls, a, b, work});
+}
+
+}  // namespace pwq
+
 extern "C" {
+
+pwq_status pwq_profile_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    prof_recycle();
+    g_prof_on.store(on != 0);
+    return PWQ_OK;
+}
+
+pwq_status pwq_profile_read(double* ms, double* work, int64_t* launches, int n_classes) {
+    if (n_classes < 1 || !ms || !work || !launches) return PWQ_EINVAL;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (int c = 0; c < n_classes; ++c) {
+        ms[c] = 0.0;
+        work[c] = 0.0;
+        launches[c] = 0;
+    }
+    hipError_t err = hipSuccess;
+    for (const auto& r : g_prof_recs) {
+        if (r.cls >= n_classes) continue;
+        float t = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+        if (e != hipSuccess) {
+            err = e;
+            continue;
+        }
+        ms[r.cls] += t;
+        work[r.cls] += r.work;
+        launches[r.cls] += 1;
+    }
+    prof_recycle();
+    return hip_status(err);
+}
 
 int pwq_version(void) { return PWQ_ABI_VERSION; }
 

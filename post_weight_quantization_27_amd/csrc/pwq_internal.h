@@ -11,6 +11,11 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Opt-in kernel timing (pwq_profile_enable): events around one launch of a class, with its
+// algorithmic work; no-ops while timing is off.
+void prof_begin(int cls, hipStream_t s);
+void prof_end(int cls, hipStream_t s, double work);
+
 // Hessian build: H += 2 X^T X (float32 MFMA, upper tiles, deterministic split-K, mirror).
 struct HessPlan {
     int bm;            // tile edge (64, 128, or 256 on the direct-load engine)

@@ -74,6 +74,9 @@ _SIGS = {
     "pwq_recon_mse_hessian": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, ctypes.c_int, _i64,
                                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
                                              _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "pwq_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "pwq_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int]),
     "pwq_recon_mse_workspace_size": (_sz, [_i64, _i64, _i64]),
     "pwq_recon_mse": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, ctypes.c_int, _i64,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _c_void_p,
@@ -456,3 +459,21 @@ def gptq_layer(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group_size: int 
     res = q(W, U, info, bits, group_size, block_size, perm=perm, want_codes=want_codes, want_packed=want_packed)
     res.update({"H": H, "lambda": lam, "U": U, "info": info, "perm": perm})
     return res
+
+
+# ------------------------------------------------------------------ kernel timing
+PROF_CLASSES = ("xtx", "update", "columns")
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (or stop) recording HIP events around the library's large kernels."""
+    _check("pwq_profile_enable", lib().pwq_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{class: (milliseconds, algorithmic work, launches)} summed since profile_enable; clears the record."""
+    n = len(PROF_CLASSES)
+    ms, work, cnt = (ctypes.c_double * n)(), (ctypes.c_double * n)(), (ctypes.c_int64 * n)()
+    _check("pwq_profile_read", lib().pwq_profile_read(ms, work, cnt, n))
+    return {c: (ms[i], work[i], int(cnt[i])) for i, c in enumerate(PROF_CLASSES)}
+

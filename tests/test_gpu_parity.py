@@ -545,97 +545,3 @@ def test_workload_layer_end_to_end(pwq, wl, layer):
     assert abs(hr - want["rtn_mse"]) <= 1e-4 * want["rtn_mse"]
     assert abs(hg - mse_g) <= 1e-4 * mse_g
     print(f"{layer}: agreement {agree:.6f} mse rtn {mse_r:.5g} gptq {mse_g:.5g} (oracle {want['gptq_mse']:.5g})")
-
-
-# =============================================================================== full-size 1.3B / 70B layers
-# At these sizes the float64 oracle cannot run the layer end to end inside a test (the 70B
-# Hessian alone is 1.8e13 multiply-adds), so each step is checked on sampled outputs it can
-# compute one by one, or through properties that hold at any size.
-FULL_CASES = [("llama70b", "q_proj", False), ("llama70b", "q_proj", True), ("gpt2_1p3b", "h0.qkv", False)]
-
-
-@pytest.mark.parametrize("wl,layer,act", FULL_CASES)
-def test_full_size_layer(pwq, wl, layer, act):
-    spec = synth.layer(wl, layer)
-    n, m, N, g = spec.d_in, spec.d_out, spec.n_tok, spec.group_size
-    W = synth.weight(spec)
-    X = synth.x_full(spec, threads=16)
-    Wd, Xd = dev(W), dev_bf16(X)
-
-    # Hessian: sampled entries against float64 sums over all tokens, outlier channels included
-    H = torch.zeros((n, n), dtype=torch.float32, device=DEV)
-    pwq.hessian_accumulate(Xd, H)
-    assert torch.equal(H, H.T)
-    rng = np.random.default_rng(7)
-    outl = synth.outlier_channels(spec)
-    ii = np.concatenate([rng.integers(0, n, 40), outl[:4], outl[:4]])
-    jj = np.concatenate([rng.integers(0, n, 40), rng.integers(0, n, 4), outl[4:8]])
-    cols = np.unique(np.concatenate([ii, jj]))
-    Xc = synth.as_f64(X[:, cols], synth.BF16)
-    pos = {c: k for k, c in enumerate(cols)}
-    Hh = host(H)
-    for i, j in zip(ii, jj):
-        want = 2.0 * float(Xc[:, pos[i]] @ Xc[:, pos[j]])
-        scale = 2.0 * np.sqrt(float(Xc[:, pos[i]] @ Xc[:, pos[i]]) * float(Xc[:, pos[j]] @ Xc[:, pos[j]]))
-        assert abs(float(Hh[i, j]) - want) <= 1e-5 * scale, (i, j, Hh[i, j], want)
-
-    # damping: every diagonal entry moved by the same float32 lambda = damp * mean(diag)
-    Hd = H.clone()
-    lam = torch.zeros(1, dtype=torch.float32, device=DEV)
-    pwq.hessian_damp(Hd, spec.damp, lambda_out=lam)
-    lam_h = float(host(lam)[0])
-    assert abs(lam_h - spec.damp * float(np.mean(np.diag(Hh).astype(np.float64)))) <= 1e-6 * lam_h
-    dd = host(torch.diagonal(Hd))
-    assert np.array_equal(dd, (np.diag(Hh) + np.float32(lam_h)).astype(np.float32))
-
-    perm = None
-    if act:
-        perm = pwq.act_order_perm(Hd)
-        _check_desc_stable(host(perm), dd)
-
-    # factor: upper, positive diagonal, U^T U Hp e_j = e_j on sampled columns (float64 check)
-    U, info = pwq.chol_inverse_upper(Hd, perm)
-    assert int(host(info)[0]) == 0
-    assert torch.count_nonzero(torch.tril(U, -1)).item() == 0
-    assert torch.all(torch.diagonal(U) > 0).item()
-    Hp = Hd if perm is None else Hd[perm.long()][:, perm.long()]
-    js = torch.tensor(rng.integers(0, n, 8), device=DEV)
-    U64 = U.double()
-    Z = U64.T @ (U64 @ Hp[:, js].double())
-    E = torch.zeros_like(Z)
-    E[js, torch.arange(8, device=DEV)] = 1.0
-    resid = (Z - E).abs().max().item()
-    print(f"{layer} act={act}: max |U^T U H e_j - e_j| = {resid:.3g}")
-    assert resid <= 5e-3
-    del U64, Z
-
-    # GPTQ: code range, packed bytes = nibbles of the codes, g_idx of the permutation
-    res = pwq.gptq_quantize_layer(Wd, U, info, spec.bits, g, spec.block_size, perm=perm)
-    codes = host(res["codes"])
-    assert codes.min() >= -7 and codes.max() <= 7
-    assert np.array_equal(host(res["packed"]), O.pack_int4(codes))
-    sc = host(res["scales"]).astype(np.float32)
-    assert np.all(np.isfinite(sc)) and np.all(sc > 0)
-    if act:
-        p = host(perm)
-        gi = np.empty(n, dtype=np.int64)
-        gi[p] = np.arange(n) // g
-        assert np.array_equal(host(res["g_idx"]), gi)
-
-    # RTN over the whole layer against the oracle, bit for bit
-    r = pwq.rtn_quantize(Wd, spec.bits, g)
-    want_r = O.rtn(W, spec.bits, g)
-    assert np.array_equal(host(r["codes"]), want_r["codes"])
-    assert np.array_equal(host(r["scales"]), want_r["scales"])
-
-    # MSE: the GPU value equals tr(dW X^T X dW^T) / (N m) with the undamped Hessian (float64 on
-    # the GPU as the check), and GPTQ's error is below RTN's
-    gi_d = res.get("g_idx")
-    mse_g = float(host(pwq.recon_mse(Xd, Wd, res["scales"], spec.bits, g, packed=res["packed"], g_idx=gi_d))[0])
-    mse_r = float(host(pwq.recon_mse(Xd, Wd, r["scales"], spec.bits, g, packed=r["packed"]))[0])
-    What = pwq.dequant(res["scales"], n, spec.bits, g, packed=res["packed"], g_idx=gi_d, out_dtype=torch.float32)
-    dW = Wd.double() - What.double()
-    tr = float(((dW @ (H.double() / 2.0)) * dW).sum().item()) / (N * m)
-    print(f"{layer} act={act}: mse gptq {mse_g:.6g} (trace {tr:.6g}) rtn {mse_r:.6g}")
-    assert abs(mse_g - tr) <= 1e-4 * tr
-    assert mse_g < mse_r
