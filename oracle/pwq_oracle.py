@@ -208,6 +208,17 @@ def quantize_codes_asym(w: np.ndarray, s16: np.ndarray, z: np.ndarray, bits: int
     return q.astype(np.uint8)
 
 
+def _pre_scale(vals: np.ndarray, bits: int, sym: bool) -> np.ndarray:
+    """The float32 quotient a group's stored scale rounds to float16 (R7, A2), float64."""
+    if sym:
+        a32 = np.max(np.abs(vals), axis=1).astype(np.float32)
+        return (a32 / np.float32(qmax(bits))).astype(np.float32).astype(np.float64)
+    lo32 = np.minimum(np.min(vals, axis=1), 0.0).astype(np.float32)
+    hi32 = np.maximum(np.max(vals, axis=1), 0.0).astype(np.float32)
+    span = (hi32 - lo32).astype(np.float32)
+    return (span / np.float32((1 << bits) - 1)).astype(np.float32).astype(np.float64)
+
+
 def _group_params(vals: np.ndarray, bits: int, sym: bool):
     """Per-row quantizer of a group from its current values (rows x columns): the
     symmetric scale (R7), or the zero-point pair of A1-A3."""
@@ -369,7 +380,9 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
     distance of the exact quotient (plus the zero) from the rounding boundary between the
     two codes, in units of the scale (0 at an exact tie).  ``forced_scales`` (and
     ``forced_zeros``) likewise replace each group's quantizer once this function has taken
-    its own and recorded how far apart the two are.  The arithmetic is otherwise unchanged;
+    its own and recorded how far apart the two are (float16 ulps, and for a differing scale
+    the relative distance of its float32 quotient from the float16 rounding boundary between
+    the two).  The arithmetic is otherwise unchanged;
     it checks that the other run decided like this one given the same history.
 
     Rows are independent (each row has its own scales and sees the same U), so a subset of
@@ -390,7 +403,7 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
     forced = None
     if forced_codes is not None:
         forced = {"count": 0, "max_distance": 0.0, "max_step": 0, "groups": 0, "scale_mismatch": 0,
-                  "scale_max_ulp": 0, "zero_mismatch": 0, "zero_max_step": 0}
+                  "scale_max_ulp": 0, "scale_max_distance": 0.0, "zero_mismatch": 0, "zero_max_step": 0}
     for b0 in range(0, n, B):
         b1 = min(b0 + B, n)
         cur = _current(Wp, E, U, b0, b0, b1)            # every earlier block's errors, one product
@@ -405,6 +418,14 @@ def gptq(W: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128, blo
                     forced["groups"] += m
                     forced["scale_mismatch"] += int((d != 0).sum())
                     forced["scale_max_ulp"] = max(forced["scale_max_ulp"], int(d.max()))
+                    if (d != 0).any():
+                        # relative distance of this function's float32 quotient from the float16
+                        # rounding boundary between the two scales (their midpoint when they are
+                        # neighbours)
+                        pre = _pre_scale(vals[d != 0], bits, sym)
+                        mid = 0.5 * (fs[d != 0].astype(np.float64) + sG[d != 0].astype(np.float64))
+                        forced["scale_max_distance"] = max(forced["scale_max_distance"],
+                                                           float(np.max(np.abs(pre - mid) / mid)))
                     sG = fs
                     if not sym and forced_zeros is not None:
                         fz = np.asarray(forced_zeros).astype(np.int64).reshape(m, ng)[:, G]
