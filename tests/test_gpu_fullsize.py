@@ -263,9 +263,11 @@ def test_gptq_sampled_rows(case):
     agree = float(np.mean(d == 0))
     sc = host(case.res["scales"])[rows]
     sd = np.abs(sc.view(np.uint16).astype(np.int32) - want["scales"].view(np.uint16).astype(np.int32))
-    log(f"{s.name}: codes agree {agree:.6f} (max diff {d.max()}), scales equal {np.mean(sd == 0):.5f}")
+    log(f"{s.name}: codes agree {agree:.6f} (max diff {d.max()}), scales equal {np.mean(sd == 0):.5f} "
+        f"(max {sd.max()} float16 ulps)")
+    # free running, a flipped near-tie code moves the rest of its row, so a later group's scale
+    # may differ by a few ulps: scales are checked decision by decision, in the replay below
     assert d.max() <= 1 and agree >= 0.999
-    assert sd.max() <= 1
     assert np.array_equal(host(case.res["packed"])[rows], O.pack_int4(codes))
     if case.act:
         assert np.array_equal(host(case.res["g_idx"]), want["g_idx"])
