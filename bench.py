@@ -475,19 +475,23 @@ def measure(a, layers, streams, main_stream, pwq, torch, act):
 
     # per-kernel durations: each layer alone on its stream, the library's events around its
     # large kernels (the Hessian's contraction, the trailing updates, the column blocks)
-    kern = {}
+    # large kernels, with per-call events as well (each call's duration uncontended)
+    kern, alone = {}, {}
     for i, L in enumerate(layers):
+        T = {}
         with torch.cuda.stream(streams[i]):
             pwq.profile_enable(True)
             for _ in range(a.prof_reps):
-                run_step(L, pwq)
+                run_step(L, pwq, T)
             torch.cuda.synchronize()
             got = pwq.profile_read()
             pwq.profile_enable(False)
         kern[L.spec.name] = {c: {"ms_per_step": v[0] / a.prof_reps, "work_per_step": v[1] / a.prof_reps,
                                  "launches_per_step": v[2] / a.prof_reps} for c, v in got.items()}
-    return {"ms": ms, "wall": wall, "submit_ms": submit_ms, "per": per, "kern": kern, "stagger": stagger,
-            "side": side}
+        for name, ev in T.items():
+            alone[(L.spec.name, name)] = sum(x[0].elapsed_time(x[1]) for x in ev) / a.prof_reps
+    return {"ms": ms, "wall": wall, "submit_ms": submit_ms, "per": per, "kern": kern, "alone": alone,
+            "stagger": stagger, "side": side}
 
 
 def report(a, layers, m, zero_point):
@@ -515,7 +519,7 @@ def report(a, layers, m, zero_point):
             cands.append(("update", s, u["ms_per_step"], u["work_per_step"], u["launches_per_step"], "mfma_f32",
                           "flop"))
         for call in ("rtn_quantize", "dequant"):
-            d = per.get((s.name, call))
+            d = m["alone"].get((s.name, call))
             if d:
                 b, amt, unit = work_of(call, s, zero_point)
                 cands.append((call, s, d, amt, 1, b, unit))
@@ -571,10 +575,11 @@ def report(a, layers, m, zero_point):
     out["update_mfma_util"] = upd
     out["update"] = upd_detail
     out["column_blocks"] = cols
+    alone = m["alone"]
     codec = {}
     for s in specs:
         for call in ("rtn_quantize", "dequant"):
-            d = per.get((s.name, call))
+            d = alone.get((s.name, call))
             if d:
                 _, byt, _ = work_of(call, s, zero_point)
                 gbs = byt / (d * 1e-3) / 1e9
@@ -583,6 +588,10 @@ def report(a, layers, m, zero_point):
     out["codec_hbm"] = codec
     out["breakdown_ms"] = {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])}
     out["breakdown_ms_by_layer"] = {f"{ln}/{nm}": round(v, 4) for (ln, nm), v in sorted(per.items(), key=lambda kv: -kv[1])}
+    # each layer alone on the GPU (the per-kernel pass): what the layer costs without the others
+    out["layer_ms_alone"] = {s.name: round(sum(v for (ln, _), v in alone.items() if ln == s.name), 3) for s in specs}
+    out["breakdown_ms_alone_by_layer"] = {f"{ln}/{nm}": round(v, 4)
+                                          for (ln, nm), v in sorted(alone.items(), key=lambda kv: -kv[1])}
     out["mse_gptq_rtn"] = {L.spec.name: [float(x) for x in L.mse.cpu().tolist()] for L in layers}
     return out
 

@@ -18,9 +18,10 @@ Usage (the CSV files are rocprofv3's ``--output-format csv`` results)::
     python -m post_weight_quantization_27_amd.profile_summary traffic FETCH.csv WRITE.csv \\
         CFETCH.csv CWRITE.csv --steps N --workload W --layer L --cmd "..." --out profiles/traffic.json
 
-N is the number of steps of the path the profiled run executed (bench.py runs warmup + 1 +
-2 x steps of them: warm-up, one step timed on the host, the timed steps, and the same number
-again with per-call events).
+N is the number of steps of the path the profiled run executed (bench.py prints it as
+``path_steps_run``).  Per-kernel entries (the classes of the library's timing record: the
+Hessian's contraction, the trailing updates, the column blocks) hold the summed bytes over
+every dispatch of the run and the dispatch count, so bytes per launch need no step count.
 """
 from __future__ import annotations
 
@@ -56,6 +57,17 @@ CALL_OF = [
     ("awq_", "awq_search"), ("EpiDot", "awq_search"),
     ("tensor_max", "tensor_scales"), ("tensor_scale", "tensor_scales"),
 ]
+
+
+# kernel-name fragments -> kernel class of the library's timing record (pwq_profile_read)
+CLASS_OF = [("EpiHess", "xtx"), ("EpiSub", "update"), ("gptq_block_kernel", "columns"), ("gptq_row_kernel", "columns")]
+
+
+def class_of(name: str):
+    for frag, cls in CLASS_OF:
+        if frag in name:
+            return cls
+    return None
 
 
 def call_of(name: str) -> str:
@@ -122,6 +134,17 @@ def _counter_sum(path: str) -> dict:
     return out
 
 
+def _class_sum(path: str):
+    """kernel class -> (summed counter value, dispatches)."""
+    val, cnt = defaultdict(float), defaultdict(int)
+    for r in csv.DictReader(open(path)):
+        c = class_of(r["Kernel_Name"])
+        if c:
+            val[c] += float(r["Counter_Value"])
+            cnt[c] += 1
+    return val, cnt
+
+
 def _copy_factor(path: str, nbytes: int) -> float:
     """bytes per counter unit, from the 1 GiB copy dispatches of the calibration run."""
     vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if "copyBuffer" in r["Kernel_Name"]]
@@ -138,12 +161,21 @@ def traffic(a) -> None:
     for c in sorted(set(fetch) | set(write)):
         calls[c] = {"fetch_bytes": fetch.get(c, 0.0) * ff / a.steps, "write_bytes": write.get(c, 0.0) * fw / a.steps}
         calls[c]["hbm_bytes"] = calls[c]["fetch_bytes"] + calls[c]["write_bytes"]
+    (kf, nf), (kw, nw) = _class_sum(a.fetch_csv), _class_sum(a.write_csv)
+    kernels = {}
+    for c in sorted(set(kf) | set(kw)):
+        kernels[c] = {"fetch_bytes": kf.get(c, 0.0) * ff, "write_bytes": kw.get(c, 0.0) * fw,
+                      "launches": nf.get(c, 0)}
+        kernels[c]["hbm_bytes"] = kernels[c]["fetch_bytes"] + kernels[c]["write_bytes"]
+        if nf.get(c, 0) != nw.get(c, 0):
+            raise SystemExit(f"{c}: {nf.get(c, 0)} dispatches in the FETCH run, {nw.get(c, 0)} in the WRITE run")
     data = {}
     if os.path.exists(a.out):
         data = json.load(open(a.out))
     data[f"{a.workload}/{a.layer}"] = {
         "command": a.cmd, "source_hash": source_hash(), "steps_run": a.steps,
-        "fetch_bytes_per_counter_unit": ff, "write_bytes_per_counter_unit": fw, "per_call": calls}
+        "fetch_bytes_per_counter_unit": ff, "write_bytes_per_counter_unit": fw, "per_call": calls,
+        "per_kernel": kernels}
     with open(a.out, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
 
