@@ -381,6 +381,26 @@ pwq_status pwq_quantized_matmul(const void* X, int x_dtype, int64_t n_tok, int64
                                 int64_t d_out, int32_t group_size, void* Y, int y_dtype, int64_t ldy,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* The same product for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Identical arguments and
+ * results to pwq_quantized_matmul, without the workspace: the column splits' partial sums go
+ * to a scratch array of PWQ_QMM_SCRATCH_BYTES that the library holds in device memory on
+ * every GPU it runs on, until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); its first call on a device looks up that device's
+ * copy of the array (hipGetSymbolAddress, with the device current).
+ *   Errors: as pwq_quantized_matmul; PWQ_EWORKSPACE when
+ *   pwq_quantized_matmul_workspace_size(n_tok, d_in, d_out) exceeds PWQ_QMM_SCRATCH_BYTES
+ *   (e.g. d_in = 28672, d_out = 8192 fits up to n_tok = 36; d_in = 8192, d_out = 28672 up
+ *   to 36 as well); PWQ_EHIP when the lookup fails.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ *   streams, or two threads) race and may return wrong sums.  Each call writes every
+ *   partial sum it later reads, so nothing needs clearing between calls. */
+#define PWQ_QMM_SCRATCH_BYTES ((size_t)32 << 20)
+pwq_status pwq_quantized_matmul_noalloc(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, int64_t ldx,
+                                        const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                                        int64_t d_out, int32_t group_size, void* Y, int y_dtype, int64_t ldy,
+                                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,8 @@ hipError_t awq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t 
 
 // Y = X What^T with the quantized weights (float16 X, decode regime).
 size_t w4a16_ws_bytes(int64_t T, int64_t n, int64_t m);
+// this device's copy of the allocation-free entry point's scratch array (looked up once per device)
+hipError_t w4a16_scratch(void** out);
 hipError_t w4a16_launch(const uint16_t* X, int64_t T, int64_t n, int64_t ldx, const uint8_t* packed,
                         const uint16_t* scales, const uint16_t* zeros, int64_t m, int group_size, void* Y,
                         int y_dtype, int64_t ldy, void* ws, hipStream_t s);

@@ -20,8 +20,16 @@
 //
 // The columns are split in pieces of at most 1024; the splits' partial sums go to the
 // workspace and one more pass adds them in split order (deterministic).
+#include <mutex>
+
+#include "../../include/pwq.h"
 #include "pwq_internal.h"
 #include "pwq_common.h"
+
+// Partial sums of the allocation-free entry point: one copy per GPU, held until the process
+// ends.  Host code never uses this name as an address (on the host it is a stand-in symbol);
+// it takes each device's address from hipGetSymbolAddress (w4a16_scratch below).
+static __device__ __align__(256) unsigned char scratch[PWQ_QMM_SCRATCH_BYTES];
 
 namespace pwq {
 
@@ -270,6 +278,29 @@ W4Plan w4_plan(int64_t T, int64_t n, int64_t m) {
 size_t w4a16_ws_bytes(int64_t T, int64_t n, int64_t m) {
     const W4Plan p = w4_plan(T, n, m);
     return p.splits > 1 ? (size_t)p.splits * (size_t)T * (size_t)m * sizeof(float) : 0;
+}
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t w4a16_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));     // this device is current
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t w4a16_launch(const uint16_t* X, int64_t T, int64_t n, int64_t ldx, const uint8_t* packed,

@@ -74,6 +74,8 @@ _SIGS = {
     "pwq_recon_mse_hessian": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, ctypes.c_int, _i64,
                                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
                                              _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "pwq_quantized_matmul_noalloc": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                                    _c_void_p, _i64, _i32, _c_void_p, ctypes.c_int, _i64, _c_void_p]),
     "pwq_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "pwq_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int]),
@@ -439,6 +441,20 @@ def quantized_matmul(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
     _check("pwq_quantized_matmul", lib().pwq_quantized_matmul(
         _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(packed), _p(scales), _p(zeros), d_out, group_size, _p(out),
         _dtype_code(out), ldy, _p(ws) if nb else None, nb, _stream(X)))
+    return out
+
+
+def quantized_matmul_noalloc(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, out: torch.Tensor,
+                             group_size: int = 128, zeros: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """quantized_matmul into a caller-given ``out`` through the allocation-free entry point
+    (the library's static scratch array holds the partial sums; nothing is allocated)."""
+    ldx = _rows(X, "X")
+    n_tok, d_in = X.shape
+    d_out = packed.shape[0]
+    ldy = _rows(out, "Y") if n_tok > 0 else d_out
+    _check("pwq_quantized_matmul_noalloc", lib().pwq_quantized_matmul_noalloc(
+        _p(X), _dtype_code(X), n_tok, d_in, ldx, _p(packed), _p(scales), _p(zeros), d_out, group_size, _p(out),
+        _dtype_code(out), ldy, _stream(X)))
     return out
 
 

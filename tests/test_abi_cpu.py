@@ -307,3 +307,17 @@ def test_profile_calls_on_the_host(L):
     assert L.pwq_profile_read(ms, work, cnt, 0) == 1
     assert L.pwq_profile_read(None, work, cnt, n) == 1
 
+
+def test_noalloc_product_rejects_on_the_host(L):
+    """The allocation-free product checks its arguments, and that the partial sums fit its
+    scratch array, before any HIP call."""
+    fake = ctypes.c_void_p(0x1000)            # 16-byte aligned, never dereferenced on these paths
+    f = L.pwq_quantized_matmul_noalloc
+    # 28 column splits x 4096 tokens x 8192 rows of float32 partial sums: far past the array
+    assert L.pwq_quantized_matmul_workspace_size(4096, 28672, 8192) > 32 << 20
+    assert f(fake, 1, 4096, 28672, 28672, fake, fake, None, 8192, 128, fake, 1, 8192, None) == 3
+    assert f(fake, 0, 4, 256, 256, fake, fake, None, 64, 128, fake, 1, 64, None) == 2      # float32 X
+    assert f(fake, 1, 4, 250, 256, fake, fake, None, 64, 128, fake, 1, 64, None) == 1      # d_in % 32
+    assert f(fake, 1, 4, 256, 256, fake, fake, None, 64, 64, fake, 1, 64, None) == 1       # group 64
+    assert f(None, 1, 4, 256, 256, fake, fake, None, 64, 128, fake, 1, 64, None) == 1
+    assert f(fake, 1, 0, 256, 256, fake, fake, None, 64, 128, fake, 1, 64, None) == 0      # empty
