@@ -42,7 +42,11 @@ def parse():
     ap.add_argument("--act-order", choices=("off", "on", "both"), default="both",
                     help="act-order off, on, or both (the line's value is the first; 'both' adds an act_order_on object)")
     ap.add_argument("--zero-point", action="store_true", help="the asymmetric form (a scale and a zero per group)")
-    ap.add_argument("--streams", type=int, default=1, help="1: one stream per layer (default), 0: all on one stream")
+    ap.add_argument("--streams", type=int, default=-1,
+                    help="1: one stream per layer, 0: all on one stream, -1 (default): one stream per layer when every "
+                         "layer has fewer than 4096 inputs (their factors are chains of small launches that other "
+                         "layers' work can fill), else one stream (every step then fills the GPU by itself, and "
+                         "sharing it only slows the longest chain)")
     ap.add_argument("--stagger", type=int, default=1,
                     help="1: the layer with the longest chain starts alone and the others once its Hessian is "
                          "formed (default), 0: all layers start together")
@@ -518,11 +522,10 @@ def report(a, layers, m, zero_point):
         if u["launches_per_step"]:
             cands.append(("update", s, u["ms_per_step"], u["work_per_step"], u["launches_per_step"], "mfma_f32",
                           "flop"))
-        for call in ("rtn_quantize", "dequant"):
-            d = m["alone"].get((s.name, call))
-            if d:
-                b, amt, unit = work_of(call, s, zero_point)
-                cands.append((call, s, d, amt, 1, b, unit))
+        for cls, call in (("rtn", "rtn_quantize"), ("dequant", "dequant")):
+            k = kern[s.name][cls]
+            if k["launches_per_step"]:
+                cands.append((call, s, k["ms_per_step"], k["work_per_step"], k["launches_per_step"], "hbm", "byte"))
     dom = max(cands, key=lambda c: c[2])
     cls, s, dms, amt, nl, pk, unit = dom
     achieved = amt / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
@@ -578,13 +581,14 @@ def report(a, layers, m, zero_point):
     alone = m["alone"]
     codec = {}
     for s in specs:
-        for call in ("rtn_quantize", "dequant"):
-            d = alone.get((s.name, call))
-            if d:
-                _, byt, _ = work_of(call, s, zero_point)
-                gbs = byt / (d * 1e-3) / 1e9
-                codec[f"{s.name}/{call}"] = {"us": round(d * 1e3, 1), "GB/s": round(gbs, 1),
-                                             "frac_hbm": round(gbs / PEAK["hbm"], 4)}
+        for cls, call in (("rtn", "rtn_quantize"), ("dequant", "dequant")):
+            k = kern[s.name][cls]
+            if k["launches_per_step"]:
+                ms_k = k["ms_per_step"] / k["launches_per_step"]
+                gbs = k["work_per_step"] / k["launches_per_step"] / (ms_k * 1e-3) / 1e9
+                codec[f"{s.name}/{call}"] = {"us": round(ms_k * 1e3, 1), "GB/s": round(gbs, 1),
+                                             "frac_hbm": round(gbs / PEAK["hbm"], 4),
+                                             "call_us": round(alone.get((s.name, call), 0.0) * 1e3, 1)}
     out["codec_hbm"] = codec
     out["breakdown_ms"] = {k: round(v, 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1])}
     out["breakdown_ms_by_layer"] = {f"{ln}/{nm}": round(v, 4) for (ln, nm), v in sorted(per.items(), key=lambda kv: -kv[1])}
@@ -612,6 +616,8 @@ def main():
         keep = set(a.layers.split(","))
         specs = [s for s in specs if s.name in keep]
     settings = {"off": [False], "on": [True], "both": [False, True]}[a.act_order]
+    if a.streams < 0:
+        a.streams = 1 if max(s.d_in for s in specs) < 4096 else 0
     t_in = time.perf_counter()
     layers = [Layer(s, torch, pwq, synth, settings[0], a.zero_point) for s in specs]
     torch.cuda.synchronize()

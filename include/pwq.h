@@ -99,7 +99,11 @@ int pwq_last_hip_error(void);
  *                     columns); over a layer they sum to d_out d_in (d_in - B) when the
  *                     kernel with four lanes per row runs (d_out > 4096);
  *   PWQ_PROF_COLUMNS  the column-block kernels (quantize, error, in-block rank-1 updates):
- *                     d_out B (B - 1) flops per block of B columns.
+ *                     d_out B (B - 1) flops per block of B columns;
+ *   PWQ_PROF_RTN      the kernel of pwq_rtn_quantize(_zp): the bytes it must move (W, the
+ *                     codes and nibbles asked for, the scales and zeros);
+ *   PWQ_PROF_DEQUANT  the kernel of pwq_dequant(_zp): nibbles or codes, scales and zeros,
+ *                     g_idx and the output, once each.
  * The record is process-wide and guarded by a mutex.  The events add a little time
  * between launches: time throughput with timing disabled.
  *   pwq_profile_enable  nonzero starts recording (discarding anything unread), 0 stops.
@@ -111,7 +115,9 @@ typedef enum pwq_prof_class {
     PWQ_PROF_XTX = 0,
     PWQ_PROF_UPDATE = 1,
     PWQ_PROF_COLUMNS = 2,
-    PWQ_PROF_CLASSES = 3
+    PWQ_PROF_RTN = 3,
+    PWQ_PROF_DEQUANT = 4,
+    PWQ_PROF_CLASSES = 5
 } pwq_prof_class;
 pwq_status pwq_profile_enable(int on);
 pwq_status pwq_profile_read(double* ms, double* work, int64_t* launches, int n_classes);

@@ -254,8 +254,15 @@ static pwq_status rtn_checked(const void* W, int w_dtype, int64_t d_out, int64_t
     if (packed && (bits != 4 || d_in % 2 != 0)) return PWQ_EINVAL;
     if (d_out == 0) return PWQ_OK;
     if (!W) return PWQ_EINVAL;
-    return hip_status(rtn_launch(W, w_dtype, d_out, d_in, ldw, bits, group_size, scales_in, codes, packed, scales_out,
-                                 (hipStream_t)stream, zeros_in, zeros_out));
+    // bytes the call must move: W once, the outputs once, fixed quantizers once
+    const double per_group = (zeros_out ? 4.0 : 2.0) * (double)d_out * (double)n_groups(d_in, group_size);
+    const double bytes = (double)d_out * d_in * (w_dtype == PWQ_F32 ? 4 : 2) + (codes ? (double)d_out * d_in : 0.0) +
+                         (packed ? (double)d_out * d_in / 2 : 0.0) + per_group * (scales_in ? 2 : 1);
+    prof_begin(PWQ_PROF_RTN, (hipStream_t)stream);
+    const hipError_t e = rtn_launch(W, w_dtype, d_out, d_in, ldw, bits, group_size, scales_in, codes, packed,
+                                    scales_out, (hipStream_t)stream, zeros_in, zeros_out);
+    prof_end(PWQ_PROF_RTN, (hipStream_t)stream, bytes);
+    return hip_status(e);
 }
 
 pwq_status pwq_rtn_quantize(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw, int32_t bits,
@@ -284,8 +291,14 @@ static pwq_status dequant_checked(const uint8_t* packed, const int8_t* codes, co
     if (packed && (bits != 4 || d_in % 2 != 0)) return PWQ_EINVAL;
     if (g_idx && group_size == 0) return PWQ_EINVAL;
     if (!scales || !W_out) return PWQ_EINVAL;
-    return hip_status(dequant_launch(packed, codes, scales, g_idx, d_out, d_in, bits, group_size, W_out, out_dtype,
-                                     (hipStream_t)stream, zeros));
+    const double bytes = (packed ? (double)d_out * d_in / 2 : (double)d_out * d_in) +
+                         (zeros ? 4.0 : 2.0) * (double)d_out * (double)n_groups(d_in, group_size) +
+                         (double)d_out * d_in * (out_dtype == PWQ_F32 ? 4 : 2) + (g_idx ? 4.0 * d_in : 0.0);
+    prof_begin(PWQ_PROF_DEQUANT, (hipStream_t)stream);
+    const hipError_t e = dequant_launch(packed, codes, scales, g_idx, d_out, d_in, bits, group_size, W_out, out_dtype,
+                                        (hipStream_t)stream, zeros);
+    prof_end(PWQ_PROF_DEQUANT, (hipStream_t)stream, bytes);
+    return hip_status(e);
 }
 
 pwq_status pwq_dequant(const uint8_t* packed, const int8_t* codes, const uint16_t* scales, const int32_t* g_idx,

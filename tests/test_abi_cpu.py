@@ -302,7 +302,7 @@ def test_profile_calls_on_the_host(L):
     got = pwq.profile_read()
     assert got == {c: (0.0, 0.0, 0) for c in pwq.PROF_CLASSES}
     assert L.pwq_profile_enable(0) == 0
-    n = 3
+    n = 5
     ms, work, cnt = (ctypes.c_double * n)(), (ctypes.c_double * n)(), (ctypes.c_int64 * n)()
     assert L.pwq_profile_read(ms, work, cnt, 0) == 1
     assert L.pwq_profile_read(None, work, cnt, n) == 1
