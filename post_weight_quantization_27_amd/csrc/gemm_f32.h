@@ -402,14 +402,36 @@ __device__ __forceinline__ void gemm_tile(const LA& la, const LB& lb, const Tile
         }
     }
 
+    if constexpr (EpiIsRmw<EPI>::value) {
+        // each row of accumulator blocks reads all its old values before writing any: FM
+        // memory latencies per tile instead of FM * FN
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int i = 0; i < FM; ++i) {
             const int64_t r0 = t.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
-            const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-            epi_block16(epi, t, acc[i][j], [&](int v) { return r0 + 8 * (v >> 2) + (v & 3); }, col);
+            float old[FN][16];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) old[j][v] = epi.old(t, r0 + 8 * (v >> 2) + (v & 3), col);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) epi.put(t, r0 + 8 * (v >> 2) + (v & 3), col, acc[i][j][v], old[j][v]);
+            }
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int64_t r0 = t.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
+                const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+                epi_block16(epi, t, acc[i][j], [&](int v) { return r0 + 8 * (v >> 2) + (v & 3); }, col);
+            }
+    }
 }
 
 template <int BM, int BN, class LA, class LB, class MAP, class EPI>
