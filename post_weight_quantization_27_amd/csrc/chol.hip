@@ -23,7 +23,7 @@
 // one per upper 32 x 32 tile, each forming the rows of P it needs from A and Z_kk.  From
 // n = 4096 on, updates are batched per super-block.
 // Every kernel reads `info` first and does nothing once a pivot has failed.
-#include "gemm_f32.h"
+#include "gemm_f32_dl.h"
 #include "pwq_internal.h"
 
 namespace pwq {
@@ -397,9 +397,14 @@ struct EpiStore {                 // out[row][col] = alpha * acc
 };
 
 struct EpiSyrk {                  // A[row][col] -= acc on the upper triangle of the leading N x N
-    static constexpr bool kRmw = true;
+    static constexpr bool kRmw = true, kFast = true;
     float* U;
     int64_t ld, N;
+    __device__ __forceinline__ bool whole(const Tile& t, int bm, int bn) const {
+        return t.m0 + bm - 1 <= t.n0 && t.n0 + bn <= N;
+    }
+    __device__ __forceinline__ float* at(int64_t row, int64_t col) const { return U + row * ld + col; }
+    __device__ __forceinline__ float combine(float o, float v) const { return o - v; }
     __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
         return (row <= col && col < N) ? U[row * ld + col] : 0.f;
     }
@@ -410,9 +415,14 @@ struct EpiSyrk {                  // A[row][col] -= acc on the upper triangle of
 };
 
 struct EpiSyrkRect {              // A[row][col0 + col] -= acc on the upper triangle (row <= col0 + col)
-    static constexpr bool kRmw = true;
+    static constexpr bool kRmw = true, kFast = true;
     float* U;                     // = A + col0
     int64_t ld, col0, N;
+    __device__ __forceinline__ bool whole(const Tile& t, int bm, int bn) const {
+        return t.m0 + bm - 1 <= col0 + t.n0 && t.n0 + bn <= N;
+    }
+    __device__ __forceinline__ float* at(int64_t row, int64_t col) const { return U + row * ld + col; }
+    __device__ __forceinline__ float combine(float o, float v) const { return o - v; }
     __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
         return (row <= col0 + col && col < N) ? U[row * ld + col] : 0.f;
     }
@@ -423,9 +433,14 @@ struct EpiSyrkRect {              // A[row][col0 + col] -= acc on the upper tria
 };
 
 struct EpiPush {                  // R[row][col] (+)= acc; the first `fresh` columns are overwritten
-    static constexpr bool kRmw = true;
+    static constexpr bool kRmw = true, kFast = true;
     float* out;
     int64_t ld, M, N, fresh;
+    __device__ __forceinline__ bool whole(const Tile& t, int bm, int bn) const {
+        return t.m0 + bm <= M && t.n0 + bn <= N && t.n0 >= fresh;
+    }
+    __device__ __forceinline__ float* at(int64_t row, int64_t col) const { return out + row * ld + col; }
+    __device__ __forceinline__ float combine(float o, float v) const { return o + v; }
     __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
         return (row < M && col < N && col >= fresh) ? out[row * ld + col] : 0.f;
     }
@@ -463,7 +478,10 @@ int ntiles(const UpperMap& m) { return m.tiles * (m.tiles + 1) / 2; }
 
 // Panels of a super-block: P holds the V columns of its chol_sb(n) blocks side by side (row
 // stride pld = chol_sb(n) * CHOL_NB, the workspace's width); block slot t at column t * CHOL_NB.
-constexpr int CHOL_SB = 4;
+constexpr int CHOL_SB = 8;
+// 256-tile rows x columns of the whole trailing matrix from which the direct-load engine takes
+// a far update (its tiles are four times as large, so fewer of them must still fill the chip)
+constexpr int64_t FAR_DL_MIN_TILES = 1024;
 constexpr int64_t CHOL_LAZY_N = 4096;            // batch the updates from this size on
 inline int chol_sb(int64_t n) { return n >= CHOL_LAZY_N ? CHOL_SB : 1; }
 
@@ -485,6 +503,33 @@ hipError_t launch_far(float* U, const float* P, int pld, int64_t n, int64_t s0, 
     pu.epi = EpiPush{U + s0, n, s0, n - s0, kf};
     const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
     hipLaunchKernelGGL((gemm_f32_dual_kernel<SyrkTask<T>, PushTask<T>>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy, pu, n1,
+                       info);
+    return hipGetLastError();
+}
+
+// launch_far on the direct-load engine (256 x 256 tiles): the same two products, for deep
+// super-blocks (kf a whole number of its stages) with every row 16-byte aligned
+typedef FdlTask<FdlRows, FdlRows, UpperMap, EpiSyrk> SyrkDlTask;
+typedef FdlTask<FdlRows, FdlCols, RectMap, EpiPush> PushDlTask;
+
+inline bool far_dl_ok(int64_t n, int64_t s0, int kf, int pld, int vu) {
+    return vu && n % 4 == 0 && pld % 4 == 0 && kf % FDL_BK == 0 && s0 > 0 &&
+           cdiv(s0, FDL_TILE) * cdiv(n, FDL_TILE) >= FAR_DL_MIN_TILES;
+}
+
+hipError_t launch_far_dl(float* U, const float* P, int pld, int64_t n, int64_t s0, int kf, int32_t* info, hipStream_t s) {
+    SyrkDlTask sy{};
+    sy.la = FdlRows{P, pld, s0};
+    sy.lb = sy.la;
+    sy.map = UpperMap{s0, kf, (int)cdiv(s0, FDL_TILE), 1, kf, nullptr};
+    sy.epi = EpiSyrk{U, n, s0};
+    PushDlTask pu{};
+    pu.la = FdlRows{P, pld, s0};
+    pu.lb = FdlCols{U + s0 * n + s0, n, n - s0};
+    pu.map = rect(FDL_TILE, FDL_TILE, s0, n - s0, kf);
+    pu.epi = EpiPush{U + s0, n, s0, n - s0, kf};
+    const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
+    hipLaunchKernelGGL((gemm_fdl_dual_kernel<SyrkDlTask, PushDlTask>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy, pu, n1,
                        info);
     return hipGetLastError();
 }
@@ -821,8 +866,9 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
             // super-block done: everything above and right of it, depth = its width
             const int kf = (int)((kb_lo + sb) * (int64_t)CHOL_NB < n ? sb * CHOL_NB : n - s0);
             const int64_t big = cdiv(s0, 128) * cdiv(n, 128);
-            e = big >= 512 ? launch_far<128>(U, P, pld, n, s0, kf, info, vu, s)
-                           : launch_far<64>(U, P, pld, n, s0, kf, info, vu, s);
+            e = far_dl_ok(n, s0, kf, pld, vu) ? launch_far_dl(U, P, pld, n, s0, kf, info, s)
+                : big >= 512                  ? launch_far<128>(U, P, pld, n, s0, kf, info, vu, s)
+                                              : launch_far<64>(U, P, pld, n, s0, kf, info, vu, s);
         }
         if (e != hipSuccess) return e;
     }

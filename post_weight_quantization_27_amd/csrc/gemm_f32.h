@@ -298,6 +298,104 @@ __device__ __forceinline__ void epi_block16(EPI& epi, const Tile& t, const f32x1
     }
 }
 
+// Read-modify-write epilogues may also declare `static constexpr bool kFast = true` and give
+//   bool whole(const Tile&, int BM, int BN) const : every element of the BM x BN tile is
+//       written, with no range or triangle test
+//   float* at(int64_t row, int64_t col) const     : an output element's address (row stride ld)
+//   float combine(float old, float v) const       : the value written over old
+template <class EPI, class = void>
+struct EpiIsFast { static constexpr bool value = false; };
+template <class EPI>
+struct EpiIsFast<EPI, decltype((void)EPI::kFast)> { static constexpr bool value = EPI::kFast; };
+
+// Raw buffer resource over a wave-uniform base, no range limit (gfx9 descriptor word 3)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const float* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, -1, 0x00020000);
+}
+
+// Read-modify-write epilogue of one wave's FM x FN accumulator blocks (32 x 32 MFMA layout:
+// lane l holds column c0 + 32 j + l % 32 and rows r0 + 32 i + 4 (l / 32) + 8 (v / 4) + v % 4),
+// r0 and c0 wave-uniform.  A whole tile of a fast epilogue goes through buffer loads and
+// stores off the wave's corner (per element one scalar row offset and an immediate column
+// offset, no 64-bit address arithmetic) and loads the old values of the next row of blocks
+// before it writes the current one (two buffers of FN x 16 registers): one memory latency
+// is exposed per tile, and nothing is tested per element.  Otherwise each row of blocks
+// reads all its old values before writing any: FM latencies per tile instead of FM * FN.
+template <int FM, int FN, class EPI>
+__device__ __forceinline__ void epi_rmw_wave(EPI& epi, const Tile& t, const f32x16 (&acc)[FM][FN], int64_t r0, int64_t c0,
+                                             int lane, bool whole) {
+    if constexpr (EpiIsFast<EPI>::value) {
+        if (whole) {
+            // element (i, j, v): lane offset vq[v % 4], scalar row offset (32 i + 8 (v / 4)) ld,
+            // immediate column offset 32 j
+            const int ld4 = (int)epi.ld * 4;
+            const __amdgpu_buffer_rsrc_t rs = wave_rsrc(epi.at(r0, c0));
+            const int vo = 4 * (lane >> 5) * ld4 + 4 * (lane & 31);
+            int vq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) vq[q] = vo + q * ld4;
+            float old[2][FN][16];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    old[0][j][v] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(rs, vq[v & 3] + 128 * j, 8 * (v >> 2) * ld4, 0));
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                if (i + 1 < FM) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            old[(i + 1) & 1][j][v] = __builtin_bit_cast(
+                                float, __builtin_amdgcn_raw_buffer_load_b32(rs, vq[v & 3] + 128 * j,
+                                                                            (32 * (i + 1) + 8 * (v >> 2)) * ld4, 0));
+                }
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __builtin_bit_cast(uint32_t, epi.combine(old[i & 1][j][v], acc[i][j][v])), rs,
+                            vq[v & 3] + 128 * j, (32 * i + 8 * (v >> 2)) * ld4, 0);
+            }
+            return;
+        }
+    }
+    const int64_t rl = r0 + 4 * (lane >> 5), cl = c0 + (lane & 31);
+    if constexpr (EpiIsFast<EPI>::value) {
+        // edge tiles of a fast epilogue: block by block, few registers
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                epi_block16(epi, t, acc[i][j], [&](int v) { return rl + 32 * i + 8 * (v >> 2) + (v & 3); }, cl + 32 * j);
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t rb = rl + 32 * i;
+            float old[FN][16];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) old[j][v] = epi.old(t, rb + 8 * (v >> 2) + (v & 3), cl + 32 * j);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    epi.put(t, rb + 8 * (v >> 2) + (v & 3), cl + 32 * j, acc[i][j][v], old[j][v]);
+        }
+    }
+}
+
+template <class EPI>
+__device__ __forceinline__ bool epi_whole(const EPI& epi, const Tile& t, int bm, int bn) {
+    if constexpr (EpiIsFast<EPI>::value) return epi.whole(t, bm, bn);
+    else return false;
+}
+
+
 // ---------------------------------------------------------------- the tile engine
 // Epilogue interface:
 //   __device__ void element(const Tile&, int64_t row, int64_t col, float v)  for every
@@ -403,25 +501,9 @@ __device__ __forceinline__ void gemm_tile(const LA& la, const LB& lb, const Tile
     }
 
     if constexpr (EpiIsRmw<EPI>::value) {
-        // each row of accumulator blocks reads all its old values before writing any: FM
-        // memory latencies per tile instead of FM * FN
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int64_t r0 = t.m0 + wm * (BM / 2) + i * 32 + 4 * (lane >> 5);
-            float old[FN][16];
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) old[j][v] = epi.old(t, r0 + 8 * (v >> 2) + (v & 3), col);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int64_t col = t.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) epi.put(t, r0 + 8 * (v >> 2) + (v & 3), col, acc[i][j][v], old[j][v]);
-            }
-        }
+        const int wu = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform corner for buffer addressing
+        epi_rmw_wave<FM, FN>(epi, t, acc, t.m0 + (wu & 1) * (BM / 2), t.n0 + (wu >> 1) * (BN / 2), lane,
+                             epi_whole(epi, t, BM, BN));
     } else {
 #pragma unroll
         for (int i = 0; i < FM; ++i)

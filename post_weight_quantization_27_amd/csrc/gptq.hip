@@ -28,7 +28,7 @@
 //              LAZY_COLS columns (float32 MFMA engine)
 //   finish   : act-order only: codes back to the original column order, nibble packing and
 //              g_idx.
-#include "gemm_f32.h"
+#include "gemm_f32_dl.h"
 #include "../../include/pwq.h"
 #include "pwq_internal.h"
 
@@ -39,12 +39,15 @@ namespace {
 constexpr int GB = 128;   // widest panel (block size)
 // Error panels are kept for a super-block of columns: a block updates only the columns left
 // in its super-block, and the columns past it get one product as deep as the super-block when
-// it is done (the lazy batching of the column loop, one level up).  512 columns, except that a
-// group wider than a block must start a super-block (its scale reads the columns past the
-// panel, which are current only at a super-block's start): then the super-block is the group
-// (up to 2048 columns; wider groups update every column after each block).
-inline int lazy_cols(int group_size, int block_size) {
-    if (group_size == 0 || group_size <= block_size) return 512;
+// it is done (the lazy batching of the column loop, one level up).  1024 columns for more than
+// 4096 rows (the read-modify-write of the columns past a super-block then costs half as much
+// per flop), else 512 (the row kernels apply the pending part of the super-block to their
+// block themselves); except that a group wider than a block must start a super-block (its
+// scale reads the columns past the panel, which are current only at a super-block's start):
+// then the super-block is the group (up to 2048 columns; wider groups update every column
+// after each block).
+inline int lazy_cols(int group_size, int block_size, int64_t m) {
+    if (group_size == 0 || group_size <= block_size) return m > 4096 ? 1024 : 512;
     return group_size <= 2048 ? group_size : block_size;
 }
 
@@ -628,9 +631,14 @@ __global__ __launch_bounds__(NWV * 64) void gptq_row_kernel(BlockArgs a) {
 
 // Wf[r][c0 + col] -= acc
 struct EpiSub {
-    static constexpr bool kRmw = true;
+    static constexpr bool kRmw = true, kFast = true;
     float* out;
     int64_t ld, M, N;
+    __device__ __forceinline__ bool whole(const Tile& t, int bm, int bn) const {
+        return t.m0 + bm <= M && t.n0 + bn <= N;
+    }
+    __device__ __forceinline__ float* at(int64_t row, int64_t col) const { return out + row * ld + col; }
+    __device__ __forceinline__ float combine(float o, float v) const { return o - v; }
     __device__ __forceinline__ float old(const Tile&, int64_t row, int64_t col) const {
         return (row < M && col < N) ? out[row * ld + col] : 0.f;
     }
@@ -688,12 +696,39 @@ hipError_t trailing(float* Wf, const float* err, int ld, const float* U, const i
     return hipGetLastError();
 }
 
+// The same product on the direct-load engine (256 x 256 tiles; kw a whole number of its
+// stages, 16-byte aligned rows)
+hipError_t trailing_dl(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
+                       int64_t kb0, int kw, int64_t c0, int64_t c1, hipStream_t s) {
+    const int64_t N = c1 - c0;
+    FdlRows a{err, ld, m};
+    FdlCols b{U + kb0 * n + c0, n, N};
+    RectMap mp{};
+    mp.M = m; mp.N = N; mp.K = kw;
+    mp.tiles_m = (int)cdiv(m, FDL_TILE);
+    mp.tiles_n = (int)cdiv(N, FDL_TILE);
+    mp.splits = 1;
+    mp.kchunk = kw;
+    mp.tri_k = 0;
+    mp.guard = info;
+    EpiSub ep{Wf + c0, n, m, N};
+    hipLaunchKernelGGL((gemm_fdl_kernel<FdlRows, FdlCols, RectMap, EpiSub>), dim3(mp.tiles_m * mp.tiles_n),
+                       dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
+    return hipGetLastError();
+}
+
+// 256-tiles from which the direct-load engine takes a trailing product
+constexpr int64_t TRAIL_DL_MIN_TILES = 512;
+
 hipError_t update(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
                   int64_t kb0, int kw, int64_t c0, int64_t c1, hipStream_t s) {
     const int64_t big_tiles = cdiv(m, 128) * cdiv(c1 - c0, 128);
+    const bool dl = kw % FDL_BK == 0 && ld % 4 == 0 && n % 4 == 0 && c0 % 4 == 0 && aligned(err, 16) &&
+                    aligned(U, 16) && cdiv(m, FDL_TILE) * cdiv(c1 - c0, FDL_TILE) >= TRAIL_DL_MIN_TILES;
     prof_begin(PWQ_PROF_UPDATE, s);
-    const hipError_t e = big_tiles >= 512 ? trailing<128, 128>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
-                                          : trailing<64, 64>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s);
+    const hipError_t e = dl                ? trailing_dl(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
+                         : big_tiles >= 512 ? trailing<128, 128>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
+                                            : trailing<64, 64>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s);
     prof_end(PWQ_PROF_UPDATE, s, 2.0 * m * kw * (c1 - c0));
     return e;
 }
@@ -704,7 +739,7 @@ GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int group_siz
     GptqWs w{};
     size_t off = 0;
     w.wf = off;    off = align_up(off + (size_t)d_out * d_in * sizeof(float), 256);
-    w.err = off;   off = align_up(off + (size_t)d_out * lazy_cols(group_size, block_size) * sizeof(float), 256);
+    w.err = off;   off = align_up(off + (size_t)d_out * lazy_cols(group_size, block_size, d_out) * sizeof(float), 256);
     w.codes = off; if (act_order) off = align_up(off + (size_t)d_out * d_in, 256);
     w.inv = off;   if (act_order) off = align_up(off + (size_t)d_in * sizeof(int32_t), 256);
     w.total = off;
@@ -718,7 +753,7 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
     if (m == 0 || n == 0) return hipSuccess;
     hipError_t e;
     const GptqWs L = gptq_ws_layout(m, n, block_size, group_size, act_order);
-    const int lz = lazy_cols(group_size, block_size);
+    const int lz = lazy_cols(group_size, block_size, m);
     char* base = (char*)ws;
     float* Wf = (float*)(base + L.wf);
     float* err = (float*)(base + L.err);
