@@ -143,19 +143,30 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-// Issue order of one half tile: MFMA, fragment read, eight times, then the last eight MFMAs.
-// With one wave per SIMD the order is what overlaps the reads with the matrix pipe; the
-// first MFMA of a half only waits for reads issued during the half before.
+// Issue order of one half tile (16 MFMAs): NV times one MFMA and one global copy, eight
+// times one MFMA and one fragment read, then the rest.  With one wave per SIMD the order is
+// what overlaps the copies and reads with the matrix pipe; the first MFMA of a half only
+// waits for reads issued during the half before.
+template <int NV>
 __device__ __forceinline__ void dl_interleave() {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if constexpr (NV < 8) __builtin_amdgcn_sched_group_barrier(0x008, 8 - NV, 0);
 }
 
-template <class LA, class LB, class EPI>
+// STEADY: every iteration issues the same eight copies per wave (past the last tile they
+// repeat it into a stage nothing reads any more) and waits the same way, and the copies go
+// out between the second half's MFMAs; measured faster for the long, uniform k ranges of
+// the Hessian, slower for the error products.
+template <bool STEADY, class LA, class LB, class EPI>
 __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const Tile& t, EPI& epi, uint16_t* lds) {
     constexpr int FM = 4, FN = 4;
     constexpr int AB = DL_TILE * DL_BK;                  // B's offset inside a stage
@@ -172,17 +183,18 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int64_t nk = (t.kend - t.kbeg) / DL_BK;        // host guarantees whole tiles
+    auto kof = [&](int64_t kt) { return t.kbeg + (kt < nk ? kt : nk - 1) * DL_BK; };
     // tiles 0 .. 2 into stages 0 .. 2 (eight load instructions per wave and tile)
 #pragma unroll
     for (int st = 0; st < DL_NS - 1; ++st)
-        if (st < nk) {
-            la.load(lds + st * DL_STAGE, t.m0, t.kbeg + st * DL_BK, wave, lane);
-            lb.load(lds + st * DL_STAGE + AB, t.n0, t.kbeg + st * DL_BK, wave, lane);
+        if (STEADY || st < nk) {
+            la.load(lds + st * DL_STAGE, t.m0, kof(st), wave, lane);
+            lb.load(lds + st * DL_STAGE + AB, t.n0, kof(st), wave, lane);
         }
     const int arow = wm * 128 + (lane & 31);
     const int brow = wn * 128 + (lane & 31);
     const int half = lane >> 5;
-    if (nk > 2) wait_vmcnt<16>();
+    if (STEADY || nk > 2) wait_vmcnt<16>();
     else if (nk == 2) wait_vmcnt<8>();
     else wait_vmcnt<0>();
     barrier_nofence();
@@ -203,8 +215,14 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-        dl_interleave();
-        if (it + 1 < nk) {
+        dl_interleave<0>();
+        if constexpr (STEADY) {
+            wait_vmcnt<8>();
+            barrier_nofence();
+            uint16_t* Sn = lds + ((it + 3) & 3) * DL_STAGE;
+            la.load(Sn, t.m0, kof(it + 3), wave, lane);
+            lb.load(Sn + AB, t.n0, kof(it + 3), wave, lane);
+        } else if (it + 1 < nk) {
             // this wave's share of tile it + 1 has landed (tile it + 2 may still fly); past the
             // barrier every wave's has, and every wave is done with tile it - 1
             if (it + 2 < nk) wait_vmcnt<8>();
@@ -228,7 +246,7 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-        dl_interleave();
+        dl_interleave<STEADY ? 8 : 0>();
         // keep those reads in this iteration (not sunk into the next one's first MFMAs), and
         // their wait after this half's MFMAs
         __builtin_amdgcn_sched_barrier(0);
@@ -237,6 +255,7 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
 #pragma unroll
         for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b0[j]));
     }
+    if constexpr (STEADY) wait_vmcnt<0>();               // no copy may land after the workgroup ends
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -247,7 +266,7 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
         }
 }
 
-template <class LA, class LB, class MAP, class EPI>
+template <class LA, class LB, class MAP, class EPI, bool STEADY = false>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_dl_kernel(LA la, LB lb, MAP map, EPI epi) {
     if (map.guard && *map.guard != 0) return;
     __shared__ __attribute__((aligned(16))) uint16_t lds[DL_NS * DL_STAGE];
@@ -256,7 +275,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_dl_kernel(LA la, LB lb, MAP
         epi.finish(t, threadIdx.x, false);
         return;
     }
-    gemm_dl_tile(la, lb, t, epi, lds);
+    gemm_dl_tile<STEADY>(la, lb, t, epi, lds);
     epi.finish(t, threadIdx.x, true);
 }
 

@@ -252,7 +252,7 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
     const int nwg = hess_dl_grid(pl, ntile);
     prof_begin(PWQ_PROF_XTX, s);
-    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
+    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess, true>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
     prof_end(PWQ_PROF_XTX, s, (double)n_tok * n * (n + 1));
     return hipGetLastError();
@@ -277,7 +277,7 @@ hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, f
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
     const int nwg = hess_dl_grid(pl, ntile);
     prof_begin(PWQ_PROF_XTX, s);
-    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
+    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess, true>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, a, b, map, epi);
     prof_end(PWQ_PROF_XTX, s, (double)n_tok * n * (n + 1));
     return hipGetLastError();
