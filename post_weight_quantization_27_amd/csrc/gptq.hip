@@ -781,7 +781,11 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
     // per wave (issue slots decide), eight-wave workgroups.
     const bool quad = m > 4096;
     const int rwv = m <= 1024 ? 4 : 16;
-    const unsigned nblk = quad ? (unsigned)cdiv(m, 128) : (unsigned)cdiv(m, rwv);
+    // quad kernel: up to 16384 rows, workgroups of 2 waves (16 rows each; two fit a CU's LDS)
+    // spread the rows over every CU in one round, with at most one wave per SIMD (the column
+    // chain of a wave issues faster alone); more rows take 8-wave workgroups, one per CU
+    const int qwv = m <= 16384 ? 2 : 8;
+    const unsigned nblk = quad ? (unsigned)cdiv(m, 16 * qwv) : (unsigned)cdiv(m, rwv);
 
     for (int64_t b0 = 0; b0 < n; b0 += block_size) {
         const int bw = (int)((n - b0) < block_size ? (n - b0) : block_size);
@@ -802,9 +806,16 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
         a.err_sb = err;
         prof_begin(PWQ_PROF_COLUMNS, s);
         if (quad) {
-            if (block_size == 128) hipLaunchKernelGGL((gptq_block_kernel<128, 8>), dim3(nblk), dim3(512), 0, s, a);
-            else if (block_size == 64) hipLaunchKernelGGL((gptq_block_kernel<64, 8>), dim3(nblk), dim3(512), 0, s, a);
-            else hipLaunchKernelGGL((gptq_block_kernel<32, 8>), dim3(nblk), dim3(512), 0, s, a);
+#define PWQ_QUAD(PW)                                                                                              \
+    do {                                                                                                          \
+        if (qwv == 8) hipLaunchKernelGGL((gptq_block_kernel<PW, 8>), dim3(nblk), dim3(512), 0, s, a);            \
+        else if (qwv == 4) hipLaunchKernelGGL((gptq_block_kernel<PW, 4>), dim3(nblk), dim3(256), 0, s, a);       \
+        else hipLaunchKernelGGL((gptq_block_kernel<PW, 2>), dim3(nblk), dim3(128), 0, s, a);                     \
+    } while (0)
+            if (block_size == 128) PWQ_QUAD(128);
+            else if (block_size == 64) PWQ_QUAD(64);
+            else PWQ_QUAD(32);
+#undef PWQ_QUAD
         } else if (rwv == 4) {
             if (block_size == 128) hipLaunchKernelGGL((gptq_row_kernel<128, 4>), dim3(nblk), dim3(256), 0, s, a);
             else if (block_size == 64) hipLaunchKernelGGL((gptq_row_kernel<64, 4>), dim3(nblk), dim3(256), 0, s, a);

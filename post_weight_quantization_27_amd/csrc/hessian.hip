@@ -71,22 +71,22 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(const float* __restric
         if (col + c < n) H[row * n + col + c] += 2.f * a[c];
 }
 
-// lower triangle := upper triangle, 32 x 32 blocks through LDS (coalesced both ways)
+// lower triangle := upper triangle, 64 x 64 blocks through LDS (coalesced both ways); grid
+// (column block bj, row block bi), blocks below the diagonal return at once
 __global__ __launch_bounds__(256) void mirror_upper_kernel(float* __restrict__ H, int64_t n) {
-    __shared__ float tile[32][33];
-    const int64_t nb = cdiv(n, 32);
-    // blockIdx.x enumerates block pairs bi <= bj
-    int64_t r = blockIdx.x, bi = 0;
-    while (r >= nb - bi) { r -= nb - bi; ++bi; }
-    const int64_t bj = bi + r;
-    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
-    for (int k = ty; k < 32; k += 8) {
-        int64_t i = bi * 32 + k, j = bj * 32 + tx;
+    const int64_t bi = blockIdx.y, bj = blockIdx.x;
+    if (bi > bj) return;
+    __shared__ float tile[64][65];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
+#pragma unroll 4
+    for (int k = ty; k < 64; k += 4) {
+        const int64_t i = bi * 64 + k, j = bj * 64 + tx;
         tile[k][tx] = (i < n && j < n) ? H[i * n + j] : 0.f;
     }
     __syncthreads();
-    for (int k = ty; k < 32; k += 8) {
-        int64_t i = bj * 32 + k, j = bi * 32 + tx;      // target H[i][j] = H[j][i], i > j
+#pragma unroll 4
+    for (int k = ty; k < 64; k += 4) {
+        const int64_t i = bj * 64 + k, j = bi * 64 + tx;      // target H[i][j] = H[j][i], i > j
         if (i < n && j < n && i > j) H[i * n + j] = tile[tx][k];
     }
 }
@@ -377,8 +377,8 @@ hipError_t hessian_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_i
                            pl.full, pl.splits, pl.bm, pl.dl ? 1 : 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int64_t nb = cdiv(d_in, 32);
-    hipLaunchKernelGGL(mirror_upper_kernel, dim3((unsigned)(nb * (nb + 1) / 2)), dim3(256), 0, s, H, d_in);
+    const unsigned nb = (unsigned)cdiv(d_in, 64);
+    hipLaunchKernelGGL(mirror_upper_kernel, dim3(nb, nb), dim3(256), 0, s, H, d_in);
     return hipGetLastError();
 }
 
