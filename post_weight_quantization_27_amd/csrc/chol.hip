@@ -21,7 +21,9 @@
 // launches per block, and the serial factor overlaps the update.  Block k's update of that
 // diagonal block is then done ahead, in block k's trsm + finalize launch: ten workgroups,
 // one per upper 32 x 32 tile, each forming the rows of P it needs from A and Z_kk.  From
-// n = 4096 on, updates are batched per super-block.
+// n = 4096 on, updates are batched per super-block, and the same overlap holds inside a
+// super-block (the diagonal factor joins the launch of the products the super-block's later
+// blocks need now); the first block past a super-block waits for its far products.
 // Every kernel reads `info` first and does nothing once a pivot has failed.
 #include "gemm_f32_dl.h"
 #include "pwq_internal.h"
@@ -473,7 +475,25 @@ using PushTask = GemmTask<T, T, OpMMajor<0>, OpKMajor<0>, RectMap, EpiPush>;
 template <int T>
 using SyrkRectTask = GemmTask<T, T, OpMMajor<0>, OpMMajor<0>, RectMap, EpiSyrkRect>;
 
+// A rectangular grid without the tiles at or past (m_from, n_from) in both directions (the
+// next diagonal block, updated ahead by the trsm launch); their workgroups do nothing
+struct SkipRectMap {
+    RectMap r;
+    int64_t m_from, n_from;
+    __device__ __forceinline__ bool get(int bid, int BM, int BN, Tile& t) const {
+        if (!r.get(bid, BM, BN, t)) return false;
+        if (t.m0 >= m_from && t.n0 >= n_from) {
+            t.kend = t.kbeg;
+            return false;
+        }
+        return true;
+    }
+};
+template <int T>
+using SyrkRectSkipTask = GemmTask<T, T, OpMMajor<0>, OpMMajor<0>, SkipRectMap, EpiSyrkRect>;
+
 int ntiles(const RectMap& m) { return m.tiles_m * m.tiles_n; }
+int ntiles(const SkipRectMap& m) { return ntiles(m.r); }
 int ntiles(const UpperMap& m) { return m.tiles * (m.tiles + 1) / 2; }
 
 // Panels of a super-block: P holds the V columns of its chol_sb(n) blocks side by side (row
@@ -534,29 +554,6 @@ hipError_t launch_far_dl(float* U, const float* P, int pld, int64_t n, int64_t s
     return hipGetLastError();
 }
 
-// After block [k0, k0 + bs) of a super-block starting at s0 < k0, for the blocks of the
-// super-block still to come (its panel Pk = V[0:k0, block] in P):
-//   A[0:k0, s0:k0] -= Pk Pk[s0:k0]^T       (their columns, every row above)
-//   R[s0:k0, k0:n] (+)= Pk[s0:k0] U[block, k0:n]   (their rows; columns k0..k0+bs overwritten)
-template <int T>
-hipError_t launch_near(float* U, const float* Pk, int pld, int64_t n, int64_t s0, int64_t k0, int bs, int32_t* info,
-                       int vu, hipStream_t s) {
-    SyrkRectTask<T> sy{};
-    sy.la = OpMMajor<0>{Pk, pld, k0, bs, 1};
-    sy.lb = OpMMajor<0>{Pk + s0 * pld, pld, k0 - s0, bs, 1};
-    sy.map = rect(T, T, k0, k0 - s0, bs);
-    sy.epi = EpiSyrkRect{U + s0, n, s0, k0 - s0};
-    PushTask<T> pu{};
-    pu.la = OpMMajor<0>{Pk + s0 * pld, pld, k0 - s0, bs, 1};
-    pu.lb = OpKMajor<0>{U + k0 * n + k0, n, n - k0, bs, vu && (k0 % 4 == 0)};
-    pu.map = rect(T, T, k0 - s0, n - k0, bs);
-    pu.epi = EpiPush{U + s0 * n + k0, n, k0 - s0, n - k0, bs};
-    const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
-    hipLaunchKernelGGL((gemm_f32_dual_kernel<SyrkRectTask<T>, PushTask<T>>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy,
-                       pu, n1, info);
-    return hipGetLastError();
-}
-
 // One launch for the update of block k (syrk + push tiles, workgroups 1 ..) and the
 // factor of the next diagonal block [kd0, kd0 + NB) (workgroup 0): block k's update of that
 // block was applied by block k's trsm launch (pre_update_tile), and the syrk tiles covering
@@ -572,6 +569,33 @@ __global__ __launch_bounds__(GEMM_THREADS, 2) void chol_update_diag_kernel(TA a,
     if (bid == 0) diag_block(U, n, kd0, CHOL_NB, info, lds);
     else if (bid - 1 < n1) a.run(bid - 1, lds);
     else b.run(bid - 1 - n1, lds);
+}
+
+// After block [k0, k0 + bs) of a super-block starting at s0 < k0, for the blocks of the
+// super-block still to come (its panel Pk = V[0:k0, block] in P):
+//   A[0:k0, s0:k0] -= Pk Pk[s0:k0]^T       (their columns, every row above)
+//   R[s0:k0, k0:n] (+)= Pk[s0:k0] U[block, k0:n]   (their rows; columns k0..k0+bs overwritten)
+// together with the factor of the next diagonal block [k0 - NB, k0): block k's trsm launch
+// has already applied block k's update to that block, so its syrk tiles are left out and
+// workgroup 0 factors it while the other tiles run
+template <int T>
+hipError_t launch_near_diag(float* U, const float* Pk, int pld, int64_t n, int64_t s0, int64_t k0, int bs,
+                            int32_t* info, int vu, hipStream_t s) {
+    const int64_t k1 = k0 - CHOL_NB;
+    SyrkRectSkipTask<T> sy{};
+    sy.la = OpMMajor<0>{Pk, pld, k0, bs, 1};
+    sy.lb = OpMMajor<0>{Pk + s0 * pld, pld, k0 - s0, bs, 1};
+    sy.map = SkipRectMap{rect(T, T, k0, k0 - s0, bs), k1, k1 - s0};
+    sy.epi = EpiSyrkRect{U + s0, n, s0, k0 - s0};
+    PushTask<T> pu{};
+    pu.la = OpMMajor<0>{Pk + s0 * pld, pld, k0 - s0, bs, 1};
+    pu.lb = OpKMajor<0>{U + k0 * n + k0, n, n - k0, bs, vu && (k0 % 4 == 0)};
+    pu.map = rect(T, T, k0 - s0, n - k0, bs);
+    pu.epi = EpiPush{U + s0 * n + k0, n, k0 - s0, n - k0, bs};
+    const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
+    hipLaunchKernelGGL((chol_update_diag_kernel<SyrkRectSkipTask<T>, PushTask<T>>), dim3(1 + n1 + n2),
+                       dim3(GEMM_THREADS), 0, s, sy, pu, n1, info, U, n, k1);
+    return hipGetLastError();
 }
 
 // Block k's update of the next diagonal block D = A[k1:k0, k1:k0] (k1 = k0 - NB), done in
@@ -828,6 +852,7 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
         }
         return hipSuccess;
     }
+    bool diag_done = false;                              // this block's diagonal factor already launched
     for (int kb = nt - 1; kb >= 0; --kb) {
         const int64_t k0 = (int64_t)kb * CHOL_NB;
         const int bs = (int)((n - k0) < CHOL_NB ? (n - k0) : CHOL_NB);
@@ -835,8 +860,13 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
         const int kb_lo = kb / sb * sb;                  // first block of this super-block
         const int64_t s0 = (int64_t)kb_lo * CHOL_NB;
         float* Pk = P + (kb - kb_lo) * CHOL_NB;          // this block's panel slot
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, U, n, k0, bs, info);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (!diag_done) {
+            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, U, n, k0, bs, info);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        // block kb - 1 in this super-block: this block's update of its diagonal block goes in
+        // the trsm launch, and its factor in the near launch
+        const bool fuse = kb > kb_lo && k0 > 0;
 
         // trsm (rows above) + finalize (block row k of U, right of the diagonal)
         TrsmTask tt{};
@@ -849,19 +879,23 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
         ft.lb = OpKMajor<0>{U + k0 * n + k0 + bs, n, r, bs, vu && ((k0 + bs) % 4 == 0)};
         ft.map = rect(64, 64, bs, r, bs);
         ft.epi = EpiStore{U + k0 * n + k0 + bs, n, bs, r, -1.f};
+        const int n0 = fuse ? PRE_TILES : 0;
         const int n1 = k0 > 0 ? ntiles(tt.map) : 0;
         const int n2 = r > 0 ? ntiles(ft.map) : 0;
-        if (n1 + n2 > 0) {
-            hipLaunchKernelGGL((gemm_f32_dual_kernel<TrsmTask, FinalizeTask>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, tt, ft,
-                               n1, info);
+        if (n0 + n1 + n2 > 0) {
+            hipLaunchKernelGGL((chol_panel_kernel<TrsmTask, FinalizeTask>), dim3(n0 + n1 + n2), dim3(GEMM_THREADS), 0, s,
+                               tt, ft, n0, n1, info, U, n, k0, bs);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
+        diag_done = false;
         if (k0 == 0) break;
-        if (kb > kb_lo) {
-            // more blocks of this super-block follow: only what they need now
+        if (fuse) {
+            // more blocks of this super-block follow: only what they need now, and the next
+            // block's diagonal factor
             const int64_t big = cdiv(k0, 128) * cdiv(k0 - s0, 128) + cdiv(k0 - s0, 128) * cdiv(n - k0, 128);
-            e = big >= 512 ? launch_near<128>(U, Pk, pld, n, s0, k0, bs, info, vu, s)
-                           : launch_near<64>(U, Pk, pld, n, s0, k0, bs, info, vu, s);
+            e = big >= 512 ? launch_near_diag<128>(U, Pk, pld, n, s0, k0, bs, info, vu, s)
+                           : launch_near_diag<64>(U, Pk, pld, n, s0, k0, bs, info, vu, s);
+            diag_done = true;
         } else {
             // super-block done: everything above and right of it, depth = its width
             const int kf = (int)((kb_lo + sb) * (int64_t)CHOL_NB < n ? sb * CHOL_NB : n - s0);
