@@ -49,7 +49,7 @@ TILE = 8192
 ROWS = 128                    # sampled rows per layer for the oracle's column loop
 
 SAMPLED = [("llama70b", "q_proj", False), ("llama70b", "q_proj", True), ("llama70b", "gate_up_proj", False),
-           ("llama70b", "down_proj", False), ("gpt2_1p3b", "h0.fc2", False)]
+           ("llama70b", "down_proj", False), ("llama70b", "down_proj", True), ("gpt2_1p3b", "h0.fc2", False)]
 
 
 def log(msg):
@@ -239,7 +239,11 @@ def test_act_order_and_factor_whole_matrix(case):
         same = float(np.mean(p == np.argsort(-d64, kind="stable")))
         log(f"{s.name}: act-order: float32 diagonal within {eps:.3g} relative; i-th in the GPU order within "
             f"{off:.3g} of the i-th largest; positions equal to the float64 order {same:.4f}")
-        assert eps <= 1e-5
+        # the float32 diagonal is a running sum of n_tok products, 16 added per MFMA step: a
+        # random walk of n_tok / 16 roundings of at most 2^-24 relative each, bounded here at
+        # 4.5 standard deviations over the layer's diagonal entries (3.4e-5 at 262144 tokens;
+        # measured 9.6e-6 at 8192 inputs, 1.15e-5 at 28672)
+        assert eps <= 4.5 * 2.0 ** -24 * np.sqrt(s.n_tok / 16)
         assert off <= 2.001 * eps
     Ud = torch.from_numpy(U64).to(DEV)
     rf = rel_frob_dev(case.U, Ud)
