@@ -13,7 +13,8 @@
 // RTN, groups that tile their rows (n % g == 0, 16-byte aligned rows, g * element size a
 // power-of-two multiple of 16 bytes up to 1 KiB): a lane holds one 16-byte vector of its
 // group (8 float16 or 4 float32 weights), LG = g * size / 16 lanes make a group, and each
-// lane issues four independent loads (four sets of 64 / LG groups) before reducing.  The
+// lane issues eight independent loads (eight sets of 64 / LG groups; nontemporal when rows
+// are contiguous) before reducing.  The
 // group max is a DPP reduction within rows of 16 lanes, the code a branch-free exact
 // rounding; codes go out as 8 or 4 bytes per lane, INT4 nibbles as 4 or 2.
 // RTN, other shapes (one scale per row, ragged or unaligned groups): a segment (row,
@@ -179,13 +180,15 @@ __device__ __forceinline__ float lanes_max(float f) {
 // FAST: rows contiguous (ldw = n) and scales (and zeros) computed here, the common case:
 // a group's offsets are multiples of its segment number, and a zero scale needs no branch
 // (reciprocal 0 and clamp bounds [0, 0] give the code 0, or Z = 0).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <int DT, int LG, bool ZP, bool FAST>
 __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
     typedef typename Elem<DT>::T T;
     constexpr int ES = (int)sizeof(T);
     constexpr int EPV = 16 / ES;                           // weights per 16-byte vector
     constexpr int SPW = 64 / LG;                           // groups per wave load
-    constexpr int U = 4;                                   // loads in flight per lane
+    constexpr int U = 8;                                   // loads in flight per lane
     const int lane = threadIdx.x & 63;
     const int sub = lane / LG, li = lane % LG;
     const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -205,7 +208,9 @@ __global__ __launch_bounds__(256) void rtn_group_kernel(RtnArgs a) {
             seg[u] = live[u] ? sg0 : 0u;                   // a dead slot reads group 0
             if (FAST) {
                 rr[u] = 0;
-                raw[u] = *(const uint4*)(Wb + (seg[u] * glb + (uint32_t)li * 16u));
+                // W is read once: nontemporal, so it does not displace what is cached
+                const u32x4 t4 = __builtin_nontemporal_load((const u32x4*)(Wb + (seg[u] * glb + (uint32_t)li * 16u)));
+                raw[u] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
             } else {
                 rr[u] = (uint32_t)(((uint64_t)seg[u] * a.dmul) >> a.dsh);
                 const uint32_t G = seg[u] - rr[u] * ng;
