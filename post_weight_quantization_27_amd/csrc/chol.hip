@@ -527,30 +527,33 @@ hipError_t launch_far(float* U, const float* P, int pld, int64_t n, int64_t s0, 
     return hipGetLastError();
 }
 
-// launch_far on the direct-load engine (256 x 256 tiles): the same two products, for deep
-// super-blocks (kf a whole number of its stages) with every row 16-byte aligned
-typedef FdlTask<FdlRows, FdlRows, UpperMap, EpiSyrk> SyrkDlTask;
-typedef FdlTask<FdlRows, FdlCols, RectMap, EpiPush> PushDlTask;
+// launch_far on the direct-load engine (T x T tiles): the same two products, for super-blocks
+// a whole number of its stages deep, every row 16-byte aligned
+template <int T>
+using SyrkDlTask = FdlTask<FdlRows<T>, FdlRows<T>, UpperMap, EpiSyrk>;
+template <int T>
+using PushDlTask = FdlTask<FdlRows<T>, FdlCols<T>, RectMap, EpiPush>;
 
-inline bool far_dl_ok(int64_t n, int64_t s0, int kf, int pld, int vu) {
-    return vu && n % 4 == 0 && pld % 4 == 0 && kf % FDL_BK == 0 && s0 > 0 &&
-           cdiv(s0, FDL_TILE) * cdiv(n, FDL_TILE) >= FAR_DL_MIN_TILES;
+// rows of the panels and of U 16-byte aligned, depth whole stages: the direct-load engines apply
+inline bool dl_ok(int64_t n, int depth, int pld, int vu) {
+    return vu && n % 4 == 0 && pld % 4 == 0 && depth % FDL_BK == 0;
 }
 
+template <int T>
 hipError_t launch_far_dl(float* U, const float* P, int pld, int64_t n, int64_t s0, int kf, int32_t* info, hipStream_t s) {
-    SyrkDlTask sy{};
-    sy.la = FdlRows{P, pld, s0};
+    SyrkDlTask<T> sy{};
+    sy.la = FdlRows<T>{P, pld, s0};
     sy.lb = sy.la;
-    sy.map = UpperMap{s0, kf, (int)cdiv(s0, FDL_TILE), 1, kf, nullptr};
+    sy.map = UpperMap{s0, kf, (int)cdiv(s0, T), 1, kf, nullptr};
     sy.epi = EpiSyrk{U, n, s0};
-    PushDlTask pu{};
-    pu.la = FdlRows{P, pld, s0};
-    pu.lb = FdlCols{U + s0 * n + s0, n, n - s0};
-    pu.map = rect(FDL_TILE, FDL_TILE, s0, n - s0, kf);
+    PushDlTask<T> pu{};
+    pu.la = FdlRows<T>{P, pld, s0};
+    pu.lb = FdlCols<T>{U + s0 * n + s0, n, n - s0};
+    pu.map = rect(T, T, s0, n - s0, kf);
     pu.epi = EpiPush{U + s0, n, s0, n - s0, kf};
     const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
-    hipLaunchKernelGGL((gemm_fdl_dual_kernel<SyrkDlTask, PushDlTask>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy, pu, n1,
-                       info);
+    hipLaunchKernelGGL((gemm_fdl_dual_kernel<SyrkDlTask<T>, PushDlTask<T>>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy,
+                       pu, n1, info);
     return hipGetLastError();
 }
 
@@ -594,6 +597,30 @@ hipError_t launch_near_diag(float* U, const float* Pk, int pld, int64_t n, int64
     pu.epi = EpiPush{U + s0 * n + k0, n, k0 - s0, n - k0, bs};
     const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
     hipLaunchKernelGGL((chol_update_diag_kernel<SyrkRectSkipTask<T>, PushTask<T>>), dim3(1 + n1 + n2),
+                       dim3(GEMM_THREADS), 0, s, sy, pu, n1, info, U, n, k1);
+    return hipGetLastError();
+}
+
+// launch_near_diag on the direct-load engine (T x T tiles, two workgroups per CU at T = 128)
+template <int T>
+using SyrkRectSkipDlTask = FdlTask<FdlRows<T>, FdlRows<T>, SkipRectMap, EpiSyrkRect>;
+
+template <int T>
+hipError_t launch_near_diag_dl(float* U, const float* Pk, int pld, int64_t n, int64_t s0, int64_t k0, int bs,
+                               int32_t* info, hipStream_t s) {
+    const int64_t k1 = k0 - CHOL_NB;
+    SyrkRectSkipDlTask<T> sy{};
+    sy.la = FdlRows<T>{Pk, pld, k0};
+    sy.lb = FdlRows<T>{Pk + s0 * pld, pld, k0 - s0};
+    sy.map = SkipRectMap{rect(T, T, k0, k0 - s0, bs), k1, k1 - s0};
+    sy.epi = EpiSyrkRect{U + s0, n, s0, k0 - s0};
+    PushDlTask<T> pu{};
+    pu.la = FdlRows<T>{Pk + s0 * pld, pld, k0 - s0};
+    pu.lb = FdlCols<T>{U + k0 * n + k0, n, n - k0};
+    pu.map = rect(T, T, k0 - s0, n - k0, bs);
+    pu.epi = EpiPush{U + s0 * n + k0, n, k0 - s0, n - k0, bs};
+    const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
+    hipLaunchKernelGGL((chol_update_diag_kernel<SyrkRectSkipDlTask<T>, PushDlTask<T>>), dim3(1 + n1 + n2),
                        dim3(GEMM_THREADS), 0, s, sy, pu, n1, info, U, n, k1);
     return hipGetLastError();
 }
@@ -893,16 +920,21 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
             // more blocks of this super-block follow: only what they need now, and the next
             // block's diagonal factor
             const int64_t big = cdiv(k0, 128) * cdiv(k0 - s0, 128) + cdiv(k0 - s0, 128) * cdiv(n - k0, 128);
-            e = big >= 512 ? launch_near_diag<128>(U, Pk, pld, n, s0, k0, bs, info, vu, s)
-                           : launch_near_diag<64>(U, Pk, pld, n, s0, k0, bs, info, vu, s);
+            e = dl_ok(n, bs, pld, vu) && big >= 256 ? launch_near_diag_dl<128>(U, Pk, pld, n, s0, k0, bs, info, s)
+                : big >= 512                          ? launch_near_diag<128>(U, Pk, pld, n, s0, k0, bs, info, vu, s)
+                                                      : launch_near_diag<64>(U, Pk, pld, n, s0, k0, bs, info, vu, s);
             diag_done = true;
         } else {
             // super-block done: everything above and right of it, depth = its width
             const int kf = (int)((kb_lo + sb) * (int64_t)CHOL_NB < n ? sb * CHOL_NB : n - s0);
             const int64_t big = cdiv(s0, 128) * cdiv(n, 128);
-            e = far_dl_ok(n, s0, kf, pld, vu) ? launch_far_dl(U, P, pld, n, s0, kf, info, s)
-                : big >= 512                  ? launch_far<128>(U, P, pld, n, s0, kf, info, vu, s)
-                                              : launch_far<64>(U, P, pld, n, s0, kf, info, vu, s);
+            // 256-tiles from 1024 of them (their four-times-larger tiles must still fill the
+            // chip), 128-tiles (two workgroups per CU) from 256
+            const bool dl = dl_ok(n, kf, pld, vu);
+            e = dl && cdiv(s0, 256) * cdiv(n, 256) >= FAR_DL_MIN_TILES ? launch_far_dl<256>(U, P, pld, n, s0, kf, info, s)
+                : dl && big >= 256                                    ? launch_far_dl<128>(U, P, pld, n, s0, kf, info, s)
+                : big >= 512                                          ? launch_far<128>(U, P, pld, n, s0, kf, info, vu, s)
+                                                                      : launch_far<64>(U, P, pld, n, s0, kf, info, vu, s);
         }
         if (e != hipSuccess) return e;
     }

@@ -696,39 +696,43 @@ hipError_t trailing(float* Wf, const float* err, int ld, const float* U, const i
     return hipGetLastError();
 }
 
-// The same product on the direct-load engine (256 x 256 tiles; kw a whole number of its
-// stages, 16-byte aligned rows)
+// The same product on the direct-load engine (T x T tiles; kw a whole number of its stages,
+// 16-byte aligned rows)
+template <int T>
 hipError_t trailing_dl(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
                        int64_t kb0, int kw, int64_t c0, int64_t c1, hipStream_t s) {
     const int64_t N = c1 - c0;
-    FdlRows a{err, ld, m};
-    FdlCols b{U + kb0 * n + c0, n, N};
+    FdlRows<T> a{err, ld, m};
+    FdlCols<T> b{U + kb0 * n + c0, n, N};
     RectMap mp{};
     mp.M = m; mp.N = N; mp.K = kw;
-    mp.tiles_m = (int)cdiv(m, FDL_TILE);
-    mp.tiles_n = (int)cdiv(N, FDL_TILE);
+    mp.tiles_m = (int)cdiv(m, T);
+    mp.tiles_n = (int)cdiv(N, T);
     mp.splits = 1;
     mp.kchunk = kw;
     mp.tri_k = 0;
     mp.guard = info;
     EpiSub ep{Wf + c0, n, m, N};
-    hipLaunchKernelGGL((gemm_fdl_kernel<FdlRows, FdlCols, RectMap, EpiSub>), dim3(mp.tiles_m * mp.tiles_n),
+    hipLaunchKernelGGL((gemm_fdl_kernel<FdlRows<T>, FdlCols<T>, RectMap, EpiSub>), dim3(mp.tiles_m * mp.tiles_n),
                        dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
     return hipGetLastError();
 }
 
-// 256-tiles from which the direct-load engine takes a trailing product
+// 256-tiles from which the direct-load engine takes a trailing product on 256 x 256 tiles;
+// below that, 128-tiles from which it takes one on 128 x 128 tiles (two workgroups per CU)
 constexpr int64_t TRAIL_DL_MIN_TILES = 512;
+constexpr int64_t TRAIL_DL128_MIN_TILES = 256;
 
 hipError_t update(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
                   int64_t kb0, int kw, int64_t c0, int64_t c1, hipStream_t s) {
     const int64_t big_tiles = cdiv(m, 128) * cdiv(c1 - c0, 128);
-    const bool dl = kw % FDL_BK == 0 && ld % 4 == 0 && n % 4 == 0 && c0 % 4 == 0 && aligned(err, 16) &&
-                    aligned(U, 16) && cdiv(m, FDL_TILE) * cdiv(c1 - c0, FDL_TILE) >= TRAIL_DL_MIN_TILES;
+    const bool dl = kw % FDL_BK == 0 && ld % 4 == 0 && n % 4 == 0 && c0 % 4 == 0 && aligned(err, 16) && aligned(U, 16);
     prof_begin(PWQ_PROF_UPDATE, s);
-    const hipError_t e = dl                ? trailing_dl(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
-                         : big_tiles >= 512 ? trailing<128, 128>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
-                                            : trailing<64, 64>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s);
+    const hipError_t e =
+        dl && cdiv(m, 256) * cdiv(c1 - c0, 256) >= TRAIL_DL_MIN_TILES ? trailing_dl<256>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
+        : dl && big_tiles >= TRAIL_DL128_MIN_TILES                  ? trailing_dl<128>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
+        : big_tiles >= 512                                          ? trailing<128, 128>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
+                                                                    : trailing<64, 64>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s);
     prof_end(PWQ_PROF_UPDATE, s, 2.0 * m * kw * (c1 - c0));
     return e;
 }

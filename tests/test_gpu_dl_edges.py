@@ -1,14 +1,15 @@
-"""Parity of the large-tile (256 x 256, direct-load) float32 products on their edges.
+"""Parity of the direct-load float32 products (256 x 256 and 128 x 128 tiles) on their edges.
 
-The far updates of the factor and the GPTQ trailing products run on 256 x 256 tiles once a
-launch has enough of them.  The full-size layers have dimensions that are multiples of 256;
-these cases add what those do not reach:
+The far updates of the factor, its near updates (with the next diagonal factor in the same
+launch) and the GPTQ trailing products run on the direct-load engine once a launch has
+enough tiles: 256 x 256 tiles for the largest, 128 x 128 below.  The full-size layers have
+dimensions that are multiples of 256; these cases add what those do not reach:
 
 * the factor at n = 12000: push tiles with a ragged last column block (columns clamped in
   the loads, discarded by the epilogue), diagonal syrk tiles (the per-element triangle test),
   and a first super-block 736 deep (not a multiple of 128);
 * GPTQ with 12000 rows and 4608 inputs: ragged last row tile in the trailing products, and
-  launches on both the 256-tile engine and the 128-tile one within one layer.
+  launches on both tile sizes within one layer.
 
 Inputs are seeded; the float64 references are the oracle's (``oracle.chol_inverse_upper`` up
 to 8192 inputs, the same textbook route through torch.linalg on the device past that, as in
