@@ -48,16 +48,44 @@ __global__ __launch_bounds__(256) void copy_upper_kernel(const float* __restrict
 __global__ void set_int_kernel(int32_t* p, int32_t v) { *p = v; }
 
 // U[i][j] = H[perm[i]][perm[j]] for j >= i, 0 below: row perm[i] of the full symmetric H is
-// staged in LDS, so both the read and the write are coalesced.  One workgroup per row.
+// staged in LDS, so both the read and the write are coalesced.  One workgroup per row; each
+// thread issues its loads (of the row, then of perm) in batches of eight, so the workgroup
+// waits for one memory latency per batch rather than per element.
 __global__ __launch_bounds__(256) void copy_perm_kernel(const float* __restrict__ H, const int32_t* __restrict__ perm,
                                                         float* __restrict__ U, int64_t n) {
     __shared__ float row[PERM_MAX_N];
+    constexpr int UR = 8;
     const int64_t i = blockIdx.x;
+    const int tid = threadIdx.x;
     const float* src = H + (int64_t)perm[i] * n;
-    for (int64_t j = threadIdx.x; j < n; j += 256) row[j] = src[j];
+    for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
+        float v[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = j0 + u * 256 + tid;
+            v[u] = j < n ? src[j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = j0 + u * 256 + tid;
+            if (j < n) row[j] = v[u];
+        }
+    }
     __syncthreads();
     float* dst = U + i * n;
-    for (int64_t j = threadIdx.x; j < n; j += 256) dst[j] = j >= i ? row[perm[j]] : 0.f;
+    for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
+        int32_t pj[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = j0 + u * 256 + tid;
+            pj[u] = (j < n && j >= i) ? perm[j] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = j0 + u * 256 + tid;
+            if (j < n) dst[j] = j >= i ? row[pj[u]] : 0.f;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ diagonal block

@@ -62,22 +62,96 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
                                                             uint16_t* __restrict__ zeros_out) {
     if (*info) return;
     typedef typename Elem<DT>::T T;
-    __shared__ float row[PERM ? PERM_MAX_N : 1];
+    __shared__ __attribute__((aligned(16))) float row[PERM ? PERM_MAX_N : 1];
     __shared__ float red[8];
     const int64_t r = blockIdx.x;
     const T* src = (const T*)W + r * ldw;
     float* dst = Wf + r * n;
     float amax = 0.f, hi = 0.f, nlo = 0.f;    // max |w|; max(w, 0), max(-w, 0)
-    if (PERM) {
-        for (int64_t j = threadIdx.x; j < n; j += 256) {
-            const float v = Elem<DT>::get(src, j);
-            row[j] = v;
-            amax = fmaxf(amax, fabsf(v));
-            hi = fmaxf(hi, v);
-            nlo = fmaxf(nlo, -v);
+    // rows of whole 4-element vectors, aligned: four weights per load
+    const bool v4 = n % 4 == 0 && ldw % 4 == 0 && ((uintptr_t)W % (4 * sizeof(T))) == 0;
+    if (PERM && v4) {
+        constexpr int UR = 4;                  // vector loads in batches of four per thread
+        const int64_t nv = n / 4;
+        for (int64_t j0 = 0; j0 < nv; j0 += 256 * UR) {
+            float4 v[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + threadIdx.x;
+                v[u] = j < nv ? Elem<DT>::get4(src, 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + threadIdx.x;
+                if (j < nv) *(float4*)(row + 4 * j) = v[u];
+                const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    amax = fmaxf(amax, fabsf(e[k]));
+                    hi = fmaxf(hi, e[k]);
+                    nlo = fmaxf(nlo, -e[k]);
+                }
+            }
         }
+    } else if (PERM) {
+        // loads in batches of eight per thread (one memory latency per batch)
+        constexpr int UR = 8;
+        for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
+            float v[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + threadIdx.x;
+                v[u] = j < n ? Elem<DT>::get(src, j) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + threadIdx.x;
+                if (j < n) row[j] = v[u];
+                amax = fmaxf(amax, fabsf(v[u]));
+                hi = fmaxf(hi, v[u]);
+                nlo = fmaxf(nlo, -v[u]);
+            }
+        }
+    }
+    if (PERM) {
+        constexpr int UR = 8;
         __syncthreads();
-        for (int64_t p = threadIdx.x; p < n; p += 256) dst[p] = row[perm[p]];
+        for (int64_t p0 = 0; p0 < n; p0 += 256 * UR) {
+            int32_t pj[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t p = p0 + u * 256 + threadIdx.x;
+                pj[u] = p < n ? perm[p] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t p = p0 + u * 256 + threadIdx.x;
+                if (p < n) dst[p] = row[pj[u]];
+            }
+        }
+    } else if (v4) {
+        constexpr int UR = 4;                  // vector loads in batches of four per thread
+        const int64_t nv = n / 4;
+        for (int64_t j0 = 0; j0 < nv; j0 += 256 * UR) {
+            float4 v[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + threadIdx.x;
+                v[u] = j < nv ? Elem<DT>::get4(src, 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + threadIdx.x;
+                if (j < nv) *(float4*)(dst + 4 * j) = v[u];
+                const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    amax = fmaxf(amax, fabsf(e[k]));
+                    hi = fmaxf(hi, e[k]);
+                    nlo = fmaxf(nlo, -e[k]);
+                }
+            }
+        }
     } else {
         for (int64_t j = threadIdx.x; j < n; j += 256) {
             const float v = Elem<DT>::get(src, j);
@@ -662,16 +736,74 @@ __global__ __launch_bounds__(256) void unpermute_codes_kernel(const int8_t* __re
                                                               int64_t n, int8_t* __restrict__ codes, uint8_t* __restrict__ packed,
                                                               int nib_off, const int32_t* __restrict__ info) {
     if (*info) return;
-    __shared__ int8_t row[PERM_MAX_N];
+    __shared__ __attribute__((aligned(16))) int8_t row[PERM_MAX_N];
+    constexpr int UR = 8;                  // loads in batches of eight per thread
     const int64_t r = blockIdx.x;
-    for (int64_t j = threadIdx.x; j < n; j += 256) row[j] = cp[r * n + j];
+    const int tid = threadIdx.x;
+    if (n % 4 == 0) {
+        // four codes per load (rows of n bytes, n a multiple of 4: every row 4-byte aligned)
+        const uint32_t* src = (const uint32_t*)(cp + r * n);
+        uint32_t* dst = (uint32_t*)row;
+        const int64_t nw = n / 4;
+        for (int64_t j0 = 0; j0 < nw; j0 += 256 * UR) {
+            uint32_t v[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + tid;
+                v[u] = j < nw ? src[j] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + tid;
+                if (j < nw) dst[j] = v[u];
+            }
+        }
+    } else {
+        for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
+            int8_t v[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + tid;
+                v[u] = j < n ? cp[r * n + j] : (int8_t)0;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * 256 + tid;
+                if (j < n) row[j] = v[u];
+            }
+        }
+    }
     __syncthreads();
     if (codes)
-        for (int64_t c = threadIdx.x; c < n; c += 256) codes[r * n + c] = row[inv[c]];
+        for (int64_t c0 = 0; c0 < n; c0 += 256 * UR) {
+            int32_t ic[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t c = c0 + u * 256 + tid;
+                ic[u] = c < n ? inv[c] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t c = c0 + u * 256 + tid;
+                if (c < n) codes[r * n + c] = row[ic[u]];
+            }
+        }
     if (packed)
-        for (int64_t b = threadIdx.x; b < n / 2; b += 256) {
-            const int lo = row[inv[2 * b]], hi = row[inv[2 * b + 1]];
-            packed[r * (n / 2) + b] = (uint8_t)(((lo + nib_off) & 15) | (((hi + nib_off) & 15) << 4));
+        for (int64_t b0 = 0; b0 < n / 2; b0 += 256 * UR) {
+            int2 ib[UR];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t b = b0 + u * 256 + tid;
+                ib[u] = b < n / 2 ? make_int2(inv[2 * b], inv[2 * b + 1]) : make_int2(0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t b = b0 + u * 256 + tid;
+                if (b < n / 2) {
+                    const int lo = row[ib[u].x], hi = row[ib[u].y];
+                    packed[r * (n / 2) + b] = (uint8_t)(((lo + nib_off) & 15) | (((hi + nib_off) & 15) << 4));
+                }
+            }
         }
 }
 

@@ -126,6 +126,44 @@ __global__ __launch_bounds__(256) void act_order_kernel(const float* __restrict_
     if (i < n) perm[rank] = (int32_t)i;
 }
 
+// The same ranks for n <= PERM_MAX_N: every workgroup stages the whole diagonal in LDS once,
+// and each thread scans it four values per (broadcast) read, with 32-bit counts.
+__global__ __launch_bounds__(256) void act_order_lds_kernel(const float* __restrict__ H, int64_t n,
+                                                            int32_t* __restrict__ perm) {
+    __shared__ __attribute__((aligned(16))) float d[PERM_MAX_N];
+    constexpr int UR = 8;                                // strided loads in batches of eight per thread
+    for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
+        float v[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = j0 + u * 256 + threadIdx.x;
+            v[u] = j < n ? H[j * n + j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t j = j0 + u * 256 + threadIdx.x;
+            if (j < n) d[j] = v[u];
+        }
+    }
+    __syncthreads();
+    const int64_t i64 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i64 >= n) return;
+    const int i = (int)i64, nn = (int)n;
+    const float di = d[i];
+    int rank = 0;
+    const int n4 = nn / 4;
+    for (int t = 0; t < n4; ++t) {
+        const float4 q = ((const float4*)d)[t];
+        const int j = 4 * t;
+        rank += (q.x > di) || (q.x == di && j < i);
+        rank += (q.y > di) || (q.y == di && j + 1 < i);
+        rank += (q.z > di) || (q.z == di && j + 2 < i);
+        rank += (q.w > di) || (q.w == di && j + 3 < i);
+    }
+    for (int j = 4 * n4; j < nn; ++j) rank += (d[j] > di) || (d[j] == di && j < i);
+    perm[rank] = i;
+}
+
 // bfloat16 X: native bf16 MFMA (products exact in float32), 128 x 128 upper tiles; the two
 // operand loaders split the 256 threads (each tile operand has 128 transposing blocks)
 hipError_t hess_gemm_bf16(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, float* part, const HessPlan& pl,
@@ -390,7 +428,8 @@ hipError_t damp_launch(float* H, int64_t n, float damp, float* lambda_out, hipSt
 
 hipError_t act_order_launch(const float* H, int64_t n, int32_t* perm, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(act_order_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, H, n, perm);
+    if (n <= PERM_MAX_N) hipLaunchKernelGGL(act_order_lds_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, H, n, perm);
+    else hipLaunchKernelGGL(act_order_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, H, n, perm);
     return hipGetLastError();
 }
 

@@ -394,7 +394,9 @@ __device__ __forceinline__ void dq_store(void* out, int64_t i, float v) {
 // per pass, lane l the chunks 64 j + l (j < 4): each load instruction reads 4 (nibbles) or 8
 // (codes) contiguous bytes per lane, each store writes 16 or 32 contiguous bytes per lane,
 // and the four loads of a lane are in flight together.
-template <int OT, bool ZP>
+// GI: columns carry their own group (g_idx, act-order): each of a chunk's 8 columns takes the
+// scale (and zero) of its group, read through one 32-byte load of g_idx.
+template <int OT, bool ZP, bool GI = false>
 __global__ __launch_bounds__(256) void dequant_vec_kernel(DqArgs a) {
     constexpr int U = 4;
     const int lane = threadIdx.x & 63;
@@ -417,18 +419,32 @@ __global__ __launch_bounds__(256) void dequant_vec_kernel(DqArgs a) {
             c0[u] = (tt - r[u] * cpr) * 8;
             if (a.packed) w[u] = make_uint2(*(const uint32_t*)(a.packed + r[u] * (a.n / 2) + c0[u] / 2), 0u);
             else w[u] = *(const uint2*)(a.codes + r[u] * a.n + c0[u]);
-            const int64_t gi = r[u] * a.ng + (a.g == 0 ? 0 : c0[u] / a.g);
-            sc[u] = f16_bits_to_f32(a.scales[gi]);
-            zz[u] = ZP ? (int)a.zeros[gi] : 0;
+            if (!GI) {
+                const int64_t gi = r[u] * a.ng + (a.g == 0 ? 0 : c0[u] / a.g);
+                sc[u] = f16_bits_to_f32(a.scales[gi]);
+                zz[u] = ZP ? (int)a.zeros[gi] : 0;
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (!live[u]) continue;
             int q[8];
-            dq_unpack8<ZP>(a, w[u], zz[u], q);
             float v[8];
+            if (GI) {
+                const int4 g0 = *(const int4*)(a.g_idx + c0[u]), g1 = *(const int4*)(a.g_idx + c0[u] + 4);
+                const int gk[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                dq_unpack8<ZP>(a, w[u], 0, q);             // zero-point form: the stored codes
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = sc[u] * (float)q[k];     // exact: 11 x at most 8 significant bits (zeros within the code range)
+                for (int k = 0; k < 8; ++k) {
+                    const int64_t gi = r[u] * a.ng + gk[k];
+                    const int z = ZP ? (int)a.zeros[gi] : 0;
+                    v[k] = f16_bits_to_f32(a.scales[gi]) * (float)(q[k] - z);
+                }
+            } else {
+                dq_unpack8<ZP>(a, w[u], zz[u], q);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = sc[u] * (float)q[k];     // exact: 11 x at most 8 significant bits (zeros within the code range)
+            }
             if (OT == 0) {
                 float4* o = (float4*)((float*)a.out + r[u] * a.n + c0[u]);
                 o[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -733,6 +749,8 @@ hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint
     const size_t os = out_dtype == 0 ? 4 : 2;
     a.vec = (n % 8 == 0) && (group_size == 0 || (group_size % 8 == 0 && !g_idx)) && aligned(out, 8 * os) &&
             (!packed || aligned(packed, 4)) && (!codes || aligned(codes, 8));
+    const bool vec_gi = g_idx && group_size > 0 && (n % 8 == 0) && aligned(g_idx, 16) && aligned(out, 8 * os) &&
+                        (!packed || aligned(packed, 4)) && (!codes || aligned(codes, 8));
     const int64_t gc = group_size / 8;
     if (packed && out_dtype == 1 && group_size > 0 && group_size % 8 == 0 && (gc & (gc - 1)) == 0 &&
         n % group_size == 0 && !g_idx && aligned(packed, 4) && aligned(out, 16) && m * a.chunks < ((int64_t)1 << 31)) {
@@ -745,14 +763,22 @@ hipError_t dequant_launch(const uint8_t* packed, const int8_t* codes, const uint
                                 dim3(256), 0, s, a, gsh);
         return hipGetLastError();
     }
-    if (a.vec) {
+    if (a.vec || vec_gi) {
         const int64_t want = cdiv(m * a.chunks, 4 * 256);
-#define PWQ_DQV(OT, ZPV) \
-        hipLaunchKernelGGL((dequant_vec_kernel<OT, ZPV>), dim3((unsigned)resident_blocks<dequant_vec_kernel<OT, ZPV>>(want)), \
-                           dim3(256), 0, s, a)
-        if (out_dtype == 0) { if (zp) PWQ_DQV(0, true); else PWQ_DQV(0, false); }
-        else if (out_dtype == 1) { if (zp) PWQ_DQV(1, true); else PWQ_DQV(1, false); }
-        else { if (zp) PWQ_DQV(2, true); else PWQ_DQV(2, false); }
+#define PWQ_DQV(OT, ZPV, GIV) \
+        hipLaunchKernelGGL((dequant_vec_kernel<OT, ZPV, GIV>), \
+                           dim3((unsigned)resident_blocks<dequant_vec_kernel<OT, ZPV, GIV>>(want)), dim3(256), 0, s, a)
+#define PWQ_DQV2(OT, GIV) do { if (zp) PWQ_DQV(OT, true, GIV); else PWQ_DQV(OT, false, GIV); } while (0)
+        if (vec_gi) {
+            if (out_dtype == 0) PWQ_DQV2(0, true);
+            else if (out_dtype == 1) PWQ_DQV2(1, true);
+            else PWQ_DQV2(2, true);
+        } else {
+            if (out_dtype == 0) PWQ_DQV2(0, false);
+            else if (out_dtype == 1) PWQ_DQV2(1, false);
+            else PWQ_DQV2(2, false);
+        }
+#undef PWQ_DQV2
 #undef PWQ_DQV
         return hipGetLastError();
     }

@@ -164,15 +164,26 @@ def test_dequant_exact(pwq, m, n, g, src, out_dtype):
     assert np.array_equal(host(got).view(np.uint8), want.view(np.uint8))
 
 
-def test_dequant_g_idx(pwq):
-    rng = np.random.default_rng(4)
-    m, n, g = 16, 64, 16
+# n = 64: the vector kernel with per-column groups; n = 68: the element-wise kernel
+@pytest.mark.parametrize("n", [64, 68])
+@pytest.mark.parametrize("src", ["packed", "codes"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_dequant_g_idx(pwq, n, src, out_dtype):
+    rng = np.random.default_rng(4 + n)
+    m, g = 40, 16
+    ng = -(-n // g)
     codes = rng.integers(-7, 8, size=(m, n)).astype(np.int8)
-    scales = (np.abs(rng.standard_normal((m, n // g))) * 0.01).astype(np.float16)
-    g_idx = rng.permutation(np.repeat(np.arange(n // g), g)).astype(np.int32)
-    want = O.dequant(codes, scales, g, g_idx=g_idx, out_dtype=np.float32)
-    got = pwq.dequant(dev(scales), n, 4, g, packed=dev(O.pack_int4(codes)), g_idx=dev(g_idx), out_dtype=torch.float32)
-    assert np.array_equal(host(got), want)
+    scales = (np.abs(rng.standard_normal((m, ng))) * 0.01).astype(np.float16)
+    g_idx = rng.permutation(np.arange(n) % ng).astype(np.int32)
+    kw = {"packed": dev(O.pack_int4(codes))} if src == "packed" else {"codes": dev(codes)}
+    got = pwq.dequant(dev(scales), n, 4, g, g_idx=dev(g_idx), out_dtype=out_dtype, **kw)
+    exact = O.dequant(codes, scales, g, g_idx=g_idx, out_dtype=np.float64)     # exact products
+    if out_dtype == torch.bfloat16:
+        want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16)
+        assert torch.equal(got.cpu().view(torch.int16), want.view(torch.int16))
+        return
+    want = exact.astype(np.float32 if out_dtype == torch.float32 else np.float16)
+    assert np.array_equal(host(got).view(np.uint8), want.view(np.uint8))
 
 
 # =============================================================================== Hessian
