@@ -529,8 +529,8 @@ def report(a, layers, m, zero_point):
     dom = max(cands, key=lambda c: c[2])
     cls, s, dms, amt, nl, pk, unit = dom
     achieved = amt / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
-    names = {"xtx": "gemm_dl_kernel<..., EpiHess> (pwq_hessian_accumulate's contraction)",
-             "update": "gemm_f32_kernel<..., EpiSub> (pwq_gptq_quantize_layer's trailing updates)",
+    names = {"xtx": "gemm_rs_kernel<2, DlTiled1, DlTiled1, UpperMap, EpiHess> (pwq_hessian_accumulate's contraction)",
+             "update": "gemm_fdl_kernel<..., EpiSub> (pwq_gptq_quantize_layer's trailing updates)",
              "rtn_quantize": "pwq_rtn_quantize", "dequant": "pwq_dequant"}
     traffic = None
     if not zero_point and cls in ("xtx", "update"):

@@ -1,5 +1,6 @@
-// Large-tile bfloat16 MFMA contraction for gfx950 with direct global -> LDS loads
-// (global_load_lds_dwordx4), float32 accumulate:
+// Large-tile bfloat16 MFMA contraction for gfx950, float32 accumulate, with operand tiles
+// copied global -> LDS directly (global_load_lds_dwordx4; gemm_dl_kernel) or, for
+// tile-major operands, staged through VGPRs (gemm_rs_kernel, at the end of this file):
 //
 //   acc(m, n) = sum_{k in [kbeg, kend)} A(m, k) * B(n, k),   A, B row-major with k contiguous.
 //
@@ -102,10 +103,14 @@ struct DlTiled {
     const uint16_t* seg[4];
     int nseg;
     int64_t kseg;
-    __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
+    // the 256 x 32 block of rows m0.. and logical k0..
+    __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
         int64_t kk = k0;
         const uint16_t* base = dl_segment(seg, nseg, kseg, kk);
-        dl_load_block(base + ((m0 >> 8) * (kseg >> 5) + (kk >> 5)) * (int64_t)(DL_TILE * DL_BK), S, wave, lane);
+        return base + ((m0 >> 8) * (kseg >> 5) + (kk >> 5)) * (int64_t)(DL_TILE * DL_BK);
+    }
+    __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
+        dl_load_block(block(m0, k0), S, wave, lane);
     }
 };
 
@@ -116,9 +121,12 @@ struct DlTiled {
 struct DlTri {
     const uint16_t* p;
     int kt;                                             // KT: k-tiles per 256 columns of the band
-    __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
+    __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
         const int64_t pan = m0 >> 8;
-        dl_load_block(p + ((int64_t)kt * (pan * (pan + 1) / 2) + (k0 >> 5)) * (int64_t)(DL_TILE * DL_BK), S, wave, lane);
+        return p + ((int64_t)kt * (pan * (pan + 1) / 2) + (k0 >> 5)) * (int64_t)(DL_TILE * DL_BK);
+    }
+    __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
+        dl_load_block(block(m0, k0), S, wave, lane);
     }
 };
 // element (r, k) of one segment in the tile-major layout
@@ -276,6 +284,178 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_dl_kernel(LA la, LB lb, MAP
         return;
     }
     gemm_dl_tile<STEADY>(la, lb, t, epi, lds);
+    epi.finish(t, threadIdx.x, true);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Register-staged variant for tile-major operands: the same LDS layout and MFMA schedule,
+// but each 16 KiB block travels global -> VGPR (four 16-byte loads per lane, every wave
+// instruction 1 KiB in one piece) -> LDS (ds_write_b128 to the swizzled position).  Three
+// LDS stages and NR register sets: tile j's loads go out NR tiles before its LDS write (set
+// j % NR), its LDS write two tiles before its MFMAs.  One barrier per tile, between the
+// halves: before it every wave has finished its reads of tile it - 1 and its writes of
+// tile it + 1; past it, tile it + 2 goes into tile it - 1's stage.  k ranges are whole
+// multiples of NR tiles (the host pads them).
+constexpr int RS_NS = 3;
+
+typedef unsigned int rs_u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const rs_u32x4* rs_gptr_t;
+
+// One k segment, tile-major as DlTiled
+struct DlTiled1 {
+    const uint16_t* p;
+    int64_t kseg;
+    __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
+        return p + ((m0 >> 8) * (kseg >> 5) + (k0 >> 5)) * (int64_t)(DL_TILE * DL_BK);
+    }
+};
+
+// Four k segments of kseg each, tile-major as DlTiled (logical k in [s kseg, (s+1) kseg)
+// reads seg[s]); the segment is picked by selects, so the loop stays one basic block
+struct DlTiled4 {
+    const uint16_t* seg[4];
+    int64_t kseg;
+    __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
+        const int sg = (int)(k0 >= kseg) + (int)(k0 >= 2 * kseg) + (int)(k0 >= 3 * kseg);
+        const uint16_t* p = sg == 0 ? seg[0] : seg[1];
+        p = sg == 2 ? seg[2] : p;
+        p = sg == 3 ? seg[3] : p;
+        return p + ((m0 >> 8) * (kseg >> 5) + ((k0 - sg * kseg) >> 5)) * (int64_t)(DL_TILE * DL_BK);
+    }
+};
+
+__device__ __forceinline__ void rs_fetch(const uint16_t* blk, rs_u32x4* r, int tid) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *(rs_gptr_t)(blk + (q * 256 + tid) * 8);
+}
+
+// chunk q 256 + tid of the block is row q 64 + tid / 4, logical chunk tid % 4
+__device__ __forceinline__ void rs_store(uint16_t* S, const rs_u32x4* r, int tid) {
+    uint16_t* d = S + dl_off(tid >> 2, tid & 3);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *(rs_u32x4*)(d + q * 64 * DL_BK) = r[q];
+}
+
+// s_waitcnt with only the LDS / scalar-memory count constrained: lgkmcnt == 0
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int NR, class LA, class LB, class EPI>
+__device__ __forceinline__ void gemm_rs_tile(const LA& la, const LB& lb, const Tile& t, EPI& epi, uint16_t* lds) {
+    constexpr int FM = 4, FN = 4;
+    constexpr int AB = DL_TILE * DL_BK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int64_t nk = (t.kend - t.kbeg) / DL_BK;
+    auto kof = [&](int64_t kt) { return t.kbeg + (kt < nk ? kt : nk - 1) * DL_BK; };
+    rs_u32x4 ra[NR][4], rb[NR][4];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        rs_fetch(la.block(t.m0, kof(r)), ra[r], tid);
+        rs_fetch(lb.block(t.n0, kof(r)), rb[r], tid);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        rs_store(lds + r * DL_STAGE, ra[r], tid);
+        rs_store(lds + r * DL_STAGE + AB, rb[r], tid);
+        rs_fetch(la.block(t.m0, kof(NR + r)), ra[r], tid);
+        rs_fetch(lb.block(t.n0, kof(NR + r)), rb[r], tid);
+    }
+    wait_lgkm0();
+    barrier_nofence();
+
+    const int arow = wm * 128 + (lane & 31);
+    const int brow = wn * 128 + (lane & 31);
+    const int half = lane >> 5;
+    bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a0[i] = *(const bf16x8*)(lds + dl_off(arow + 32 * i, half));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b0[j] = *(const bf16x8*)(lds + AB + dl_off(brow + 32 * j, half));
+
+    int sc = 0, sn = 1, sw = 2;                          // stages of tiles it, it + 1, it + 2
+    for (int64_t it0 = 0; it0 < nk; it0 += NR) {
+#pragma unroll
+        for (int u = 0; u < NR; ++u) {
+            const int64_t it = it0 + u;
+            const int r = (u + 2) % NR;                  // register set of tile it + 2
+            const uint16_t* As = lds + sc * DL_STAGE;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a1[i] = *(const bf16x8*)(As + dl_off(arow + 32 * i, 2 + half));
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b1[j] = *(const bf16x8*)(As + AB + dl_off(brow + 32 * j, 2 + half));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+            dl_interleave<0>();
+            __builtin_amdgcn_sched_barrier(0);
+            wait_lgkm0();
+            barrier_nofence();
+            uint16_t* Sw = lds + sw * DL_STAGE;
+            rs_store(Sw, ra[r], tid);
+            rs_store(Sw + AB, rb[r], tid);
+            rs_fetch(la.block(t.m0, kof(it + 2 + NR)), ra[r], tid);
+            rs_fetch(lb.block(t.n0, kof(it + 2 + NR)), rb[r], tid);
+            const uint16_t* An = lds + sn * DL_STAGE;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a0[i] = *(const bf16x8*)(An + dl_off(arow + 32 * i, half));
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b0[j] = *(const bf16x8*)(An + AB + dl_off(brow + 32 * j, half));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const int s0 = sc;
+            sc = sn;
+            sn = sw;
+            sw = s0;
+        }
+    }
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t r0 = t.m0 + wm * 128 + i * 32 + 4 * (lane >> 5);
+            const int64_t col = t.n0 + wn * 128 + j * 32 + (lane & 31);
+            epi_block16(epi, t, acc[i][j], [&](int v) { return r0 + 8 * (v >> 2) + (v & 3); }, col);
+        }
+}
+
+template <int NR, class LA, class LB, class MAP, class EPI>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_rs_kernel(LA la, LB lb, MAP map, EPI epi) {
+    if (map.guard && *map.guard != 0) return;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[RS_NS * DL_STAGE];
+    Tile t;
+    if (!map.get((int)blockIdx.x, DL_TILE, DL_TILE, t)) {
+        epi.finish(t, threadIdx.x, false);
+        return;
+    }
+    gemm_rs_tile<NR>(la, lb, t, epi, lds);
     epi.finish(t, threadIdx.x, true);
 }
 

@@ -4,12 +4,14 @@
 // section "Running GPTQ with AutoGPTQ").
 //
 // The contraction runs over the upper-triangular tiles of H only, accumulating in float32.
-// bfloat16 X: bfloat16 MFMA (products exact), large problems on the 256 x 256 direct-load
-// engine through a transposed copy.  float32 X: small problems on the float32 MFMA engine;
-// larger ones as the four products of a bfloat16 pair X = XH + XL on the direct-load engine
-// (each product exact; only X's residual below 2^-17 relative is dropped).  Small d_in gives few tiles, so the token range is cut into chunks whose partial
-// tiles land in a workspace and are summed in a fixed order (bit-reproducible, no
-// atomics).  A last pass copies the upper triangle onto the lower one.
+// bfloat16 X: bfloat16 MFMA (products exact), large problems on the 256 x 256 engine
+// through a transposed, tile-major copy (operand tiles staged global -> VGPR -> LDS).
+// float32 X: small problems on the float32 MFMA engine; larger ones as the four products of
+// a bfloat16 pair X = XH + XL on the same 256 x 256 engine (each product exact; only X's
+// residual below 2^-17 relative is dropped).  Small d_in gives few tiles, so the token
+// range is cut into chunks whose partial tiles land in a workspace and are summed in a
+// fixed order (bit-reproducible, no atomics).  A last pass copies the upper triangle onto
+// the lower one.
 #include "gemm_bf16_dl.h"
 #include "../../include/pwq.h"
 #include "pwq_internal.h"
@@ -268,13 +270,13 @@ __global__ __launch_bounds__(256) void transpose_split_f32_kernel(const float* _
     }
 }
 
-// workgroups of the direct-load Hessian in the per-XCD order of UpperMap (xcd set)
+// workgroups of the 256 x 256 Hessian in the per-XCD order of UpperMap (xcd set)
 int hess_dl_grid(const HessPlan& pl, int ntile) {
     const int nsplit = pl.full < ntile ? (ntile - pl.full) * pl.splits : 0;
     return 8 * ((pl.full + 7) / 8 + (nsplit + 7) / 8);
 }
 
-// bfloat16 X on the direct-load engine: both operands are rows of the transposed copy
+// bfloat16 X on the 256 x 256 engine: both operands are rows of the transposed copy
 // (stored tile-major, zero past n_tok and past n), 256 x 256 upper tiles
 hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, uint16_t* XT, float* part,
                         const HessPlan& pl, hipStream_t s) {
@@ -283,20 +285,23 @@ hipError_t hess_gemm_dl(const void* X, int64_t n_tok, int64_t n, int64_t ldx, fl
                        dim3(256), 0, s, (const uint16_t*)X, n_tok, n, ldx, vec, XT, pl.npad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    DlTiled op{{XT, nullptr, nullptr, nullptr}, 1, pl.npad};
+    DlTiled1 op{XT, pl.npad};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
     // work items in L2-friendly bands, an equal share per XCD
     UpperMap map{n, pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, 1};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
     const int nwg = hess_dl_grid(pl, ntile);
     prof_begin(PWQ_PROF_XTX, s);
-    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess, true>), dim3(nwg), dim3(GEMM_THREADS),
+    // register-staged loads, two tiles per unrolled step: k ranges are whole multiples of
+    // 64 (npad and kchunk are)
+    static_assert(BK16 % (2 * DL_BK) == 0, "k chunks must hold whole pairs of k-tiles");
+    hipLaunchKernelGGL((gemm_rs_kernel<2, DlTiled1, DlTiled1, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, op, op, map, epi);
     prof_end(PWQ_PROF_XTX, s, (double)n_tok * n * (n + 1));
     return hipGetLastError();
 }
 
-// float32 X on the direct-load engine: X = XH + XL (+ a residual below 2^-17 |x|), and
+// float32 X on the 256 x 256 engine: X = XH + XL (+ a residual below 2^-17 |x|), and
 // X^T X = XH XH^T + XH XL^T + XL XH^T + XL XL^T, all four products exact in float32, summed
 // by one contraction over four k segments (A: XH XH XL XL, B: XH XL XH XL)
 hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, float* H, uint16_t* XH, float* part,
@@ -307,15 +312,15 @@ hipError_t hess_gemm_dl4(const void* X, int64_t n_tok, int64_t n, int64_t ldx, f
                        dim3(256), 0, s, (const float*)X, n_tok, n, ldx, vec, XH, XL, pl.npad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    DlTiled a{{XH, XH, XL, XL}, 4, pl.npad};
-    DlTiled b{{XH, XL, XH, XL}, 4, pl.npad};
+    DlTiled4 a{{XH, XH, XL, XL}, pl.npad};
+    DlTiled4 b{{XH, XL, XH, XL}, pl.npad};
     const int ntile = pl.tiles * (pl.tiles + 1) / 2;
     // work items in L2-friendly bands, an equal share per XCD
     UpperMap map{n, 4 * pl.npad, pl.tiles, pl.splits, pl.kchunk, nullptr, pl.full, 1};
     EpiHess epi{H, part, n, pl.full, ntile - pl.full, DL_TILE};
     const int nwg = hess_dl_grid(pl, ntile);
     prof_begin(PWQ_PROF_XTX, s);
-    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTiled, UpperMap, EpiHess, true>), dim3(nwg), dim3(GEMM_THREADS),
+    hipLaunchKernelGGL((gemm_rs_kernel<2, DlTiled4, DlTiled4, UpperMap, EpiHess>), dim3(nwg), dim3(GEMM_THREADS),
                        0, s, a, b, map, epi);
     prof_end(PWQ_PROF_XTX, s, (double)n_tok * n * (n + 1));
     return hipGetLastError();

@@ -288,8 +288,8 @@ hipError_t mse_launch(const void* X, int x_dtype, int64_t n_tok, int64_t d_in, i
 // of 256 x 256: H symmetric gives tr(dW H dW^T) = sum_i sum_c dW[i][c] (dW G)[i][c] with
 // G = diag(H) + 2 (strict upper part of H), so output column block cb only contracts over
 // the column blocks 0 .. cb (half the products).  That product runs on the bfloat16
-// direct-load engine as a three-term split: a = a_hi + a_lo (each bfloat16, a_hi = bf16(a),
-// a_lo = bf16(a - a_hi), so |a - a_hi - a_lo| <= 2^-18 |a|), and
+// 256 x 256 engine (register-staged) as a three-term split: a = a_hi + a_lo (each
+// bfloat16, a_hi = bf16(a), a_lo = bf16(a - a_hi), so |a - a_hi - a_lo| <= 2^-18 |a|), and
 // a b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi, each product exact in float32, the dropped terms
 // (a_lo b_lo and the residuals) below 2^-16 |a b| and of either sign.  The three pieces are
 // interleaved per 256-column block jb along k (k = 768 jb + 256 s + offset, pieces s = 0, 1,
@@ -500,12 +500,14 @@ hipError_t split_pieces_launch(const float* dW, int64_t ld, int64_t m, int64_t n
 hipError_t split_trace_launch(const uint16_t* a3, const uint16_t* b3, const float* dW, int64_t ld, int64_t m, int64_t n,
                               const float* shift, double* part, hipStream_t s) {
     const int64_t mpad = cdiv(m, DL_TILE) * DL_TILE, npad = cdiv(n, DL_TILE) * DL_TILE;
-    DlTiled a{{a3, nullptr, nullptr, nullptr}, 1, 3 * npad};
+    DlTiled1 a{a3, 3 * npad};
     DlTri b{b3, SPLIT_KT};
     SplitTriMap mp{(int)(mpad / DL_TILE), (int)(npad / DL_TILE), nullptr};
     EpiTrace ep{dW, ld, m, n, part, shift, 0.f};
-    hipLaunchKernelGGL((gemm_dl_kernel<DlTiled, DlTri, SplitTriMap, EpiTrace>), dim3((unsigned)((mpad / DL_TILE) * (npad / DL_TILE))),
-                       dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
+    // register-staged loads, two k-tiles per unrolled step: every k range is 768 (cb + 1)
+    static_assert((SPLIT_KT * DL_BK) % (2 * DL_BK) == 0, "k ranges must hold whole pairs of k-tiles");
+    hipLaunchKernelGGL((gemm_rs_kernel<2, DlTiled1, DlTri, SplitTriMap, EpiTrace>),
+                       dim3((unsigned)((mpad / DL_TILE) * (npad / DL_TILE))), dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
     return hipGetLastError();
 }
 
