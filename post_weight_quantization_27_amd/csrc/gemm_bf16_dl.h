@@ -1,29 +1,29 @@
-// Large-tile bfloat16 MFMA contraction for gfx950, float32 accumulate, with operand tiles
-// copied global -> LDS directly (global_load_lds_dwordx4; gemm_dl_kernel) or, for
-// tile-major operands, staged through VGPRs (gemm_rs_kernel, at the end of this file):
+// Large-tile bfloat16 MFMA contraction for gfx950, float32 accumulate:
 //
 //   acc(m, n) = sum_{k in [kbeg, kend)} A(m, k) * B(n, k),   A, B row-major with k contiguous.
 //
 // 256 threads (4 wave64 in 2 x 2) own a 256 x 256 tile; a wave owns 128 x 128 as 4 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16, i.e. 8 operand fragments (16-byte LDS reads) per 16 MFMAs: half
-// the LDS read traffic per MFMA of a 64 x 64 wave tile.  Operand tiles of 32 k are copied by
-// the load unit straight into LDS (no staging registers, which leaves room for 256
-// accumulators per lane): one wave instruction moves 16 rows x 64 bytes, lane i carrying
-// row i / 4 and the 16-byte chunk that lands at position i % 4.  Row r keeps its chunk c at
-// position c ^ ((r / 4) % 4), the swizzle the fragment reads undo (8 or 16 consecutive rows
-// of one chunk then hit distinct banks).
+// the LDS read traffic per MFMA of a 64 x 64 wave tile.  An operand tile of 32 k sits in LDS
+// as 256 rows of 64 bytes; row r keeps its 16-byte chunk c at position c ^ ((r / 4) % 4), the
+// swizzle the fragment reads undo (8 or 16 consecutive rows of one chunk then hit distinct
+// banks).  One barrier per k-tile, placed after the first half of the tile's MFMAs, so
+// neither the barrier nor the first LDS reads of a tile stand between two tiles' MFMAs.
 //
-// Four LDS stages (128 KiB), one barrier per k-tile, placed after the first half of the
-// tile's MFMAs: past it, every wave has its share of the next tile in LDS and is done with
-// the tile before this one, whose stage then takes the loads three tiles ahead; the next
-// tile's first fragments are read while the second half's MFMAs issue.  So neither the
-// barrier nor the first LDS reads of a tile stand between two tiles' MFMAs.
+// Two copy paths into that layout:
+// * gemm_dl_kernel (rows of any length, DlRows): the load unit copies straight into LDS
+//   (global_load_lds_dwordx4, no staging registers): one wave instruction moves 16 rows x
+//   64 bytes, lane i carrying row i / 4 and the chunk that lands at position i % 4.  Four
+//   LDS stages (128 KiB); past the barrier of tile it, tile it - 1's stage takes the loads
+//   three tiles ahead.
+// * gemm_rs_kernel (tile-major operands, at the end of this file): loads into VGPRs, then
+//   ds_write_b128.  Faster on the Hessian's and the trace product's long k ranges.
 //
-// Operand requirements (checked by the host side): ld % 8 == 0, 16-byte aligned bases, k
-// ranges in whole tiles of 32, and for every k at or past an operand's K inside a segment
-// the OTHER operand is 0 there (a chunk start is clamped to K - 8, so reads stay inside the
-// row; rows at or past M are clamped to M - 1, and their outputs are discarded by the
-// epilogue).
+// Operand requirements of DlRows (checked by the host side): ld % 8 == 0, 16-byte aligned
+// bases, k ranges in whole tiles of 32, and for every k at or past an operand's K inside a
+// segment the OTHER operand is 0 there (a chunk start is clamped to K - 8, so reads stay
+// inside the row; rows at or past M are clamped to M - 1, and their outputs are discarded by
+// the epilogue).
 #pragma once
 
 #include "gemm_bf16.h"
@@ -80,37 +80,35 @@ struct DlRows {
     }
 };
 
-// one 256 x 32 tile-major block (16 KiB in one piece) into the stage tile S, swizzled: wave
-// w issues the four 16-row groups g = w + 4 q, lane i carrying row i / 4 and the chunk that
-// lands at position i % 4
-__device__ __forceinline__ void dl_load_block(const uint16_t* blk, uint16_t* S, int wave, int lane) {
-    const int pc = lane & 3, rl = lane >> 2;
-    const int lc = pc ^ ((rl >> 2) & 3);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r0 = 16 * (wave + 4 * q);
-        dl_load16(blk + (r0 + rl) * DL_BK + 8 * lc, S + r0 * DL_BK);
-    }
-}
+// Tile-major rows (the operands of the register-staged engine at the end of this file):
+// the k-tile kt (32 k) of the 256-row panel P is one contiguous 256 x 32 block, element
+// (r, k) of a segment at ((r / 256) kpan + k / 32) 8192 + (r % 256) 32 + k % 32,
+// kpan = kseg / 32.  A tile's load then reads 16 KiB in one piece (each instruction 1 KiB),
+// instead of 256 rows a whole row length apart.  Rows are padded to whole panels and k to
+// whole segments (the writer zeroes both), so nothing is clamped; tile row offsets m0 are
+// multiples of 256.
 
-// Rows stored tile-major: the k-tile kt (32 k) of the 256-row panel P is one contiguous
-// 256 x 32 block, element (r, k) of a segment at ((r / 256) kpan + k / 32) 8192 +
-// (r % 256) 32 + k % 32, kpan = kseg / 32.  A tile's load then reads 16 KiB in one piece
-// (each instruction 1 KiB), instead of 256 rows a whole row length apart.  Rows are padded
-// to whole panels and k to whole segments (the writer zeroes both), so nothing is clamped.
-// Up to four k segments as in DlRows; tile row offsets m0 are multiples of 256.
-struct DlTiled {
-    const uint16_t* seg[4];
-    int nseg;
+// One k segment
+struct DlTiled1 {
+    const uint16_t* p;
     int64_t kseg;
-    // the 256 x 32 block of rows m0.. and logical k0..
+    // the 256 x 32 block of rows m0.. and k0..
     __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
-        int64_t kk = k0;
-        const uint16_t* base = dl_segment(seg, nseg, kseg, kk);
-        return base + ((m0 >> 8) * (kseg >> 5) + (kk >> 5)) * (int64_t)(DL_TILE * DL_BK);
+        return p + ((m0 >> 8) * (kseg >> 5) + (k0 >> 5)) * (int64_t)(DL_TILE * DL_BK);
     }
-    __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
-        dl_load_block(block(m0, k0), S, wave, lane);
+};
+
+// Four k segments of kseg each (logical k in [s kseg, (s+1) kseg) reads seg[s]); the
+// segment is picked by selects, so the loop stays one basic block
+struct DlTiled4 {
+    const uint16_t* seg[4];
+    int64_t kseg;
+    __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
+        const int sg = (int)(k0 >= kseg) + (int)(k0 >= 2 * kseg) + (int)(k0 >= 3 * kseg);
+        const uint16_t* p = sg == 0 ? seg[0] : seg[1];
+        p = sg == 2 ? seg[2] : p;
+        p = sg == 3 ? seg[3] : p;
+        return p + ((m0 >> 8) * (kseg >> 5) + ((k0 - sg * kseg) >> 5)) * (int64_t)(DL_TILE * DL_BK);
     }
 };
 
@@ -124,9 +122,6 @@ struct DlTri {
     __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
         const int64_t pan = m0 >> 8;
         return p + ((int64_t)kt * (pan * (pan + 1) / 2) + (k0 >> 5)) * (int64_t)(DL_TILE * DL_BK);
-    }
-    __device__ __forceinline__ void load(uint16_t* S, int64_t m0, int64_t k0, int wave, int lane) const {
-        dl_load_block(block(m0, k0), S, wave, lane);
     }
 };
 // element (r, k) of one segment in the tile-major layout
@@ -170,11 +165,7 @@ __device__ __forceinline__ void dl_interleave() {
     if constexpr (NV < 8) __builtin_amdgcn_sched_group_barrier(0x008, 8 - NV, 0);
 }
 
-// STEADY: every iteration issues the same eight copies per wave (past the last tile they
-// repeat it into a stage nothing reads any more) and waits the same way, and the copies go
-// out between the second half's MFMAs; measured faster for the long, uniform k ranges of
-// the Hessian, slower for the error products.
-template <bool STEADY, class LA, class LB, class EPI>
+template <class LA, class LB, class EPI>
 __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const Tile& t, EPI& epi, uint16_t* lds) {
     constexpr int FM = 4, FN = 4;
     constexpr int AB = DL_TILE * DL_BK;                  // B's offset inside a stage
@@ -191,18 +182,17 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int64_t nk = (t.kend - t.kbeg) / DL_BK;        // host guarantees whole tiles
-    auto kof = [&](int64_t kt) { return t.kbeg + (kt < nk ? kt : nk - 1) * DL_BK; };
     // tiles 0 .. 2 into stages 0 .. 2 (eight load instructions per wave and tile)
 #pragma unroll
     for (int st = 0; st < DL_NS - 1; ++st)
-        if (STEADY || st < nk) {
-            la.load(lds + st * DL_STAGE, t.m0, kof(st), wave, lane);
-            lb.load(lds + st * DL_STAGE + AB, t.n0, kof(st), wave, lane);
+        if (st < nk) {
+            la.load(lds + st * DL_STAGE, t.m0, t.kbeg + st * DL_BK, wave, lane);
+            lb.load(lds + st * DL_STAGE + AB, t.n0, t.kbeg + st * DL_BK, wave, lane);
         }
     const int arow = wm * 128 + (lane & 31);
     const int brow = wn * 128 + (lane & 31);
     const int half = lane >> 5;
-    if (STEADY || nk > 2) wait_vmcnt<16>();
+    if (nk > 2) wait_vmcnt<16>();
     else if (nk == 2) wait_vmcnt<8>();
     else wait_vmcnt<0>();
     barrier_nofence();
@@ -224,13 +214,7 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
         dl_interleave<0>();
-        if constexpr (STEADY) {
-            wait_vmcnt<8>();
-            barrier_nofence();
-            uint16_t* Sn = lds + ((it + 3) & 3) * DL_STAGE;
-            la.load(Sn, t.m0, kof(it + 3), wave, lane);
-            lb.load(Sn + AB, t.n0, kof(it + 3), wave, lane);
-        } else if (it + 1 < nk) {
+        if (it + 1 < nk) {
             // this wave's share of tile it + 1 has landed (tile it + 2 may still fly); past the
             // barrier every wave's has, and every wave is done with tile it - 1
             if (it + 2 < nk) wait_vmcnt<8>();
@@ -254,7 +238,7 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-        dl_interleave<STEADY ? 8 : 0>();
+        dl_interleave<0>();
         // keep those reads in this iteration (not sunk into the next one's first MFMAs), and
         // their wait after this half's MFMAs
         __builtin_amdgcn_sched_barrier(0);
@@ -263,7 +247,6 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
 #pragma unroll
         for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b0[j]));
     }
-    if constexpr (STEADY) wait_vmcnt<0>();               // no copy may land after the workgroup ends
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -274,7 +257,7 @@ __device__ __forceinline__ void gemm_dl_tile(const LA& la, const LB& lb, const T
         }
 }
 
-template <class LA, class LB, class MAP, class EPI, bool STEADY = false>
+template <class LA, class LB, class MAP, class EPI>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_dl_kernel(LA la, LB lb, MAP map, EPI epi) {
     if (map.guard && *map.guard != 0) return;
     __shared__ __attribute__((aligned(16))) uint16_t lds[DL_NS * DL_STAGE];
@@ -283,7 +266,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_dl_kernel(LA la, LB lb, MAP
         epi.finish(t, threadIdx.x, false);
         return;
     }
-    gemm_dl_tile<STEADY>(la, lb, t, epi, lds);
+    gemm_dl_tile(la, lb, t, epi, lds);
     epi.finish(t, threadIdx.x, true);
 }
 
@@ -300,29 +283,6 @@ constexpr int RS_NS = 3;
 
 typedef unsigned int rs_u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const rs_u32x4* rs_gptr_t;
-
-// One k segment, tile-major as DlTiled
-struct DlTiled1 {
-    const uint16_t* p;
-    int64_t kseg;
-    __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
-        return p + ((m0 >> 8) * (kseg >> 5) + (k0 >> 5)) * (int64_t)(DL_TILE * DL_BK);
-    }
-};
-
-// Four k segments of kseg each, tile-major as DlTiled (logical k in [s kseg, (s+1) kseg)
-// reads seg[s]); the segment is picked by selects, so the loop stays one basic block
-struct DlTiled4 {
-    const uint16_t* seg[4];
-    int64_t kseg;
-    __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
-        const int sg = (int)(k0 >= kseg) + (int)(k0 >= 2 * kseg) + (int)(k0 >= 3 * kseg);
-        const uint16_t* p = sg == 0 ? seg[0] : seg[1];
-        p = sg == 2 ? seg[2] : p;
-        p = sg == 3 ? seg[3] : p;
-        return p + ((m0 >> 8) * (kseg >> 5) + ((k0 - sg * kseg) >> 5)) * (int64_t)(DL_TILE * DL_BK);
-    }
-};
 
 __device__ __forceinline__ void rs_fetch(const uint16_t* blk, rs_u32x4* r, int tid) {
 #pragma unroll

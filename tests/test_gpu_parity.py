@@ -197,7 +197,8 @@ def _hess(pwq, X_dev, d_in, tiles=None):
     return H
 
 
-@pytest.mark.parametrize("n_tok,d_in", [(1280, 768), (8192, 3072), (1000, 200), (1, 5), (33, 1030), (8192, 768)])
+@pytest.mark.parametrize("n_tok,d_in", [(1280, 768), (8192, 3072), (1000, 200), (1, 5), (33, 1030), (8192, 768),
+                                         (2080, 1030)])   # bf16-pair path: ragged last panel, 2080 tokens padded to 2112
 def test_hessian_f32(pwq, n_tok, d_in):
     rng = np.random.default_rng(n_tok + d_in)
     X = rng.standard_normal((n_tok, d_in)).astype(np.float32)
