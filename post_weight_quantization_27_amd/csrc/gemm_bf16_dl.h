@@ -277,8 +277,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_dl_kernel(LA la, LB lb, MAP
 // LDS stages and NR register sets: tile j's loads go out NR tiles before its LDS write (set
 // j % NR), its LDS write two tiles before its MFMAs.  One barrier per tile, between the
 // halves: before it every wave has finished its reads of tile it - 1 and its writes of
-// tile it + 1; past it, tile it + 2 goes into tile it - 1's stage.  k ranges are whole
-// multiples of NR tiles (the host pads them).
+// tile it + 1; past it, tile it + 2 goes into tile it - 1's stage.  Every step issues the
+// same loads and writes: past the last tile they repeat it, into stages nothing reads any
+// more, so the loop has no branch and the compiler can count the loads in flight.  k ranges
+// are whole multiples of NR tiles (the host pads them).
 constexpr int RS_NS = 3;
 
 typedef unsigned int rs_u32x4 __attribute__((ext_vector_type(4)));
