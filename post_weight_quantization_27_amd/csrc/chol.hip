@@ -849,6 +849,34 @@ hipError_t launch_update_diag(float* U, const float* P, int pld, int64_t n, int6
     return hipGetLastError();
 }
 
+// 64 x 64 tiles of a block's trsm and finalize above which they take 128 x 128 tiles
+constexpr int64_t PANEL64_MAX_TILES = 256;
+
+// block k's trsm (rows above, into its panel slot Pk) + finalize (block row k right of the
+// diagonal), with block k's update of the next diagonal block in workgroups [0, PRE_TILES)
+// when `fuse`, on T x T tiles
+template <int T>
+hipError_t launch_panel(float* U, float* Pk, int pld, int64_t n, int64_t k0, int bs, int64_t r, bool fuse, int vu,
+                        int32_t* info, hipStream_t s) {
+    GemmTask<T, T, OpMMajor<0>, OpMMajor<0>, RectMap, EpiStore> tt{};
+    tt.la = OpMMajor<0>{U + k0, n, k0, bs, vu && (k0 % 4 == 0)};
+    tt.lb = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
+    tt.map = rect(T, T, k0, bs, bs);
+    tt.epi = EpiStore{Pk, pld, k0, bs, 1.f};
+    GemmTask<T, T, OpMMajor<0>, OpKMajor<0>, RectMap, EpiStore> ft{};
+    ft.la = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
+    ft.lb = OpKMajor<0>{U + k0 * n + k0 + bs, n, r, bs, vu && ((k0 + bs) % 4 == 0)};
+    ft.map = rect(T, T, bs, r, bs);
+    ft.epi = EpiStore{U + k0 * n + k0 + bs, n, bs, r, -1.f};
+    const int n0 = fuse ? PRE_TILES : 0;
+    const int n1 = k0 > 0 ? ntiles(tt.map) : 0;
+    const int n2 = r > 0 ? ntiles(ft.map) : 0;
+    if (n0 + n1 + n2 == 0) return hipSuccess;
+    hipLaunchKernelGGL((chol_panel_kernel<decltype(tt), decltype(ft)>), dim3(n0 + n1 + n2), dim3(GEMM_THREADS), 0, s, tt,
+                       ft, n0, n1, info, U, n, k0, bs);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t chol_ws_bytes(int64_t n) { return (size_t)n * (chol_sb(n) * CHOL_NB) * sizeof(float); }
@@ -923,25 +951,13 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
         // the trsm launch, and its factor in the near launch
         const bool fuse = kb > kb_lo && k0 > 0;
 
-        // trsm (rows above) + finalize (block row k of U, right of the diagonal)
-        TrsmTask tt{};
-        tt.la = OpMMajor<0>{U + k0, n, k0, bs, vu && (k0 % 4 == 0)};
-        tt.lb = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
-        tt.map = rect(64, 64, k0, bs, bs);
-        tt.epi = EpiStore{Pk, pld, k0, bs, 1.f};
-        FinalizeTask ft{};
-        ft.la = OpMMajor<0>{U + k0 * n + k0, n, bs, bs, vu && (k0 % 4 == 0)};
-        ft.lb = OpKMajor<0>{U + k0 * n + k0 + bs, n, r, bs, vu && ((k0 + bs) % 4 == 0)};
-        ft.map = rect(64, 64, bs, r, bs);
-        ft.epi = EpiStore{U + k0 * n + k0 + bs, n, bs, r, -1.f};
-        const int n0 = fuse ? PRE_TILES : 0;
-        const int n1 = k0 > 0 ? ntiles(tt.map) : 0;
-        const int n2 = r > 0 ? ntiles(ft.map) : 0;
-        if (n0 + n1 + n2 > 0) {
-            hipLaunchKernelGGL((chol_panel_kernel<TrsmTask, FinalizeTask>), dim3(n0 + n1 + n2), dim3(GEMM_THREADS), 0, s,
-                               tt, ft, n0, n1, info, U, n, k0, bs);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
+        // trsm (rows above) + finalize (block row k of U, right of the diagonal): 64 x 64 tiles
+        // while they fit one round on the chip (the launch's LDS allows one workgroup per CU),
+        // 128 x 128 tiles past that
+        const int64_t tiles64 = cdiv(k0, 64) * cdiv(bs, 64) + cdiv(bs, 64) * cdiv(r, 64);
+        e = tiles64 > PANEL64_MAX_TILES ? launch_panel<128>(U, Pk, pld, n, k0, bs, r, fuse, vu, info, s)
+                                        : launch_panel<64>(U, Pk, pld, n, k0, bs, r, fuse, vu, info, s);
+        if (e != hipSuccess) return e;
         diag_done = false;
         if (k0 == 0) break;
         if (fuse) {
