@@ -370,8 +370,8 @@ pwq_status pwq_awq_search(const void* W, int w_dtype, int64_t d_out, int64_t d_i
  * What is never rounded: each group's sum of x (code - zero) is formed from exact products
  * (float16 MFMA on the small integer codes) and scaled once by its scale, in float32; the
  * result is rounded once to y_dtype.
- *   X       n_tok x d_in float16 (x_dtype PWQ_F16), leading dimension ldx (a multiple of 8),
- *           16-byte aligned.
+ *   X       n_tok x d_in float16 (x_dtype PWQ_F16), leading dimension ldx (a multiple of 8,
+ *           at most 2^24), 16-byte aligned.
  *   packed  d_out x d_in/2 (d_in a multiple of 32), 16-byte aligned; columns in their
  *           original order (no g_idx: a layer quantized with act-order is served by its
  *           dequantized weights).

@@ -24,6 +24,7 @@ pwq_status hip_status(hipError_t e) {
 constexpr int64_t MAX_DIM = (int64_t)1 << 30;
 
 bool bad_dim(int64_t v) { return v < 0 || v > MAX_DIM; }
+constexpr int64_t QMM_MAX_COLS = (int64_t)1 << 24;     // ldx (>= d_in) of the quantized product
 
 bool group_ok(int32_t g, int64_t d_in) {
     (void)d_in;
@@ -453,7 +454,7 @@ pwq_status pwq_quantized_matmul(const void* X, int x_dtype, int64_t n_tok, int64
     if (x_dtype != PWQ_F16) return PWQ_EDTYPE;
     if (y_dtype != PWQ_F32 && y_dtype != PWQ_F16 && y_dtype != PWQ_BF16) return PWQ_EDTYPE;
     if (bad_dim(n_tok) || bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldx < d_in || ldy < d_out) return PWQ_EINVAL;
-    if (n_tok > (int64_t)65535 * 16 || d_in % 32 != 0 || ldx % 8 != 0) return PWQ_EINVAL;
+    if (n_tok > (int64_t)65535 * 16 || d_in % 32 != 0 || ldx % 8 != 0 || ldx > QMM_MAX_COLS) return PWQ_EINVAL;
     if (group_size != 0 && (group_size < 0 || group_size % 128 != 0)) return PWQ_EINVAL;
     if (n_tok == 0 || d_out == 0) return PWQ_OK;
     if (!packed || !scales || !Y) return PWQ_EINVAL;
@@ -471,7 +472,7 @@ pwq_status pwq_quantized_matmul_noalloc(const void* X, int x_dtype, int64_t n_to
     if (x_dtype != PWQ_F16) return PWQ_EDTYPE;
     if (y_dtype != PWQ_F32 && y_dtype != PWQ_F16 && y_dtype != PWQ_BF16) return PWQ_EDTYPE;
     if (bad_dim(n_tok) || bad_dim(d_out) || d_in <= 0 || bad_dim(d_in) || ldx < d_in || ldy < d_out) return PWQ_EINVAL;
-    if (n_tok > (int64_t)65535 * 16 || d_in % 32 != 0 || ldx % 8 != 0) return PWQ_EINVAL;
+    if (n_tok > (int64_t)65535 * 16 || d_in % 32 != 0 || ldx % 8 != 0 || ldx > QMM_MAX_COLS) return PWQ_EINVAL;
     if (group_size != 0 && (group_size < 0 || group_size % 128 != 0)) return PWQ_EINVAL;
     if (n_tok == 0 || d_out == 0) return PWQ_OK;
     if (!packed || !scales || !Y) return PWQ_EINVAL;

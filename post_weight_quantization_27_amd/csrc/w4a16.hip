@@ -43,6 +43,7 @@ constexpr int W4_CHUNK = 128;      // columns per step of a wave
 constexpr int W4_ROWS = 32;        // rows per wave (two 16-row MFMA tiles)
 constexpr int W4_TOK = 16;         // tokens per wave
 constexpr int W4_MAXC = 8;         // steps per split (all loaded at once); 4 * 32 * W4_MAXC a multiple of 256
+constexpr int64_t W4_MAX_COLS = (int64_t)1 << 24;   // d_in and ldx limit (32-bit buffer ranges)
 
 struct W4Args {
     const uint16_t* X;             // float16 bits, T x n, leading dimension ldx
@@ -59,6 +60,22 @@ struct W4Args {
 };
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// Buffer loads with a range: an offset at or past `bytes` reads 0.  Loads that are out of
+// range (past the rows, columns, tokens or steps of a workgroup) take W4_OOB as their
+// offset instead of being skipped, so every load is issued unconditionally and the compiler
+// can count the loads in flight (a load behind a branch makes it wait for all of them).
+// Each range starts at the workgroup's first row or token, so it spans at most 128 rows or
+// 16 tokens; d_in and ldx up to W4_MAX_COLS keep it below 2^31 bytes.
+constexpr uint32_t W4_OOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t w4_rsrc(const void* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 w4_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 template <int YT>
 __device__ __forceinline__ void store4(void* Y, int64_t off, const float* v, int cnt) {
@@ -109,22 +126,29 @@ __global__ __launch_bounds__(256) void w4a16_kernel(W4Args a) {
     {
         const int tok = tid % W4_TOK, wd = (tid / W4_TOK) % 4, qq = tid / (4 * W4_TOK);
         const int64_t t = t0 + tok;
+        const int64_t nt = a.T - t0 < W4_TOK ? a.T - t0 : W4_TOK;
+        const __amdgpu_buffer_rsrc_t rx = w4_rsrc(a.X + t0 * a.ldx, ((nt - 1) * a.ldx + a.n) * 2);
 #pragma unroll
         for (int c = 0; c < W4_MAXC; ++c) {
             const int64_t col = (k0 + c) * W4_CHUNK + 32 * qq + 8 * wd;
-            xr[c] = (c < nk && t < a.T && col < a.n) ? *(const uint4*)(a.X + t * a.ldx + col) : make_uint4(0, 0, 0, 0);
+            const bool ok = c < nk && t < a.T && col < a.n;
+            xr[c] = w4_load16(rx, ok ? (uint32_t)(((t - t0) * a.ldx + col) * 2) : W4_OOB);
         }
     }
     constexpr int SPT = 4 * W4_ROWS * W4_MAXC / 256;        // (row, group) entries per thread
     uint16_t sv[SPT], zv[SPT];
+    const int64_t nrow = a.m - R0 < 4 * W4_ROWS ? a.m - R0 : 4 * W4_ROWS;     // rows of the workgroup
+    const __amdgpu_buffer_rsrc_t rsc = w4_rsrc(a.scales + R0 * a.ng, nrow * a.ng * 2);
+    const __amdgpu_buffer_rsrc_t rz = w4_rsrc((ZP ? a.zeros : a.scales) + R0 * a.ng, nrow * a.ng * 2);
 #pragma unroll
     for (int c = 0; c < SPT; ++c) {
         const int idx = c * 256 + tid;
         const int row = idx / W4_MAXC, gg = idx % W4_MAXC;
         const int64_t o = R0 + row;
         const bool ok = gg < ngs && o < a.m;
-        sv[c] = ok ? a.scales[o * a.ng + G0 + gg] : (uint16_t)0;
-        zv[c] = (ZP && ok) ? a.zeros[o * a.ng + G0 + gg] : (uint16_t)0;
+        const uint32_t off = ok ? (uint32_t)(((o - R0) * a.ng + G0 + gg) * 2) : W4_OOB;
+        sv[c] = __builtin_amdgcn_raw_buffer_load_b16(rsc, off, 0, 0);
+        zv[c] = ZP ? __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0) : (uint16_t)0;
     }
 
     // 2. the nibbles of every step, for this lane's rows of both tiles
@@ -136,13 +160,14 @@ __global__ __launch_bounds__(256) void w4a16_kernel(W4Args a) {
         row_ok[r] = orow[r] < a.m;
     }
     uint4 w[W4_MAXC][2];
+    const __amdgpu_buffer_rsrc_t rw = w4_rsrc(a.packed + R0 * half_n, nrow * half_n);
 #pragma unroll
     for (int c = 0; c < W4_MAXC; ++c) {
         const int64_t col = (k0 + c) * W4_CHUNK + 32 * q;
         const bool ok = c < nk && col < a.n;                // n % 32 == 0: a lane's 32 columns are all in or all out
 #pragma unroll
         for (int r = 0; r < 2; ++r)
-            w[c][r] = (ok && row_ok[r]) ? *(const uint4*)(a.packed + orow[r] * half_n + col / 2) : make_uint4(0, 0, 0, 0);
+            w[c][r] = w4_load16(rw, (ok && row_ok[r]) ? (uint32_t)((orow[r] - R0) * half_n + col / 2) : W4_OOB);
     }
 
     // 3. staging stores: X paired (c, c+2), (c+1, c+3) per four columns, like the decoded nibbles
@@ -307,6 +332,7 @@ hipError_t w4a16_launch(const uint16_t* X, int64_t T, int64_t n, int64_t ldx, co
                         const uint16_t* scales, const uint16_t* zeros, int64_t m, int group_size, void* Y,
                         int y_dtype, int64_t ldy, void* ws, hipStream_t s) {
     if (T == 0 || m == 0) return hipSuccess;
+    if (n > W4_MAX_COLS || ldx > W4_MAX_COLS) return hipErrorInvalidValue;
     const W4Plan p = w4_plan(T, n, m);
     W4Args a{};
     a.X = X; a.ldx = ldx; a.T = T; a.n = n; a.m = m;

@@ -219,6 +219,7 @@ def test_quantized_matmul_rejects(L):
     assert L.pwq_quantized_matmul_workspace_size(4, 1024, 64) == 0  # one split: no partial sums
     assert with_(n=2048, ldx=2048, ws=None) == pwq.PWQ_EWORKSPACE
     assert with_(n=2048, ldx=2048, wsb=need - 1) == pwq.PWQ_EWORKSPACE
+    assert with_(ldx=(1 << 24) + 8) == pwq.PWQ_EINVAL              # past the 32-bit load ranges
 
 
 def test_tensor_scales_rejects(L):
