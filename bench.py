@@ -407,8 +407,13 @@ def kernel_traffic(workload, layer, cls):
         e = data.get(f"{workload}/{layer}")
         if not e or e.get("source_hash") != profile_summary.source_hash():
             return None
-        k = e.get("per_kernel", {}).get(cls)
-        return None if not k or not k.get("launches") else k["hbm_bytes"] / k["launches"]
+        pk = e.get("per_kernel", {})
+        k = pk.get(cls)
+        if not k or not k.get("launches"):
+            return None
+        # the split route's bytes include its splitting kernels, per product launch
+        extra = pk.get("update_split_pieces", {}).get("hbm_bytes", 0.0) if cls == "update_split" else 0.0
+        return (k["hbm_bytes"] + extra) / k["launches"]
     except (OSError, ValueError, KeyError):
         return None
 
@@ -522,6 +527,10 @@ def report(a, layers, m, zero_point):
         if u["launches_per_step"]:
             cands.append(("update", s, u["ms_per_step"], u["work_per_step"], u["launches_per_step"], "mfma_f32",
                           "flop"))
+        u = k["update_split"]
+        if u["launches_per_step"]:
+            cands.append(("update_split", s, u["ms_per_step"], u["work_per_step"], u["launches_per_step"], "mfma_bf16",
+                          "flop"))
         for cls, call in (("rtn", "rtn_quantize"), ("dequant", "dequant")):
             k = kern[s.name][cls]
             if k["launches_per_step"]:
@@ -531,9 +540,11 @@ def report(a, layers, m, zero_point):
     achieved = amt / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
     names = {"xtx": "gemm_rs_kernel<2, DlTiled1, DlTiled1, UpperMap, EpiHess> (pwq_hessian_accumulate's contraction)",
              "update": "gemm_fdl_kernel<..., EpiSub> (pwq_gptq_quantize_layer's trailing updates)",
+             "update_split": "gemm_rs_kernel<2, DlTiled6, DlTiled6, RectMap, EpiSub> with its split kernels "
+                             "(pwq_gptq_quantize_layer's deep trailing updates on six bf16 products)",
              "rtn_quantize": "pwq_rtn_quantize", "dequant": "pwq_dequant"}
     traffic = None
-    if not zero_point and cls in ("xtx", "update"):
+    if not zero_point and cls in ("xtx", "update", "update_split"):
         tb = kernel_traffic(a.workload, s.name, cls)
         traffic = None if tb is None else tb * nl
     elif not zero_point:
@@ -554,16 +565,36 @@ def report(a, layers, m, zero_point):
         d = per.get((s.name, "hessian_accumulate"))
         if d:
             xtx_call[s.name] = round(work_of("hessian_accumulate", s)[1] / (d * 1e-3) / 1e12 / PEAK[pk], 4)
-        u = k["update"]
-        if u["ms_per_step"]:
-            tf = u["work_per_step"] / (u["ms_per_step"] * 1e-3) / 1e12
-            upd[s.name] = round(tf / PEAK["mfma_f32"], 4)
+        u, us = k["update"], k["update_split"]
+        ms_u = u["ms_per_step"] + us["ms_per_step"]
+        if ms_u:
+            # the MFMA utilisation of the update's time: each route's executed work against the
+            # peak of the pipe it runs on (float32 products; bf16 products of the split route)
+            busy_s = u["work_per_step"] / (PEAK["mfma_f32"] * 1e12) + us["work_per_step"] / (PEAK["mfma_bf16"] * 1e12)
+            upd[s.name] = round(busy_s / (ms_u * 1e-3), 4)
             alg = s.d_out * s.d_in * (s.d_in - s.block_size)
-            upd_detail[s.name] = {"ms": round(u["ms_per_step"], 3), "launches": u["launches_per_step"],
-                                  "flops": u["work_per_step"], "algorithmic_flops": alg, "TFLOP/s": round(tf, 2)}
+            # float32 work done: the split route executes six bf16 products per float32 one
+            # (its depth, 1024 error columns, is a whole multiple of 64)
+            f32_work = u["work_per_step"] + us["work_per_step"] / 6.0
+            routes = {}
+            if u["ms_per_step"]:
+                tf = u["work_per_step"] / (u["ms_per_step"] * 1e-3) / 1e12
+                routes["f32"] = {"ms": round(u["ms_per_step"], 3), "launches": u["launches_per_step"],
+                                 "flops": u["work_per_step"], "TFLOP/s": round(tf, 2),
+                                 "frac_peak": round(tf / PEAK["mfma_f32"], 4)}
+            if us["ms_per_step"]:
+                tf = us["work_per_step"] / (us["ms_per_step"] * 1e-3) / 1e12
+                routes["bf16_split"] = {"ms": round(us["ms_per_step"], 3), "launches": us["launches_per_step"],
+                                        "bf16_flops": us["work_per_step"], "TFLOP/s": round(tf, 2),
+                                        "frac_peak": round(tf / PEAK["mfma_bf16"], 4)}
+            upd_detail[s.name] = {"ms": round(ms_u, 3), "launches": u["launches_per_step"] + us["launches_per_step"],
+                                  "algorithmic_flops": alg, "f32_flops_done": f32_work,
+                                  "f32_equivalent_TFLOP/s": round(f32_work / (ms_u * 1e-3) / 1e12, 2), "routes": routes}
             tb = None if zero_point else kernel_traffic(a.workload, s.name, "update")
-            if tb is not None:
-                hb = tb * u["launches_per_step"]
+            tbs = None if zero_point or not us["launches_per_step"] else kernel_traffic(a.workload, s.name,
+                                                                                        "update_split")
+            if tb is not None and (tbs is not None or not us["launches_per_step"]):
+                hb = tb * u["launches_per_step"] + (tbs * us["launches_per_step"] if tbs else 0.0)
                 # without lazy batching every column's error would be applied to all later
                 # columns of the float32 working copy at once: a read and a write of each
                 # (d_out x (d_in - j - 1)) slab, 8 d_out (d_in - j - 1) bytes for column j
@@ -644,8 +675,11 @@ def main():
         "metric": METRIC, "value": r0["value"], "unit": "weights/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": r0["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16 X: bf16 MFMA with f32 accumulation (X^T X); f32 factor and GPTQ loop" if bf else
-                  "f32 X as bf16 hi/lo pairs on bf16 MFMA, f32 accumulation (X^T X); f32 factor and GPTQ loop"),
+        "dtype": ("bf16 X: bf16 MFMA with f32 accumulation (X^T X); f32 factor and GPTQ loop, their deep "
+                  "products on 256-tile grids as six bf16 MFMA products of three-piece bf16 splits (f32-level "
+                  "terms, f32 accumulation)" if bf else
+                  "f32 X as bf16 hi/lo pairs on bf16 MFMA, f32 accumulation (X^T X); f32 factor and GPTQ loop, their "
+                  "deep products on 256-tile grids as six bf16 MFMA products of three-piece bf16 splits"),
         "data": "synthetic",
         "config": {"workload": a.workload, "layers": [f"{s.name}:{s.d_in}->{s.d_out}" for s in specs],
                    "n_tok": specs[0].n_tok, "bits": specs[0].bits, "group_size": specs[0].group_size,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PWQ_ABI_VERSION 4
+#define PWQ_ABI_VERSION 5
 
 typedef enum pwq_status {
     PWQ_OK = 0,
@@ -95,9 +95,16 @@ int pwq_last_hip_error(void);
  *   PWQ_PROF_XTX      the MFMA contraction of pwq_hessian_accumulate: n_tok d_in (d_in + 1)
  *                     flops per call (the symmetric half of 2 n_tok d_in^2);
  *   PWQ_PROF_UPDATE   the products W[:, c0:c1] -= Err U[rows, c0:c1] of
- *                     pwq_gptq_quantize_layer(_zp): 2 d_out k (c1 - c0) flops each (k error
- *                     columns); over a layer they sum to d_out d_in (d_in - B) when the
- *                     kernel with four lanes per row runs (d_out > 4096);
+ *                     pwq_gptq_quantize_layer(_zp) on float32 MFMA: 2 d_out k (c1 - c0)
+ *                     flops each (k error columns); with PWQ_PROF_UPDATE_SPLIT's products
+ *                     (counted as float32 work) they sum to d_out d_in (d_in - B) over a
+ *                     layer when the kernel with four lanes per row runs (d_out > 4096);
+ *   PWQ_PROF_UPDATE_SPLIT  the same products where they run on bfloat16 MFMA as the six
+ *                     larger products of their operands' three-piece bfloat16 splits (deep
+ *                     products past a super-block on large layers; the splitting kernels
+ *                     are inside the timed span): 12 d_out k (c1 - c0) flops each, k the
+ *                     error columns rounded up to a multiple of 64 (the bfloat16 work
+ *                     executed);
  *   PWQ_PROF_COLUMNS  the column-block kernels (quantize, error, in-block rank-1 updates):
  *                     d_out B (B - 1) flops per block of B columns;
  *   PWQ_PROF_RTN      the kernel of pwq_rtn_quantize(_zp): the bytes it must move (W, the
@@ -117,7 +124,8 @@ typedef enum pwq_prof_class {
     PWQ_PROF_COLUMNS = 2,
     PWQ_PROF_RTN = 3,
     PWQ_PROF_DEQUANT = 4,
-    PWQ_PROF_CLASSES = 5
+    PWQ_PROF_UPDATE_SPLIT = 5,
+    PWQ_PROF_CLASSES = 6
 } pwq_prof_class;
 pwq_status pwq_profile_enable(int on);
 pwq_status pwq_profile_read(double* ms, double* work, int64_t* launches, int n_classes);

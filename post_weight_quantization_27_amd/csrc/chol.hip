@@ -585,6 +585,59 @@ hipError_t launch_far_dl(float* U, const float* P, int pld, int64_t n, int64_t s
     return hipGetLastError();
 }
 
+// launch_far with its products on bfloat16 MFMA (the 256-tile register-staged engine): P and
+// the rows U[s0:s0+kf, s0:n] are cut into their three-piece splits (split3_tiled_block), and
+// each float32 product is the sum of the six larger piece products.  The dropped three are
+// below 2^-23 of |a| |b| each, so every product term is as accurate as a float32 product,
+// and the sums run on the bfloat16 pipe (eight times the float32 rate, six products per term).
+// pcs: 3 (panel-padded s0 + panel-padded (n - s0)) kseg bfloat16 values, kseg = kf rounded up
+// to 64.
+template <bool KMAJ>
+__global__ __launch_bounds__(256) void chol_split3_kernel(const float* __restrict__ src, int64_t ld, int64_t M, int64_t K,
+                                                          uint16_t* __restrict__ out, int64_t kseg, int64_t pstride) {
+    split3_tiled_block<KMAJ>(src, ld, M, K, out, kseg, pstride);
+}
+
+using SyrkSplitTask = RsTask<2, DlTiled6, DlTiled6, UpperMap, EpiSyrk>;
+using PushSplitTask = RsTask<2, DlTiled6, DlTiled6, RectMap, EpiPush>;
+
+hipError_t launch_far_split(float* U, const float* P, int pld, int64_t n, int64_t s0, int kf, int32_t* info,
+                            uint16_t* pcs, hipStream_t s) {
+    const int64_t kseg = cdiv(kf, 64) * 64;
+    const int64_t ma = dl_panel_pad(s0), mb = dl_panel_pad(n - s0);
+    uint16_t* A = pcs;                                   // pieces of P[0:s0, 0:kf]
+    uint16_t* B = pcs + 3 * ma * kseg;                   // pieces of U[s0:s0+kf, s0:n]^T
+    hipLaunchKernelGGL(chol_split3_kernel<false>, dim3((unsigned)(ma / 64), (unsigned)(kseg / 64)), dim3(256), 0, s, P,
+                       (int64_t)pld, s0, (int64_t)kf, A, kseg, ma * kseg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chol_split3_kernel<true>, dim3((unsigned)(mb / 64), (unsigned)(kseg / 64)), dim3(256), 0, s,
+                       (const float*)(U + s0 * n + s0), n, n - s0, (int64_t)kf, B, kseg, mb * kseg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint16_t* A1 = A;
+    const uint16_t* A2 = A + ma * kseg;
+    const uint16_t* A3 = A + 2 * ma * kseg;
+    const uint16_t* B1 = B;
+    const uint16_t* B2 = B + mb * kseg;
+    const uint16_t* B3 = B + 2 * mb * kseg;
+    // (i, j) of the segments: (3,1), (1,3), (2,2), (2,1), (1,2), (1,1)
+    const DlTiled6 pa{{A3, A1, A2, A2, A1, A1}, kseg};
+    SyrkSplitTask sy{};
+    sy.la = pa;
+    sy.lb = DlTiled6{{A1, A3, A2, A1, A2, A1}, kseg};
+    sy.map = UpperMap{s0, 6 * kseg, (int)cdiv(s0, DL_TILE), 1, 6 * kseg, nullptr};
+    sy.epi = EpiSyrk{U, n, s0};
+    PushSplitTask pu{};
+    pu.la = pa;
+    pu.lb = DlTiled6{{B1, B3, B2, B1, B2, B1}, kseg};
+    pu.map = rect(DL_TILE, DL_TILE, s0, n - s0, 6 * kseg);
+    pu.epi = EpiPush{U + s0, n, s0, n - s0, kf};
+    const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
+    hipLaunchKernelGGL((gemm_rs_dual_kernel<SyrkSplitTask, PushSplitTask>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy, pu,
+                       n1, (const int32_t*)info);
+    return hipGetLastError();
+}
+
 // One launch for the update of block k (syrk + push tiles, workgroups 1 ..) and the
 // factor of the next diagonal block [kd0, kd0 + NB) (workgroup 0): block k's update of that
 // block was applied by block k's trsm launch (pre_update_tile), and the syrk tiles covering
@@ -879,7 +932,17 @@ hipError_t launch_panel(float* U, float* Pk, int pld, int64_t n, int64_t k0, int
 
 }  // namespace
 
-size_t chol_ws_bytes(int64_t n) { return (size_t)n * (chol_sb(n) * CHOL_NB) * sizeof(float); }
+// far products of 256-tile size take the split route (launch_far_split) once the trailing
+// matrix holds FAR_DL_MIN_TILES of those tiles
+inline bool far_split(int64_t n, int64_t s0) { return cdiv(s0, DL_TILE) * cdiv(n, DL_TILE) >= FAR_DL_MIN_TILES; }
+inline bool far_split_possible(int64_t n) { return chol_sb(n) > 1 && far_split(n, n - 1); }
+
+// the super-block panels P, then (when the split route can run) its pieces
+size_t chol_ws_bytes(int64_t n) {
+    const size_t panels = (size_t)n * (chol_sb(n) * CHOL_NB) * sizeof(float);
+    if (!far_split_possible(n)) return panels;
+    return panels + (size_t)3 * (size_t)(dl_panel_pad(n) + DL_TILE) * (size_t)(CHOL_SB * CHOL_NB) * sizeof(uint16_t);
+}
 
 hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U, int32_t* info, void* ws, hipStream_t s) {
     if (n == 0) return hipSuccess;
@@ -895,6 +958,7 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
     // blocks aligned to their size: the updates a block owes to the matrix above and left of
     // its super-block wait until the super-block is done, and then go as one deeper product.
     float* P = (float*)ws;     // n x pld: the super-block's V panels
+    uint16_t* pcs = (uint16_t*)(P + n * (int64_t)(chol_sb(n) * CHOL_NB));   // their split pieces (far_split_possible)
     const int nt = (int)cdiv(n, CHOL_NB);
     const int sb = chol_sb(n);
     const int pld = sb * CHOL_NB;
@@ -972,13 +1036,13 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
             // super-block done: everything above and right of it, depth = its width
             const int kf = (int)((kb_lo + sb) * (int64_t)CHOL_NB < n ? sb * CHOL_NB : n - s0);
             const int64_t big = cdiv(s0, 128) * cdiv(n, 128);
-            // 256-tiles from 1024 of them (their four-times-larger tiles must still fill the
-            // chip), 128-tiles (two workgroups per CU) from 256
+            // 256-tiles on the split route from 1024 of them (their four-times-larger tiles
+            // must still fill the chip), float32 128-tiles (two workgroups per CU) from 256
             const bool dl = dl_ok(n, kf, pld, vu);
-            e = dl && cdiv(s0, 256) * cdiv(n, 256) >= FAR_DL_MIN_TILES ? launch_far_dl<256>(U, P, pld, n, s0, kf, info, s)
-                : dl && big >= 256                                    ? launch_far_dl<128>(U, P, pld, n, s0, kf, info, s)
-                : big >= 512                                          ? launch_far<128>(U, P, pld, n, s0, kf, info, vu, s)
-                                                                      : launch_far<64>(U, P, pld, n, s0, kf, info, vu, s);
+            e = far_split(n, s0)     ? launch_far_split(U, P, pld, n, s0, kf, info, pcs, s)
+                : dl && big >= 256   ? launch_far_dl<128>(U, P, pld, n, s0, kf, info, s)
+                : big >= 512         ? launch_far<128>(U, P, pld, n, s0, kf, info, vu, s)
+                                     : launch_far<64>(U, P, pld, n, s0, kf, info, vu, s);
         }
         if (e != hipSuccess) return e;
     }

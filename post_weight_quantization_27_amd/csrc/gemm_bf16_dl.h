@@ -112,6 +112,25 @@ struct DlTiled4 {
     }
 };
 
+// Six k segments of kseg each, picked like DlTiled4's.  A float32 product runs on it as the
+// six larger terms of its three-piece bfloat16 split (split3_tiled_block below): segment s
+// holds the pieces (i, j) of a_i b_j in the order (3,1), (1,3), (2,2), (2,1), (1,2), (1,1),
+// the small terms first so they build up before the large ones join the sum.
+struct DlTiled6 {
+    const uint16_t* seg[6];
+    int64_t kseg;
+    __device__ __forceinline__ const uint16_t* block(int64_t m0, int64_t k0) const {
+        const int sg = (int)(k0 >= kseg) + (int)(k0 >= 2 * kseg) + (int)(k0 >= 3 * kseg) + (int)(k0 >= 4 * kseg) +
+                       (int)(k0 >= 5 * kseg);
+        const uint16_t* p = sg == 0 ? seg[0] : seg[1];
+        p = sg == 2 ? seg[2] : p;
+        p = sg == 3 ? seg[3] : p;
+        p = sg == 4 ? seg[4] : p;
+        p = sg == 5 ? seg[5] : p;
+        return p + ((m0 >> 8) * (kseg >> 5) + ((k0 - sg * kseg) >> 5)) * (int64_t)(DL_TILE * DL_BK);
+    }
+};
+
 // Rows of a lower-triangular operand stored as whole tile-major panels of growing length:
 // panel p (rows 256 p .. 256 p + 255) holds its k-tiles 0 .. KT (p + 1) - 1 of 32 k each,
 // panel after panel (panel p starts at k-tile KT p (p + 1) / 2).  Tiles of panel p only read
@@ -124,6 +143,9 @@ struct DlTri {
         return p + ((int64_t)kt * (pan * (pan + 1) / 2) + (k0 >> 5)) * (int64_t)(DL_TILE * DL_BK);
     }
 };
+// rows of a tile-major operand: whole 256-row panels
+__host__ __device__ __forceinline__ int64_t dl_panel_pad(int64_t m) { return (m + DL_TILE - 1) / DL_TILE * DL_TILE; }
+
 // element (r, k) of one segment in the tile-major layout
 __host__ __device__ __forceinline__ int64_t dl_tiled_index(int64_t r, int64_t k, int64_t kseg) {
     return ((r >> 8) * (kseg >> 5) + (k >> 5)) * (int64_t)(DL_TILE * DL_BK) + (r & 255) * DL_BK + (k & 31);
@@ -398,14 +420,101 @@ __device__ __forceinline__ void gemm_rs_tile(const LA& la, const LB& lb, const T
         }
     }
     wait_vmcnt<0>();
+    if constexpr (EpiIsFast<EPI>::value) {
+        // whole-tile read-modify-write through buffer addressing (the float32 engines' epilogue)
+        const int wu = __builtin_amdgcn_readfirstlane(wave);
+        epi_rmw_wave<FM, FN>(epi, t, acc, t.m0 + (wu & 1) * 128, t.n0 + (wu >> 1) * 128, lane,
+                             epi_whole(epi, t, DL_TILE, DL_TILE));
+    } else {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t r0 = t.m0 + wm * 128 + i * 32 + 4 * (lane >> 5);
-            const int64_t col = t.n0 + wn * 128 + j * 32 + (lane & 31);
-            epi_block16(epi, t, acc[i][j], [&](int v) { return r0 + 8 * (v >> 2) + (v & 3); }, col);
+            for (int j = 0; j < FN; ++j) {
+                const int64_t r0 = t.m0 + wm * 128 + i * 32 + 4 * (lane >> 5);
+                const int64_t col = t.n0 + wn * 128 + j * 32 + (lane & 31);
+                epi_block16(epi, t, acc[i][j], [&](int v) { return r0 + 8 * (v >> 2) + (v & 3); }, col);
+            }
+    }
+}
+
+// One tile task of the register-staged engine, for launches that run two of them
+template <int NR, class LA_, class LB_, class MAP_, class EPI_>
+struct RsTask {
+    LA_ la;
+    LB_ lb;
+    MAP_ map;
+    EPI_ epi;
+    __device__ __forceinline__ void run(int bid, uint16_t* lds) {
+        Tile t;
+        if (!map.get(bid, DL_TILE, DL_TILE, t)) {
+            epi.finish(t, threadIdx.x, false);
+            return;
         }
+        gemm_rs_tile<NR>(la, lb, t, epi, lds);
+        epi.finish(t, threadIdx.x, true);
+    }
+};
+
+// Workgroups [0, n1) run task a, the rest task b; nothing runs while *guard != 0
+template <class TA, class TB>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_rs_dual_kernel(TA a, TB b, int n1, const int32_t* guard) {
+    if (guard && *guard != 0) return;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[RS_NS * DL_STAGE];
+    if ((int)blockIdx.x < n1) a.run((int)blockIdx.x, lds);
+    else b.run((int)blockIdx.x - n1, lds);
+}
+
+// The three bfloat16 pieces of a float32 value: a = p0 + p1 + p2 exactly.  p0 = bf16(a);
+// a - p0 is exact in float32 and holds at most 16 significant bits, p1 = bf16(a - p0); the
+// rest, at most 8 significant bits, is p2 exactly (bfloat16 shares float32's exponent range).
+__device__ __forceinline__ void split3(float a, uint16_t (&p)[3]) {
+    p[0] = f32_to_bf16_bits(a);
+    const float r1 = a - bf16_bits_to_f32(p[0]);
+    p[1] = f32_to_bf16_bits(r1);
+    p[2] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(p[1]));
+}
+
+// The pieces of a float32 operand (m, k), m < M, k < K, tile-major for DlTiled6: piece p of
+// element (m, k) at out + p pstride + dl_tiled_index(m, k, kseg); zero for m >= M (up to the
+// whole 256-row panel) or k >= K (up to kseg, a multiple of 64).  Source element (m, k) at
+// src[k ld + m] (KMAJ) or src[m ld + k].  One 64 x 64 block per workgroup through LDS, read
+// along the source's contiguous index and written 16 bytes (8 k) at a time: the body of a
+// 256-thread kernel with grid (panel-padded M / 64, kseg / 64); each file that launches it
+// wraps it in a kernel of its own name.
+template <bool KMAJ>
+__device__ __forceinline__ void split3_tiled_block(const float* __restrict__ src, int64_t ld, int64_t M, int64_t K,
+                                                   uint16_t* __restrict__ out, int64_t kseg, int64_t pstride) {
+    __shared__ float tl[64][65];
+    const int64_t m0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll 4
+    for (int q = ty; q < 64; q += 4) {
+        if (KMAJ) {
+            const int64_t k = k0 + q, m = m0 + tx;
+            tl[tx][q] = (k < K && m < M) ? src[k * ld + m] : 0.f;
+        } else {
+            const int64_t m = m0 + q, k = k0 + tx;
+            tl[q][tx] = (m < M && k < K) ? src[m * ld + k] : 0.f;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int idx = (int)threadIdx.x + 256 * h;
+        const int r = idx >> 3, kc = (idx & 7) * 8;      // row r, k kc .. kc + 7 of the block
+        uint32_t w[3][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint16_t lo[3], hi[3];
+            split3(tl[r][kc + 2 * j], lo);
+            split3(tl[r][kc + 2 * j + 1], hi);
+#pragma unroll
+            for (int p = 0; p < 3; ++p) w[p][j] = (uint32_t)lo[p] | ((uint32_t)hi[p] << 16);
+        }
+        const int64_t o = dl_tiled_index(m0 + r, k0 + kc, kseg);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) *(uint4*)(out + p * pstride + o) = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
+    }
 }
 
 template <int NR, class LA, class LB, class MAP, class EPI>

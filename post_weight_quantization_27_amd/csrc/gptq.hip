@@ -850,15 +850,71 @@ hipError_t trailing_dl(float* Wf, const float* err, int ld, const float* U, cons
     return hipGetLastError();
 }
 
+// The same product on bfloat16 MFMA (the 256-tile register-staged engine): Err[:, 0:kw] and
+// the rows U[kb0:kb0+kw, c0:c1] are cut into their three-piece splits (split3_tiled_block)
+// and each float32 product is the sum of the six larger piece products, as in the factor's
+// far products; the dropped three are below 2^-23 of |a| |b| each.  pcs: 3 (panel-padded m +
+// panel-padded (c1 - c0)) kseg values, kseg = kw rounded up to 64.
+template <bool KMAJ>
+__global__ __launch_bounds__(256) void gptq_split3_kernel(const float* __restrict__ src, int64_t ld, int64_t M, int64_t K,
+                                                          uint16_t* __restrict__ out, int64_t kseg, int64_t pstride) {
+    split3_tiled_block<KMAJ>(src, ld, M, K, out, kseg, pstride);
+}
+
+hipError_t trailing_split(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
+                          int64_t kb0, int kw, int64_t c0, int64_t c1, uint16_t* pcs, hipStream_t s) {
+    const int64_t N = c1 - c0;
+    const int64_t kseg = cdiv(kw, 64) * 64;
+    const int64_t ma = dl_panel_pad(m), mb = dl_panel_pad(N);
+    uint16_t* A = pcs;                                   // pieces of Err[:, 0:kw]
+    uint16_t* B = pcs + 3 * ma * kseg;                   // pieces of U[kb0:kb0+kw, c0:c1]^T
+    hipLaunchKernelGGL(gptq_split3_kernel<false>, dim3((unsigned)(ma / 64), (unsigned)(kseg / 64)), dim3(256), 0, s, err,
+                       (int64_t)ld, m, (int64_t)kw, A, kseg, ma * kseg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gptq_split3_kernel<true>, dim3((unsigned)(mb / 64), (unsigned)(kseg / 64)), dim3(256), 0, s,
+                       U + kb0 * n + c0, n, N, (int64_t)kw, B, kseg, mb * kseg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // (i, j) of the segments: (3,1), (1,3), (2,2), (2,1), (1,2), (1,1)
+    const DlTiled6 a{{A + 2 * ma * kseg, A, A + ma * kseg, A + ma * kseg, A, A}, kseg};
+    const DlTiled6 b{{B, B + 2 * mb * kseg, B + mb * kseg, B, B + mb * kseg, B}, kseg};
+    RectMap mp{};
+    mp.M = m; mp.N = N; mp.K = 6 * kseg;
+    mp.tiles_m = (int)cdiv(m, DL_TILE);
+    mp.tiles_n = (int)cdiv(N, DL_TILE);
+    mp.splits = 1;
+    mp.kchunk = 6 * kseg;
+    mp.tri_k = 0;
+    mp.guard = info;
+    EpiSub ep{Wf + c0, n, m, N};
+    hipLaunchKernelGGL((gemm_rs_kernel<2, DlTiled6, DlTiled6, RectMap, EpiSub>), dim3(mp.tiles_m * mp.tiles_n),
+                       dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
+    return hipGetLastError();
+}
+
 // 256-tiles from which the direct-load engine takes a trailing product on 256 x 256 tiles;
-// below that, 128-tiles from which it takes one on 128 x 128 tiles (two workgroups per CU)
+// below that, 128-tiles from which it takes one on 128 x 128 tiles (two workgroups per CU).
+// Products at least TRAIL_SPLIT_MIN_K deep with that many 256-tiles take the split route.
 constexpr int64_t TRAIL_DL_MIN_TILES = 512;
 constexpr int64_t TRAIL_DL128_MIN_TILES = 256;
+constexpr int TRAIL_SPLIT_MIN_K = 512;
 
+inline bool trail_split(int64_t m, int64_t N, int kw) {
+    return kw >= TRAIL_SPLIT_MIN_K && cdiv(m, DL_TILE) * cdiv(N, DL_TILE) >= TRAIL_DL_MIN_TILES;
+}
+
+// pcs: the split route's pieces, or null where the workspace holds none (the route is off)
 hipError_t update(float* Wf, const float* err, int ld, const float* U, const int32_t* info, int64_t m, int64_t n,
-                  int64_t kb0, int kw, int64_t c0, int64_t c1, hipStream_t s) {
+                  int64_t kb0, int kw, int64_t c0, int64_t c1, uint16_t* pcs, hipStream_t s) {
     const int64_t big_tiles = cdiv(m, 128) * cdiv(c1 - c0, 128);
     const bool dl = kw % FDL_BK == 0 && ld % 4 == 0 && n % 4 == 0 && c0 % 4 == 0 && aligned(err, 16) && aligned(U, 16);
+    if (pcs && trail_split(m, c1 - c0, kw)) {
+        // timed as its six bfloat16 products of kseg (the split kernels included)
+        prof_begin(PWQ_PROF_UPDATE_SPLIT, s);
+        const hipError_t e = trailing_split(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, pcs, s);
+        prof_end(PWQ_PROF_UPDATE_SPLIT, s, 12.0 * m * (cdiv(kw, 64) * 64) * (c1 - c0));
+        return e;
+    }
     prof_begin(PWQ_PROF_UPDATE, s);
     const hipError_t e =
         dl && cdiv(m, 256) * cdiv(c1 - c0, 256) >= TRAIL_DL_MIN_TILES ? trailing_dl<256>(Wf, err, ld, U, info, m, n, kb0, kw, c0, c1, s)
@@ -878,6 +934,13 @@ GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int group_siz
     w.err = off;   off = align_up(off + (size_t)d_out * lazy_cols(group_size, block_size, d_out) * sizeof(float), 256);
     w.codes = off; if (act_order) off = align_up(off + (size_t)d_out * d_in, 256);
     w.inv = off;   if (act_order) off = align_up(off + (size_t)d_in * sizeof(int32_t), 256);
+    // the split route's pieces (trailing_split), for the products past each super-block
+    const int lz = lazy_cols(group_size, block_size, d_out);
+    w.pcs = off;
+    if (d_in > lz && trail_split(d_out, d_in - lz, lz))
+        off = align_up(off + (size_t)3 * (size_t)(dl_panel_pad(d_out) + dl_panel_pad(d_in)) * (size_t)(cdiv(lz, 64) * 64) *
+                                 sizeof(uint16_t), 256);
+    w.has_pcs = off > w.pcs;
     w.total = off;
     return w;
 }
@@ -895,6 +958,7 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
     float* err = (float*)(base + L.err);
     int8_t* cproc = act_order ? (int8_t*)(base + L.codes) : codes;
     int32_t* inv = act_order ? (int32_t*)(base + L.inv) : nullptr;
+    uint16_t* pcs = L.has_pcs ? (uint16_t*)(base + L.pcs) : nullptr;
     const int qmax = (1 << (bits - 1)) - 1;
     const int64_t ng = group_size == 0 ? 1 : cdiv(n, group_size);
 
@@ -965,9 +1029,9 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int64_t b1 = b0 + bw;
         if (b1 < s1) {                     // the rest of the super-block, from this block's errors
-            if (quad && (e = update(Wf, err + (b0 - s0), lz, U, info, m, n, b0, bw, b1, s1, s)) != hipSuccess) return e;
+            if (quad && (e = update(Wf, err + (b0 - s0), lz, U, info, m, n, b0, bw, b1, s1, pcs, s)) != hipSuccess) return e;
         } else if (s1 < n) {               // super-block done: every column past it, depth s1 - s0
-            if ((e = update(Wf, err, lz, U, info, m, n, s0, (int)(s1 - s0), s1, n, s)) != hipSuccess) return e;
+            if ((e = update(Wf, err, lz, U, info, m, n, s0, (int)(s1 - s0), s1, n, pcs, s)) != hipSuccess) return e;
         }
     }
     if (act_order) {

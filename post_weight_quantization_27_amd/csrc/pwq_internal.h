@@ -46,7 +46,8 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
 // given zeros (zeros_out for the quantizers, zeros for the decoders): codes are then the
 // unsigned bytes 0 .. 2^bits - 1 and nibbles hold the code itself.
 struct GptqWs {
-    size_t wf, err, codes, inv, total;
+    size_t wf, err, codes, inv, pcs, total;
+    bool has_pcs;
 };
 GptqWs gptq_ws_layout(int64_t d_out, int64_t d_in, int block_size, int group_size, int act_order);
 hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, const float* U,

@@ -45,6 +45,7 @@ CALL_OF = [
     ("damp_kernel", "hessian_damp"), ("act_order_kernel", "act_order_perm"),
     ("copy_upper", "chol_inverse_upper"), ("copy_perm", "chol_inverse_upper"), ("set_int", "chol_inverse_upper"),
     ("chol_diag", "chol_inverse_upper"), ("chol_update_diag", "chol_inverse_upper"),
+    ("chol_split3", "chol_inverse_upper"),
     ("EpiStore", "chol_inverse_upper"), ("EpiSyrk", "chol_inverse_upper"), ("EpiPush", "chol_inverse_upper"),
     ("gptq_", "gptq_quantize_layer"), ("EpiSub", "gptq_quantize_layer"), ("inv_perm", "gptq_quantize_layer"),
     ("unpermute_codes", "gptq_quantize_layer"),
@@ -60,7 +61,9 @@ CALL_OF = [
 
 
 # kernel-name fragments -> kernel class of the library's timing record (pwq_profile_read)
-CLASS_OF = [("EpiHess", "xtx"), ("EpiSub", "update"), ("gptq_block_kernel", "columns"), ("gptq_row_kernel", "columns")]
+CLASS_OF = [("EpiHess", "xtx"), ("DlTiled6, DlTiled6, RectMap, EpiSub", "update_split"),
+            ("gptq_split3", "update_split_pieces"), ("EpiSub", "update"), ("gptq_block_kernel", "columns"),
+            ("gptq_row_kernel", "columns")]
 
 
 def class_of(name: str):

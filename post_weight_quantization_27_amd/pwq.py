@@ -478,7 +478,7 @@ def gptq_layer(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group_size: int 
 
 
 # ------------------------------------------------------------------ kernel timing
-PROF_CLASSES = ("xtx", "update", "columns", "rtn", "dequant")
+PROF_CLASSES = ("xtx", "update", "columns", "rtn", "dequant", "update_split")
 
 
 def profile_enable(on: bool = True) -> None:
