@@ -540,7 +540,7 @@ def report(a, layers, m, zero_point):
     achieved = amt / (dms * 1e-3) / (1e9 if unit == "byte" else 1e12)
     names = {"xtx": "gemm_rs_kernel<2, DlTiled1, DlTiled1, UpperMap, EpiHess> (pwq_hessian_accumulate's contraction)",
              "update": "gemm_fdl_kernel<..., EpiSub> (pwq_gptq_quantize_layer's trailing updates)",
-             "update_split": "gemm_rs_kernel<2, DlTiled6, DlTiled6, RectMap, EpiSub> with its split kernels "
+             "update_split": "gemm_rs_kernel<2, DlTiled6, DlTiled6, XcdRectMap, EpiSub> with its split kernels "
                              "(pwq_gptq_quantize_layer's deep trailing updates on six bf16 products)",
              "rtn_quantize": "pwq_rtn_quantize", "dequant": "pwq_dequant"}
     traffic = None

@@ -599,7 +599,7 @@ __global__ __launch_bounds__(256) void chol_split3_kernel(const float* __restric
 }
 
 using SyrkSplitTask = RsTask<2, DlTiled6, DlTiled6, UpperMap, EpiSyrk>;
-using PushSplitTask = RsTask<2, DlTiled6, DlTiled6, RectMap, EpiPush>;
+using PushSplitTask = RsTask<2, DlTiled6, DlTiled6, XcdRectMap, EpiPush>;
 
 hipError_t launch_far_split(float* U, const float* P, int pld, int64_t n, int64_t s0, int kf, int32_t* info,
                             uint16_t* pcs, hipStream_t s) {
@@ -625,14 +625,16 @@ hipError_t launch_far_split(float* U, const float* P, int pld, int64_t n, int64_
     SyrkSplitTask sy{};
     sy.la = pa;
     sy.lb = DlTiled6{{A1, A3, A2, A1, A2, A1}, kseg};
-    sy.map = UpperMap{s0, 6 * kseg, (int)cdiv(s0, DL_TILE), 1, 6 * kseg, nullptr};
+    // both tile sets in the per-XCD band order (each XCD's workgroups share operand panels)
+    sy.map = UpperMap{s0, 6 * kseg, (int)cdiv(s0, DL_TILE), 1, 6 * kseg, nullptr, 0, 1};
     sy.epi = EpiSyrk{U, n, s0};
     PushSplitTask pu{};
     pu.la = pa;
     pu.lb = DlTiled6{{B1, B3, B2, B1, B2, B1}, kseg};
-    pu.map = rect(DL_TILE, DL_TILE, s0, n - s0, 6 * kseg);
+    pu.map = XcdRectMap{s0, n - s0, 6 * kseg, (int)cdiv(s0, DL_TILE), (int)cdiv(n - s0, DL_TILE), nullptr};
     pu.epi = EpiPush{U + s0, n, s0, n - s0, kf};
-    const int n1 = ntiles(sy.map), n2 = ntiles(pu.map);
+    // n1 a multiple of 8, so the push's workgroups keep their XCD numbering
+    const int n1 = xcd_grid(ntiles(sy.map)), n2 = xcd_grid(pu.map.tiles_m * pu.map.tiles_n);
     hipLaunchKernelGGL((gemm_rs_dual_kernel<SyrkSplitTask, PushSplitTask>), dim3(n1 + n2), dim3(GEMM_THREADS), 0, s, sy, pu,
                        n1, (const int32_t*)info);
     return hipGetLastError();

@@ -271,6 +271,41 @@ struct UpperMap {
     }
 };
 
+// Rectangular grid of BM x BN tiles over M x N, whole k range [0, K), in the per-XCD order
+// of UpperMap's xcd mode: tiles in bands of four tile-rows, within a band columns left to
+// right and the band's rows fastest; workgroup b runs on XCD b % 8 and takes position
+// (b % 8) ceil(ntile / 8) + b / 8 of that order.  The workgroups in flight on one XCD then
+// hold about four row blocks and eight column blocks of operands in its L2 (with the plain
+// order and many row blocks, nearly every workgroup of an XCD reads its own row block).
+// Grid: 8 ceil(ntile / 8); padding workgroups have no tile.
+struct XcdRectMap {
+    int64_t M, N, K;
+    int tiles_m, tiles_n;
+    const int32_t* guard;
+    __device__ __forceinline__ bool get(int bid, int BM, int BN, Tile& t) const {
+        const int ntile = tiles_m * tiles_n;
+        const int per = (ntile + 7) / 8;
+        const int L = (bid % 8) * per + bid / 8;
+        t.split = 0;
+        t.tile = L;
+        t.kbeg = 0;
+        if (L >= ntile) {
+            t.m0 = t.n0 = 0;
+            t.kend = 0;
+            return false;
+        }
+        const int band = L / (4 * tiles_n);              // whole bands of 4 rows before it
+        const int r0 = band * 4;
+        const int R = tiles_m - r0 < 4 ? tiles_m - r0 : 4;
+        const int p = L - band * 4 * tiles_n;
+        t.m0 = (int64_t)(r0 + p % R) * BM;
+        t.n0 = (int64_t)(p / R) * BN;
+        t.kend = K;
+        return true;
+    }
+};
+inline int xcd_grid(int ntile) { return 8 * ((ntile + 7) / 8); }
+
 // ---------------------------------------------------------------- epilogue protocol
 // Plain epilogues take element(t, row, col, v) for every output.  Epilogues that read the
 // output before writing it declare `static constexpr bool kRmw = true` and give

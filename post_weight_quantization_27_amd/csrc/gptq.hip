@@ -878,17 +878,11 @@ hipError_t trailing_split(float* Wf, const float* err, int ld, const float* U, c
     // (i, j) of the segments: (3,1), (1,3), (2,2), (2,1), (1,2), (1,1)
     const DlTiled6 a{{A + 2 * ma * kseg, A, A + ma * kseg, A + ma * kseg, A, A}, kseg};
     const DlTiled6 b{{B, B + 2 * mb * kseg, B + mb * kseg, B, B + mb * kseg, B}, kseg};
-    RectMap mp{};
-    mp.M = m; mp.N = N; mp.K = 6 * kseg;
-    mp.tiles_m = (int)cdiv(m, DL_TILE);
-    mp.tiles_n = (int)cdiv(N, DL_TILE);
-    mp.splits = 1;
-    mp.kchunk = 6 * kseg;
-    mp.tri_k = 0;
-    mp.guard = info;
+    // tiles in the per-XCD band order: each XCD's workgroups share operand panels
+    const XcdRectMap mp{m, N, 6 * kseg, (int)cdiv(m, DL_TILE), (int)cdiv(N, DL_TILE), info};
     EpiSub ep{Wf + c0, n, m, N};
-    hipLaunchKernelGGL((gemm_rs_kernel<2, DlTiled6, DlTiled6, RectMap, EpiSub>), dim3(mp.tiles_m * mp.tiles_n),
-                       dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
+    hipLaunchKernelGGL((gemm_rs_kernel<2, DlTiled6, DlTiled6, XcdRectMap, EpiSub>),
+                       dim3((unsigned)xcd_grid(mp.tiles_m * mp.tiles_n)), dim3(GEMM_THREADS), 0, s, a, b, mp, ep);
     return hipGetLastError();
 }
 

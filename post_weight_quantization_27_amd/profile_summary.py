@@ -61,7 +61,7 @@ CALL_OF = [
 
 
 # kernel-name fragments -> kernel class of the library's timing record (pwq_profile_read)
-CLASS_OF = [("EpiHess", "xtx"), ("DlTiled6, DlTiled6, RectMap, EpiSub", "update_split"),
+CLASS_OF = [("EpiHess", "xtx"), ("DlTiled6, DlTiled6, XcdRectMap, EpiSub", "update_split"),
             ("gptq_split3", "update_split_pieces"), ("EpiSub", "update"), ("gptq_block_kernel", "columns"),
             ("gptq_row_kernel", "columns")]
 
