@@ -67,6 +67,8 @@ CLASS_OF = [("EpiHess", "xtx"), ("DlTiled6, DlTiled6, XcdRectMap, EpiSub", "upda
 
 
 def class_of(name: str):
+    # counter runs name kernels with their namespaces, kernel traces without
+    name = name.replace("(anonymous namespace)::", "").replace("pwq::", "")
     for frag, cls in CLASS_OF:
         if frag in name:
             return cls
