@@ -168,7 +168,12 @@ pwq_status pwq_act_order_perm(const float* H, int64_t d_in, int32_t* perm, void*
  *   info  device int32: 0 on success; k > 0 if the pivot of column k-1 (in the order
  *         of P H P^T) was not positive, i.e. H is not positive definite.  U is then
  *         undefined, and pwq_gptq_quantize_layer given this info writes nothing.
- *   ws    pwq_chol_workspace_size(n) bytes. */
+ *   ws    pwq_chol_workspace_size(n) bytes: the panels of up to 1024 columns (n x 1024
+ *         floats from n = 4096 on, n x 128 below) and, where the deep products can run on
+ *         bfloat16 MFMA as six products of three-piece splits (n above 8192),
+ *         their pieces (3 x 1024 bfloat16 per row, rows in whole 256-row panels).
+ * Those split products keep every product term within 2^-23 relative of the exact one
+ * and accumulate in float32, as a float32 product does. */
 size_t pwq_chol_workspace_size(int64_t n);
 pwq_status pwq_chol_inverse_upper(const float* H, int64_t n, const int32_t* perm, float* U, int32_t* info,
                                   void* ws, size_t ws_bytes, void* stream);
@@ -194,7 +199,11 @@ pwq_status pwq_chol_inverse_upper(const float* H, int64_t n, const int32_t* perm
  *              At least one of codes / packed must be given.
  *   scales_out fp16 d_out x n_groups (groups in processing order), required.
  *   g_idx      int32[d_in], group of each original column; required iff act_order.
- *   ws         pwq_gptq_workspace_size(d_out, d_in, params) bytes. */
+ *   ws         pwq_gptq_workspace_size(d_out, d_in, params) bytes: the float32 working
+ *              copy of W, the errors of up to 1024 columns, the act-order buffers, and on
+ *              large layers the pieces of the trailing products that run on bfloat16
+ *              MFMA (six products of three-piece splits, each product term within 2^-23
+ *              relative of the exact one, float32 accumulation). */
 size_t pwq_gptq_workspace_size(int64_t d_out, int64_t d_in, const pwq_params* params);
 pwq_status pwq_gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, int64_t ldw,
                                    const float* U, const int32_t* info, const pwq_params* params,

@@ -937,7 +937,12 @@ hipError_t launch_panel(float* U, float* Pk, int pld, int64_t n, int64_t k0, int
 // far products of 256-tile size take the split route (launch_far_split) once the trailing
 // matrix holds FAR_DL_MIN_TILES of those tiles
 inline bool far_split(int64_t n, int64_t s0) { return cdiv(s0, DL_TILE) * cdiv(n, DL_TILE) >= FAR_DL_MIN_TILES; }
-inline bool far_split_possible(int64_t n) { return chol_sb(n) > 1 && far_split(n, n - 1); }
+// (the largest far product is the one after the last super-block, which starts at the last
+// multiple of CHOL_SB * CHOL_NB below n)
+inline bool far_split_possible(int64_t n) {
+    constexpr int64_t w = CHOL_SB * CHOL_NB;
+    return chol_sb(n) > 1 && far_split(n, (n - 1) / w * w);
+}
 
 // the super-block panels P, then (when the split route can run) its pieces
 size_t chol_ws_bytes(int64_t n) {
