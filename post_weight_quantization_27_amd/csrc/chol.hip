@@ -49,40 +49,59 @@ __global__ void set_int_kernel(int32_t* p, int32_t v) { *p = v; }
 
 // U[i][j] = H[perm[i]][perm[j]] for j >= i, 0 below: row perm[i] of the full symmetric H is
 // staged in LDS, so both the read and the write are coalesced.  One workgroup per row; each
-// thread issues its loads (of the row, then of perm) in batches of eight, so the workgroup
-// waits for one memory latency per batch rather than per element.
-__global__ __launch_bounds__(256) void copy_perm_kernel(const float* __restrict__ H, const int32_t* __restrict__ perm,
-                                                        float* __restrict__ U, int64_t n) {
-    __shared__ float row[PERM_MAX_N];
-    constexpr int UR = 8;
+// thread issues its loads (of the row, then of perm) in batches of four, so the workgroup
+// waits for one memory latency per batch rather than per element.  The row's LDS allows one
+// workgroup per CU, so it takes 16 waves, and 16-byte loads where rows are aligned, to keep
+// enough bytes in flight to stream the row.
+__global__ __launch_bounds__(1024) void copy_perm_kernel(const float* __restrict__ H, const int32_t* __restrict__ perm,
+                                                         float* __restrict__ U, int64_t n) {
+    __shared__ __attribute__((aligned(16))) float row[PERM_MAX_N];
+    constexpr int NT = 1024, UR = 4;
     const int64_t i = blockIdx.x;
     const int tid = threadIdx.x;
     const float* src = H + (int64_t)perm[i] * n;
-    for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
-        float v[UR];
+    if (n % 4 == 0 && ((uintptr_t)H & 15) == 0) {
+        const int64_t nv = n / 4;
+        for (int64_t j0 = 0; j0 < nv; j0 += NT * UR) {
+            float4 v[UR];
 #pragma unroll
-        for (int u = 0; u < UR; ++u) {
-            const int64_t j = j0 + u * 256 + tid;
-            v[u] = j < n ? src[j] : 0.f;
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * NT + tid;
+                v[u] = j < nv ? *(const float4*)(src + 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * NT + tid;
+                if (j < nv) *(float4*)(row + 4 * j) = v[u];
+            }
         }
+    } else {
+        for (int64_t j0 = 0; j0 < n; j0 += NT * UR) {
+            float v[UR];
 #pragma unroll
-        for (int u = 0; u < UR; ++u) {
-            const int64_t j = j0 + u * 256 + tid;
-            if (j < n) row[j] = v[u];
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * NT + tid;
+                v[u] = j < n ? src[j] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int64_t j = j0 + u * NT + tid;
+                if (j < n) row[j] = v[u];
+            }
         }
     }
     __syncthreads();
     float* dst = U + i * n;
-    for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
+    for (int64_t j0 = 0; j0 < n; j0 += NT * UR) {
         int32_t pj[UR];
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const int64_t j = j0 + u * 256 + tid;
+            const int64_t j = j0 + u * NT + tid;
             pj[u] = (j < n && j >= i) ? perm[j] : 0;
         }
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const int64_t j = j0 + u * 256 + tid;
+            const int64_t j = j0 + u * NT + tid;
             if (j < n) dst[j] = j >= i ? row[pj[u]] : 0.f;
         }
     }
@@ -957,7 +976,7 @@ hipError_t chol_launch(const float* H, int64_t n, const int32_t* perm, float* U,
     // a fill kernel, not a memset node, so the sequence can be captured in a graph
     hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, s, info, 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (perm) hipLaunchKernelGGL(copy_perm_kernel, dim3((unsigned)n), dim3(256), 0, s, H, perm, U, n);
+    if (perm) hipLaunchKernelGGL(copy_perm_kernel, dim3((unsigned)n), dim3(1024), 0, s, H, perm, U, n);
     else hipLaunchKernelGGL(copy_upper_kernel, dim3((unsigned)cdiv(n, 1024), (unsigned)n), dim3(256), 0, s, H, U, n);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 

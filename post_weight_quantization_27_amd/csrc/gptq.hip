@@ -52,8 +52,10 @@ inline int lazy_cols(int group_size, int block_size, int64_t m) {
 }
 
 // zero-point form (zeros_out given): top = 2^bits - 1; fixed zeros are copied clamped to top
+// Permuted rows are staged in LDS (one workgroup per CU), so those workgroups take 16 waves to
+// keep enough loads in flight; plain rows take 4 (several workgroups per CU).
 template <int DT, bool PERM>
-__global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restrict__ W, int64_t ldw, int64_t m, int64_t n,
+__global__ __launch_bounds__(PERM ? 1024 : 256) void gptq_prologue_kernel(const void* __restrict__ W, int64_t ldw, int64_t m, int64_t n,
                                                             const int32_t* __restrict__ perm, float* __restrict__ Wf,
                                                             int row_scales, int qmax, const uint16_t* __restrict__ scales_in,
                                                             uint16_t* __restrict__ scales_out, int64_t ng,
@@ -62,8 +64,9 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
                                                             uint16_t* __restrict__ zeros_out) {
     if (*info) return;
     typedef typename Elem<DT>::T T;
+    constexpr int NT = PERM ? 1024 : 256, NW = NT / 64;
     __shared__ __attribute__((aligned(16))) float row[PERM ? PERM_MAX_N : 1];
-    __shared__ float red[8];
+    __shared__ float red[2 * NW];
     const int64_t r = blockIdx.x;
     const T* src = (const T*)W + r * ldw;
     float* dst = Wf + r * n;
@@ -73,16 +76,16 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
     if (PERM && v4) {
         constexpr int UR = 4;                  // vector loads in batches of four per thread
         const int64_t nv = n / 4;
-        for (int64_t j0 = 0; j0 < nv; j0 += 256 * UR) {
+        for (int64_t j0 = 0; j0 < nv; j0 += NT * UR) {
             float4 v[UR];
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
-                const int64_t j = j0 + u * 256 + threadIdx.x;
+                const int64_t j = j0 + u * NT + threadIdx.x;
                 v[u] = j < nv ? Elem<DT>::get4(src, 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
-                const int64_t j = j0 + u * 256 + threadIdx.x;
+                const int64_t j = j0 + u * NT + threadIdx.x;
                 if (j < nv) *(float4*)(row + 4 * j) = v[u];
                 const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
@@ -96,16 +99,16 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
     } else if (PERM) {
         // loads in batches of eight per thread (one memory latency per batch)
         constexpr int UR = 8;
-        for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
+        for (int64_t j0 = 0; j0 < n; j0 += NT * UR) {
             float v[UR];
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
-                const int64_t j = j0 + u * 256 + threadIdx.x;
+                const int64_t j = j0 + u * NT + threadIdx.x;
                 v[u] = j < n ? Elem<DT>::get(src, j) : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
-                const int64_t j = j0 + u * 256 + threadIdx.x;
+                const int64_t j = j0 + u * NT + threadIdx.x;
                 if (j < n) row[j] = v[u];
                 amax = fmaxf(amax, fabsf(v[u]));
                 hi = fmaxf(hi, v[u]);
@@ -116,32 +119,32 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
     if (PERM) {
         constexpr int UR = 8;
         __syncthreads();
-        for (int64_t p0 = 0; p0 < n; p0 += 256 * UR) {
+        for (int64_t p0 = 0; p0 < n; p0 += NT * UR) {
             int32_t pj[UR];
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
-                const int64_t p = p0 + u * 256 + threadIdx.x;
+                const int64_t p = p0 + u * NT + threadIdx.x;
                 pj[u] = p < n ? perm[p] : 0;
             }
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
-                const int64_t p = p0 + u * 256 + threadIdx.x;
+                const int64_t p = p0 + u * NT + threadIdx.x;
                 if (p < n) dst[p] = row[pj[u]];
             }
         }
     } else if (v4) {
         constexpr int UR = 4;                  // vector loads in batches of four per thread
         const int64_t nv = n / 4;
-        for (int64_t j0 = 0; j0 < nv; j0 += 256 * UR) {
+        for (int64_t j0 = 0; j0 < nv; j0 += NT * UR) {
             float4 v[UR];
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
-                const int64_t j = j0 + u * 256 + threadIdx.x;
+                const int64_t j = j0 + u * NT + threadIdx.x;
                 v[u] = j < nv ? Elem<DT>::get4(src, 4 * j) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int u = 0; u < UR; ++u) {
-                const int64_t j = j0 + u * 256 + threadIdx.x;
+                const int64_t j = j0 + u * NT + threadIdx.x;
                 if (j < nv) *(float4*)(dst + 4 * j) = v[u];
                 const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
             }
         }
     } else {
-        for (int64_t j = threadIdx.x; j < n; j += 256) {
+        for (int64_t j = threadIdx.x; j < n; j += NT) {
             const float v = Elem<DT>::get(src, j);
             dst[j] = v;
             amax = fmaxf(amax, fabsf(v));
@@ -162,23 +165,26 @@ __global__ __launch_bounds__(256) void gptq_prologue_kernel(const void* __restri
         }
     }
     if (scales_in) {
-        for (int64_t g = threadIdx.x; g < ng; g += 256) scales_out[r * ng + g] = scales_in[r * ng + g];
+        for (int64_t g = threadIdx.x; g < ng; g += NT) scales_out[r * ng + g] = scales_in[r * ng + g];
         if (zeros_out)
-            for (int64_t g = threadIdx.x; g < ng; g += 256) zeros_out[r * ng + g] = (uint16_t)min((int)zeros_in[r * ng + g], top);
+            for (int64_t g = threadIdx.x; g < ng; g += NT) zeros_out[r * ng + g] = (uint16_t)min((int)zeros_in[r * ng + g], top);
     } else if (row_scales) {
         if (zeros_out) {
             hi = wave_max(hi);
             nlo = wave_max(nlo);
-            if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = hi; red[4 + (threadIdx.x >> 6)] = nlo; }
+            if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = hi; red[NW + (threadIdx.x >> 6)] = nlo; }
         } else {
             amax = wave_max(amax);
             if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
-            const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            float a = red[0], nl = zeros_out ? red[NW] : 0.f;
+            for (int w = 1; w < NW; ++w) {
+                a = fmaxf(a, red[w]);
+                if (zeros_out) nl = fmaxf(nl, red[NW + w]);
+            }
             if (zeros_out) {
-                const float nl = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
                 const uint16_t sb = zp_scale_bits(nl, a, top);
                 scales_out[r] = sb;
                 zeros_out[r] = (uint16_t)zp_zero(nl, f16_bits_to_f32(sb), (float)top);
@@ -959,7 +965,7 @@ hipError_t gptq_launch(const void* W, int w_dtype, int64_t m, int64_t n, int64_t
     {
         auto k = w_dtype == 0 ? (act_order ? gptq_prologue_kernel<0, true> : gptq_prologue_kernel<0, false>)
                               : (act_order ? gptq_prologue_kernel<1, true> : gptq_prologue_kernel<1, false>);
-        hipLaunchKernelGGL(k, dim3((unsigned)m), dim3(256), 0, s, W, ldw, m, n, act_order ? perm : nullptr, Wf,
+        hipLaunchKernelGGL(k, dim3((unsigned)m), dim3(act_order ? 1024 : 256), 0, s, W, ldw, m, n, act_order ? perm : nullptr, Wf,
                            (int)(group_size == 0), qmax, scales_in, scales_out, ng, info, (1 << bits) - 1, zeros_in,
                            zeros_out);
     }

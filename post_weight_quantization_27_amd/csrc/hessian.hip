@@ -128,42 +128,49 @@ __global__ __launch_bounds__(256) void act_order_kernel(const float* __restrict_
     if (i < n) perm[rank] = (int32_t)i;
 }
 
-// The same ranks for n <= PERM_MAX_N: every workgroup stages the whole diagonal in LDS once,
-// and each thread scans it four values per (broadcast) read, with 32-bit counts.
-__global__ __launch_bounds__(256) void act_order_lds_kernel(const float* __restrict__ H, int64_t n,
-                                                            int32_t* __restrict__ perm) {
+// The same ranks for n <= PERM_MAX_N: every workgroup stages the whole diagonal in LDS once
+// (so one workgroup fits a CU, and it takes 16 waves), and four threads count for each
+// column, thread q of the four over the float4 chunks q, q + 4, q + 8, ... (the four
+// addresses a wave reads at once fall in different banks); the quad's counts are summed
+// with two lane exchanges.  256 columns per workgroup.
+__global__ __launch_bounds__(1024) void act_order_lds_kernel(const float* __restrict__ H, int64_t n,
+                                                             int32_t* __restrict__ perm) {
     __shared__ __attribute__((aligned(16))) float d[PERM_MAX_N];
-    constexpr int UR = 8;                                // strided loads in batches of eight per thread
-    for (int64_t j0 = 0; j0 < n; j0 += 256 * UR) {
+    constexpr int NT = 1024, UR = 8;                     // strided loads in batches of eight per thread
+    for (int64_t j0 = 0; j0 < n; j0 += NT * UR) {
         float v[UR];
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const int64_t j = j0 + u * 256 + threadIdx.x;
+            const int64_t j = j0 + u * NT + threadIdx.x;
             v[u] = j < n ? H[j * n + j] : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const int64_t j = j0 + u * 256 + threadIdx.x;
+            const int64_t j = j0 + u * NT + threadIdx.x;
             if (j < n) d[j] = v[u];
         }
     }
     __syncthreads();
-    const int64_t i64 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i64 >= n) return;
-    const int i = (int)i64, nn = (int)n;
+    const int q = (int)(threadIdx.x & 3);
+    const int64_t i64 = (int64_t)blockIdx.x * 256 + (threadIdx.x >> 2);
+    const bool live = i64 < n;                           // every lane takes part in the exchanges
+    const int i = live ? (int)i64 : 0, nn = (int)n;
     const float di = d[i];
     int rank = 0;
     const int n4 = nn / 4;
-    for (int t = 0; t < n4; ++t) {
-        const float4 q = ((const float4*)d)[t];
+    for (int t = q; t < n4; t += 4) {
+        const float4 c = ((const float4*)d)[t];
         const int j = 4 * t;
-        rank += (q.x > di) || (q.x == di && j < i);
-        rank += (q.y > di) || (q.y == di && j + 1 < i);
-        rank += (q.z > di) || (q.z == di && j + 2 < i);
-        rank += (q.w > di) || (q.w == di && j + 3 < i);
+        rank += (c.x > di) || (c.x == di && j < i);
+        rank += (c.y > di) || (c.y == di && j + 1 < i);
+        rank += (c.z > di) || (c.z == di && j + 2 < i);
+        rank += (c.w > di) || (c.w == di && j + 3 < i);
     }
-    for (int j = 4 * n4; j < nn; ++j) rank += (d[j] > di) || (d[j] == di && j < i);
-    perm[rank] = i;
+    if (q == 0)
+        for (int j = 4 * n4; j < nn; ++j) rank += (d[j] > di) || (d[j] == di && j < i);
+    rank += __shfl_xor(rank, 1);
+    rank += __shfl_xor(rank, 2);
+    if (live && q == 0) perm[rank] = i;
 }
 
 // bfloat16 X: native bf16 MFMA (products exact in float32), 128 x 128 upper tiles; the two
@@ -433,7 +440,7 @@ hipError_t damp_launch(float* H, int64_t n, float damp, float* lambda_out, hipSt
 
 hipError_t act_order_launch(const float* H, int64_t n, int32_t* perm, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    if (n <= PERM_MAX_N) hipLaunchKernelGGL(act_order_lds_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, H, n, perm);
+    if (n <= PERM_MAX_N) hipLaunchKernelGGL(act_order_lds_kernel, dim3((unsigned)cdiv(n, 256)), dim3(1024), 0, s, H, n, perm);
     else hipLaunchKernelGGL(act_order_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, H, n, perm);
     return hipGetLastError();
 }
