@@ -1,15 +1,19 @@
-"""Parity of the direct-load float32 products (256 x 256 and 128 x 128 tiles) on their edges.
+"""Parity of the large-tile products (256 x 256 and 128 x 128 tiles) on their edges.
 
 The far updates of the factor, its near updates (with the next diagonal factor in the same
-launch) and the GPTQ trailing products run on the direct-load engine once a launch has
-enough tiles: 256 x 256 tiles for the largest, 128 x 128 below.  The full-size layers have
-dimensions that are multiples of 256; these cases add what those do not reach:
+launch) and the GPTQ trailing products run on the large-tile engines once a launch has
+enough tiles: the deepest, on 256 x 256 tiles, as six bfloat16 products of their operands'
+three-piece splits (the split route), the others on the direct-load float32 engine, 128 x 128
+tiles below.  The full-size layers have dimensions that are multiples of 256; these cases
+add what those do not reach:
 
-* the factor at n = 12000: push tiles with a ragged last column block (columns clamped in
-  the loads, discarded by the epilogue), diagonal syrk tiles (the per-element triangle test),
-  and a first super-block 736 deep (not a multiple of 128);
+* the factor at n = 12000: push tiles with a ragged last column block (rows of the split
+  pieces zero past the matrix, outputs discarded by the epilogue), diagonal syrk tiles (the
+  per-element triangle test), and a first super-block 736 deep (not a multiple of 128);
 * GPTQ with 12000 rows and 4608 inputs: ragged last row tile in the trailing products, and
-  launches on both tile sizes within one layer.
+  launches on the split route and on the float32 engines within one layer;
+* GPTQ with 9000 rows and 4700 inputs: a split-route product whose columns end in a ragged
+  tile (3676 of them), a ragged last block and group (92 columns).
 
 Inputs are seeded; the float64 references are the oracle's (``oracle.chol_inverse_upper`` up
 to 8192 inputs, the same textbook route through torch.linalg on the device past that, as in
@@ -73,6 +77,31 @@ def test_gptq_large_tiles_ragged_rows(pwq):
     W = (rng.standard_t(4.0, size=(m, n)) * 0.0106).astype(np.float16)
     res = pwq.gptq_quantize_layer(torch.from_numpy(W).to(DEV), Ud, info, 4, g, B)
     rows = np.sort(np.concatenate([rng.choice(11776, 96, replace=False), np.arange(11968, 12000)]))
+    want = O.gptq(W[rows], U64, 4, g, B)
+    codes = host(res["codes"])[rows]
+    sc = host(res["scales"])[rows]
+    d = np.abs(codes.astype(np.int16) - want["codes"].astype(np.int16))
+    agree = float(np.mean(d == 0))
+    rep = O.gptq(W[rows], U64, 4, g, B, forced_codes=codes, forced_scales=sc)
+    f = rep["forced"]
+    log(f"gptq {m}x{n}: codes agree {agree:.6f} (max diff {d.max()}), replay {f}")
+    assert d.max() <= 1 and agree >= 0.999
+    assert f["max_step"] <= 1 and f["max_distance"] <= 1e-3 and f["count"] <= 1e-3 * codes.size
+    assert f["scale_max_ulp"] <= 1 and f["scale_max_distance"] <= 1e-4
+
+
+def test_gptq_split_route_ragged_columns(pwq):
+    m, n, g, B = 9000, 4700, 128, 128
+    H64 = damped_hessian64(n, 2 * n, 74)
+    U64 = O.chol_inverse_upper(host(H64))
+    del H64
+    Ud = torch.from_numpy(U64.astype(np.float32)).to(DEV)
+    info = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rng = np.random.default_rng(75)
+    W = (rng.standard_t(4.0, size=(m, n)) * 0.0106).astype(np.float16)
+    res = pwq.gptq_quantize_layer(torch.from_numpy(W).to(DEV), Ud, info, 4, g, B)
+    # rows of every row tile, the ragged last one (8960 .. 8999) among them
+    rows = np.sort(np.concatenate([rng.choice(8960, 96, replace=False), np.arange(8968, 9000)]))
     want = O.gptq(W[rows], U64, 4, g, B)
     codes = host(res["codes"])[rows]
     sc = host(res["scales"])[rows]
