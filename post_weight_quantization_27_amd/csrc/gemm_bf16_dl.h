@@ -466,7 +466,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_rs_dual_kernel(TA a, TB b, 
 
 // The three bfloat16 pieces of a float32 value: a = p0 + p1 + p2 exactly.  p0 = bf16(a);
 // a - p0 is exact in float32 and holds at most 16 significant bits, p1 = bf16(a - p0); the
-// rest, at most 8 significant bits, is p2 exactly (bfloat16 shares float32's exponent range).
+// rest, at most 8 significant bits, is p2 exactly (bfloat16 shares float32's exponent range,
+// and its subnormals hold such a rest whenever |a| >= 2^-110).
 __device__ __forceinline__ void split3(float a, uint16_t (&p)[3]) {
     p[0] = f32_to_bf16_bits(a);
     const float r1 = a - bf16_bits_to_f32(p[0]);
