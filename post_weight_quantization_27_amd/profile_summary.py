@@ -42,7 +42,7 @@ CALL_OF = [
     ("EpiHess", "hessian_accumulate"), ("hess_reduce", "hessian_accumulate"),
     ("mirror_upper", "hessian_accumulate"), ("transpose_bf16", "hessian_accumulate"),
     ("transpose_split", "hessian_accumulate"), ("FillFunctor", "hessian_accumulate"),
-    ("damp_kernel", "hessian_damp"), ("act_order_kernel", "act_order_perm"),
+    ("damp_kernel", "hessian_damp"), ("act_order_kernel", "act_order_perm"), ("act_order_lds", "act_order_perm"),
     ("copy_upper", "chol_inverse_upper"), ("copy_perm", "chol_inverse_upper"), ("set_int", "chol_inverse_upper"),
     ("chol_diag", "chol_inverse_upper"), ("chol_update_diag", "chol_inverse_upper"),
     ("chol_split3", "chol_inverse_upper"),
