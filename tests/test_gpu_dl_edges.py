@@ -13,7 +13,8 @@ add what those do not reach:
 * GPTQ with 12000 rows and 4608 inputs: ragged last row tile in the trailing products, and
   launches on the split route and on the float32 engines within one layer;
 * GPTQ with 9000 rows and 4700 inputs: a split-route product whose columns end in a ragged
-  tile (3676 of them), a ragged last block and group (92 columns).
+  tile (3676 of them), a ragged last block and group (92 columns); symmetric, and with
+  zero-points (codes compared as grid indices code - Z, the zeros within one).
 
 Inputs are seeded; the float64 references are the oracle's (``oracle.chol_inverse_upper`` up
 to 8192 inputs, the same textbook route through torch.linalg on the device past that, as in
@@ -113,3 +114,29 @@ def test_gptq_split_route_ragged_columns(pwq):
     assert d.max() <= 1 and agree >= 0.999
     assert f["max_step"] <= 1 and f["max_distance"] <= 1e-3 and f["count"] <= 1e-3 * codes.size
     assert f["scale_max_ulp"] <= 1 and f["scale_max_distance"] <= 1e-4
+
+
+def test_gptq_zp_split_route_ragged_columns(pwq):
+    m, n, g, B = 9000, 4700, 128, 128
+    H64 = damped_hessian64(n, 2 * n, 76)
+    U64 = O.chol_inverse_upper(host(H64))
+    del H64
+    Ud = torch.from_numpy(U64.astype(np.float32)).to(DEV)
+    info = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rng = np.random.default_rng(77)
+    W = (rng.standard_t(4.0, size=(m, n)) * 0.0106).astype(np.float16)
+    res = pwq.gptq_quantize_layer_zp(torch.from_numpy(W).to(DEV), Ud, info, 4, g, B)
+    rows = np.sort(np.concatenate([rng.choice(8960, 96, replace=False), np.arange(8968, 9000)]))
+    want = O.gptq(W[rows], U64, 4, g, B, sym=False)
+    gi = np.arange(n) // g
+    z = host(res["zeros"])[rows].astype(np.int32)
+    zw = want["zeros"].astype(np.int32)
+    # a zero one off shifts its whole group: compare the grid indices code - Z
+    got = host(res["codes"])[rows].astype(np.int32) - z[:, gi]
+    ref = want["codes"].astype(np.int32) - zw[:, gi]
+    d = np.abs(got - ref)
+    agree = float(np.mean(d == 0))
+    log(f"gptq zero-point {m}x{n}: grid indices agree {agree:.6f} (max diff {d.max()}), "
+        f"zeros equal {float(np.mean(z == zw)):.5f}")
+    assert d.max() <= 1 and agree >= 0.999
+    assert np.abs(z - zw).max() <= 1 and np.mean(z == zw) >= 0.99
