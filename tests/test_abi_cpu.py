@@ -65,6 +65,18 @@ def test_workspace_sizes(L):
     assert got == up(up(m * n * 4) + m * 512 * 4)
     pa = pwq.PwqParams(4, 128, 128, 1)
     assert L.pwq_gptq_workspace_size(m, n, ctypes.byref(pa)) == up(up(up(up(m * n * 4) + m * 512 * 4) + m * n) + n * 4)
+    # large layers: the bf16 pieces of the deep products (three per element, rows in whole
+    # 256-row panels) follow the float32 buffers where a deep product can take that route
+    def pad(x):
+        return (x + 255) // 256 * 256
+    assert L.pwq_chol_workspace_size(8192) == 8192 * 1024 * 4      # no far product has 1024 tiles of 256^2
+    assert L.pwq_chol_workspace_size(9000) == 9000 * 1024 * 4 + 3 * (pad(9000) + 256) * 1024 * 2
+    assert L.pwq_chol_workspace_size(28672) == 28672 * 1024 * 4 + 3 * (28672 + 256) * 1024 * 2
+    m2, n2 = 9000, 4700                         # 36 x 15 tiles of 256^2 past the first super-block
+    got = L.pwq_gptq_workspace_size(m2, n2, ctypes.byref(p))
+    assert got == up(up(up(m2 * n2 * 4) + m2 * 1024 * 4) + 3 * (pad(m2) + pad(n2)) * 1024 * 2)
+    m3, n3 = 4100, 2048                         # 17 x 4 tiles: the float32 engines only
+    assert L.pwq_gptq_workspace_size(m3, n3, ctypes.byref(p)) == up(up(m3 * n3 * 4) + m3 * 1024 * 4)
     bad = pwq.PwqParams(4, 96, 128, 0)          # group neither divides nor is a multiple of B
     assert L.pwq_gptq_workspace_size(m, n, ctypes.byref(bad)) == 0
     assert L.pwq_recon_mse_workspace_size(8192, 768, 3072) > 0
